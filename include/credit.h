@@ -1,0 +1,171 @@
+/*
+ * credit.h -- C ABI of libcredit.so: row-wise reduction-reuse operators
+ * (softmax, LayerNorm, RMSNorm) for AMD Instinct MI355X (gfx950).
+ *
+ * The operators are the "wide reduction-reuse" workload class of the CREDIT
+ * paper ("CREDIT: Cost-guided Reduction-reuse with Efficient DSMEM Inter-CTA
+ * Tiling", Sec. I and Sec. III-B, Eq. 1): each row of width N is reduced to a
+ * few statistics and every element is then reused to write a full-size output.
+ * The library reads each row from HBM once whenever the row, or a 1/P slice of
+ * it, fits on chip.
+ *
+ * Problem statement (Sec. III-B): M rows ("rows"), N elements per row ("cols"),
+ * a statistic set per operator, and, for the split-row path, P workgroups per
+ * row ("split_p", P in {2, 4, 8}; Sec. IV-A sweeps the same set).
+ *
+ * Conventions shared by every entry point:
+ *   - x, gamma, beta and y are caller-owned DEVICE pointers; the library never
+ *     frees or retains them.  Layout is dense row-major [rows][cols]; gamma and
+ *     beta are [cols].  Every pointer must be 16-byte aligned.  gamma and beta
+ *     have the same dtype as x and y.  In-place operation (y == x) is allowed;
+ *     any other overlap is undefined.
+ *   - Calls are asynchronous and stream-ordered on `stream` (a hipStream_t;
+ *     NULL means the default stream).  A successful return means the work was
+ *     enqueued; device faults surface at the caller's next synchronization.
+ *   - Argument errors return a status before anything is enqueued, and y is
+ *     left untouched.  rows == 0 is a successful no-op.
+ *   - The library owns only a small exchange scratch per (device, stream) for
+ *     the split-row path, allocated on first use of that path on that stream.
+ *     That first call must not be made under stream capture.  Two streams never
+ *     share a scratch; concurrent calls on one stream are ordered by the stream.
+ *
+ * Arithmetic: fp32 inputs compute in fp32; bf16 inputs are widened exactly to
+ * fp32, computed in fp32 and rounded to nearest-even bf16 on output.
+ */
+#ifndef CREDIT_H
+#define CREDIT_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    CREDIT_OK = 0,
+    CREDIT_ERR_INVALID_ARG = 1,    /* null pointer, cols < 1, rows < 0, bad enum, eps < 0 or not finite */
+    CREDIT_ERR_UNSUPPORTED = 2,    /* shape or option this build has no kernel for */
+    CREDIT_ERR_ALIGNMENT = 3,      /* a pointer is not 16-byte aligned */
+    CREDIT_ERR_ILLEGAL_PATH = 4,   /* a forced path / split_p / plan cannot hold the row */
+    CREDIT_ERR_NOT_CORESIDENT = 5, /* the device cannot hold split_p workgroups of this kernel at once */
+    CREDIT_ERR_NO_CALIBRATION = 6, /* calibration file missing or malformed */
+    CREDIT_ERR_HIP = 7,            /* a HIP runtime call failed */
+    CREDIT_ERR_DEVICE_TIMEOUT = 8  /* a split-row spin-wait gave up (reported by credit_check_errors) */
+} credit_status_t;
+
+typedef enum { CREDIT_F32 = 0, CREDIT_BF16 = 1 } credit_dtype_t;
+
+typedef enum { CREDIT_OP_SOFTMAX = 0, CREDIT_OP_LAYERNORM = 1, CREDIT_OP_RMSNORM = 2 } credit_op_t;
+
+typedef enum {
+    CREDIT_PATH_AUTO = 0,      /* the selector decides (credit_select_path) */
+    CREDIT_PATH_SINGLE_WG = 1, /* path 1: one wavefront or workgroup per row, row held on chip */
+    CREDIT_PATH_SPLIT_ROW = 2, /* path 2: split_p workgroups per row, slices held on chip */
+    CREDIT_PATH_REREAD = 3     /* path 3: reduce pass + output pass, the row is read twice */
+} credit_path_t;
+
+/* A launch plan.  predicted_us[i] is the selector's estimate for path i+1
+ * (at its best split_p for path 2); a negative value means illegal. */
+typedef struct {
+    int32_t path;          /* credit_path_t, never AUTO in a returned plan */
+    int32_t split_p;       /* workgroups per row: 1 for paths 1 and 3 */
+    int32_t block_threads; /* threads per row owner: 64 = one wavefront per row */
+    int32_t items;         /* vectors per thread held (paths 1, 2) or streamed per step (path 3) */
+    int32_t vec_bytes;     /* bytes per global access: 16, or one element for rows not 16-B multiples */
+    int32_t reserved;
+    double predicted_us[3];
+} credit_plan_t;
+
+/*
+ * Row-wise softmax over the last dimension (the two-stage reduction-reuse form
+ * of Sec. III-B, Eq. 1: max, then sum of exp(x - max); output
+ * exp(x_i - max) / sum).
+ *   x, y     : [rows][cols] of dtype `dt`.
+ *   path     : CREDIT_PATH_AUTO or a forced path.
+ *   split_p  : 0 = library chooses; else 2, 4 or 8 (path 2 only; must be 0 or 1 otherwise).
+ */
+credit_status_t credit_softmax(const void *x, void *y, int64_t rows, int64_t cols, credit_dtype_t dt,
+                               credit_path_t path, int32_t split_p, void *stream);
+
+/*
+ * Row-wise LayerNorm (Ba et al., cited by the paper for its LayerNorm
+ * workload, Sec. IV-A): y = (x - mean) / sqrt(var + eps) * gamma + beta with the
+ * biased (1/N) variance.  eps must be finite and >= 0.
+ */
+credit_status_t credit_layernorm(const void *x, const void *gamma, const void *beta, void *y, int64_t rows,
+                                 int64_t cols, float eps, credit_dtype_t dt, credit_path_t path,
+                                 int32_t split_p, void *stream);
+
+/*
+ * Row-wise RMSNorm: y = x / sqrt(mean(x^2) + eps) * gamma.  eps finite, >= 0.
+ */
+credit_status_t credit_rmsnorm(const void *x, const void *gamma, void *y, int64_t rows, int64_t cols,
+                               float eps, credit_dtype_t dt, credit_path_t path, int32_t split_p,
+                               void *stream);
+
+/*
+ * The selector (Sec. III-D, Eq. 3 and 7-9, adapted): legality of each path
+ * from the on-chip capacity of the compiled kernels, then the predicted time of
+ * each legal candidate; writes the fastest into *out.  Host-only: it queries
+ * device properties once per device unless a calibration with a device
+ * description is loaded.  Returns CREDIT_ERR_INVALID_ARG for a null `out` or
+ * bad shape.
+ */
+credit_status_t credit_select_path(credit_op_t op, credit_dtype_t dt, int64_t rows, int64_t cols,
+                                   credit_plan_t *out);
+
+/*
+ * Run one operator with an explicit plan (as returned by credit_select_path,
+ * or hand-built for exhaustive timing).  op selects which of gamma/beta are
+ * read (softmax: neither; RMSNorm: gamma).  Returns CREDIT_ERR_ILLEGAL_PATH if
+ * the plan's tile cannot hold the row or slice, CREDIT_ERR_UNSUPPORTED if no
+ * kernel with that tile exists.
+ */
+credit_status_t credit_run_plan(credit_op_t op, const void *x, const void *gamma, const void *beta, void *y,
+                                int64_t rows, int64_t cols, float eps, credit_dtype_t dt,
+                                const credit_plan_t *plan, void *stream);
+
+/*
+ * Work-free control kernel (Sec. III-D, the control that isolates launch,
+ * scheduling, occupancy and synchronization costs): the split-row kernel of
+ * `plan` with the same grid, tickets and exchange but no row loads or output
+ * stores.  plan->path must be CREDIT_PATH_SPLIT_ROW.
+ */
+credit_status_t credit_control(credit_op_t op, int64_t rows, int64_t cols, credit_dtype_t dt,
+                               const credit_plan_t *plan, void *stream);
+
+/*
+ * Measurement helpers.  credit_copy: 128-bit streaming copy of `bytes` bytes
+ * (a multiple of 16), the achievable read+write ceiling.  credit_flush: a
+ * read-modify-write pass over `bytes` bytes of `buf` to evict L2 and the
+ * Infinity Cache between timed runs.  Both are asynchronous on `stream`.
+ */
+credit_status_t credit_copy(const void *src, void *dst, int64_t bytes, void *stream);
+credit_status_t credit_flush(void *buf, int64_t bytes, void *stream);
+
+/*
+ * Load selector calibration from a JSON file written by the calibration
+ * script.  NULL clears it (back to the built-in model).  Returns
+ * CREDIT_ERR_NO_CALIBRATION if the file is missing or malformed, in which case
+ * the previous calibration stays in force.
+ */
+credit_status_t credit_load_calibration(const char *json_path);
+
+/*
+ * Synchronize `stream` and read (then clear) the device error word of that
+ * stream's split-row scratch: CREDIT_ERR_DEVICE_TIMEOUT if a spin-wait gave up
+ * since the last check, CREDIT_ERR_HIP if synchronization failed, else CREDIT_OK.
+ */
+credit_status_t credit_check_errors(void *stream);
+
+/* Static, human-readable name of a status code. */
+const char *credit_status_str(credit_status_t status);
+
+/* Library version, as MAJOR * 10000 + MINOR * 100 + PATCH. */
+int32_t credit_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CREDIT_H */

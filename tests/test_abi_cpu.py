@@ -1,0 +1,144 @@
+"""The C-ABI library on a machine without a GPU: it loads, exports every entry
+point include/credit.h declares, validates arguments before touching the
+device, and its host-only selector and calibration loader work."""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+from wide_reduction_reuse_amd import credit as C
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "credit.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(credit_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = C.lib()
+    names = _declared()
+    assert "credit_softmax" in names and "credit_select_path" in names
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(C.EXPORTED)
+    assert C.credit_version() == 100
+
+
+def test_status_strings():
+    for code in range(9):
+        assert C.credit_status_str(code) and C.credit_status_str(code) != "unknown status"
+    assert C.credit_status_str(99) == "unknown status"
+
+
+# Fake but 16-byte-aligned device addresses: validation must reject the call
+# before any HIP call could dereference them.
+A = ctypes.c_void_p(0x7F0000000000)
+B = ctypes.c_void_p(0x7F0000100000)
+G = ctypes.c_void_p(0x7F0000200000)
+MIS = ctypes.c_void_p(0x7F0000000004)
+
+
+def _sm(x=A, y=B, rows=4, cols=64, dt=0, path=0, p=0):
+    return C.lib().credit_softmax(x, y, rows, cols, dt, path, p, None)
+
+
+def _ln(x=A, g=G, b=G, y=B, rows=4, cols=64, eps=1e-5, dt=0, path=0, p=0):
+    return C.lib().credit_layernorm(x, g, b, y, rows, cols, eps, dt, path, p, None)
+
+
+def _rms(x=A, g=G, y=B, rows=4, cols=64, eps=1e-6, dt=0, path=0, p=0):
+    return C.lib().credit_rmsnorm(x, g, y, rows, cols, eps, dt, path, p, None)
+
+
+@pytest.mark.parametrize("call,status", [
+    (lambda: _sm(x=None), 1), (lambda: _sm(y=None), 1), (lambda: _sm(cols=0), 1),
+    (lambda: _sm(rows=-1), 1), (lambda: _sm(dt=2), 1), (lambda: _sm(path=4), 1),
+    (lambda: _sm(path=2, p=3), 1), (lambda: _sm(path=1, p=4), 1), (lambda: _sm(x=MIS), 3),
+    (lambda: _sm(y=MIS), 3), (lambda: _sm(rows=1 << 40, cols=1 << 40), 1),
+    (lambda: _ln(g=None), 1), (lambda: _ln(b=None), 1), (lambda: _ln(eps=-1.0), 1),
+    (lambda: _ln(eps=float("nan")), 1), (lambda: _ln(eps=float("inf")), 1), (lambda: _ln(b=MIS), 3),
+    (lambda: _rms(g=None), 1), (lambda: _rms(eps=-1e-6), 1), (lambda: _rms(g=MIS), 3),
+])
+def test_invalid_arguments_rejected_before_launch(call, status):
+    assert call() == status
+
+
+def test_rows_zero_is_a_noop_without_device():
+    assert _sm(rows=0) == 0
+    assert _sm(x=None, y=None, rows=0) == 0
+    assert _ln(rows=0) == 0
+    assert _rms(rows=0) == 0
+
+
+def test_forced_path_that_cannot_hold_the_row_is_refused():
+    # path 1 cannot hold a 1 MiB fp32 row; P=2 cannot either
+    assert _sm(cols=262144, path=1) == 4
+    assert _sm(cols=262144, path=2, p=2) == 4
+    # too narrow to split eight ways (the last slice would be empty)
+    assert _sm(cols=8, path=2, p=8) == 4
+
+
+def test_run_plan_validation():
+    L = C.lib()
+    plan = C.Plan.make(C.PATH_SINGLE_WG, 1, 64, 3, 16)  # no such tile
+    assert L.credit_run_plan(0, A, None, None, B, 4, 64, 0.0, 0, ctypes.byref(plan), None) == 2
+    plan = C.Plan.make(C.PATH_SINGLE_WG, 1, 64, 1, 16)  # holds 64 vectors = 256 fp32 only
+    assert L.credit_run_plan(0, A, None, None, B, 4, 1024, 0.0, 0, ctypes.byref(plan), None) == 4
+    plan = C.Plan.make(C.PATH_SPLIT_ROW, 3, 256, 8, 16)  # P must be 2, 4 or 8
+    assert L.credit_run_plan(0, A, None, None, B, 4, 4096, 0.0, 0, ctypes.byref(plan), None) == 4
+    assert L.credit_run_plan(0, A, None, None, B, 4, 4096, 0.0, 0, None, None) == 1
+    plan = C.Plan.make(C.PATH_REREAD, 1, 256, 4, 4)  # vec_bytes does not match the row
+    assert L.credit_run_plan(0, A, None, None, B, 4, 4096, 0.0, 0, ctypes.byref(plan), None) == 4
+
+
+def test_misc_entry_points_validate():
+    L = C.lib()
+    assert L.credit_copy(None, B, 16, None) == 1
+    assert L.credit_copy(A, B, 15, None) == 1
+    assert L.credit_copy(MIS, B, 16, None) == 3
+    assert L.credit_copy(A, B, 0, None) == 0
+    assert L.credit_flush(None, 16, None) == 1
+    assert L.credit_flush(A, 0, None) == 0
+    plan = C.Plan.make(C.PATH_SINGLE_WG, 1, 64, 1, 16)
+    assert L.credit_control(0, 4, 64, 0, ctypes.byref(plan), None) == 1  # control needs a split plan
+    assert L.credit_control(0, 4, 64, 0, None, None) == 1
+
+
+def test_selector_legality_on_cpu():
+    # rows of one MiB (fp32 262144) exceed one CU: path 1 illegal, path 2 chosen
+    p = C.credit_select_path("softmax", "f32", 256, 262144)
+    assert p.predicted_us[0] < 0 and p.predicted_us[1] > 0 and p.predicted_us[2] > 0
+    assert p.path in (C.PATH_SPLIT_ROW, C.PATH_REREAD)
+    # a 16 KiB row fits one owner
+    p = C.credit_select_path("layernorm", "bf16", 4096, 8192)
+    assert p.predicted_us[0] > 0
+    # rows whose byte length is not a multiple of 16 use one-element accesses
+    p = C.credit_select_path("rmsnorm", "bf16", 10, 1001)
+    assert p.vec_bytes == 2
+    assert C.lib().credit_select_path(0, 0, 1, 1, None) == 1
+    assert C.lib().credit_select_path(3, 0, 1, 1, ctypes.byref(C.Plan())) == 1
+
+
+def test_calibration_loader(tmp_path):
+    L = C.lib()
+    assert L.credit_load_calibration(str(tmp_path / "missing.json").encode()) == 6
+    bad = tmp_path / "bad.json"
+    bad.write_text("{ not json")
+    assert L.credit_load_calibration(str(bad).encode()) == 6
+    noversion = tmp_path / "nov.json"
+    noversion.write_text(json.dumps({"stream_gbs": 5000}))
+    assert L.credit_load_calibration(str(noversion).encode()) == 6
+    good = tmp_path / "good.json"
+    good.write_text(json.dumps({"version": 1, "stream_gbs": 1000.0, "launch_us": 2.0,
+                                "device": {"cus": 256, "xcds": 8}}))
+    assert L.credit_load_calibration(str(good).encode()) == 0
+    slow = C.credit_select_path("softmax", "f32", 4096, 4096).predicted_us[0]
+    assert L.credit_load_calibration(None) == 0
+    fast = C.credit_select_path("softmax", "f32", 4096, 4096).predicted_us[0]
+    assert slow > fast  # 1000 GB/s calibrated streaming is slower than the default model

@@ -1,0 +1,222 @@
+"""Thin ctypes binding to libcredit.so (include/credit.h).
+
+Argument marshalling only: tensors are passed as device pointers, the stream as
+torch's current HIP stream.  Every computation runs in the library's kernels;
+if the library has not been built this module raises on first use.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libcredit.so")
+
+# status codes (credit_status_t)
+OK = 0
+STATUS_NAMES = {0: "CREDIT_OK", 1: "CREDIT_ERR_INVALID_ARG", 2: "CREDIT_ERR_UNSUPPORTED",
+                3: "CREDIT_ERR_ALIGNMENT", 4: "CREDIT_ERR_ILLEGAL_PATH", 5: "CREDIT_ERR_NOT_CORESIDENT",
+                6: "CREDIT_ERR_NO_CALIBRATION", 7: "CREDIT_ERR_HIP", 8: "CREDIT_ERR_DEVICE_TIMEOUT"}
+# dtypes, ops, paths
+F32, BF16 = 0, 1
+SOFTMAX, LAYERNORM, RMSNORM = 0, 1, 2
+PATH_AUTO, PATH_SINGLE_WG, PATH_SPLIT_ROW, PATH_REREAD = 0, 1, 2, 3
+PATHS = {"auto": 0, "single": 1, "split": 2, "reread": 3}
+OPS = {"softmax": 0, "layernorm": 1, "rmsnorm": 2}
+DTYPES = {"f32": 0, "bf16": 1}
+
+EXPORTED = ["credit_softmax", "credit_layernorm", "credit_rmsnorm", "credit_select_path",
+            "credit_run_plan", "credit_control", "credit_copy", "credit_flush",
+            "credit_load_calibration", "credit_check_errors", "credit_status_str", "credit_version"]
+
+
+class CreditError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s: %s (%d)" % (where, STATUS_NAMES.get(status, "?"), status))
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [("path", ctypes.c_int32), ("split_p", ctypes.c_int32), ("block_threads", ctypes.c_int32),
+                ("items", ctypes.c_int32), ("vec_bytes", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("predicted_us", ctypes.c_double * 3)]
+
+    def as_dict(self) -> dict:
+        return {"path": self.path, "split_p": self.split_p, "block_threads": self.block_threads,
+                "items": self.items, "vec_bytes": self.vec_bytes,
+                "predicted_us": [self.predicted_us[i] for i in range(3)]}
+
+    @classmethod
+    def make(cls, path: int, split_p: int, block_threads: int, items: int, vec_bytes: int = 0) -> "Plan":
+        p = cls()
+        p.path, p.split_p, p.block_threads, p.items, p.vec_bytes = path, split_p, block_threads, items, vec_bytes
+        return p
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libcredit.so.  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libcredit.so is not built (run `python -m wide_reduction_reuse_amd.build`); "
+                           "there is no fallback implementation")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
+    sig = {
+        "credit_softmax": [vp, vp, i64, i64, i32, i32, i32, vp],
+        "credit_layernorm": [vp, vp, vp, vp, i64, i64, f32, i32, i32, i32, vp],
+        "credit_rmsnorm": [vp, vp, vp, i64, i64, f32, i32, i32, i32, vp],
+        "credit_select_path": [i32, i32, i64, i64, ctypes.POINTER(Plan)],
+        "credit_run_plan": [i32, vp, vp, vp, vp, i64, i64, f32, i32, ctypes.POINTER(Plan), vp],
+        "credit_control": [i32, i64, i64, i32, ctypes.POINTER(Plan), vp],
+        "credit_copy": [vp, vp, i64, vp],
+        "credit_flush": [vp, i64, vp],
+        "credit_load_calibration": [ctypes.c_char_p],
+        "credit_check_errors": [vp],
+        "credit_status_str": [i32],
+        "credit_version": [],
+    }
+    for name, args in sig.items():
+        fn = getattr(L, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int32
+    L.credit_status_str.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _check(status: int, where: str) -> None:
+    if status != OK:
+        raise CreditError(status, where)
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError("unsupported dtype %s (float32 or bfloat16)" % t.dtype)
+
+
+def _shape2d(x):
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+    cols = x.shape[-1] if x.dim() else 1
+    rows = x.numel() // cols if cols else 0
+    return rows, cols
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _path(path) -> int:
+    return PATHS[path] if isinstance(path, str) else int(path)
+
+
+def _out(x, y):
+    import torch
+    if y is None:
+        y = torch.empty_like(x)
+    if y.shape != x.shape or y.dtype != x.dtype or not y.is_contiguous():
+        raise ValueError("y must be a contiguous tensor with x's shape and dtype")
+    return y
+
+
+def credit_softmax(x, y=None, path="auto", split_p: int = 0, stream=None):
+    y = _out(x, y)
+    rows, cols = _shape2d(x)
+    _check(lib().credit_softmax(_ptr(x), _ptr(y), rows, cols, _dtype_code(x), _path(path), split_p,
+                                _stream(stream)), "credit_softmax")
+    return y
+
+
+def credit_layernorm(x, gamma, beta, eps: float, y=None, path="auto", split_p: int = 0, stream=None):
+    y = _out(x, y)
+    rows, cols = _shape2d(x)
+    _check(lib().credit_layernorm(_ptr(x), _ptr(gamma), _ptr(beta), _ptr(y), rows, cols, float(eps),
+                                  _dtype_code(x), _path(path), split_p, _stream(stream)), "credit_layernorm")
+    return y
+
+
+def credit_rmsnorm(x, gamma, eps: float, y=None, path="auto", split_p: int = 0, stream=None):
+    y = _out(x, y)
+    rows, cols = _shape2d(x)
+    _check(lib().credit_rmsnorm(_ptr(x), _ptr(gamma), _ptr(y), rows, cols, float(eps), _dtype_code(x),
+                                _path(path), split_p, _stream(stream)), "credit_rmsnorm")
+    return y
+
+
+def credit_select_path(op, dtype, rows: int, cols: int) -> Plan:
+    p = Plan()
+    op = OPS[op] if isinstance(op, str) else int(op)
+    dt = DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
+    _check(lib().credit_select_path(op, dt, rows, cols, ctypes.byref(p)), "credit_select_path")
+    return p
+
+
+def credit_run_plan(op, x, gamma, beta, y, eps: float, plan: Plan, stream=None):
+    op = OPS[op] if isinstance(op, str) else int(op)
+    rows, cols = _shape2d(x)
+    _check(lib().credit_run_plan(op, _ptr(x), _ptr(gamma), _ptr(beta), _ptr(y), rows, cols, float(eps),
+                                 _dtype_code(x), ctypes.byref(plan), _stream(stream)), "credit_run_plan")
+    return y
+
+
+def credit_control(op, rows: int, cols: int, dtype, plan: Plan, stream=None) -> None:
+    op = OPS[op] if isinstance(op, str) else int(op)
+    dt = DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
+    _check(lib().credit_control(op, rows, cols, dt, ctypes.byref(plan), _stream(stream)), "credit_control")
+
+
+def credit_copy(src, dst, stream=None) -> None:
+    nbytes = src.numel() * src.element_size()
+    _check(lib().credit_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream)), "credit_copy")
+
+
+def credit_flush(buf, stream=None) -> None:
+    nbytes = buf.numel() * buf.element_size()
+    _check(lib().credit_flush(_ptr(buf), nbytes, _stream(stream)), "credit_flush")
+
+
+def credit_load_calibration(path: Optional[str]) -> None:
+    _check(lib().credit_load_calibration(None if path is None else path.encode()), "credit_load_calibration")
+
+
+def credit_check_errors(stream=None) -> None:
+    _check(lib().credit_check_errors(_stream(stream)), "credit_check_errors")
+
+
+def credit_status_str(status: int) -> str:
+    return lib().credit_status_str(status).decode()
+
+
+def credit_version() -> int:
+    return int(lib().credit_version())
+
+
+def run(op: str, x, gamma=None, beta=None, eps: float = 0.0, y=None, path="auto", split_p: int = 0,
+        stream=None):
+    """Dispatch by operator name to the matching entry point."""
+    if op == "softmax":
+        return credit_softmax(x, y, path, split_p, stream)
+    if op == "layernorm":
+        return credit_layernorm(x, gamma, beta, eps, y, path, split_p, stream)
+    if op == "rmsnorm":
+        return credit_rmsnorm(x, gamma, eps, y, path, split_p, stream)
+    raise ValueError(op)

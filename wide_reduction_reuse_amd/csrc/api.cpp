@@ -1,0 +1,570 @@
+// C ABI of libcredit.so (declared in include/credit.h): argument validation,
+// planning, the per-(device, stream) split-row scratch, and kernel launches.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <fstream>
+#include <map>
+#include <mutex>
+#include <sstream>
+#include <utility>
+#include <vector>
+
+#include "args.hpp"
+#include "credit.h"
+#include "planner.hpp"
+#include "registry.hpp"
+
+namespace credit {
+namespace {
+
+// ---------------------------------------------------------------------------
+// kernel registry
+// ---------------------------------------------------------------------------
+const std::vector<KernelEntry> &registry()
+{
+    static const std::vector<KernelEntry> table = [] {
+        std::vector<KernelEntry> r;
+        register_softmax_kernels(r);
+        register_layernorm_kernels(r);
+        register_rmsnorm_kernels(r);
+        register_misc_kernels(r);
+        return r;
+    }();
+    return table;
+}
+
+const KernelEntry *find_kernel(int kind, int op, int dt, int vb, int block, int items)
+{
+    for (const KernelEntry &e : registry())
+        if (e.kind == kind && e.op == op && e.dt == dt && e.vb == vb && e.block == block && e.items == items)
+            return &e;
+    return nullptr;
+}
+
+const KernelEntry *find_misc(int id)
+{
+    for (const KernelEntry &e : registry())
+        if (e.kind == 0 && e.op == id)
+            return &e;
+    return nullptr;
+}
+
+// ---------------------------------------------------------------------------
+// calibration and device description
+// ---------------------------------------------------------------------------
+std::mutex g_mu;
+Calibration g_cal;
+std::map<int, DeviceModel> g_devices;
+
+DeviceModel device_model_locked()
+{
+    if (g_cal.has_device)
+        return g_cal.device;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return DeviceModel{};
+    }
+    auto it = g_devices.find(dev);
+    if (it != g_devices.end())
+        return it->second;
+    DeviceModel d;
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
+        d.cus = cus;
+    else
+        (void)hipGetLastError();
+    g_devices[dev] = d;
+    return d;
+}
+
+bool log_enabled()
+{
+    static const bool on = [] {
+        const char *v = std::getenv("CREDIT_LOG");
+        return v != nullptr && v[0] != '\0' && v[0] != '0';
+    }();
+    return on;
+}
+
+// ---------------------------------------------------------------------------
+// split-row scratch, one per (device, stream)
+// ---------------------------------------------------------------------------
+constexpr size_t kSlotWords = size_t(1) << 20;  // 8 MiB of exchange words
+constexpr uint32_t kSpinLimit = 1u << 20;
+
+struct Scratch {
+    SplitCtl *ctl = nullptr;
+    uint64_t *slots = nullptr;
+};
+std::map<std::pair<int, hipStream_t>, Scratch> g_scratch;
+
+credit_status_t get_scratch(hipStream_t s, Scratch *out)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return CREDIT_ERR_HIP;
+    std::lock_guard<std::mutex> lk(g_mu);
+    auto key = std::make_pair(dev, s);
+    auto it = g_scratch.find(key);
+    if (it != g_scratch.end()) {
+        *out = it->second;
+        return CREDIT_OK;
+    }
+    void *mem = nullptr;
+    const size_t bytes = sizeof(SplitCtl) + kSlotWords * sizeof(uint64_t);
+    if (hipMalloc(&mem, bytes) != hipSuccess)
+        return CREDIT_ERR_HIP;
+    SplitCtl init;
+    std::memset(&init, 0, sizeof(init));
+    init.epoch = 1;  // slot words start at tag 0, which no launch uses
+    if (hipMemset(mem, 0, bytes) != hipSuccess || hipMemcpy(mem, &init, sizeof(init), hipMemcpyHostToDevice) != hipSuccess) {
+        (void)hipFree(mem);
+        return CREDIT_ERR_HIP;
+    }
+    Scratch sc;
+    sc.ctl = static_cast<SplitCtl *>(mem);
+    sc.slots = reinterpret_cast<uint64_t *>(static_cast<char *>(mem) + sizeof(SplitCtl));
+    g_scratch[key] = sc;
+    *out = sc;
+    return CREDIT_OK;
+}
+
+// ---------------------------------------------------------------------------
+// validation
+// ---------------------------------------------------------------------------
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+credit_status_t validate(int op, const void *x, const void *g, const void *b, const void *y, int64_t rows,
+                         int64_t cols, float eps, int dt, bool *noop)
+{
+    *noop = false;
+    if (op < 0 || op > 2 || (dt != CREDIT_F32 && dt != CREDIT_BF16))
+        return CREDIT_ERR_INVALID_ARG;
+    if (rows < 0 || cols < 1)
+        return CREDIT_ERR_INVALID_ARG;
+    if (op != CREDIT_OP_SOFTMAX && (!std::isfinite(eps) || eps < 0.0f))
+        return CREDIT_ERR_INVALID_ARG;
+    // element count and byte size must fit comfortably in int64
+    const int64_t eb = elem_bytes(dt);
+    if (rows > 0 && cols > (INT64_C(1) << 62) / eb / rows)
+        return CREDIT_ERR_INVALID_ARG;
+    if (rows == 0) {
+        *noop = true;
+        return CREDIT_OK;
+    }
+    if (x == nullptr || y == nullptr)
+        return CREDIT_ERR_INVALID_ARG;
+    if (op >= 1 && g == nullptr)
+        return CREDIT_ERR_INVALID_ARG;
+    if (op == 1 && b == nullptr)
+        return CREDIT_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(y) || (op >= 1 && !aligned16(g)) || (op == 1 && !aligned16(b)))
+        return CREDIT_ERR_ALIGNMENT;
+    return CREDIT_OK;
+}
+
+credit_status_t check_path_args(int path, int split_p)
+{
+    if (path < CREDIT_PATH_AUTO || path > CREDIT_PATH_REREAD)
+        return CREDIT_ERR_INVALID_ARG;
+    if (path == CREDIT_PATH_SPLIT_ROW) {
+        if (split_p != 0 && split_p != 2 && split_p != 4 && split_p != 8)
+            return CREDIT_ERR_INVALID_ARG;
+    } else if (path == CREDIT_PATH_AUTO) {
+        if (split_p != 0 && split_p != 1 && split_p != 2 && split_p != 4 && split_p != 8)
+            return CREDIT_ERR_INVALID_ARG;
+    } else if (split_p != 0 && split_p != 1) {
+        return CREDIT_ERR_INVALID_ARG;
+    }
+    return CREDIT_OK;
+}
+
+// ---------------------------------------------------------------------------
+// launches
+// ---------------------------------------------------------------------------
+constexpr int64_t kMaxGridWgs = INT64_C(1) << 30;
+
+credit_status_t launch_raw(const KernelEntry *k, uint32_t grid, uint32_t block, void *arg, hipStream_t s)
+{
+    void *args[] = {arg};
+    const hipError_t e = hipLaunchKernel(k->fn, dim3(grid), dim3(block), args, 0, s);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return CREDIT_ERR_HIP;
+    }
+    return CREDIT_OK;
+}
+
+credit_status_t launch_rowwise(const KernelEntry *k, const RowArgs &a0, hipStream_t s)
+{
+    const int64_t rows_per_wg = k->kind == kKindWave ? kWaveRowsPerWg : 1;
+    const int block = k->kind == kKindWave ? 64 * kWaveRowsPerWg : k->block;
+    const int64_t eb = elem_bytes(k->dt);
+    const int64_t chunk_rows = kMaxGridWgs * rows_per_wg;
+    for (int64_t r0 = 0; r0 < a0.rows; r0 += chunk_rows) {
+        RowArgs a = a0;
+        const int64_t n = std::min(chunk_rows, a0.rows - r0);
+        const int64_t off = r0 * a0.cols * eb;
+        a.x = static_cast<const char *>(a0.x) + off;
+        a.y = static_cast<char *>(a0.y) + off;
+        a.rows = n;
+        const int64_t grid = (n + rows_per_wg - 1) / rows_per_wg;
+        const credit_status_t st = launch_raw(k, static_cast<uint32_t>(grid), block, &a, s);
+        if (st != CREDIT_OK)
+            return st;
+    }
+    return CREDIT_OK;
+}
+
+credit_status_t launch_split(const KernelEntry *k, const RowArgs &a0, int p, int q, hipStream_t s)
+{
+    Scratch sc;
+    credit_status_t st = get_scratch(s, &sc);
+    if (st != CREDIT_OK)
+        return st;
+    int occ = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k->fn, k->block, 0) != hipSuccess) {
+        (void)hipGetLastError();
+        return CREDIT_ERR_HIP;
+    }
+    DeviceModel d;
+    {
+        std::lock_guard<std::mutex> lk(g_mu);
+        d = device_model_locked();
+    }
+    if (static_cast<int64_t>(occ) * d.cus < p)
+        return CREDIT_ERR_NOT_CORESIDENT;
+    const int64_t chunk_rows = static_cast<int64_t>(kSlotWords) / (static_cast<int64_t>(p) * q);
+    for (int64_t r0 = 0; r0 < a0.rows; r0 += chunk_rows) {
+        SplitArgs sa;
+        sa.r = a0;
+        sa.ctl = sc.ctl;
+        sa.slots = sc.slots;
+        sa.row0 = r0;
+        sa.p = p;
+        sa.spin_limit = kSpinLimit;
+        const int64_t n = std::min(chunk_rows, a0.rows - r0);
+        st = launch_raw(k, static_cast<uint32_t>(n * p), k->block, &sa, s);
+        if (st != CREDIT_OK)
+            return st;
+    }
+    return CREDIT_OK;
+}
+
+// Does `plan`'s tile exist and hold the row (or slice)?
+credit_status_t resolve_plan(int op, int dt, int64_t cols, const credit_plan_t &plan, const KernelEntry **out,
+                             int *kind_out)
+{
+    const int vb = vec_bytes_for(dt, cols);
+    if (plan.vec_bytes != 0 && plan.vec_bytes != vb)
+        return CREDIT_ERR_ILLEGAL_PATH;
+    const int64_t nv = cols * elem_bytes(dt) / vb;
+    int kind = 0;
+    int64_t need = nv;
+    switch (plan.path) {
+    case CREDIT_PATH_SINGLE_WG:
+        kind = plan.block_threads == 64 ? kKindWave : kKindWg;
+        break;
+    case CREDIT_PATH_SPLIT_ROW:
+        kind = kKindSplit;
+        if (plan.split_p != 2 && plan.split_p != 4 && plan.split_p != 8)
+            return CREDIT_ERR_ILLEGAL_PATH;
+        need = (nv + plan.split_p - 1) / plan.split_p;
+        if (need * (plan.split_p - 1) >= nv)
+            return CREDIT_ERR_ILLEGAL_PATH;
+        break;
+    case CREDIT_PATH_REREAD:
+        kind = kKindReread;
+        need = 0;
+        break;
+    default:
+        return CREDIT_ERR_INVALID_ARG;
+    }
+    const KernelEntry *k = find_kernel(kind, op, dt, vb, plan.block_threads, plan.items);
+    if (k == nullptr)
+        return CREDIT_ERR_UNSUPPORTED;
+    if (need > static_cast<int64_t>(plan.block_threads) * plan.items)
+        return CREDIT_ERR_ILLEGAL_PATH;
+    *out = k;
+    *kind_out = kind;
+    return CREDIT_OK;
+}
+
+void to_c_plan(const Plan &p, credit_plan_t *out)
+{
+    std::memset(out, 0, sizeof(*out));
+    out->path = p.path;
+    out->split_p = p.split_p;
+    out->block_threads = p.tile.block;
+    out->items = p.tile.items;
+    out->vec_bytes = p.tile.vb;
+    for (int i = 0; i < 3; ++i)
+        out->predicted_us[i] = p.est[i].legal ? p.est[i].us : -1.0;
+}
+
+credit_status_t run_plan_checked(int op, const void *x, const void *g, const void *b, void *y, int64_t rows,
+                                 int64_t cols, float eps, int dt, const credit_plan_t &plan, hipStream_t s,
+                                 bool control)
+{
+    const KernelEntry *k = nullptr;
+    int kind = 0;
+    credit_status_t st = resolve_plan(op, dt, cols, plan, &k, &kind);
+    if (st != CREDIT_OK)
+        return st;
+    if (control) {
+        if (kind != kKindSplit)
+            return CREDIT_ERR_INVALID_ARG;
+        k = find_kernel(kKindControl, op, dt, k->vb, k->block, k->items);
+        if (k == nullptr)
+            return CREDIT_ERR_UNSUPPORTED;
+    }
+    RowArgs a;
+    a.x = x;
+    a.gamma = g;
+    a.beta = b;
+    a.y = y;
+    a.rows = rows;
+    a.cols = cols;
+    a.eps = eps;
+    if (log_enabled())
+        std::fprintf(stderr, "[credit] op=%d dt=%d rows=%lld cols=%lld path=%d p=%d block=%d items=%d vb=%d%s\n",
+                     op, dt, static_cast<long long>(rows), static_cast<long long>(cols), plan.path, plan.split_p,
+                     plan.block_threads, plan.items, k->vb, control ? " (control)" : "");
+    if (kind == kKindSplit)
+        return launch_split(k, a, plan.split_p, stats_per_partial(op), s);
+    return launch_rowwise(k, a, s);
+}
+
+credit_status_t run_op(int op, const void *x, const void *g, const void *b, void *y, int64_t rows, int64_t cols,
+                       float eps, int dt, int path, int split_p, void *stream)
+{
+    bool noop = false;
+    credit_status_t st = validate(op, x, g, b, y, rows, cols, eps, dt, &noop);
+    if (st != CREDIT_OK)
+        return st;
+    st = check_path_args(path, split_p);
+    if (st != CREDIT_OK)
+        return st;
+    if (noop)
+        return CREDIT_OK;
+    Plan p;
+    {
+        std::lock_guard<std::mutex> lk(g_mu);
+        Calibration cal = g_cal;
+        cal.device = device_model_locked();
+        PlanRequest req;
+        req.op = op;
+        req.dt = dt;
+        req.rows = rows;
+        req.cols = cols;
+        const int fp = split_p <= 1 ? 0 : split_p;
+        if (!make_plan(req, cal, path, fp, &p))
+            return CREDIT_ERR_ILLEGAL_PATH;
+    }
+    credit_plan_t cp;
+    to_c_plan(p, &cp);
+    return run_plan_checked(op, x, g, b, y, rows, cols, eps, dt, cp, static_cast<hipStream_t>(stream), false);
+}
+
+}  // namespace
+}  // namespace credit
+
+using namespace credit;
+
+extern "C" {
+
+credit_status_t credit_softmax(const void *x, void *y, int64_t rows, int64_t cols, credit_dtype_t dt,
+                               credit_path_t path, int32_t split_p, void *stream)
+{
+    return run_op(CREDIT_OP_SOFTMAX, x, nullptr, nullptr, y, rows, cols, 0.0f, dt, path, split_p, stream);
+}
+
+credit_status_t credit_layernorm(const void *x, const void *gamma, const void *beta, void *y, int64_t rows,
+                                 int64_t cols, float eps, credit_dtype_t dt, credit_path_t path,
+                                 int32_t split_p, void *stream)
+{
+    return run_op(CREDIT_OP_LAYERNORM, x, gamma, beta, y, rows, cols, eps, dt, path, split_p, stream);
+}
+
+credit_status_t credit_rmsnorm(const void *x, const void *gamma, void *y, int64_t rows, int64_t cols, float eps,
+                               credit_dtype_t dt, credit_path_t path, int32_t split_p, void *stream)
+{
+    return run_op(CREDIT_OP_RMSNORM, x, gamma, nullptr, y, rows, cols, eps, dt, path, split_p, stream);
+}
+
+credit_status_t credit_select_path(credit_op_t op, credit_dtype_t dt, int64_t rows, int64_t cols,
+                                   credit_plan_t *out)
+{
+    if (out == nullptr || op < 0 || op > 2 || (dt != CREDIT_F32 && dt != CREDIT_BF16) || rows < 0 || cols < 1)
+        return CREDIT_ERR_INVALID_ARG;
+    std::lock_guard<std::mutex> lk(g_mu);
+    Calibration cal = g_cal;
+    cal.device = device_model_locked();
+    PlanRequest req;
+    req.op = op;
+    req.dt = dt;
+    req.rows = rows;
+    req.cols = cols;
+    Plan p;
+    if (!make_plan(req, cal, 0, 0, &p))
+        return CREDIT_ERR_ILLEGAL_PATH;
+    to_c_plan(p, out);
+    return CREDIT_OK;
+}
+
+credit_status_t credit_run_plan(credit_op_t op, const void *x, const void *gamma, const void *beta, void *y,
+                                int64_t rows, int64_t cols, float eps, credit_dtype_t dt,
+                                const credit_plan_t *plan, void *stream)
+{
+    if (plan == nullptr)
+        return CREDIT_ERR_INVALID_ARG;
+    bool noop = false;
+    credit_status_t st = validate(op, x, gamma, beta, y, rows, cols, eps, dt, &noop);
+    if (st != CREDIT_OK || noop)
+        return st;
+    return run_plan_checked(op, x, gamma, beta, y, rows, cols, eps, dt, *plan, static_cast<hipStream_t>(stream),
+                            false);
+}
+
+credit_status_t credit_control(credit_op_t op, int64_t rows, int64_t cols, credit_dtype_t dt,
+                               const credit_plan_t *plan, void *stream)
+{
+    if (plan == nullptr || op < 0 || op > 2 || (dt != CREDIT_F32 && dt != CREDIT_BF16) || rows < 0 || cols < 1)
+        return CREDIT_ERR_INVALID_ARG;
+    if (plan->path != CREDIT_PATH_SPLIT_ROW)
+        return CREDIT_ERR_INVALID_ARG;
+    if (rows == 0)
+        return CREDIT_OK;
+    return run_plan_checked(op, nullptr, nullptr, nullptr, nullptr, rows, cols, 0.0f, dt, *plan,
+                            static_cast<hipStream_t>(stream), true);
+}
+
+credit_status_t credit_copy(const void *src, void *dst, int64_t bytes, void *stream)
+{
+    if (src == nullptr || dst == nullptr || bytes < 0 || bytes % 16 != 0)
+        return CREDIT_ERR_INVALID_ARG;
+    if (!aligned16(src) || !aligned16(dst))
+        return CREDIT_ERR_ALIGNMENT;
+    if (bytes == 0)
+        return CREDIT_OK;
+    const KernelEntry *k = find_misc(-1);
+    int64_t n16 = bytes / 16;
+    const int64_t grid = std::min<int64_t>((n16 + 1023) / 1024, INT64_C(1) << 30);
+    struct {
+        const void *s;
+        void *d;
+        int64_t n;
+    } a{src, dst, n16};
+    void *args[] = {&a.s, &a.d, &a.n};
+    if (hipLaunchKernel(k->fn, dim3(static_cast<uint32_t>(grid)), dim3(256), args, 0,
+                        static_cast<hipStream_t>(stream)) != hipSuccess) {
+        (void)hipGetLastError();
+        return CREDIT_ERR_HIP;
+    }
+    return CREDIT_OK;
+}
+
+credit_status_t credit_flush(void *buf, int64_t bytes, void *stream)
+{
+    if (buf == nullptr || bytes < 0 || bytes % 16 != 0)
+        return CREDIT_ERR_INVALID_ARG;
+    if (!aligned16(buf))
+        return CREDIT_ERR_ALIGNMENT;
+    if (bytes == 0)
+        return CREDIT_OK;
+    const KernelEntry *k = find_misc(-2);
+    int64_t n16 = bytes / 16;
+    const int64_t grid = std::min<int64_t>((n16 + 255) / 256, INT64_C(1) << 20);
+    void *b = buf;
+    void *args[] = {&b, &n16};
+    if (hipLaunchKernel(k->fn, dim3(static_cast<uint32_t>(grid)), dim3(256), args, 0,
+                        static_cast<hipStream_t>(stream)) != hipSuccess) {
+        (void)hipGetLastError();
+        return CREDIT_ERR_HIP;
+    }
+    return CREDIT_OK;
+}
+
+credit_status_t credit_load_calibration(const char *json_path)
+{
+    if (json_path == nullptr) {
+        std::lock_guard<std::mutex> lk(g_mu);
+        g_cal = Calibration{};
+        return CREDIT_OK;
+    }
+    std::ifstream f(json_path);
+    if (!f)
+        return CREDIT_ERR_NO_CALIBRATION;
+    std::stringstream ss;
+    ss << f.rdbuf();
+    Calibration c;
+    if (!parse_calibration(ss.str(), &c))
+        return CREDIT_ERR_NO_CALIBRATION;
+    std::lock_guard<std::mutex> lk(g_mu);
+    g_cal = c;
+    return CREDIT_OK;
+}
+
+credit_status_t credit_check_errors(void *stream)
+{
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (hipStreamSynchronize(s) != hipSuccess) {
+        (void)hipGetLastError();
+        return CREDIT_ERR_HIP;
+    }
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return CREDIT_ERR_HIP;
+    Scratch sc;
+    {
+        std::lock_guard<std::mutex> lk(g_mu);
+        auto it = g_scratch.find(std::make_pair(dev, s));
+        if (it == g_scratch.end())
+            return CREDIT_OK;
+        sc = it->second;
+    }
+    uint32_t err = 0;
+    if (hipMemcpy(&err, &sc.ctl->error, sizeof(err), hipMemcpyDeviceToHost) != hipSuccess)
+        return CREDIT_ERR_HIP;
+    if (err != 0) {
+        const uint32_t zero = 0;
+        if (hipMemcpy(&sc.ctl->error, &zero, sizeof(zero), hipMemcpyHostToDevice) != hipSuccess)
+            return CREDIT_ERR_HIP;
+        return CREDIT_ERR_DEVICE_TIMEOUT;
+    }
+    return CREDIT_OK;
+}
+
+const char *credit_status_str(credit_status_t status)
+{
+    switch (status) {
+    case CREDIT_OK:
+        return "ok";
+    case CREDIT_ERR_INVALID_ARG:
+        return "invalid argument";
+    case CREDIT_ERR_UNSUPPORTED:
+        return "unsupported shape or option";
+    case CREDIT_ERR_ALIGNMENT:
+        return "pointer not 16-byte aligned";
+    case CREDIT_ERR_ILLEGAL_PATH:
+        return "path or split cannot hold the row";
+    case CREDIT_ERR_NOT_CORESIDENT:
+        return "split workgroups cannot be co-resident";
+    case CREDIT_ERR_NO_CALIBRATION:
+        return "calibration missing or malformed";
+    case CREDIT_ERR_HIP:
+        return "HIP runtime error";
+    case CREDIT_ERR_DEVICE_TIMEOUT:
+        return "split-row exchange wait timed out";
+    }
+    return "unknown status";
+}
+
+int32_t credit_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,232 @@
+// Device-side building blocks for the gfx950 reduction-reuse kernels:
+// 128-bit row tiles held in VGPRs, bf16 conversion, wave64 DPP reductions and
+// the fp32 exponential used by softmax.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace credit {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// Storage types.  `bf16_t` is the raw 16-bit pattern; arithmetic is in fp32.
+// ---------------------------------------------------------------------------
+struct bf16_t {
+    uint16_t bits;
+};
+
+template <class T> struct StorageTraits;
+template <> struct StorageTraits<float> {
+    static constexpr int kBytes = 4;
+};
+template <> struct StorageTraits<bf16_t> {
+    static constexpr int kBytes = 2;
+};
+
+// A vector of VB bytes (16, or one element) moved by a single global access.
+template <int VB> struct RawVec;
+template <> struct RawVec<16> {
+    static constexpr int kWords = 4;
+    u32x4 w;
+};
+template <> struct RawVec<4> {
+    static constexpr int kWords = 1;
+    uint32_t w;
+};
+template <> struct RawVec<2> {
+    static constexpr int kWords = 1;  // low half used
+    uint32_t w;
+};
+
+template <int VB>
+__device__ __forceinline__ RawVec<VB> load_vec(const void *p)
+{
+    RawVec<VB> r;
+    if constexpr (VB == 16) {
+        r.w = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    } else if constexpr (VB == 4) {
+        r.w = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(p));
+    } else {
+        r.w = __builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(p));
+    }
+    return r;
+}
+
+// Cached load, for parameter vectors (gamma, beta) shared by every row.
+template <int VB>
+__device__ __forceinline__ RawVec<VB> load_vec_cached(const void *p)
+{
+    RawVec<VB> r;
+    if constexpr (VB == 16) {
+        r.w = *reinterpret_cast<const u32x4 *>(p);
+    } else if constexpr (VB == 4) {
+        r.w = *reinterpret_cast<const uint32_t *>(p);
+    } else {
+        r.w = *reinterpret_cast<const uint16_t *>(p);
+    }
+    return r;
+}
+
+template <int VB>
+__device__ __forceinline__ void store_vec(void *p, const RawVec<VB> &r)
+{
+    if constexpr (VB == 16) {
+        __builtin_nontemporal_store(r.w, reinterpret_cast<u32x4 *>(p));
+    } else if constexpr (VB == 4) {
+        __builtin_nontemporal_store(r.w, reinterpret_cast<uint32_t *>(p));
+    } else {
+        __builtin_nontemporal_store(static_cast<uint16_t>(r.w), reinterpret_cast<uint16_t *>(p));
+    }
+}
+
+template <int VB> __device__ __forceinline__ uint32_t word(const RawVec<VB> &r, int i)
+{
+    if constexpr (VB == 16)
+        return r.w[i];
+    else
+        return r.w;
+}
+template <int VB> __device__ __forceinline__ void set_word(RawVec<VB> &r, int i, uint32_t v)
+{
+    if constexpr (VB == 16)
+        r.w[i] = v;
+    else
+        r.w = v;
+}
+
+// Element e (0 <= e < elements per vector) of a raw vector, as fp32.
+template <class T, int VB>
+__device__ __forceinline__ float elem(const RawVec<VB> &r, int e)
+{
+    if constexpr (StorageTraits<T>::kBytes == 4) {
+        return __uint_as_float(word<VB>(r, e));
+    } else {
+        uint32_t w = word<VB>(r, e >> 1);
+        return (e & 1) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16);
+    }
+}
+
+// Pack fp32 results into a raw vector of the storage type (bf16: round to
+// nearest even with v_cvt_pk_bf16_f32).
+template <class T, int VB, int EPV>
+__device__ __forceinline__ RawVec<VB> pack(const float (&v)[EPV])
+{
+    RawVec<VB> r;
+    if constexpr (StorageTraits<T>::kBytes == 4) {
+#pragma unroll
+        for (int e = 0; e < EPV; ++e)
+            set_word<VB>(r, e, __float_as_uint(v[e]));
+    } else if constexpr (EPV == 1) {
+        bf16x2 b = __builtin_convertvector((f32x2){v[0], 0.0f}, bf16x2);
+        set_word<VB>(r, 0, __builtin_bit_cast(uint32_t, b) & 0xffffu);
+    } else {
+#pragma unroll
+        for (int e = 0; e < EPV; e += 2) {
+            bf16x2 b = __builtin_convertvector((f32x2){v[e], v[e + 1]}, bf16x2);
+            set_word<VB>(r, e >> 1, __builtin_bit_cast(uint32_t, b));
+        }
+    }
+    return r;
+}
+
+// ---------------------------------------------------------------------------
+// Wave64 reductions.  Four DPP steps reduce each row of 16 lanes (quad swaps,
+// half-row mirror, row mirror), leaving the row result in every lane of the
+// row; the four row results are then read as uniform values with readlane and
+// combined in a fixed order, so every lane gets the same bits.
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // row_half_mirror
+constexpr int kDppRowMirror = 0x140;   // row_mirror
+
+__device__ __forceinline__ float lane_read(float v, int lane)
+{
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+__device__ __forceinline__ float wave_sum(float v)
+{
+    v += dpp<kDppQuadXor1>(v);
+    v += dpp<kDppQuadXor2>(v);
+    v += dpp<kDppHalfMirror>(v);
+    v += dpp<kDppRowMirror>(v);
+    return (lane_read(v, 0) + lane_read(v, 16)) + (lane_read(v, 32) + lane_read(v, 48));
+}
+
+__device__ __forceinline__ float wave_max(float v)
+{
+    v = fmaxf(v, dpp<kDppQuadXor1>(v));
+    v = fmaxf(v, dpp<kDppQuadXor2>(v));
+    v = fmaxf(v, dpp<kDppHalfMirror>(v));
+    v = fmaxf(v, dpp<kDppRowMirror>(v));
+    return fmaxf(fmaxf(lane_read(v, 0), lane_read(v, 16)), fmaxf(lane_read(v, 32), lane_read(v, 48)));
+}
+
+// ---------------------------------------------------------------------------
+// Exponentials.
+//
+// exp_acc: exp(d) to about 2 ulp for the fp32 outputs.  exp(d) = 2^(d log2 e);
+// the product is split as t + c, t = fl(d * L) with L = fl(log2 e), and
+// c = (d * L - t) + d * (log2 e - L) (the first term exact by FMA), so
+// exp(d) = 2^t * 2^c with |c| < 2^-20 and 2^c = 1 + c ln 2 to within 1e-13.
+// 2^t uses the hardware v_exp_f32.
+//
+// exp_fast: 2^(d * L) only; used where the output is bf16.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float exp_acc(float d)
+{
+    const float L = 1.44269502162933349609375f;       // fl(log2 e)
+    const float Llo = 1.925963033500011e-08f;          // log2 e - L
+    const float Ln2 = 0.693147180559945309f;
+    float t = d * L;
+    float c = __builtin_fmaf(d, L, -t) + d * Llo;
+    return __builtin_amdgcn_exp2f(t) * __builtin_fmaf(c, Ln2, 1.0f);
+}
+
+__device__ __forceinline__ float exp_fast(float d)
+{
+    return __builtin_amdgcn_exp2f(d * 1.44269502162933349609375f);
+}
+
+// ---------------------------------------------------------------------------
+// Agent-scope atomics on 64-bit words, used for the split-row exchange.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void store_u64_agent(uint64_t *p, uint64_t v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t load_u64_agent(const uint64_t *p)
+{
+    return __hip_atomic_load(const_cast<uint64_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t load_u32_agent(const uint32_t *p)
+{
+    return __hip_atomic_load(const_cast<uint32_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_u32_agent(uint32_t *p, uint32_t v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t fetch_add_u32_agent(uint32_t *p, uint32_t v)
+{
+    return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void fetch_or_u32_agent(uint32_t *p, uint32_t v)
+{
+    (void)__hip_atomic_fetch_or(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace credit

@@ -1,0 +1,494 @@
+// Host-only planner and cost model (see planner.hpp).
+#include "planner.hpp"
+
+#include <algorithm>
+#include <cctype>
+#include <cmath>
+#include <cstdlib>
+#include <map>
+
+#include "registry.hpp"
+
+namespace credit {
+
+int elem_bytes(int dt) { return dt == 1 ? 2 : 4; }
+int n_params(int op) { return op == 1 ? 2 : (op == 2 ? 1 : 0); }
+int stats_per_partial(int op) { return op == 1 ? 3 : (op == 2 ? 1 : 2); }
+
+int vec_bytes_for(int dt, int64_t cols)
+{
+    return (cols * elem_bytes(dt)) % 16 == 0 ? 16 : elem_bytes(dt);
+}
+
+// ---------------------------------------------------------------------------
+// Tile ladders (must match instantiate.hpp; the library checks at load time
+// that every tile listed here has a compiled kernel).
+// ---------------------------------------------------------------------------
+static std::vector<TileSpec> make_ladder(int kind, bool v16)
+{
+    std::vector<TileSpec> t;
+    auto add = [&](int block, int items) { t.push_back(TileSpec{kind, block, items, v16 ? 16 : 0}); };
+    if (v16) {
+        switch (kind) {
+        case kKindWave:
+            for (int it : {1, 2, 4, 8, 16})
+                add(64, it);
+            break;
+        case kKindWg:
+            for (int it : {2, 4, 8, 16})
+                add(256, it);
+            for (int it : {4, 8, 16})
+                add(512, it);
+            for (int it : {4, 8, 16})
+                add(1024, it);
+            break;
+        case kKindSplit:
+        case kKindControl:
+            add(256, 8);
+            add(256, 16);
+            add(512, 8);
+            add(512, 16);
+            add(1024, 4);
+            add(1024, 8);
+            add(1024, 16);
+            break;
+        case kKindReread:
+            add(256, 4);
+            add(512, 4);
+            add(1024, 4);
+            break;
+        }
+    } else {
+        switch (kind) {
+        case kKindWave:
+            add(64, 4);
+            add(64, 16);
+            break;
+        case kKindWg:
+            add(1024, 4);
+            add(1024, 16);
+            break;
+        case kKindSplit:
+        case kKindControl:
+            add(1024, 16);
+            break;
+        case kKindReread:
+            add(256, 8);
+            break;
+        }
+    }
+    return t;
+}
+
+const std::vector<TileSpec> &tiles_for(int kind, int vb_is_16)
+{
+    static std::map<int, std::vector<TileSpec>> cache[2];
+    auto &m = cache[vb_is_16 ? 1 : 0];
+    auto it = m.find(kind);
+    if (it == m.end())
+        it = m.emplace(kind, make_ladder(kind, vb_is_16 != 0)).first;
+    return it->second;
+}
+
+static int64_t vectors_in_row(int dt, int64_t cols, int vb) { return cols * elem_bytes(dt) / vb; }
+
+// Preference among tiles that can hold `nv` vectors: the smallest capacity,
+// and within a capacity the one with 8 vectors per thread (then fewer threads).
+static bool pick_holding_tile(const std::vector<TileSpec> &ladder, int64_t nv, TileSpec *out)
+{
+    bool found = false;
+    TileSpec best;
+    int64_t best_cap = 0;
+    for (const TileSpec &t : ladder) {
+        const int64_t cap = static_cast<int64_t>(t.block) * t.items;
+        if (cap < nv)
+            continue;
+        bool better = !found || cap < best_cap;
+        if (found && cap == best_cap) {
+            const int d_new = std::abs(t.items - 8), d_old = std::abs(best.items - 8);
+            better = d_new < d_old || (d_new == d_old && t.block < best.block);
+        }
+        if (better) {
+            best = t;
+            best_cap = cap;
+            found = true;
+        }
+    }
+    if (found)
+        *out = best;
+    return found;
+}
+
+bool single_tile(int dt, int64_t cols, TileSpec *out)
+{
+    const int vb = vec_bytes_for(dt, cols);
+    const bool v16 = vb == 16;
+    const int64_t nv = vectors_in_row(dt, cols, vb);
+    TileSpec t;
+    if (pick_holding_tile(tiles_for(kKindWave, v16), nv, &t) ||
+        pick_holding_tile(tiles_for(kKindWg, v16), nv, &t)) {
+        t.vb = vb;
+        *out = t;
+        return true;
+    }
+    return false;
+}
+
+bool split_tile(int dt, int64_t cols, int p, TileSpec *out)
+{
+    if (p != 2 && p != 4 && p != 8)
+        return false;
+    const int vb = vec_bytes_for(dt, cols);
+    const int64_t nv = vectors_in_row(dt, cols, vb);
+    const int64_t per = (nv + p - 1) / p;
+    if (per * (p - 1) >= nv)
+        return false;  // the last slice would be empty: too narrow to split p ways
+    TileSpec t;
+    if (!pick_holding_tile(tiles_for(kKindSplit, vb == 16), per, &t))
+        return false;
+    t.vb = vb;
+    *out = t;
+    return true;
+}
+
+TileSpec reread_tile(int dt, int64_t cols)
+{
+    const int vb = vec_bytes_for(dt, cols);
+    const int64_t nv = vectors_in_row(dt, cols, vb);
+    const auto &ladder = tiles_for(kKindReread, vb == 16);
+    TileSpec t = ladder.front();
+    if (vb == 16) {
+        // enough threads to give each one a few vectors per pass
+        for (const TileSpec &c : ladder)
+            if (static_cast<int64_t>(c.block) * c.items * 2 <= nv)
+                t = c;
+    }
+    t.vb = vb;
+    return t;
+}
+
+double tile_capacity_bytes(const TileSpec &t) { return static_cast<double>(t.block) * t.items * t.vb; }
+
+double onchip_budget_bytes(const DeviceModel &d) { return d.vgpr_bytes_per_cu + d.lds_bytes_per_cu; }
+
+// ---------------------------------------------------------------------------
+// Cost model
+// ---------------------------------------------------------------------------
+namespace {
+
+struct Model {
+    double stream_gbs, per_cu_gbs, launch_us, exchange_us, hit_l2;
+};
+
+Model model_of(const Calibration &c)
+{
+    Model m;
+    m.stream_gbs = c.stream_gbs > 0 ? c.stream_gbs : 0.8 * c.device.hbm_peak_gbs;
+    m.per_cu_gbs = c.per_cu_gbs > 0 ? c.per_cu_gbs : 50.0;
+    m.launch_us = c.launch_us >= 0 ? c.launch_us : 4.0;
+    m.exchange_us = c.exchange_us >= 0 ? c.exchange_us : 3.0;
+    m.hit_l2 = c.reread_hit_l2 >= 0 ? c.reread_hit_l2 : 0.9;
+    return m;
+}
+
+double eff_of(const double (&e)[3][2], int op, int dt)
+{
+    const double v = e[op][dt];
+    return v > 0 ? v : 1.0;
+}
+
+// Estimated resident workgroups per CU for a tile: VGPRs from the held data
+// plus a fixed overhead, 512 VGPRs per SIMD lane, 4 SIMDs, at most 8 waves/SIMD.
+int wgs_per_cu(const TileSpec &t)
+{
+    const int waves = t.block / 64;
+    const int data_vgprs = (t.kind == kKindReread) ? t.items * t.vb / 4 * 2 : t.items * t.vb / 4;
+    int vgprs = data_vgprs + 32;
+    vgprs = (vgprs + 7) / 8 * 8;
+    int waves_per_simd = std::min(8, 512 / vgprs);
+    int per_cu = (4 * waves_per_simd) / std::max(1, waves);
+    if (t.kind == kKindWave)
+        per_cu = (4 * waves_per_simd) / 4;  // 4 waves (4 rows) per workgroup
+    return std::max(1, per_cu);
+}
+
+// Time to stream `bytes` with `units` independent workgroups of which at most
+// `resident` run at once on `cus` CUs.
+double stream_us(const Model &m, const DeviceModel &d, double bytes, double units, double per_cu)
+{
+    const double active_cus = std::min<double>(d.cus, units);
+    double bw = std::min(m.stream_gbs, active_cus * m.per_cu_gbs);
+    (void)per_cu;
+    return bytes / (bw * 1e3);  // GB/s = 1e3 bytes/us
+}
+
+}  // namespace
+
+bool make_plan(const PlanRequest &req, const Calibration &cal, int forced_path, int forced_p, Plan *out)
+{
+    const DeviceModel &d = cal.device;
+    const Model m = model_of(cal);
+    const double M = static_cast<double>(req.rows), N = static_cast<double>(req.cols);
+    const int b = elem_bytes(req.dt);
+    const double row_bytes = N * b;
+    const double bytes_io = M * N * 2.0 * b + N * b * n_params(req.op);
+    Plan p;
+
+    // path 1
+    PathEstimate &e1 = p.est[0];
+    e1.legal = single_tile(req.dt, req.cols, &e1.tile);
+    if (e1.legal) {
+        const double units = e1.tile.kind == kKindWave ? std::ceil(M / 4.0) : M;
+        e1.t_stream_us = stream_us(m, d, bytes_io, units, wgs_per_cu(e1.tile));
+        e1.us = m.launch_us + e1.t_stream_us * eff_of(cal.single_eff, req.op, req.dt);
+    }
+
+    // path 3 (always legal): the reread is served on chip when the rows in
+    // flight on one XCD fit its L2, from the Infinity Cache when all rows in
+    // flight fit it (counted as half an HBM read), else from HBM.
+    PathEstimate &e3 = p.est[2];
+    e3.legal = true;
+    e3.tile = reread_tile(req.dt, req.cols);
+    {
+        const double resident = std::min(M, static_cast<double>(d.cus) * wgs_per_cu(e3.tile));
+        const double per_xcd = resident / d.xcds;
+        double miss;
+        if (per_xcd * row_bytes <= d.l2_bytes_per_xcd)
+            miss = 1.0 - m.hit_l2;
+        else if (resident * row_bytes <= d.mall_bytes)
+            miss = 0.5;
+        else
+            miss = 1.0;
+        const double bytes3 = bytes_io + M * N * b * miss;
+        e3.t_stream_us = stream_us(m, d, bytes3, M, wgs_per_cu(e3.tile));
+        e3.us = m.launch_us + e3.t_stream_us * eff_of(cal.reread_eff, req.op, req.dt);
+    }
+
+    // path 2 at each legal P: Eq. 9 against the non-split baseline B
+    // (path 1 if legal, else path 3); the prediction itself streams the row
+    // once over M*P workgroups and pays one exchange round per row wave (Eq. 8).
+    const PathEstimate &base = e1.legal ? e1 : e3;
+    const double b_base = e1.legal ? 2.0 * b : 2.0 * b + b;  // bytes/element of the baseline schedule
+    const double b_reread = e1.legal ? 0.0 : b;
+    PathEstimate &e2 = p.est[1];
+    for (int P : {2, 4, 8}) {
+        if (forced_p != 0 && P != forced_p)
+            continue;
+        TileSpec t;
+        if (!split_tile(req.dt, req.cols, P, &t))
+            continue;
+        PathEstimate e;
+        e.legal = true;
+        e.split_p = P;
+        e.tile = t;
+        const double clusters = std::max(1.0, std::floor(static_cast<double>(d.cus) * wgs_per_cu(t) / P));
+        e.waves = std::ceil(M / clusters);
+        e.t_stream_us = stream_us(m, d, bytes_io, M * P, wgs_per_cu(t));
+        e.t_ctrl_us = e.waves * m.exchange_us;
+        e.t_save_us = (b_reread / b_base) * base.us;  // Eq. 7
+        e.us = m.launch_us + e.t_stream_us * eff_of(cal.split_eff, req.op, req.dt) + e.t_ctrl_us;
+        if (!e2.legal || e.us < e2.us)
+            e2 = e;
+    }
+
+    // choice
+    int path = forced_path;
+    if (path == kPathAuto) {
+        double best = -1.0;
+        for (int i = 0; i < 3; ++i)
+            if (p.est[i].legal && (best < 0 || p.est[i].us < best)) {
+                best = p.est[i].us;
+                path = i + 1;
+            }
+    }
+    if (path < 1 || path > 3 || !p.est[path - 1].legal)
+        return false;
+    p.path = path;
+    p.split_p = path == kPathSplit ? p.est[1].split_p : 1;
+    p.tile = p.est[path - 1].tile;
+    *out = p;
+    return true;
+}
+
+// ---------------------------------------------------------------------------
+// Minimal JSON reader for the calibration file: objects, arrays, numbers,
+// strings, true/false/null.  Values are flattened to "a.b.c" -> number and
+// "a.b[i][j]" -> number.
+// ---------------------------------------------------------------------------
+namespace {
+
+struct JsonReader {
+    const std::string &s;
+    size_t i = 0;
+    std::map<std::string, double> nums;
+    explicit JsonReader(const std::string &t) : s(t) {}
+
+    void ws()
+    {
+        while (i < s.size() && std::isspace(static_cast<unsigned char>(s[i])))
+            ++i;
+    }
+    bool lit(const char *w)
+    {
+        size_t n = std::char_traits<char>::length(w);
+        if (s.compare(i, n, w) == 0) {
+            i += n;
+            return true;
+        }
+        return false;
+    }
+    bool str(std::string *out)
+    {
+        ws();
+        if (i >= s.size() || s[i] != '"')
+            return false;
+        ++i;
+        std::string r;
+        while (i < s.size() && s[i] != '"') {
+            if (s[i] == '\\') {
+                if (i + 1 >= s.size())
+                    return false;
+                r.push_back(s[i + 1]);
+                i += 2;
+            } else {
+                r.push_back(s[i++]);
+            }
+        }
+        if (i >= s.size())
+            return false;
+        ++i;
+        *out = r;
+        return true;
+    }
+    bool value(const std::string &path, int depth)
+    {
+        if (depth > 16)
+            return false;
+        ws();
+        if (i >= s.size())
+            return false;
+        const char c = s[i];
+        if (c == '{') {
+            ++i;
+            ws();
+            if (i < s.size() && s[i] == '}') {
+                ++i;
+                return true;
+            }
+            for (;;) {
+                std::string k;
+                if (!str(&k))
+                    return false;
+                ws();
+                if (i >= s.size() || s[i] != ':')
+                    return false;
+                ++i;
+                if (!value(path.empty() ? k : path + "." + k, depth + 1))
+                    return false;
+                ws();
+                if (i < s.size() && s[i] == ',') {
+                    ++i;
+                    continue;
+                }
+                if (i < s.size() && s[i] == '}') {
+                    ++i;
+                    return true;
+                }
+                return false;
+            }
+        }
+        if (c == '[') {
+            ++i;
+            ws();
+            if (i < s.size() && s[i] == ']') {
+                ++i;
+                return true;
+            }
+            for (int idx = 0;; ++idx) {
+                if (!value(path + "[" + std::to_string(idx) + "]", depth + 1))
+                    return false;
+                ws();
+                if (i < s.size() && s[i] == ',') {
+                    ++i;
+                    continue;
+                }
+                if (i < s.size() && s[i] == ']') {
+                    ++i;
+                    return true;
+                }
+                return false;
+            }
+        }
+        if (c == '"') {
+            std::string tmp;
+            return str(&tmp);
+        }
+        if (lit("true")) {
+            nums[path] = 1.0;
+            return true;
+        }
+        if (lit("false")) {
+            nums[path] = 0.0;
+            return true;
+        }
+        if (lit("null"))
+            return true;
+        const char *begin = s.c_str() + i;
+        char *end = nullptr;
+        const double v = std::strtod(begin, &end);
+        if (end == begin)
+            return false;
+        i += static_cast<size_t>(end - begin);
+        nums[path] = v;
+        return true;
+    }
+};
+
+}  // namespace
+
+bool parse_calibration(const std::string &text, Calibration *out)
+{
+    JsonReader r(text);
+    if (!r.value("", 0))
+        return false;
+    r.ws();
+    if (r.i != text.size())
+        return false;
+    Calibration c;
+    auto get = [&](const char *k, double *dst) {
+        auto it = r.nums.find(k);
+        if (it != r.nums.end())
+            *dst = it->second;
+    };
+    if (r.nums.find("version") == r.nums.end())
+        return false;
+    get("stream_gbs", &c.stream_gbs);
+    get("per_cu_gbs", &c.per_cu_gbs);
+    get("launch_us", &c.launch_us);
+    get("exchange_us", &c.exchange_us);
+    get("reread_hit_l2", &c.reread_hit_l2);
+    const char *effs[3] = {"single_eff", "reread_eff", "split_eff"};
+    double(*dst[3])[3][2] = {&c.single_eff, &c.reread_eff, &c.split_eff};
+    for (int k = 0; k < 3; ++k)
+        for (int op = 0; op < 3; ++op)
+            for (int dt = 0; dt < 2; ++dt)
+                get((std::string(effs[k]) + "[" + std::to_string(op) + "][" + std::to_string(dt) + "]").c_str(),
+                    &(*dst[k])[op][dt]);
+    double cus = -1;
+    get("device.cus", &cus);
+    if (cus > 0) {
+        c.has_device = true;
+        c.device.cus = static_cast<int>(cus);
+        get("device.xcds", &cus);
+        c.device.xcds = std::max(1, static_cast<int>(cus));
+        get("device.clock_ghz", &c.device.clock_ghz);
+        get("device.hbm_peak_gbs", &c.device.hbm_peak_gbs);
+        get("device.l2_bytes_per_xcd", &c.device.l2_bytes_per_xcd);
+        get("device.mall_bytes", &c.device.mall_bytes);
+    }
+    c.loaded = true;
+    *out = c;
+    return true;
+}
+
+}  // namespace credit

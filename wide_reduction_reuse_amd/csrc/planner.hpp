@@ -1,0 +1,116 @@
+// Host-only planner: which tiles can hold a row (or slice) on chip, and the
+// cost model that picks among path 1 (one owner per row), path 2 (P workgroups
+// per row) and path 3 (reread).  No HIP calls: everything here is arithmetic on
+// shapes, tile ladders and a device/calibration description, so it runs and is
+// tested without a GPU.
+//
+// Cost model: CREDIT paper, Sec. III-D.  Eq. 3 gives legality (the retained
+// slice plus fixed scratch must fit the per-workgroup on-chip budget); Eq. 7
+// prices the avoided reread at the bandwidth the baseline actually achieves,
+// T_save = (b_reread / b_B) * T_B; Eq. 8 counts sequential cluster waves
+// W = ceil(M / floor(S / P)) and the replay and exchange times; Eq. 9 takes
+// dT = T_save - T_ctrl - T_replay - T_deposit - T_DSM.
+#pragma once
+
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+namespace credit {
+
+enum PathId { kPathAuto = 0, kPathSingle = 1, kPathSplit = 2, kPathReread = 3 };
+
+struct TileSpec {
+    int kind = 0;   // KernelKind
+    int block = 0;  // threads per row owner (64: one wave per row)
+    int items = 0;  // vectors per thread (held) or per step (reread)
+    int vb = 16;    // bytes per access
+};
+
+// What the planner knows about the device.  Defaults describe an MI355X.
+struct DeviceModel {
+    int cus = 256;
+    int xcds = 8;
+    double clock_ghz = 2.4;
+    double hbm_peak_gbs = 8000.0;
+    double l2_bytes_per_xcd = 4.0 * 1024 * 1024;
+    double mall_bytes = 256.0 * 1024 * 1024;
+    double lds_bytes_per_cu = 160.0 * 1024;
+    double vgpr_bytes_per_cu = 512.0 * 1024;
+};
+
+// Measured quantities (from the calibration file); negative = not measured.
+struct Calibration {
+    bool loaded = false;
+    double stream_gbs = -1.0;       // achieved read+write streaming bandwidth (copy kernel)
+    double per_cu_gbs = -1.0;       // bandwidth one busy CU sustains
+    double launch_us = -1.0;        // fixed cost of a launch (empty grid time)
+    double exchange_us = -1.0;      // one split-row exchange round (control kernel excess)
+    double reread_hit_l2 = -1.0;    // fraction of a reread served on chip when the working set fits L2
+    // per-(op, dtype) multipliers on the streaming time, fitted to path-1 and path-3 timings
+    double single_eff[3][2] = {{-1, -1}, {-1, -1}, {-1, -1}};
+    double reread_eff[3][2] = {{-1, -1}, {-1, -1}, {-1, -1}};
+    double split_eff[3][2] = {{-1, -1}, {-1, -1}, {-1, -1}};
+    DeviceModel device;
+    bool has_device = false;
+};
+
+struct PlanRequest {
+    int op = 0;  // credit_op_t
+    int dt = 0;  // credit_dtype_t
+    int64_t rows = 0;
+    int64_t cols = 0;
+};
+
+struct PathEstimate {
+    bool legal = false;
+    int split_p = 1;
+    TileSpec tile;
+    double us = -1.0;
+    // model terms, kept for reporting and tests
+    double t_stream_us = 0.0;
+    double t_save_us = 0.0;
+    double t_ctrl_us = 0.0;
+    double waves = 0.0;
+};
+
+struct Plan {
+    int path = kPathSingle;
+    int split_p = 1;
+    TileSpec tile;
+    PathEstimate est[3];  // paths 1..3
+};
+
+int elem_bytes(int dt);
+int n_params(int op);
+int stats_per_partial(int op);  // q: scalars exchanged per partial
+
+// Bytes per global access for a row of `cols` elements: 16 when the row's byte
+// length is a multiple of 16 (rows stay 16-byte aligned), else one element.
+int vec_bytes_for(int dt, int64_t cols);
+
+// Tile ladders, mirroring the compiled instantiations.
+const std::vector<TileSpec> &tiles_for(int kind, int vb_is_16);
+
+// Path 1: the tile that holds a row of `cols`, or false if none can.
+bool single_tile(int dt, int64_t cols, TileSpec *out);
+// Path 2: the tile that holds a 1/p slice, or false if none can.
+bool split_tile(int dt, int64_t cols, int p, TileSpec *out);
+// Path 3: always possible.
+TileSpec reread_tile(int dt, int64_t cols);
+
+// Retained bytes per workgroup for a held tile (Eq. 3's S_CTA) and the budget.
+double tile_capacity_bytes(const TileSpec &t);
+double onchip_budget_bytes(const DeviceModel &d);
+
+// Plan with the cost model; forced_path / forced_p restrict the choice
+// (0 = free).  Returns false if the forced choice is illegal for the shape.
+bool make_plan(const PlanRequest &req, const Calibration &cal, int forced_path, int forced_p, Plan *out);
+
+// Parse a calibration JSON document (the subset written by the calibration
+// script: one object of numbers and nested number arrays).  Returns false and
+// leaves *out untouched on any syntax or schema error.
+bool parse_calibration(const std::string &text, Calibration *out);
+
+}  // namespace credit
