@@ -1,23 +1,30 @@
 #!/usr/bin/env python3
 """Benchmark of the reduction-reuse hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--all FILE]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--all FILE] [--no-cpu]
 
-A step is one call of the operator through the C ABI with the selector on
-(CREDIT_PATH_AUTO: plan + the chosen kernel) over one batch of synthetic input
-that is already resident in HBM.  Before every step an untimed 1 GiB
-read-modify-write evicts L2 and the Infinity Cache, so the input is read from
-HBM.  Each launch is bracketed by HIP events on the stream it runs on; the
-flush queued ahead of it keeps host-side planning out of that interval.
+A step is one pass of the hot path over one batch of synthetic input that is
+already resident in HBM: the selector picks a plan for the shape
+(credit_select_path, host only) and the chosen kernel runs it through the C ABI
+(credit_run_plan_timed).  Before every step an untimed 1 GiB read-modify-write
+evicts L2 and the Infinity Cache, so the input is read from HBM.
+
+Timing: the library launches with hipExtLaunchKernel and a pair of HIP events
+per step, which take the begin and end timestamps of the kernel dispatch
+itself on the stream it runs on (the same interval rocprofv3's kernel trace
+reports), so the flush, host-side planning and launch latency are outside it.
 
 Prints one JSON line: metric, value (algorithmic GB/s = one read of x + one
-write of y + parameter vectors once, over the mean launch duration), the
+write of y + each parameter vector once, over the mean kernel duration), the
 roofline object for the kernel, and the CPU oracle's rate on the same workload.
-With --all FILE it also writes one JSON line per (workload, path) to FILE.
+With --all FILE it also writes one JSON line per (workload, path) and the
+streaming-copy ceiling to FILE.
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -33,6 +40,8 @@ HBM_PEAK_GBS = 8000.0
 DEFAULT_WORKLOAD = "layernorm_bf16_4096x8192"
 FLUSH_BYTES = 1 << 30
 PROFILES = os.path.join(ROOT, "profiles")
+CPU_BASELINE_SECONDS = 10.0
+METRIC = "achieved HBM GB/s (one read + one write) and % of MI355X peak per op/shape"
 
 
 def csrc_hash() -> str:
@@ -60,9 +69,43 @@ def load_traffic(workload: str):
     return e
 
 
+class HipEvents:
+    """Pairs of timing-enabled hipEvent_t from the HIP runtime torch loaded."""
+
+    def __init__(self, n: int):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.pairs = []
+        for _ in range(n):
+            a, b = ctypes.c_void_p(), ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(a)) or self.hip.hipEventCreate(ctypes.byref(b)):
+                raise RuntimeError("hipEventCreate failed")
+            self.pairs.append((a.value, b.value))
+
+    def elapsed_ms(self, i: int) -> float:
+        a, b = self.pairs[i]
+        if self.hip.hipEventSynchronize(b):
+            raise RuntimeError("hipEventSynchronize failed")
+        ms = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b):
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+    def close(self):
+        for a, b in self.pairs:
+            self.hip.hipEventDestroy(a)
+            self.hip.hipEventDestroy(b)
+        self.pairs = []
+
+
 def upload(inp: W.HostInputs):
     import numpy as np
     import torch
+
     def dev(a):
         if a is None:
             return None
@@ -72,46 +115,59 @@ def upload(inp: W.HostInputs):
     return dev(inp.x), dev(inp.gamma), dev(inp.beta)
 
 
-def time_launches(fn, steps: int, warmup: int, flush_buf):
-    """Run fn() warmup + steps times, each after an untimed cache flush;
-    return (per-launch event durations in ms, wall seconds of the timed loop)."""
+def time_launches(launch, steps: int, warmup: int, flush_buf):
+    """Call launch(start_event, stop_event) warmup + steps times, each after an
+    untimed cache flush; return per-step kernel durations (ms) and the wall
+    seconds of the timed loop."""
     import torch
     from wide_reduction_reuse_amd import credit as C
-    for _ in range(warmup):
-        C.credit_flush(flush_buf)
-        fn()
-    torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    t0 = time.perf_counter()
-    for i in range(steps):
-        C.credit_flush(flush_buf)
-        starts[i].record()
-        fn()
-        ends[i].record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    return [s.elapsed_time(e) for s, e in zip(starts, ends)], wall
+    ev = HipEvents(warmup + steps)
+    try:
+        for i in range(warmup):
+            C.credit_flush(flush_buf)
+            launch(*ev.pairs[i])
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(warmup, warmup + steps):
+            C.credit_flush(flush_buf)
+            launch(*ev.pairs[i])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        durs = [ev.elapsed_ms(i) for i in range(warmup, warmup + steps)]
+    finally:
+        ev.close()
+    return durs, wall
 
 
-def run_workload(w: W.Workload, path: str, split_p: int, steps: int, warmup: int, flush_buf, inputs=None):
+def summarize(durs, nbytes: int) -> dict:
+    s = sorted(durs)
+    mean_ms = sum(durs) / len(durs)
+    med_ms = s[len(s) // 2]
+    return {"mean_ms": mean_ms, "median_ms": med_ms, "min_ms": s[0], "max_ms": s[-1],
+            "gbs": nbytes / (mean_ms * 1e-3) / 1e9, "gbs_median": nbytes / (med_ms * 1e-3) / 1e9}
+
+
+def run_workload(w: W.Workload, path: str, split_p: int, steps: int, warmup: int, flush_buf, inputs=None,
+                 plan=None):
+    """Time one workload.  path 'auto' runs the selector every step; a forced
+    path (or an explicit plan) is planned once, as a caller forcing it would."""
     import torch
     from wide_reduction_reuse_amd import credit as C
     inp = W.generate(w) if inputs is None else inputs
     x, g, b = upload(inp)
     y = torch.empty_like(x)
+    if plan is None and path != "auto":
+        plan = C.credit_plan(w.op, w.dtype, w.rows, w.cols, path, split_p)
 
-    def step():
-        C.run(w.op, x, g, b, inp.eps, y=y, path=path, split_p=split_p)
+    def launch(e0, e1):
+        p = plan if plan is not None else C.credit_select_path(w.op, w.dtype, w.rows, w.cols)
+        C.credit_run_plan_timed(w.op, x, g, b, y, inp.eps, p, e0, e1)
 
-    durs, wall = time_launches(step, steps, warmup, flush_buf)
+    durs, wall = time_launches(launch, steps, warmup, flush_buf)
     C.credit_check_errors()
-    durs_sorted = sorted(durs)
-    mean_ms = sum(durs) / len(durs)
-    med_ms = durs_sorted[len(durs) // 2]
-    return {"mean_ms": mean_ms, "median_ms": med_ms, "min_ms": durs_sorted[0], "wall_s": wall,
-            "gbs": w.algorithmic_bytes() / (mean_ms * 1e-3) / 1e9,
-            "gbs_median": w.algorithmic_bytes() / (med_ms * 1e-3) / 1e9}
+    r = summarize(durs, w.algorithmic_bytes())
+    r["wall_s"] = wall
+    return r
 
 
 def copy_ceiling(nbytes: int, steps: int, warmup: int, flush_buf):
@@ -119,35 +175,54 @@ def copy_ceiling(nbytes: int, steps: int, warmup: int, flush_buf):
     from wide_reduction_reuse_amd import credit as C
     src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
     dst = torch.empty_like(src)
-    durs, _ = time_launches(lambda: C.credit_copy(src, dst), steps, warmup, flush_buf)
-    mean_ms = sum(durs) / len(durs)
-    return {"bytes": 2 * nbytes, "mean_ms": mean_ms, "gbs": 2 * nbytes / (mean_ms * 1e-3) / 1e9}
+    durs, _ = time_launches(lambda e0, e1: C.credit_copy(src, dst, e0, e1), steps, warmup, flush_buf)
+    r = summarize(durs, 2 * nbytes)
+    r["bytes"] = 2 * nbytes
+    return r
 
 
-def cpu_baseline(w: W.Workload, inp: W.HostInputs, repeats: int = 3):
-    """The oracle, untuned, on the host cores: median of `repeats` runs."""
+def cpu_baseline(w: W.Workload, inp: W.HostInputs, seconds: float = CPU_BASELINE_SECONDS):
+    """The oracle, untuned, on the host cores: repeated on the workload for
+    about `seconds` of CPU time (at least 3 runs; a run is the whole workload
+    when it takes under `seconds`, else the leading rows that fit), median."""
     import numpy as np
     import oracle
+
     def vals(a):
         if a is None:
             return None
         return oracle.bf16_bits_to_f64(a) if w.dtype == "bf16" else a.astype(np.float64)
-    x, g, b = vals(inp.x), vals(inp.gamma), vals(inp.beta)
-    times = []
-    for _ in range(repeats):
-        t0 = time.perf_counter()
+
+    def run(xs):
         if w.op == "softmax":
-            oracle.softmax(x)
+            oracle.softmax(xs)
         elif w.op == "layernorm":
-            oracle.layernorm(x, g, b, inp.eps)
+            oracle.layernorm(xs, g, b, inp.eps)
         else:
-            oracle.rmsnorm(x, g, inp.eps)
+            oracle.rmsnorm(xs, g, inp.eps)
+
+    g, b = vals(inp.gamma), vals(inp.beta)
+    rows = w.rows
+    x = vals(inp.x[:rows])
+    t0 = time.perf_counter()
+    run(x)
+    t1 = time.perf_counter() - t0
+    if t1 > seconds / 3:  # bound the sample: the leading rows that take ~seconds/3 per run
+        rows = max(1, int(w.rows * (seconds / 3) / t1))
+        x = vals(inp.x[:rows])
+    times = []
+    start = time.perf_counter()
+    while len(times) < 3 or time.perf_counter() - start < seconds:
+        t0 = time.perf_counter()
+        run(x)
         times.append(time.perf_counter() - t0)
     t = sorted(times)[len(times) // 2]
-    return {"value": round(w.algorithmic_bytes() / t / 1e9, 3), "unit": "GB/s",
-            "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": "the full %dx%d workload, double precision, median of %d runs (%.2f s each)"
-                      % (w.rows, w.cols, repeats, t)}
+    nbytes = rows * w.cols * 2 * w.elem_bytes + w.cols * w.elem_bytes * W.N_PARAMS[w.op]
+    return {"value": round(nbytes / t / 1e9, 3), "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": "%d of %d rows x %d cols, float64 oracle (OpenMP over rows), median of %d runs "
+                      "of %.4f s each over %.1f s" % (rows, w.rows, w.cols, len(times), t,
+                                                       time.perf_counter() - start)}
 
 
 def main(argv=None) -> int:
@@ -156,13 +231,13 @@ def main(argv=None) -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(W.NAMED))
-    ap.add_argument("--all", default=None, help="also time every workload and path; JSON lines to this file")
+    ap.add_argument("--all", default=None, help="also time every named workload and path; JSON lines to FILE")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     a = ap.parse_args(argv)
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: the row-wise operators shard by rows with no "
-              "exchange between GPUs, so a multi-GPU figure would be N independent copies of "
-              "this one; run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the row-wise operators shard by rows with no "
+              "exchange between GPUs, and this build runs on a single MI355X; use --gpus 1.",
+              file=sys.stderr)
         return 2
 
     import torch
@@ -177,10 +252,10 @@ def main(argv=None) -> int:
     inp = W.generate(w)
     plan = C.credit_select_path(w.op, w.dtype, w.rows, w.cols)
     r = run_workload(w, "auto", 0, a.steps, a.warmup, flush_buf, inputs=inp)
-    achieved = w.algorithmic_bytes() / (r["mean_ms"] * 1e-3) / 1e9
+    achieved = r["gbs"]
     traffic = load_traffic(a.workload)
     result = {
-        "metric": "achieved HBM GB/s (one read + one write) and % of MI355X peak per op/shape",
+        "metric": METRIC,
         "value": round(achieved, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -196,7 +271,9 @@ def main(argv=None) -> int:
                    "path": plan.path, "split_p": plan.split_p, "block_threads": plan.block_threads,
                    "items": plan.items, "accumulate": "f32", "algorithmic_bytes": w.algorithmic_bytes(),
                    "cache_flush_bytes_between_steps": FLUSH_BYTES,
-                   "median_ms": round(r["median_ms"], 5), "wall_s_timed_loop_incl_flush": round(r["wall_s"], 4)},
+                   "median_ms": round(r["median_ms"], 5), "min_ms": round(r["min_ms"], 5),
+                   "wall_s_timed_loop_incl_flush": round(r["wall_s"], 4),
+                   "timing": "hipExtLaunchKernel dispatch timestamps"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None if traffic is None else traffic["bytes_per_launch"]},
@@ -206,9 +283,12 @@ def main(argv=None) -> int:
 
     if a.all:
         with open(a.all, "w") as f:
-            cc = copy_ceiling(128 << 20, a.steps, a.warmup, flush_buf)
-            f.write(json.dumps({"kind": "copy_ceiling", **cc}) + "\n")
-            f.flush()
+            for mib in (128, 256, 1024):
+                cc = copy_ceiling(mib << 20, a.steps, a.warmup, flush_buf)
+                f.write(json.dumps({"kind": "copy_ceiling", **cc}) + "\n")
+                f.flush()
+                print("[all] copy %d MiB %.1f GB/s (%.4f ms)" % (mib, cc["gbs"], cc["mean_ms"]),
+                      file=sys.stderr, flush=True)
             for name in W.CONFIG_ORDER:
                 wk = W.NAMED[name]
                 inpk = W.generate(wk)

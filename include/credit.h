@@ -115,6 +115,16 @@ credit_status_t credit_select_path(credit_op_t op, credit_dtype_t dt, int64_t ro
                                    credit_plan_t *out);
 
 /*
+ * The plan the operator entry points use for `path` and `split_p` (the same
+ * arguments and rules as credit_softmax & co.; CREDIT_PATH_AUTO with
+ * split_p = 0 equals credit_select_path).  Returns CREDIT_ERR_ILLEGAL_PATH if
+ * the forced path or split cannot hold the row, CREDIT_ERR_INVALID_ARG for bad
+ * arguments.  Host-only, like credit_select_path.
+ */
+credit_status_t credit_make_plan(credit_op_t op, credit_dtype_t dt, int64_t rows, int64_t cols,
+                                 credit_path_t path, int32_t split_p, credit_plan_t *out);
+
+/*
  * Run one operator with an explicit plan (as returned by credit_select_path,
  * or hand-built for exhaustive timing).  op selects which of gamma/beta are
  * read (softmax: neither; RMSNorm: gamma).  Returns CREDIT_ERR_ILLEGAL_PATH if
@@ -124,6 +134,20 @@ credit_status_t credit_select_path(credit_op_t op, credit_dtype_t dt, int64_t ro
 credit_status_t credit_run_plan(credit_op_t op, const void *x, const void *gamma, const void *beta, void *y,
                                 int64_t rows, int64_t cols, float eps, credit_dtype_t dt,
                                 const credit_plan_t *plan, void *stream);
+
+/*
+ * credit_run_plan with timing: start_event receives the begin timestamp of the
+ * first kernel the plan launches and stop_event the end timestamp of the last
+ * (both are hipEvent_t created by the caller; the timestamps come from the
+ * kernel dispatches, so hipEventElapsedTime(start, stop) is device execution
+ * time without queueing or launch latency).  Both events are required;
+ * rows == 0 returns CREDIT_ERR_INVALID_ARG because nothing would be timed.
+ * Otherwise identical to credit_run_plan.
+ */
+credit_status_t credit_run_plan_timed(credit_op_t op, const void *x, const void *gamma, const void *beta,
+                                      void *y, int64_t rows, int64_t cols, float eps, credit_dtype_t dt,
+                                      const credit_plan_t *plan, void *start_event, void *stop_event,
+                                      void *stream);
 
 /*
  * Work-free control kernel (Sec. III-D, the control that isolates launch,
@@ -136,11 +160,14 @@ credit_status_t credit_control(credit_op_t op, int64_t rows, int64_t cols, credi
 
 /*
  * Measurement helpers.  credit_copy: 128-bit streaming copy of `bytes` bytes
- * (a multiple of 16), the achievable read+write ceiling.  credit_flush: a
- * read-modify-write pass over `bytes` bytes of `buf` to evict L2 and the
- * Infinity Cache between timed runs.  Both are asynchronous on `stream`.
+ * (a multiple of 16), the achievable read+write ceiling; start_event and
+ * stop_event (hipEvent_t, each may be NULL) receive the copy kernel's begin and
+ * end timestamps.  credit_flush: a read-modify-write pass over `bytes` bytes of
+ * `buf` to evict L2 and the Infinity Cache between timed runs.  Both are
+ * asynchronous on `stream`.
  */
-credit_status_t credit_copy(const void *src, void *dst, int64_t bytes, void *stream);
+credit_status_t credit_copy(const void *src, void *dst, int64_t bytes, void *start_event, void *stop_event,
+                            void *stream);
 credit_status_t credit_flush(void *buf, int64_t bytes, void *stream);
 
 /*

@@ -97,12 +97,24 @@ def test_run_plan_validation():
     assert L.credit_run_plan(0, A, None, None, B, 4, 4096, 0.0, 0, ctypes.byref(plan), None) == 4
 
 
+def test_run_plan_timed_validation():
+    L = C.lib()
+    E1, E2 = ctypes.c_void_p(0x1000), ctypes.c_void_p(0x2000)
+    plan = C.Plan.make(C.PATH_SINGLE_WG, 1, 64, 1, 16)
+    # both events are required, and an empty launch cannot be timed
+    assert L.credit_run_plan_timed(0, A, None, None, B, 4, 64, 0.0, 0, ctypes.byref(plan), None, E2, None) == 1
+    assert L.credit_run_plan_timed(0, A, None, None, B, 4, 64, 0.0, 0, ctypes.byref(plan), E1, None, None) == 1
+    assert L.credit_run_plan_timed(0, A, None, None, B, 0, 64, 0.0, 0, ctypes.byref(plan), E1, E2, None) == 1
+    assert L.credit_run_plan_timed(0, MIS, None, None, B, 4, 64, 0.0, 0, ctypes.byref(plan), E1, E2, None) == 3
+    assert L.credit_run_plan_timed(0, A, None, None, B, 4, 1024, 0.0, 0, ctypes.byref(plan), E1, E2, None) == 4
+
+
 def test_misc_entry_points_validate():
     L = C.lib()
-    assert L.credit_copy(None, B, 16, None) == 1
-    assert L.credit_copy(A, B, 15, None) == 1
-    assert L.credit_copy(MIS, B, 16, None) == 3
-    assert L.credit_copy(A, B, 0, None) == 0
+    assert L.credit_copy(None, B, 16, None, None, None) == 1
+    assert L.credit_copy(A, B, 15, None, None, None) == 1
+    assert L.credit_copy(MIS, B, 16, None, None, None) == 3
+    assert L.credit_copy(A, B, 0, None, None, None) == 0
     assert L.credit_flush(None, 16, None) == 1
     assert L.credit_flush(A, 0, None) == 0
     plan = C.Plan.make(C.PATH_SINGLE_WG, 1, 64, 1, 16)
@@ -142,3 +154,20 @@ def test_calibration_loader(tmp_path):
     assert L.credit_load_calibration(None) == 0
     fast = C.credit_select_path("softmax", "f32", 4096, 4096).predicted_us[0]
     assert slow > fast  # 1000 GB/s calibrated streaming is slower than the default model
+
+
+def test_make_plan_matches_selector_and_honours_forced_paths():
+    for op, dt, rows, cols in [("softmax", "f32", 64, 4096), ("layernorm", "bf16", 4096, 8192),
+                               ("rmsnorm", "bf16", 1024, 65536), ("softmax", "f32", 256, 262144)]:
+        a = C.credit_select_path(op, dt, rows, cols).as_dict()
+        b = C.credit_plan(op, dt, rows, cols).as_dict()
+        assert a == b
+    p = C.credit_plan("softmax", "f32", 256, 262144, "split", 8)
+    assert p.path == C.PATH_SPLIT_ROW and p.split_p == 8
+    p = C.credit_plan("layernorm", "bf16", 4096, 8192, "reread")
+    assert p.path == C.PATH_REREAD and p.split_p == 1
+    with pytest.raises(C.CreditError) as ei:
+        C.credit_plan("softmax", "f32", 256, 262144, "single")
+    assert ei.value.status == 4
+    assert C.lib().credit_make_plan(0, 0, 4, 64, 2, 3, ctypes.byref(C.Plan())) == 1
+    assert C.lib().credit_make_plan(0, 0, 4, 64, 0, 0, None) == 1

@@ -98,9 +98,9 @@ def _tile_cases():
     cases = []
     ladders = {
         "wave": [(64, it) for it in (1, 2, 4, 8, 16)],
-        "wg": [(256, it) for it in (2, 4, 8, 16)] + [(512, it) for it in (4, 8, 16)] +
-              [(1024, it) for it in (4, 8, 16)],
-        "split": [(256, 8), (256, 16), (512, 8), (512, 16), (1024, 4), (1024, 8), (1024, 16)],
+        "wg": [(128, it) for it in (4, 8, 16)] + [(256, it) for it in (2, 4, 8, 16)] +
+              [(512, it) for it in (4, 8, 16)] + [(1024, it) for it in (4, 8, 16)],
+        "split": [(256, 8), (256, 16), (512, 4), (512, 8), (512, 16), (1024, 4), (1024, 8), (1024, 16)],
         "reread": [(256, 4), (512, 4), (1024, 4)],
     }
     for op in W.OPS:

@@ -26,8 +26,8 @@ PATHS = {"auto": 0, "single": 1, "split": 2, "reread": 3}
 OPS = {"softmax": 0, "layernorm": 1, "rmsnorm": 2}
 DTYPES = {"f32": 0, "bf16": 1}
 
-EXPORTED = ["credit_softmax", "credit_layernorm", "credit_rmsnorm", "credit_select_path",
-            "credit_run_plan", "credit_control", "credit_copy", "credit_flush",
+EXPORTED = ["credit_softmax", "credit_layernorm", "credit_rmsnorm", "credit_select_path", "credit_make_plan",
+            "credit_run_plan", "credit_run_plan_timed", "credit_control", "credit_copy", "credit_flush",
             "credit_load_calibration", "credit_check_errors", "credit_status_str", "credit_version"]
 
 
@@ -65,6 +65,12 @@ def lib() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise RuntimeError("libcredit.so is not built (run `python -m wide_reduction_reuse_amd.build`); "
                            "there is no fallback implementation")
+    # torch bundles its own HIP runtime under the same soname; loading torch
+    # first makes libcredit.so bind to that one copy rather than a second one
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     L = ctypes.CDLL(LIB_PATH)
     vp, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
     sig = {
@@ -72,9 +78,11 @@ def lib() -> ctypes.CDLL:
         "credit_layernorm": [vp, vp, vp, vp, i64, i64, f32, i32, i32, i32, vp],
         "credit_rmsnorm": [vp, vp, vp, i64, i64, f32, i32, i32, i32, vp],
         "credit_select_path": [i32, i32, i64, i64, ctypes.POINTER(Plan)],
+        "credit_make_plan": [i32, i32, i64, i64, i32, i32, ctypes.POINTER(Plan)],
         "credit_run_plan": [i32, vp, vp, vp, vp, i64, i64, f32, i32, ctypes.POINTER(Plan), vp],
+        "credit_run_plan_timed": [i32, vp, vp, vp, vp, i64, i64, f32, i32, ctypes.POINTER(Plan), vp, vp, vp],
         "credit_control": [i32, i64, i64, i32, ctypes.POINTER(Plan), vp],
-        "credit_copy": [vp, vp, i64, vp],
+        "credit_copy": [vp, vp, i64, vp, vp, vp],
         "credit_flush": [vp, i64, vp],
         "credit_load_calibration": [ctypes.c_char_p],
         "credit_check_errors": [vp],
@@ -170,11 +178,31 @@ def credit_select_path(op, dtype, rows: int, cols: int) -> Plan:
     return p
 
 
+def credit_plan(op, dtype, rows: int, cols: int, path="auto", split_p: int = 0) -> Plan:
+    """credit_make_plan: the plan the entry points use for a (possibly forced) path."""
+    p = Plan()
+    op = OPS[op] if isinstance(op, str) else int(op)
+    dt = DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
+    _check(lib().credit_make_plan(op, dt, rows, cols, _path(path), split_p, ctypes.byref(p)), "credit_make_plan")
+    return p
+
+
 def credit_run_plan(op, x, gamma, beta, y, eps: float, plan: Plan, stream=None):
     op = OPS[op] if isinstance(op, str) else int(op)
     rows, cols = _shape2d(x)
     _check(lib().credit_run_plan(op, _ptr(x), _ptr(gamma), _ptr(beta), _ptr(y), rows, cols, float(eps),
                                  _dtype_code(x), ctypes.byref(plan), _stream(stream)), "credit_run_plan")
+    return y
+
+
+def credit_run_plan_timed(op, x, gamma, beta, y, eps: float, plan: Plan, start_event: int, stop_event: int,
+                          stream=None):
+    """start_event / stop_event: raw hipEvent_t handles (integers)."""
+    op = OPS[op] if isinstance(op, str) else int(op)
+    rows, cols = _shape2d(x)
+    _check(lib().credit_run_plan_timed(op, _ptr(x), _ptr(gamma), _ptr(beta), _ptr(y), rows, cols, float(eps),
+                                       _dtype_code(x), ctypes.byref(plan), ctypes.c_void_p(start_event),
+                                       ctypes.c_void_p(stop_event), _stream(stream)), "credit_run_plan_timed")
     return y
 
 
@@ -184,9 +212,11 @@ def credit_control(op, rows: int, cols: int, dtype, plan: Plan, stream=None) -> 
     _check(lib().credit_control(op, rows, cols, dt, ctypes.byref(plan), _stream(stream)), "credit_control")
 
 
-def credit_copy(src, dst, stream=None) -> None:
+def credit_copy(src, dst, start_event: Optional[int] = None, stop_event: Optional[int] = None,
+                stream=None) -> None:
     nbytes = src.numel() * src.element_size()
-    _check(lib().credit_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream)), "credit_copy")
+    _check(lib().credit_copy(_ptr(src), _ptr(dst), nbytes, ctypes.c_void_p(start_event),
+                             ctypes.c_void_p(stop_event), _stream(stream)), "credit_copy")
 
 
 def credit_flush(buf, stream=None) -> None:

@@ -1,5 +1,6 @@
 // C ABI of libcredit.so (declared in include/credit.h): argument validation,
 // planning, the per-(device, stream) split-row scratch, and kernel launches.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -93,44 +94,53 @@ bool log_enabled()
 
 // ---------------------------------------------------------------------------
 // split-row scratch, one per (device, stream)
+//
+// The host mirrors the device ticket counter (next_ticket) and hands out the
+// exchange tags (next_tag); both advance only after a launch was enqueued, and
+// launches on one stream run in enqueue order, so each launch's ticket_base is
+// the device counter's value when it starts and its tags were never written
+// before.  Tag 0 is never used (the words start at zero); when the tags would
+// wrap, the words are cleared first.
 // ---------------------------------------------------------------------------
-constexpr size_t kSlotWords = size_t(1) << 20;  // 8 MiB of exchange words
+constexpr int64_t kSlotWords = INT64_C(1) << 17;  // 1 MiB of exchange words
 constexpr uint32_t kSpinLimit = 1u << 20;
 
 struct Scratch {
     SplitCtl *ctl = nullptr;
     uint64_t *slots = nullptr;
+    uint32_t next_ticket = 0;
+    uint32_t next_tag = 1;
 };
 std::map<std::pair<int, hipStream_t>, Scratch> g_scratch;
 
-credit_status_t get_scratch(hipStream_t s, Scratch *out)
+// Returns the scratch of (current device, s), allocating it on first use.
+// Caller holds g_mu.
+credit_status_t get_scratch_locked(hipStream_t s, Scratch **out)
 {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess)
         return CREDIT_ERR_HIP;
-    std::lock_guard<std::mutex> lk(g_mu);
     auto key = std::make_pair(dev, s);
     auto it = g_scratch.find(key);
     if (it != g_scratch.end()) {
-        *out = it->second;
+        *out = &it->second;
         return CREDIT_OK;
     }
     void *mem = nullptr;
     const size_t bytes = sizeof(SplitCtl) + kSlotWords * sizeof(uint64_t);
-    if (hipMalloc(&mem, bytes) != hipSuccess)
+    if (hipMalloc(&mem, bytes) != hipSuccess) {
+        (void)hipGetLastError();
         return CREDIT_ERR_HIP;
-    SplitCtl init;
-    std::memset(&init, 0, sizeof(init));
-    init.epoch = 1;  // slot words start at tag 0, which no launch uses
-    if (hipMemset(mem, 0, bytes) != hipSuccess || hipMemcpy(mem, &init, sizeof(init), hipMemcpyHostToDevice) != hipSuccess) {
+    }
+    if (hipMemset(mem, 0, bytes) != hipSuccess) {
+        (void)hipGetLastError();
         (void)hipFree(mem);
         return CREDIT_ERR_HIP;
     }
     Scratch sc;
     sc.ctl = static_cast<SplitCtl *>(mem);
     sc.slots = reinterpret_cast<uint64_t *>(static_cast<char *>(mem) + sizeof(SplitCtl));
-    g_scratch[key] = sc;
-    *out = sc;
+    *out = &(g_scratch[key] = sc);
     return CREDIT_OK;
 }
 
@@ -189,10 +199,19 @@ credit_status_t check_path_args(int path, int split_p)
 // ---------------------------------------------------------------------------
 constexpr int64_t kMaxGridWgs = INT64_C(1) << 30;
 
-credit_status_t launch_raw(const KernelEntry *k, uint32_t grid, uint32_t block, void *arg, hipStream_t s)
+// Optional timing events: `start` takes the first kernel's begin timestamp and
+// `stop` the last kernel's end timestamp (hipExtLaunchKernel records them from
+// the dispatch itself, so the interval holds no queueing or dispatch latency).
+struct LaunchEvents {
+    hipEvent_t start = nullptr;
+    hipEvent_t stop = nullptr;
+};
+
+credit_status_t launch_raw(const KernelEntry *k, uint32_t grid, uint32_t block, void *arg, hipStream_t s,
+                           hipEvent_t ev_start, hipEvent_t ev_stop)
 {
     void *args[] = {arg};
-    const hipError_t e = hipLaunchKernel(k->fn, dim3(grid), dim3(block), args, 0, s);
+    const hipError_t e = hipExtLaunchKernel(k->fn, dim3(grid), dim3(block), args, 0, s, ev_start, ev_stop, 0);
     if (e != hipSuccess) {
         (void)hipGetLastError();
         return CREDIT_ERR_HIP;
@@ -200,7 +219,7 @@ credit_status_t launch_raw(const KernelEntry *k, uint32_t grid, uint32_t block, 
     return CREDIT_OK;
 }
 
-credit_status_t launch_rowwise(const KernelEntry *k, const RowArgs &a0, hipStream_t s)
+credit_status_t launch_rowwise(const KernelEntry *k, const RowArgs &a0, hipStream_t s, const LaunchEvents &ev)
 {
     const int64_t rows_per_wg = k->kind == kKindWave ? kWaveRowsPerWg : 1;
     const int block = k->kind == kKindWave ? 64 * kWaveRowsPerWg : k->block;
@@ -214,44 +233,97 @@ credit_status_t launch_rowwise(const KernelEntry *k, const RowArgs &a0, hipStrea
         a.y = static_cast<char *>(a0.y) + off;
         a.rows = n;
         const int64_t grid = (n + rows_per_wg - 1) / rows_per_wg;
-        const credit_status_t st = launch_raw(k, static_cast<uint32_t>(grid), block, &a, s);
+        const credit_status_t st = launch_raw(k, static_cast<uint32_t>(grid), block, &a, s,
+                                              r0 == 0 ? ev.start : nullptr,
+                                              r0 + n >= a0.rows ? ev.stop : nullptr);
         if (st != CREDIT_OK)
             return st;
     }
     return CREDIT_OK;
 }
 
-credit_status_t launch_split(const KernelEntry *k, const RowArgs &a0, int p, int q, hipStream_t s)
+// Workgroups of kernel `fn` (block threads) one CU holds at once; cached.
+credit_status_t occupancy(const KernelEntry *k, int *out)
 {
-    Scratch sc;
-    credit_status_t st = get_scratch(s, &sc);
-    if (st != CREDIT_OK)
-        return st;
+    static std::map<const void *, int> cache;
+    {
+        std::lock_guard<std::mutex> lk(g_mu);
+        auto it = cache.find(k->fn);
+        if (it != cache.end()) {
+            *out = it->second;
+            return CREDIT_OK;
+        }
+    }
     int occ = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k->fn, k->block, 0) != hipSuccess) {
         (void)hipGetLastError();
         return CREDIT_ERR_HIP;
     }
-    DeviceModel d;
-    {
-        std::lock_guard<std::mutex> lk(g_mu);
-        d = device_model_locked();
-    }
-    if (static_cast<int64_t>(occ) * d.cus < p)
+    std::lock_guard<std::mutex> lk(g_mu);
+    cache[k->fn] = occ;
+    *out = occ;
+    return CREDIT_OK;
+}
+
+credit_status_t launch_split(const KernelEntry *k, const RowArgs &a0, int p, int q, hipStream_t s,
+                             const LaunchEvents &ev)
+{
+    int occ = 0;
+    credit_status_t st = occupancy(k, &occ);
+    if (st != CREDIT_OK)
+        return st;
+    std::lock_guard<std::mutex> lk(g_mu);
+    const DeviceModel d = device_model_locked();
+    const int64_t resident = static_cast<int64_t>(occ) * d.cus;
+    if (resident < p)
         return CREDIT_ERR_NOT_CORESIDENT;
-    const int64_t chunk_rows = static_cast<int64_t>(kSlotWords) / (static_cast<int64_t>(p) * q);
-    for (int64_t r0 = 0; r0 < a0.rows; r0 += chunk_rows) {
+    Scratch *sc = nullptr;
+    st = get_scratch_locked(s, &sc);
+    if (st != CREDIT_OK)
+        return st;
+    // persistent clusters: as many as the device holds at once and the
+    // exchange words cover, never more than there are rows
+    const int64_t clusters = std::min({resident / p, kSlotWords / (INT64_C(2) * p * q), a0.rows});
+    const int64_t max_iters = INT64_C(1) << 30;  // row iterations per launch (tag range)
+    const int64_t rows_per_launch = clusters * max_iters;
+    const int64_t eb = elem_bytes(k->dt);
+    for (int64_t r0 = 0; r0 < a0.rows; r0 += rows_per_launch) {
+        const int64_t n = std::min(rows_per_launch, a0.rows - r0);
+        const int64_t c = std::min(clusters, n);
+        const uint32_t iters = static_cast<uint32_t>((n + c - 1) / c);
+        if (static_cast<uint64_t>(sc->next_tag) + iters > UINT64_C(0xFFFFFFFF)) {
+            const KernelEntry *z = find_misc(-3);
+            uint64_t *slots = sc->slots;
+            int64_t nw = kSlotWords;
+            void *zargs[] = {&slots, &nw};
+            if (hipLaunchKernel(z->fn, dim3(static_cast<uint32_t>(kSlotWords / 256)), dim3(256), zargs, 0, s) !=
+                hipSuccess) {
+                (void)hipGetLastError();
+                return CREDIT_ERR_HIP;
+            }
+            sc->next_tag = 1;
+        }
         SplitArgs sa;
         sa.r = a0;
-        sa.ctl = sc.ctl;
-        sa.slots = sc.slots;
-        sa.row0 = r0;
+        const int64_t off = r0 * a0.cols * eb;
+        sa.r.x = a0.x == nullptr ? nullptr : static_cast<const char *>(a0.x) + off;
+        sa.r.y = a0.y == nullptr ? nullptr : static_cast<char *>(a0.y) + off;
+        sa.r.rows = n;
+        sa.ticket = &sc->ctl->ticket;
+        sa.error = &sc->ctl->error;
+        sa.slots = sc->slots;
         sa.p = p;
+        sa.clusters = static_cast<int32_t>(c);
+        sa.ticket_base = sc->next_ticket;
+        sa.tag_base = sc->next_tag;
         sa.spin_limit = kSpinLimit;
-        const int64_t n = std::min(chunk_rows, a0.rows - r0);
-        st = launch_raw(k, static_cast<uint32_t>(n * p), k->block, &sa, s);
+        const uint32_t grid = static_cast<uint32_t>(c * p);
+        st = launch_raw(k, grid, k->block, &sa, s, r0 == 0 ? ev.start : nullptr,
+                        r0 + n >= a0.rows ? ev.stop : nullptr);
         if (st != CREDIT_OK)
             return st;
+        sc->next_ticket += grid;
+        sc->next_tag += iters;
     }
     return CREDIT_OK;
 }
@@ -290,6 +362,9 @@ credit_status_t resolve_plan(int op, int dt, int64_t cols, const credit_plan_t &
         return CREDIT_ERR_UNSUPPORTED;
     if (need > static_cast<int64_t>(plan.block_threads) * plan.items)
         return CREDIT_ERR_ILLEGAL_PATH;
+    // a row or slice is one buffer descriptor: its byte length must fit 32 bits
+    if (kind != kKindReread && need * vb > INT64_C(0xFFFFFFFF))
+        return CREDIT_ERR_UNSUPPORTED;
     *out = k;
     *kind_out = kind;
     return CREDIT_OK;
@@ -309,7 +384,7 @@ void to_c_plan(const Plan &p, credit_plan_t *out)
 
 credit_status_t run_plan_checked(int op, const void *x, const void *g, const void *b, void *y, int64_t rows,
                                  int64_t cols, float eps, int dt, const credit_plan_t &plan, hipStream_t s,
-                                 bool control)
+                                 bool control, const LaunchEvents &ev = LaunchEvents{})
 {
     const KernelEntry *k = nullptr;
     int kind = 0;
@@ -336,8 +411,8 @@ credit_status_t run_plan_checked(int op, const void *x, const void *g, const voi
                      op, dt, static_cast<long long>(rows), static_cast<long long>(cols), plan.path, plan.split_p,
                      plan.block_threads, plan.items, k->vb, control ? " (control)" : "");
     if (kind == kKindSplit)
-        return launch_split(k, a, plan.split_p, stats_per_partial(op), s);
-    return launch_rowwise(k, a, s);
+        return launch_split(k, a, plan.split_p, stats_per_partial(op), s, ev);
+    return launch_rowwise(k, a, s, ev);
 }
 
 credit_status_t run_op(int op, const void *x, const void *g, const void *b, void *y, int64_t rows, int64_t cols,
@@ -417,6 +492,29 @@ credit_status_t credit_select_path(credit_op_t op, credit_dtype_t dt, int64_t ro
     return CREDIT_OK;
 }
 
+credit_status_t credit_make_plan(credit_op_t op, credit_dtype_t dt, int64_t rows, int64_t cols, credit_path_t path,
+                                 int32_t split_p, credit_plan_t *out)
+{
+    if (out == nullptr || op < 0 || op > 2 || (dt != CREDIT_F32 && dt != CREDIT_BF16) || rows < 0 || cols < 1)
+        return CREDIT_ERR_INVALID_ARG;
+    credit_status_t st = check_path_args(path, split_p);
+    if (st != CREDIT_OK)
+        return st;
+    std::lock_guard<std::mutex> lk(g_mu);
+    Calibration cal = g_cal;
+    cal.device = device_model_locked();
+    PlanRequest req;
+    req.op = op;
+    req.dt = dt;
+    req.rows = rows;
+    req.cols = cols;
+    Plan p;
+    if (!make_plan(req, cal, path, split_p <= 1 ? 0 : split_p, &p))
+        return CREDIT_ERR_ILLEGAL_PATH;
+    to_c_plan(p, out);
+    return CREDIT_OK;
+}
+
 credit_status_t credit_run_plan(credit_op_t op, const void *x, const void *gamma, const void *beta, void *y,
                                 int64_t rows, int64_t cols, float eps, credit_dtype_t dt,
                                 const credit_plan_t *plan, void *stream)
@@ -429,6 +527,26 @@ credit_status_t credit_run_plan(credit_op_t op, const void *x, const void *gamma
         return st;
     return run_plan_checked(op, x, gamma, beta, y, rows, cols, eps, dt, *plan, static_cast<hipStream_t>(stream),
                             false);
+}
+
+credit_status_t credit_run_plan_timed(credit_op_t op, const void *x, const void *gamma, const void *beta, void *y,
+                                      int64_t rows, int64_t cols, float eps, credit_dtype_t dt,
+                                      const credit_plan_t *plan, void *start_event, void *stop_event,
+                                      void *stream)
+{
+    if (plan == nullptr || start_event == nullptr || stop_event == nullptr)
+        return CREDIT_ERR_INVALID_ARG;
+    bool noop = false;
+    credit_status_t st = validate(op, x, gamma, beta, y, rows, cols, eps, dt, &noop);
+    if (st != CREDIT_OK)
+        return st;
+    if (noop)
+        return CREDIT_ERR_INVALID_ARG;  // nothing would be launched, so nothing could be timed
+    LaunchEvents ev;
+    ev.start = static_cast<hipEvent_t>(start_event);
+    ev.stop = static_cast<hipEvent_t>(stop_event);
+    return run_plan_checked(op, x, gamma, beta, y, rows, cols, eps, dt, *plan, static_cast<hipStream_t>(stream),
+                            false, ev);
 }
 
 credit_status_t credit_control(credit_op_t op, int64_t rows, int64_t cols, credit_dtype_t dt,
@@ -444,7 +562,8 @@ credit_status_t credit_control(credit_op_t op, int64_t rows, int64_t cols, credi
                             static_cast<hipStream_t>(stream), true);
 }
 
-credit_status_t credit_copy(const void *src, void *dst, int64_t bytes, void *stream)
+credit_status_t credit_copy(const void *src, void *dst, int64_t bytes, void *start_event, void *stop_event,
+                            void *stream)
 {
     if (src == nullptr || dst == nullptr || bytes < 0 || bytes % 16 != 0)
         return CREDIT_ERR_INVALID_ARG;
@@ -454,15 +573,16 @@ credit_status_t credit_copy(const void *src, void *dst, int64_t bytes, void *str
         return CREDIT_OK;
     const KernelEntry *k = find_misc(-1);
     int64_t n16 = bytes / 16;
-    const int64_t grid = std::min<int64_t>((n16 + 1023) / 1024, INT64_C(1) << 30);
+    const int64_t grid = std::min<int64_t>((n16 + 255) / 256, INT64_C(1) << 22);
     struct {
         const void *s;
         void *d;
         int64_t n;
     } a{src, dst, n16};
     void *args[] = {&a.s, &a.d, &a.n};
-    if (hipLaunchKernel(k->fn, dim3(static_cast<uint32_t>(grid)), dim3(256), args, 0,
-                        static_cast<hipStream_t>(stream)) != hipSuccess) {
+    if (hipExtLaunchKernel(k->fn, dim3(static_cast<uint32_t>(grid)), dim3(256), args, 0,
+                           static_cast<hipStream_t>(stream), static_cast<hipEvent_t>(start_event),
+                           static_cast<hipEvent_t>(stop_event), 0) != hipSuccess) {
         (void)hipGetLastError();
         return CREDIT_ERR_HIP;
     }
@@ -526,7 +646,7 @@ credit_status_t credit_check_errors(void *stream)
         auto it = g_scratch.find(std::make_pair(dev, s));
         if (it == g_scratch.end())
             return CREDIT_OK;
-        sc = it->second;
+        sc = it->second;  // the device pointers only
     }
     uint32_t err = 0;
     if (hipMemcpy(&err, &sc.ctl->error, sizeof(err), hipMemcpyDeviceToHost) != hipSuccess)

@@ -18,23 +18,22 @@ struct RowArgs {
 
 // Exchange control block (one per scratch); each counter on its own 128-byte line.
 struct SplitCtl {
-    uint32_t ticket;
+    uint32_t ticket;  // monotonic: every split workgroup takes one ticket when it starts
     uint32_t pad0[31];
-    uint32_t done;
+    uint32_t error;   // bit 0: a spin-wait gave up
     uint32_t pad1[31];
-    uint32_t epoch;
-    uint32_t pad2[31];
-    uint32_t error;  // bit 0: a spin-wait gave up
-    uint32_t pad3[31];
 };
 
 struct SplitArgs {
     RowArgs r;
-    SplitCtl *ctl;
-    uint64_t *slots;     // [rows in launch][P][Q] words {value bits | epoch << 32}
-    int64_t row0;        // first row of this launch
-    int32_t p;           // workgroups per row
-    uint32_t spin_limit; // polls before a wait gives up and flags ctl->error
+    uint32_t *ticket;      // &ctl->ticket
+    uint32_t *error;       // &ctl->error
+    uint64_t *slots;       // [clusters][2][P][Q] words {value bits | tag << 32}
+    int32_t p;             // workgroups per row
+    int32_t clusters;      // C: cluster k handles rows k, k + C, k + 2C, ...
+    uint32_t ticket_base;  // value of *ticket when this launch starts
+    uint32_t tag_base;     // row iteration i of this launch exchanges tag tag_base + i
+    uint32_t spin_limit;   // polls before a wait gives up and flags *error
 };
 
 constexpr int kMaxSplit = 8;

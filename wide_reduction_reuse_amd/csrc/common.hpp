@@ -45,45 +45,74 @@ template <> struct RawVec<2> {
     uint32_t w;
 };
 
-template <int VB>
-__device__ __forceinline__ RawVec<VB> load_vec(const void *p)
+// ---------------------------------------------------------------------------
+// Buffer accesses.  A row, slice or parameter vector is addressed through a
+// buffer descriptor whose base is its first byte and whose size is its length:
+// the lane offset is one VGPR, the per-vector step a scalar offset, and the
+// hardware range check makes every access past the end harmless (loads return
+// zero, stores are dropped), so tails need no branches.  The descriptor's
+// third dword 0x00020000 is the raw 32-bit-element format of the gfx9 family.
+// Cache policy: kStream marks the row data non-temporal (it is touched once),
+// kKeep leaves the parameter vectors, shared by every row, cacheable.
+// ---------------------------------------------------------------------------
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+constexpr int kKeep = 0;
+constexpr int kStream = 2;  // nt
+
+// `bytes` must fit in 32 bits; callers keep one descriptor per row or slice.
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes)
 {
-    RawVec<VB> r;
-    if constexpr (VB == 16) {
-        r.w = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
-    } else if constexpr (VB == 4) {
-        r.w = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(p));
-    } else {
-        r.w = __builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(p));
-    }
-    return r;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), static_cast<short>(0),
+                                             static_cast<int>(bytes), 0x00020000);
 }
 
-// Cached load, for parameter vectors (gamma, beta) shared by every row.
-template <int VB>
-__device__ __forceinline__ RawVec<VB> load_vec_cached(const void *p)
+// voff: the lane's whole byte offset into the buffer.  The scalar offset is
+// always the constant 0, for two reasons: the range check covers the VGPR
+// offset (plus the instruction's immediate) but not the scalar one, and on
+// gfx950 a 16-byte buffer store whose scalar offset is an SGPR was observed to
+// store data VGPRs that a VALU instruction right after it had already
+// overwritten (the compiler inserts the store-data wait state only for a
+// constant scalar offset).
+template <int VB, int POLICY>
+__device__ __forceinline__ RawVec<VB> buf_load(rsrc_t r, uint32_t voff)
 {
-    RawVec<VB> r;
+    RawVec<VB> v;
     if constexpr (VB == 16) {
-        r.w = *reinterpret_cast<const u32x4 *>(p);
+        v.w = __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(voff), 0, POLICY);
     } else if constexpr (VB == 4) {
-        r.w = *reinterpret_cast<const uint32_t *>(p);
+        v.w = __builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(voff), 0, POLICY);
     } else {
-        r.w = *reinterpret_cast<const uint16_t *>(p);
+        v.w = __builtin_amdgcn_raw_buffer_load_b16(r, static_cast<int>(voff), 0, POLICY);
     }
-    return r;
+    return v;
 }
 
-template <int VB>
-__device__ __forceinline__ void store_vec(void *p, const RawVec<VB> &r)
+template <int VB, int POLICY>
+__device__ __forceinline__ void buf_store(const RawVec<VB> &v, rsrc_t r, uint32_t voff)
 {
     if constexpr (VB == 16) {
-        __builtin_nontemporal_store(r.w, reinterpret_cast<u32x4 *>(p));
+        __builtin_amdgcn_raw_buffer_store_b128(v.w, r, static_cast<int>(voff), 0, POLICY);
     } else if constexpr (VB == 4) {
-        __builtin_nontemporal_store(r.w, reinterpret_cast<uint32_t *>(p));
+        __builtin_amdgcn_raw_buffer_store_b32(v.w, r, static_cast<int>(voff), 0, POLICY);
     } else {
-        __builtin_nontemporal_store(static_cast<uint16_t>(r.w), reinterpret_cast<uint16_t *>(p));
+        __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(v.w), r, static_cast<int>(voff), 0, POLICY);
     }
+}
+
+// Make a value the compiler treats as per-lane known to be wave-uniform.
+__device__ __forceinline__ int64_t uniform(int64_t v)
+{
+    const uint64_t u = static_cast<uint64_t>(v);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u >> 32));
+    return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// True in every lane iff `pred` holds in every active lane of the wave.
+__device__ __forceinline__ bool wave_all(bool pred)
+{
+    return __builtin_amdgcn_ballot_w64(!pred) == 0;
 }
 
 template <int VB> __device__ __forceinline__ uint32_t word(const RawVec<VB> &r, int i)

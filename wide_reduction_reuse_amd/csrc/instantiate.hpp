@@ -1,4 +1,5 @@
-// Instantiates every tile of the ladders in registry.hpp for one operator.
+// Instantiates every tile of the ladders in registry.hpp for one operator and
+// storage type, plus the work-free control twin of every split tile.
 #pragma once
 
 #include "kernels.hpp"
@@ -13,50 +14,36 @@ void register_op_dtype(std::vector<KernelEntry> &v)
     constexpr int VS = StorageTraits<T>::kBytes;  // one-element access
 #define CREDIT_K(kind, vb, block, items, ...) \
     v.push_back(KernelEntry{kind, OP, DT, vb, block, items, reinterpret_cast<const void *>(&__VA_ARGS__)})
-    // path 1a
-    CREDIT_K(kKindWave, VB, 64, 1, single_wave_kernel<OP, T, VB, 1>);
-    CREDIT_K(kKindWave, VB, 64, 2, single_wave_kernel<OP, T, VB, 2>);
-    CREDIT_K(kKindWave, VB, 64, 4, single_wave_kernel<OP, T, VB, 4>);
-    CREDIT_K(kKindWave, VB, 64, 8, single_wave_kernel<OP, T, VB, 8>);
-    CREDIT_K(kKindWave, VB, 64, 16, single_wave_kernel<OP, T, VB, 16>);
-    // path 1b
-    CREDIT_K(kKindWg, VB, 256, 2, single_wg_kernel<OP, T, VB, 256, 2>);
-    CREDIT_K(kKindWg, VB, 256, 4, single_wg_kernel<OP, T, VB, 256, 4>);
-    CREDIT_K(kKindWg, VB, 256, 8, single_wg_kernel<OP, T, VB, 256, 8>);
-    CREDIT_K(kKindWg, VB, 256, 16, single_wg_kernel<OP, T, VB, 256, 16>);
-    CREDIT_K(kKindWg, VB, 512, 4, single_wg_kernel<OP, T, VB, 512, 4>);
-    CREDIT_K(kKindWg, VB, 512, 8, single_wg_kernel<OP, T, VB, 512, 8>);
-    CREDIT_K(kKindWg, VB, 512, 16, single_wg_kernel<OP, T, VB, 512, 16>);
-    CREDIT_K(kKindWg, VB, 1024, 4, single_wg_kernel<OP, T, VB, 1024, 4>);
-    CREDIT_K(kKindWg, VB, 1024, 8, single_wg_kernel<OP, T, VB, 1024, 8>);
-    CREDIT_K(kKindWg, VB, 1024, 16, single_wg_kernel<OP, T, VB, 1024, 16>);
-    // path 2 and its work-free control
-    CREDIT_K(kKindSplit, VB, 256, 8, split_kernel<OP, T, VB, 256, 8, false>);
-    CREDIT_K(kKindSplit, VB, 256, 16, split_kernel<OP, T, VB, 256, 16, false>);
-    CREDIT_K(kKindSplit, VB, 512, 8, split_kernel<OP, T, VB, 512, 8, false>);
-    CREDIT_K(kKindSplit, VB, 512, 16, split_kernel<OP, T, VB, 512, 16, false>);
-    CREDIT_K(kKindSplit, VB, 1024, 4, split_kernel<OP, T, VB, 1024, 4, false>);
-    CREDIT_K(kKindSplit, VB, 1024, 8, split_kernel<OP, T, VB, 1024, 8, false>);
-    CREDIT_K(kKindSplit, VB, 1024, 16, split_kernel<OP, T, VB, 1024, 16, false>);
-    CREDIT_K(kKindControl, VB, 256, 8, split_kernel<OP, T, VB, 256, 8, true>);
-    CREDIT_K(kKindControl, VB, 256, 16, split_kernel<OP, T, VB, 256, 16, true>);
-    CREDIT_K(kKindControl, VB, 512, 8, split_kernel<OP, T, VB, 512, 8, true>);
-    CREDIT_K(kKindControl, VB, 512, 16, split_kernel<OP, T, VB, 512, 16, true>);
-    CREDIT_K(kKindControl, VB, 1024, 4, split_kernel<OP, T, VB, 1024, 4, true>);
-    CREDIT_K(kKindControl, VB, 1024, 8, split_kernel<OP, T, VB, 1024, 8, true>);
-    CREDIT_K(kKindControl, VB, 1024, 16, split_kernel<OP, T, VB, 1024, 16, true>);
-    // path 3
-    CREDIT_K(kKindReread, VB, 256, 4, reread_kernel<OP, T, VB, 256, 4>);
-    CREDIT_K(kKindReread, VB, 512, 4, reread_kernel<OP, T, VB, 512, 4>);
-    CREDIT_K(kKindReread, VB, 1024, 4, reread_kernel<OP, T, VB, 1024, 4>);
-    // one-element accesses
-    CREDIT_K(kKindWave, VS, 64, 4, single_wave_kernel<OP, T, VS, 4>);
-    CREDIT_K(kKindWave, VS, 64, 16, single_wave_kernel<OP, T, VS, 16>);
-    CREDIT_K(kKindWg, VS, 1024, 4, single_wg_kernel<OP, T, VS, 1024, 4>);
-    CREDIT_K(kKindWg, VS, 1024, 16, single_wg_kernel<OP, T, VS, 1024, 16>);
-    CREDIT_K(kKindSplit, VS, 1024, 16, split_kernel<OP, T, VS, 1024, 16, false>);
-    CREDIT_K(kKindControl, VS, 1024, 16, split_kernel<OP, T, VS, 1024, 16, true>);
-    CREDIT_K(kKindReread, VS, 256, 8, reread_kernel<OP, T, VS, 256, 8>);
+#define WAVE(it) CREDIT_K(kKindWave, VB, 64, it, single_wave_kernel<OP, T, VB, it>);
+#define WG(b, it) CREDIT_K(kKindWg, VB, b, it, single_wg_kernel<OP, T, VB, b, it>);
+#define SPLIT(b, it)                                                        \
+    CREDIT_K(kKindSplit, VB, b, it, split_kernel<OP, T, VB, b, it, false>); \
+    CREDIT_K(kKindControl, VB, b, it, split_kernel<OP, T, VB, b, it, true>);
+#define REREAD(b, it) CREDIT_K(kKindReread, VB, b, it, reread_kernel<OP, T, VB, b, it>);
+#define WAVE1E(it) CREDIT_K(kKindWave, VS, 64, it, single_wave_kernel<OP, T, VS, it>);
+#define WG1E(b, it) CREDIT_K(kKindWg, VS, b, it, single_wg_kernel<OP, T, VS, b, it>);
+#define SPLIT1E(b, it)                                                      \
+    CREDIT_K(kKindSplit, VS, b, it, split_kernel<OP, T, VS, b, it, false>); \
+    CREDIT_K(kKindControl, VS, b, it, split_kernel<OP, T, VS, b, it, true>);
+#define REREAD1E(b, it) CREDIT_K(kKindReread, VS, b, it, reread_kernel<OP, T, VS, b, it>);
+
+    CREDIT_WAVE_TILES(WAVE)
+    CREDIT_WG_TILES(WG)
+    CREDIT_SPLIT_TILES(SPLIT)
+    CREDIT_REREAD_TILES(REREAD)
+    CREDIT_WAVE_TILES_1E(WAVE1E)
+    CREDIT_WG_TILES_1E(WG1E)
+    CREDIT_SPLIT_TILES_1E(SPLIT1E)
+    CREDIT_REREAD_TILES_1E(REREAD1E)
+
+#undef WAVE
+#undef WG
+#undef SPLIT
+#undef REREAD
+#undef WAVE1E
+#undef WG1E
+#undef SPLIT1E
+#undef REREAD1E
 #undef CREDIT_K
 }
 

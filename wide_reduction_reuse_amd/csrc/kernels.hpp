@@ -15,20 +15,31 @@
 //           workgroup streams its row to reduce it, then streams it again to
 //           write the output.
 //
-// Co-residency of the P workgroups of a split row: workgroups take a ticket
-// from a device counter when they start, and ticket t owns slice t mod P of row
-// t / P.  Tickets are handed out in start order, so every complete group of P
-// tickets belongs to workgroups that are running or finished; only the newest
-// group can be incomplete, and its missing members are the next workgroups to
-// start.  As long as the device can hold P workgroups at once, every waiting
-// workgroup's peers are resident or will be dispatched, so no launch-wide
-// guarantee (cooperative launch) is needed.
+// Memory access: every row (or slice, or streamed chunk) is one buffer
+// descriptor sized to its length.  A thread at position `pos` of a group of G
+// threads holds vectors pos, pos + G, ..., pos + (IT-1) G of it; the IT loads
+// issue back to back with no branch, and the ones past the end return zero and
+// are excluded from the reduction by the valid count `kv`, while the matching
+// stores are dropped by the range check.
 //
-// Exchange words are 64-bit {value bits, epoch}; a reader polls each word until
-// it carries the current launch's epoch, so no fence is needed between the data
-// and its flag.  The last workgroup to finish resets the ticket counter and
-// advances the epoch, which makes the scratch reusable by the next launch on the
-// same stream (and by replays of a captured graph) with no host-side clearing.
+// Split-row launches are persistent: the grid is C clusters of P workgroups,
+// no larger than the device holds at once, and cluster k handles rows k, k+C,
+// k+2C, ...  A workgroup takes a ticket from a device counter when it starts
+// and ticket t is slice t mod P of cluster t / P.  Tickets are handed out in
+// start order, so every complete group of P tickets belongs to workgroups that
+// are running or finished; only the newest group can be incomplete, and its
+// missing members are the next workgroups to start.  As long as the device can
+// hold P workgroups at once, every waiting workgroup's peers are resident or
+// will be dispatched, so no launch-wide co-residency guarantee is needed.  The
+// counter is never reset: the host passes the value it holds at launch start.
+//
+// Exchange words are 64-bit {value bits, tag}.  A cluster's words are double
+// buffered by the parity of the row iteration, and iteration i of a launch
+// writes tag tag_base + i; the host advances tag_base past every tag a launch
+// uses, so a reader polls a word until it carries the tag it expects and no
+// fence is needed between the data and its flag.  A peer can only overwrite a
+// buffer two iterations later, after every member has passed the exchange of
+// the iteration in between, i.e. after every member has read this buffer.
 #pragma once
 
 #include "args.hpp"
@@ -36,7 +47,6 @@
 #include "ops.hpp"
 
 namespace credit {
-
 
 template <class Partial>
 __device__ __forceinline__ float comp(const Partial &p, int j)
@@ -65,29 +75,31 @@ __device__ __forceinline__ int count_valid(int64_t n, int pos)
 }
 
 template <class T, int VB, int IT, int G>
-__device__ __forceinline__ void load_tile(Tile<T, VB, IT> &t, const char *row_base, int64_t first,
-                                          int pos, int kvalid)
+__device__ __forceinline__ void load_tile(Tile<T, VB, IT> &t, rsrc_t src, int pos)
 {
 #pragma unroll
     for (int k = 0; k < IT; ++k)
-        if (k < kvalid)
-            t.v[k] = load_vec<VB>(row_base + (first + pos + static_cast<int64_t>(k) * G) * VB);
+        t.v[k] = buf_load<VB, kStream>(src, static_cast<uint32_t>(pos + k * G) * VB);
 }
 
-// Apply h to the held tile and write it out.  Parameter vectors are indexed by
-// column, i.e. by the same vector index as x within the row.
-template <OpKind OP, class T, int VB, int IT, int G, bool STREAM>
-__device__ __forceinline__ void store_vec_out(const RawVec<VB> &in, char *yrow, const char *grow,
-                                              const char *brow, int64_t vidx, const Coef &c)
+// The wave partial of a held tile.  (A second, unmasked copy for full waves
+// behind a wave-uniform branch was measured to raise register use by a third
+// with no gain: the masks are register selects.)
+template <OpKind OP, class T, int VB, int IT>
+__device__ __forceinline__ Partial tile_partial(Tile<T, VB, IT> &t, int kv)
+{
+    return OpTraits<OP>::template wave_partial<T, VB, IT>(t, kv);
+}
+
+// h for one vector: `in` is the held (or reread) input vector, g and b the
+// parameter vectors of the same columns.
+template <OpKind OP, class T, int VB, bool STREAM>
+__device__ __forceinline__ RawVec<VB> apply_vec(const RawVec<VB> &in, const RawVec<VB> &g, const RawVec<VB> &b,
+                                                const Coef &c)
 {
     using Op = OpTraits<OP>;
     constexpr int E = VB / StorageTraits<T>::kBytes;
     float out[E];
-    RawVec<VB> g, b;
-    if constexpr (Op::kParams >= 1)
-        g = load_vec_cached<VB>(grow + vidx * VB);
-    if constexpr (Op::kParams >= 2)
-        b = load_vec_cached<VB>(brow + vidx * VB);
 #pragma unroll
     for (int e = 0; e < E; ++e) {
         const float gv = Op::kParams >= 1 ? elem<T, VB>(g, e) : 1.0f;
@@ -97,24 +109,53 @@ __device__ __forceinline__ void store_vec_out(const RawVec<VB> &in, char *yrow, 
         else
             out[e] = Op::template apply<T>(elem<T, VB>(in, e), c, gv, bv);
     }
-    store_vec<VB>(yrow + vidx * VB, pack<T, VB, E>(out));
+    return pack<T, VB, E>(out);
 }
 
+// Parameter vectors fetched per group of the output loop: four while the held
+// tile is small, two when it already takes 64 VGPRs.
+template <int IT, int VB>
+constexpr int param_group()
+{
+    return IT * VB / 4 >= 64 ? (IT < 2 ? IT : 2) : (IT < 4 ? IT : 4);
+}
+
+// Apply h to the held tile and write it out.  dst, gam and bet describe the
+// same columns (the row or slice); parameter vectors are fetched a group at a
+// time ahead of the arithmetic that needs them.
 template <OpKind OP, class T, int VB, int IT, int G>
-__device__ __forceinline__ void store_tile(Tile<T, VB, IT> &t, char *yrow, const char *grow,
-                                           const char *brow, int64_t first, int pos, int kvalid,
+__device__ __forceinline__ void store_tile(Tile<T, VB, IT> &t, rsrc_t dst, rsrc_t gam, rsrc_t bet, int pos,
                                            const Coef &c)
 {
+    using Op = OpTraits<OP>;
+    constexpr int GP = param_group<IT, VB>();
     fence_tile(t);
+    // recompute the offsets here (one add each) instead of keeping the load
+    // phase's sixteen offset registers alive across the reduction
+    uint32_t base = static_cast<uint32_t>(pos) * VB;
+    asm volatile("" : "+v"(base));
 #pragma unroll
-    for (int k = 0; k < IT; ++k)
-        if (k < kvalid)
-            store_vec_out<OP, T, VB, IT, G, false>(t.v[k], yrow, grow, brow,
-                                                   first + pos + static_cast<int64_t>(k) * G, c);
+    for (int kb = 0; kb < IT; kb += GP) {
+        RawVec<VB> g[GP], b[GP];
+#pragma unroll
+        for (int j = 0; j < GP; ++j) {
+            const uint32_t off = base + static_cast<uint32_t>((kb + j) * G * VB);
+            if constexpr (Op::kParams >= 1)
+                g[j] = buf_load<VB, kKeep>(gam, off);
+            if constexpr (Op::kParams >= 2)
+                b[j] = buf_load<VB, kKeep>(bet, off);
+        }
+#pragma unroll
+        for (int j = 0; j < GP; ++j) {
+            const uint32_t off = base + static_cast<uint32_t>((kb + j) * G * VB);
+            buf_store<VB, kStream>(apply_vec<OP, T, VB, false>(t.v[kb + j], g[j], b[j], c), dst, off);
+        }
+    }
 }
 
 // Combine the wave partials of a workgroup through LDS; every thread returns
-// the same workgroup partial (fixed order w = 0..NW-1).
+// the same workgroup partial (fixed order w = 0..NW-1).  The caller must not
+// rewrite `sh` before every thread has passed a later barrier.
 template <OpKind OP, int NW>
 __device__ __forceinline__ Partial block_combine(const Partial &wp, Partial *sh)
 {
@@ -130,6 +171,16 @@ __device__ __forceinline__ Partial block_combine(const Partial &wp, Partial *sh)
     return OpTraits<OP>::template merge<NW>(loc, NW);
 }
 
+// Descriptor of `nvec` vectors starting at vector `first` of array `base`.
+// (Integer arithmetic on the address: the parameter pointers are null for
+// operators without parameters, whose descriptors are never used.)
+template <int VB>
+__device__ __forceinline__ rsrc_t span(const void *base, int64_t first, int64_t nvec)
+{
+    const uintptr_t p = reinterpret_cast<uintptr_t>(base) + static_cast<uintptr_t>(first * VB);
+    return make_rsrc(reinterpret_cast<const void *>(p), static_cast<uint32_t>(nvec * VB));
+}
+
 // ---------------------------------------------------------------------------
 // Path 1a: one wavefront per row, four rows per 256-thread workgroup.  No LDS
 // and no barrier: the wave reduction is the row reduction.
@@ -140,20 +191,17 @@ __global__ __launch_bounds__(kWave *kWaveRowsPerWg) void single_wave_kernel(RowA
     using Op = OpTraits<OP>;
     constexpr int E = VB / StorageTraits<T>::kBytes;
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t row = static_cast<int64_t>(blockIdx.x) * kWaveRowsPerWg + threadIdx.x / kWave;
+    const int64_t row = uniform(static_cast<int64_t>(blockIdx.x) * kWaveRowsPerWg + threadIdx.x / kWave);
     if (row >= a.rows)
         return;  // wave-uniform
     const int64_t nv = a.cols / E;
-    const int64_t row_off = row * nv * VB;
-    const char *xrow = static_cast<const char *>(a.x) + row_off;
-    char *yrow = static_cast<char *>(a.y) + row_off;
     Tile<T, VB, IT> t;
+    load_tile<T, VB, IT, kWave>(t, span<VB>(a.x, row * nv, nv), lane);
     const int kv = count_valid<IT, kWave>(nv, lane);
-    load_tile<T, VB, IT, kWave>(t, xrow, 0, lane, kv);
-    const Partial wp = Op::template wave_partial<T, VB, IT>(t, kv);
+    const Partial wp = tile_partial<OP, T, VB, IT>(t, kv);
     const Coef c = Op::template finalize<T>(wp, wp, a.cols, a.eps);
-    store_tile<OP, T, VB, IT, kWave>(t, yrow, static_cast<const char *>(a.gamma),
-                                     static_cast<const char *>(a.beta), 0, lane, kv, c);
+    store_tile<OP, T, VB, IT, kWave>(t, span<VB>(a.y, row * nv, nv), span<VB>(a.gamma, 0, nv),
+                                     span<VB>(a.beta, 0, nv), lane, c);
 }
 
 // ---------------------------------------------------------------------------
@@ -169,17 +217,14 @@ __global__ __launch_bounds__(BLOCK) void single_wg_kernel(RowArgs a)
     const int tid = threadIdx.x;
     const int64_t row = blockIdx.x;
     const int64_t nv = a.cols / E;
-    const int64_t row_off = row * nv * VB;
-    const char *xrow = static_cast<const char *>(a.x) + row_off;
-    char *yrow = static_cast<char *>(a.y) + row_off;
     Tile<T, VB, IT> t;
+    load_tile<T, VB, IT, BLOCK>(t, span<VB>(a.x, row * nv, nv), tid);
     const int kv = count_valid<IT, BLOCK>(nv, tid);
-    load_tile<T, VB, IT, BLOCK>(t, xrow, 0, tid, kv);
-    const Partial wp = Op::template wave_partial<T, VB, IT>(t, kv);
+    const Partial wp = tile_partial<OP, T, VB, IT>(t, kv);
     const Partial rp = block_combine<OP, NW>(wp, sh);
     const Coef c = Op::template finalize<T>(rp, wp, a.cols, a.eps);
-    store_tile<OP, T, VB, IT, BLOCK>(t, yrow, static_cast<const char *>(a.gamma),
-                                     static_cast<const char *>(a.beta), 0, tid, kv, c);
+    store_tile<OP, T, VB, IT, BLOCK>(t, span<VB>(a.y, row * nv, nv), span<VB>(a.gamma, 0, nv),
+                                     span<VB>(a.beta, 0, nv), tid, c);
 }
 
 // ---------------------------------------------------------------------------
@@ -196,82 +241,70 @@ __global__ __launch_bounds__(BLOCK) void split_kernel(SplitArgs a)
     constexpr int Q = Op::kQ;
     __shared__ Partial sh[NW];
     __shared__ Partial peer[kMaxSplit];
-    __shared__ uint32_t sh_ticket, sh_epoch;
+    __shared__ uint32_t sh_ticket;
     const int tid = threadIdx.x;
-    if (tid == 0) {
-        sh_ticket = fetch_add_u32_agent(&a.ctl->ticket, 1u);
-        sh_epoch = load_u32_agent(&a.ctl->epoch);
-    }
+    if (tid == 0)
+        sh_ticket = fetch_add_u32_agent(a.ticket, 1u) - a.ticket_base;
     __syncthreads();
-    // the counter starts each launch at 0; the modulo keeps indices inside this
-    // launch's rows and slots even if it did not (tickets stay a permutation)
+    // the modulo only guards against a counter the host's bookkeeping does not
+    // match; it keeps every index inside this launch's clusters and slots
     const uint32_t ticket = sh_ticket % gridDim.x;
-    const uint32_t epoch = sh_epoch;
     const int P = a.p;
-    const int64_t rl = ticket / static_cast<uint32_t>(P);
+    const int64_t k = ticket / static_cast<uint32_t>(P);
     const int c = static_cast<int>(ticket % static_cast<uint32_t>(P));
-    const int64_t row = a.row0 + rl;
 
     const int64_t nv = a.r.cols / E;
     const int64_t per = (nv + P - 1) / P;
     const int64_t v0 = min(nv, per * c);
-    const int64_t v1 = min(nv, v0 + per);
-    const int64_t row_off = row * nv * VB;
-    const char *xrow = static_cast<const char *>(a.r.x) + row_off;
-    char *yrow = static_cast<char *>(a.r.y) + row_off;
+    const int64_t ns = min(nv, v0 + per) - v0;  // vectors in this slice
+    const int kv = count_valid<IT, BLOCK>(ns, tid);
+    const rsrc_t gam = span<VB>(a.r.gamma, v0, ns);
+    const rsrc_t bet = span<VB>(a.r.beta, v0, ns);
+    uint64_t *cslots = a.slots + k * 2 * P * Q;
 
-    Tile<T, VB, IT> t;
-    const int kv = count_valid<IT, BLOCK>(v1 - v0, tid);
-    if constexpr (CONTROL) {
+    uint32_t it = 0;
+    for (int64_t row = k; row < a.r.rows; row += a.clusters, ++it) {
+        Tile<T, VB, IT> t;
+        if constexpr (CONTROL) {
 #pragma unroll
-        for (int k = 0; k < IT; ++k)
+            for (int q = 0; q < IT; ++q)
 #pragma unroll
-            for (int w = 0; w < RawVec<VB>::kWords; ++w)
-                set_word<VB>(t.v[k], w, 0u);
-    } else {
-        load_tile<T, VB, IT, BLOCK>(t, xrow, v0, tid, kv);
-    }
-    const Partial wp = Op::template wave_partial<T, VB, IT>(t, kv);
-    const Partial sp = block_combine<OP, NW>(wp, sh);
+                for (int w = 0; w < RawVec<VB>::kWords; ++w)
+                    set_word<VB>(t.v[q], w, 0u);
+        } else {
+            load_tile<T, VB, IT, BLOCK>(t, span<VB>(a.r.x, row * nv + v0, ns), tid);
+        }
+        const Partial wp = tile_partial<OP, T, VB, IT>(t, kv);
+        const Partial sp = block_combine<OP, NW>(wp, sh);
 
-    // publish this slice's partial, then gather all P partials of the row
-    uint64_t *row_slots = a.slots + rl * P * Q;
-    if (tid < Q)
-        store_u64_agent(row_slots + c * Q + tid,
-                        (static_cast<uint64_t>(epoch) << 32) | __float_as_uint(comp(sp, tid)));
-    if (tid < P * Q) {
-        uint64_t w = load_u64_agent(row_slots + tid);
-        uint32_t polls = 0;
-        while (static_cast<uint32_t>(w >> 32) != epoch) {
-            if (++polls > a.spin_limit) {
-                fetch_or_u32_agent(&a.ctl->error, 1u);
-                break;
+        // publish this slice's partial, then gather all P partials of the row
+        const uint32_t tag = a.tag_base + it;
+        uint64_t *slots = cslots + (it & 1u) * P * Q;
+        if (tid < Q)
+            store_u64_agent(slots + c * Q + tid, (static_cast<uint64_t>(tag) << 32) | __float_as_uint(comp(sp, tid)));
+        if (tid < P * Q) {
+            uint64_t w = load_u64_agent(slots + tid);
+            uint32_t polls = 0;
+            while (static_cast<uint32_t>(w >> 32) != tag) {
+                if (++polls > a.spin_limit) {
+                    fetch_or_u32_agent(a.error, 1u);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+                w = load_u64_agent(slots + tid);
             }
-            __builtin_amdgcn_s_sleep(2);
-            w = load_u64_agent(row_slots + tid);
+            set_comp(peer[tid / Q], tid % Q, __uint_as_float(static_cast<uint32_t>(w)));
         }
-        set_comp(peer[tid / Q], tid % Q, __uint_as_float(static_cast<uint32_t>(w)));
-    }
-    __syncthreads();
-    if (tid == 0) {
-        // every workgroup has taken its ticket and read the epoch before it
-        // counts itself done, so the last one can recycle both
-        const uint32_t d = fetch_add_u32_agent(&a.ctl->done, 1u);
-        if (d == gridDim.x - 1) {
-            store_u32_agent(&a.ctl->ticket, 0u);
-            store_u32_agent(&a.ctl->done, 0u);
-            store_u32_agent(&a.ctl->epoch, epoch + 1u == 0u ? 1u : epoch + 1u);
-        }
-    }
-    Partial parts[kMaxSplit];
+        __syncthreads();
+        Partial parts[kMaxSplit];
 #pragma unroll
-    for (int i = 0; i < kMaxSplit; ++i)
-        parts[i] = peer[i];
-    const Partial rp = Op::template merge<kMaxSplit>(parts, P);
-    const Coef cf = Op::template finalize<T>(rp, wp, a.r.cols, a.r.eps);
-    if constexpr (!CONTROL)
-        store_tile<OP, T, VB, IT, BLOCK>(t, yrow, static_cast<const char *>(a.r.gamma),
-                                         static_cast<const char *>(a.r.beta), v0, tid, kv, cf);
+        for (int i = 0; i < kMaxSplit; ++i)
+            parts[i] = peer[i];
+        const Partial rp = Op::template merge<kMaxSplit>(parts, P);
+        const Coef cf = Op::template finalize<T>(rp, wp, a.r.cols, a.r.eps);
+        if constexpr (!CONTROL)
+            store_tile<OP, T, VB, IT, BLOCK>(t, span<VB>(a.r.y, row * nv + v0, ns), gam, bet, tid, cf);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -285,41 +318,52 @@ __global__ __launch_bounds__(BLOCK) void reread_kernel(RowArgs a)
     using Op = OpTraits<OP>;
     constexpr int E = VB / StorageTraits<T>::kBytes;
     constexpr int NW = BLOCK / kWave;
+    constexpr int GP = U < 4 ? U : 4;
     constexpr int64_t CH = static_cast<int64_t>(BLOCK) * U;
     __shared__ Partial sh[NW];
     const int tid = threadIdx.x;
     const int64_t row = blockIdx.x;
     const int64_t nv = a.cols / E;
-    const int64_t row_off = row * nv * VB;
-    const char *xrow = static_cast<const char *>(a.x) + row_off;
-    char *yrow = static_cast<char *>(a.y) + row_off;
-
     Partial r = Op::stream_init();
     for (int64_t base = 0; base < nv; base += CH) {
+        const int64_t n = min(CH, nv - base);
+        const rsrc_t src = span<VB>(a.x, row * nv + base, n);
         RawVec<VB> v[U];
-        const int kv = count_valid<U, BLOCK>(nv - base, tid);
 #pragma unroll
         for (int k = 0; k < U; ++k)
-            if (k < kv)
-                v[k] = load_vec_cached<VB>(xrow + (base + tid + static_cast<int64_t>(k) * BLOCK) * VB);
-        Op::template stream_update<T, VB, U>(r, v, kv);
+            v[k] = buf_load<VB, kKeep>(src, static_cast<uint32_t>(tid + k * BLOCK) * VB);
+        Op::template stream_update<T, VB, U>(r, v, count_valid<U, BLOCK>(n, tid));
     }
     const Partial wp = Op::wave_from_thread(r);
     const Partial rp = block_combine<OP, NW>(wp, sh);
     const Coef c = Op::template finalize_stream<T>(rp, a.cols, a.eps);
     for (int64_t base = 0; base < nv; base += CH) {
+        const int64_t n = min(CH, nv - base);
+        const rsrc_t src = span<VB>(a.x, row * nv + base, n);
+        const rsrc_t dst = span<VB>(a.y, row * nv + base, n);
+        const rsrc_t gam = span<VB>(a.gamma, base, n);
+        const rsrc_t bet = span<VB>(a.beta, base, n);
         RawVec<VB> v[U];
-        const int kv = count_valid<U, BLOCK>(nv - base, tid);
 #pragma unroll
         for (int k = 0; k < U; ++k)
-            if (k < kv)
-                v[k] = load_vec<VB>(xrow + (base + tid + static_cast<int64_t>(k) * BLOCK) * VB);
+            v[k] = buf_load<VB, kStream>(src, static_cast<uint32_t>(tid + k * BLOCK) * VB);
 #pragma unroll
-        for (int k = 0; k < U; ++k)
-            if (k < kv)
-                store_vec_out<OP, T, VB, U, BLOCK, true>(v[k], yrow, static_cast<const char *>(a.gamma),
-                                                         static_cast<const char *>(a.beta),
-                                                         base + tid + static_cast<int64_t>(k) * BLOCK, c);
+        for (int kb = 0; kb < U; kb += GP) {
+            RawVec<VB> g[GP], b[GP];
+#pragma unroll
+            for (int j = 0; j < GP; ++j) {
+                const uint32_t off = static_cast<uint32_t>(tid + (kb + j) * BLOCK) * VB;
+                if constexpr (Op::kParams >= 1)
+                    g[j] = buf_load<VB, kKeep>(gam, off);
+                if constexpr (Op::kParams >= 2)
+                    b[j] = buf_load<VB, kKeep>(bet, off);
+            }
+#pragma unroll
+            for (int j = 0; j < GP; ++j) {
+                const uint32_t off = static_cast<uint32_t>(tid + (kb + j) * BLOCK) * VB;
+                buf_store<VB, kStream>(apply_vec<OP, T, VB, true>(v[kb + j], g[j], b[j], c), dst, off);
+            }
+        }
     }
 }
 

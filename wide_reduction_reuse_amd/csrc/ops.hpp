@@ -71,7 +71,7 @@ struct OpTraits<kSoftmax> {
     // overwritten with e_i = exp(x_i - m_wave) so that the output needs no
     // second exponential.
     template <class T, int VB, int IT>
-    __device__ static Partial wave_partial(Tile<T, VB, IT> &t, int kvalid)
+    __device__ __forceinline__ static Partial wave_partial(Tile<T, VB, IT> &t, int kvalid)
     {
         constexpr int E = Tile<T, VB, IT>::kEpv;
         float mt = -INFINITY;
@@ -107,7 +107,7 @@ struct OpTraits<kSoftmax> {
 
     // Combine partials p[0..n-1] (n <= N) in index order.
     template <int N>
-    __device__ static Partial merge(const Partial (&p)[N], int n)
+    __device__ __forceinline__ static Partial merge(const Partial (&p)[N], int n)
     {
         float m = -INFINITY;
 #pragma unroll
@@ -124,7 +124,7 @@ struct OpTraits<kSoftmax> {
 
     // `own` is the partial whose exponentials are stored in this thread's tile.
     template <class T>
-    __device__ static Coef finalize(const Partial &row, const Partial &own, int64_t, float)
+    __device__ __forceinline__ static Coef finalize(const Partial &row, const Partial &own, int64_t, float)
     {
         const float inv_s = 1.0f / row.b;
         if constexpr (StorageTraits<T>::kBytes == 4)
@@ -134,7 +134,7 @@ struct OpTraits<kSoftmax> {
     }
 
     template <class T>
-    __device__ static float apply(float x, const Coef &c, float, float)
+    __device__ __forceinline__ static float apply(float x, const Coef &c, float, float)
     {
         if constexpr (StorageTraits<T>::kBytes == 4)
             return x * c.scale;  // x already holds exp(x - m_wave)
@@ -146,7 +146,7 @@ struct OpTraits<kSoftmax> {
     // thread keeps a running partial over the chunks it streams, and the
     // output pass recomputes the exponential from the reread input.
     template <class T>
-    __device__ static float expf_t(float d)
+    __device__ __forceinline__ static float expf_t(float d)
     {
         if constexpr (StorageTraits<T>::kBytes == 4)
             return exp_acc(d);
@@ -155,7 +155,7 @@ struct OpTraits<kSoftmax> {
     }
 
     template <class T, int VB, int U>
-    __device__ static void stream_update(Partial &r, const RawVec<VB> (&v)[U], int kvalid)
+    __device__ __forceinline__ static void stream_update(Partial &r, const RawVec<VB> (&v)[U], int kvalid)
     {
         constexpr int E = VB / StorageTraits<T>::kBytes;
         float cm = -INFINITY;
@@ -179,9 +179,9 @@ struct OpTraits<kSoftmax> {
         r.b += s;
     }
 
-    __device__ static Partial stream_init() { return Partial{-INFINITY, 0.0f, 0.0f}; }
+    __device__ __forceinline__ static Partial stream_init() { return Partial{-INFINITY, 0.0f, 0.0f}; }
 
-    __device__ static Partial wave_from_thread(const Partial &r)
+    __device__ __forceinline__ static Partial wave_from_thread(const Partial &r)
     {
         const float mw = wave_max(r.a);
         const float s = r.b != 0.0f ? r.b * exp_acc(r.a - mw) : 0.0f;
@@ -189,13 +189,13 @@ struct OpTraits<kSoftmax> {
     }
 
     template <class T>
-    __device__ static Coef finalize_stream(const Partial &row, int64_t, float)
+    __device__ __forceinline__ static Coef finalize_stream(const Partial &row, int64_t, float)
     {
         return Coef{0.0f, 1.0f / row.b, row.a};
     }
 
     template <class T>
-    __device__ static float apply_stream(float x, const Coef &c, float, float)
+    __device__ __forceinline__ static float apply_stream(float x, const Coef &c, float, float)
     {
         return expf_t<T>(x - c.m) * c.scale;
     }
@@ -210,7 +210,7 @@ struct OpTraits<kLayerNorm> {
     static constexpr int kParams = 2;
 
     template <class T, int VB, int IT>
-    __device__ static Partial wave_partial(Tile<T, VB, IT> &t, int kvalid)
+    __device__ __forceinline__ static Partial wave_partial(Tile<T, VB, IT> &t, int kvalid)
     {
         constexpr int E = Tile<T, VB, IT>::kEpv;
         float sum = 0.0f;
@@ -238,7 +238,7 @@ struct OpTraits<kLayerNorm> {
 
     // mean = sum n_i mean_i / n;  M2 = sum (M2_i + n_i (mean_i - mean)^2).
     template <int N>
-    __device__ static Partial merge(const Partial (&p)[N], int n)
+    __device__ __forceinline__ static Partial merge(const Partial (&p)[N], int n)
     {
         float nt = 0.0f, acc = 0.0f;
 #pragma unroll
@@ -259,14 +259,14 @@ struct OpTraits<kLayerNorm> {
     }
 
     template <class T>
-    __device__ static Coef finalize(const Partial &row, const Partial &, int64_t cols, float eps)
+    __device__ __forceinline__ static Coef finalize(const Partial &row, const Partial &, int64_t cols, float eps)
     {
         const float var = row.c / static_cast<float>(cols);
         return Coef{row.b, 1.0f / sqrtf(var + eps), 0.0f};
     }
 
     template <class T>
-    __device__ static float apply(float x, const Coef &c, float g, float b)
+    __device__ __forceinline__ static float apply(float x, const Coef &c, float g, float b)
     {
         return __builtin_fmaf((x - c.mean) * c.scale, g, b);
     }
@@ -274,7 +274,7 @@ struct OpTraits<kLayerNorm> {
     // ---- streaming form: each chunk is reduced two-pass in registers to
     // (n_c, mean_c, M2_c) and folded into the running partial pairwise.
     template <class T, int VB, int U>
-    __device__ static void stream_update(Partial &r, const RawVec<VB> (&v)[U], int kvalid)
+    __device__ __forceinline__ static void stream_update(Partial &r, const RawVec<VB> (&v)[U], int kvalid)
     {
         constexpr int E = VB / StorageTraits<T>::kBytes;
         if (kvalid <= 0)
@@ -304,9 +304,9 @@ struct OpTraits<kLayerNorm> {
         r.a = n2;
     }
 
-    __device__ static Partial stream_init() { return Partial{0.0f, 0.0f, 0.0f}; }
+    __device__ __forceinline__ static Partial stream_init() { return Partial{0.0f, 0.0f, 0.0f}; }
 
-    __device__ static Partial wave_from_thread(const Partial &r)
+    __device__ __forceinline__ static Partial wave_from_thread(const Partial &r)
     {
         const float nw = wave_sum(r.a);
         const float mean = nw > 0.0f ? wave_sum(r.a * r.b) / nw : 0.0f;
@@ -315,13 +315,13 @@ struct OpTraits<kLayerNorm> {
     }
 
     template <class T>
-    __device__ static Coef finalize_stream(const Partial &row, int64_t cols, float eps)
+    __device__ __forceinline__ static Coef finalize_stream(const Partial &row, int64_t cols, float eps)
     {
         return finalize<T>(row, row, cols, eps);
     }
 
     template <class T>
-    __device__ static float apply_stream(float x, const Coef &c, float g, float b)
+    __device__ __forceinline__ static float apply_stream(float x, const Coef &c, float g, float b)
     {
         return apply<T>(x, c, g, b);
     }
@@ -336,7 +336,7 @@ struct OpTraits<kRmsNorm> {
     static constexpr int kParams = 1;
 
     template <class T, int VB, int IT>
-    __device__ static Partial wave_partial(Tile<T, VB, IT> &t, int kvalid)
+    __device__ __forceinline__ static Partial wave_partial(Tile<T, VB, IT> &t, int kvalid)
     {
         constexpr int E = Tile<T, VB, IT>::kEpv;
         float ss = 0.0f;
@@ -352,7 +352,7 @@ struct OpTraits<kRmsNorm> {
     }
 
     template <int N>
-    __device__ static Partial merge(const Partial (&p)[N], int n)
+    __device__ __forceinline__ static Partial merge(const Partial (&p)[N], int n)
     {
         float ss = 0.0f;
 #pragma unroll
@@ -363,19 +363,19 @@ struct OpTraits<kRmsNorm> {
     }
 
     template <class T>
-    __device__ static Coef finalize(const Partial &row, const Partial &, int64_t cols, float eps)
+    __device__ __forceinline__ static Coef finalize(const Partial &row, const Partial &, int64_t cols, float eps)
     {
         return Coef{0.0f, 1.0f / sqrtf(row.a / static_cast<float>(cols) + eps), 0.0f};
     }
 
     template <class T>
-    __device__ static float apply(float x, const Coef &c, float g, float)
+    __device__ __forceinline__ static float apply(float x, const Coef &c, float g, float)
     {
         return x * c.scale * g;
     }
 
     template <class T, int VB, int U>
-    __device__ static void stream_update(Partial &r, const RawVec<VB> (&v)[U], int kvalid)
+    __device__ __forceinline__ static void stream_update(Partial &r, const RawVec<VB> (&v)[U], int kvalid)
     {
         constexpr int E = VB / StorageTraits<T>::kBytes;
 #pragma unroll
@@ -388,21 +388,21 @@ struct OpTraits<kRmsNorm> {
                 }
     }
 
-    __device__ static Partial stream_init() { return Partial{0.0f, 0.0f, 0.0f}; }
+    __device__ __forceinline__ static Partial stream_init() { return Partial{0.0f, 0.0f, 0.0f}; }
 
-    __device__ static Partial wave_from_thread(const Partial &r)
+    __device__ __forceinline__ static Partial wave_from_thread(const Partial &r)
     {
         return Partial{wave_sum(r.a), 0.0f, 0.0f};
     }
 
     template <class T>
-    __device__ static Coef finalize_stream(const Partial &row, int64_t cols, float eps)
+    __device__ __forceinline__ static Coef finalize_stream(const Partial &row, int64_t cols, float eps)
     {
         return finalize<T>(row, row, cols, eps);
     }
 
     template <class T>
-    __device__ static float apply_stream(float x, const Coef &c, float g, float b)
+    __device__ __forceinline__ static float apply_stream(float x, const Coef &c, float g, float b)
     {
         return apply<T>(x, c, g, b);
     }

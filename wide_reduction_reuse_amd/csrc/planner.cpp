@@ -21,62 +21,49 @@ int vec_bytes_for(int dt, int64_t cols)
 }
 
 // ---------------------------------------------------------------------------
-// Tile ladders (must match instantiate.hpp; the library checks at load time
-// that every tile listed here has a compiled kernel).
+// Tile ladders: the same X-macro lists the kernel instantiations expand.
 // ---------------------------------------------------------------------------
 static std::vector<TileSpec> make_ladder(int kind, bool v16)
 {
     std::vector<TileSpec> t;
-    auto add = [&](int block, int items) { t.push_back(TileSpec{kind, block, items, v16 ? 16 : 0}); };
+    const int vb = v16 ? 16 : 0;
+#define ADD1(it) t.push_back(TileSpec{kind, 64, it, vb});
+#define ADD2(b, it) t.push_back(TileSpec{kind, b, it, vb});
     if (v16) {
         switch (kind) {
         case kKindWave:
-            for (int it : {1, 2, 4, 8, 16})
-                add(64, it);
+            CREDIT_WAVE_TILES(ADD1)
             break;
         case kKindWg:
-            for (int it : {2, 4, 8, 16})
-                add(256, it);
-            for (int it : {4, 8, 16})
-                add(512, it);
-            for (int it : {4, 8, 16})
-                add(1024, it);
+            CREDIT_WG_TILES(ADD2)
             break;
         case kKindSplit:
         case kKindControl:
-            add(256, 8);
-            add(256, 16);
-            add(512, 8);
-            add(512, 16);
-            add(1024, 4);
-            add(1024, 8);
-            add(1024, 16);
+            CREDIT_SPLIT_TILES(ADD2)
             break;
         case kKindReread:
-            add(256, 4);
-            add(512, 4);
-            add(1024, 4);
+            CREDIT_REREAD_TILES(ADD2)
             break;
         }
     } else {
         switch (kind) {
         case kKindWave:
-            add(64, 4);
-            add(64, 16);
+            CREDIT_WAVE_TILES_1E(ADD1)
             break;
         case kKindWg:
-            add(1024, 4);
-            add(1024, 16);
+            CREDIT_WG_TILES_1E(ADD2)
             break;
         case kKindSplit:
         case kKindControl:
-            add(1024, 16);
+            CREDIT_SPLIT_TILES_1E(ADD2)
             break;
         case kKindReread:
-            add(256, 8);
+            CREDIT_REREAD_TILES_1E(ADD2)
             break;
         }
     }
+#undef ADD1
+#undef ADD2
     return t;
 }
 

@@ -1,5 +1,7 @@
 // Table of compiled kernel instantiations, filled by the per-operator
 // translation units and searched by the host library when it plans a launch.
+// The tile ladders are X-macro lists so that the instantiations and the
+// planner's ladders come from one definition.
 #pragma once
 
 #include <vector>
@@ -23,12 +25,20 @@ void register_layernorm_kernels(std::vector<KernelEntry> &out);
 void register_rmsnorm_kernels(std::vector<KernelEntry> &out);
 void register_misc_kernels(std::vector<KernelEntry> &out);
 
-// Tile ladders (shared by the instantiation units and the planner).
-// Path 1a, one wave per row:    items in {1, 2, 4, 8, 16}.
-// Path 1b, one workgroup/row:   (256: 2,4,8,16) (512: 4,8,16) (1024: 4,8,16).
-// Path 2, split row:            (256: 8,16) (512: 8,16) (1024: 4,8,16).
-// Path 3, reread:               (256: 4) (512: 4) (1024: 4).
-// One-element accesses (rows whose byte length is not a multiple of 16):
-//   1a items {4, 16}; 1b (1024: 4, 16); 2 (1024: 16); 3 (256: 8).
+// Tile ladders for 16-byte accesses: X(items) for wave-per-row, X(block, items)
+// for the others.
+#define CREDIT_WAVE_TILES(X) X(1) X(2) X(4) X(8) X(16)
+#define CREDIT_WG_TILES(X) \
+    X(128, 4) X(128, 8) X(128, 16) X(256, 2) X(256, 4) X(256, 8) X(256, 16) X(512, 4) X(512, 8) X(512, 16) \
+    X(1024, 4) X(1024, 8) X(1024, 16)
+#define CREDIT_SPLIT_TILES(X) X(256, 8) X(256, 16) X(512, 4) X(512, 8) X(512, 16) X(1024, 4) X(1024, 8) X(1024, 16)
+#define CREDIT_REREAD_TILES(X) X(256, 4) X(512, 4) X(1024, 4)
+
+// Ladders for one-element accesses (rows whose byte length is not a multiple
+// of 16 bytes).
+#define CREDIT_WAVE_TILES_1E(X) X(4) X(16)
+#define CREDIT_WG_TILES_1E(X) X(1024, 4) X(1024, 16)
+#define CREDIT_SPLIT_TILES_1E(X) X(1024, 16)
+#define CREDIT_REREAD_TILES_1E(X) X(256, 8)
 
 }  // namespace credit
