@@ -24,7 +24,6 @@ streaming-copy ceiling to FILE.
 from __future__ import annotations
 
 import argparse
-import ctypes
 import hashlib
 import json
 import os
@@ -35,10 +34,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 from wide_reduction_reuse_amd import workloads as W  # noqa: E402
+from wide_reduction_reuse_amd.timing import FLUSH_BYTES, summarize, time_launches  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 DEFAULT_WORKLOAD = "layernorm_bf16_4096x8192"
-FLUSH_BYTES = 1 << 30
 PROFILES = os.path.join(ROOT, "profiles")
 CPU_BASELINE_SECONDS = 10.0
 METRIC = "achieved HBM GB/s (one read + one write) and % of MI355X peak per op/shape"
@@ -69,39 +68,6 @@ def load_traffic(workload: str):
     return e
 
 
-class HipEvents:
-    """Pairs of timing-enabled hipEvent_t from the HIP runtime torch loaded."""
-
-    def __init__(self, n: int):
-        self.hip = ctypes.CDLL("libamdhip64.so.7")
-        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
-        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
-                                                 ctypes.c_void_p]
-        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
-        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
-        self.pairs = []
-        for _ in range(n):
-            a, b = ctypes.c_void_p(), ctypes.c_void_p()
-            if self.hip.hipEventCreate(ctypes.byref(a)) or self.hip.hipEventCreate(ctypes.byref(b)):
-                raise RuntimeError("hipEventCreate failed")
-            self.pairs.append((a.value, b.value))
-
-    def elapsed_ms(self, i: int) -> float:
-        a, b = self.pairs[i]
-        if self.hip.hipEventSynchronize(b):
-            raise RuntimeError("hipEventSynchronize failed")
-        ms = ctypes.c_float()
-        if self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b):
-            raise RuntimeError("hipEventElapsedTime failed")
-        return float(ms.value)
-
-    def close(self):
-        for a, b in self.pairs:
-            self.hip.hipEventDestroy(a)
-            self.hip.hipEventDestroy(b)
-        self.pairs = []
-
-
 def upload(inp: W.HostInputs):
     import numpy as np
     import torch
@@ -113,38 +79,6 @@ def upload(inp: W.HostInputs):
             return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
         return torch.from_numpy(a).cuda()
     return dev(inp.x), dev(inp.gamma), dev(inp.beta)
-
-
-def time_launches(launch, steps: int, warmup: int, flush_buf):
-    """Call launch(start_event, stop_event) warmup + steps times, each after an
-    untimed cache flush; return per-step kernel durations (ms) and the wall
-    seconds of the timed loop."""
-    import torch
-    from wide_reduction_reuse_amd import credit as C
-    ev = HipEvents(warmup + steps)
-    try:
-        for i in range(warmup):
-            C.credit_flush(flush_buf)
-            launch(*ev.pairs[i])
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(warmup, warmup + steps):
-            C.credit_flush(flush_buf)
-            launch(*ev.pairs[i])
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        durs = [ev.elapsed_ms(i) for i in range(warmup, warmup + steps)]
-    finally:
-        ev.close()
-    return durs, wall
-
-
-def summarize(durs, nbytes: int) -> dict:
-    s = sorted(durs)
-    mean_ms = sum(durs) / len(durs)
-    med_ms = s[len(s) // 2]
-    return {"mean_ms": mean_ms, "median_ms": med_ms, "min_ms": s[0], "max_ms": s[-1],
-            "gbs": nbytes / (mean_ms * 1e-3) / 1e9, "gbs_median": nbytes / (med_ms * 1e-3) / 1e9}
 
 
 def run_workload(w: W.Workload, path: str, split_p: int, steps: int, warmup: int, flush_buf, inputs=None,

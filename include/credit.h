@@ -72,7 +72,10 @@ typedef struct {
     int32_t block_threads; /* threads per row owner: 64 = one wavefront per row */
     int32_t items;         /* vectors per thread held (paths 1, 2) or streamed per step (path 3) */
     int32_t vec_bytes;     /* bytes per global access: 16, or one element for rows not 16-B multiples */
-    int32_t reserved;
+    int32_t wgs_per_cu;    /* paths 1, 2: 0 = as many workgroups as the device holds at once, each
+                              owner looping over rows (and loading the next row while writing the
+                              current one); k > 0 = at most k per CU; path 1 only: -1 = one
+                              workgroup per row (four rows for block_threads 64), no looping */
     double predicted_us[3];
 } credit_plan_t;
 
@@ -123,6 +126,20 @@ credit_status_t credit_select_path(credit_op_t op, credit_dtype_t dt, int64_t ro
  */
 credit_status_t credit_make_plan(credit_op_t op, credit_dtype_t dt, int64_t rows, int64_t cols,
                                  credit_path_t path, int32_t split_p, credit_plan_t *out);
+
+/*
+ * Every worthwhile legal plan for a shape: each path 1 tile that holds the
+ * row, each path 3 tile, and each (P, tile) of path 2 whose slice fits, in
+ * that order; a held tile is listed when at least half of it is used or when
+ * it is the smallest tile that holds the row (or slice).  Each plan carries
+ * the model's estimate in predicted_us[path - 1] (the other two entries are
+ * -1).  Writes min(capacity, *count) plans to `out` and the total number
+ * to *count (call with capacity 0 to size the array).  For exhaustive timing,
+ * the final search among legal candidates that the selector's screen narrows.
+ * Host-only.
+ */
+credit_status_t credit_enumerate_plans(credit_op_t op, credit_dtype_t dt, int64_t rows, int64_t cols,
+                                       credit_plan_t *out, int32_t capacity, int32_t *count);
 
 /*
  * Run one operator with an explicit plan (as returned by credit_select_path,

@@ -27,6 +27,7 @@ OPS = {"softmax": 0, "layernorm": 1, "rmsnorm": 2}
 DTYPES = {"f32": 0, "bf16": 1}
 
 EXPORTED = ["credit_softmax", "credit_layernorm", "credit_rmsnorm", "credit_select_path", "credit_make_plan",
+            "credit_enumerate_plans",
             "credit_run_plan", "credit_run_plan_timed", "credit_control", "credit_copy", "credit_flush",
             "credit_load_calibration", "credit_check_errors", "credit_status_str", "credit_version"]
 
@@ -39,18 +40,20 @@ class CreditError(RuntimeError):
 
 class Plan(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("split_p", ctypes.c_int32), ("block_threads", ctypes.c_int32),
-                ("items", ctypes.c_int32), ("vec_bytes", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("items", ctypes.c_int32), ("vec_bytes", ctypes.c_int32), ("wgs_per_cu", ctypes.c_int32),
                 ("predicted_us", ctypes.c_double * 3)]
 
     def as_dict(self) -> dict:
         return {"path": self.path, "split_p": self.split_p, "block_threads": self.block_threads,
-                "items": self.items, "vec_bytes": self.vec_bytes,
+                "items": self.items, "vec_bytes": self.vec_bytes, "wgs_per_cu": self.wgs_per_cu,
                 "predicted_us": [self.predicted_us[i] for i in range(3)]}
 
     @classmethod
-    def make(cls, path: int, split_p: int, block_threads: int, items: int, vec_bytes: int = 0) -> "Plan":
+    def make(cls, path: int, split_p: int, block_threads: int, items: int, vec_bytes: int = 0,
+             wgs_per_cu: int = 0) -> "Plan":
         p = cls()
         p.path, p.split_p, p.block_threads, p.items, p.vec_bytes = path, split_p, block_threads, items, vec_bytes
+        p.wgs_per_cu = wgs_per_cu
         return p
 
 
@@ -79,6 +82,7 @@ def lib() -> ctypes.CDLL:
         "credit_rmsnorm": [vp, vp, vp, i64, i64, f32, i32, i32, i32, vp],
         "credit_select_path": [i32, i32, i64, i64, ctypes.POINTER(Plan)],
         "credit_make_plan": [i32, i32, i64, i64, i32, i32, ctypes.POINTER(Plan)],
+        "credit_enumerate_plans": [i32, i32, i64, i64, ctypes.POINTER(Plan), i32, ctypes.POINTER(i32)],
         "credit_run_plan": [i32, vp, vp, vp, vp, i64, i64, f32, i32, ctypes.POINTER(Plan), vp],
         "credit_run_plan_timed": [i32, vp, vp, vp, vp, i64, i64, f32, i32, ctypes.POINTER(Plan), vp, vp, vp],
         "credit_control": [i32, i64, i64, i32, ctypes.POINTER(Plan), vp],
@@ -185,6 +189,18 @@ def credit_plan(op, dtype, rows: int, cols: int, path="auto", split_p: int = 0) 
     dt = DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
     _check(lib().credit_make_plan(op, dt, rows, cols, _path(path), split_p, ctypes.byref(p)), "credit_make_plan")
     return p
+
+
+def credit_enumerate_plans(op, dtype, rows: int, cols: int):
+    """Every legal plan for the shape (credit_enumerate_plans), as a list of Plan."""
+    op = OPS[op] if isinstance(op, str) else int(op)
+    dt = DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
+    n = ctypes.c_int32()
+    _check(lib().credit_enumerate_plans(op, dt, rows, cols, None, 0, ctypes.byref(n)), "credit_enumerate_plans")
+    arr = (Plan * max(1, n.value))()
+    _check(lib().credit_enumerate_plans(op, dt, rows, cols, arr, n.value, ctypes.byref(n)),
+           "credit_enumerate_plans")
+    return [arr[i] for i in range(n.value)]
 
 
 def credit_run_plan(op, x, gamma, beta, y, eps: float, plan: Plan, stream=None):

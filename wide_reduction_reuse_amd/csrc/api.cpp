@@ -219,11 +219,35 @@ credit_status_t launch_raw(const KernelEntry *k, uint32_t grid, uint32_t block, 
     return CREDIT_OK;
 }
 
-credit_status_t launch_rowwise(const KernelEntry *k, const RowArgs &a0, hipStream_t s, const LaunchEvents &ev)
+// Workgroups of kernel `k` one CU holds at once; cached per kernel.
+credit_status_t occupancy(const KernelEntry *k, int *out);
+
+// Paths 1 and 3.  Path 1 kernels loop over rows: with wgs_per_cu == 0 the grid
+// is as many workgroups as the device holds at once (each owner then takes
+// every G-th row, loading the next row while it writes the current one), with
+// k > 0 at most k workgroups per CU, and with -1 one workgroup per row (or per
+// four rows for wave-per-row).  The reread kernel always takes one row per
+// workgroup.
+credit_status_t launch_rowwise(const KernelEntry *k, const RowArgs &a0, int wgs_per_cu, hipStream_t s,
+                               const LaunchEvents &ev)
 {
     const int64_t rows_per_wg = k->kind == kKindWave ? kWaveRowsPerWg : 1;
     const int block = k->kind == kKindWave ? 64 * kWaveRowsPerWg : k->block;
     const int64_t eb = elem_bytes(k->dt);
+    int64_t grid_cap = kMaxGridWgs;
+    if (k->kind != kKindReread && wgs_per_cu >= 0) {
+        int occ = 0;
+        const credit_status_t st = occupancy(k, &occ);
+        if (st != CREDIT_OK)
+            return st;
+        DeviceModel d;
+        {
+            std::lock_guard<std::mutex> lk(g_mu);
+            d = device_model_locked();
+        }
+        const int per_cu = wgs_per_cu == 0 ? occ : std::min(occ, wgs_per_cu);
+        grid_cap = std::max<int64_t>(1, static_cast<int64_t>(per_cu) * d.cus);
+    }
     const int64_t chunk_rows = kMaxGridWgs * rows_per_wg;
     for (int64_t r0 = 0; r0 < a0.rows; r0 += chunk_rows) {
         RowArgs a = a0;
@@ -232,7 +256,7 @@ credit_status_t launch_rowwise(const KernelEntry *k, const RowArgs &a0, hipStrea
         a.x = static_cast<const char *>(a0.x) + off;
         a.y = static_cast<char *>(a0.y) + off;
         a.rows = n;
-        const int64_t grid = (n + rows_per_wg - 1) / rows_per_wg;
+        const int64_t grid = std::min(grid_cap, (n + rows_per_wg - 1) / rows_per_wg);
         const credit_status_t st = launch_raw(k, static_cast<uint32_t>(grid), block, &a, s,
                                               r0 == 0 ? ev.start : nullptr,
                                               r0 + n >= a0.rows ? ev.stop : nullptr);
@@ -265,8 +289,8 @@ credit_status_t occupancy(const KernelEntry *k, int *out)
     return CREDIT_OK;
 }
 
-credit_status_t launch_split(const KernelEntry *k, const RowArgs &a0, int p, int q, hipStream_t s,
-                             const LaunchEvents &ev)
+credit_status_t launch_split(const KernelEntry *k, const RowArgs &a0, int p, int q, int wgs_per_cu,
+                             hipStream_t s, const LaunchEvents &ev)
 {
     int occ = 0;
     credit_status_t st = occupancy(k, &occ);
@@ -275,6 +299,8 @@ credit_status_t launch_split(const KernelEntry *k, const RowArgs &a0, int p, int
     std::lock_guard<std::mutex> lk(g_mu);
     const DeviceModel d = device_model_locked();
     const int64_t resident = static_cast<int64_t>(occ) * d.cus;
+    // wgs_per_cu > 0 caps the clusters (never above what the device holds)
+    const int64_t allowed = wgs_per_cu > 0 ? std::min<int64_t>(resident, int64_t(wgs_per_cu) * d.cus) : resident;
     if (resident < p)
         return CREDIT_ERR_NOT_CORESIDENT;
     Scratch *sc = nullptr;
@@ -283,7 +309,7 @@ credit_status_t launch_split(const KernelEntry *k, const RowArgs &a0, int p, int
         return st;
     // persistent clusters: as many as the device holds at once and the
     // exchange words cover, never more than there are rows
-    const int64_t clusters = std::min({resident / p, kSlotWords / (INT64_C(2) * p * q), a0.rows});
+    const int64_t clusters = std::min({std::max<int64_t>(1, allowed / p), kSlotWords / (INT64_C(2) * p * q), a0.rows});
     const int64_t max_iters = INT64_C(1) << 30;  // row iterations per launch (tag range)
     const int64_t rows_per_launch = clusters * max_iters;
     const int64_t eb = elem_bytes(k->dt);
@@ -378,6 +404,7 @@ void to_c_plan(const Plan &p, credit_plan_t *out)
     out->block_threads = p.tile.block;
     out->items = p.tile.items;
     out->vec_bytes = p.tile.vb;
+    out->wgs_per_cu = p.wgs_per_cu;
     for (int i = 0; i < 3; ++i)
         out->predicted_us[i] = p.est[i].legal ? p.est[i].us : -1.0;
 }
@@ -411,8 +438,8 @@ credit_status_t run_plan_checked(int op, const void *x, const void *g, const voi
                      op, dt, static_cast<long long>(rows), static_cast<long long>(cols), plan.path, plan.split_p,
                      plan.block_threads, plan.items, k->vb, control ? " (control)" : "");
     if (kind == kKindSplit)
-        return launch_split(k, a, plan.split_p, stats_per_partial(op), s, ev);
-    return launch_rowwise(k, a, s, ev);
+        return launch_split(k, a, plan.split_p, stats_per_partial(op), plan.wgs_per_cu, s, ev);
+    return launch_rowwise(k, a, plan.wgs_per_cu, s, ev);
 }
 
 credit_status_t run_op(int op, const void *x, const void *g, const void *b, void *y, int64_t rows, int64_t cols,
@@ -512,6 +539,40 @@ credit_status_t credit_make_plan(credit_op_t op, credit_dtype_t dt, int64_t rows
     if (!make_plan(req, cal, path, split_p <= 1 ? 0 : split_p, &p))
         return CREDIT_ERR_ILLEGAL_PATH;
     to_c_plan(p, out);
+    return CREDIT_OK;
+}
+
+credit_status_t credit_enumerate_plans(credit_op_t op, credit_dtype_t dt, int64_t rows, int64_t cols,
+                                       credit_plan_t *out, int32_t capacity, int32_t *count)
+{
+    if (count == nullptr || capacity < 0 || (out == nullptr && capacity > 0) || op < 0 || op > 2 ||
+        (dt != CREDIT_F32 && dt != CREDIT_BF16) || rows < 0 || cols < 1)
+        return CREDIT_ERR_INVALID_ARG;
+    std::vector<Candidate> cands;
+    {
+        std::lock_guard<std::mutex> lk(g_mu);
+        Calibration cal = g_cal;
+        cal.device = device_model_locked();
+        PlanRequest req;
+        req.op = op;
+        req.dt = dt;
+        req.rows = rows;
+        req.cols = cols;
+        enumerate_candidates(req, cal, &cands);
+    }
+    *count = static_cast<int32_t>(cands.size());
+    for (int32_t i = 0; i < capacity && i < *count; ++i) {
+        credit_plan_t &c = out[i];
+        std::memset(&c, 0, sizeof(c));
+        c.path = cands[i].path;
+        c.split_p = cands[i].split_p;
+        c.block_threads = cands[i].est.tile.block;
+        c.items = cands[i].est.tile.items;
+        c.vec_bytes = cands[i].est.tile.vb;
+        c.wgs_per_cu = cands[i].wgs_per_cu;
+        for (int j = 0; j < 3; ++j)
+            c.predicted_us[j] = j == cands[i].path - 1 ? cands[i].est.us : -1.0;
+    }
     return CREDIT_OK;
 }
 

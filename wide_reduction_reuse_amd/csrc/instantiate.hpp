@@ -12,8 +12,9 @@ void register_op_dtype(std::vector<KernelEntry> &v)
 {
     constexpr int VB = 16;
     constexpr int VS = StorageTraits<T>::kBytes;  // one-element access
-#define CREDIT_K(kind, vb, block, items, ...) \
-    v.push_back(KernelEntry{kind, OP, DT, vb, block, items, reinterpret_cast<const void *>(&__VA_ARGS__)})
+#define CREDIT_K(kind, vb, block, items, ...)                                                                  \
+    if constexpr (tile_enabled(OP, kind, block, items, vb))                                                       \
+        v.push_back(KernelEntry{kind, OP, DT, vb, block, items, reinterpret_cast<const void *>(&__VA_ARGS__)})
 #define WAVE(it) CREDIT_K(kKindWave, VB, 64, it, single_wave_kernel<OP, T, VB, it>);
 #define WG(b, it) CREDIT_K(kKindWg, VB, b, it, single_wg_kernel<OP, T, VB, b, it>);
 #define SPLIT(b, it)                                                        \

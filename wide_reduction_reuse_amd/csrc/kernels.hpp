@@ -112,45 +112,180 @@ __device__ __forceinline__ RawVec<VB> apply_vec(const RawVec<VB> &in, const RawV
     return pack<T, VB, E>(out);
 }
 
-// Parameter vectors fetched per group of the output loop: four while the held
-// tile is small, two when it already takes 64 VGPRs.
-template <int IT, int VB>
+// Parameter vectors fetched per group of the output loop when they are
+// re-read for every row: four while the held tile is small; when it already
+// takes 64 VGPRs, two (one pair for LayerNorm's two parameters).
+template <int IT, int VB, int NP>
 constexpr int param_group()
 {
-    return IT * VB / 4 >= 64 ? (IT < 2 ? IT : 2) : (IT < 4 ? IT : 4);
+    return IT * VB / 4 >= 64 ? (NP >= 2 ? 1 : (IT < 2 ? IT : 2)) : (IT < 4 ? IT : 4);
 }
 
-// Apply h to the held tile and write it out.  dst, gam and bet describe the
-// same columns (the row or slice); parameter vectors are fetched a group at a
-// time ahead of the arithmetic that needs them.
-template <OpKind OP, class T, int VB, int IT, int G>
-__device__ __forceinline__ void store_tile(Tile<T, VB, IT> &t, rsrc_t dst, rsrc_t gam, rsrc_t bet, int pos,
-                                           const Coef &c)
+// ---------------------------------------------------------------------------
+// Parameter vectors (gamma, beta) of the columns a thread holds.  They are the
+// same for every row, so a persistent owner fetches them once:
+//   kParamNone   the operator has none (softmax);
+//   kParamReg    held in VGPRs next to the tile, when both fit in 64 VGPRs;
+//   kParamLds    staged in LDS once per workgroup, when that takes <= 64 KiB;
+//   kParamDirect re-read from L2 for every row, a few vectors ahead of use.
+// With the first three the output loop also loads the next row (below): its
+// parameter reads do not queue behind HBM loads.  kParamDirect cannot do that
+// (vector-memory loads complete in issue order, so a parameter load issued
+// after the next row's loads would wait for them) and loads the next row
+// after the output loop instead.
+// ---------------------------------------------------------------------------
+enum ParamMode { kParamNone = 0, kParamReg = 1, kParamLds = 2, kParamDirect = 3 };
+
+// Which mode a kernel uses.  G: threads that together hold one row's (or
+// slice's) columns.  Measured on MI355X: a workgroup-per-row kernel runs one
+// row per workgroup, where an LDS or register copy only lowers occupancy, so
+// it re-reads (kOwnerRow); the four waves of a wave-per-row workgroup share
+// one LDS copy (kOwnerWaves); a split-row workgroup keeps its slice's columns
+// for every row of its cluster (kOwnerSlice).
+enum OwnerKind { kOwnerRow = 0, kOwnerWaves = 1, kOwnerSlice = 2 };
+
+template <OpKind OP, int VB, int IT, int G, int OWNER>
+constexpr int param_mode()
 {
-    using Op = OpTraits<OP>;
-    constexpr int GP = param_group<IT, VB>();
-    fence_tile(t);
-    // recompute the offsets here (one add each) instead of keeping the load
-    // phase's sixteen offset registers alive across the reduction
-    uint32_t base = static_cast<uint32_t>(pos) * VB;
-    asm volatile("" : "+v"(base));
+    constexpr int np = OpTraits<OP>::kParams;
+    // tile + parameter VGPRs allowed: 64, but 32 for LayerNorm at 1024
+    // threads, whose 128-VGPR cap leaves less room beside its statistics
+    constexpr int reg_budget = (G >= 1024 && np >= 2) ? 32 : 64;
+    if (np == 0)
+        return kParamNone;
+    if (OWNER == kOwnerRow)
+        return kParamDirect;
+    if (OWNER == kOwnerSlice && (np + 1) * IT * VB / 4 <= reg_budget)
+        return kParamReg;
+    if (np * G * IT * VB <= 64 * 1024)
+        return kParamLds;
+    return kParamDirect;
+}
+
+template <OpKind OP, int VB, int IT, int G, int OWNER>
+constexpr int param_lds_vectors()
+{
+    return param_mode<OP, VB, IT, G, OWNER>() == kParamLds ? OpTraits<OP>::kParams * G * IT : 1;
+}
+
+template <OpKind OP, class T, int VB, int IT, int G, int OWNER>
+struct ParamCache {
+    static constexpr int kMode = param_mode<OP, VB, IT, G, OWNER>();
+    static constexpr int kNp = OpTraits<OP>::kParams;
+    static constexpr int kRegs = kMode == kParamReg ? IT : 1;
+    rsrc_t gam, bet;         // kParamDirect
+    RawVec<VB> g[kRegs], b[kRegs];  // kParamReg
+    const RawVec<VB> *lds;   // kParamLds: [kNp][IT][G], vector k of thread pos at k*G + pos
+
+    // Call once per owner, before the row loop.  `nthreads` threads with ids
+    // `tid` fill the LDS copy (kParamLds); the caller puts a barrier between
+    // this and the first get().
+    __device__ __forceinline__ void init(rsrc_t gam_, rsrc_t bet_, int pos, RawVec<VB> *lds_buf, int tid,
+                                         int nthreads)
+    {
+        gam = gam_;
+        bet = bet_;
+        lds = lds_buf;
+        if constexpr (kMode == kParamReg) {
 #pragma unroll
-    for (int kb = 0; kb < IT; kb += GP) {
-        RawVec<VB> g[GP], b[GP];
-#pragma unroll
-        for (int j = 0; j < GP; ++j) {
-            const uint32_t off = base + static_cast<uint32_t>((kb + j) * G * VB);
-            if constexpr (Op::kParams >= 1)
-                g[j] = buf_load<VB, kKeep>(gam, off);
-            if constexpr (Op::kParams >= 2)
-                b[j] = buf_load<VB, kKeep>(bet, off);
-        }
-#pragma unroll
-        for (int j = 0; j < GP; ++j) {
-            const uint32_t off = base + static_cast<uint32_t>((kb + j) * G * VB);
-            buf_store<VB, kStream>(apply_vec<OP, T, VB, false>(t.v[kb + j], g[j], b[j], c), dst, off);
+            for (int k = 0; k < IT; ++k) {
+                const uint32_t off = static_cast<uint32_t>(pos + k * G) * VB;
+                g[k] = buf_load<VB, kKeep>(gam, off);
+                if constexpr (kNp >= 2)
+                    b[k] = buf_load<VB, kKeep>(bet, off);
+            }
+        } else if constexpr (kMode == kParamLds) {
+            for (int i = tid; i < G * IT; i += nthreads) {
+                lds_buf[i] = buf_load<VB, kKeep>(gam, static_cast<uint32_t>(i) * VB);
+                if constexpr (kNp >= 2)
+                    lds_buf[G * IT + i] = buf_load<VB, kKeep>(bet, static_cast<uint32_t>(i) * VB);
+            }
         }
     }
+
+    __device__ __forceinline__ void get(int k, int pos, RawVec<VB> &gk, RawVec<VB> &bk) const
+    {
+        if constexpr (kMode == kParamReg) {
+            gk = g[k];
+            if constexpr (kNp >= 2)
+                bk = b[k];
+        } else if constexpr (kMode == kParamLds) {
+            gk = lds[k * G + pos];
+            if constexpr (kNp >= 2)
+                bk = lds[G * IT + k * G + pos];
+        }
+    }
+};
+
+// Whether the output loop loads the next row into the registers it frees
+// ("rolling"), for owners that loop over rows.  Measured on MI355X it did not
+// pay: one-row-per-owner path 1 launches were as fast or faster than rolling
+// persistent ones, and the split kernel streamed about 5% slower with it, so
+// it is off; the code path is kept for kernels where it is switched on.
+constexpr bool kRollNextRow = false;
+
+template <int MODE>
+constexpr bool rolls()
+{
+    return kRollNextRow && MODE != kParamDirect;
+}
+
+// Apply h to the held tile and write it out; dst, and the parameter
+// descriptors, cover the same columns (the row or slice).  When rolling,
+// vector k of the next row (`next`, a zero-length descriptor when there is
+// none: its loads return zero without touching memory) is loaded into the
+// register that vector k of this row leaves free.
+template <OpKind OP, class T, int VB, int IT, int G, int OWNER>
+__device__ __forceinline__ void store_tile(Tile<T, VB, IT> &t, rsrc_t dst,
+                                           const ParamCache<OP, T, VB, IT, G, OWNER> &pc, int pos, const Coef &c,
+                                           rsrc_t next)
+{
+    using Op = OpTraits<OP>;
+    constexpr int MODE = ParamCache<OP, T, VB, IT, G, OWNER>::kMode;
+    fence_tile(t);
+    // recompute the offsets here (one add each) instead of keeping the load
+    // phase's offset registers alive across the reduction
+    uint32_t base = static_cast<uint32_t>(pos) * VB;
+    asm volatile("" : "+v"(base));
+    (void)next;
+    if constexpr (MODE != kParamDirect) {
+#pragma unroll
+        for (int k = 0; k < IT; ++k) {
+            const uint32_t off = base + static_cast<uint32_t>(k * G * VB);
+            RawVec<VB> g, b;
+            pc.get(k, pos, g, b);
+            buf_store<VB, kStream>(apply_vec<OP, T, VB, false>(t.v[k], g, b, c), dst, off);
+            if constexpr (rolls<MODE>())
+                t.v[k] = buf_load<VB, kStream>(next, off);
+        }
+    } else {
+        constexpr int GP = param_group<IT, VB, Op::kParams>();
+#pragma unroll
+        for (int kb = 0; kb < IT; kb += GP) {
+            RawVec<VB> g[GP], b[GP];
+#pragma unroll
+            for (int j = 0; j < GP; ++j) {
+                const uint32_t off = base + static_cast<uint32_t>((kb + j) * G * VB);
+                if constexpr (Op::kParams >= 1)
+                    g[j] = buf_load<VB, kKeep>(pc.gam, off);
+                if constexpr (Op::kParams >= 2)
+                    b[j] = buf_load<VB, kKeep>(pc.bet, off);
+            }
+#pragma unroll
+            for (int j = 0; j < GP; ++j) {
+                const uint32_t off = base + static_cast<uint32_t>((kb + j) * G * VB);
+                buf_store<VB, kStream>(apply_vec<OP, T, VB, false>(t.v[kb + j], g[j], b[j], c), dst, off);
+            }
+        }
+    }
+}
+
+// After store_tile: load the next row unless store_tile already did.
+template <OpKind OP, class T, int VB, int IT, int G, int OWNER>
+__device__ __forceinline__ void load_next(Tile<T, VB, IT> &t, rsrc_t next, int pos)
+{
+    if constexpr (!rolls<ParamCache<OP, T, VB, IT, G, OWNER>::kMode>())
+        load_tile<T, VB, IT, G>(t, next, pos);
 }
 
 // Combine the wave partials of a workgroup through LDS; every thread returns
@@ -182,49 +317,73 @@ __device__ __forceinline__ rsrc_t span(const void *base, int64_t first, int64_t 
 }
 
 // ---------------------------------------------------------------------------
-// Path 1a: one wavefront per row, four rows per 256-thread workgroup.  No LDS
-// and no barrier: the wave reduction is the row reduction.
+// Path 1a: one wavefront per row, four waves per 256-thread workgroup; wave w
+// of the grid handles rows w, w + W, w + 2W, ... (W waves in the grid).  No
+// barrier on the row: the wave reduction is the row reduction.
 // ---------------------------------------------------------------------------
 template <OpKind OP, class T, int VB, int IT>
 __global__ __launch_bounds__(kWave *kWaveRowsPerWg) void single_wave_kernel(RowArgs a)
 {
     using Op = OpTraits<OP>;
+    using PC = ParamCache<OP, T, VB, IT, kWave, kOwnerWaves>;
     constexpr int E = VB / StorageTraits<T>::kBytes;
+    __shared__ RawVec<VB> lds_params[param_lds_vectors<OP, VB, IT, kWave, kOwnerWaves>()];
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t row = uniform(static_cast<int64_t>(blockIdx.x) * kWaveRowsPerWg + threadIdx.x / kWave);
-    if (row >= a.rows)
-        return;  // wave-uniform
     const int64_t nv = a.cols / E;
+    const int64_t waves = static_cast<int64_t>(gridDim.x) * kWaveRowsPerWg;
+    int64_t row = uniform(static_cast<int64_t>(blockIdx.x) * kWaveRowsPerWg + threadIdx.x / kWave);
     Tile<T, VB, IT> t;
-    load_tile<T, VB, IT, kWave>(t, span<VB>(a.x, row * nv, nv), lane);
+    load_tile<T, VB, IT, kWave>(t, span<VB>(a.x, row * nv, row < a.rows ? nv : 0), lane);
+    PC pc;
+    pc.init(span<VB>(a.gamma, 0, nv), span<VB>(a.beta, 0, nv), lane, lds_params, threadIdx.x,
+            kWave * kWaveRowsPerWg);
+    if constexpr (PC::kMode == kParamLds)
+        __syncthreads();
     const int kv = count_valid<IT, kWave>(nv, lane);
-    const Partial wp = tile_partial<OP, T, VB, IT>(t, kv);
-    const Coef c = Op::template finalize<T>(wp, wp, a.cols, a.eps);
-    store_tile<OP, T, VB, IT, kWave>(t, span<VB>(a.y, row * nv, nv), span<VB>(a.gamma, 0, nv),
-                                     span<VB>(a.beta, 0, nv), lane, c);
+    for (; row < a.rows; row += waves) {
+        const int64_t next = row + waves;
+        const Partial wp = tile_partial<OP, T, VB, IT>(t, kv);
+        const Coef c = Op::template finalize<T>(wp, wp, a.cols, a.eps);
+        const rsrc_t nsrc = span<VB>(a.x, next * nv, next < a.rows ? nv : 0);
+        store_tile<OP, T, VB, IT, kWave, kOwnerWaves>(t, span<VB>(a.y, row * nv, nv), pc, lane, c, nsrc);
+        load_next<OP, T, VB, IT, kWave, kOwnerWaves>(t, nsrc, lane);
+    }
 }
 
 // ---------------------------------------------------------------------------
-// Path 1b: one workgroup of BLOCK threads per row.
+// Path 1b: one workgroup of BLOCK threads per row; workgroup g handles rows
+// g, g + G, g + 2G, ... (G workgroups in the grid).
 // ---------------------------------------------------------------------------
 template <OpKind OP, class T, int VB, int BLOCK, int IT>
 __global__ __launch_bounds__(BLOCK) void single_wg_kernel(RowArgs a)
 {
     using Op = OpTraits<OP>;
+    using PC = ParamCache<OP, T, VB, IT, BLOCK, kOwnerRow>;
     constexpr int E = VB / StorageTraits<T>::kBytes;
     constexpr int NW = BLOCK / kWave;
     __shared__ Partial sh[NW];
+    __shared__ RawVec<VB> lds_params[param_lds_vectors<OP, VB, IT, BLOCK, kOwnerRow>()];
     const int tid = threadIdx.x;
-    const int64_t row = blockIdx.x;
     const int64_t nv = a.cols / E;
+    int64_t row = blockIdx.x;
     Tile<T, VB, IT> t;
     load_tile<T, VB, IT, BLOCK>(t, span<VB>(a.x, row * nv, nv), tid);
+    PC pc;
+    pc.init(span<VB>(a.gamma, 0, nv), span<VB>(a.beta, 0, nv), tid, lds_params, tid, BLOCK);
+    if constexpr (PC::kMode == kParamLds)
+        __syncthreads();
     const int kv = count_valid<IT, BLOCK>(nv, tid);
-    const Partial wp = tile_partial<OP, T, VB, IT>(t, kv);
-    const Partial rp = block_combine<OP, NW>(wp, sh);
-    const Coef c = Op::template finalize<T>(rp, wp, a.cols, a.eps);
-    store_tile<OP, T, VB, IT, BLOCK>(t, span<VB>(a.y, row * nv, nv), span<VB>(a.gamma, 0, nv),
-                                     span<VB>(a.beta, 0, nv), tid, c);
+    for (; row < a.rows; row += gridDim.x) {
+        const int64_t next = row + gridDim.x;
+        const Partial wp = tile_partial<OP, T, VB, IT>(t, kv);
+        const Partial rp = block_combine<OP, NW>(wp, sh);
+        const Coef c = Op::template finalize<T>(rp, wp, a.cols, a.eps);
+        const rsrc_t nsrc = span<VB>(a.x, next * nv, next < a.rows ? nv : 0);
+        store_tile<OP, T, VB, IT, BLOCK, kOwnerRow>(t, span<VB>(a.y, row * nv, nv), pc, tid, c, nsrc);
+        load_next<OP, T, VB, IT, BLOCK, kOwnerRow>(t, nsrc, tid);
+        // the next block_combine rewrites sh: every wave must have read it
+        __syncthreads();
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -236,12 +395,14 @@ template <OpKind OP, class T, int VB, int BLOCK, int IT, bool CONTROL>
 __global__ __launch_bounds__(BLOCK) void split_kernel(SplitArgs a)
 {
     using Op = OpTraits<OP>;
+    using PC = ParamCache<OP, T, VB, IT, BLOCK, kOwnerSlice>;
     constexpr int E = VB / StorageTraits<T>::kBytes;
     constexpr int NW = BLOCK / kWave;
     constexpr int Q = Op::kQ;
     __shared__ Partial sh[NW];
     __shared__ Partial peer[kMaxSplit];
     __shared__ uint32_t sh_ticket;
+    __shared__ RawVec<VB> lds_params[param_lds_vectors<OP, VB, IT, BLOCK, kOwnerSlice>()];
     const int tid = threadIdx.x;
     if (tid == 0)
         sh_ticket = fetch_add_u32_agent(a.ticket, 1u) - a.ticket_base;
@@ -258,22 +419,21 @@ __global__ __launch_bounds__(BLOCK) void split_kernel(SplitArgs a)
     const int64_t v0 = min(nv, per * c);
     const int64_t ns = min(nv, v0 + per) - v0;  // vectors in this slice
     const int kv = count_valid<IT, BLOCK>(ns, tid);
-    const rsrc_t gam = span<VB>(a.r.gamma, v0, ns);
-    const rsrc_t bet = span<VB>(a.r.beta, v0, ns);
     uint64_t *cslots = a.slots + k * 2 * P * Q;
+
+    // CONTROL: a zero-length source, so every load returns zero without
+    // touching memory, and a zero-length destination that drops every store
+    const int64_t nload = CONTROL ? 0 : ns;
+    Tile<T, VB, IT> t;
+    load_tile<T, VB, IT, BLOCK>(t, span<VB>(a.r.x, k * nv + v0, k < a.r.rows ? nload : 0), tid);
+    PC pc;
+    pc.init(span<VB>(a.r.gamma, v0, ns), span<VB>(a.r.beta, v0, ns), tid, lds_params, tid, BLOCK);
+    if constexpr (PC::kMode == kParamLds)
+        __syncthreads();
 
     uint32_t it = 0;
     for (int64_t row = k; row < a.r.rows; row += a.clusters, ++it) {
-        Tile<T, VB, IT> t;
-        if constexpr (CONTROL) {
-#pragma unroll
-            for (int q = 0; q < IT; ++q)
-#pragma unroll
-                for (int w = 0; w < RawVec<VB>::kWords; ++w)
-                    set_word<VB>(t.v[q], w, 0u);
-        } else {
-            load_tile<T, VB, IT, BLOCK>(t, span<VB>(a.r.x, row * nv + v0, ns), tid);
-        }
+        const int64_t next = row + a.clusters;
         const Partial wp = tile_partial<OP, T, VB, IT>(t, kv);
         const Partial sp = block_combine<OP, NW>(wp, sh);
 
@@ -302,8 +462,12 @@ __global__ __launch_bounds__(BLOCK) void split_kernel(SplitArgs a)
             parts[i] = peer[i];
         const Partial rp = Op::template merge<kMaxSplit>(parts, P);
         const Coef cf = Op::template finalize<T>(rp, wp, a.r.cols, a.r.eps);
-        if constexpr (!CONTROL)
-            store_tile<OP, T, VB, IT, BLOCK>(t, span<VB>(a.r.y, row * nv + v0, ns), gam, bet, tid, cf);
+        const rsrc_t nsrc = span<VB>(a.r.x, next * nv + v0, next < a.r.rows ? nload : 0);
+        store_tile<OP, T, VB, IT, BLOCK, kOwnerSlice>(t, span<VB>(a.r.y, row * nv + v0, nload), pc, tid, cf, nsrc);
+        load_next<OP, T, VB, IT, BLOCK, kOwnerSlice>(t, nsrc, tid);
+        // (no barrier needed before the next iteration rewrites sh or peer:
+        // every wave has read sh before the exchange barrier above and reads
+        // peer before it reaches the next block_combine barrier)
     }
 }
 

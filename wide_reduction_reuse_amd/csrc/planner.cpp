@@ -121,7 +121,7 @@ bool single_tile(int dt, int64_t cols, TileSpec *out)
     return false;
 }
 
-bool split_tile(int dt, int64_t cols, int p, TileSpec *out)
+bool split_tile(int op, int dt, int64_t cols, int p, TileSpec *out)
 {
     if (p != 2 && p != 4 && p != 8)
         return false;
@@ -130,8 +130,12 @@ bool split_tile(int dt, int64_t cols, int p, TileSpec *out)
     const int64_t per = (nv + p - 1) / p;
     if (per * (p - 1) >= nv)
         return false;  // the last slice would be empty: too narrow to split p ways
+    std::vector<TileSpec> ladder;
+    for (const TileSpec &u : tiles_for(kKindSplit, vb == 16))
+        if (tile_enabled(op, kKindSplit, u.block, u.items, vb))
+            ladder.push_back(u);
     TileSpec t;
-    if (!pick_holding_tile(tiles_for(kKindSplit, vb == 16), per, &t))
+    if (!pick_holding_tile(ladder, per, &t))
         return false;
     t.vb = vb;
     *out = t;
@@ -211,74 +215,107 @@ double stream_us(const Model &m, const DeviceModel &d, double bytes, double unit
 
 }  // namespace
 
+namespace {
+
+struct Shape {
+    double M, N, b, row_bytes, bytes_io;
+};
+
+Shape shape_of(const PlanRequest &req)
+{
+    Shape s;
+    s.M = static_cast<double>(req.rows);
+    s.N = static_cast<double>(req.cols);
+    s.b = elem_bytes(req.dt);
+    s.row_bytes = s.N * s.b;
+    s.bytes_io = s.M * s.N * 2.0 * s.b + s.N * s.b * n_params(req.op);
+    return s;
+}
+
+PathEstimate estimate_single(const PlanRequest &req, const Calibration &cal, const TileSpec &t)
+{
+    const Model m = model_of(cal);
+    const Shape s = shape_of(req);
+    PathEstimate e;
+    e.legal = true;
+    e.tile = t;
+    const double units = t.kind == kKindWave ? std::ceil(s.M / 4.0) : s.M;
+    e.t_stream_us = stream_us(m, cal.device, s.bytes_io, units, wgs_per_cu(t));
+    e.us = m.launch_us + e.t_stream_us * eff_of(cal.single_eff, req.op, req.dt);
+    return e;
+}
+
+// The reread is served on chip when the rows in flight on one XCD fit its L2,
+// from the Infinity Cache when all rows in flight fit it (counted as half an
+// HBM read), else from HBM.
+PathEstimate estimate_reread(const PlanRequest &req, const Calibration &cal, const TileSpec &t)
+{
+    const Model m = model_of(cal);
+    const DeviceModel &d = cal.device;
+    const Shape s = shape_of(req);
+    PathEstimate e;
+    e.legal = true;
+    e.tile = t;
+    const double resident = std::min(s.M, static_cast<double>(d.cus) * wgs_per_cu(t));
+    const double per_xcd = resident / d.xcds;
+    double miss;
+    if (per_xcd * s.row_bytes <= d.l2_bytes_per_xcd)
+        miss = 1.0 - m.hit_l2;
+    else if (resident * s.row_bytes <= d.mall_bytes)
+        miss = 0.5;
+    else
+        miss = 1.0;
+    const double bytes3 = s.bytes_io + s.M * s.N * s.b * miss;
+    e.t_stream_us = stream_us(m, d, bytes3, s.M, wgs_per_cu(t));
+    e.us = m.launch_us + e.t_stream_us * eff_of(cal.reread_eff, req.op, req.dt);
+    return e;
+}
+
+// Path 2 at split P against the non-split baseline `base` (path 1 if legal,
+// else path 3): the row streams once over M*P workgroups and pays one exchange
+// round per row wave (Eq. 8); Eq. 7 prices the avoided reread.
+PathEstimate estimate_split(const PlanRequest &req, const Calibration &cal, int P, const TileSpec &t,
+                            const PathEstimate &base, bool base_is_single)
+{
+    const Model m = model_of(cal);
+    const DeviceModel &d = cal.device;
+    const Shape s = shape_of(req);
+    const double b_base = base_is_single ? 2.0 * s.b : 3.0 * s.b;  // bytes/element of the baseline schedule
+    const double b_reread = base_is_single ? 0.0 : s.b;
+    PathEstimate e;
+    e.legal = true;
+    e.split_p = P;
+    e.tile = t;
+    const double clusters = std::max(1.0, std::floor(static_cast<double>(d.cus) * wgs_per_cu(t) / P));
+    e.waves = std::ceil(s.M / clusters);
+    e.t_stream_us = stream_us(m, d, s.bytes_io, s.M * P, wgs_per_cu(t));
+    e.t_ctrl_us = e.waves * m.exchange_us;
+    e.t_save_us = (b_reread / b_base) * base.us;  // Eq. 7
+    e.us = m.launch_us + e.t_stream_us * eff_of(cal.split_eff, req.op, req.dt) + e.t_ctrl_us;
+    return e;
+}
+
+}  // namespace
+
 bool make_plan(const PlanRequest &req, const Calibration &cal, int forced_path, int forced_p, Plan *out)
 {
-    const DeviceModel &d = cal.device;
-    const Model m = model_of(cal);
-    const double M = static_cast<double>(req.rows), N = static_cast<double>(req.cols);
-    const int b = elem_bytes(req.dt);
-    const double row_bytes = N * b;
-    const double bytes_io = M * N * 2.0 * b + N * b * n_params(req.op);
     Plan p;
-
-    // path 1
-    PathEstimate &e1 = p.est[0];
-    e1.legal = single_tile(req.dt, req.cols, &e1.tile);
-    if (e1.legal) {
-        const double units = e1.tile.kind == kKindWave ? std::ceil(M / 4.0) : M;
-        e1.t_stream_us = stream_us(m, d, bytes_io, units, wgs_per_cu(e1.tile));
-        e1.us = m.launch_us + e1.t_stream_us * eff_of(cal.single_eff, req.op, req.dt);
-    }
-
-    // path 3 (always legal): the reread is served on chip when the rows in
-    // flight on one XCD fit its L2, from the Infinity Cache when all rows in
-    // flight fit it (counted as half an HBM read), else from HBM.
-    PathEstimate &e3 = p.est[2];
-    e3.legal = true;
-    e3.tile = reread_tile(req.dt, req.cols);
-    {
-        const double resident = std::min(M, static_cast<double>(d.cus) * wgs_per_cu(e3.tile));
-        const double per_xcd = resident / d.xcds;
-        double miss;
-        if (per_xcd * row_bytes <= d.l2_bytes_per_xcd)
-            miss = 1.0 - m.hit_l2;
-        else if (resident * row_bytes <= d.mall_bytes)
-            miss = 0.5;
-        else
-            miss = 1.0;
-        const double bytes3 = bytes_io + M * N * b * miss;
-        e3.t_stream_us = stream_us(m, d, bytes3, M, wgs_per_cu(e3.tile));
-        e3.us = m.launch_us + e3.t_stream_us * eff_of(cal.reread_eff, req.op, req.dt);
-    }
-
-    // path 2 at each legal P: Eq. 9 against the non-split baseline B
-    // (path 1 if legal, else path 3); the prediction itself streams the row
-    // once over M*P workgroups and pays one exchange round per row wave (Eq. 8).
-    const PathEstimate &base = e1.legal ? e1 : e3;
-    const double b_base = e1.legal ? 2.0 * b : 2.0 * b + b;  // bytes/element of the baseline schedule
-    const double b_reread = e1.legal ? 0.0 : b;
-    PathEstimate &e2 = p.est[1];
+    TileSpec t;
+    if (single_tile(req.dt, req.cols, &t))
+        p.est[0] = estimate_single(req, cal, t);
+    p.est[2] = estimate_reread(req, cal, reread_tile(req.dt, req.cols));
+    const bool single_legal = p.est[0].legal;
+    const PathEstimate &base = single_legal ? p.est[0] : p.est[2];
     for (int P : {2, 4, 8}) {
         if (forced_p != 0 && P != forced_p)
             continue;
-        TileSpec t;
-        if (!split_tile(req.dt, req.cols, P, &t))
+        if (!split_tile(req.op, req.dt, req.cols, P, &t))
             continue;
-        PathEstimate e;
-        e.legal = true;
-        e.split_p = P;
-        e.tile = t;
-        const double clusters = std::max(1.0, std::floor(static_cast<double>(d.cus) * wgs_per_cu(t) / P));
-        e.waves = std::ceil(M / clusters);
-        e.t_stream_us = stream_us(m, d, bytes_io, M * P, wgs_per_cu(t));
-        e.t_ctrl_us = e.waves * m.exchange_us;
-        e.t_save_us = (b_reread / b_base) * base.us;  // Eq. 7
-        e.us = m.launch_us + e.t_stream_us * eff_of(cal.split_eff, req.op, req.dt) + e.t_ctrl_us;
-        if (!e2.legal || e.us < e2.us)
-            e2 = e;
+        const PathEstimate e = estimate_split(req, cal, P, t, base, single_legal);
+        if (!p.est[1].legal || e.us < p.est[1].us)
+            p.est[1] = e;
     }
 
-    // choice
     int path = forced_path;
     if (path == kPathAuto) {
         double best = -1.0;
@@ -292,9 +329,75 @@ bool make_plan(const PlanRequest &req, const Calibration &cal, int forced_path, 
         return false;
     p.path = path;
     p.split_p = path == kPathSplit ? p.est[1].split_p : 1;
+    // path 1: one row per owner (measured at least as fast as owners that loop)
+    p.wgs_per_cu = path == kPathSingle ? -1 : 0;
     p.tile = p.est[path - 1].tile;
     *out = p;
     return true;
+}
+
+// A held tile is a candidate when it holds `need` vectors and is at least
+// half used (or is the smallest tile that holds them).
+static bool worth_holding(const std::vector<TileSpec> &ladder, const TileSpec &t, int64_t need)
+{
+    const int64_t cap = static_cast<int64_t>(t.block) * t.items;
+    if (cap < need)
+        return false;
+    if (cap < 2 * need)
+        return true;
+    for (const TileSpec &u : ladder) {
+        const int64_t c = static_cast<int64_t>(u.block) * u.items;
+        if (c >= need && c < cap)
+            return false;
+    }
+    return true;
+}
+
+void enumerate_candidates(const PlanRequest &req, const Calibration &cal, std::vector<Candidate> *out)
+{
+    out->clear();
+    const int vb = vec_bytes_for(req.dt, req.cols);
+    const bool v16 = vb == 16;
+    const int64_t nv = vectors_in_row(req.dt, req.cols, vb);
+    std::vector<TileSpec> held = tiles_for(kKindWave, v16);
+    for (const TileSpec &t : tiles_for(kKindWg, v16))
+        held.push_back(t);
+    PathEstimate best1;
+    for (int kind : {kKindWave, kKindWg})
+        for (TileSpec t : tiles_for(kind, v16)) {
+            if (!worth_holding(held, t, nv))
+                continue;
+            t.vb = vb;
+            const PathEstimate e = estimate_single(req, cal, t);
+            out->push_back(Candidate{kPathSingle, 1, e, 0});
+            out->push_back(Candidate{kPathSingle, 1, e, -1});
+            if (!best1.legal || e.us < best1.us)
+                best1 = e;
+        }
+    PathEstimate best3;
+    for (TileSpec t : tiles_for(kKindReread, v16)) {
+        t.vb = vb;
+        const PathEstimate e = estimate_reread(req, cal, t);
+        out->push_back(Candidate{kPathReread, 1, e, 0});
+        if (!best3.legal || e.us < best3.us)
+            best3 = e;
+    }
+    const PathEstimate &base = best1.legal ? best1 : best3;
+    for (int P : {2, 4, 8}) {
+        const int64_t per = (nv + P - 1) / P;
+        if (per * (P - 1) >= nv)
+            continue;
+        std::vector<TileSpec> ladder;
+        for (const TileSpec &u : tiles_for(kKindSplit, v16))
+            if (tile_enabled(req.op, kKindSplit, u.block, u.items, vb))
+                ladder.push_back(u);
+        for (TileSpec t : ladder) {
+            if (!worth_holding(ladder, t, per))
+                continue;
+            t.vb = vb;
+            out->push_back(Candidate{kPathSplit, P, estimate_split(req, cal, P, t, base, best1.legal), 0});
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------

@@ -78,6 +78,7 @@ struct PathEstimate {
 struct Plan {
     int path = kPathSingle;
     int split_p = 1;
+    int wgs_per_cu = 0;  // credit_plan_t::wgs_per_cu
     TileSpec tile;
     PathEstimate est[3];  // paths 1..3
 };
@@ -96,13 +97,22 @@ const std::vector<TileSpec> &tiles_for(int kind, int vb_is_16);
 // Path 1: the tile that holds a row of `cols`, or false if none can.
 bool single_tile(int dt, int64_t cols, TileSpec *out);
 // Path 2: the tile that holds a 1/p slice, or false if none can.
-bool split_tile(int dt, int64_t cols, int p, TileSpec *out);
+bool split_tile(int op, int dt, int64_t cols, int p, TileSpec *out);
 // Path 3: always possible.
 TileSpec reread_tile(int dt, int64_t cols);
 
 // Retained bytes per workgroup for a held tile (Eq. 3's S_CTA) and the budget.
 double tile_capacity_bytes(const TileSpec &t);
 double onchip_budget_bytes(const DeviceModel &d);
+
+// Every legal (path, P, tile) for a shape, each with the model's estimate.
+struct Candidate {
+    int path;
+    int split_p;
+    PathEstimate est;
+    int wgs_per_cu = 0;
+};
+void enumerate_candidates(const PlanRequest &req, const Calibration &cal, std::vector<Candidate> *out);
 
 // Plan with the cost model; forced_path / forced_p restrict the choice
 // (0 = free).  Returns false if the forced choice is illegal for the shape.

@@ -1,0 +1,127 @@
+"""Exhaustive timing of every legal plan on a set of shapes.
+
+    python -m wide_reduction_reuse_amd.sweep --points named|sweep|all [--out FILE]
+                                             [--steps 15] [--warmup 3] [--ops ...]
+
+For each shape it enumerates the legal plans (credit_enumerate_plans: every
+path 1 tile that holds the row, every path 3 tile, every (P, tile) of path 2),
+times each one (median of `steps` flushed launches, dispatch timestamps) and
+writes one JSON line per shape with all candidates, the selector's choice and
+the model's predictions.  These records are the raw material of the selector
+calibration and of its accuracy score (the CREDIT paper's evaluation times
+every legal cluster size P and reports the fastest, Sec. IV-A; its
+profitability accuracy compares predicted and measured winners, Sec. IV-C).
+
+Inputs are synthetic and seeded: for timing, x (and gamma, beta) are drawn on
+the device with torch's seeded generator from the workload's distribution, so
+that 1 GiB shapes need no host-side generation.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import sys
+import time
+
+from . import workloads as W
+from .timing import flush_buffer, summarize, time_launches
+
+
+def device_inputs(w: W.Workload):
+    """x, gamma, beta on the device, drawn from w's distributions (seeded)."""
+    import torch
+    g = torch.Generator(device="cuda")
+    g.manual_seed(w.seed)
+    x = torch.randn((w.rows, w.cols), generator=g, device="cuda", dtype=torch.float32)
+    if w.x_dist == "scaled_shifted":
+        x.mul_(w.x_scale).add_(w.x_shift)
+    elif w.x_dist == "outliers":
+        mask = torch.rand((w.rows, w.cols), generator=g, device="cuda") < w.outlier_prob
+        x = torch.where(mask, x * w.outlier_scale, x)
+    elif w.x_dist == "row_offset":
+        off = (torch.rand((w.rows, 1), generator=g, device="cuda") * 2.0 - 1.0) * w.row_offset
+        x.mul_(w.x_scale).add_(off)
+    gamma = beta = None
+    if w.op in ("layernorm", "rmsnorm"):
+        gamma = torch.rand(w.cols, generator=g, device="cuda") + 0.5
+    if w.op == "layernorm":
+        beta = torch.randn(w.cols, generator=g, device="cuda") * 0.1
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    cast = (lambda t: None if t is None else t.to(dt).contiguous())
+    return cast(x), cast(gamma), cast(beta)
+
+
+def plan_key(p) -> str:
+    return "p%d-P%d-%dx%d-v%d" % (p.path, p.split_p, p.block_threads, p.items, p.vec_bytes)
+
+
+def sweep_shape(w: W.Workload, steps: int, warmup: int, flush_buf) -> dict:
+    import torch
+    from . import credit as C
+    x, g, b = device_inputs(w)
+    y = torch.empty_like(x)
+    sel = C.credit_select_path(w.op, w.dtype, w.rows, w.cols)
+    cands = C.credit_enumerate_plans(w.op, w.dtype, w.rows, w.cols)
+    rec = {"workload": w.name, "op": w.op, "dtype": w.dtype, "rows": w.rows, "cols": w.cols,
+           "bytes": w.algorithmic_bytes(), "selected": plan_key(sel), "selected_plan": sel.as_dict(),
+           "candidates": []}
+    for p in cands:
+        def launch(e0, e1, p=p):
+            C.credit_run_plan_timed(w.op, x, g, b, y, w.eps, p, e0, e1)
+        durs, _ = time_launches(launch, steps, warmup, flush_buf)
+        C.credit_check_errors()
+        s = summarize(durs, w.algorithmic_bytes())
+        rec["candidates"].append({"key": plan_key(p), "plan": p.as_dict(),
+                                  "predicted_us": p.predicted_us[p.path - 1], **s})
+    best = min(rec["candidates"], key=lambda c: c["median_ms"])
+    rec["best"] = best["key"]
+    rec["best_median_ms"] = best["median_ms"]
+    del x, g, b, y
+    torch.cuda.empty_cache()
+    return rec
+
+
+def points(which: str, ops=None):
+    pts = []
+    if which in ("named", "all"):
+        pts += [W.NAMED[n] for n in W.CONFIG_ORDER]
+    if which in ("sweep", "all"):
+        pts += W.sweep_points()
+    if ops:
+        pts = [p for p in pts if p.op in ops]
+    return pts
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--points", default="named", choices=("named", "sweep", "all"))
+    ap.add_argument("--ops", nargs="*", default=None)
+    ap.add_argument("--out", default="-")
+    ap.add_argument("--steps", type=int, default=15)
+    ap.add_argument("--warmup", type=int, default=3)
+    a = ap.parse_args(argv)
+    import torch
+    from . import credit as C
+    if not torch.cuda.is_available():
+        print("the sweep needs a GPU", file=sys.stderr)
+        return 2
+    C.lib()
+    flush_buf = flush_buffer()
+    out = sys.stdout if a.out == "-" else open(a.out, "w")
+    t0 = time.time()
+    for w in points(a.points, a.ops):
+        rec = sweep_shape(w, a.steps, a.warmup, flush_buf)
+        out.write(json.dumps(rec) + "\n")
+        out.flush()
+        sel = next(c for c in rec["candidates"] if c["key"] == rec["selected"]) \
+            if any(c["key"] == rec["selected"] for c in rec["candidates"]) else None
+        print("[sweep %6.1fs] %-40s best %-22s %.4f ms  selected %-22s %s" %
+              (time.time() - t0, w.name, rec["best"], rec["best_median_ms"], rec["selected"],
+               "%.4f ms" % sel["median_ms"] if sel else "?"), file=sys.stderr, flush=True)
+    if out is not sys.stdout:
+        out.close()
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
