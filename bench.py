@@ -167,6 +167,8 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(W.NAMED))
     ap.add_argument("--all", default=None, help="also time every named workload and path; JSON lines to FILE")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy", type=int, default=0, metavar="MIB",
+                    help="only time the streaming-copy kernel on MIB MiB (the reference for counter scaling)")
     a = ap.parse_args(argv)
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the row-wise operators shard by rows with no "
@@ -181,6 +183,10 @@ def main(argv=None) -> int:
         return 2
     C.lib()
     flush_buf = torch.empty(FLUSH_BYTES // 4, dtype=torch.int32, device="cuda").zero_()
+    if a.copy:
+        cc = copy_ceiling(a.copy << 20, a.steps, a.warmup, flush_buf)
+        print(json.dumps({"kind": "copy_ceiling", "mib": a.copy, **cc}), flush=True)
+        return 0
 
     w = W.NAMED[a.workload]
     inp = W.generate(w)
