@@ -142,6 +142,17 @@ credit_status_t credit_enumerate_plans(credit_op_t op, credit_dtype_t dt, int64_
                                        credit_plan_t *out, int32_t capacity, int32_t *count);
 
 /*
+ * Workgroups of the kernel that `plan` selects for rows of `cols` elements
+ * that one CU holds at once (from the compiled kernel's registers and LDS, via
+ * the HIP occupancy calculator); the wave-per-row kernel's workgroups hold
+ * four rows each.  Queries the current device.  Errors as credit_run_plan
+ * (CREDIT_ERR_ILLEGAL_PATH, CREDIT_ERR_UNSUPPORTED), CREDIT_ERR_HIP if the
+ * query fails.
+ */
+credit_status_t credit_occupancy(credit_op_t op, credit_dtype_t dt, int64_t cols, const credit_plan_t *plan,
+                                 int32_t *wgs_per_cu);
+
+/*
  * Run one operator with an explicit plan (as returned by credit_select_path,
  * or hand-built for exhaustive timing).  op selects which of gamma/beta are
  * read (softmax: neither; RMSNorm: gamma).  Returns CREDIT_ERR_ILLEGAL_PATH if
@@ -189,9 +200,16 @@ credit_status_t credit_flush(void *buf, int64_t bytes, void *stream);
 
 /*
  * Load selector calibration from a JSON file written by the calibration
- * script.  NULL clears it (back to the built-in model).  Returns
- * CREDIT_ERR_NO_CALIBRATION if the file is missing or malformed, in which case
- * the previous calibration stays in force.
+ * script (wide_reduction_reuse_amd/calibrate.py): device constants for the
+ * analytic model and a table of measured candidates, each a plan for one
+ * (op, dtype, cols) with its median kernel time at several row counts.  A shape
+ * whose (op, dtype, cols) the table measured is planned from it (each
+ * candidate's time interpolated piecewise linearly in log rows / log time,
+ * the fastest chosen); other shapes use the analytic model.  NULL clears it
+ * (back to the analytic model alone).  Returns CREDIT_ERR_NO_CALIBRATION if the
+ * file is missing or malformed, in which case the previous calibration stays
+ * in force.  If the environment variable CREDIT_CALIB names a file, it is
+ * loaded before the first plan unless a calibration was loaded explicitly.
  */
 credit_status_t credit_load_calibration(const char *json_path);
 

@@ -1,0 +1,114 @@
+"""The selector's calibration table on a machine without a GPU: file parsing
+and validation, interpolation in (log rows, log time), the choice among
+measured candidates, forced paths, the analytic fallback for widths the table
+did not measure, and the CREDIT_CALIB environment variable."""
+import json
+import math
+import os
+import subprocess
+import sys
+
+import pytest
+
+from wide_reduction_reuse_amd import credit as C
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(autouse=True)
+def restore_bundled_calibration():
+    yield
+    C.credit_load_calibration(C.CALIB_PATH if os.path.exists(C.CALIB_PATH) else None)
+
+
+# two measured candidates for softmax fp32 rows of 4096 columns
+ENTRY_A = [0, 0, 4096, 1, 1, 512, 2, 16, -1, 2, 100, 10.0, 1000, 50.0]   # path 1, 512 x 2
+ENTRY_B = [0, 0, 4096, 2, 2, 256, 8, 16, 0, 2, 100, 5.0, 1000, 100.0]    # path 2, P = 2, 256 x 8
+
+
+def _write(tmp_path, table, name="cal.json", **extra):
+    doc = {"version": 2, "stream_gbs": 5000.0, "table": table}
+    doc.update(extra)
+    p = tmp_path / name
+    p.write_text(json.dumps(doc))
+    return str(p)
+
+
+def _loglog(r1, t1, r2, t2, r):
+    return math.exp(math.log(t1) + (math.log(t2) - math.log(t1)) * (math.log(r) - math.log(r1)) /
+                    (math.log(r2) - math.log(r1)))
+
+
+def test_table_choice_follows_interpolated_times(tmp_path):
+    C.credit_load_calibration(_write(tmp_path, [ENTRY_A, ENTRY_B]))
+    p = C.credit_select_path("softmax", "f32", 100, 4096)
+    assert (p.path, p.split_p, p.block_threads, p.items) == (2, 2, 256, 8)
+    p = C.credit_select_path("softmax", "f32", 1000, 4096)
+    assert (p.path, p.split_p, p.block_threads, p.items, p.wgs_per_cu) == (1, 1, 512, 2, -1)
+    # 300 rows: A = 10 * 5^k, B = 5 * 20^k with k = log(3)/log(10): B is faster
+    p = C.credit_select_path("softmax", "f32", 300, 4096)
+    assert p.path == 2
+    assert p.predicted_us[0] == pytest.approx(_loglog(100, 10, 1000, 50, 300), rel=1e-9)
+    assert p.predicted_us[1] == pytest.approx(_loglog(100, 5, 1000, 100, 300), rel=1e-9)
+    assert p.predicted_us[2] < 0  # path 3 not measured for this width
+    # beyond the measured rows the end segment extends
+    p = C.credit_select_path("softmax", "f32", 10000, 4096)
+    assert p.path == 1 and p.predicted_us[0] == pytest.approx(_loglog(100, 10, 1000, 50, 10000), rel=1e-9)
+
+
+def test_forced_paths_use_the_table_and_fall_back(tmp_path):
+    C.credit_load_calibration(_write(tmp_path, [ENTRY_A, ENTRY_B]))
+    p = C.credit_plan("softmax", "f32", 100, 4096, "single")
+    assert (p.path, p.block_threads, p.items) == (1, 512, 2)
+    p = C.credit_plan("softmax", "f32", 1000, 4096, "split", 2)
+    assert (p.path, p.split_p, p.block_threads, p.items) == (2, 2, 256, 8)
+    # P = 4 and path 3 are not in the table: the analytic model plans them
+    p = C.credit_plan("softmax", "f32", 1000, 4096, "split", 4)
+    assert p.path == 2 and p.split_p == 4
+    p = C.credit_plan("softmax", "f32", 1000, 4096, "reread")
+    assert p.path == 3
+
+
+def test_unmeasured_width_uses_the_analytic_model(tmp_path):
+    C.credit_load_calibration(_write(tmp_path, [ENTRY_A, ENTRY_B]))
+    a = C.credit_select_path("softmax", "f32", 1000, 8192).as_dict()
+    C.credit_load_calibration(None)
+    b = C.credit_select_path("softmax", "f32", 1000, 8192).as_dict()
+    assert a["path"] == b["path"] and a["block_threads"] == b["block_threads"] and a["items"] == b["items"]
+
+
+@pytest.mark.parametrize("bad", [
+    [0, 0, 4096, 1, 1, 512, 2, 16, -1, 2, 1000, 10.0, 100, 50.0],   # rows not ascending
+    [0, 0, 4096, 4, 1, 512, 2, 16, -1, 2, 100, 10.0, 1000, 50.0],   # no path 4
+    [0, 0, 4096, 1, 1, 512, 2, 16, -1, 2, 100, 10.0, 1000],         # a point is missing
+    [0, 0, 4096, 1, 1, 512, 2, 16, -1, 2, 100, -1.0, 1000, 50.0],   # non-positive time
+    [3, 0, 4096, 1, 1, 512, 2, 16, -1, 2, 100, 10.0, 1000, 50.0],   # no op 3
+    [0, 0, 4096, 1, 1, 512, 2, 16, -1],                             # header cut short
+])
+def test_malformed_tables_are_refused_and_the_previous_one_stays(tmp_path, bad):
+    C.credit_load_calibration(_write(tmp_path, [ENTRY_A, ENTRY_B], "good.json"))
+    assert C.lib().credit_load_calibration(_write(tmp_path, [ENTRY_A, bad], "bad.json").encode()) == 6
+    assert C.credit_select_path("softmax", "f32", 100, 4096).path == 2
+
+
+def test_bundled_calibration_loads_and_chooses_the_one_read_paths():
+    assert os.path.exists(C.CALIB_PATH)
+    C.credit_load_calibration(C.CALIB_PATH)
+    p = C.credit_select_path("softmax", "f32", 256, 262144)
+    assert p.path == 2 and p.split_p in (2, 4, 8)  # one CU cannot hold a 1 MiB row
+    for op, dt, rows, cols in [("softmax", "f32", 64, 4096), ("layernorm", "bf16", 4096, 8192),
+                               ("rmsnorm", "bf16", 1024, 65536)]:
+        p = C.credit_select_path(op, dt, rows, cols)
+        assert p.path in (1, 2, 3) and p.predicted_us[p.path - 1] > 0
+
+
+def test_calibration_from_environment(tmp_path):
+    path = _write(tmp_path, [ENTRY_A, ENTRY_B])
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "from wide_reduction_reuse_amd import credit as C\n"
+            "p = C.credit_select_path('softmax', 'f32', 100, 4096)\n"
+            "print(p.path, p.split_p, p.block_threads, p.items)\n" % ROOT)
+    env = dict(os.environ, CREDIT_CALIB=path)
+    out = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=120)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.split() == ["2", "2", "256", "8"]

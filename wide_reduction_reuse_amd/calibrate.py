@@ -1,0 +1,95 @@
+"""Selector calibration: measured candidates to a calibration file.
+
+    python -m wide_reduction_reuse_amd.calibrate --out FILE [--sweep SWEEP.jsonl] [--run]
+
+With --run it first times every legal plan on the calibration shapes
+(workloads.calibration_points(): the crossover sweep's operators, dtypes and
+widths at 8, 64, 512 and 2048 MiB, sizes the scored sweep does not use) with
+the sweep driver and writes the records to --sweep.  It then builds the table
+credit_load_calibration reads: for each (op, dtype, cols) and each candidate
+plan, the median kernel time at every calibrated row count.  The selector
+interpolates these in (log rows, log time) for the rows it is asked about
+(the CREDIT paper prices a schedule at the rate measured for it rather than a
+device peak, Sec. III-D, Eq. 7; here every candidate is measured the same way).
+The analytic model's streaming bandwidth is set to the best rate measured on
+the largest calibration shapes.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import sys
+from collections import defaultdict
+
+OPS = {"softmax": 0, "layernorm": 1, "rmsnorm": 2}
+DTS = {"f32": 0, "bf16": 1}
+
+
+def build_table(records):
+    pts = defaultdict(dict)
+    for r in records:
+        for c in r["candidates"]:
+            p = c["plan"]
+            key = (OPS[r["op"]], DTS[r["dtype"]], r["cols"], p["path"], p["split_p"], p["block_threads"],
+                   p["items"], p["vec_bytes"], p["wgs_per_cu"])
+            pts[key][r["rows"]] = c["median_ms"] * 1000.0
+    table = []
+    for key in sorted(pts):
+        rows = sorted(pts[key])
+        row = list(key) + [len(rows)]
+        for n in rows:
+            row += [n, round(pts[key][n], 4)]
+        table.append(row)
+    return table
+
+
+def device_info():
+    try:
+        import torch
+        if torch.cuda.is_available():
+            p = torch.cuda.get_device_properties(0)
+            return {"name": getattr(p, "gcnArchName", p.name), "cus": p.multi_processor_count}
+    except Exception:
+        pass
+    return {}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--out", required=True)
+    ap.add_argument("--sweep", default=None, help="calibration sweep records (JSON lines)")
+    ap.add_argument("--run", action="store_true", help="time the calibration shapes first (needs a GPU)")
+    ap.add_argument("--steps", type=int, default=15)
+    a = ap.parse_args(argv)
+    if a.run:
+        from . import sweep
+        if not a.sweep:
+            ap.error("--run needs --sweep FILE for the records")
+        rc = sweep.main(["--points", "calib", "--out", a.sweep, "--steps", str(a.steps)])
+        if rc:
+            return rc
+    if not a.sweep:
+        ap.error("--sweep FILE is required")
+    records = [json.loads(l) for l in open(a.sweep) if l.strip()]
+    biggest = max(r["bytes"] for r in records)
+    stream = max(r["bytes"] / (c["median_ms"] * 1e-3) / 1e9 for r in records if r["bytes"] == biggest
+                 for c in r["candidates"])
+    dev = device_info()
+    cal = {"version": 2, "source": "median kernel times of every legal plan on %d calibration shapes" % len(records),
+           "stream_gbs": round(stream, 1), "table": build_table(records)}
+    if dev.get("cus"):
+        cal["device"] = {"cus": dev["cus"]}
+    with open(a.out, "w") as f:
+        f.write("{\n")
+        f.write(' "version": 2,\n "source": %s,\n "stream_gbs": %s,\n' % (json.dumps(cal["source"]), cal["stream_gbs"]))
+        if "device" in cal:
+            f.write(' "device": %s,\n' % json.dumps(cal["device"]))
+        f.write(' "table": [\n')
+        f.write(",\n".join("  " + json.dumps(row) for row in cal["table"]))
+        f.write("\n ]\n}\n")
+    print("wrote %s: %d candidates over %d shapes" % (a.out, len(cal["table"]), len(records)), file=sys.stderr)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -12,6 +12,9 @@ from typing import Optional
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libcredit.so")
+# selector calibration measured on MI355X, loaded with the library unless
+# CREDIT_CALIB names another file (the library then loads that one itself)
+CALIB_PATH = os.path.join(PKG, "calib", "mi355x.json")
 
 # status codes (credit_status_t)
 OK = 0
@@ -27,7 +30,7 @@ OPS = {"softmax": 0, "layernorm": 1, "rmsnorm": 2}
 DTYPES = {"f32": 0, "bf16": 1}
 
 EXPORTED = ["credit_softmax", "credit_layernorm", "credit_rmsnorm", "credit_select_path", "credit_make_plan",
-            "credit_enumerate_plans",
+            "credit_enumerate_plans", "credit_occupancy",
             "credit_run_plan", "credit_run_plan_timed", "credit_control", "credit_copy", "credit_flush",
             "credit_load_calibration", "credit_check_errors", "credit_status_str", "credit_version"]
 
@@ -83,6 +86,7 @@ def lib() -> ctypes.CDLL:
         "credit_select_path": [i32, i32, i64, i64, ctypes.POINTER(Plan)],
         "credit_make_plan": [i32, i32, i64, i64, i32, i32, ctypes.POINTER(Plan)],
         "credit_enumerate_plans": [i32, i32, i64, i64, ctypes.POINTER(Plan), i32, ctypes.POINTER(i32)],
+        "credit_occupancy": [i32, i32, i64, ctypes.POINTER(Plan), ctypes.POINTER(i32)],
         "credit_run_plan": [i32, vp, vp, vp, vp, i64, i64, f32, i32, ctypes.POINTER(Plan), vp],
         "credit_run_plan_timed": [i32, vp, vp, vp, vp, i64, i64, f32, i32, ctypes.POINTER(Plan), vp, vp, vp],
         "credit_control": [i32, i64, i64, i32, ctypes.POINTER(Plan), vp],
@@ -98,6 +102,10 @@ def lib() -> ctypes.CDLL:
         fn.argtypes = args
         fn.restype = ctypes.c_int32
     L.credit_status_str.restype = ctypes.c_char_p
+    if not os.environ.get("CREDIT_CALIB") and os.path.exists(CALIB_PATH):
+        status = L.credit_load_calibration(CALIB_PATH.encode())
+        if status != OK:
+            raise CreditError(status, "credit_load_calibration(%s)" % CALIB_PATH)
     _lib = L
     return L
 
@@ -201,6 +209,15 @@ def credit_enumerate_plans(op, dtype, rows: int, cols: int):
     _check(lib().credit_enumerate_plans(op, dt, rows, cols, arr, n.value, ctypes.byref(n)),
            "credit_enumerate_plans")
     return [arr[i] for i in range(n.value)]
+
+
+def credit_occupancy(op, dtype, cols: int, plan: Plan) -> int:
+    """Resident workgroups per CU of the kernel `plan` selects (credit_occupancy)."""
+    op = OPS[op] if isinstance(op, str) else int(op)
+    dt = DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
+    n = ctypes.c_int32()
+    _check(lib().credit_occupancy(op, dt, cols, ctypes.byref(plan), ctypes.byref(n)), "credit_occupancy")
+    return n.value
 
 
 def credit_run_plan(op, x, gamma, beta, y, eps: float, plan: Plan, stream=None):

@@ -61,8 +61,27 @@ std::mutex g_mu;
 Calibration g_cal;
 std::map<int, DeviceModel> g_devices;
 
+credit_status_t load_calibration_file(const char *json_path, Calibration *out);
+
+// The calibration named by CREDIT_CALIB, loaded once before the first plan.
+// Caller holds g_mu.
+void load_env_calibration_locked()
+{
+    static bool done = false;
+    if (done)
+        return;
+    done = true;
+    const char *path = std::getenv("CREDIT_CALIB");
+    if (path == nullptr || path[0] == '\0' || g_cal.loaded)
+        return;
+    Calibration c;
+    if (load_calibration_file(path, &c) == CREDIT_OK)
+        g_cal = c;
+}
+
 DeviceModel device_model_locked()
 {
+    load_env_calibration_locked();
     if (g_cal.has_device)
         return g_cal.device;
     int dev = 0;
@@ -81,6 +100,16 @@ DeviceModel device_model_locked()
         (void)hipGetLastError();
     g_devices[dev] = d;
     return d;
+}
+
+// The calibration in force with the device description filled in.  Caller
+// holds g_mu.
+Calibration calibration_locked()
+{
+    load_env_calibration_locked();
+    Calibration cal = g_cal;
+    cal.device = device_model_locked();
+    return cal;
 }
 
 bool log_enabled()
@@ -457,8 +486,7 @@ credit_status_t run_op(int op, const void *x, const void *g, const void *b, void
     Plan p;
     {
         std::lock_guard<std::mutex> lk(g_mu);
-        Calibration cal = g_cal;
-        cal.device = device_model_locked();
+        const Calibration cal = calibration_locked();
         PlanRequest req;
         req.op = op;
         req.dt = dt;
@@ -471,6 +499,24 @@ credit_status_t run_op(int op, const void *x, const void *g, const void *b, void
     credit_plan_t cp;
     to_c_plan(p, &cp);
     return run_plan_checked(op, x, g, b, y, rows, cols, eps, dt, cp, static_cast<hipStream_t>(stream), false);
+}
+
+}  // namespace
+}  // namespace credit
+
+namespace credit {
+namespace {
+
+credit_status_t load_calibration_file(const char *json_path, Calibration *out)
+{
+    std::ifstream f(json_path);
+    if (!f)
+        return CREDIT_ERR_NO_CALIBRATION;
+    std::stringstream ss;
+    ss << f.rdbuf();
+    if (!parse_calibration(ss.str(), out))
+        return CREDIT_ERR_NO_CALIBRATION;
+    return CREDIT_OK;
 }
 
 }  // namespace
@@ -505,8 +551,7 @@ credit_status_t credit_select_path(credit_op_t op, credit_dtype_t dt, int64_t ro
     if (out == nullptr || op < 0 || op > 2 || (dt != CREDIT_F32 && dt != CREDIT_BF16) || rows < 0 || cols < 1)
         return CREDIT_ERR_INVALID_ARG;
     std::lock_guard<std::mutex> lk(g_mu);
-    Calibration cal = g_cal;
-    cal.device = device_model_locked();
+    const Calibration cal = calibration_locked();
     PlanRequest req;
     req.op = op;
     req.dt = dt;
@@ -528,8 +573,7 @@ credit_status_t credit_make_plan(credit_op_t op, credit_dtype_t dt, int64_t rows
     if (st != CREDIT_OK)
         return st;
     std::lock_guard<std::mutex> lk(g_mu);
-    Calibration cal = g_cal;
-    cal.device = device_model_locked();
+    const Calibration cal = calibration_locked();
     PlanRequest req;
     req.op = op;
     req.dt = dt;
@@ -551,8 +595,7 @@ credit_status_t credit_enumerate_plans(credit_op_t op, credit_dtype_t dt, int64_
     std::vector<Candidate> cands;
     {
         std::lock_guard<std::mutex> lk(g_mu);
-        Calibration cal = g_cal;
-        cal.device = device_model_locked();
+        const Calibration cal = calibration_locked();
         PlanRequest req;
         req.op = op;
         req.dt = dt;
@@ -573,6 +616,25 @@ credit_status_t credit_enumerate_plans(credit_op_t op, credit_dtype_t dt, int64_
         for (int j = 0; j < 3; ++j)
             c.predicted_us[j] = j == cands[i].path - 1 ? cands[i].est.us : -1.0;
     }
+    return CREDIT_OK;
+}
+
+credit_status_t credit_occupancy(credit_op_t op, credit_dtype_t dt, int64_t cols, const credit_plan_t *plan,
+                                 int32_t *wgs_per_cu)
+{
+    if (plan == nullptr || wgs_per_cu == nullptr || op < 0 || op > 2 || (dt != CREDIT_F32 && dt != CREDIT_BF16) ||
+        cols < 1)
+        return CREDIT_ERR_INVALID_ARG;
+    const KernelEntry *k = nullptr;
+    int kind = 0;
+    credit_status_t st = resolve_plan(op, dt, cols, *plan, &k, &kind);
+    if (st != CREDIT_OK)
+        return st;
+    int occ = 0;
+    st = occupancy(k, &occ);
+    if (st != CREDIT_OK)
+        return st;
+    *wgs_per_cu = occ;
     return CREDIT_OK;
 }
 
@@ -678,14 +740,10 @@ credit_status_t credit_load_calibration(const char *json_path)
         g_cal = Calibration{};
         return CREDIT_OK;
     }
-    std::ifstream f(json_path);
-    if (!f)
-        return CREDIT_ERR_NO_CALIBRATION;
-    std::stringstream ss;
-    ss << f.rdbuf();
     Calibration c;
-    if (!parse_calibration(ss.str(), &c))
-        return CREDIT_ERR_NO_CALIBRATION;
+    const credit_status_t st = load_calibration_file(json_path, &c);
+    if (st != CREDIT_OK)
+        return st;
     std::lock_guard<std::mutex> lk(g_mu);
     g_cal = c;
     return CREDIT_OK;

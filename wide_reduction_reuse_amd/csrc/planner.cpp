@@ -80,7 +80,9 @@ const std::vector<TileSpec> &tiles_for(int kind, int vb_is_16)
 static int64_t vectors_in_row(int dt, int64_t cols, int vb) { return cols * elem_bytes(dt) / vb; }
 
 // Preference among tiles that can hold `nv` vectors: the smallest capacity,
-// and within a capacity the one with 8 vectors per thread (then fewer threads).
+// and within a capacity the one closest to 2 vectors per thread (then more
+// threads); measured on MI355X, two 16-byte vectors per thread over many
+// threads streamed fastest for most widths, one per thread slower.
 static bool pick_holding_tile(const std::vector<TileSpec> &ladder, int64_t nv, TileSpec *out)
 {
     bool found = false;
@@ -92,8 +94,8 @@ static bool pick_holding_tile(const std::vector<TileSpec> &ladder, int64_t nv, T
             continue;
         bool better = !found || cap < best_cap;
         if (found && cap == best_cap) {
-            const int d_new = std::abs(t.items - 8), d_old = std::abs(best.items - 8);
-            better = d_new < d_old || (d_new == d_old && t.block < best.block);
+            const int d_new = std::abs(t.items - 2), d_old = std::abs(best.items - 2);
+            better = d_new < d_old || (d_new == d_old && t.block > best.block);
         }
         if (better) {
             best = t;
@@ -111,14 +113,15 @@ bool single_tile(int dt, int64_t cols, TileSpec *out)
     const int vb = vec_bytes_for(dt, cols);
     const bool v16 = vb == 16;
     const int64_t nv = vectors_in_row(dt, cols, vb);
+    std::vector<TileSpec> ladder = tiles_for(kKindWave, v16);
+    for (const TileSpec &u : tiles_for(kKindWg, v16))
+        ladder.push_back(u);
     TileSpec t;
-    if (pick_holding_tile(tiles_for(kKindWave, v16), nv, &t) ||
-        pick_holding_tile(tiles_for(kKindWg, v16), nv, &t)) {
-        t.vb = vb;
-        *out = t;
-        return true;
-    }
-    return false;
+    if (!pick_holding_tile(ladder, nv, &t))
+        return false;
+    t.vb = vb;
+    *out = t;
+    return true;
 }
 
 bool split_tile(int op, int dt, int64_t cols, int p, TileSpec *out)
@@ -297,8 +300,69 @@ PathEstimate estimate_split(const PlanRequest &req, const Calibration &cal, int 
 
 }  // namespace
 
+double calib_time_us(const CalibEntry &e, double rows)
+{
+    const size_t n = e.rows.size();
+    if (n == 0)
+        return -1.0;
+    if (n == 1)
+        return e.us[0] * rows / e.rows[0];
+    size_t i = 0;
+    while (i + 2 < n && rows > e.rows[i + 1])
+        ++i;
+    const double l1 = std::log(e.rows[i]), l2 = std::log(e.rows[i + 1]);
+    const double t1 = std::log(e.us[i]), t2 = std::log(e.us[i + 1]);
+    const double lx = std::log(std::max(rows, 1.0));
+    return std::exp(t1 + (t2 - t1) * (lx - l1) / (l2 - l1));
+}
+
+namespace {
+
+// Plan from the calibration table when it measured this (op, dtype, cols)
+// and holds a candidate the forced path / P allow: every such candidate's
+// time at req.rows is interpolated from its measurements, and the fastest
+// wins.  Returns false when the table cannot decide.
+bool plan_from_table(const PlanRequest &req, const Calibration &cal, int forced_path, int forced_p, Plan *out)
+{
+    Plan p;
+    const CalibEntry *best = nullptr;
+    double best_us = 0.0;
+    for (const CalibEntry &e : cal.table) {
+        if (e.op != req.op || e.dt != req.dt || e.cols != req.cols)
+            continue;
+        if (forced_path != kPathAuto && e.path != forced_path)
+            continue;
+        if (forced_p != 0 && e.path == kPathSplit && e.split_p != forced_p)
+            continue;
+        const double us = calib_time_us(e, static_cast<double>(req.rows));
+        PathEstimate &pe = p.est[e.path - 1];
+        if (!pe.legal || us < pe.us) {
+            pe.legal = true;
+            pe.us = us;
+            pe.split_p = e.split_p;
+            pe.tile = TileSpec{0, e.block, e.items, e.vb};
+        }
+        if (best == nullptr || us < best_us) {
+            best = &e;
+            best_us = us;
+        }
+    }
+    if (best == nullptr)
+        return false;
+    p.path = best->path;
+    p.split_p = best->split_p;
+    p.wgs_per_cu = best->wgs_per_cu;
+    p.tile = TileSpec{0, best->block, best->items, best->vb};
+    *out = p;
+    return true;
+}
+
+}  // namespace
+
 bool make_plan(const PlanRequest &req, const Calibration &cal, int forced_path, int forced_p, Plan *out)
 {
+    if (!cal.table.empty() && plan_from_table(req, cal, forced_path, forced_p, out))
+        return true;
     Plan p;
     TileSpec t;
     if (single_tile(req.dt, req.cols, &t))
@@ -564,6 +628,48 @@ bool parse_calibration(const std::string &text, Calibration *out)
             for (int dt = 0; dt < 2; ++dt)
                 get((std::string(effs[k]) + "[" + std::to_string(op) + "][" + std::to_string(dt) + "]").c_str(),
                     &(*dst[k])[op][dt]);
+    // table[i] = [op, dt, cols, path, split_p, block, items, vec_bytes, wgs_per_cu, n,
+    //             rows_1, us_1, ..., rows_n, us_n]
+    for (int i = 0;; ++i) {
+        const std::string pre = "table[" + std::to_string(i) + "]";
+        auto at = [&](int j, double *v) {
+            auto it = r.nums.find(pre + "[" + std::to_string(j) + "]");
+            if (it == r.nums.end())
+                return false;
+            *v = it->second;
+            return true;
+        };
+        double f[10];
+        if (!at(0, &f[0]))
+            break;
+        for (int j = 1; j < 10; ++j)
+            if (!at(j, &f[j]))
+                return false;
+        CalibEntry e;
+        e.op = static_cast<int>(f[0]);
+        e.dt = static_cast<int>(f[1]);
+        e.cols = static_cast<int64_t>(f[2]);
+        e.path = static_cast<int>(f[3]);
+        e.split_p = static_cast<int>(f[4]);
+        e.block = static_cast<int>(f[5]);
+        e.items = static_cast<int>(f[6]);
+        e.vb = static_cast<int>(f[7]);
+        e.wgs_per_cu = static_cast<int>(f[8]);
+        const int n = static_cast<int>(f[9]);
+        if (e.op < 0 || e.op > 2 || e.dt < 0 || e.dt > 1 || e.cols < 1 || e.path < 1 || e.path > 3 || n < 1 ||
+            n > 64)
+            return false;
+        for (int j = 0; j < n; ++j) {
+            double rr = 0.0, tt = 0.0;
+            if (!at(10 + 2 * j, &rr) || !at(11 + 2 * j, &tt) || !(rr >= 1.0) || !(tt > 0.0))
+                return false;
+            if (!e.rows.empty() && rr <= e.rows.back())
+                return false;
+            e.rows.push_back(rr);
+            e.us.push_back(tt);
+        }
+        c.table.push_back(e);
+    }
     double cus = -1;
     get("device.cus", &cus);
     if (cus > 0) {

@@ -40,6 +40,20 @@ struct DeviceModel {
     double vgpr_bytes_per_cu = 512.0 * 1024;
 };
 
+// One measured candidate of a calibration table: a plan for rows of `cols`
+// elements of one operator and dtype, with its median kernel time (us) at
+// several row counts (ascending).
+struct CalibEntry {
+    int op = 0, dt = 0;
+    int64_t cols = 0;
+    int path = 0, split_p = 1, block = 0, items = 0, vb = 16, wgs_per_cu = 0;
+    std::vector<double> rows, us;
+};
+
+// Time of `e` at `rows`, interpolated piecewise linearly in (log rows,
+// log time) between its measurements and extrapolated along the end segments.
+double calib_time_us(const CalibEntry &e, double rows);
+
 // Measured quantities (from the calibration file); negative = not measured.
 struct Calibration {
     bool loaded = false;
@@ -54,6 +68,9 @@ struct Calibration {
     double split_eff[3][2] = {{-1, -1}, {-1, -1}, {-1, -1}};
     DeviceModel device;
     bool has_device = false;
+    // measured candidates; shapes whose (op, dtype, cols) appear here are
+    // planned from them, all others by the analytic model
+    std::vector<CalibEntry> table;
 };
 
 struct PlanRequest {

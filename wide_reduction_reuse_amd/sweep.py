@@ -1,6 +1,6 @@
 """Exhaustive timing of every legal plan on a set of shapes.
 
-    python -m wide_reduction_reuse_amd.sweep --points named|sweep|all [--out FILE]
+    python -m wide_reduction_reuse_amd.sweep --points named|sweep|all|calib [--out FILE]
                                              [--steps 15] [--warmup 3] [--ops ...]
 
 For each shape it enumerates the legal plans (credit_enumerate_plans: every
@@ -52,7 +52,7 @@ def device_inputs(w: W.Workload):
 
 
 def plan_key(p) -> str:
-    return "p%d-P%d-%dx%d-v%d" % (p.path, p.split_p, p.block_threads, p.items, p.vec_bytes)
+    return "p%d-P%d-%dx%d-v%d-w%d" % (p.path, p.split_p, p.block_threads, p.items, p.vec_bytes, p.wgs_per_cu)
 
 
 def sweep_shape(w: W.Workload, steps: int, warmup: int, flush_buf) -> dict:
@@ -72,6 +72,7 @@ def sweep_shape(w: W.Workload, steps: int, warmup: int, flush_buf) -> dict:
         C.credit_check_errors()
         s = summarize(durs, w.algorithmic_bytes())
         rec["candidates"].append({"key": plan_key(p), "plan": p.as_dict(),
+                                  "occupancy": C.credit_occupancy(w.op, w.dtype, w.cols, p),
                                   "predicted_us": p.predicted_us[p.path - 1], **s})
     best = min(rec["candidates"], key=lambda c: c["median_ms"])
     rec["best"] = best["key"]
@@ -87,6 +88,8 @@ def points(which: str, ops=None):
         pts += [W.NAMED[n] for n in W.CONFIG_ORDER]
     if which in ("sweep", "all"):
         pts += W.sweep_points()
+    if which == "calib":
+        pts += W.calibration_points()
     if ops:
         pts = [p for p in pts if p.op in ops]
     return pts
@@ -94,7 +97,7 @@ def points(which: str, ops=None):
 
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
-    ap.add_argument("--points", default="named", choices=("named", "sweep", "all"))
+    ap.add_argument("--points", default="named", choices=("named", "sweep", "all", "calib"))
     ap.add_argument("--ops", nargs="*", default=None)
     ap.add_argument("--out", default="-")
     ap.add_argument("--steps", type=int, default=15)

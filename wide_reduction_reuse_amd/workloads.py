@@ -85,6 +85,28 @@ CONFIG_ORDER = ["softmax_f32_64x4096", "layernorm_bf16_4096x8192",
                 "rmsnorm_bf16_1024x65536", "softmax_f32_256x262144"]
 
 
+CALIB_BYTES = (8 << 20, 64 << 20, 512 << 20, 2048 << 20)
+CALIB_COLS = tuple(1 << k for k in range(10, 19))  # 1024 ... 262144
+
+
+def calibration_points() -> List[Workload]:
+    """The selector's calibration shapes: the sweep's operators and dtypes at
+    every power-of-two width from 1024 to 262144, at input sizes the scored
+    sweep does not use (8, 64, 512 and 2048 MiB, bracketing its 16 MiB,
+    256 MiB and 1 GiB)."""
+    pts = []
+    idx = 0
+    for op in OPS:
+        for dt in DTYPES:
+            for cols in CALIB_COLS:
+                for nbytes in CALIB_BYTES:
+                    rows = nbytes // (cols * ELEM_BYTES[dt])
+                    name = "calib%02d_%s_%s_%dx%d" % (idx, op, dt, rows, cols)
+                    pts.append(Workload(name, op, dt, rows, cols, seed=2000 + idx, eps=DEFAULT_EPS[op]))
+                    idx += 1
+    return pts
+
+
 def sweep_points() -> List[Workload]:
     """The 90-point crossover sweep, in a fixed order (op, dtype, cols, bytes)."""
     pts = []
