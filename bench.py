@@ -44,26 +44,33 @@ METRIC = "achieved HBM GB/s (one read + one write) and % of MI355X peak per op/s
 
 
 def csrc_hash() -> str:
-    """Hash of the kernel sources: counter-derived traffic is only reported
-    while the kernels it was measured on are unchanged."""
+    """Hash of the device-code sources (kernels, their headers and
+    instantiations; not the host library): counter-derived traffic is only
+    reported while the kernels it was measured on are unchanged."""
     h = hashlib.sha256()
     d = os.path.join(ROOT, "wide_reduction_reuse_amd", "csrc")
     for name in sorted(os.listdir(d)):
-        if name.endswith((".hip", ".hpp", ".cpp")):
+        if name.endswith((".hip", ".hpp")) and name != "planner.hpp":
             with open(os.path.join(d, name), "rb") as f:
                 h.update(name.encode())
                 h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload: str):
+def plan_tag(plan) -> str:
+    return "p%d-P%d-%dx%d" % (plan.path, plan.split_p, plan.block_threads, plan.items)
+
+
+def load_traffic(workload: str, plan):
+    """The counter-derived HBM bytes per launch, if they were measured on the
+    current kernels with the plan the selector now picks."""
     path = os.path.join(PROFILES, "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
     e = t.get(workload)
-    if not e or e.get("csrc_hash") != csrc_hash():
+    if not e or e.get("csrc_hash") != csrc_hash() or e.get("plan") != plan_tag(plan):
         return None
     return e
 
@@ -193,7 +200,7 @@ def main(argv=None) -> int:
     plan = C.credit_select_path(w.op, w.dtype, w.rows, w.cols)
     r = run_workload(w, "auto", 0, a.steps, a.warmup, flush_buf, inputs=inp)
     achieved = r["gbs"]
-    traffic = load_traffic(a.workload)
+    traffic = load_traffic(a.workload, plan)
     result = {
         "metric": METRIC,
         "value": round(achieved, 2),
