@@ -7,7 +7,7 @@
         per-kernel average of each counter over its dispatches from a --pmc run
         (the *_counter_collection.csv file in DIR)
     python -m wide_reduction_reuse_amd.rocprof_summary traffic OUT.json WORKLOAD KERNEL_SUBSTR \\
-        FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR COPY_BYTES CSRC_HASH
+        FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR COPY_BYTES CSRC_HASH PLAN_TAG
         HBM bytes per launch of the kernel: FETCH_SIZE and WRITE_SIZE (KiB per
         dispatch) of the kernel, each scaled by bytes / counter of the streaming
         copy kernel on COPY_BYTES read + COPY_BYTES written; merged into OUT.json
@@ -62,14 +62,15 @@ def _counter(dirname: str, kernel_sub: str, counter: str) -> float:
     return vals[0]
 
 
-def traffic(out_json, workload, kernel_sub, fetch_dir, write_dir, cfetch_dir, cwrite_dir, copy_bytes, csrc_hash):
+def traffic(out_json, workload, kernel_sub, fetch_dir, write_dir, cfetch_dir, cwrite_dir, copy_bytes, csrc_hash,
+            plan_tag):
     copy_bytes = float(copy_bytes)
     cf = _counter(cfetch_dir, "copy_kernel", "FETCH_SIZE")
     cw = _counter(cwrite_dir, "copy_kernel", "WRITE_SIZE")
     f = _counter(fetch_dir, kernel_sub, "FETCH_SIZE")
     w = _counter(write_dir, kernel_sub, "WRITE_SIZE")
     sf, sw = copy_bytes / cf, copy_bytes / cw
-    rec = {"kernel": kernel_sub, "csrc_hash": csrc_hash,
+    rec = {"kernel": kernel_sub, "csrc_hash": csrc_hash, "plan": plan_tag,
            "fetch_kib": f, "write_kib": w, "copy_fetch_kib": cf, "copy_write_kib": cw, "copy_bytes": copy_bytes,
            "scale_fetch": sf, "scale_write": sw,
            "fetch_bytes": f * sf, "write_bytes": w * sw, "bytes_per_launch": f * sf + w * sw}
@@ -97,7 +98,7 @@ def main(argv=None) -> int:
                 print("%-100s %-24s mean=%14.1f n=%d min=%.1f max=%.1f" % (k[:100], c, v["mean"], v["n"],
                                                                           v["min"], v["max"]))
     elif cmd == "traffic":
-        print(json.dumps(traffic(*argv[1:10]), indent=1))
+        print(json.dumps(traffic(*argv[1:11]), indent=1))
     else:
         print(__doc__)
         return 2
