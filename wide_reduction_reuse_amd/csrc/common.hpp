@@ -52,13 +52,16 @@ template <> struct RawVec<2> {
 // hardware range check makes every access past the end harmless (loads return
 // zero, stores are dropped), so tails need no branches.  The descriptor's
 // third dword 0x00020000 is the raw 32-bit-element format of the gfx9 family.
-// Cache policy: kStream marks the row data non-temporal (it is touched once),
-// kKeep leaves the parameter vectors, shared by every row, cacheable.
+// Cache policy: kStream marks row data non-temporal (it is touched once),
+// kStreamStore additionally makes the output stores system-coherent (sc1),
+// which measured 2-4% more write bandwidth on MI355X than nt alone; kKeep
+// leaves the parameter vectors, shared by every row, cacheable.
 // ---------------------------------------------------------------------------
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 constexpr int kKeep = 0;
-constexpr int kStream = 2;  // nt
+constexpr int kStream = 2;        // nt
+constexpr int kStreamStore = 18;  // sc1 nt
 
 // `bytes` must fit in 32 bits; callers keep one descriptor per row or slice.
 __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes)

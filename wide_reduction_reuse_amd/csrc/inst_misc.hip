@@ -9,12 +9,18 @@ namespace credit {
 // thread per grid-stride step: consecutive workgroups cover consecutive 4 KiB
 // pieces, so the addresses in flight at any time form one compact window
 // (measured on MI355X to stream faster than per-thread multi-vector chunks).
+// Loads and stores use the row kernels' cache policies.
 __global__ __launch_bounds__(256) void copy_kernel(const u32x4 *__restrict__ src, u32x4 *__restrict__ dst,
                                                    int64_t n16)
 {
-    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
-    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n16; i += stride)
-        __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+    const int64_t step = static_cast<int64_t>(gridDim.x) * 256;
+    for (int64_t b = static_cast<int64_t>(blockIdx.x) * 256; b < n16; b += step) {
+        const uint32_t bytes = static_cast<uint32_t>(min<int64_t>(256, n16 - b) * 16);
+        const rsrc_t s = make_rsrc(src + b, bytes);
+        const rsrc_t d = make_rsrc(dst + b, bytes);
+        const uint32_t off = threadIdx.x * 16u;
+        buf_store<16, kStreamStore>(buf_load<16, kStream>(s, off), d, off);
+    }
 }
 
 // Read-modify-write of a large buffer, to evict L2 and the Infinity Cache.
