@@ -18,8 +18,9 @@
 // Memory access: every row (or slice, or streamed chunk) is one buffer
 // descriptor sized to its length.  Each wave of an owner holds one contiguous
 // run of 64 * IT vectors: wave w's lane l holds vectors w*64*IT + l + 64k,
-// k < IT (measured on MI355X, contiguous runs per wave stream 10-20% faster
-// than vectors strided by the workgroup width).  The IT loads issue back to
+// k < IT (a streaming probe on MI355X favoured contiguous runs per wave over
+// vectors strided by the workgroup width; in these kernels the two layouts
+// measured within a few percent either way).  The IT loads issue back to
 // back with no branch, and the ones past the end return zero and are excluded
 // from the reduction by the valid count `kv`, while the matching stores are
 // dropped by the range check.
