@@ -56,6 +56,16 @@ def _load():
         lib.oracle_layernorm_merge.argtypes = [_D, _D, _D, ctypes.c_int, _D, _D, _D]
         lib.oracle_rmsnorm_partials.argtypes = [_D, P64, ctypes.c_int, _D]
         lib.oracle_round_bf16.argtypes = [_D, ctypes.POINTER(ctypes.c_uint16), _I64]
+        lib.oracle_softmax_backward.argtypes = [_D, _D, _D, _I64, _I64]
+        lib.oracle_layernorm_backward.argtypes = [_D, _D, _D, ctypes.c_double, _D, _I64, _I64]
+        lib.oracle_quantize_int8.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_int8),
+                                             ctypes.POINTER(ctypes.c_float), _I64, _I64]
+        lib.oracle_softmax_backward_stats.argtypes = [_D, _D, _I64, _I64, _D, _D, _D]
+        lib.oracle_softmax_backward_partials.argtypes = [_D, _D, P64, ctypes.c_int, _D, _D, _D]
+        lib.oracle_softmax_backward_merge.argtypes = [_D, _D, _D, ctypes.c_int, _D, _D, _D]
+        lib.oracle_layernorm_backward_stats.argtypes = [_D, _D, _I64, _I64, _D, _D, _D, _D]
+        lib.oracle_layernorm_backward_partials.argtypes = [_D, _D, P64, ctypes.c_int, _D, _D, _D, _D, _D]
+        lib.oracle_layernorm_backward_merge.argtypes = [_D, _D, _D, _D, _D, ctypes.c_int, _D, _D, _D, _D, _D]
         lib.oracle_num_threads.restype = ctypes.c_int
         lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
         _lib = lib
@@ -206,6 +216,117 @@ def round_bf16(y) -> np.ndarray:
     if a.size:
         _load().oracle_round_bf16(_dptr(a), out.ctypes.data_as(ctypes.POINTER(ctypes.c_uint16)), a.size)
     return out
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Exact float32 value of bfloat16 bit patterns."""
+    b = np.asarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# the three further workloads (definitions and readings at the end of oracle.c)
+# ---------------------------------------------------------------------------
+def softmax_backward(x, dy) -> np.ndarray:
+    """Gradient of row-wise softmax with respect to its logits x, given dy."""
+    a = _as_f64_2d(x)
+    g = _as_f64_2d(dy)
+    if g.shape != a.shape:
+        raise ValueError("dy must have x's shape")
+    out = np.empty_like(a)
+    if a.size:
+        _load().oracle_softmax_backward(_dptr(a), _dptr(g), _dptr(out), a.shape[0], a.shape[1])
+    return out
+
+
+def layernorm_backward(x, dy, gamma, eps: float) -> np.ndarray:
+    """Row part of the LayerNorm gradient: dL/dx given dL/dy (statistics recomputed from x)."""
+    a = _as_f64_2d(x)
+    g = _as_f64_2d(dy)
+    if g.shape != a.shape:
+        raise ValueError("dy must have x's shape")
+    gam = _as_f64_1d(gamma, a.shape[1])
+    out = np.empty_like(a)
+    if a.size:
+        _load().oracle_layernorm_backward(_dptr(a), _dptr(g), _dptr(gam), float(eps), _dptr(out),
+                                          a.shape[0], a.shape[1])
+    return out
+
+
+def quantize_int8(x):
+    """Row-wise symmetric int8 quantization of float32 values: (codes int8 [rows, cols],
+    scale float32 [rows]), computed in IEEE single precision."""
+    a = np.asarray(x)
+    if a.dtype != np.float32:
+        raise TypeError("quantize_int8 takes float32 values (decode bf16 with bf16_bits_to_f32)")
+    a = np.ascontiguousarray(a)
+    if a.ndim == 1:
+        a = a.reshape(1, -1)
+    if a.ndim != 2:
+        raise ValueError("expected a 2-D [rows, cols] array")
+    q = np.empty(a.shape, dtype=np.int8)
+    scale = np.empty(a.shape[0], dtype=np.float32)
+    if a.size:
+        _load().oracle_quantize_int8(a.ctypes.data_as(ctypes.POINTER(ctypes.c_float)),
+                                     q.ctypes.data_as(ctypes.POINTER(ctypes.c_int8)),
+                                     scale.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), a.shape[0], a.shape[1])
+    return q, scale
+
+
+def softmax_backward_stats(x, dy):
+    a = _as_f64_2d(x)
+    g = _as_f64_2d(dy)
+    m, s, u = (np.empty(a.shape[0]) for _ in range(3))
+    _load().oracle_softmax_backward_stats(_dptr(a), _dptr(g), a.shape[0], a.shape[1], _dptr(m), _dptr(s), _dptr(u))
+    return m, s, u
+
+
+def softmax_backward_partials(xrow, dyrow, bounds):
+    x = np.ascontiguousarray(np.asarray(xrow, dtype=np.float64))
+    g = np.ascontiguousarray(np.asarray(dyrow, dtype=np.float64))
+    b = _bounds(bounds, x.shape[0])
+    p = b.shape[0] - 1
+    m, s, u = (np.empty(p) for _ in range(3))
+    _load().oracle_softmax_backward_partials(_dptr(x), _dptr(g), b.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                             p, _dptr(m), _dptr(s), _dptr(u))
+    return m, s, u
+
+
+def softmax_backward_merge(m_c, s_c, u_c):
+    m_c, s_c, u_c = (np.ascontiguousarray(v, dtype=np.float64) for v in (m_c, s_c, u_c))
+    out = [ctypes.c_double() for _ in range(3)]
+    _load().oracle_softmax_backward_merge(_dptr(m_c), _dptr(s_c), _dptr(u_c), m_c.shape[0],
+                                          *(ctypes.byref(o) for o in out))
+    return tuple(o.value for o in out)
+
+
+def layernorm_backward_stats(x, g):
+    """Per row: (mean, M2, sum g, sum g (x - mean)) for g = gamma * dy given directly."""
+    a = _as_f64_2d(x)
+    gg = _as_f64_2d(g)
+    mu, m2, sa, sb = (np.empty(a.shape[0]) for _ in range(4))
+    _load().oracle_layernorm_backward_stats(_dptr(a), _dptr(gg), a.shape[0], a.shape[1], _dptr(mu), _dptr(m2),
+                                            _dptr(sa), _dptr(sb))
+    return mu, m2, sa, sb
+
+
+def layernorm_backward_partials(xrow, grow, bounds):
+    x = np.ascontiguousarray(np.asarray(xrow, dtype=np.float64))
+    g = np.ascontiguousarray(np.asarray(grow, dtype=np.float64))
+    b = _bounds(bounds, x.shape[0])
+    p = b.shape[0] - 1
+    outs = [np.empty(p) for _ in range(5)]
+    _load().oracle_layernorm_backward_partials(_dptr(x), _dptr(g), b.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                               p, *(_dptr(o) for o in outs))
+    return tuple(outs)
+
+
+def layernorm_backward_merge(n_c, mu_c, m2_c, a_c, b_c):
+    ins = [np.ascontiguousarray(v, dtype=np.float64) for v in (n_c, mu_c, m2_c, a_c, b_c)]
+    out = [ctypes.c_double() for _ in range(5)]
+    _load().oracle_layernorm_backward_merge(*(_dptr(v) for v in ins), ins[0].shape[0],
+                                            *(ctypes.byref(o) for o in out))
+    return tuple(o.value for o in out)
 
 
 def num_threads() -> int:
