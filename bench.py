@@ -15,11 +15,13 @@ per step, which take the begin and end timestamps of the kernel dispatch
 itself on the stream it runs on (the same interval rocprofv3's kernel trace
 reports), so the flush, host-side planning and launch latency are outside it.
 
-Prints one JSON line: metric, value (algorithmic GB/s = one read of x + one
-write of y + each parameter vector once, over the mean kernel duration), the
-roofline object for the kernel, and the CPU oracle's rate on the same workload.
-With --all FILE it also writes one JSON line per (workload, path) and the
-streaming-copy ceiling to FILE.
+Prints one JSON line: metric, value (algorithmic GB/s = one read of every row
+input + one write of the output + each parameter vector once, over the mean
+kernel duration), the roofline object for the kernel, and the CPU oracle's rate
+on the same workload.  --workload picks any named workload, including the three
+further workloads (softmax-logits backward, LayerNorm backward, int8
+quantization).  With --all FILE it also writes one JSON line per (workload,
+path) and the streaming-copy ceiling to FILE.
 """
 from __future__ import annotations
 
@@ -75,34 +77,19 @@ def load_traffic(workload: str, plan):
     return e
 
 
-def upload(inp: W.HostInputs):
-    import numpy as np
-    import torch
-
-    def dev(a):
-        if a is None:
-            return None
-        if inp.workload.dtype == "bf16":
-            return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
-        return torch.from_numpy(a).cuda()
-    return dev(inp.x), dev(inp.gamma), dev(inp.beta)
-
-
 def run_workload(w: W.Workload, path: str, split_p: int, steps: int, warmup: int, flush_buf, inputs=None,
                  plan=None):
     """Time one workload.  path 'auto' runs the selector every step; a forced
     path (or an explicit plan) is planned once, as a caller forcing it would."""
-    import torch
     from wide_reduction_reuse_amd import credit as C
     inp = W.generate(w) if inputs is None else inputs
-    x, g, b = upload(inp)
-    y = torch.empty_like(x)
+    t = W.alloc_outputs(w, W.to_device(inp))
     if plan is None and path != "auto":
         plan = C.credit_plan(w.op, w.dtype, w.rows, w.cols, path, split_p)
 
     def launch(e0, e1):
         p = plan if plan is not None else C.credit_select_path(w.op, w.dtype, w.rows, w.cols)
-        C.credit_run_plan_timed(w.op, x, g, b, y, inp.eps, p, e0, e1)
+        C.credit_run_plan_timed(w.op, p, t, e0, e1, eps=inp.eps)
 
     durs, wall = time_launches(launch, steps, warmup, flush_buf)
     C.credit_check_errors()
@@ -132,38 +119,51 @@ def cpu_baseline(w: W.Workload, inp: W.HostInputs, seconds: float = CPU_BASELINE
     def vals(a):
         if a is None:
             return None
+        if w.op == "quantize_int8":  # the quantizer's oracle works in float32
+            return oracle.bf16_bits_to_f32(a) if w.dtype == "bf16" else a
         return oracle.bf16_bits_to_f64(a) if w.dtype == "bf16" else a.astype(np.float64)
 
-    def run(xs):
+    def run(xs, dys):
         if w.op == "softmax":
             oracle.softmax(xs)
         elif w.op == "layernorm":
             oracle.layernorm(xs, g, b, inp.eps)
-        else:
+        elif w.op == "rmsnorm":
             oracle.rmsnorm(xs, g, inp.eps)
+        elif w.op == "softmax_bwd":
+            oracle.softmax_backward(xs, dys)
+        elif w.op == "layernorm_bwd":
+            oracle.layernorm_backward(xs, dys, g, inp.eps)
+        else:
+            oracle.quantize_int8(xs)
 
     g, b = vals(inp.gamma), vals(inp.beta)
-    rows = w.rows
-    x = vals(inp.x[:rows])
+
+    def sample(rows):
+        return vals(inp.x[:rows]), (None if inp.dy is None else vals(inp.dy[:rows]))
+
+    rows = min(w.rows, 64)
+    xs, dys = sample(rows)
     t0 = time.perf_counter()
-    run(x)
+    run(xs, dys)
     t1 = time.perf_counter() - t0
-    if t1 > seconds / 3:  # bound the sample: the leading rows that take ~seconds/3 per run
-        rows = max(1, int(w.rows * (seconds / 3) / t1))
-        x = vals(inp.x[:rows])
+    # bound the sample: the leading rows that take ~seconds/3 per run
+    rows = max(1, min(w.rows, int(rows * (seconds / 3) / max(t1, 1e-9))))
+    xs, dys = sample(rows)
     times = []
     start = time.perf_counter()
     while len(times) < 3 or time.perf_counter() - start < seconds:
         t0 = time.perf_counter()
-        run(x)
+        run(xs, dys)
         times.append(time.perf_counter() - t0)
     t = sorted(times)[len(times) // 2]
-    nbytes = rows * w.cols * 2 * w.elem_bytes + w.cols * w.elem_bytes * W.N_PARAMS[w.op]
+    nbytes = w.with_shape(rows, w.cols).algorithmic_bytes()
     return {"value": round(nbytes / t / 1e9, 3), "unit": "GB/s", "cores": oracle.num_threads(),
             "kind": "oracle",
-            "sample": "%d of %d rows x %d cols, float64 oracle (OpenMP over rows), median of %d runs "
-                      "of %.4f s each over %.1f s" % (rows, w.rows, w.cols, len(times), t,
-                                                       time.perf_counter() - start)}
+            "sample": "%d of %d rows x %d cols, %s oracle (OpenMP over rows), median of %d runs "
+                      "of %.4f s each over %.1f s" % (rows, w.rows, w.cols,
+                                                       "float32" if w.op == "quantize_int8" else "float64",
+                                                       len(times), t, time.perf_counter() - start)}
 
 
 def main(argv=None) -> int:
@@ -236,7 +236,7 @@ def main(argv=None) -> int:
                 f.flush()
                 print("[all] copy %d MiB %.1f GB/s (%.4f ms)" % (mib, cc["gbs"], cc["mean_ms"]),
                       file=sys.stderr, flush=True)
-            for name in W.CONFIG_ORDER:
+            for name in W.CONFIG_ORDER + W.NEXT_ORDER:
                 wk = W.NAMED[name]
                 inpk = W.generate(wk)
                 pl = C.credit_select_path(wk.op, wk.dtype, wk.rows, wk.cols)

@@ -1,6 +1,7 @@
 /*
  * credit.h -- C ABI of libcredit.so: row-wise reduction-reuse operators
- * (softmax, LayerNorm, RMSNorm) for AMD Instinct MI355X (gfx950).
+ * (softmax, LayerNorm, RMSNorm; softmax-logits backward, LayerNorm backward,
+ * int8 quantization) for AMD Instinct MI355X (gfx950).
  *
  * The operators are the "wide reduction-reuse" workload class of the CREDIT
  * paper ("CREDIT: Cost-guided Reduction-reuse with Efficient DSMEM Inter-CTA
@@ -14,11 +15,12 @@
  * row ("split_p", P in {2, 4, 8}; Sec. IV-A sweeps the same set).
  *
  * Conventions shared by every entry point:
- *   - x, gamma, beta and y are caller-owned DEVICE pointers; the library never
- *     frees or retains them.  Layout is dense row-major [rows][cols]; gamma and
- *     beta are [cols].  Every pointer must be 16-byte aligned.  gamma and beta
- *     have the same dtype as x and y.  In-place operation (y == x) is allowed;
- *     any other overlap is undefined.
+ *   - x, dy, gamma, beta, y (dx, q) and scale are caller-owned DEVICE pointers;
+ *     the library never frees or retains them.  Layout is dense row-major
+ *     [rows][cols]; gamma and beta are [cols]; scale is [rows].  Every pointer
+ *     must be 16-byte aligned, except scale (4-byte).  gamma, beta, dy and a
+ *     floating-point output have the same dtype as x.  In-place operation
+ *     (output == x, or dx == dy) is allowed; any other overlap is undefined.
  *   - Calls are asynchronous and stream-ordered on `stream` (a hipStream_t;
  *     NULL means the default stream).  A successful return means the work was
  *     enqueued; device faults surface at the caller's next synchronization.
@@ -30,7 +32,8 @@
  *     share a scratch; concurrent calls on one stream are ordered by the stream.
  *
  * Arithmetic: fp32 inputs compute in fp32; bf16 inputs are widened exactly to
- * fp32, computed in fp32 and rounded to nearest-even bf16 on output.
+ * fp32, computed in fp32 and rounded to nearest-even bf16 on output (the int8
+ * quantizer's codes are integers decided in fp32).
  */
 #ifndef CREDIT_H
 #define CREDIT_H
@@ -55,7 +58,34 @@ typedef enum {
 
 typedef enum { CREDIT_F32 = 0, CREDIT_BF16 = 1 } credit_dtype_t;
 
-typedef enum { CREDIT_OP_SOFTMAX = 0, CREDIT_OP_LAYERNORM = 1, CREDIT_OP_RMSNORM = 2 } credit_op_t;
+typedef enum {
+    CREDIT_OP_SOFTMAX = 0,
+    CREDIT_OP_LAYERNORM = 1,
+    CREDIT_OP_RMSNORM = 2,
+    CREDIT_OP_SOFTMAX_BACKWARD = 3,   /* softmax-logits backward */
+    CREDIT_OP_LAYERNORM_BACKWARD = 4, /* LayerNorm backward, row part (fp32 only) */
+    CREDIT_OP_QUANTIZE_INT8 = 5       /* row-wise symmetric int8 quantization */
+} credit_op_t;
+
+/*
+ * Operands of one operator call, for the explicit-plan entry points.  Each
+ * operator reads the fields it needs and requires them non-NULL:
+ *   softmax              x, y
+ *   LayerNorm            x, gamma, beta, y
+ *   RMSNorm              x, gamma, y
+ *   softmax backward     x (logits), dy, y (= dx)
+ *   LayerNorm backward   x, dy, gamma, y (= dx)
+ *   int8 quantization    x, y (= int8 codes q), row_out (= fp32 scale per row)
+ * Fields an operator does not use are ignored.
+ */
+typedef struct {
+    const void *x;
+    const void *dy;
+    const void *gamma;
+    const void *beta;
+    void *y;
+    void *row_out;
+} credit_operands_t;
 
 typedef enum {
     CREDIT_PATH_AUTO = 0,      /* the selector decides (credit_select_path) */
@@ -107,12 +137,53 @@ credit_status_t credit_rmsnorm(const void *x, const void *gamma, void *y, int64_
                                void *stream);
 
 /*
+ * Softmax-logits backward, one of the reduction-reuse workloads of the
+ * paper's evaluation (Sec. IV-A; its traffic in Sec. IV-D): the gradient of
+ * row-wise softmax with respect to its logits x given the gradient dy of the
+ * softmax output, with the probabilities recomputed from x:
+ *   p = softmax(x),  dx_i = p_i (dy_i - sum_j dy_j p_j).
+ * Reads x and dy once, writes dx once.
+ *   x, dy, dx : [rows][cols] of dtype `dt` (fp32 or bf16).
+ */
+credit_status_t credit_softmax_backward(const void *x, const void *dy, void *dx, int64_t rows, int64_t cols,
+                                        credit_dtype_t dt, credit_path_t path, int32_t split_p, void *stream);
+
+/*
+ * LayerNorm backward, row part (the LayerNorm workload of Sec. IV-A, in its
+ * backward form): the gradient with respect to x of the LayerNorm above,
+ * given dy, with mean and variance recomputed from x.  With
+ * rstd = 1/sqrt(var + eps), xhat = (x - mean) rstd and g = gamma dy:
+ *   dx_i = rstd (g_i - mean_j g_j - xhat_i mean_j (g_j xhat_j)).
+ * The per-column sums for the gamma and beta gradients are not computed.
+ *   x, dy, dx : [rows][cols]; gamma : [cols]; fp32 only (CREDIT_ERR_UNSUPPORTED
+ *   for bf16).  eps finite, >= 0.
+ */
+credit_status_t credit_layernorm_backward(const void *x, const void *dy, const void *gamma, void *dx,
+                                          int64_t rows, int64_t cols, float eps, credit_dtype_t dt,
+                                          credit_path_t path, int32_t split_p, void *stream);
+
+/*
+ * Row-wise symmetric int8 quantization (the quantization workload of
+ * Sec. IV-A; 9 -> 5 bytes per element in Sec. IV-D), in fp32 arithmetic:
+ *   a = max_i |x_i|;  inv = min(127 / a, FLT_MAX) (0 when a = 0);
+ *   q_i = clamp(round_half_even(x_i * inv), -127, 127);  scale = a / 127,
+ * each division and product correctly rounded, so the codes are fully
+ * determined by x.  Inputs must be finite (non-finite values give
+ * unspecified codes).
+ *   x : [rows][cols] of dtype `dt` (fp32 or bf16); q : [rows][cols] int8;
+ *   scale : [rows] fp32 (4-byte aligned).
+ */
+credit_status_t credit_quantize_int8(const void *x, int8_t *q, float *scale, int64_t rows, int64_t cols,
+                                     credit_dtype_t dt, credit_path_t path, int32_t split_p, void *stream);
+
+/*
  * The selector (Sec. III-D, Eq. 3 and 7-9, adapted): legality of each path
  * from the on-chip capacity of the compiled kernels, then the predicted time of
  * each legal candidate; writes the fastest into *out.  Host-only: it queries
  * device properties once per device unless a calibration with a device
  * description is loaded.  Returns CREDIT_ERR_INVALID_ARG for a null `out` or
- * bad shape.
+ * bad shape, CREDIT_ERR_UNSUPPORTED for an (op, dtype) pair with no kernels
+ * (LayerNorm backward in bf16).
  */
 credit_status_t credit_select_path(credit_op_t op, credit_dtype_t dt, int64_t rows, int64_t cols,
                                    credit_plan_t *out);
@@ -154,14 +225,15 @@ credit_status_t credit_occupancy(credit_op_t op, credit_dtype_t dt, int64_t cols
 
 /*
  * Run one operator with an explicit plan (as returned by credit_select_path,
- * or hand-built for exhaustive timing).  op selects which of gamma/beta are
- * read (softmax: neither; RMSNorm: gamma).  Returns CREDIT_ERR_ILLEGAL_PATH if
- * the plan's tile cannot hold the row or slice, CREDIT_ERR_UNSUPPORTED if no
- * kernel with that tile exists.
+ * or hand-built for exhaustive timing) on the operands `ops` (see
+ * credit_operands_t for which fields each operator needs).  eps is used by
+ * the normalizations and ignored otherwise.  Returns CREDIT_ERR_ILLEGAL_PATH
+ * if the plan's tile cannot hold the row or slice, CREDIT_ERR_UNSUPPORTED if
+ * no kernel with that tile exists, and the argument errors of the operator's
+ * own entry point.
  */
-credit_status_t credit_run_plan(credit_op_t op, const void *x, const void *gamma, const void *beta, void *y,
-                                int64_t rows, int64_t cols, float eps, credit_dtype_t dt,
-                                const credit_plan_t *plan, void *stream);
+credit_status_t credit_run_plan(credit_op_t op, const credit_operands_t *ops, int64_t rows, int64_t cols,
+                                float eps, credit_dtype_t dt, const credit_plan_t *plan, void *stream);
 
 /*
  * credit_run_plan with timing: start_event receives the begin timestamp of the
@@ -172,10 +244,9 @@ credit_status_t credit_run_plan(credit_op_t op, const void *x, const void *gamma
  * rows == 0 returns CREDIT_ERR_INVALID_ARG because nothing would be timed.
  * Otherwise identical to credit_run_plan.
  */
-credit_status_t credit_run_plan_timed(credit_op_t op, const void *x, const void *gamma, const void *beta,
-                                      void *y, int64_t rows, int64_t cols, float eps, credit_dtype_t dt,
-                                      const credit_plan_t *plan, void *start_event, void *stop_event,
-                                      void *stream);
+credit_status_t credit_run_plan_timed(credit_op_t op, const credit_operands_t *ops, int64_t rows, int64_t cols,
+                                      float eps, credit_dtype_t dt, const credit_plan_t *plan, void *start_event,
+                                      void *stop_event, void *stream);
 
 /*
  * Work-free control kernel (Sec. III-D, the control that isolates launch,

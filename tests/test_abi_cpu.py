@@ -17,7 +17,7 @@ HEADER = os.path.join(ROOT, "include", "credit.h")
 def _declared():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(credit_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(credit_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_symbol():
@@ -56,6 +56,21 @@ def _rms(x=A, g=G, y=B, rows=4, cols=64, eps=1e-6, dt=0, path=0, p=0):
     return C.lib().credit_rmsnorm(x, g, y, rows, cols, eps, dt, path, p, None)
 
 
+def _smb(x=A, dy=G, dx=B, rows=4, cols=64, dt=0, path=0, p=0):
+    return C.lib().credit_softmax_backward(x, dy, dx, rows, cols, dt, path, p, None)
+
+
+def _lnb(x=A, dy=G, g=G, dx=B, rows=4, cols=64, eps=1e-5, dt=0, path=0, p=0):
+    return C.lib().credit_layernorm_backward(x, dy, g, dx, rows, cols, eps, dt, path, p, None)
+
+
+S4 = ctypes.c_void_p(0x7F0000300004)  # 4-byte aligned: enough for the scale vector
+
+
+def _q(x=A, q=B, s=S4, rows=4, cols=64, dt=0, path=0, p=0):
+    return C.lib().credit_quantize_int8(x, q, s, rows, cols, dt, path, p, None)
+
+
 @pytest.mark.parametrize("call,status", [
     (lambda: _sm(x=None), 1), (lambda: _sm(y=None), 1), (lambda: _sm(cols=0), 1),
     (lambda: _sm(rows=-1), 1), (lambda: _sm(dt=2), 1), (lambda: _sm(path=4), 1),
@@ -64,6 +79,11 @@ def _rms(x=A, g=G, y=B, rows=4, cols=64, eps=1e-6, dt=0, path=0, p=0):
     (lambda: _ln(g=None), 1), (lambda: _ln(b=None), 1), (lambda: _ln(eps=-1.0), 1),
     (lambda: _ln(eps=float("nan")), 1), (lambda: _ln(eps=float("inf")), 1), (lambda: _ln(b=MIS), 3),
     (lambda: _rms(g=None), 1), (lambda: _rms(eps=-1e-6), 1), (lambda: _rms(g=MIS), 3),
+    (lambda: _smb(dy=None), 1), (lambda: _smb(dx=None), 1), (lambda: _smb(dy=MIS), 3), (lambda: _smb(dt=2), 1),
+    (lambda: _lnb(dy=None), 1), (lambda: _lnb(g=None), 1), (lambda: _lnb(eps=-1.0), 1),
+    (lambda: _lnb(dy=MIS), 3), (lambda: _lnb(dt=1), 2),  # LayerNorm backward: fp32 only
+    (lambda: _q(q=None), 1), (lambda: _q(s=None), 1), (lambda: _q(x=MIS), 3),
+    (lambda: _q(s=ctypes.c_void_p(0x7F0000300002)), 3), (lambda: _q(cols=0), 1),
 ])
 def test_invalid_arguments_rejected_before_launch(call, status):
     assert call() == status
@@ -74,6 +94,7 @@ def test_rows_zero_is_a_noop_without_device():
     assert _sm(x=None, y=None, rows=0) == 0
     assert _ln(rows=0) == 0
     assert _rms(rows=0) == 0
+    assert _smb(rows=0) == 0 and _lnb(rows=0) == 0 and _q(rows=0) == 0
 
 
 def test_forced_path_that_cannot_hold_the_row_is_refused():
@@ -84,29 +105,48 @@ def test_forced_path_that_cannot_hold_the_row_is_refused():
     assert _sm(cols=8, path=2, p=8) == 4
 
 
+def _ops(**kw):
+    o = C.Operands()
+    for k, v in kw.items():
+        setattr(o, k, v.value if isinstance(v, ctypes.c_void_p) else v)
+    return ctypes.byref(o)
+
+
 def test_run_plan_validation():
     L = C.lib()
+    sm = _ops(x=A, y=B)
     plan = C.Plan.make(C.PATH_SINGLE_WG, 1, 64, 3, 16)  # no such tile
-    assert L.credit_run_plan(0, A, None, None, B, 4, 64, 0.0, 0, ctypes.byref(plan), None) == 2
+    assert L.credit_run_plan(0, sm, 4, 64, 0.0, 0, ctypes.byref(plan), None) == 2
     plan = C.Plan.make(C.PATH_SINGLE_WG, 1, 64, 1, 16)  # holds 64 vectors = 256 fp32 only
-    assert L.credit_run_plan(0, A, None, None, B, 4, 1024, 0.0, 0, ctypes.byref(plan), None) == 4
+    assert L.credit_run_plan(0, sm, 4, 1024, 0.0, 0, ctypes.byref(plan), None) == 4
     plan = C.Plan.make(C.PATH_SPLIT_ROW, 3, 256, 8, 16)  # P must be 2, 4 or 8
-    assert L.credit_run_plan(0, A, None, None, B, 4, 4096, 0.0, 0, ctypes.byref(plan), None) == 4
-    assert L.credit_run_plan(0, A, None, None, B, 4, 4096, 0.0, 0, None, None) == 1
+    assert L.credit_run_plan(0, sm, 4, 4096, 0.0, 0, ctypes.byref(plan), None) == 4
+    assert L.credit_run_plan(0, sm, 4, 4096, 0.0, 0, None, None) == 1
+    assert L.credit_run_plan(0, None, 4, 4096, 0.0, 0, ctypes.byref(plan), None) == 1
     plan = C.Plan.make(C.PATH_REREAD, 1, 256, 4, 4)  # vec_bytes does not match the row
-    assert L.credit_run_plan(0, A, None, None, B, 4, 4096, 0.0, 0, ctypes.byref(plan), None) == 4
+    assert L.credit_run_plan(0, sm, 4, 4096, 0.0, 0, ctypes.byref(plan), None) == 4
+    # each operator requires its own operands
+    plan = C.Plan.make(C.PATH_SINGLE_WG, 1, 64, 1, 16)
+    assert L.credit_run_plan(3, sm, 4, 64, 0.0, 0, ctypes.byref(plan), None) == 1        # dy missing
+    assert L.credit_run_plan(4, _ops(x=A, dy=G, y=B), 4, 64, 1e-5, 0, ctypes.byref(plan), None) == 1  # gamma
+    assert L.credit_run_plan(5, sm, 4, 64, 0.0, 0, ctypes.byref(plan), None) == 1        # scale missing
+    assert L.credit_run_plan(6, sm, 4, 64, 0.0, 0, ctypes.byref(plan), None) == 1        # no such operator
+    # a spilling tile the registry leaves out is not compiled for that operator
+    plan = C.Plan.make(C.PATH_SINGLE_WG, 1, 1024, 8, 16)
+    assert L.credit_run_plan(4, _ops(x=A, dy=G, gamma=G, y=B), 4, 32768, 1e-5, 0, ctypes.byref(plan), None) == 2
 
 
 def test_run_plan_timed_validation():
     L = C.lib()
     E1, E2 = ctypes.c_void_p(0x1000), ctypes.c_void_p(0x2000)
     plan = C.Plan.make(C.PATH_SINGLE_WG, 1, 64, 1, 16)
+    sm = _ops(x=A, y=B)
     # both events are required, and an empty launch cannot be timed
-    assert L.credit_run_plan_timed(0, A, None, None, B, 4, 64, 0.0, 0, ctypes.byref(plan), None, E2, None) == 1
-    assert L.credit_run_plan_timed(0, A, None, None, B, 4, 64, 0.0, 0, ctypes.byref(plan), E1, None, None) == 1
-    assert L.credit_run_plan_timed(0, A, None, None, B, 0, 64, 0.0, 0, ctypes.byref(plan), E1, E2, None) == 1
-    assert L.credit_run_plan_timed(0, MIS, None, None, B, 4, 64, 0.0, 0, ctypes.byref(plan), E1, E2, None) == 3
-    assert L.credit_run_plan_timed(0, A, None, None, B, 4, 1024, 0.0, 0, ctypes.byref(plan), E1, E2, None) == 4
+    assert L.credit_run_plan_timed(0, sm, 4, 64, 0.0, 0, ctypes.byref(plan), None, E2, None) == 1
+    assert L.credit_run_plan_timed(0, sm, 4, 64, 0.0, 0, ctypes.byref(plan), E1, None, None) == 1
+    assert L.credit_run_plan_timed(0, sm, 0, 64, 0.0, 0, ctypes.byref(plan), E1, E2, None) == 1
+    assert L.credit_run_plan_timed(0, _ops(x=MIS, y=B), 4, 64, 0.0, 0, ctypes.byref(plan), E1, E2, None) == 3
+    assert L.credit_run_plan_timed(0, sm, 4, 1024, 0.0, 0, ctypes.byref(plan), E1, E2, None) == 4
 
 
 def test_misc_entry_points_validate():
@@ -134,7 +174,25 @@ def test_selector_legality_on_cpu():
     p = C.credit_select_path("rmsnorm", "bf16", 10, 1001)
     assert p.vec_bytes == 2
     assert C.lib().credit_select_path(0, 0, 1, 1, None) == 1
-    assert C.lib().credit_select_path(3, 0, 1, 1, ctypes.byref(C.Plan())) == 1
+    assert C.lib().credit_select_path(6, 0, 1, 1, ctypes.byref(C.Plan())) == 1
+    assert C.lib().credit_select_path(4, 1, 1, 1, ctypes.byref(C.Plan())) == 2  # LayerNorm backward bf16
+
+
+def test_selector_legality_of_the_further_workloads():
+    # x and dy held: path 1 holds at most 32768 fp32 columns (two inputs)
+    for op in ("softmax_bwd", "layernorm_bwd"):
+        assert C.credit_select_path(op, "f32", 4096, 32768).predicted_us[0] > 0
+        p = C.credit_select_path(op, "f32", 4096, 65536)
+        assert p.predicted_us[0] < 0 and p.path in (C.PATH_SPLIT_ROW, C.PATH_REREAD)
+        with pytest.raises(C.CreditError) as ei:
+            C.credit_plan(op, "f32", 4096, 65536, "single")
+        assert ei.value.status == 4
+    # the quantizer holds one fp32 input: 65536 columns fit one workgroup
+    assert C.credit_select_path("quantize_int8", "f32", 4096, 65536).predicted_us[0] > 0
+    # every enumerated plan of a two-input operator resolves to a compiled kernel
+    for op in ("softmax_bwd", "layernorm_bwd"):
+        for plan in C.credit_enumerate_plans(op, "f32", 2048, 65536):
+            assert C.lib().credit_run_plan(C.OPS[op], None, 1, 1, 0.0, 0, ctypes.byref(plan), None) == 1
 
 
 def test_calibration_loader(tmp_path):

@@ -82,7 +82,8 @@ def test_unmeasured_width_uses_the_analytic_model(tmp_path):
     [0, 0, 4096, 4, 1, 512, 2, 16, -1, 2, 100, 10.0, 1000, 50.0],   # no path 4
     [0, 0, 4096, 1, 1, 512, 2, 16, -1, 2, 100, 10.0, 1000],         # a point is missing
     [0, 0, 4096, 1, 1, 512, 2, 16, -1, 2, 100, -1.0, 1000, 50.0],   # non-positive time
-    [3, 0, 4096, 1, 1, 512, 2, 16, -1, 2, 100, 10.0, 1000, 50.0],   # no op 3
+    [6, 0, 4096, 1, 1, 512, 2, 16, -1, 2, 100, 10.0, 1000, 50.0],   # no op 6
+    [4, 1, 4096, 1, 1, 512, 2, 16, -1, 2, 100, 10.0, 1000, 50.0],   # LayerNorm backward has no bf16
     [0, 0, 4096, 1, 1, 512, 2, 16, -1],                             # header cut short
 ])
 def test_malformed_tables_are_refused_and_the_previous_one_stays(tmp_path, bad):

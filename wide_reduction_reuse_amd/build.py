@@ -30,8 +30,8 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,
           "-Wall", "-Wno-unused-command-line-argument",
           "-I", INCLUDE, "-I", CSRC]
 
-SOURCES = ["inst_softmax.hip", "inst_layernorm.hip", "inst_rmsnorm.hip", "inst_misc.hip",
-           "api.cpp", "planner.cpp"]
+SOURCES = ["inst_softmax.hip", "inst_layernorm.hip", "inst_rmsnorm.hip", "inst_softmax_bwd.hip",
+           "inst_layernorm_bwd.hip", "inst_quantize.hip", "inst_misc.hip", "api.cpp", "planner.cpp"]
 
 
 def _compile(src: str) -> str:
@@ -51,7 +51,9 @@ def build(jobs: int = 0, verbose: bool = False) -> str:
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + objs
+    # -z defs: every symbol the library uses must resolve at link time (a
+    # missing translation unit fails here, not at load time)
+    cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH, "-Wl,-z,defs", "-o", tmp] + objs
     subprocess.check_call(cmd)
     os.replace(tmp, LIB)
     if verbose:

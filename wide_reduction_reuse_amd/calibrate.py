@@ -1,11 +1,13 @@
 """Selector calibration: measured candidates to a calibration file.
 
-    python -m wide_reduction_reuse_amd.calibrate --out FILE [--sweep SWEEP.jsonl] [--run]
+    python -m wide_reduction_reuse_amd.calibrate --out FILE [--sweep SWEEP.jsonl ...] [--run]
 
 With --run it first times every legal plan on the calibration shapes
 (workloads.calibration_points(): the crossover sweep's operators, dtypes and
-widths at 8, 64, 512 and 2048 MiB, sizes the scored sweep does not use) with
-the sweep driver and writes the records to --sweep.  It then builds the table
+widths at 8, 64, 512 and 2048 MiB, sizes the scored sweep does not use; and
+workloads.calibration_points_next(): the three further workloads at row counts
+their width grid does not use) with the sweep driver and writes the records to
+the (one) --sweep file.  Several --sweep files are merged.  It then builds the table
 credit_load_calibration reads: for each (op, dtype, cols) and each candidate
 plan, the median kernel time at every calibrated row count.  The selector
 interpolates these in (log rows, log time) for the rows it is asked about
@@ -21,8 +23,7 @@ import json
 import sys
 from collections import defaultdict
 
-OPS = {"softmax": 0, "layernorm": 1, "rmsnorm": 2}
-DTS = {"f32": 0, "bf16": 1}
+from .credit import DTYPES as DTS, OPS
 
 
 def build_table(records):
@@ -57,20 +58,20 @@ def device_info():
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--out", required=True)
-    ap.add_argument("--sweep", default=None, help="calibration sweep records (JSON lines)")
+    ap.add_argument("--sweep", nargs="*", default=None, help="calibration sweep records (JSON lines)")
     ap.add_argument("--run", action="store_true", help="time the calibration shapes first (needs a GPU)")
     ap.add_argument("--steps", type=int, default=15)
     a = ap.parse_args(argv)
     if a.run:
         from . import sweep
-        if not a.sweep:
-            ap.error("--run needs --sweep FILE for the records")
-        rc = sweep.main(["--points", "calib", "--out", a.sweep, "--steps", str(a.steps)])
+        if not a.sweep or len(a.sweep) != 1:
+            ap.error("--run needs one --sweep FILE for the records")
+        rc = sweep.main(["--points", "calib_all", "--out", a.sweep[0], "--steps", str(a.steps)])
         if rc:
             return rc
     if not a.sweep:
         ap.error("--sweep FILE is required")
-    records = [json.loads(l) for l in open(a.sweep) if l.strip()]
+    records = [json.loads(l) for path in a.sweep for l in open(path) if l.strip()]
     biggest = max(r["bytes"] for r in records)
     stream = max(r["bytes"] / (c["median_ms"] * 1e-3) / 1e9 for r in records if r["bytes"] == biggest
                  for c in r["candidates"])

@@ -23,13 +23,18 @@ STATUS_NAMES = {0: "CREDIT_OK", 1: "CREDIT_ERR_INVALID_ARG", 2: "CREDIT_ERR_UNSU
                 6: "CREDIT_ERR_NO_CALIBRATION", 7: "CREDIT_ERR_HIP", 8: "CREDIT_ERR_DEVICE_TIMEOUT"}
 # dtypes, ops, paths
 F32, BF16 = 0, 1
-SOFTMAX, LAYERNORM, RMSNORM = 0, 1, 2
+SOFTMAX, LAYERNORM, RMSNORM, SOFTMAX_BACKWARD, LAYERNORM_BACKWARD, QUANTIZE_INT8 = 0, 1, 2, 3, 4, 5
 PATH_AUTO, PATH_SINGLE_WG, PATH_SPLIT_ROW, PATH_REREAD = 0, 1, 2, 3
 PATHS = {"auto": 0, "single": 1, "split": 2, "reread": 3}
-OPS = {"softmax": 0, "layernorm": 1, "rmsnorm": 2}
+OPS = {"softmax": 0, "layernorm": 1, "rmsnorm": 2, "softmax_bwd": 3, "layernorm_bwd": 4, "quantize_int8": 5}
 DTYPES = {"f32": 0, "bf16": 1}
+# operands each operator reads or writes (credit_operands_t)
+OPERANDS = {"softmax": ("x", "y"), "layernorm": ("x", "gamma", "beta", "y"), "rmsnorm": ("x", "gamma", "y"),
+            "softmax_bwd": ("x", "dy", "y"), "layernorm_bwd": ("x", "dy", "gamma", "y"),
+            "quantize_int8": ("x", "y", "row_out")}
 
-EXPORTED = ["credit_softmax", "credit_layernorm", "credit_rmsnorm", "credit_select_path", "credit_make_plan",
+EXPORTED = ["credit_softmax", "credit_layernorm", "credit_rmsnorm", "credit_softmax_backward",
+            "credit_layernorm_backward", "credit_quantize_int8", "credit_select_path", "credit_make_plan",
             "credit_enumerate_plans", "credit_occupancy",
             "credit_run_plan", "credit_run_plan_timed", "credit_control", "credit_copy", "credit_flush",
             "credit_load_calibration", "credit_check_errors", "credit_status_str", "credit_version"]
@@ -60,6 +65,11 @@ class Plan(ctypes.Structure):
         return p
 
 
+class Operands(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("dy", ctypes.c_void_p), ("gamma", ctypes.c_void_p),
+                ("beta", ctypes.c_void_p), ("y", ctypes.c_void_p), ("row_out", ctypes.c_void_p)]
+
+
 _lib = None
 
 
@@ -83,12 +93,16 @@ def lib() -> ctypes.CDLL:
         "credit_softmax": [vp, vp, i64, i64, i32, i32, i32, vp],
         "credit_layernorm": [vp, vp, vp, vp, i64, i64, f32, i32, i32, i32, vp],
         "credit_rmsnorm": [vp, vp, vp, i64, i64, f32, i32, i32, i32, vp],
+        "credit_softmax_backward": [vp, vp, vp, i64, i64, i32, i32, i32, vp],
+        "credit_layernorm_backward": [vp, vp, vp, vp, i64, i64, f32, i32, i32, i32, vp],
+        "credit_quantize_int8": [vp, vp, vp, i64, i64, i32, i32, i32, vp],
         "credit_select_path": [i32, i32, i64, i64, ctypes.POINTER(Plan)],
         "credit_make_plan": [i32, i32, i64, i64, i32, i32, ctypes.POINTER(Plan)],
         "credit_enumerate_plans": [i32, i32, i64, i64, ctypes.POINTER(Plan), i32, ctypes.POINTER(i32)],
         "credit_occupancy": [i32, i32, i64, ctypes.POINTER(Plan), ctypes.POINTER(i32)],
-        "credit_run_plan": [i32, vp, vp, vp, vp, i64, i64, f32, i32, ctypes.POINTER(Plan), vp],
-        "credit_run_plan_timed": [i32, vp, vp, vp, vp, i64, i64, f32, i32, ctypes.POINTER(Plan), vp, vp, vp],
+        "credit_run_plan": [i32, ctypes.POINTER(Operands), i64, i64, f32, i32, ctypes.POINTER(Plan), vp],
+        "credit_run_plan_timed": [i32, ctypes.POINTER(Operands), i64, i64, f32, i32, ctypes.POINTER(Plan), vp, vp,
+                                  vp],
         "credit_control": [i32, i64, i64, i32, ctypes.POINTER(Plan), vp],
         "credit_copy": [vp, vp, i64, vp, vp, vp],
         "credit_flush": [vp, i64, vp],
@@ -149,13 +163,19 @@ def _path(path) -> int:
     return PATHS[path] if isinstance(path, str) else int(path)
 
 
-def _out(x, y):
+def _out(x, y, dtype=None):
     import torch
+    dtype = x.dtype if dtype is None else dtype
     if y is None:
-        y = torch.empty_like(x)
-    if y.shape != x.shape or y.dtype != x.dtype or not y.is_contiguous():
-        raise ValueError("y must be a contiguous tensor with x's shape and dtype")
+        y = torch.empty(x.shape, dtype=dtype, device=x.device)
+    if y.shape != x.shape or y.dtype != dtype or not y.is_contiguous():
+        raise ValueError("the output must be a contiguous %s tensor with x's shape" % dtype)
     return y
+
+
+def _same(x, t, name):
+    if t.shape != x.shape or t.dtype != x.dtype or not t.is_contiguous():
+        raise ValueError("%s must be a contiguous tensor with x's shape and dtype" % name)
 
 
 def credit_softmax(x, y=None, path="auto", split_p: int = 0, stream=None):
@@ -180,6 +200,41 @@ def credit_rmsnorm(x, gamma, eps: float, y=None, path="auto", split_p: int = 0, 
     _check(lib().credit_rmsnorm(_ptr(x), _ptr(gamma), _ptr(y), rows, cols, float(eps), _dtype_code(x),
                                 _path(path), split_p, _stream(stream)), "credit_rmsnorm")
     return y
+
+
+def credit_softmax_backward(x, dy, dx=None, path="auto", split_p: int = 0, stream=None):
+    """Gradient of row-wise softmax with respect to its logits x, given dy."""
+    _same(x, dy, "dy")
+    dx = _out(x, dx)
+    rows, cols = _shape2d(x)
+    _check(lib().credit_softmax_backward(_ptr(x), _ptr(dy), _ptr(dx), rows, cols, _dtype_code(x), _path(path),
+                                         split_p, _stream(stream)), "credit_softmax_backward")
+    return dx
+
+
+def credit_layernorm_backward(x, dy, gamma, eps: float, dx=None, path="auto", split_p: int = 0, stream=None):
+    """Row part of the LayerNorm gradient: dL/dx given dL/dy (fp32)."""
+    _same(x, dy, "dy")
+    dx = _out(x, dx)
+    rows, cols = _shape2d(x)
+    _check(lib().credit_layernorm_backward(_ptr(x), _ptr(dy), _ptr(gamma), _ptr(dx), rows, cols, float(eps),
+                                           _dtype_code(x), _path(path), split_p, _stream(stream)),
+           "credit_layernorm_backward")
+    return dx
+
+
+def credit_quantize_int8(x, q=None, scale=None, path="auto", split_p: int = 0, stream=None):
+    """Row-wise symmetric int8 quantization: returns (q int8 like x, scale float32 [rows])."""
+    import torch
+    q = _out(x, q, torch.int8)
+    rows, cols = _shape2d(x)
+    if scale is None:
+        scale = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+    if scale.numel() != rows or scale.dtype != torch.float32 or not scale.is_contiguous():
+        raise ValueError("scale must be a contiguous float32 tensor with one entry per row")
+    _check(lib().credit_quantize_int8(_ptr(x), _ptr(q), _ptr(scale), rows, cols, _dtype_code(x), _path(path),
+                                      split_p, _stream(stream)), "credit_quantize_int8")
+    return q, scale
 
 
 def credit_select_path(op, dtype, rows: int, cols: int) -> Plan:
@@ -220,23 +275,35 @@ def credit_occupancy(op, dtype, cols: int, plan: Plan) -> int:
     return n.value
 
 
-def credit_run_plan(op, x, gamma, beta, y, eps: float, plan: Plan, stream=None):
-    op = OPS[op] if isinstance(op, str) else int(op)
-    rows, cols = _shape2d(x)
-    _check(lib().credit_run_plan(op, _ptr(x), _ptr(gamma), _ptr(beta), _ptr(y), rows, cols, float(eps),
-                                 _dtype_code(x), ctypes.byref(plan), _stream(stream)), "credit_run_plan")
-    return y
+def operands(t) -> Operands:
+    """credit_operands_t from a mapping with keys among x, dy, gamma, beta, y,
+    row_out (tensors or None)."""
+    o = Operands()
+    for k in ("x", "dy", "gamma", "beta", "y", "row_out"):
+        v = t.get(k)
+        setattr(o, k, None if v is None else v.data_ptr())
+    return o
 
 
-def credit_run_plan_timed(op, x, gamma, beta, y, eps: float, plan: Plan, start_event: int, stop_event: int,
-                          stream=None):
-    """start_event / stop_event: raw hipEvent_t handles (integers)."""
+def credit_run_plan(op, plan: Plan, t, eps: float = 0.0, stream=None):
+    """Run `plan` on the operands in mapping `t` (see operands())."""
     op = OPS[op] if isinstance(op, str) else int(op)
-    rows, cols = _shape2d(x)
-    _check(lib().credit_run_plan_timed(op, _ptr(x), _ptr(gamma), _ptr(beta), _ptr(y), rows, cols, float(eps),
-                                       _dtype_code(x), ctypes.byref(plan), ctypes.c_void_p(start_event),
+    rows, cols = _shape2d(t["x"])
+    o = operands(t)
+    _check(lib().credit_run_plan(op, ctypes.byref(o), rows, cols, float(eps), _dtype_code(t["x"]),
+                                 ctypes.byref(plan), _stream(stream)), "credit_run_plan")
+    return t["y"]
+
+
+def credit_run_plan_timed(op, plan: Plan, t, start_event: int, stop_event: int, eps: float = 0.0, stream=None):
+    """credit_run_plan with timing; start_event / stop_event: raw hipEvent_t handles (integers)."""
+    op = OPS[op] if isinstance(op, str) else int(op)
+    rows, cols = _shape2d(t["x"])
+    o = operands(t)
+    _check(lib().credit_run_plan_timed(op, ctypes.byref(o), rows, cols, float(eps), _dtype_code(t["x"]),
+                                       ctypes.byref(plan), ctypes.c_void_p(start_event),
                                        ctypes.c_void_p(stop_event), _stream(stream)), "credit_run_plan_timed")
-    return y
+    return t["y"]
 
 
 def credit_control(op, rows: int, cols: int, dtype, plan: Plan, stream=None) -> None:
@@ -273,13 +340,22 @@ def credit_version() -> int:
     return int(lib().credit_version())
 
 
-def run(op: str, x, gamma=None, beta=None, eps: float = 0.0, y=None, path="auto", split_p: int = 0,
-        stream=None):
-    """Dispatch by operator name to the matching entry point."""
+def run(op: str, t, eps: float = 0.0, path="auto", split_p: int = 0, stream=None):
+    """Dispatch by operator name to the matching entry point.  `t` maps operand
+    names (x, dy, gamma, beta; outputs y and row_out, allocated when absent)
+    to tensors.  Returns the output row tensor (for quantization, (q, scale))."""
+    x = t["x"]
+    y = t.get("y")
     if op == "softmax":
         return credit_softmax(x, y, path, split_p, stream)
     if op == "layernorm":
-        return credit_layernorm(x, gamma, beta, eps, y, path, split_p, stream)
+        return credit_layernorm(x, t["gamma"], t["beta"], eps, y, path, split_p, stream)
     if op == "rmsnorm":
-        return credit_rmsnorm(x, gamma, eps, y, path, split_p, stream)
+        return credit_rmsnorm(x, t["gamma"], eps, y, path, split_p, stream)
+    if op == "softmax_bwd":
+        return credit_softmax_backward(x, t["dy"], y, path, split_p, stream)
+    if op == "layernorm_bwd":
+        return credit_layernorm_backward(x, t["dy"], t["gamma"], eps, y, path, split_p, stream)
+    if op == "quantize_int8":
+        return credit_quantize_int8(x, y, t.get("row_out"), path, split_p, stream)
     raise ValueError(op)

@@ -32,6 +32,9 @@ const std::vector<KernelEntry> &registry()
         register_softmax_kernels(r);
         register_layernorm_kernels(r);
         register_rmsnorm_kernels(r);
+        register_softmax_bwd_kernels(r);
+        register_layernorm_bwd_kernels(r);
+        register_quantize_kernels(r);
         register_misc_kernels(r);
         return r;
     }();
@@ -177,16 +180,39 @@ credit_status_t get_scratch_locked(hipStream_t s, Scratch **out)
 // validation
 // ---------------------------------------------------------------------------
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
-credit_status_t validate(int op, const void *x, const void *g, const void *b, const void *y, int64_t rows,
-                         int64_t cols, float eps, int dt, bool *noop)
+// CREDIT_ERR_INVALID_ARG for an operator or dtype outside the enums,
+// CREDIT_ERR_UNSUPPORTED for a pair without kernels.
+credit_status_t check_op_dt(int op, int dt)
+{
+    if (op < 0 || op >= kNumOps || (dt != CREDIT_F32 && dt != CREDIT_BF16))
+        return CREDIT_ERR_INVALID_ARG;
+    if (!op_supported(op, dt))
+        return CREDIT_ERR_UNSUPPORTED;
+    return CREDIT_OK;
+}
+
+// Which operands an operator reads or writes (credit_operands_t).
+bool uses_dy(int op) { return op == CREDIT_OP_SOFTMAX_BACKWARD || op == CREDIT_OP_LAYERNORM_BACKWARD; }
+bool uses_gamma(int op) { return n_params(op) >= 1; }
+bool uses_beta(int op) { return n_params(op) >= 2; }
+bool uses_row_out(int op) { return row_out_bytes(op) > 0; }
+bool uses_eps(int op)
+{
+    return op == CREDIT_OP_LAYERNORM || op == CREDIT_OP_RMSNORM || op == CREDIT_OP_LAYERNORM_BACKWARD;
+}
+
+credit_status_t validate(int op, const credit_operands_t &t, int64_t rows, int64_t cols, float eps, int dt,
+                         bool *noop)
 {
     *noop = false;
-    if (op < 0 || op > 2 || (dt != CREDIT_F32 && dt != CREDIT_BF16))
-        return CREDIT_ERR_INVALID_ARG;
+    credit_status_t st = check_op_dt(op, dt);
+    if (st != CREDIT_OK)
+        return st;
     if (rows < 0 || cols < 1)
         return CREDIT_ERR_INVALID_ARG;
-    if (op != CREDIT_OP_SOFTMAX && (!std::isfinite(eps) || eps < 0.0f))
+    if (uses_eps(op) && (!std::isfinite(eps) || eps < 0.0f))
         return CREDIT_ERR_INVALID_ARG;
     // element count and byte size must fit comfortably in int64
     const int64_t eb = elem_bytes(dt);
@@ -196,13 +222,13 @@ credit_status_t validate(int op, const void *x, const void *g, const void *b, co
         *noop = true;
         return CREDIT_OK;
     }
-    if (x == nullptr || y == nullptr)
+    if (t.x == nullptr || t.y == nullptr || (uses_dy(op) && t.dy == nullptr) ||
+        (uses_gamma(op) && t.gamma == nullptr) || (uses_beta(op) && t.beta == nullptr) ||
+        (uses_row_out(op) && t.row_out == nullptr))
         return CREDIT_ERR_INVALID_ARG;
-    if (op >= 1 && g == nullptr)
-        return CREDIT_ERR_INVALID_ARG;
-    if (op == 1 && b == nullptr)
-        return CREDIT_ERR_INVALID_ARG;
-    if (!aligned16(x) || !aligned16(y) || (op >= 1 && !aligned16(g)) || (op == 1 && !aligned16(b)))
+    if (!aligned16(t.x) || !aligned16(t.y) || (uses_dy(op) && !aligned16(t.dy)) ||
+        (uses_gamma(op) && !aligned16(t.gamma)) || (uses_beta(op) && !aligned16(t.beta)) ||
+        (uses_row_out(op) && !aligned4(t.row_out)))
         return CREDIT_ERR_ALIGNMENT;
     return CREDIT_OK;
 }
@@ -251,6 +277,22 @@ credit_status_t launch_raw(const KernelEntry *k, uint32_t grid, uint32_t block, 
 // Workgroups of kernel `k` one CU holds at once; cached per kernel.
 credit_status_t occupancy(const KernelEntry *k, int *out);
 
+// The arguments for rows [r0, r0 + n) of `a` (null pointers stay null).
+RowArgs rows_from(const RowArgs &a, int op, int dt, int64_t r0, int64_t n)
+{
+    auto at = [](const void *p, int64_t off) -> const char * {
+        return p == nullptr ? nullptr : static_cast<const char *>(p) + off;
+    };
+    const int64_t in_off = r0 * a.cols * elem_bytes(dt);
+    RowArgs r = a;
+    r.x = at(a.x, in_off);
+    r.dy = at(a.dy, in_off);
+    r.y = const_cast<char *>(at(a.y, r0 * a.cols * out_bytes(op, dt)));
+    r.row_out = const_cast<char *>(at(a.row_out, r0 * row_out_bytes(op)));
+    r.rows = n;
+    return r;
+}
+
 // Paths 1 and 3.  Path 1 kernels loop over rows: with wgs_per_cu == 0 the grid
 // is as many workgroups as the device holds at once (each owner then takes
 // every G-th row, loading the next row while it writes the current one), with
@@ -262,7 +304,6 @@ credit_status_t launch_rowwise(const KernelEntry *k, const RowArgs &a0, int wgs_
 {
     const int64_t rows_per_wg = k->kind == kKindWave ? kWaveRowsPerWg : 1;
     const int block = k->kind == kKindWave ? 64 * kWaveRowsPerWg : k->block;
-    const int64_t eb = elem_bytes(k->dt);
     int64_t grid_cap = kMaxGridWgs;
     if (k->kind != kKindReread && wgs_per_cu >= 0) {
         int occ = 0;
@@ -279,12 +320,8 @@ credit_status_t launch_rowwise(const KernelEntry *k, const RowArgs &a0, int wgs_
     }
     const int64_t chunk_rows = kMaxGridWgs * rows_per_wg;
     for (int64_t r0 = 0; r0 < a0.rows; r0 += chunk_rows) {
-        RowArgs a = a0;
         const int64_t n = std::min(chunk_rows, a0.rows - r0);
-        const int64_t off = r0 * a0.cols * eb;
-        a.x = static_cast<const char *>(a0.x) + off;
-        a.y = static_cast<char *>(a0.y) + off;
-        a.rows = n;
+        RowArgs a = rows_from(a0, k->op, k->dt, r0, n);
         const int64_t grid = std::min(grid_cap, (n + rows_per_wg - 1) / rows_per_wg);
         const credit_status_t st = launch_raw(k, static_cast<uint32_t>(grid), block, &a, s,
                                               r0 == 0 ? ev.start : nullptr,
@@ -341,7 +378,6 @@ credit_status_t launch_split(const KernelEntry *k, const RowArgs &a0, int p, int
     const int64_t clusters = std::min({std::max<int64_t>(1, allowed / p), kSlotWords / (INT64_C(2) * p * q), a0.rows});
     const int64_t max_iters = INT64_C(1) << 30;  // row iterations per launch (tag range)
     const int64_t rows_per_launch = clusters * max_iters;
-    const int64_t eb = elem_bytes(k->dt);
     for (int64_t r0 = 0; r0 < a0.rows; r0 += rows_per_launch) {
         const int64_t n = std::min(rows_per_launch, a0.rows - r0);
         const int64_t c = std::min(clusters, n);
@@ -359,11 +395,7 @@ credit_status_t launch_split(const KernelEntry *k, const RowArgs &a0, int p, int
             sc->next_tag = 1;
         }
         SplitArgs sa;
-        sa.r = a0;
-        const int64_t off = r0 * a0.cols * eb;
-        sa.r.x = a0.x == nullptr ? nullptr : static_cast<const char *>(a0.x) + off;
-        sa.r.y = a0.y == nullptr ? nullptr : static_cast<char *>(a0.y) + off;
-        sa.r.rows = n;
+        sa.r = rows_from(a0, k->op, k->dt, r0, n);
         sa.ticket = &sc->ctl->ticket;
         sa.error = &sc->ctl->error;
         sa.slots = sc->slots;
@@ -438,9 +470,9 @@ void to_c_plan(const Plan &p, credit_plan_t *out)
         out->predicted_us[i] = p.est[i].legal ? p.est[i].us : -1.0;
 }
 
-credit_status_t run_plan_checked(int op, const void *x, const void *g, const void *b, void *y, int64_t rows,
-                                 int64_t cols, float eps, int dt, const credit_plan_t &plan, hipStream_t s,
-                                 bool control, const LaunchEvents &ev = LaunchEvents{})
+credit_status_t run_plan_checked(int op, const credit_operands_t &t, int64_t rows, int64_t cols, float eps, int dt,
+                                 const credit_plan_t &plan, hipStream_t s, bool control,
+                                 const LaunchEvents &ev = LaunchEvents{})
 {
     const KernelEntry *k = nullptr;
     int kind = 0;
@@ -455,10 +487,12 @@ credit_status_t run_plan_checked(int op, const void *x, const void *g, const voi
             return CREDIT_ERR_UNSUPPORTED;
     }
     RowArgs a;
-    a.x = x;
-    a.gamma = g;
-    a.beta = b;
-    a.y = y;
+    a.x = t.x;
+    a.dy = uses_dy(op) ? t.dy : nullptr;
+    a.gamma = uses_gamma(op) ? t.gamma : nullptr;
+    a.beta = uses_beta(op) ? t.beta : nullptr;
+    a.y = t.y;
+    a.row_out = uses_row_out(op) ? t.row_out : nullptr;
     a.rows = rows;
     a.cols = cols;
     a.eps = eps;
@@ -471,11 +505,11 @@ credit_status_t run_plan_checked(int op, const void *x, const void *g, const voi
     return launch_rowwise(k, a, plan.wgs_per_cu, s, ev);
 }
 
-credit_status_t run_op(int op, const void *x, const void *g, const void *b, void *y, int64_t rows, int64_t cols,
-                       float eps, int dt, int path, int split_p, void *stream)
+credit_status_t run_op(int op, const credit_operands_t &t, int64_t rows, int64_t cols, float eps, int dt, int path,
+                       int split_p, void *stream)
 {
     bool noop = false;
-    credit_status_t st = validate(op, x, g, b, y, rows, cols, eps, dt, &noop);
+    credit_status_t st = validate(op, t, rows, cols, eps, dt, &noop);
     if (st != CREDIT_OK)
         return st;
     st = check_path_args(path, split_p);
@@ -498,7 +532,20 @@ credit_status_t run_op(int op, const void *x, const void *g, const void *b, void
     }
     credit_plan_t cp;
     to_c_plan(p, &cp);
-    return run_plan_checked(op, x, g, b, y, rows, cols, eps, dt, cp, static_cast<hipStream_t>(stream), false);
+    return run_plan_checked(op, t, rows, cols, eps, dt, cp, static_cast<hipStream_t>(stream), false);
+}
+
+credit_operands_t operands(const void *x, const void *dy, const void *gamma, const void *beta, void *y,
+                           void *row_out)
+{
+    credit_operands_t t;
+    t.x = x;
+    t.dy = dy;
+    t.gamma = gamma;
+    t.beta = beta;
+    t.y = y;
+    t.row_out = row_out;
+    return t;
 }
 
 }  // namespace
@@ -529,27 +576,55 @@ extern "C" {
 credit_status_t credit_softmax(const void *x, void *y, int64_t rows, int64_t cols, credit_dtype_t dt,
                                credit_path_t path, int32_t split_p, void *stream)
 {
-    return run_op(CREDIT_OP_SOFTMAX, x, nullptr, nullptr, y, rows, cols, 0.0f, dt, path, split_p, stream);
+    return run_op(CREDIT_OP_SOFTMAX, operands(x, nullptr, nullptr, nullptr, y, nullptr), rows, cols, 0.0f, dt, path,
+                  split_p, stream);
 }
 
 credit_status_t credit_layernorm(const void *x, const void *gamma, const void *beta, void *y, int64_t rows,
                                  int64_t cols, float eps, credit_dtype_t dt, credit_path_t path,
                                  int32_t split_p, void *stream)
 {
-    return run_op(CREDIT_OP_LAYERNORM, x, gamma, beta, y, rows, cols, eps, dt, path, split_p, stream);
+    return run_op(CREDIT_OP_LAYERNORM, operands(x, nullptr, gamma, beta, y, nullptr), rows, cols, eps, dt, path,
+                  split_p, stream);
 }
 
 credit_status_t credit_rmsnorm(const void *x, const void *gamma, void *y, int64_t rows, int64_t cols, float eps,
                                credit_dtype_t dt, credit_path_t path, int32_t split_p, void *stream)
 {
-    return run_op(CREDIT_OP_RMSNORM, x, gamma, nullptr, y, rows, cols, eps, dt, path, split_p, stream);
+    return run_op(CREDIT_OP_RMSNORM, operands(x, nullptr, gamma, nullptr, y, nullptr), rows, cols, eps, dt, path,
+                  split_p, stream);
+}
+
+credit_status_t credit_softmax_backward(const void *x, const void *dy, void *dx, int64_t rows, int64_t cols,
+                                        credit_dtype_t dt, credit_path_t path, int32_t split_p, void *stream)
+{
+    return run_op(CREDIT_OP_SOFTMAX_BACKWARD, operands(x, dy, nullptr, nullptr, dx, nullptr), rows, cols, 0.0f, dt,
+                  path, split_p, stream);
+}
+
+credit_status_t credit_layernorm_backward(const void *x, const void *dy, const void *gamma, void *dx,
+                                          int64_t rows, int64_t cols, float eps, credit_dtype_t dt,
+                                          credit_path_t path, int32_t split_p, void *stream)
+{
+    return run_op(CREDIT_OP_LAYERNORM_BACKWARD, operands(x, dy, gamma, nullptr, dx, nullptr), rows, cols, eps, dt,
+                  path, split_p, stream);
+}
+
+credit_status_t credit_quantize_int8(const void *x, int8_t *q, float *scale, int64_t rows, int64_t cols,
+                                     credit_dtype_t dt, credit_path_t path, int32_t split_p, void *stream)
+{
+    return run_op(CREDIT_OP_QUANTIZE_INT8, operands(x, nullptr, nullptr, nullptr, q, scale), rows, cols, 0.0f, dt,
+                  path, split_p, stream);
 }
 
 credit_status_t credit_select_path(credit_op_t op, credit_dtype_t dt, int64_t rows, int64_t cols,
                                    credit_plan_t *out)
 {
-    if (out == nullptr || op < 0 || op > 2 || (dt != CREDIT_F32 && dt != CREDIT_BF16) || rows < 0 || cols < 1)
+    if (out == nullptr || rows < 0 || cols < 1)
         return CREDIT_ERR_INVALID_ARG;
+    credit_status_t st = check_op_dt(op, dt);
+    if (st != CREDIT_OK)
+        return st;
     std::lock_guard<std::mutex> lk(g_mu);
     const Calibration cal = calibration_locked();
     PlanRequest req;
@@ -567,9 +642,12 @@ credit_status_t credit_select_path(credit_op_t op, credit_dtype_t dt, int64_t ro
 credit_status_t credit_make_plan(credit_op_t op, credit_dtype_t dt, int64_t rows, int64_t cols, credit_path_t path,
                                  int32_t split_p, credit_plan_t *out)
 {
-    if (out == nullptr || op < 0 || op > 2 || (dt != CREDIT_F32 && dt != CREDIT_BF16) || rows < 0 || cols < 1)
+    if (out == nullptr || rows < 0 || cols < 1)
         return CREDIT_ERR_INVALID_ARG;
-    credit_status_t st = check_path_args(path, split_p);
+    credit_status_t st = check_op_dt(op, dt);
+    if (st != CREDIT_OK)
+        return st;
+    st = check_path_args(path, split_p);
     if (st != CREDIT_OK)
         return st;
     std::lock_guard<std::mutex> lk(g_mu);
@@ -589,9 +667,11 @@ credit_status_t credit_make_plan(credit_op_t op, credit_dtype_t dt, int64_t rows
 credit_status_t credit_enumerate_plans(credit_op_t op, credit_dtype_t dt, int64_t rows, int64_t cols,
                                        credit_plan_t *out, int32_t capacity, int32_t *count)
 {
-    if (count == nullptr || capacity < 0 || (out == nullptr && capacity > 0) || op < 0 || op > 2 ||
-        (dt != CREDIT_F32 && dt != CREDIT_BF16) || rows < 0 || cols < 1)
+    if (count == nullptr || capacity < 0 || (out == nullptr && capacity > 0) || rows < 0 || cols < 1)
         return CREDIT_ERR_INVALID_ARG;
+    const credit_status_t st = check_op_dt(op, dt);
+    if (st != CREDIT_OK)
+        return st;
     std::vector<Candidate> cands;
     {
         std::lock_guard<std::mutex> lk(g_mu);
@@ -622,12 +702,14 @@ credit_status_t credit_enumerate_plans(credit_op_t op, credit_dtype_t dt, int64_
 credit_status_t credit_occupancy(credit_op_t op, credit_dtype_t dt, int64_t cols, const credit_plan_t *plan,
                                  int32_t *wgs_per_cu)
 {
-    if (plan == nullptr || wgs_per_cu == nullptr || op < 0 || op > 2 || (dt != CREDIT_F32 && dt != CREDIT_BF16) ||
-        cols < 1)
+    if (plan == nullptr || wgs_per_cu == nullptr || cols < 1)
         return CREDIT_ERR_INVALID_ARG;
+    credit_status_t st = check_op_dt(op, dt);
+    if (st != CREDIT_OK)
+        return st;
     const KernelEntry *k = nullptr;
     int kind = 0;
-    credit_status_t st = resolve_plan(op, dt, cols, *plan, &k, &kind);
+    st = resolve_plan(op, dt, cols, *plan, &k, &kind);
     if (st != CREDIT_OK)
         return st;
     int occ = 0;
@@ -638,29 +720,26 @@ credit_status_t credit_occupancy(credit_op_t op, credit_dtype_t dt, int64_t cols
     return CREDIT_OK;
 }
 
-credit_status_t credit_run_plan(credit_op_t op, const void *x, const void *gamma, const void *beta, void *y,
-                                int64_t rows, int64_t cols, float eps, credit_dtype_t dt,
-                                const credit_plan_t *plan, void *stream)
+credit_status_t credit_run_plan(credit_op_t op, const credit_operands_t *ops, int64_t rows, int64_t cols,
+                                float eps, credit_dtype_t dt, const credit_plan_t *plan, void *stream)
 {
-    if (plan == nullptr)
+    if (plan == nullptr || ops == nullptr)
         return CREDIT_ERR_INVALID_ARG;
     bool noop = false;
-    credit_status_t st = validate(op, x, gamma, beta, y, rows, cols, eps, dt, &noop);
+    credit_status_t st = validate(op, *ops, rows, cols, eps, dt, &noop);
     if (st != CREDIT_OK || noop)
         return st;
-    return run_plan_checked(op, x, gamma, beta, y, rows, cols, eps, dt, *plan, static_cast<hipStream_t>(stream),
-                            false);
+    return run_plan_checked(op, *ops, rows, cols, eps, dt, *plan, static_cast<hipStream_t>(stream), false);
 }
 
-credit_status_t credit_run_plan_timed(credit_op_t op, const void *x, const void *gamma, const void *beta, void *y,
-                                      int64_t rows, int64_t cols, float eps, credit_dtype_t dt,
-                                      const credit_plan_t *plan, void *start_event, void *stop_event,
-                                      void *stream)
+credit_status_t credit_run_plan_timed(credit_op_t op, const credit_operands_t *ops, int64_t rows, int64_t cols,
+                                      float eps, credit_dtype_t dt, const credit_plan_t *plan, void *start_event,
+                                      void *stop_event, void *stream)
 {
-    if (plan == nullptr || start_event == nullptr || stop_event == nullptr)
+    if (plan == nullptr || ops == nullptr || start_event == nullptr || stop_event == nullptr)
         return CREDIT_ERR_INVALID_ARG;
     bool noop = false;
-    credit_status_t st = validate(op, x, gamma, beta, y, rows, cols, eps, dt, &noop);
+    credit_status_t st = validate(op, *ops, rows, cols, eps, dt, &noop);
     if (st != CREDIT_OK)
         return st;
     if (noop)
@@ -668,21 +747,23 @@ credit_status_t credit_run_plan_timed(credit_op_t op, const void *x, const void 
     LaunchEvents ev;
     ev.start = static_cast<hipEvent_t>(start_event);
     ev.stop = static_cast<hipEvent_t>(stop_event);
-    return run_plan_checked(op, x, gamma, beta, y, rows, cols, eps, dt, *plan, static_cast<hipStream_t>(stream),
-                            false, ev);
+    return run_plan_checked(op, *ops, rows, cols, eps, dt, *plan, static_cast<hipStream_t>(stream), false, ev);
 }
 
 credit_status_t credit_control(credit_op_t op, int64_t rows, int64_t cols, credit_dtype_t dt,
                                const credit_plan_t *plan, void *stream)
 {
-    if (plan == nullptr || op < 0 || op > 2 || (dt != CREDIT_F32 && dt != CREDIT_BF16) || rows < 0 || cols < 1)
+    if (plan == nullptr || rows < 0 || cols < 1)
         return CREDIT_ERR_INVALID_ARG;
+    const credit_status_t st = check_op_dt(op, dt);
+    if (st != CREDIT_OK)
+        return st;
     if (plan->path != CREDIT_PATH_SPLIT_ROW)
         return CREDIT_ERR_INVALID_ARG;
     if (rows == 0)
         return CREDIT_OK;
-    return run_plan_checked(op, nullptr, nullptr, nullptr, nullptr, rows, cols, 0.0f, dt, *plan,
-                            static_cast<hipStream_t>(stream), true);
+    return run_plan_checked(op, operands(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr), rows, cols, 0.0f, dt,
+                            *plan, static_cast<hipStream_t>(stream), true);
 }
 
 credit_status_t credit_copy(const void *src, void *dst, int64_t bytes, void *start_event, void *stop_event,

@@ -7,13 +7,15 @@
 namespace credit {
 
 struct RowArgs {
-    const void *x;
-    const void *gamma;
+    const void *x;      // [rows][cols] row input
+    const void *gamma;  // [cols] parameters, else null
     const void *beta;
-    void *y;
+    void *y;            // [rows][cols] output (int8 codes for quantization)
     int64_t rows;
     int64_t cols;
     float eps;
+    const void *dy;     // [rows][cols] second row input (backward operators), else null
+    void *row_out;      // [rows] fp32 per-row output (quantization scale), else null
 };
 
 // Exchange control block (one per scratch); each counter on its own 128-byte line.

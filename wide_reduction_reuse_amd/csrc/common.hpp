@@ -29,12 +29,25 @@ template <> struct StorageTraits<float> {
 template <> struct StorageTraits<bf16_t> {
     static constexpr int kBytes = 2;
 };
+// int8 output codes (quantization); never an input type.
+struct i8_t {
+    int8_t bits;
+};
+template <> struct StorageTraits<i8_t> {
+    static constexpr int kBytes = 1;
+};
 
-// A vector of VB bytes (16, or one element) moved by a single global access.
+// A vector of VB bytes moved by a single global access: 16 bytes, or one
+// element; 8 and 1 bytes occur as the int8 output of a 16-byte bf16 or a
+// one-element input vector.
 template <int VB> struct RawVec;
 template <> struct RawVec<16> {
     static constexpr int kWords = 4;
     u32x4 w;
+};
+template <> struct RawVec<8> {
+    static constexpr int kWords = 2;
+    u32x2 w;
 };
 template <> struct RawVec<4> {
     static constexpr int kWords = 1;
@@ -42,6 +55,10 @@ template <> struct RawVec<4> {
 };
 template <> struct RawVec<2> {
     static constexpr int kWords = 1;  // low half used
+    uint32_t w;
+};
+template <> struct RawVec<1> {
+    static constexpr int kWords = 1;  // low byte used
     uint32_t w;
 };
 
@@ -96,10 +113,14 @@ __device__ __forceinline__ void buf_store(const RawVec<VB> &v, rsrc_t r, uint32_
 {
     if constexpr (VB == 16) {
         __builtin_amdgcn_raw_buffer_store_b128(v.w, r, static_cast<int>(voff), 0, POLICY);
+    } else if constexpr (VB == 8) {
+        __builtin_amdgcn_raw_buffer_store_b64(v.w, r, static_cast<int>(voff), 0, POLICY);
     } else if constexpr (VB == 4) {
         __builtin_amdgcn_raw_buffer_store_b32(v.w, r, static_cast<int>(voff), 0, POLICY);
-    } else {
+    } else if constexpr (VB == 2) {
         __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(v.w), r, static_cast<int>(voff), 0, POLICY);
+    } else {
+        __builtin_amdgcn_raw_buffer_store_b8(static_cast<unsigned char>(v.w), r, static_cast<int>(voff), 0, POLICY);
     }
 }
 
@@ -120,14 +141,14 @@ __device__ __forceinline__ bool wave_all(bool pred)
 
 template <int VB> __device__ __forceinline__ uint32_t word(const RawVec<VB> &r, int i)
 {
-    if constexpr (VB == 16)
+    if constexpr (VB >= 8)
         return r.w[i];
     else
         return r.w;
 }
 template <int VB> __device__ __forceinline__ void set_word(RawVec<VB> &r, int i, uint32_t v)
 {
-    if constexpr (VB == 16)
+    if constexpr (VB >= 8)
         r.w[i] = v;
     else
         r.w = v;
@@ -146,12 +167,22 @@ __device__ __forceinline__ float elem(const RawVec<VB> &r, int e)
 }
 
 // Pack fp32 results into a raw vector of the storage type (bf16: round to
-// nearest even with v_cvt_pk_bf16_f32).
+// nearest even with v_cvt_pk_bf16_f32; int8: the values are already integers
+// in [-127, 127], converted exactly and packed little-endian).
 template <class T, int VB, int EPV>
 __device__ __forceinline__ RawVec<VB> pack(const float (&v)[EPV])
 {
     RawVec<VB> r;
-    if constexpr (StorageTraits<T>::kBytes == 4) {
+    if constexpr (StorageTraits<T>::kBytes == 1) {
+#pragma unroll
+        for (int w = 0; w < (EPV + 3) / 4; ++w) {
+            uint32_t acc = 0;
+#pragma unroll
+            for (int e = 4 * w; e < EPV && e < 4 * w + 4; ++e)
+                acc |= (static_cast<uint32_t>(static_cast<int32_t>(v[e])) & 0xffu) << (8 * (e - 4 * w));
+            set_word<VB>(r, w, acc);
+        }
+    } else if constexpr (StorageTraits<T>::kBytes == 4) {
 #pragma unroll
         for (int e = 0; e < EPV; ++e)
             set_word<VB>(r, e, __float_as_uint(v[e]));

@@ -1,0 +1,11 @@
+// Kernel instantiations for LayerNorm backward (row part) (fp32).
+#include "instantiate.hpp"
+
+namespace credit {
+
+void register_layernorm_bwd_kernels(std::vector<KernelEntry> &out)
+{
+    register_op_dtype<kLayerNormBwd, float, 0>(out);
+}
+
+}  // namespace credit

@@ -10,6 +10,8 @@ namespace credit {
 template <OpKind OP, class T, int DT>
 void register_op_dtype(std::vector<KernelEntry> &v)
 {
+    static_assert(OpTraits<OP>::kIn == op_inputs(OP), "registry.hpp's op_inputs must match the operator");
+    static_assert(OpTraits<OP>::kQ == op_stats(OP), "registry.hpp's op_stats must match the operator");
     constexpr int VB = 16;
     constexpr int VS = StorageTraits<T>::kBytes;  // one-element access
 #define CREDIT_K(kind, vb, block, items, ...)                                                                  \

@@ -51,20 +51,49 @@
 
 namespace credit {
 
-template <class Partial>
-__device__ __forceinline__ float comp(const Partial &p, int j)
+// Component j < Q of a partial, j a run-time index, as one explicit if/else
+// chain on j.  (Written as a loop of conditional moves, or as a recursive
+// template, the split kernel's exchange compiled to up to 19 more VGPRs.)
+template <int Q>
+__device__ __forceinline__ float comp(const Part<Q> &p, int j)
 {
-    return j == 0 ? p.a : (j == 1 ? p.b : p.c);
-}
-template <class Partial>
-__device__ __forceinline__ void set_comp(Partial &p, int j, float v)
-{
-    if (j == 0)
-        p.a = v;
-    else if (j == 1)
-        p.b = v;
+    static_assert(Q >= 1 && Q <= 5, "partials hold 1 to 5 scalars");
+    if constexpr (Q <= 3)
+        return j == 0 ? p.v[0] : (j == 1 ? p.v[1 % Q] : p.v[2 % Q]);
     else
-        p.c = v;
+        return j == 0 ? p.v[0] : (j == 1 ? p.v[1] : (j == 2 ? p.v[2] : (j == 3 ? p.v[3] : p.v[4 % Q])));
+}
+template <int Q>
+__device__ __forceinline__ void set_comp(Part<Q> &p, int j, float v)
+{
+    static_assert(Q >= 1 && Q <= 5, "partials hold 1 to 5 scalars");
+    if (j == 0)
+        p.v[0] = v;
+    else if (j == 1)
+        p.v[1 % Q] = v;
+    else if (Q <= 3 || j == 2)
+        p.v[2 % Q] = v;
+    else if (j == 3)
+        p.v[3 % Q] = v;
+    else
+        p.v[4 % Q] = v;
+}
+
+// Output storage type and bytes per output vector for input vectors of VB bytes.
+template <OpKind OP, class T>
+using OutT = typename OpTraits<OP>::template Out<T>;
+template <OpKind OP, class T, int VB>
+constexpr int out_vb()
+{
+    return VB / StorageTraits<T>::kBytes * StorageTraits<OutT<OP, T>>::kBytes;
+}
+
+// Parameter vectors the output function reads on a held row (none when the
+// parameters were folded into the tile before the reduction).
+template <OpKind OP>
+constexpr int out_params()
+{
+    return OpTraits<OP>::kParamsInReduce ? 0 : OpTraits<OP>::kParams;
 }
 
 // Number of k in [0, IT) with pos + k*G < n (a prefix).
@@ -77,42 +106,48 @@ __device__ __forceinline__ int count_valid(int64_t n, int pos)
     return c < IT ? static_cast<int>(c) : IT;
 }
 
-template <class T, int VB, int IT, int G>
-__device__ __forceinline__ void load_tile(Tile<T, VB, IT> &t, rsrc_t src, int pos)
+// The row inputs of one owner: x, and dy for the backward operators; all of
+// them cover the same columns.
+template <int NI>
+struct Srcs {
+    rsrc_t r[NI];
+};
+
+template <class T, int VB, int IT, int G, int NI>
+__device__ __forceinline__ void load_tile(Tile<T, VB, IT> (&t)[NI], const Srcs<NI> &src, int pos)
 {
 #pragma unroll
-    for (int k = 0; k < IT; ++k)
-        t.v[k] = buf_load<VB, kStream>(src, static_cast<uint32_t>(pos + k * G) * VB);
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int k = 0; k < IT; ++k)
+            t[i].v[k] = buf_load<VB, kStream>(src.r[i], static_cast<uint32_t>(pos + k * G) * VB);
 }
 
-// The wave partial of a held tile.  (A second, unmasked copy for full waves
-// behind a wave-uniform branch was measured to raise register use by a third
-// with no gain: the masks are register selects.)
-template <OpKind OP, class T, int VB, int IT>
-__device__ __forceinline__ Partial tile_partial(Tile<T, VB, IT> &t, int kv)
-{
-    return OpTraits<OP>::template wave_partial<T, VB, IT>(t, kv);
-}
-
-// h for one vector: `in` is the held (or reread) input vector, g and b the
+// h for one vector: in[i] are the held (or reread) input vectors, g and b the
 // parameter vectors of the same columns.
 template <OpKind OP, class T, int VB, bool STREAM>
-__device__ __forceinline__ RawVec<VB> apply_vec(const RawVec<VB> &in, const RawVec<VB> &g, const RawVec<VB> &b,
-                                                const Coef &c)
+__device__ __forceinline__ RawVec<out_vb<OP, T, VB>()> apply_vec(const RawVec<VB> (&in)[OpTraits<OP>::kIn],
+                                                                 const RawVec<VB> &g, const RawVec<VB> &b,
+                                                                 const Coef &c)
 {
     using Op = OpTraits<OP>;
     constexpr int E = VB / StorageTraits<T>::kBytes;
+    constexpr int NP = STREAM ? Op::kParams : out_params<OP>();
     float out[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-        const float gv = Op::kParams >= 1 ? elem<T, VB>(g, e) : 1.0f;
-        const float bv = Op::kParams >= 2 ? elem<T, VB>(b, e) : 0.0f;
+        const float gv = NP >= 1 ? elem<T, VB>(g, e) : 1.0f;
+        const float bv = NP >= 2 ? elem<T, VB>(b, e) : 0.0f;
+        float xin[Op::kIn];
+#pragma unroll
+        for (int i = 0; i < Op::kIn; ++i)
+            xin[i] = elem<T, VB>(in[i], e);
         if constexpr (STREAM)
-            out[e] = Op::template apply_stream<T>(elem<T, VB>(in, e), c, gv, bv);
+            out[e] = Op::template apply_stream<T>(xin, c, gv, bv);
         else
-            out[e] = Op::template apply<T>(elem<T, VB>(in, e), c, gv, bv);
+            out[e] = Op::template apply<T>(xin, c, gv, bv);
     }
-    return pack<T, VB, E>(out);
+    return pack<OutT<OP, T>, out_vb<OP, T, VB>(), E>(out);
 }
 
 // Parameter vectors fetched per group of the output loop when they are
@@ -123,6 +158,7 @@ constexpr int param_group()
 {
     return IT * VB / 4 >= 64 ? (NP >= 2 ? 1 : (IT < 2 ? IT : 2)) : (IT < 4 ? IT : 4);
 }
+
 
 // ---------------------------------------------------------------------------
 // Parameter vectors (gamma, beta) of the columns a thread holds.  They are the
@@ -151,14 +187,16 @@ template <OpKind OP, int VB, int IT, int G, int OWNER>
 constexpr int param_mode()
 {
     constexpr int np = OpTraits<OP>::kParams;
-    // tile + parameter VGPRs allowed: 64, but 32 for LayerNorm at 1024
-    // threads, whose 128-VGPR cap leaves less room beside its statistics
-    constexpr int reg_budget = (G >= 1024 && np >= 2) ? 32 : 64;
+    constexpr int ni = OpTraits<OP>::kIn;
+    // tile + parameter VGPRs allowed: 64, but 32 for two parameter vectors or
+    // two inputs at 1024 threads, whose 128-VGPR cap leaves less room beside
+    // the statistics
+    constexpr int reg_budget = (G >= 1024 && (np >= 2 || ni >= 2)) ? 32 : 64;
     if (np == 0)
         return kParamNone;
     if (OWNER == kOwnerRow)
         return kParamDirect;
-    if (OWNER == kOwnerSlice && (np + 1) * IT * VB / 4 <= reg_budget)
+    if (OWNER == kOwnerSlice && (np + ni) * IT * VB / 4 <= reg_budget)
         return kParamReg;
     if (np * G * IT * VB <= 64 * 1024)
         return kParamLds;
@@ -221,7 +259,41 @@ struct ParamCache {
                 bk = lds[W * IT + pos + k * kWave];
         }
     }
+
+    // As get(), and in kParamDirect mode a load from L2 (used where the
+    // parameters enter the reduction).
+    __device__ __forceinline__ void fetch(int k, int pos, RawVec<VB> &gk, RawVec<VB> &bk) const
+    {
+        if constexpr (kMode == kParamDirect) {
+            const uint32_t off = static_cast<uint32_t>(pos + k * kWave) * VB;
+            gk = buf_load<VB, kKeep>(gam, off);
+            if constexpr (kNp >= 2)
+                bk = buf_load<VB, kKeep>(bet, off);
+        } else {
+            get(k, pos, gk, bk);
+        }
+    }
 };
+
+// The wave partial of a held tile, after folding the parameters into it when
+// the operator reduces over them.  (A second, unmasked copy for full waves
+// behind a wave-uniform branch was measured to raise register use by a third
+// with no gain: the masks are register selects.)
+template <OpKind OP, class T, int VB, int IT, int W, int OWNER>
+__device__ __forceinline__ typename OpTraits<OP>::Partial tile_partial(
+    Tile<T, VB, IT> (&t)[OpTraits<OP>::kIn], int kv, const ParamCache<OP, T, VB, IT, W, OWNER> &pc, int pos)
+{
+    using Op = OpTraits<OP>;
+    if constexpr (Op::kParamsInReduce) {
+#pragma unroll
+        for (int k = 0; k < IT; ++k) {
+            RawVec<VB> g, b;
+            pc.fetch(k, pos, g, b);
+            Op::template prepare<T, VB, IT>(t, k, g);
+        }
+    }
+    return Op::template wave_partial<T, VB, IT>(t, kv);
+}
 
 // Whether the output loop loads the next row into the registers it frees
 // ("rolling"), for owners that loop over rows.  Measured on MI355X it did not
@@ -242,46 +314,71 @@ constexpr bool rolls()
 // none: its loads return zero without touching memory) is loaded into the
 // register that vector k of this row leaves free.
 template <OpKind OP, class T, int VB, int IT, int W, int OWNER>
-__device__ __forceinline__ void store_tile(Tile<T, VB, IT> &t, rsrc_t dst,
+__device__ __forceinline__ void store_tile(Tile<T, VB, IT> (&t)[OpTraits<OP>::kIn], rsrc_t dst,
                                            const ParamCache<OP, T, VB, IT, W, OWNER> &pc, int pos, const Coef &c,
-                                           rsrc_t next)
+                                           const Srcs<OpTraits<OP>::kIn> &next)
 {
     using Op = OpTraits<OP>;
+    constexpr int NI = Op::kIn;
+    constexpr int NP = out_params<OP>();
     constexpr int MODE = ParamCache<OP, T, VB, IT, W, OWNER>::kMode;
+    constexpr int VBO = out_vb<OP, T, VB>();
     constexpr int G = kWave;  // vector stride between a thread's vectors
-    fence_tile(t);
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+        fence_tile(t[i]);
     // recompute the offsets here (one add each) instead of keeping the load
     // phase's offset registers alive across the reduction
     uint32_t base = static_cast<uint32_t>(pos) * VB;
     asm volatile("" : "+v"(base));
     (void)next;
-    if constexpr (MODE != kParamDirect) {
+    // output offsets: the input offsets when input and output vectors have
+    // the same size, else their own
+    uint32_t obase = base;
+    if constexpr (VBO != VB) {
+        obase = static_cast<uint32_t>(pos) * VBO;
+        asm volatile("" : "+v"(obase));
+    }
+    if constexpr (MODE != kParamDirect || NP == 0) {
 #pragma unroll
         for (int k = 0; k < IT; ++k) {
             const uint32_t off = base + static_cast<uint32_t>(k * G * VB);
+            const uint32_t ooff = VBO == VB ? off : obase + static_cast<uint32_t>(k * G * VBO);
             RawVec<VB> g, b;
-            pc.get(k, pos, g, b);
-            buf_store<VB, kStreamStore>(apply_vec<OP, T, VB, false>(t.v[k], g, b, c), dst, off);
+            if constexpr (NP > 0)
+                pc.get(k, pos, g, b);
+            RawVec<VB> in[NI];
+#pragma unroll
+            for (int i = 0; i < NI; ++i)
+                in[i] = t[i].v[k];
+            buf_store<VBO, kStreamStore>(apply_vec<OP, T, VB, false>(in, g, b, c), dst, ooff);
             if constexpr (rolls<MODE>())
-                t.v[k] = buf_load<VB, kStream>(next, off);
+#pragma unroll
+                for (int i = 0; i < NI; ++i)
+                    t[i].v[k] = buf_load<VB, kStream>(next.r[i], off);
         }
     } else {
-        constexpr int GP = param_group<IT, VB, Op::kParams>();
+        constexpr int GP = param_group<IT, VB, NP>();
 #pragma unroll
         for (int kb = 0; kb < IT; kb += GP) {
             RawVec<VB> g[GP], b[GP];
 #pragma unroll
             for (int j = 0; j < GP; ++j) {
                 const uint32_t off = base + static_cast<uint32_t>((kb + j) * G * VB);
-                if constexpr (Op::kParams >= 1)
+                if constexpr (NP >= 1)
                     g[j] = buf_load<VB, kKeep>(pc.gam, off);
-                if constexpr (Op::kParams >= 2)
+                if constexpr (NP >= 2)
                     b[j] = buf_load<VB, kKeep>(pc.bet, off);
             }
 #pragma unroll
             for (int j = 0; j < GP; ++j) {
                 const uint32_t off = base + static_cast<uint32_t>((kb + j) * G * VB);
-                buf_store<VB, kStreamStore>(apply_vec<OP, T, VB, false>(t.v[kb + j], g[j], b[j], c), dst, off);
+                const uint32_t ooff = VBO == VB ? off : obase + static_cast<uint32_t>((kb + j) * G * VBO);
+                RawVec<VB> in[NI];
+#pragma unroll
+                for (int i = 0; i < NI; ++i)
+                    in[i] = t[i].v[kb + j];
+                buf_store<VBO, kStreamStore>(apply_vec<OP, T, VB, false>(in, g[j], b[j], c), dst, ooff);
             }
         }
     }
@@ -289,7 +386,8 @@ __device__ __forceinline__ void store_tile(Tile<T, VB, IT> &t, rsrc_t dst,
 
 // After store_tile: load the next row unless store_tile already did.
 template <OpKind OP, class T, int VB, int IT, int W, int OWNER>
-__device__ __forceinline__ void load_next(Tile<T, VB, IT> &t, rsrc_t next, int pos)
+__device__ __forceinline__ void load_next(Tile<T, VB, IT> (&t)[OpTraits<OP>::kIn],
+                                          const Srcs<OpTraits<OP>::kIn> &next, int pos)
 {
     if constexpr (!rolls<ParamCache<OP, T, VB, IT, W, OWNER>::kMode>())
         load_tile<T, VB, IT, kWave>(t, next, pos);
@@ -299,8 +397,10 @@ __device__ __forceinline__ void load_next(Tile<T, VB, IT> &t, rsrc_t next, int p
 // the same workgroup partial (fixed order w = 0..NW-1).  The caller must not
 // rewrite `sh` before every thread has passed a later barrier.
 template <OpKind OP, int NW>
-__device__ __forceinline__ Partial block_combine(const Partial &wp, Partial *sh)
+__device__ __forceinline__ typename OpTraits<OP>::Partial block_combine(const typename OpTraits<OP>::Partial &wp,
+                                                                        typename OpTraits<OP>::Partial *sh)
 {
+    using Partial = typename OpTraits<OP>::Partial;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     if (lane == 0)
@@ -323,6 +423,32 @@ __device__ __forceinline__ rsrc_t span(const void *base, int64_t first, int64_t 
     return make_rsrc(reinterpret_cast<const void *>(p), static_cast<uint32_t>(nvec * VB));
 }
 
+// The row inputs (x, and dy for two-input operators): `nvec` vectors from
+// vector `first` of row `row` (nv vectors per row).
+template <OpKind OP, int VB>
+__device__ __forceinline__ Srcs<OpTraits<OP>::kIn> row_srcs(const RowArgs &a, int64_t row, int64_t nv,
+                                                            int64_t first, int64_t nvec)
+{
+    Srcs<OpTraits<OP>::kIn> s;
+    s.r[0] = span<VB>(a.x, row * nv + first, nvec);
+    if constexpr (OpTraits<OP>::kIn >= 2)
+        s.r[1] = span<VB>(a.dy, row * nv + first, nvec);
+    return s;
+}
+
+// The per-row output (quantization scale) of `row`, written by one lane.
+template <OpKind OP>
+__device__ __forceinline__ void store_row_value(const RowArgs &a, int64_t row, const Coef &c, bool writer)
+{
+    if constexpr (OpTraits<OP>::kRowOut) {
+        if (writer) {
+            RawVec<4> v;
+            v.w = __float_as_uint(OpTraits<OP>::row_value(c));
+            buf_store<4, kStreamStore>(v, span<4>(a.row_out, row, 1), 0u);
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Path 1a: one wavefront per row, four waves per 256-thread workgroup; wave w
 // of the grid handles rows w, w + W, w + 2W, ... (W waves in the grid).  No
@@ -334,13 +460,14 @@ __global__ __launch_bounds__(kWave *kWaveRowsPerWg) void single_wave_kernel(RowA
     using Op = OpTraits<OP>;
     using PC = ParamCache<OP, T, VB, IT, kWave, kOwnerWaves>;
     constexpr int E = VB / StorageTraits<T>::kBytes;
+    constexpr int VBO = out_vb<OP, T, VB>();
     __shared__ RawVec<VB> lds_params[param_lds_vectors<OP, VB, IT, kWave, kOwnerWaves>()];
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t nv = a.cols / E;
     const int64_t waves = static_cast<int64_t>(gridDim.x) * kWaveRowsPerWg;
     int64_t row = uniform(static_cast<int64_t>(blockIdx.x) * kWaveRowsPerWg + threadIdx.x / kWave);
-    Tile<T, VB, IT> t;
-    load_tile<T, VB, IT, kWave>(t, span<VB>(a.x, row * nv, row < a.rows ? nv : 0), lane);
+    Tile<T, VB, IT> t[Op::kIn];
+    load_tile<T, VB, IT, kWave>(t, row_srcs<OP, VB>(a, row, nv, 0, row < a.rows ? nv : 0), lane);
     PC pc;
     pc.init(span<VB>(a.gamma, 0, nv), span<VB>(a.beta, 0, nv), lane, lds_params, threadIdx.x,
             kWave * kWaveRowsPerWg);
@@ -349,10 +476,11 @@ __global__ __launch_bounds__(kWave *kWaveRowsPerWg) void single_wave_kernel(RowA
     const int kv = count_valid<IT, kWave>(nv, lane);
     for (; row < a.rows; row += waves) {
         const int64_t next = row + waves;
-        const Partial wp = tile_partial<OP, T, VB, IT>(t, kv);
+        const auto wp = tile_partial<OP, T, VB, IT, kWave, kOwnerWaves>(t, kv, pc, lane);
         const Coef c = Op::template finalize<T>(wp, wp, a.cols, a.eps);
-        const rsrc_t nsrc = span<VB>(a.x, next * nv, next < a.rows ? nv : 0);
-        store_tile<OP, T, VB, IT, kWave, kOwnerWaves>(t, span<VB>(a.y, row * nv, nv), pc, lane, c, nsrc);
+        store_row_value<OP>(a, row, c, lane == 0);
+        const auto nsrc = row_srcs<OP, VB>(a, next, nv, 0, next < a.rows ? nv : 0);
+        store_tile<OP, T, VB, IT, kWave, kOwnerWaves>(t, span<VBO>(a.y, row * nv, nv), pc, lane, c, nsrc);
         load_next<OP, T, VB, IT, kWave, kOwnerWaves>(t, nsrc, lane);
     }
 }
@@ -368,14 +496,15 @@ __global__ __launch_bounds__(BLOCK) void single_wg_kernel(RowArgs a)
     using PC = ParamCache<OP, T, VB, IT, BLOCK, kOwnerRow>;
     constexpr int E = VB / StorageTraits<T>::kBytes;
     constexpr int NW = BLOCK / kWave;
-    __shared__ Partial sh[NW];
+    constexpr int VBO = out_vb<OP, T, VB>();
+    __shared__ typename Op::Partial sh[NW];
     __shared__ RawVec<VB> lds_params[param_lds_vectors<OP, VB, IT, BLOCK, kOwnerRow>()];
     const int tid = threadIdx.x;
     const int pos = (tid / kWave) * kWave * IT + (tid & (kWave - 1));  // this wave's run + lane
     const int64_t nv = a.cols / E;
     int64_t row = blockIdx.x;
-    Tile<T, VB, IT> t;
-    load_tile<T, VB, IT, kWave>(t, span<VB>(a.x, row * nv, nv), pos);
+    Tile<T, VB, IT> t[Op::kIn];
+    load_tile<T, VB, IT, kWave>(t, row_srcs<OP, VB>(a, row, nv, 0, nv), pos);
     PC pc;
     pc.init(span<VB>(a.gamma, 0, nv), span<VB>(a.beta, 0, nv), pos, lds_params, tid, BLOCK);
     if constexpr (PC::kMode == kParamLds)
@@ -383,11 +512,12 @@ __global__ __launch_bounds__(BLOCK) void single_wg_kernel(RowArgs a)
     const int kv = count_valid<IT, kWave>(nv, pos);
     for (; row < a.rows; row += gridDim.x) {
         const int64_t next = row + gridDim.x;
-        const Partial wp = tile_partial<OP, T, VB, IT>(t, kv);
-        const Partial rp = block_combine<OP, NW>(wp, sh);
+        const auto wp = tile_partial<OP, T, VB, IT, BLOCK, kOwnerRow>(t, kv, pc, pos);
+        const auto rp = block_combine<OP, NW>(wp, sh);
         const Coef c = Op::template finalize<T>(rp, wp, a.cols, a.eps);
-        const rsrc_t nsrc = span<VB>(a.x, next * nv, next < a.rows ? nv : 0);
-        store_tile<OP, T, VB, IT, BLOCK, kOwnerRow>(t, span<VB>(a.y, row * nv, nv), pc, pos, c, nsrc);
+        store_row_value<OP>(a, row, c, tid == 0);
+        const auto nsrc = row_srcs<OP, VB>(a, next, nv, 0, next < a.rows ? nv : 0);
+        store_tile<OP, T, VB, IT, BLOCK, kOwnerRow>(t, span<VBO>(a.y, row * nv, nv), pc, pos, c, nsrc);
         load_next<OP, T, VB, IT, BLOCK, kOwnerRow>(t, nsrc, pos);
         // the next block_combine rewrites sh: every wave must have read it
         __syncthreads();
@@ -403,10 +533,12 @@ template <OpKind OP, class T, int VB, int BLOCK, int IT, bool CONTROL>
 __global__ __launch_bounds__(BLOCK) void split_kernel(SplitArgs a)
 {
     using Op = OpTraits<OP>;
+    using Partial = typename Op::Partial;
     using PC = ParamCache<OP, T, VB, IT, BLOCK, kOwnerSlice>;
     constexpr int E = VB / StorageTraits<T>::kBytes;
     constexpr int NW = BLOCK / kWave;
     constexpr int Q = Op::kQ;
+    constexpr int VBO = out_vb<OP, T, VB>();
     __shared__ Partial sh[NW];
     __shared__ Partial peer[kMaxSplit];
     __shared__ uint32_t sh_ticket;
@@ -433,8 +565,8 @@ __global__ __launch_bounds__(BLOCK) void split_kernel(SplitArgs a)
     // CONTROL: a zero-length source, so every load returns zero without
     // touching memory, and a zero-length destination that drops every store
     const int64_t nload = CONTROL ? 0 : ns;
-    Tile<T, VB, IT> t;
-    load_tile<T, VB, IT, kWave>(t, span<VB>(a.r.x, k * nv + v0, k < a.r.rows ? nload : 0), pos);
+    Tile<T, VB, IT> t[Op::kIn];
+    load_tile<T, VB, IT, kWave>(t, row_srcs<OP, VB>(a.r, k, nv, v0, k < a.r.rows ? nload : 0), pos);
     PC pc;
     pc.init(span<VB>(a.r.gamma, v0, ns), span<VB>(a.r.beta, v0, ns), pos, lds_params, tid, BLOCK);
     if constexpr (PC::kMode == kParamLds)
@@ -443,7 +575,7 @@ __global__ __launch_bounds__(BLOCK) void split_kernel(SplitArgs a)
     uint32_t it = 0;
     for (int64_t row = k; row < a.r.rows; row += a.clusters, ++it) {
         const int64_t next = row + a.clusters;
-        const Partial wp = tile_partial<OP, T, VB, IT>(t, kv);
+        const Partial wp = tile_partial<OP, T, VB, IT, BLOCK, kOwnerSlice>(t, kv, pc, pos);
         const Partial sp = block_combine<OP, NW>(wp, sh);
 
         // publish this slice's partial, then gather all P partials of the row
@@ -471,8 +603,10 @@ __global__ __launch_bounds__(BLOCK) void split_kernel(SplitArgs a)
             parts[i] = peer[i];
         const Partial rp = Op::template merge<kMaxSplit>(parts, P);
         const Coef cf = Op::template finalize<T>(rp, wp, a.r.cols, a.r.eps);
-        const rsrc_t nsrc = span<VB>(a.r.x, next * nv + v0, next < a.r.rows ? nload : 0);
-        store_tile<OP, T, VB, IT, BLOCK, kOwnerSlice>(t, span<VB>(a.r.y, row * nv + v0, nload), pc, pos, cf, nsrc);
+        store_row_value<OP>(a.r, row, cf, !CONTROL && c == 0 && tid == 0);
+        const auto nsrc = row_srcs<OP, VB>(a.r, next, nv, v0, next < a.r.rows ? nload : 0);
+        store_tile<OP, T, VB, IT, BLOCK, kOwnerSlice>(t, span<VBO>(a.r.y, row * nv + v0, nload), pc, pos, cf,
+                                                      nsrc);
         load_next<OP, T, VB, IT, BLOCK, kOwnerSlice>(t, nsrc, pos);
         // (no barrier needed before the next iteration rewrites sh or peer:
         // every wave has read sh before the exchange barrier above and reads
@@ -489,9 +623,12 @@ template <OpKind OP, class T, int VB, int BLOCK, int U>
 __global__ __launch_bounds__(BLOCK) void reread_kernel(RowArgs a)
 {
     using Op = OpTraits<OP>;
+    using Partial = typename Op::Partial;
+    constexpr int NI = Op::kIn;
     constexpr int E = VB / StorageTraits<T>::kBytes;
     constexpr int NW = BLOCK / kWave;
     constexpr int GP = U < 4 ? U : 4;
+    constexpr int VBO = out_vb<OP, T, VB>();
     constexpr int64_t CH = static_cast<int64_t>(BLOCK) * U;
     __shared__ Partial sh[NW];
     const int tid = threadIdx.x;
@@ -500,26 +637,38 @@ __global__ __launch_bounds__(BLOCK) void reread_kernel(RowArgs a)
     Partial r = Op::stream_init();
     for (int64_t base = 0; base < nv; base += CH) {
         const int64_t n = min(CH, nv - base);
-        const rsrc_t src = span<VB>(a.x, row * nv + base, n);
-        RawVec<VB> v[U];
+        const auto src = row_srcs<OP, VB>(a, row, nv, base, n);
+        RawVec<VB> v[NI][U];
+        RawVec<VB> g[U];
 #pragma unroll
-        for (int k = 0; k < U; ++k)
-            v[k] = buf_load<VB, kKeep>(src, static_cast<uint32_t>(tid + k * BLOCK) * VB);
-        Op::template stream_update<T, VB, U>(r, v, count_valid<U, BLOCK>(n, tid));
+        for (int i = 0; i < NI; ++i)
+#pragma unroll
+            for (int k = 0; k < U; ++k)
+                v[i][k] = buf_load<VB, kKeep>(src.r[i], static_cast<uint32_t>(tid + k * BLOCK) * VB);
+        if constexpr (Op::kParamsInReduce) {
+            const rsrc_t gam = span<VB>(a.gamma, base, n);
+#pragma unroll
+            for (int k = 0; k < U; ++k)
+                g[k] = buf_load<VB, kKeep>(gam, static_cast<uint32_t>(tid + k * BLOCK) * VB);
+        }
+        Op::template stream_update<T, VB, U>(r, v, g, count_valid<U, BLOCK>(n, tid));
     }
     const Partial wp = Op::wave_from_thread(r);
     const Partial rp = block_combine<OP, NW>(wp, sh);
     const Coef c = Op::template finalize_stream<T>(rp, a.cols, a.eps);
+    store_row_value<OP>(a, row, c, tid == 0);
     for (int64_t base = 0; base < nv; base += CH) {
         const int64_t n = min(CH, nv - base);
-        const rsrc_t src = span<VB>(a.x, row * nv + base, n);
-        const rsrc_t dst = span<VB>(a.y, row * nv + base, n);
+        const auto src = row_srcs<OP, VB>(a, row, nv, base, n);
+        const rsrc_t dst = span<VBO>(a.y, row * nv + base, n);
         const rsrc_t gam = span<VB>(a.gamma, base, n);
         const rsrc_t bet = span<VB>(a.beta, base, n);
-        RawVec<VB> v[U];
+        RawVec<VB> v[U][NI];
 #pragma unroll
-        for (int k = 0; k < U; ++k)
-            v[k] = buf_load<VB, kStream>(src, static_cast<uint32_t>(tid + k * BLOCK) * VB);
+        for (int i = 0; i < NI; ++i)
+#pragma unroll
+            for (int k = 0; k < U; ++k)
+                v[k][i] = buf_load<VB, kStream>(src.r[i], static_cast<uint32_t>(tid + k * BLOCK) * VB);
 #pragma unroll
         for (int kb = 0; kb < U; kb += GP) {
             RawVec<VB> g[GP], b[GP];
@@ -533,8 +682,8 @@ __global__ __launch_bounds__(BLOCK) void reread_kernel(RowArgs a)
             }
 #pragma unroll
             for (int j = 0; j < GP; ++j) {
-                const uint32_t off = static_cast<uint32_t>(tid + (kb + j) * BLOCK) * VB;
-                buf_store<VB, kStreamStore>(apply_vec<OP, T, VB, true>(v[kb + j], g[j], b[j], c), dst, off);
+                const uint32_t ooff = static_cast<uint32_t>(tid + (kb + j) * BLOCK) * VBO;
+                buf_store<VBO, kStreamStore>(apply_vec<OP, T, VB, true>(v[kb + j], g[j], b[j], c), dst, ooff);
             }
         }
     }

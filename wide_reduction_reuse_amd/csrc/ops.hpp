@@ -1,4 +1,4 @@
-// The three reduction-reuse operators as (statistic, merge, output) triples.
+// The reduction-reuse operators as (statistic, merge, output) triples.
 //
 // CREDIT paper, Sec. III-B, Eq. 1: per-row statistics r are reduced from
 // per-element contributions, then an elementwise h(x_i, r) writes the output.
@@ -16,23 +16,48 @@
 //             two stages (mean, then variance) collapse into one partial and
 //             are combined by the Chan-Golub-LeVeque pairwise rule.
 //   RMSNorm   (ss): sum of squares; combined by addition.
+// and for three further workloads of the paper's evaluation (Sec. IV-A):
+//   softmax-logits backward (m, s, u): u = sum dy exp(x - m) rides along with
+//             the softmax pair and is rescaled with s; dx = p (dy - u/s).
+//   LayerNorm backward (n, mean, M2, a, b): with g = gamma dy, a = sum g and
+//             b = sum g (x - mean) around the partial's own mean; b is
+//             re-centred on the merged mean, b + a (mean_part - mean).
+//   int8 quantization (amax): max |x|; combined by max.
+//
+// Interface of OpTraits<OP> (what the kernels call):
+//   kQ       scalars per partial (exchanged between split workgroups)
+//   kIn      row inputs held per element: 1 (x) or 2 (x, dy)
+//   kParams  per-column parameter vectors (gamma, beta)
+//   kParamsInReduce  the parameters enter the statistics (LayerNorm backward)
+//            rather than only the output; `prepare` folds them into the
+//            held tile before the reduction
+//   kRowOut  one fp32 per row is written besides the row (quantization scale)
+//   Out<T>   storage type of the output row
+//   wave_partial, merge, finalize, apply            held rows (paths 1, 2)
+//   stream_init, stream_update, wave_from_thread,
+//   finalize_stream, apply_stream                   streamed rows (path 3)
 #pragma once
+
+#include <float.h>
 
 #include "common.hpp"
 
 namespace credit {
 
-enum OpKind { kSoftmax = 0, kLayerNorm = 1, kRmsNorm = 2 };
+enum OpKind { kSoftmax = 0, kLayerNorm = 1, kRmsNorm = 2, kSoftmaxBwd = 3, kLayerNormBwd = 4, kQuantInt8 = 5 };
 
-struct Partial {
-    float a, b, c;  // softmax: (m, s, -); LN: (n, mean, M2); RMS: (ss, -, -)
+// A partial of Q scalars.  The storage holds at least three (the unused ones
+// stay zero and are never exchanged): with a one-scalar partial the compiler
+// allocated up to 10 more VGPRs in the split kernel than with three.
+template <int Q>
+struct Part {
+    float v[Q < 3 ? 3 : Q];
 };
 
-// Coefficients of the output function h, identical in every thread of a row.
+// Coefficients of the output function h, identical in every thread of a row;
+// their meaning is given per operator.
 struct Coef {
-    float mean;   // LN: row mean
-    float scale;  // softmax: 1/s (bf16) or e^(m_wave - m)/s (fp32); LN/RMS: 1/sqrt(var + eps)
-    float m;      // softmax: row max
+    float k[4];
 };
 
 // A register tile: IT vectors of VB bytes per thread.  Vector k of a thread at
@@ -56,23 +81,47 @@ __device__ __forceinline__ void fence_tile(Tile<T, VB, IT> &t)
         asm volatile("" : "+v"(t.v[k].w));
 }
 
+template <class T>
+constexpr bool is_f32()
+{
+    return StorageTraits<T>::kBytes == 4;
+}
+
 template <OpKind OP>
 struct OpTraits;
 
+// Softmax exponential for the storage type: ~2 ulp for fp32 outputs, the bare
+// hardware exp2 where the result is rounded to bf16.
+template <class T>
+__device__ __forceinline__ float exp_for(float d)
+{
+    if constexpr (is_f32<T>())
+        return exp_acc(d);
+    else
+        return exp_fast(d);
+}
+
 // ---------------------------------------------------------------------------
-// softmax
+// softmax.  Coef: k0 = output scale (fp32: e^(m_wave - m) / s, because the
+// tile holds e^(x - m_wave); bf16: 1 / s), k1 = row max m.
 // ---------------------------------------------------------------------------
 template <>
 struct OpTraits<kSoftmax> {
-    static constexpr int kQ = 2;      // scalars exchanged per partial
-    static constexpr int kParams = 0; // parameter vectors
+    static constexpr int kQ = 2;
+    static constexpr int kIn = 1;
+    static constexpr int kParams = 0;
+    static constexpr bool kParamsInReduce = false;
+    static constexpr bool kRowOut = false;
+    template <class T> using Out = T;
+    using Partial = Part<kQ>;
 
     // Wave partial over the wave's elements.  For fp32 storage the tile is
     // overwritten with e_i = exp(x_i - m_wave) so that the output needs no
     // second exponential.
     template <class T, int VB, int IT>
-    __device__ __forceinline__ static Partial wave_partial(Tile<T, VB, IT> &t, int kvalid)
+    __device__ __forceinline__ static Partial wave_partial(Tile<T, VB, IT> (&tt)[kIn], int kvalid)
     {
+        Tile<T, VB, IT> &t = tt[0];
         constexpr int E = Tile<T, VB, IT>::kEpv;
         float mt = -INFINITY;
 #pragma unroll
@@ -84,7 +133,7 @@ struct OpTraits<kSoftmax> {
         const float mw = wave_max(mt);
         fence_tile(t);
         float st = 0.0f;
-        if constexpr (StorageTraits<T>::kBytes == 4) {
+        if constexpr (is_f32<T>()) {
 #pragma unroll
             for (int k = 0; k < IT; ++k)
                 if (k < kvalid)
@@ -102,7 +151,7 @@ struct OpTraits<kSoftmax> {
                     for (int e = 0; e < E; ++e)
                         st += exp_fast(elem<T, VB>(t.v[k], e) - mw);
         }
-        return Partial{mw, wave_sum(st), 0.0f};
+        return Partial{{mw, wave_sum(st)}};
     }
 
     // Combine partials p[0..n-1] (n <= N) in index order.
@@ -113,49 +162,41 @@ struct OpTraits<kSoftmax> {
 #pragma unroll
         for (int i = 0; i < N; ++i)
             if (i < n)
-                m = fmaxf(m, p[i].a);
+                m = fmaxf(m, p[i].v[0]);
         float s = 0.0f;
 #pragma unroll
         for (int i = 0; i < N; ++i)
-            if (i < n && p[i].b != 0.0f)
-                s += p[i].b * exp_acc(p[i].a - m);
-        return Partial{m, s, 0.0f};
+            if (i < n && p[i].v[1] != 0.0f)
+                s += p[i].v[1] * exp_acc(p[i].v[0] - m);
+        return Partial{{m, s}};
     }
 
     // `own` is the partial whose exponentials are stored in this thread's tile.
     template <class T>
     __device__ __forceinline__ static Coef finalize(const Partial &row, const Partial &own, int64_t, float)
     {
-        const float inv_s = 1.0f / row.b;
-        if constexpr (StorageTraits<T>::kBytes == 4)
-            return Coef{0.0f, own.b != 0.0f ? exp_acc(own.a - row.a) * inv_s : 0.0f, row.a};
+        const float inv_s = 1.0f / row.v[1];
+        if constexpr (is_f32<T>())
+            return Coef{{own.v[1] != 0.0f ? exp_acc(own.v[0] - row.v[0]) * inv_s : 0.0f, row.v[0], 0.0f, 0.0f}};
         else
-            return Coef{0.0f, inv_s, row.a};
+            return Coef{{inv_s, row.v[0], 0.0f, 0.0f}};
     }
 
     template <class T>
-    __device__ __forceinline__ static float apply(float x, const Coef &c, float, float)
+    __device__ __forceinline__ static float apply(const float (&in)[kIn], const Coef &c, float, float)
     {
-        if constexpr (StorageTraits<T>::kBytes == 4)
-            return x * c.scale;  // x already holds exp(x - m_wave)
+        if constexpr (is_f32<T>())
+            return in[0] * c.k[0];  // in[0] already holds exp(x - m_wave)
         else
-            return exp_fast(x - c.m) * c.scale;
+            return exp_fast(in[0] - c.k[1]) * c.k[0];
     }
 
     // ---- streaming form (the reread path): the row is not held, so each
     // thread keeps a running partial over the chunks it streams, and the
     // output pass recomputes the exponential from the reread input.
-    template <class T>
-    __device__ __forceinline__ static float expf_t(float d)
-    {
-        if constexpr (StorageTraits<T>::kBytes == 4)
-            return exp_acc(d);
-        else
-            return exp_fast(d);
-    }
-
     template <class T, int VB, int U>
-    __device__ __forceinline__ static void stream_update(Partial &r, const RawVec<VB> (&v)[U], int kvalid)
+    __device__ __forceinline__ static void stream_update(Partial &r, const RawVec<VB> (&v)[kIn][U],
+                                                         const RawVec<VB> (&)[U], int kvalid)
     {
         constexpr int E = VB / StorageTraits<T>::kBytes;
         float cm = -INFINITY;
@@ -164,10 +205,10 @@ struct OpTraits<kSoftmax> {
             if (k < kvalid)
 #pragma unroll
                 for (int e = 0; e < E; ++e)
-                    cm = fmaxf(cm, elem<T, VB>(v[k], e));
-        if (cm > r.a) {
-            r.b = r.b != 0.0f ? r.b * exp_acc(r.a - cm) : 0.0f;
-            r.a = cm;
+                    cm = fmaxf(cm, elem<T, VB>(v[0][k], e));
+        if (cm > r.v[0]) {
+            r.v[1] = r.v[1] != 0.0f ? r.v[1] * exp_acc(r.v[0] - cm) : 0.0f;
+            r.v[0] = cm;
         }
         float s = 0.0f;
 #pragma unroll
@@ -175,43 +216,49 @@ struct OpTraits<kSoftmax> {
             if (k < kvalid)
 #pragma unroll
                 for (int e = 0; e < E; ++e)
-                    s += expf_t<T>(elem<T, VB>(v[k], e) - r.a);
-        r.b += s;
+                    s += exp_for<T>(elem<T, VB>(v[0][k], e) - r.v[0]);
+        r.v[1] += s;
     }
 
-    __device__ __forceinline__ static Partial stream_init() { return Partial{-INFINITY, 0.0f, 0.0f}; }
+    __device__ __forceinline__ static Partial stream_init() { return Partial{{-INFINITY, 0.0f}}; }
 
     __device__ __forceinline__ static Partial wave_from_thread(const Partial &r)
     {
-        const float mw = wave_max(r.a);
-        const float s = r.b != 0.0f ? r.b * exp_acc(r.a - mw) : 0.0f;
-        return Partial{mw, wave_sum(s), 0.0f};
+        const float mw = wave_max(r.v[0]);
+        const float s = r.v[1] != 0.0f ? r.v[1] * exp_acc(r.v[0] - mw) : 0.0f;
+        return Partial{{mw, wave_sum(s)}};
     }
 
     template <class T>
     __device__ __forceinline__ static Coef finalize_stream(const Partial &row, int64_t, float)
     {
-        return Coef{0.0f, 1.0f / row.b, row.a};
+        return Coef{{1.0f / row.v[1], row.v[0], 0.0f, 0.0f}};
     }
 
     template <class T>
-    __device__ __forceinline__ static float apply_stream(float x, const Coef &c, float, float)
+    __device__ __forceinline__ static float apply_stream(const float (&in)[kIn], const Coef &c, float, float)
     {
-        return expf_t<T>(x - c.m) * c.scale;
+        return exp_for<T>(in[0] - c.k[1]) * c.k[0];
     }
 };
 
 // ---------------------------------------------------------------------------
-// LayerNorm
+// LayerNorm.  Coef: k0 = mean, k1 = 1/sqrt(var + eps).
 // ---------------------------------------------------------------------------
 template <>
 struct OpTraits<kLayerNorm> {
     static constexpr int kQ = 3;  // (n, mean, M2); n travels so empty slices merge correctly
+    static constexpr int kIn = 1;
     static constexpr int kParams = 2;
+    static constexpr bool kParamsInReduce = false;
+    static constexpr bool kRowOut = false;
+    template <class T> using Out = T;
+    using Partial = Part<kQ>;
 
     template <class T, int VB, int IT>
-    __device__ __forceinline__ static Partial wave_partial(Tile<T, VB, IT> &t, int kvalid)
+    __device__ __forceinline__ static Partial wave_partial(Tile<T, VB, IT> (&tt)[kIn], int kvalid)
     {
+        Tile<T, VB, IT> &t = tt[0];
         constexpr int E = Tile<T, VB, IT>::kEpv;
         float sum = 0.0f;
 #pragma unroll
@@ -233,7 +280,7 @@ struct OpTraits<kLayerNorm> {
                     float d = elem<T, VB>(t.v[k], e) - mean;
                     m2 = __builtin_fmaf(d, d, m2);
                 }
-        return Partial{nw, mean, wave_sum(m2)};
+        return Partial{{nw, mean, wave_sum(m2)}};
     }
 
     // mean = sum n_i mean_i / n;  M2 = sum (M2_i + n_i (mean_i - mean)^2).
@@ -244,37 +291,38 @@ struct OpTraits<kLayerNorm> {
 #pragma unroll
         for (int i = 0; i < N; ++i)
             if (i < n) {
-                nt += p[i].a;
-                acc = __builtin_fmaf(p[i].a, p[i].b, acc);
+                nt += p[i].v[0];
+                acc = __builtin_fmaf(p[i].v[0], p[i].v[1], acc);
             }
         const float mean = nt > 0.0f ? acc / nt : 0.0f;
         float m2 = 0.0f;
 #pragma unroll
         for (int i = 0; i < N; ++i)
             if (i < n) {
-                float d = p[i].b - mean;
-                m2 += p[i].c + p[i].a * d * d;
+                float d = p[i].v[1] - mean;
+                m2 += p[i].v[2] + p[i].v[0] * d * d;
             }
-        return Partial{nt, mean, m2};
+        return Partial{{nt, mean, m2}};
     }
 
     template <class T>
     __device__ __forceinline__ static Coef finalize(const Partial &row, const Partial &, int64_t cols, float eps)
     {
-        const float var = row.c / static_cast<float>(cols);
-        return Coef{row.b, 1.0f / sqrtf(var + eps), 0.0f};
+        const float var = row.v[2] / static_cast<float>(cols);
+        return Coef{{row.v[1], 1.0f / sqrtf(var + eps), 0.0f, 0.0f}};
     }
 
     template <class T>
-    __device__ __forceinline__ static float apply(float x, const Coef &c, float g, float b)
+    __device__ __forceinline__ static float apply(const float (&in)[kIn], const Coef &c, float g, float b)
     {
-        return __builtin_fmaf((x - c.mean) * c.scale, g, b);
+        return __builtin_fmaf((in[0] - c.k[0]) * c.k[1], g, b);
     }
 
     // ---- streaming form: each chunk is reduced two-pass in registers to
     // (n_c, mean_c, M2_c) and folded into the running partial pairwise.
     template <class T, int VB, int U>
-    __device__ __forceinline__ static void stream_update(Partial &r, const RawVec<VB> (&v)[U], int kvalid)
+    __device__ __forceinline__ static void stream_update(Partial &r, const RawVec<VB> (&v)[kIn][U],
+                                                         const RawVec<VB> (&)[U], int kvalid)
     {
         constexpr int E = VB / StorageTraits<T>::kBytes;
         if (kvalid <= 0)
@@ -285,7 +333,7 @@ struct OpTraits<kLayerNorm> {
             if (k < kvalid)
 #pragma unroll
                 for (int e = 0; e < E; ++e)
-                    sum += elem<T, VB>(v[k], e);
+                    sum += elem<T, VB>(v[0][k], e);
         const float nc = static_cast<float>(kvalid * E);
         const float mc = sum / nc;
         float m2c = 0.0f;
@@ -294,24 +342,24 @@ struct OpTraits<kLayerNorm> {
             if (k < kvalid)
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
-                    float d = elem<T, VB>(v[k], e) - mc;
+                    float d = elem<T, VB>(v[0][k], e) - mc;
                     m2c = __builtin_fmaf(d, d, m2c);
                 }
-        const float n2 = r.a + nc;
-        const float d = mc - r.b;
-        r.b = __builtin_fmaf(d, nc / n2, r.b);
-        r.c += m2c + d * d * (r.a * nc / n2);
-        r.a = n2;
+        const float n2 = r.v[0] + nc;
+        const float d = mc - r.v[1];
+        r.v[1] = __builtin_fmaf(d, nc / n2, r.v[1]);
+        r.v[2] += m2c + d * d * (r.v[0] * nc / n2);
+        r.v[0] = n2;
     }
 
-    __device__ __forceinline__ static Partial stream_init() { return Partial{0.0f, 0.0f, 0.0f}; }
+    __device__ __forceinline__ static Partial stream_init() { return Partial{{0.0f, 0.0f, 0.0f}}; }
 
     __device__ __forceinline__ static Partial wave_from_thread(const Partial &r)
     {
-        const float nw = wave_sum(r.a);
-        const float mean = nw > 0.0f ? wave_sum(r.a * r.b) / nw : 0.0f;
-        const float d = r.b - mean;
-        return Partial{nw, mean, wave_sum(r.c + r.a * d * d)};
+        const float nw = wave_sum(r.v[0]);
+        const float mean = nw > 0.0f ? wave_sum(r.v[0] * r.v[1]) / nw : 0.0f;
+        const float d = r.v[1] - mean;
+        return Partial{{nw, mean, wave_sum(r.v[2] + r.v[0] * d * d)}};
     }
 
     template <class T>
@@ -321,23 +369,29 @@ struct OpTraits<kLayerNorm> {
     }
 
     template <class T>
-    __device__ __forceinline__ static float apply_stream(float x, const Coef &c, float g, float b)
+    __device__ __forceinline__ static float apply_stream(const float (&in)[kIn], const Coef &c, float g, float b)
     {
-        return apply<T>(x, c, g, b);
+        return apply<T>(in, c, g, b);
     }
 };
 
 // ---------------------------------------------------------------------------
-// RMSNorm
+// RMSNorm.  Coef: k0 = 1/sqrt(mean(x^2) + eps).
 // ---------------------------------------------------------------------------
 template <>
 struct OpTraits<kRmsNorm> {
     static constexpr int kQ = 1;
+    static constexpr int kIn = 1;
     static constexpr int kParams = 1;
+    static constexpr bool kParamsInReduce = false;
+    static constexpr bool kRowOut = false;
+    template <class T> using Out = T;
+    using Partial = Part<kQ>;
 
     template <class T, int VB, int IT>
-    __device__ __forceinline__ static Partial wave_partial(Tile<T, VB, IT> &t, int kvalid)
+    __device__ __forceinline__ static Partial wave_partial(Tile<T, VB, IT> (&tt)[kIn], int kvalid)
     {
+        Tile<T, VB, IT> &t = tt[0];
         constexpr int E = Tile<T, VB, IT>::kEpv;
         float ss = 0.0f;
 #pragma unroll
@@ -348,7 +402,7 @@ struct OpTraits<kRmsNorm> {
                     float x = elem<T, VB>(t.v[k], e);
                     ss = __builtin_fmaf(x, x, ss);
                 }
-        return Partial{wave_sum(ss), 0.0f, 0.0f};
+        return Partial{{wave_sum(ss)}};
     }
 
     template <int N>
@@ -358,24 +412,25 @@ struct OpTraits<kRmsNorm> {
 #pragma unroll
         for (int i = 0; i < N; ++i)
             if (i < n)
-                ss += p[i].a;
-        return Partial{ss, 0.0f, 0.0f};
+                ss += p[i].v[0];
+        return Partial{{ss}};
     }
 
     template <class T>
     __device__ __forceinline__ static Coef finalize(const Partial &row, const Partial &, int64_t cols, float eps)
     {
-        return Coef{0.0f, 1.0f / sqrtf(row.a / static_cast<float>(cols) + eps), 0.0f};
+        return Coef{{1.0f / sqrtf(row.v[0] / static_cast<float>(cols) + eps), 0.0f, 0.0f, 0.0f}};
     }
 
     template <class T>
-    __device__ __forceinline__ static float apply(float x, const Coef &c, float g, float)
+    __device__ __forceinline__ static float apply(const float (&in)[kIn], const Coef &c, float g, float)
     {
-        return x * c.scale * g;
+        return in[0] * c.k[0] * g;
     }
 
     template <class T, int VB, int U>
-    __device__ __forceinline__ static void stream_update(Partial &r, const RawVec<VB> (&v)[U], int kvalid)
+    __device__ __forceinline__ static void stream_update(Partial &r, const RawVec<VB> (&v)[kIn][U],
+                                                         const RawVec<VB> (&)[U], int kvalid)
     {
         constexpr int E = VB / StorageTraits<T>::kBytes;
 #pragma unroll
@@ -383,16 +438,16 @@ struct OpTraits<kRmsNorm> {
             if (k < kvalid)
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
-                    float x = elem<T, VB>(v[k], e);
-                    r.a = __builtin_fmaf(x, x, r.a);
+                    float x = elem<T, VB>(v[0][k], e);
+                    r.v[0] = __builtin_fmaf(x, x, r.v[0]);
                 }
     }
 
-    __device__ __forceinline__ static Partial stream_init() { return Partial{0.0f, 0.0f, 0.0f}; }
+    __device__ __forceinline__ static Partial stream_init() { return Partial{{0.0f}}; }
 
     __device__ __forceinline__ static Partial wave_from_thread(const Partial &r)
     {
-        return Partial{wave_sum(r.a), 0.0f, 0.0f};
+        return Partial{{wave_sum(r.v[0])}};
     }
 
     template <class T>
@@ -402,9 +457,401 @@ struct OpTraits<kRmsNorm> {
     }
 
     template <class T>
-    __device__ __forceinline__ static float apply_stream(float x, const Coef &c, float g, float b)
+    __device__ __forceinline__ static float apply_stream(const float (&in)[kIn], const Coef &c, float g, float b)
     {
-        return apply<T>(x, c, g, b);
+        return apply<T>(in, c, g, b);
+    }
+};
+
+// ---------------------------------------------------------------------------
+// Softmax-logits backward: inputs x (logits) and dy; dx = p (dy - sum dy p)
+// with p = softmax(x) recomputed from x.  Coef: k0 = probability scale
+// (fp32: e^(m_wave - m) / s, the tile holding e^(x - m_wave); bf16: 1 / s),
+// k1 = u / s (the dot product of dy with p), k2 = row max m.
+// ---------------------------------------------------------------------------
+template <>
+struct OpTraits<kSoftmaxBwd> {
+    static constexpr int kQ = 3;  // (m, s, u)
+    static constexpr int kIn = 2;
+    static constexpr int kParams = 0;
+    static constexpr bool kParamsInReduce = false;
+    static constexpr bool kRowOut = false;
+    template <class T> using Out = T;
+    using Partial = Part<kQ>;
+
+    template <class T, int VB, int IT>
+    __device__ __forceinline__ static Partial wave_partial(Tile<T, VB, IT> (&t)[kIn], int kvalid)
+    {
+        constexpr int E = Tile<T, VB, IT>::kEpv;
+        float mt = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < IT; ++k)
+            if (k < kvalid)
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    mt = fmaxf(mt, elem<T, VB>(t[0].v[k], e));
+        const float mw = wave_max(mt);
+        fence_tile(t[0]);
+        float st = 0.0f, ut = 0.0f;
+#pragma unroll
+        for (int k = 0; k < IT; ++k)
+            if (k < kvalid)
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const float ex = exp_for<T>(elem<T, VB>(t[0].v[k], e) - mw);
+                    if constexpr (is_f32<T>())
+                        set_word<VB>(t[0].v[k], e, __float_as_uint(ex));
+                    st += ex;
+                    ut = __builtin_fmaf(ex, elem<T, VB>(t[1].v[k], e), ut);
+                }
+        return Partial{{mw, wave_sum(st), wave_sum(ut)}};
+    }
+
+    template <int N>
+    __device__ __forceinline__ static Partial merge(const Partial (&p)[N], int n)
+    {
+        float m = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+            if (i < n)
+                m = fmaxf(m, p[i].v[0]);
+        float s = 0.0f, u = 0.0f;
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+            if (i < n && p[i].v[1] != 0.0f) {
+                const float f = exp_acc(p[i].v[0] - m);
+                s += p[i].v[1] * f;
+                u += p[i].v[2] * f;
+            }
+        return Partial{{m, s, u}};
+    }
+
+    template <class T>
+    __device__ __forceinline__ static Coef finalize(const Partial &row, const Partial &own, int64_t, float)
+    {
+        const float inv_s = 1.0f / row.v[1];
+        const float dot = row.v[2] / row.v[1];
+        if constexpr (is_f32<T>())
+            return Coef{{own.v[1] != 0.0f ? exp_acc(own.v[0] - row.v[0]) * inv_s : 0.0f, dot, row.v[0], 0.0f}};
+        else
+            return Coef{{inv_s, dot, row.v[0], 0.0f}};
+    }
+
+    template <class T>
+    __device__ __forceinline__ static float apply(const float (&in)[kIn], const Coef &c, float, float)
+    {
+        float p;
+        if constexpr (is_f32<T>())
+            p = in[0] * c.k[0];  // in[0] already holds exp(x - m_wave)
+        else
+            p = exp_fast(in[0] - c.k[2]) * c.k[0];
+        return p * (in[1] - c.k[1]);
+    }
+
+    template <class T, int VB, int U>
+    __device__ __forceinline__ static void stream_update(Partial &r, const RawVec<VB> (&v)[kIn][U],
+                                                         const RawVec<VB> (&)[U], int kvalid)
+    {
+        constexpr int E = VB / StorageTraits<T>::kBytes;
+        float cm = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < U; ++k)
+            if (k < kvalid)
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    cm = fmaxf(cm, elem<T, VB>(v[0][k], e));
+        if (cm > r.v[0]) {
+            const float f = r.v[1] != 0.0f ? exp_acc(r.v[0] - cm) : 0.0f;
+            r.v[1] *= f;
+            r.v[2] *= f;
+            r.v[0] = cm;
+        }
+        float s = 0.0f, u = 0.0f;
+#pragma unroll
+        for (int k = 0; k < U; ++k)
+            if (k < kvalid)
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const float ex = exp_for<T>(elem<T, VB>(v[0][k], e) - r.v[0]);
+                    s += ex;
+                    u = __builtin_fmaf(ex, elem<T, VB>(v[1][k], e), u);
+                }
+        r.v[1] += s;
+        r.v[2] += u;
+    }
+
+    __device__ __forceinline__ static Partial stream_init() { return Partial{{-INFINITY, 0.0f, 0.0f}}; }
+
+    __device__ __forceinline__ static Partial wave_from_thread(const Partial &r)
+    {
+        const float mw = wave_max(r.v[0]);
+        const float f = r.v[1] != 0.0f ? exp_acc(r.v[0] - mw) : 0.0f;
+        return Partial{{mw, wave_sum(r.v[1] * f), wave_sum(r.v[2] * f)}};
+    }
+
+    template <class T>
+    __device__ __forceinline__ static Coef finalize_stream(const Partial &row, int64_t, float)
+    {
+        return Coef{{1.0f / row.v[1], row.v[2] / row.v[1], row.v[0], 0.0f}};
+    }
+
+    template <class T>
+    __device__ __forceinline__ static float apply_stream(const float (&in)[kIn], const Coef &c, float, float)
+    {
+        return exp_for<T>(in[0] - c.k[2]) * c.k[0] * (in[1] - c.k[1]);
+    }
+};
+
+// ---------------------------------------------------------------------------
+// LayerNorm backward, row part: inputs x and dy, parameter gamma; with
+// g = gamma dy, rstd = 1/sqrt(var + eps) and xhat = (x - mean) rstd,
+// dx = rstd (g - mean(g) - xhat mean(g xhat)).  fp32 storage only: the held
+// dy tile is overwritten with g by `prepare`.  Coef: k0 = mean, k1 = rstd,
+// k2 = mean(g), k3 = rstd^2 sum(g (x - mean)) / N.
+// ---------------------------------------------------------------------------
+template <>
+struct OpTraits<kLayerNormBwd> {
+    static constexpr int kQ = 5;  // (n, mean, M2, a, b)
+    static constexpr int kIn = 2;
+    static constexpr int kParams = 1;
+    static constexpr bool kParamsInReduce = true;
+    static constexpr bool kRowOut = false;
+    template <class T> using Out = T;
+    using Partial = Part<kQ>;
+
+    // Vector k of the dy tile becomes g = gamma dy (fp32 bits), `gv` holding
+    // the gamma vector of the same columns.
+    template <class T, int VB, int IT>
+    __device__ __forceinline__ static void prepare(Tile<T, VB, IT> (&t)[kIn], int k, const RawVec<VB> &gv)
+    {
+        static_assert(is_f32<T>(), "LayerNorm backward holds g = gamma * dy in fp32");
+        constexpr int E = Tile<T, VB, IT>::kEpv;
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            set_word<VB>(t[1].v[k], e, __float_as_uint(elem<T, VB>(gv, e) * elem<T, VB>(t[1].v[k], e)));
+    }
+
+    template <class T, int VB, int IT>
+    __device__ __forceinline__ static Partial wave_partial(Tile<T, VB, IT> (&t)[kIn], int kvalid)
+    {
+        constexpr int E = Tile<T, VB, IT>::kEpv;
+        float sx = 0.0f, sg = 0.0f;
+#pragma unroll
+        for (int k = 0; k < IT; ++k)
+            if (k < kvalid)
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    sx += elem<T, VB>(t[0].v[k], e);
+                    sg += elem<T, VB>(t[1].v[k], e);
+                }
+        const float nw = wave_sum(static_cast<float>(kvalid * E));
+        const float sw = wave_sum(sx);
+        const float mean = nw > 0.0f ? sw / nw : 0.0f;
+        fence_tile(t[0]);
+        fence_tile(t[1]);
+        float m2 = 0.0f, b = 0.0f;
+#pragma unroll
+        for (int k = 0; k < IT; ++k)
+            if (k < kvalid)
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const float d = elem<T, VB>(t[0].v[k], e) - mean;
+                    m2 = __builtin_fmaf(d, d, m2);
+                    b = __builtin_fmaf(elem<T, VB>(t[1].v[k], e), d, b);
+                }
+        return Partial{{nw, mean, wave_sum(m2), wave_sum(sg), wave_sum(b)}};
+    }
+
+    // n, mean, M2 as LayerNorm; a adds; b_i is re-centred on the merged mean.
+    template <int N>
+    __device__ __forceinline__ static Partial merge(const Partial (&p)[N], int n)
+    {
+        float nt = 0.0f, acc = 0.0f;
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+            if (i < n) {
+                nt += p[i].v[0];
+                acc = __builtin_fmaf(p[i].v[0], p[i].v[1], acc);
+            }
+        const float mean = nt > 0.0f ? acc / nt : 0.0f;
+        float m2 = 0.0f, a = 0.0f, b = 0.0f;
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+            if (i < n) {
+                const float d = p[i].v[1] - mean;
+                m2 += p[i].v[2] + p[i].v[0] * d * d;
+                a += p[i].v[3];
+                b += __builtin_fmaf(p[i].v[3], d, p[i].v[4]);
+            }
+        return Partial{{nt, mean, m2, a, b}};
+    }
+
+    template <class T>
+    __device__ __forceinline__ static Coef finalize(const Partial &row, const Partial &, int64_t cols, float eps)
+    {
+        const float inv_n = 1.0f / static_cast<float>(cols);
+        const float rstd = 1.0f / sqrtf(row.v[2] * inv_n + eps);
+        return Coef{{row.v[1], rstd, row.v[3] * inv_n, rstd * rstd * (row.v[4] * inv_n)}};
+    }
+
+    // in[0] = x, in[1] = g
+    template <class T>
+    __device__ __forceinline__ static float apply(const float (&in)[kIn], const Coef &c, float, float)
+    {
+        return c.k[1] * __builtin_fmaf(-(in[0] - c.k[0]), c.k[3], in[1] - c.k[2]);
+    }
+
+    // ---- streaming form: each chunk reduced two-pass to (n_c, mean_c, M2_c,
+    // a_c, b_c) and folded into the running partial by the merge rule.
+    template <class T, int VB, int U>
+    __device__ __forceinline__ static void stream_update(Partial &r, const RawVec<VB> (&v)[kIn][U],
+                                                         const RawVec<VB> (&gam)[U], int kvalid)
+    {
+        constexpr int E = VB / StorageTraits<T>::kBytes;
+        if (kvalid <= 0)
+            return;
+        float sx = 0.0f, sg = 0.0f;
+#pragma unroll
+        for (int k = 0; k < U; ++k)
+            if (k < kvalid)
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    sx += elem<T, VB>(v[0][k], e);
+                    sg = __builtin_fmaf(elem<T, VB>(gam[k], e), elem<T, VB>(v[1][k], e), sg);
+                }
+        const float nc = static_cast<float>(kvalid * E);
+        const float mc = sx / nc;
+        float m2c = 0.0f, bc = 0.0f;
+#pragma unroll
+        for (int k = 0; k < U; ++k)
+            if (k < kvalid)
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const float d = elem<T, VB>(v[0][k], e) - mc;
+                    m2c = __builtin_fmaf(d, d, m2c);
+                    bc = __builtin_fmaf(elem<T, VB>(gam[k], e) * elem<T, VB>(v[1][k], e), d, bc);
+                }
+        const float n2 = r.v[0] + nc;
+        const float d = mc - r.v[1];
+        const float mean2 = __builtin_fmaf(d, nc / n2, r.v[1]);
+        r.v[2] += m2c + d * d * (r.v[0] * nc / n2);
+        r.v[4] = __builtin_fmaf(r.v[3], r.v[1] - mean2, r.v[4]) + __builtin_fmaf(sg, mc - mean2, bc);
+        r.v[3] += sg;
+        r.v[1] = mean2;
+        r.v[0] = n2;
+    }
+
+    __device__ __forceinline__ static Partial stream_init() { return Partial{{0.0f, 0.0f, 0.0f, 0.0f, 0.0f}}; }
+
+    __device__ __forceinline__ static Partial wave_from_thread(const Partial &r)
+    {
+        const float nw = wave_sum(r.v[0]);
+        const float mean = nw > 0.0f ? wave_sum(r.v[0] * r.v[1]) / nw : 0.0f;
+        const float d = r.v[1] - mean;
+        return Partial{{nw, mean, wave_sum(r.v[2] + r.v[0] * d * d), wave_sum(r.v[3]),
+                        wave_sum(__builtin_fmaf(r.v[3], d, r.v[4]))}};
+    }
+
+    template <class T>
+    __device__ __forceinline__ static Coef finalize_stream(const Partial &row, int64_t cols, float eps)
+    {
+        return finalize<T>(row, row, cols, eps);
+    }
+
+    // in[0] = x, in[1] = dy (not yet multiplied by gamma)
+    template <class T>
+    __device__ __forceinline__ static float apply_stream(const float (&in)[kIn], const Coef &c, float g, float)
+    {
+        const float held[kIn] = {in[0], g * in[1]};
+        return apply<T>(held, c, g, 0.0f);
+    }
+};
+
+// ---------------------------------------------------------------------------
+// Row-wise symmetric int8 quantization: a = max |x|, inv = min(127 / a,
+// FLT_MAX) (0 for a = 0), q = clamp(rint(x * inv), -127, 127), and the row's
+// scale a / 127 written to the per-row output.  Each / and * is one correctly
+// rounded fp32 operation, so the codes are fixed by the inputs.
+// Coef: k0 = inv, k1 = scale.
+// ---------------------------------------------------------------------------
+template <>
+struct OpTraits<kQuantInt8> {
+    static constexpr int kQ = 1;
+    static constexpr int kIn = 1;
+    static constexpr int kParams = 0;
+    static constexpr bool kParamsInReduce = false;
+    static constexpr bool kRowOut = true;
+    template <class T> using Out = i8_t;
+    using Partial = Part<kQ>;
+
+    template <class T, int VB, int IT>
+    __device__ __forceinline__ static Partial wave_partial(Tile<T, VB, IT> (&t)[kIn], int kvalid)
+    {
+        constexpr int E = Tile<T, VB, IT>::kEpv;
+        float a = 0.0f;
+#pragma unroll
+        for (int k = 0; k < IT; ++k)
+            if (k < kvalid)
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    a = fmaxf(a, fabsf(elem<T, VB>(t[0].v[k], e)));
+        return Partial{{wave_max(a)}};
+    }
+
+    template <int N>
+    __device__ __forceinline__ static Partial merge(const Partial (&p)[N], int n)
+    {
+        float a = 0.0f;
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+            if (i < n)
+                a = fmaxf(a, p[i].v[0]);
+        return Partial{{a}};
+    }
+
+    template <class T>
+    __device__ __forceinline__ static Coef finalize(const Partial &row, const Partial &, int64_t, float)
+    {
+        const float a = row.v[0];
+        const float inv = a > 0.0f ? fminf(127.0f / a, FLT_MAX) : 0.0f;
+        return Coef{{inv, a / 127.0f, 0.0f, 0.0f}};
+    }
+
+    template <class T>
+    __device__ __forceinline__ static float apply(const float (&in)[kIn], const Coef &c, float, float)
+    {
+        return fminf(fmaxf(__builtin_rintf(in[0] * c.k[0]), -127.0f), 127.0f);
+    }
+
+    __device__ __forceinline__ static float row_value(const Coef &c) { return c.k[1]; }
+
+    template <class T, int VB, int U>
+    __device__ __forceinline__ static void stream_update(Partial &r, const RawVec<VB> (&v)[kIn][U],
+                                                         const RawVec<VB> (&)[U], int kvalid)
+    {
+        constexpr int E = VB / StorageTraits<T>::kBytes;
+#pragma unroll
+        for (int k = 0; k < U; ++k)
+            if (k < kvalid)
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    r.v[0] = fmaxf(r.v[0], fabsf(elem<T, VB>(v[0][k], e)));
+    }
+
+    __device__ __forceinline__ static Partial stream_init() { return Partial{{0.0f}}; }
+
+    __device__ __forceinline__ static Partial wave_from_thread(const Partial &r) { return Partial{{wave_max(r.v[0])}}; }
+
+    template <class T>
+    __device__ __forceinline__ static Coef finalize_stream(const Partial &row, int64_t cols, float eps)
+    {
+        return finalize<T>(row, row, cols, eps);
+    }
+
+    template <class T>
+    __device__ __forceinline__ static float apply_stream(const float (&in)[kIn], const Coef &c, float g, float b)
+    {
+        return apply<T>(in, c, g, b);
     }
 };
 

@@ -12,8 +12,19 @@
 namespace credit {
 
 int elem_bytes(int dt) { return dt == 1 ? 2 : 4; }
-int n_params(int op) { return op == 1 ? 2 : (op == 2 ? 1 : 0); }
-int stats_per_partial(int op) { return op == 1 ? 3 : (op == 2 ? 1 : 2); }
+
+// Per operator (credit_op_t order: softmax, LayerNorm, RMSNorm, softmax-logits
+// backward, LayerNorm backward, int8 quantization).
+int n_params(int op)
+{
+    static const int v[kNumOps] = {0, 2, 1, 0, 1, 0};
+    return op >= 0 && op < kNumOps ? v[op] : 0;
+}
+int stats_per_partial(int op) { return op_stats(op); }
+int in_bytes(int op, int dt) { return op_inputs(op) * elem_bytes(dt); }
+int out_bytes(int op, int dt) { return op == 5 ? 1 : elem_bytes(dt); }
+int row_out_bytes(int op) { return op == 5 ? 4 : 0; }
+bool op_supported(int op, int dt) { return op >= 0 && op < kNumOps && (dt == 0 || (dt == 1 && op != 4)); }
 
 int vec_bytes_for(int dt, int64_t cols)
 {
@@ -108,14 +119,23 @@ static bool pick_holding_tile(const std::vector<TileSpec> &ladder, int64_t nv, T
     return found;
 }
 
-bool single_tile(int dt, int64_t cols, TileSpec *out)
+// The held-tile ladders of path 1 (wave and workgroup tiles) that `op`
+// compiles for rows of `vb`-byte vectors.
+static std::vector<TileSpec> single_ladder(int op, int vb)
+{
+    std::vector<TileSpec> ladder;
+    for (int kind : {kKindWave, kKindWg})
+        for (const TileSpec &u : tiles_for(kind, vb == 16))
+            if (tile_enabled(op, kind, u.block, u.items, vb))
+                ladder.push_back(u);
+    return ladder;
+}
+
+bool single_tile(int op, int dt, int64_t cols, TileSpec *out)
 {
     const int vb = vec_bytes_for(dt, cols);
-    const bool v16 = vb == 16;
     const int64_t nv = vectors_in_row(dt, cols, vb);
-    std::vector<TileSpec> ladder = tiles_for(kKindWave, v16);
-    for (const TileSpec &u : tiles_for(kKindWg, v16))
-        ladder.push_back(u);
+    const std::vector<TileSpec> ladder = single_ladder(op, vb);
     TileSpec t;
     if (!pick_holding_tile(ladder, nv, &t))
         return false;
@@ -185,7 +205,7 @@ Model model_of(const Calibration &c)
     return m;
 }
 
-double eff_of(const double (&e)[3][2], int op, int dt)
+double eff_of(const double (&e)[kNumOps][2], int op, int dt)
 {
     const double v = e[op][dt];
     return v > 0 ? v : 1.0;
@@ -193,10 +213,10 @@ double eff_of(const double (&e)[3][2], int op, int dt)
 
 // Estimated resident workgroups per CU for a tile: VGPRs from the held data
 // plus a fixed overhead, 512 VGPRs per SIMD lane, 4 SIMDs, at most 8 waves/SIMD.
-int wgs_per_cu(const TileSpec &t)
+int wgs_per_cu(const TileSpec &t, int inputs)
 {
     const int waves = t.block / 64;
-    const int data_vgprs = (t.kind == kKindReread) ? t.items * t.vb / 4 * 2 : t.items * t.vb / 4;
+    const int data_vgprs = inputs * ((t.kind == kKindReread) ? t.items * t.vb / 4 * 2 : t.items * t.vb / 4);
     int vgprs = data_vgprs + 32;
     vgprs = (vgprs + 7) / 8 * 8;
     int waves_per_simd = std::min(8, 512 / vgprs);
@@ -220,8 +240,12 @@ double stream_us(const Model &m, const DeviceModel &d, double bytes, double unit
 
 namespace {
 
+// b_in: bytes per element of all row inputs (the bytes a reread reads again);
+// b_out: bytes per element written; bytes_io: one read of every input, one
+// write of the output, each parameter vector once and the per-row outputs.
 struct Shape {
-    double M, N, b, row_bytes, bytes_io;
+    double M, N, b_in, b_out, row_bytes, bytes_io;
+    int inputs;
 };
 
 Shape shape_of(const PlanRequest &req)
@@ -229,9 +253,12 @@ Shape shape_of(const PlanRequest &req)
     Shape s;
     s.M = static_cast<double>(req.rows);
     s.N = static_cast<double>(req.cols);
-    s.b = elem_bytes(req.dt);
-    s.row_bytes = s.N * s.b;
-    s.bytes_io = s.M * s.N * 2.0 * s.b + s.N * s.b * n_params(req.op);
+    s.b_in = in_bytes(req.op, req.dt);
+    s.b_out = out_bytes(req.op, req.dt);
+    s.inputs = op_inputs(req.op);
+    s.row_bytes = s.N * s.b_in;
+    s.bytes_io = s.M * s.N * (s.b_in + s.b_out) + s.N * elem_bytes(req.dt) * n_params(req.op) +
+                 s.M * row_out_bytes(req.op);
     return s;
 }
 
@@ -243,7 +270,7 @@ PathEstimate estimate_single(const PlanRequest &req, const Calibration &cal, con
     e.legal = true;
     e.tile = t;
     const double units = t.kind == kKindWave ? std::ceil(s.M / 4.0) : s.M;
-    e.t_stream_us = stream_us(m, cal.device, s.bytes_io, units, wgs_per_cu(t));
+    e.t_stream_us = stream_us(m, cal.device, s.bytes_io, units, wgs_per_cu(t, s.inputs));
     e.us = m.launch_us + e.t_stream_us * eff_of(cal.single_eff, req.op, req.dt);
     return e;
 }
@@ -259,7 +286,7 @@ PathEstimate estimate_reread(const PlanRequest &req, const Calibration &cal, con
     PathEstimate e;
     e.legal = true;
     e.tile = t;
-    const double resident = std::min(s.M, static_cast<double>(d.cus) * wgs_per_cu(t));
+    const double resident = std::min(s.M, static_cast<double>(d.cus) * wgs_per_cu(t, s.inputs));
     const double per_xcd = resident / d.xcds;
     double miss;
     if (per_xcd * s.row_bytes <= d.l2_bytes_per_xcd)
@@ -268,8 +295,8 @@ PathEstimate estimate_reread(const PlanRequest &req, const Calibration &cal, con
         miss = 0.5;
     else
         miss = 1.0;
-    const double bytes3 = s.bytes_io + s.M * s.N * s.b * miss;
-    e.t_stream_us = stream_us(m, d, bytes3, s.M, wgs_per_cu(t));
+    const double bytes3 = s.bytes_io + s.M * s.N * s.b_in * miss;
+    e.t_stream_us = stream_us(m, d, bytes3, s.M, wgs_per_cu(t, s.inputs));
     e.us = m.launch_us + e.t_stream_us * eff_of(cal.reread_eff, req.op, req.dt);
     return e;
 }
@@ -283,15 +310,16 @@ PathEstimate estimate_split(const PlanRequest &req, const Calibration &cal, int 
     const Model m = model_of(cal);
     const DeviceModel &d = cal.device;
     const Shape s = shape_of(req);
-    const double b_base = base_is_single ? 2.0 * s.b : 3.0 * s.b;  // bytes/element of the baseline schedule
-    const double b_reread = base_is_single ? 0.0 : s.b;
+    // bytes/element of the baseline schedule
+    const double b_base = base_is_single ? s.b_in + s.b_out : 2.0 * s.b_in + s.b_out;
+    const double b_reread = base_is_single ? 0.0 : s.b_in;
     PathEstimate e;
     e.legal = true;
     e.split_p = P;
     e.tile = t;
-    const double clusters = std::max(1.0, std::floor(static_cast<double>(d.cus) * wgs_per_cu(t) / P));
+    const double clusters = std::max(1.0, std::floor(static_cast<double>(d.cus) * wgs_per_cu(t, s.inputs) / P));
     e.waves = std::ceil(s.M / clusters);
-    e.t_stream_us = stream_us(m, d, s.bytes_io, s.M * P, wgs_per_cu(t));
+    e.t_stream_us = stream_us(m, d, s.bytes_io, s.M * P, wgs_per_cu(t, s.inputs));
     e.t_ctrl_us = e.waves * m.exchange_us;
     e.t_save_us = (b_reread / b_base) * base.us;  // Eq. 7
     e.us = m.launch_us + e.t_stream_us * eff_of(cal.split_eff, req.op, req.dt) + e.t_ctrl_us;
@@ -365,7 +393,7 @@ bool make_plan(const PlanRequest &req, const Calibration &cal, int forced_path, 
         return true;
     Plan p;
     TileSpec t;
-    if (single_tile(req.dt, req.cols, &t))
+    if (single_tile(req.op, req.dt, req.cols, &t))
         p.est[0] = estimate_single(req, cal, t);
     p.est[2] = estimate_reread(req, cal, reread_tile(req.dt, req.cols));
     const bool single_legal = p.est[0].legal;
@@ -423,13 +451,11 @@ void enumerate_candidates(const PlanRequest &req, const Calibration &cal, std::v
     const int vb = vec_bytes_for(req.dt, req.cols);
     const bool v16 = vb == 16;
     const int64_t nv = vectors_in_row(req.dt, req.cols, vb);
-    std::vector<TileSpec> held = tiles_for(kKindWave, v16);
-    for (const TileSpec &t : tiles_for(kKindWg, v16))
-        held.push_back(t);
+    const std::vector<TileSpec> held = single_ladder(req.op, vb);
     PathEstimate best1;
     for (int kind : {kKindWave, kKindWg})
         for (TileSpec t : tiles_for(kind, v16)) {
-            if (!worth_holding(held, t, nv))
+            if (!tile_enabled(req.op, kind, t.block, t.items, vb) || !worth_holding(held, t, nv))
                 continue;
             t.vb = vb;
             const PathEstimate e = estimate_single(req, cal, t);
@@ -622,9 +648,9 @@ bool parse_calibration(const std::string &text, Calibration *out)
     get("exchange_us", &c.exchange_us);
     get("reread_hit_l2", &c.reread_hit_l2);
     const char *effs[3] = {"single_eff", "reread_eff", "split_eff"};
-    double(*dst[3])[3][2] = {&c.single_eff, &c.reread_eff, &c.split_eff};
+    double(*dst[3])[kNumOps][2] = {&c.single_eff, &c.reread_eff, &c.split_eff};
     for (int k = 0; k < 3; ++k)
-        for (int op = 0; op < 3; ++op)
+        for (int op = 0; op < kNumOps; ++op)
             for (int dt = 0; dt < 2; ++dt)
                 get((std::string(effs[k]) + "[" + std::to_string(op) + "][" + std::to_string(dt) + "]").c_str(),
                     &(*dst[k])[op][dt]);
@@ -656,8 +682,7 @@ bool parse_calibration(const std::string &text, Calibration *out)
         e.vb = static_cast<int>(f[7]);
         e.wgs_per_cu = static_cast<int>(f[8]);
         const int n = static_cast<int>(f[9]);
-        if (e.op < 0 || e.op > 2 || e.dt < 0 || e.dt > 1 || e.cols < 1 || e.path < 1 || e.path > 3 || n < 1 ||
-            n > 64)
+        if (!op_supported(e.op, e.dt) || e.cols < 1 || e.path < 1 || e.path > 3 || n < 1 || n > 64)
             return false;
         for (int j = 0; j < n; ++j) {
             double rr = 0.0, tt = 0.0;

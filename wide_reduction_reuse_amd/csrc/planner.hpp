@@ -21,6 +21,8 @@ namespace credit {
 
 enum PathId { kPathAuto = 0, kPathSingle = 1, kPathSplit = 2, kPathReread = 3 };
 
+constexpr int kNumOps = 6;  // credit_op_t values 0..5
+
 struct TileSpec {
     int kind = 0;   // KernelKind
     int block = 0;  // threads per row owner (64: one wave per row)
@@ -63,9 +65,9 @@ struct Calibration {
     double exchange_us = -1.0;      // one split-row exchange round (control kernel excess)
     double reread_hit_l2 = -1.0;    // fraction of a reread served on chip when the working set fits L2
     // per-(op, dtype) multipliers on the streaming time, fitted to path-1 and path-3 timings
-    double single_eff[3][2] = {{-1, -1}, {-1, -1}, {-1, -1}};
-    double reread_eff[3][2] = {{-1, -1}, {-1, -1}, {-1, -1}};
-    double split_eff[3][2] = {{-1, -1}, {-1, -1}, {-1, -1}};
+    double single_eff[kNumOps][2] = {{-1, -1}, {-1, -1}, {-1, -1}, {-1, -1}, {-1, -1}, {-1, -1}};
+    double reread_eff[kNumOps][2] = {{-1, -1}, {-1, -1}, {-1, -1}, {-1, -1}, {-1, -1}, {-1, -1}};
+    double split_eff[kNumOps][2] = {{-1, -1}, {-1, -1}, {-1, -1}, {-1, -1}, {-1, -1}, {-1, -1}};
     DeviceModel device;
     bool has_device = false;
     // measured candidates; shapes whose (op, dtype, cols) appear here are
@@ -103,6 +105,10 @@ struct Plan {
 int elem_bytes(int dt);
 int n_params(int op);
 int stats_per_partial(int op);  // q: scalars exchanged per partial
+int in_bytes(int op, int dt);   // bytes per element of all row inputs (x, and dy for backward operators)
+int out_bytes(int op, int dt);  // bytes per output element (1 for int8 codes)
+int row_out_bytes(int op);      // bytes written per row besides the row (quantization scale)
+bool op_supported(int op, int dt);  // a compiled (operator, dtype) pair
 
 // Bytes per global access for a row of `cols` elements: 16 when the row's byte
 // length is a multiple of 16 (rows stay 16-byte aligned), else one element.
@@ -112,7 +118,7 @@ int vec_bytes_for(int dt, int64_t cols);
 const std::vector<TileSpec> &tiles_for(int kind, int vb_is_16);
 
 // Path 1: the tile that holds a row of `cols`, or false if none can.
-bool single_tile(int dt, int64_t cols, TileSpec *out);
+bool single_tile(int op, int dt, int64_t cols, TileSpec *out);
 // Path 2: the tile that holds a 1/p slice, or false if none can.
 bool split_tile(int op, int dt, int64_t cols, int p, TileSpec *out);
 // Path 3: always possible.

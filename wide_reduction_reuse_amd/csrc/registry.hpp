@@ -23,7 +23,21 @@ struct KernelEntry {
 void register_softmax_kernels(std::vector<KernelEntry> &out);
 void register_layernorm_kernels(std::vector<KernelEntry> &out);
 void register_rmsnorm_kernels(std::vector<KernelEntry> &out);
+void register_softmax_bwd_kernels(std::vector<KernelEntry> &out);
+void register_layernorm_bwd_kernels(std::vector<KernelEntry> &out);
+void register_quantize_kernels(std::vector<KernelEntry> &out);
 void register_misc_kernels(std::vector<KernelEntry> &out);
+
+// Row inputs an operator holds per element: x, and dy for the two backward
+// operators (credit_op_t 3 and 4).
+constexpr int op_inputs(int op) { return (op == 3 || op == 4) ? 2 : 1; }
+
+// Scalars per partial that split workgroups exchange (the host sizes each
+// cluster's exchange words from it, the kernels write and read that many).
+constexpr int op_stats(int op)
+{
+    return op == 0 ? 2 : op == 1 ? 3 : op == 2 ? 1 : op == 3 ? 3 : op == 4 ? 5 : 1;
+}
 
 // Tile ladders for 16-byte accesses: X(items) for wave-per-row, X(block, items)
 // for the others.
@@ -34,13 +48,27 @@ void register_misc_kernels(std::vector<KernelEntry> &out);
 #define CREDIT_SPLIT_TILES(X) X(256, 8) X(256, 16) X(512, 4) X(512, 8) X(512, 16) X(1024, 4) X(1024, 8) X(1024, 16)
 #define CREDIT_REREAD_TILES(X) X(256, 4) X(512, 4) X(1024, 4)
 
-// Tiles left out for one operator: LayerNorm's split kernel at 1024 threads x
-// 16 16-byte vectors needs more than the 128 VGPRs that 1024 threads allow (it
-// spills), so LayerNorm splits such slices finer instead.
+// Tiles left out for one operator, all at 1024 threads, where a thread has
+// at most 128 VGPRs; each of them spilled registers to scratch memory when
+// compiled.  held = bytes of row data a thread holds (all inputs).
+//   LayerNorm split 16 x 16 B: the next smaller tiles split such slices finer.
+//   softmax-logits backward (x and dy held): more than 256 B (path 1) or
+//     128 B (split, which also keeps the exchange state).
+//   LayerNorm backward (x and g held, five statistics): more than 64 B; its
+//     512-thread tiles hold the same rows.
 constexpr bool tile_enabled(int op, int kind, int block, int items, int vb)
 {
-    return !(op == 1 && (kind == kKindSplit || kind == kKindControl) && block == 1024 && items == 16 &&
-             vb == 16);
+    if (kind == kKindReread || block < 1024)
+        return true;
+    const bool split = kind == kKindSplit || kind == kKindControl;
+    const int held = op_inputs(op) * items * vb;
+    if (op == 1 && split && items == 16 && vb == 16)
+        return false;
+    if (op == 3 && held > (split ? 128 : 256))
+        return false;
+    if (op == 4 && held > 64)
+        return false;
+    return true;
 }
 
 // Ladders for one-element accesses (rows whose byte length is not a multiple

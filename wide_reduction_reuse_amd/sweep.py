@@ -1,6 +1,6 @@
 """Exhaustive timing of every legal plan on a set of shapes.
 
-    python -m wide_reduction_reuse_amd.sweep --points named|sweep|all|calib [--out FILE]
+    python -m wide_reduction_reuse_amd.sweep --points named|sweep|next|all|calib|calib_next|calib_all
                                              [--steps 15] [--warmup 3] [--ops ...]
 
 For each shape it enumerates the legal plans (credit_enumerate_plans: every
@@ -12,9 +12,9 @@ calibration and of its accuracy score (the CREDIT paper's evaluation times
 every legal cluster size P and reports the fastest, Sec. IV-A; its
 profitability accuracy compares predicted and measured winners, Sec. IV-C).
 
-Inputs are synthetic and seeded: for timing, x (and gamma, beta) are drawn on
-the device with torch's seeded generator from the workload's distribution, so
-that 1 GiB shapes need no host-side generation.
+Inputs are synthetic and seeded: for timing, x (and dy, gamma, beta) are drawn
+on the device with torch's seeded generator from the workload's distributions,
+so that GiB-sized shapes need no host-side generation.
 """
 from __future__ import annotations
 
@@ -27,8 +27,9 @@ from . import workloads as W
 from .timing import flush_buffer, summarize, time_launches
 
 
-def device_inputs(w: W.Workload):
-    """x, gamma, beta on the device, drawn from w's distributions (seeded)."""
+def device_inputs(w: W.Workload) -> dict:
+    """The operand mapping of w (inputs drawn on the device from w's
+    distributions, seeded; outputs allocated)."""
     import torch
     g = torch.Generator(device="cuda")
     g.manual_seed(w.seed)
@@ -41,14 +42,16 @@ def device_inputs(w: W.Workload):
     elif w.x_dist == "row_offset":
         off = (torch.rand((w.rows, 1), generator=g, device="cuda") * 2.0 - 1.0) * w.row_offset
         x.mul_(w.x_scale).add_(off)
-    gamma = beta = None
-    if w.op in ("layernorm", "rmsnorm"):
+    gamma = beta = dy = None
+    if W.N_PARAMS[w.op] >= 1:
         gamma = torch.rand(w.cols, generator=g, device="cuda") + 0.5
-    if w.op == "layernorm":
+    if W.N_PARAMS[w.op] >= 2:
         beta = torch.randn(w.cols, generator=g, device="cuda") * 0.1
+    if w.inputs >= 2:
+        dy = torch.randn((w.rows, w.cols), generator=g, device="cuda", dtype=torch.float32)
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     cast = (lambda t: None if t is None else t.to(dt).contiguous())
-    return cast(x), cast(gamma), cast(beta)
+    return W.alloc_outputs(w, {"x": cast(x), "dy": cast(dy), "gamma": cast(gamma), "beta": cast(beta)})
 
 
 def plan_key(p) -> str:
@@ -58,8 +61,7 @@ def plan_key(p) -> str:
 def sweep_shape(w: W.Workload, steps: int, warmup: int, flush_buf) -> dict:
     import torch
     from . import credit as C
-    x, g, b = device_inputs(w)
-    y = torch.empty_like(x)
+    t = device_inputs(w)
     sel = C.credit_select_path(w.op, w.dtype, w.rows, w.cols)
     cands = C.credit_enumerate_plans(w.op, w.dtype, w.rows, w.cols)
     rec = {"workload": w.name, "op": w.op, "dtype": w.dtype, "rows": w.rows, "cols": w.cols,
@@ -67,7 +69,7 @@ def sweep_shape(w: W.Workload, steps: int, warmup: int, flush_buf) -> dict:
            "candidates": []}
     for p in cands:
         def launch(e0, e1, p=p):
-            C.credit_run_plan_timed(w.op, x, g, b, y, w.eps, p, e0, e1)
+            C.credit_run_plan_timed(w.op, p, t, e0, e1, eps=w.eps)
         durs, _ = time_launches(launch, steps, warmup, flush_buf)
         C.credit_check_errors()
         s = summarize(durs, w.algorithmic_bytes())
@@ -77,7 +79,7 @@ def sweep_shape(w: W.Workload, steps: int, warmup: int, flush_buf) -> dict:
     best = min(rec["candidates"], key=lambda c: c["median_ms"])
     rec["best"] = best["key"]
     rec["best_median_ms"] = best["median_ms"]
-    del x, g, b, y
+    del t
     torch.cuda.empty_cache()
     return rec
 
@@ -85,11 +87,15 @@ def sweep_shape(w: W.Workload, steps: int, warmup: int, flush_buf) -> dict:
 def points(which: str, ops=None):
     pts = []
     if which in ("named", "all"):
-        pts += [W.NAMED[n] for n in W.CONFIG_ORDER]
+        pts += [W.NAMED[n] for n in W.CONFIG_ORDER + W.NEXT_ORDER]
     if which in ("sweep", "all"):
         pts += W.sweep_points()
-    if which == "calib":
+    if which in ("next", "all"):
+        pts += W.next_points()
+    if which in ("calib", "calib_all"):
         pts += W.calibration_points()
+    if which in ("calib_next", "calib_all"):
+        pts += W.calibration_points_next()
     if ops:
         pts = [p for p in pts if p.op in ops]
     return pts
@@ -97,7 +103,7 @@ def points(which: str, ops=None):
 
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
-    ap.add_argument("--points", default="named", choices=("named", "sweep", "all", "calib"))
+    ap.add_argument("--points", default="named", choices=("named", "sweep", "next", "all", "calib", "calib_next", "calib_all"))
     ap.add_argument("--ops", nargs="*", default=None)
     ap.add_argument("--out", default="-")
     ap.add_argument("--steps", type=int, default=15)

@@ -18,10 +18,21 @@ Workloads (rows x cols, distributions, seeds):
   rows = bytes / (cols * element size); x ~ N(0, 1); gamma, beta, eps as above;
   seed 1000 + point index.
 
+and the three further workloads of the CREDIT paper's evaluation (Sec. IV-A:
+fp32, M = 4096 rows, 2048 for LayerNorm, widths 4096 ... 65536), at the widest
+width, which the paper's traffic measurement (Fig. 5) also uses:
+
+* ``softmax_bwd_f32_4096x65536``   logits x ~ N(0, 1), dy ~ N(0, 1)          seed 5
+* ``layernorm_bwd_f32_2048x65536`` x = 3 N(0,1) + 0.5, dy ~ N(0, 1),
+  gamma ~ U(0.5, 1.5), eps = 1e-5                                           seed 6
+* ``quantize_int8_f32_4096x65536`` x ~ N(0, 1) with 1% of elements x50      seed 7
+* the width grid of those three (``next_points``): each at cols in
+  {4096, 8192, 16384, 32768, 65536}, seed 3000 + point index.
+
 The second argument of N(mu, s) is the standard deviation.  Draw order from one
 ``numpy.random.Generator(PCG64(seed))``: x (float32), then the outlier mask or the
-row offsets, then gamma, then beta.  bf16 values are the float32 draws rounded to
-nearest, ties to even.
+row offsets, then gamma, then beta, then dy.  bf16 values are the float32 draws
+rounded to nearest, ties to even.
 """
 from __future__ import annotations
 
@@ -30,11 +41,18 @@ from typing import Dict, List, Optional
 
 import numpy as np
 
-OPS = ("softmax", "layernorm", "rmsnorm")
+OPS = ("softmax", "layernorm", "rmsnorm", "softmax_bwd", "layernorm_bwd", "quantize_int8")
+FWD_OPS = ("softmax", "layernorm", "rmsnorm")          # the crossover sweep's operators
+NEXT_OPS = ("softmax_bwd", "layernorm_bwd", "quantize_int8")
 DTYPES = ("f32", "bf16")
+# (op, dtype) pairs with kernels: LayerNorm backward is fp32 only
+SUPPORTED = {(op, dt) for op in OPS for dt in DTYPES} - {("layernorm_bwd", "bf16")}
 ELEM_BYTES = {"f32": 4, "bf16": 2}
-N_PARAMS = {"softmax": 0, "layernorm": 2, "rmsnorm": 1}
-DEFAULT_EPS = {"softmax": 0.0, "layernorm": 1e-5, "rmsnorm": 1e-6}
+N_PARAMS = {"softmax": 0, "layernorm": 2, "rmsnorm": 1, "softmax_bwd": 0, "layernorm_bwd": 1, "quantize_int8": 0}
+N_INPUTS = {"softmax_bwd": 2, "layernorm_bwd": 2}      # row inputs per element (x, dy); others 1
+ROW_OUT_BYTES = {"quantize_int8": 4}                   # fp32 scale per row
+DEFAULT_EPS = {"softmax": 0.0, "layernorm": 1e-5, "rmsnorm": 1e-6, "softmax_bwd": 0.0, "layernorm_bwd": 1e-5,
+               "quantize_int8": 0.0}
 
 SWEEP_COLS = (1024, 4096, 16384, 65536, 262144)
 SWEEP_BYTES = (16 << 20, 256 << 20, 1 << 30)
@@ -60,10 +78,21 @@ class Workload:
     def elem_bytes(self) -> int:
         return ELEM_BYTES[self.dtype]
 
+    @property
+    def inputs(self) -> int:
+        return N_INPUTS.get(self.op, 1)
+
+    @property
+    def out_bytes(self) -> int:
+        """Bytes per output element (int8 codes for quantization)."""
+        return 1 if self.op == "quantize_int8" else self.elem_bytes
+
     def algorithmic_bytes(self) -> int:
-        """One read of x, one write of y, and each parameter vector read once."""
+        """One read of every row input, one write of the output, each parameter
+        vector read once and the per-row outputs written once."""
         b = self.elem_bytes
-        return self.rows * self.cols * 2 * b + self.cols * b * N_PARAMS[self.op]
+        return (self.rows * self.cols * (self.inputs * b + self.out_bytes) + self.cols * b * N_PARAMS[self.op]
+                + self.rows * ROW_OUT_BYTES.get(self.op, 0))
 
     def with_shape(self, rows: int, cols: int, name: Optional[str] = None) -> "Workload":
         return dataclasses.replace(self, rows=rows, cols=cols, name=name or self.name)
@@ -79,10 +108,33 @@ NAMED: Dict[str, Workload] = {
                  x_dist="outliers", outlier_prob=0.01, outlier_scale=50.0, eps=1e-6),
         Workload("softmax_f32_256x262144", "softmax", "f32", 256, 262144, seed=4,
                  x_dist="row_offset", x_scale=4.0, row_offset=50.0),
+        Workload("softmax_bwd_f32_4096x65536", "softmax_bwd", "f32", 4096, 65536, seed=5),
+        Workload("layernorm_bwd_f32_2048x65536", "layernorm_bwd", "f32", 2048, 65536, seed=6,
+                 x_dist="scaled_shifted", x_scale=3.0, x_shift=0.5, eps=1e-5),
+        Workload("quantize_int8_f32_4096x65536", "quantize_int8", "f32", 4096, 65536, seed=7,
+                 x_dist="outliers", outlier_prob=0.01, outlier_scale=50.0),
     ]
 }
 CONFIG_ORDER = ["softmax_f32_64x4096", "layernorm_bf16_4096x8192",
                 "rmsnorm_bf16_1024x65536", "softmax_f32_256x262144"]
+NEXT_ORDER = ["softmax_bwd_f32_4096x65536", "layernorm_bwd_f32_2048x65536", "quantize_int8_f32_4096x65536"]
+NEXT_COLS = (4096, 8192, 16384, 32768, 65536)
+NEXT_ROWS = {"softmax_bwd": 4096, "layernorm_bwd": 2048, "quantize_int8": 4096}
+
+
+def next_points() -> List[Workload]:
+    """The paper's width grid for the three further workloads (fp32; 4096 rows,
+    2048 for LayerNorm backward; the named workloads' distributions)."""
+    pts = []
+    idx = 0
+    for name in NEXT_ORDER:
+        base = NAMED[name]
+        for cols in NEXT_COLS:
+            rows = NEXT_ROWS[base.op]
+            pts.append(dataclasses.replace(base, name="next%02d_%s_f32_%dx%d" % (idx, base.op, rows, cols),
+                                           rows=rows, cols=cols, seed=3000 + idx))
+            idx += 1
+    return pts
 
 
 CALIB_BYTES = (8 << 20, 64 << 20, 512 << 20, 2048 << 20)
@@ -96,7 +148,7 @@ def calibration_points() -> List[Workload]:
     256 MiB and 1 GiB)."""
     pts = []
     idx = 0
-    for op in OPS:
+    for op in FWD_OPS:
         for dt in DTYPES:
             for cols in CALIB_COLS:
                 for nbytes in CALIB_BYTES:
@@ -107,11 +159,38 @@ def calibration_points() -> List[Workload]:
     return pts
 
 
+CALIB_NEXT_ROWS = (512, 1536, 6144, 16384)
+CALIB_NEXT_MAX_BYTES = 4 << 30  # of x
+
+
+def calibration_points_next() -> List[Workload]:
+    """Calibration shapes of the three further workloads: each supported dtype
+    at every power-of-two width from 1024 to 262144, at row counts that bracket
+    (and never equal) the 2048 and 4096 rows of their width grid, x at most
+    4 GiB."""
+    pts = []
+    idx = 0
+    for name in NEXT_ORDER:
+        base = NAMED[name]
+        for dt in DTYPES:
+            if (base.op, dt) not in SUPPORTED:
+                continue
+            for cols in CALIB_COLS:
+                for rows in CALIB_NEXT_ROWS:
+                    if rows * cols * ELEM_BYTES[dt] > CALIB_NEXT_MAX_BYTES:
+                        continue
+                    pts.append(dataclasses.replace(
+                        base, name="calibn%03d_%s_%s_%dx%d" % (idx, base.op, dt, rows, cols), dtype=dt,
+                        rows=rows, cols=cols, seed=4000 + idx))
+                    idx += 1
+    return pts
+
+
 def sweep_points() -> List[Workload]:
     """The 90-point crossover sweep, in a fixed order (op, dtype, cols, bytes)."""
     pts = []
     idx = 0
-    for op in OPS:
+    for op in FWD_OPS:
         for dt in DTYPES:
             for cols in SWEEP_COLS:
                 for nbytes in SWEEP_BYTES:
@@ -145,6 +224,7 @@ class HostInputs:
     gamma: Optional[np.ndarray]
     beta: Optional[np.ndarray]
     eps: float
+    dy: Optional[np.ndarray] = None
 
 
 def _store(a: np.ndarray, dtype: str) -> np.ndarray:
@@ -168,15 +248,48 @@ def generate(w: Workload) -> HostInputs:
         x += off
     elif w.x_dist != "normal":
         raise ValueError("unknown x_dist %r" % w.x_dist)
-    gamma = beta = None
-    if w.op in ("layernorm", "rmsnorm"):
+    gamma = beta = dy = None
+    if N_PARAMS[w.op] >= 1:
         gamma = rng.uniform(0.5, 1.5, size=w.cols).astype(np.float32)
-    if w.op == "layernorm":
+    if N_PARAMS[w.op] >= 2:
         beta = (rng.standard_normal(w.cols, dtype=np.float32) * np.float32(0.1)).astype(np.float32)
+    if w.inputs >= 2:
+        dy = rng.standard_normal(shape, dtype=np.float32)
     return HostInputs(w, _store(x, w.dtype),
                       None if gamma is None else _store(gamma, w.dtype),
                       None if beta is None else _store(beta, w.dtype),
-                      float(np.float32(w.eps)))
+                      float(np.float32(w.eps)),
+                      None if dy is None else _store(dy, w.dtype))
+
+
+# ---------------------------------------------------------------------------
+# device copies (torch is imported only here)
+# ---------------------------------------------------------------------------
+def to_device(inp: HostInputs) -> dict:
+    """The inputs as device tensors: {x, dy, gamma, beta} (absent ones None)."""
+    import torch
+
+    def dev(a):
+        if a is None:
+            return None
+        if inp.workload.dtype == "bf16":
+            return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(a).cuda()
+    return {"x": dev(inp.x), "dy": dev(inp.dy), "gamma": dev(inp.gamma), "beta": dev(inp.beta)}
+
+
+def alloc_outputs(w: Workload, t: dict) -> dict:
+    """Adds the output tensors y (int8 codes for quantization) and row_out
+    (the per-row scale, quantization only) to the operand mapping t."""
+    import torch
+    x = t["x"]
+    if w.op == "quantize_int8":
+        t["y"] = torch.empty(x.shape, dtype=torch.int8, device=x.device)
+        t["row_out"] = torch.empty(x.shape[0], dtype=torch.float32, device=x.device)
+    else:
+        t["y"] = torch.empty_like(x)
+        t["row_out"] = None
+    return t
 
 
 def custom(op: str, dtype: str, rows: int, cols: int, seed: int, **kw) -> Workload:
