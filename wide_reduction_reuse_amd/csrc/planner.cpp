@@ -197,7 +197,8 @@ struct Model {
 Model model_of(const Calibration &c)
 {
     Model m;
-    m.stream_gbs = c.stream_gbs > 0 ? c.stream_gbs : 0.8 * c.device.hbm_peak_gbs;
+    m.stream_gbs = c.peak_bandwidth ? c.device.hbm_peak_gbs
+                                    : (c.stream_gbs > 0 ? c.stream_gbs : 0.8 * c.device.hbm_peak_gbs);
     m.per_cu_gbs = c.per_cu_gbs > 0 ? c.per_cu_gbs : 50.0;
     m.launch_us = c.launch_us >= 0 ? c.launch_us : 4.0;
     m.exchange_us = c.exchange_us >= 0 ? c.exchange_us : 3.0;
@@ -647,6 +648,9 @@ bool parse_calibration(const std::string &text, Calibration *out)
     get("launch_us", &c.launch_us);
     get("exchange_us", &c.exchange_us);
     get("reread_hit_l2", &c.reread_hit_l2);
+    double peak = 0.0;
+    get("model_peak_bandwidth", &peak);
+    c.peak_bandwidth = peak != 0.0;
     const char *effs[3] = {"single_eff", "reread_eff", "split_eff"};
     double(*dst[3])[kNumOps][2] = {&c.single_eff, &c.reread_eff, &c.split_eff};
     for (int k = 0; k < 3; ++k)

@@ -64,6 +64,9 @@ struct Calibration {
     double launch_us = -1.0;        // fixed cost of a launch (empty grid time)
     double exchange_us = -1.0;      // one split-row exchange round (control kernel excess)
     double reread_hit_l2 = -1.0;    // fraction of a reread served on chip when the working set fits L2
+    // ablation of the paper's Table V (first row): price streaming at the
+    // device's peak HBM bandwidth instead of an achieved rate
+    bool peak_bandwidth = false;
     // per-(op, dtype) multipliers on the streaming time, fitted to path-1 and path-3 timings
     double single_eff[kNumOps][2] = {{-1, -1}, {-1, -1}, {-1, -1}, {-1, -1}, {-1, -1}, {-1, -1}};
     double reread_eff[kNumOps][2] = {{-1, -1}, {-1, -1}, {-1, -1}, {-1, -1}, {-1, -1}, {-1, -1}};
