@@ -113,3 +113,32 @@ def test_calibration_from_environment(tmp_path):
     out = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=120)
     assert out.returncode == 0, out.stderr
     assert out.stdout.split() == ["2", "2", "256", "8"]
+
+
+def test_crossover_width_report():
+    # a series of widths where splitting is measured to pay from 16384 on;
+    # the report finds the first width from which the split stays ahead
+    from wide_reduction_reuse_amd import selector_eval as E
+    records, rows = [], []
+    for cols, meas, pred in [(4096, False, False), (8192, True, False), (16384, True, True), (32768, True, True)]:
+        records.append({"op": "softmax", "dtype": "f32", "rows": 64, "cols": cols, "workload": "next_x"})
+        rows.append({"split_ok": meas == pred, "split_meas": meas, "split_pred": pred})
+    rep = E.crossover(records, rows)
+    assert len(rep) == 1
+    assert rep[0]["measured"] == 8192 and rep[0]["predicted"] == 16384 and rep[0]["steps_off"] == 1
+    # a split that never pays has no crossover
+    rows2 = [dict(r, split_meas=False, split_pred=False) for r in rows]
+    rep = E.crossover(records, rows2)
+    assert rep[0]["measured"] is None and rep[0]["steps_off"] == 0
+
+
+def test_peak_bandwidth_ablation_changes_only_the_rate(tmp_path):
+    # the ablation prices the stream at the device peak: every estimate can
+    # only get faster than at a lower achieved rate
+    C.credit_load_calibration(_write(tmp_path, [], "achieved.json"))
+    slow = C.credit_select_path("softmax", "f32", 4096, 4096).predicted_us[0]
+    p = tmp_path / "peak.json"
+    p.write_text(json.dumps({"version": 2, "stream_gbs": 1000.0, "model_peak_bandwidth": 1}))
+    C.credit_load_calibration(str(p))
+    fast = C.credit_select_path("softmax", "f32", 4096, 4096).predicted_us[0]
+    assert fast < slow
