@@ -84,7 +84,7 @@ def sweep_shape(w: W.Workload, steps: int, warmup: int, flush_buf) -> dict:
     return rec
 
 
-def points(which: str, ops=None):
+def points(which: str, ops=None, min_cols: int = 0):
     pts = []
     if which in ("named", "all"):
         pts += [W.NAMED[n] for n in W.CONFIG_ORDER + W.NEXT_ORDER]
@@ -98,13 +98,14 @@ def points(which: str, ops=None):
         pts += W.calibration_points_next()
     if ops:
         pts = [p for p in pts if p.op in ops]
-    return pts
+    return [p for p in pts if p.cols >= min_cols]
 
 
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--points", default="named", choices=("named", "sweep", "next", "all", "calib", "calib_next", "calib_all"))
     ap.add_argument("--ops", nargs="*", default=None)
+    ap.add_argument("--min-cols", type=int, default=0, help="only shapes at least this wide")
     ap.add_argument("--out", default="-")
     ap.add_argument("--steps", type=int, default=15)
     ap.add_argument("--warmup", type=int, default=3)
@@ -118,7 +119,7 @@ def main(argv=None) -> int:
     flush_buf = flush_buffer()
     out = sys.stdout if a.out == "-" else open(a.out, "w")
     t0 = time.time()
-    for w in points(a.points, a.ops):
+    for w in points(a.points, a.ops, a.min_cols):
         rec = sweep_shape(w, a.steps, a.warmup, flush_buf)
         out.write(json.dumps(rec) + "\n")
         out.flush()
