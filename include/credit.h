@@ -252,10 +252,13 @@ credit_status_t credit_run_plan_timed(credit_op_t op, const credit_operands_t *o
  * Work-free control kernel (Sec. III-D, the control that isolates launch,
  * scheduling, occupancy and synchronization costs): the split-row kernel of
  * `plan` with the same grid, tickets and exchange but no row loads or output
- * stores.  plan->path must be CREDIT_PATH_SPLIT_ROW.
+ * stores.  plan->path must be CREDIT_PATH_SPLIT_ROW.  start_event and
+ * stop_event (hipEvent_t, each may be NULL) receive the dispatch timestamps
+ * as in credit_run_plan_timed.  Its time at M rows minus its time at one row
+ * per cluster is the control overhead T_ctrl of Sec. III-D, Eq. 8.
  */
 credit_status_t credit_control(credit_op_t op, int64_t rows, int64_t cols, credit_dtype_t dt,
-                               const credit_plan_t *plan, void *stream);
+                               const credit_plan_t *plan, void *start_event, void *stop_event, void *stream);
 
 /*
  * Measurement helpers.  credit_copy: 128-bit streaming copy of `bytes` bytes

@@ -158,8 +158,11 @@ def test_misc_entry_points_validate():
     assert L.credit_flush(None, 16, None) == 1
     assert L.credit_flush(A, 0, None) == 0
     plan = C.Plan.make(C.PATH_SINGLE_WG, 1, 64, 1, 16)
-    assert L.credit_control(0, 4, 64, 0, ctypes.byref(plan), None) == 1  # control needs a split plan
-    assert L.credit_control(0, 4, 64, 0, None, None) == 1
+    assert L.credit_control(0, 4, 64, 0, ctypes.byref(plan), None, None, None) == 1  # control needs a split plan
+    assert L.credit_control(0, 4, 64, 0, None, None, None, None) == 1
+    split = C.Plan.make(C.PATH_SPLIT_ROW, 2, 256, 8, 16)
+    assert L.credit_control(0, 0, 4096, 0, ctypes.byref(split), None, None, None) == 0  # rows = 0: no-op
+    assert L.credit_control(4, 4, 4096, 1, ctypes.byref(split), None, None, None) == 2  # no bf16 LN backward
 
 
 def test_selector_legality_on_cpu():

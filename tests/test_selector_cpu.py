@@ -142,3 +142,9 @@ def test_peak_bandwidth_ablation_changes_only_the_rate(tmp_path):
     C.credit_load_calibration(str(p))
     fast = C.credit_select_path("softmax", "f32", 4096, 4096).predicted_us[0]
     assert fast < slow
+
+
+def test_control_fit_recovers_launch_and_per_wave_cost():
+    from wide_reduction_reuse_amd.ctrlbench import fit_line
+    a, b = fit_line([1, 2, 4, 8, 16], [3.0 + 0.5 * w for w in (1, 2, 4, 8, 16)])
+    assert abs(a - 3.0) < 1e-12 and abs(b - 0.5) < 1e-12

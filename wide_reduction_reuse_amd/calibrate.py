@@ -7,7 +7,10 @@ With --run it first times every legal plan on the calibration shapes
 widths at 8, 64, 512 and 2048 MiB, sizes the scored sweep does not use; and
 workloads.calibration_points_next(): the three further workloads at row counts
 their width grid does not use) with the sweep driver and writes the records to
-the (one) --sweep file.  Several --sweep files are merged.  It then builds the table
+the (one) --sweep file.  Several --sweep files are merged.  --ctrl FILE (the
+output of ctrlbench.py; with --run it is measured first) adds the analytic
+model's launch and per-row-wave exchange costs, fitted to the work-free
+control kernel.  It then builds the table
 credit_load_calibration reads: for each (op, dtype, cols) and each candidate
 plan, the median kernel time at every calibrated row count.  The selector
 interpolates these in (log rows, log time) for the rows it is asked about
@@ -61,6 +64,7 @@ def main(argv=None) -> int:
     ap.add_argument("--sweep", nargs="*", default=None, help="calibration sweep records (JSON lines)")
     ap.add_argument("--run", action="store_true", help="time the calibration shapes first (needs a GPU)")
     ap.add_argument("--steps", type=int, default=15)
+    ap.add_argument("--ctrl", default=None, help="control-kernel fit (ctrlbench.py output)")
     a = ap.parse_args(argv)
     if a.run:
         from . import sweep
@@ -69,6 +73,11 @@ def main(argv=None) -> int:
         rc = sweep.main(["--points", "calib_all", "--out", a.sweep[0], "--steps", str(a.steps)])
         if rc:
             return rc
+        if a.ctrl:
+            from . import ctrlbench
+            rc = ctrlbench.main(["--out", a.ctrl, "--steps", str(a.steps)])
+            if rc:
+                return rc
     if not a.sweep:
         ap.error("--sweep FILE is required")
     records = [json.loads(l) for path in a.sweep for l in open(path) if l.strip()]
@@ -78,11 +87,20 @@ def main(argv=None) -> int:
     dev = device_info()
     cal = {"version": 2, "source": "median kernel times of every legal plan on %d calibration shapes" % len(records),
            "stream_gbs": round(stream, 1), "table": build_table(records)}
+    if a.ctrl:
+        summ = [json.loads(l) for l in open(a.ctrl) if l.strip() and json.loads(l).get("summary")]
+        if not summ:
+            ap.error("%s has no summary line" % a.ctrl)
+        cal["launch_us"] = summ[-1]["launch_us"]
+        cal["exchange_us"] = summ[-1]["exchange_us"]
     if dev.get("cus"):
         cal["device"] = {"cus": dev["cus"]}
     with open(a.out, "w") as f:
         f.write("{\n")
         f.write(' "version": 2,\n "source": %s,\n "stream_gbs": %s,\n' % (json.dumps(cal["source"]), cal["stream_gbs"]))
+        for k in ("launch_us", "exchange_us"):
+            if k in cal:
+                f.write(' "%s": %s,\n' % (k, cal[k]))
         if "device" in cal:
             f.write(' "device": %s,\n' % json.dumps(cal["device"]))
         f.write(' "table": [\n')

@@ -103,7 +103,7 @@ def lib() -> ctypes.CDLL:
         "credit_run_plan": [i32, ctypes.POINTER(Operands), i64, i64, f32, i32, ctypes.POINTER(Plan), vp],
         "credit_run_plan_timed": [i32, ctypes.POINTER(Operands), i64, i64, f32, i32, ctypes.POINTER(Plan), vp, vp,
                                   vp],
-        "credit_control": [i32, i64, i64, i32, ctypes.POINTER(Plan), vp],
+        "credit_control": [i32, i64, i64, i32, ctypes.POINTER(Plan), vp, vp, vp],
         "credit_copy": [vp, vp, i64, vp, vp, vp],
         "credit_flush": [vp, i64, vp],
         "credit_load_calibration": [ctypes.c_char_p],
@@ -306,10 +306,14 @@ def credit_run_plan_timed(op, plan: Plan, t, start_event: int, stop_event: int, 
     return t["y"]
 
 
-def credit_control(op, rows: int, cols: int, dtype, plan: Plan, stream=None) -> None:
+def credit_control(op, rows: int, cols: int, dtype, plan: Plan, start_event: Optional[int] = None,
+                   stop_event: Optional[int] = None, stream=None) -> None:
+    """The work-free control kernel of a split plan; the events (raw hipEvent_t
+    handles, optional) take its dispatch timestamps."""
     op = OPS[op] if isinstance(op, str) else int(op)
     dt = DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
-    _check(lib().credit_control(op, rows, cols, dt, ctypes.byref(plan), _stream(stream)), "credit_control")
+    _check(lib().credit_control(op, rows, cols, dt, ctypes.byref(plan), ctypes.c_void_p(start_event),
+                                ctypes.c_void_p(stop_event), _stream(stream)), "credit_control")
 
 
 def credit_copy(src, dst, start_event: Optional[int] = None, stop_event: Optional[int] = None,

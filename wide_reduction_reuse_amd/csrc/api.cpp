@@ -751,7 +751,7 @@ credit_status_t credit_run_plan_timed(credit_op_t op, const credit_operands_t *o
 }
 
 credit_status_t credit_control(credit_op_t op, int64_t rows, int64_t cols, credit_dtype_t dt,
-                               const credit_plan_t *plan, void *stream)
+                               const credit_plan_t *plan, void *start_event, void *stop_event, void *stream)
 {
     if (plan == nullptr || rows < 0 || cols < 1)
         return CREDIT_ERR_INVALID_ARG;
@@ -762,8 +762,11 @@ credit_status_t credit_control(credit_op_t op, int64_t rows, int64_t cols, credi
         return CREDIT_ERR_INVALID_ARG;
     if (rows == 0)
         return CREDIT_OK;
+    LaunchEvents ev;
+    ev.start = static_cast<hipEvent_t>(start_event);
+    ev.stop = static_cast<hipEvent_t>(stop_event);
     return run_plan_checked(op, operands(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr), rows, cols, 0.0f, dt,
-                            *plan, static_cast<hipStream_t>(stream), true);
+                            *plan, static_cast<hipStream_t>(stream), true, ev);
 }
 
 credit_status_t credit_copy(const void *src, void *dst, int64_t bytes, void *start_event, void *stop_event,

@@ -527,7 +527,8 @@ __global__ __launch_bounds__(BLOCK) void single_wg_kernel(RowArgs a)
 // ---------------------------------------------------------------------------
 // Path 2: P workgroups per row (see the header comment).  CONTROL = true is the
 // work-free control kernel: identical launch shape, tickets, exchange and
-// reductions, but no row loads and no output stores.
+// reductions (over zero tiles), but no access to rows, parameters or outputs
+// at all (the control launch passes null pointers for them).
 // ---------------------------------------------------------------------------
 template <OpKind OP, class T, int VB, int BLOCK, int IT, bool CONTROL>
 __global__ __launch_bounds__(BLOCK) void split_kernel(SplitArgs a)
@@ -562,20 +563,29 @@ __global__ __launch_bounds__(BLOCK) void split_kernel(SplitArgs a)
     const int kv = count_valid<IT, kWave>(ns, pos);
     uint64_t *cslots = a.slots + k * 2 * P * Q;
 
-    // CONTROL: a zero-length source, so every load returns zero without
-    // touching memory, and a zero-length destination that drops every store
-    const int64_t nload = CONTROL ? 0 : ns;
     Tile<T, VB, IT> t[Op::kIn];
-    load_tile<T, VB, IT, kWave>(t, row_srcs<OP, VB>(a.r, k, nv, v0, k < a.r.rows ? nload : 0), pos);
     PC pc;
-    pc.init(span<VB>(a.r.gamma, v0, ns), span<VB>(a.r.beta, v0, ns), pos, lds_params, tid, BLOCK);
-    if constexpr (PC::kMode == kParamLds)
-        __syncthreads();
+    if constexpr (CONTROL) {
+#pragma unroll
+        for (int i = 0; i < Op::kIn; ++i)
+#pragma unroll
+            for (int j = 0; j < IT; ++j)
+                t[i].v[j] = RawVec<VB>{};
+    } else {
+        load_tile<T, VB, IT, kWave>(t, row_srcs<OP, VB>(a.r, k, nv, v0, k < a.r.rows ? ns : 0), pos);
+        pc.init(span<VB>(a.r.gamma, v0, ns), span<VB>(a.r.beta, v0, ns), pos, lds_params, tid, BLOCK);
+        if constexpr (PC::kMode == kParamLds)
+            __syncthreads();
+    }
 
     uint32_t it = 0;
     for (int64_t row = k; row < a.r.rows; row += a.clusters, ++it) {
         const int64_t next = row + a.clusters;
-        const Partial wp = tile_partial<OP, T, VB, IT, BLOCK, kOwnerSlice>(t, kv, pc, pos);
+        Partial wp;
+        if constexpr (CONTROL)
+            wp = Op::template wave_partial<T, VB, IT>(t, kv);
+        else
+            wp = tile_partial<OP, T, VB, IT, BLOCK, kOwnerSlice>(t, kv, pc, pos);
         const Partial sp = block_combine<OP, NW>(wp, sh);
 
         // publish this slice's partial, then gather all P partials of the row
@@ -603,11 +613,16 @@ __global__ __launch_bounds__(BLOCK) void split_kernel(SplitArgs a)
             parts[i] = peer[i];
         const Partial rp = Op::template merge<kMaxSplit>(parts, P);
         const Coef cf = Op::template finalize<T>(rp, wp, a.r.cols, a.r.eps);
-        store_row_value<OP>(a.r, row, cf, !CONTROL && c == 0 && tid == 0);
-        const auto nsrc = row_srcs<OP, VB>(a.r, next, nv, v0, next < a.r.rows ? nload : 0);
-        store_tile<OP, T, VB, IT, BLOCK, kOwnerSlice>(t, span<VBO>(a.r.y, row * nv + v0, nload), pc, pos, cf,
-                                                      nsrc);
-        load_next<OP, T, VB, IT, BLOCK, kOwnerSlice>(t, nsrc, pos);
+        if constexpr (CONTROL) {
+            (void)cf;
+            (void)next;
+        } else {
+            store_row_value<OP>(a.r, row, cf, c == 0 && tid == 0);
+            const auto nsrc = row_srcs<OP, VB>(a.r, next, nv, v0, next < a.r.rows ? ns : 0);
+            store_tile<OP, T, VB, IT, BLOCK, kOwnerSlice>(t, span<VBO>(a.r.y, row * nv + v0, ns), pc, pos, cf,
+                                                          nsrc);
+            load_next<OP, T, VB, IT, BLOCK, kOwnerSlice>(t, nsrc, pos);
+        }
         // (no barrier needed before the next iteration rewrites sh or peer:
         // every wave has read sh before the exchange barrier above and reads
         // peer before it reaches the next block_combine barrier)
