@@ -113,14 +113,30 @@ struct Srcs {
     rsrc_t r[NI];
 };
 
+// Scheduling-barrier mask that lets every instruction class cross except
+// vector-memory reads: ALU 0x1, VALU 0x2, SALU 0x4, MFMA 0x8, VMEM write 0x40,
+// DS 0x80, DS read 0x100, DS write 0x200, transcendental 0x400.
+constexpr int kLoadOrderBarrier = 0x7CF;
+
+// One-input tiles are loaded in the order the reduction consumes them
+// (vector k = 0, 1, ...): with one in-order counter for all of a wave's memory
+// operations, a vector issued early can be waited for while later ones are
+// still in flight.  The scheduling barriers keep the compiler from reordering
+// the loads (it otherwise issued them in nearly reverse order).  Two-input
+// tiles (x, dy) are left to the compiler, input by input: pinning their order
+// (either interleaved by vector or input by input) measured 1-3% slower on
+// MI355X for softmax and LayerNorm backward.
 template <class T, int VB, int IT, int G, int NI>
 __device__ __forceinline__ void load_tile(Tile<T, VB, IT> (&t)[NI], const Srcs<NI> &src, int pos)
 {
 #pragma unroll
     for (int i = 0; i < NI; ++i)
 #pragma unroll
-        for (int k = 0; k < IT; ++k)
+        for (int k = 0; k < IT; ++k) {
             t[i].v[k] = buf_load<VB, kStream>(src.r[i], static_cast<uint32_t>(pos + k * G) * VB);
+            if constexpr (NI == 1)
+                __builtin_amdgcn_sched_barrier(kLoadOrderBarrier);
+        }
 }
 
 // h for one vector: in[i] are the held (or reread) input vectors, g and b the
@@ -281,7 +297,8 @@ struct ParamCache {
 // with no gain: the masks are register selects.)
 template <OpKind OP, class T, int VB, int IT, int W, int OWNER>
 __device__ __forceinline__ typename OpTraits<OP>::Partial tile_partial(
-    Tile<T, VB, IT> (&t)[OpTraits<OP>::kIn], int kv, const ParamCache<OP, T, VB, IT, W, OWNER> &pc, int pos)
+    Tile<T, VB, IT> (&t)[OpTraits<OP>::kIn], int kv, const ParamCache<OP, T, VB, IT, W, OWNER> &pc, int pos,
+    Local &loc)
 {
     using Op = OpTraits<OP>;
     if constexpr (Op::kParamsInReduce) {
@@ -292,20 +309,25 @@ __device__ __forceinline__ typename OpTraits<OP>::Partial tile_partial(
             Op::template prepare<T, VB, IT>(t, k, g);
         }
     }
-    return Op::template wave_partial<T, VB, IT>(t, kv);
+    return Op::template wave_partial<T, VB, IT>(t, kv, loc);
 }
 
 // Whether the output loop loads the next row into the registers it frees
-// ("rolling"), for owners that loop over rows.  Measured on MI355X it did not
-// pay: one-row-per-owner path 1 launches were as fast or faster than rolling
-// persistent ones, and the split kernel streamed about 5% slower with it, so
-// it is off; the code path is kept for kernels where it is switched on.
-constexpr bool kRollNextRow = false;
-
-template <int MODE>
+// ("rolling").  A wave has one in-order counter for its loads and stores, so
+// when the next row's loads are issued after all of this row's stores, even
+// its first vector can only be used once every store has drained.  Rolling
+// issues load k right after store k, so the grouped reductions of the next row
+// start while the stores still drain.  Measured on MI355X with the ordered
+// loads and grouped softmax-family partials, the split kernel's best plan for
+// 256 x 262144 fp32 softmax gained 6% and a 4096 x 65536 int8 quantization
+// plan 4%; the two-input operators (softmax and LayerNorm backward) lost 3-5%
+// at P = 4 and 8 and gained nothing at P = 2, and path 1 gained nothing (its
+// owners mostly handle one row each).  So only one-input split slices roll.
+// kParamDirect needs the freed registers for parameters.
+template <int MODE, int OWNER, int NI>
 constexpr bool rolls()
 {
-    return kRollNextRow && MODE != kParamDirect;
+    return OWNER == kOwnerSlice && NI == 1 && MODE != kParamDirect;
 }
 
 // Apply h to the held tile and write it out; dst, and the parameter
@@ -351,11 +373,13 @@ __device__ __forceinline__ void store_tile(Tile<T, VB, IT> (&t)[OpTraits<OP>::kI
 #pragma unroll
             for (int i = 0; i < NI; ++i)
                 in[i] = t[i].v[k];
-            buf_store<VBO, kStreamStore>(apply_vec<OP, T, VB, false>(in, g, b, c), dst, ooff);
-            if constexpr (rolls<MODE>())
+            buf_store<VBO, kStreamStore>(apply_vec<OP, T, VB, false>(in, g, b, vec_coef<OP, T, IT>(c, k)), dst, ooff);
+            if constexpr (rolls<MODE, OWNER, NI>())
 #pragma unroll
-                for (int i = 0; i < NI; ++i)
+                for (int i = 0; i < NI; ++i) {
                     t[i].v[k] = buf_load<VB, kStream>(next.r[i], off);
+                    __builtin_amdgcn_sched_barrier(kLoadOrderBarrier);  // keeps the loads in order
+                }
         }
     } else {
         constexpr int GP = param_group<IT, VB, NP>();
@@ -378,7 +402,8 @@ __device__ __forceinline__ void store_tile(Tile<T, VB, IT> (&t)[OpTraits<OP>::kI
 #pragma unroll
                 for (int i = 0; i < NI; ++i)
                     in[i] = t[i].v[kb + j];
-                buf_store<VBO, kStreamStore>(apply_vec<OP, T, VB, false>(in, g[j], b[j], c), dst, ooff);
+                buf_store<VBO, kStreamStore>(apply_vec<OP, T, VB, false>(in, g[j], b[j], vec_coef<OP, T, IT>(c, kb + j)), dst,
+                                             ooff);
             }
         }
     }
@@ -389,7 +414,7 @@ template <OpKind OP, class T, int VB, int IT, int W, int OWNER>
 __device__ __forceinline__ void load_next(Tile<T, VB, IT> (&t)[OpTraits<OP>::kIn],
                                           const Srcs<OpTraits<OP>::kIn> &next, int pos)
 {
-    if constexpr (!rolls<ParamCache<OP, T, VB, IT, W, OWNER>::kMode>())
+    if constexpr (!rolls<ParamCache<OP, T, VB, IT, W, OWNER>::kMode, OWNER, OpTraits<OP>::kIn>())
         load_tile<T, VB, IT, kWave>(t, next, pos);
 }
 
@@ -476,8 +501,9 @@ __global__ __launch_bounds__(kWave *kWaveRowsPerWg) void single_wave_kernel(RowA
     const int kv = count_valid<IT, kWave>(nv, lane);
     for (; row < a.rows; row += waves) {
         const int64_t next = row + waves;
-        const auto wp = tile_partial<OP, T, VB, IT, kWave, kOwnerWaves>(t, kv, pc, lane);
-        const Coef c = Op::template finalize<T>(wp, wp, a.cols, a.eps);
+        Local loc;
+        const auto wp = tile_partial<OP, T, VB, IT, kWave, kOwnerWaves>(t, kv, pc, lane, loc);
+        const Coef c = Op::template finalize<T>(wp, loc, a.cols, a.eps);
         store_row_value<OP>(a, row, c, lane == 0);
         const auto nsrc = row_srcs<OP, VB>(a, next, nv, 0, next < a.rows ? nv : 0);
         store_tile<OP, T, VB, IT, kWave, kOwnerWaves>(t, span<VBO>(a.y, row * nv, nv), pc, lane, c, nsrc);
@@ -512,9 +538,10 @@ __global__ __launch_bounds__(BLOCK) void single_wg_kernel(RowArgs a)
     const int kv = count_valid<IT, kWave>(nv, pos);
     for (; row < a.rows; row += gridDim.x) {
         const int64_t next = row + gridDim.x;
-        const auto wp = tile_partial<OP, T, VB, IT, BLOCK, kOwnerRow>(t, kv, pc, pos);
+        Local loc;
+        const auto wp = tile_partial<OP, T, VB, IT, BLOCK, kOwnerRow>(t, kv, pc, pos, loc);
         const auto rp = block_combine<OP, NW>(wp, sh);
-        const Coef c = Op::template finalize<T>(rp, wp, a.cols, a.eps);
+        const Coef c = Op::template finalize<T>(rp, loc, a.cols, a.eps);
         store_row_value<OP>(a, row, c, tid == 0);
         const auto nsrc = row_srcs<OP, VB>(a, next, nv, 0, next < a.rows ? nv : 0);
         store_tile<OP, T, VB, IT, BLOCK, kOwnerRow>(t, span<VBO>(a.y, row * nv, nv), pc, pos, c, nsrc);
@@ -578,14 +605,20 @@ __global__ __launch_bounds__(BLOCK) void split_kernel(SplitArgs a)
             __syncthreads();
     }
 
-    uint32_t it = 0;
-    for (int64_t row = k; row < a.r.rows; row += a.clusters, ++it) {
+    // One row of this slice: reduce, exchange, write (and, rolling, load the
+    // next row).  When the slice rolls, the first row is peeled off the loop
+    // so that every path into the loop ends in the same interleaved store/load
+    // sequence, which lets the compiler wait for each held vector precisely
+    // instead of conservatively (measured: 3% on RMSNorm bf16 split plans; the
+    // kernels that do not roll gain nothing from it and are not peeled).
+    auto step = [&](int64_t row, uint32_t it) __attribute__((always_inline)) {
         const int64_t next = row + a.clusters;
         Partial wp;
+        Local loc;
         if constexpr (CONTROL)
-            wp = Op::template wave_partial<T, VB, IT>(t, kv);
+            wp = Op::template wave_partial<T, VB, IT>(t, kv, loc);
         else
-            wp = tile_partial<OP, T, VB, IT, BLOCK, kOwnerSlice>(t, kv, pc, pos);
+            wp = tile_partial<OP, T, VB, IT, BLOCK, kOwnerSlice>(t, kv, pc, pos, loc);
         const Partial sp = block_combine<OP, NW>(wp, sh);
 
         // publish this slice's partial, then gather all P partials of the row
@@ -612,7 +645,7 @@ __global__ __launch_bounds__(BLOCK) void split_kernel(SplitArgs a)
         for (int i = 0; i < kMaxSplit; ++i)
             parts[i] = peer[i];
         const Partial rp = Op::template merge<kMaxSplit>(parts, P);
-        const Coef cf = Op::template finalize<T>(rp, wp, a.r.cols, a.r.eps);
+        const Coef cf = Op::template finalize<T>(rp, loc, a.r.cols, a.r.eps);
         if constexpr (CONTROL) {
             (void)cf;
             (void)next;
@@ -623,9 +656,21 @@ __global__ __launch_bounds__(BLOCK) void split_kernel(SplitArgs a)
                                                           nsrc);
             load_next<OP, T, VB, IT, BLOCK, kOwnerSlice>(t, nsrc, pos);
         }
-        // (no barrier needed before the next iteration rewrites sh or peer:
-        // every wave has read sh before the exchange barrier above and reads
-        // peer before it reaches the next block_combine barrier)
+        // (no barrier needed before the next row rewrites sh or peer: every
+        // wave has read sh before the exchange barrier above and reads peer
+        // before it reaches the next block_combine barrier)
+    };
+    if constexpr (rolls<PC::kMode, kOwnerSlice, Op::kIn>()) {
+        if (k < a.r.rows) {
+            step(k, 0u);
+            uint32_t it = 1;
+            for (int64_t row = k + a.clusters; row < a.r.rows; row += a.clusters, ++it)
+                step(row, it);
+        }
+    } else {
+        uint32_t it = 0;
+        for (int64_t row = k; row < a.r.rows; row += a.clusters, ++it)
+            step(row, it);
     }
 }
 

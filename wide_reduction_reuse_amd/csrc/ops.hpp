@@ -54,11 +54,28 @@ struct Part {
     float v[Q < 3 ? 3 : Q];
 };
 
-// Coefficients of the output function h, identical in every thread of a row;
-// their meaning is given per operator.
+// Coefficients of the output function h, their meaning given per operator.
+// k is the same in every thread of a row (bar the softmax family's k0, see
+// vec_coef); f holds per-thread scales of the vector groups of a held tile.
 struct Coef {
     float k[4];
+    float f[4];
 };
+
+// Per-thread state that a held tile's partial leaves for the output: the
+// softmax family keeps the maximum of each group of the thread's vectors
+// (ref_groups of them), to which the fp32 tile's exponentials are relative.
+struct Local {
+    float m[4];
+};
+
+// Vector groups of a held tile of IT vectors reduced one after another (see
+// softmax_groups).
+template <int IT>
+constexpr int ref_groups()
+{
+    return IT < 4 ? IT : 4;
+}
 
 // A register tile: IT vectors of VB bytes per thread.  Vector k of a thread at
 // position `pos` in a group of G threads is vector (first + pos + k*G) of the
@@ -101,9 +118,114 @@ __device__ __forceinline__ float exp_for(float d)
         return exp_fast(d);
 }
 
+// Opaque no-op on one vector of a tile (see fence_tile).
+template <int VB>
+__device__ __forceinline__ void fence_vec(RawVec<VB> &v)
+{
+    asm volatile("" : "+v"(v.w));
+}
+
+// The exponential sums of a held softmax-family tile: x in t[0] and, with DY,
+// dy in t[1]; fp32 tiles are overwritten with the exponentials, so the output
+// needs no second exponential.  Returns the wave partial (m, s[, u]).
+//
+// Grouped (fp32 softmax): the thread's IT vectors form ref_groups<IT>() groups
+// of consecutive vectors; each group takes its own maximum gm and sums
+// e = exp(x - gm), so its work starts as soon as its own loads have landed
+// instead of after the whole tile and a wave-wide maximum, and each group is
+// rescaled to the wave maximum at the end.  Ungrouped (the others, where
+// grouping measured 1-2% slower on MI355X): every exponential is taken
+// against the wave maximum.  Either way loc.m holds the reference maximum of
+// each group's exponentials (the wave maximum for all of them, ungrouped).
+template <bool DY, class T, int VB, int IT, int NI>
+__device__ __forceinline__ Part<DY ? 3 : 2> softmax_groups(Tile<T, VB, IT> (&t)[NI], int kvalid, Local &loc)
+{
+    constexpr int E = Tile<T, VB, IT>::kEpv;
+    constexpr bool kGrouped = !DY && is_f32<T>();
+    constexpr int NG = kGrouped ? ref_groups<IT>() : 1;
+    constexpr int GS = IT / NG;
+    float sg[NG], ug[NG], gref[NG];
+    float mw = -INFINITY;
+    if constexpr (!kGrouped) {
+        float mt = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < IT; ++k)
+            if (k < kvalid)
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    mt = fmaxf(mt, elem<T, VB>(t[0].v[k], e));
+        mw = wave_max(mt);
+        fence_tile(t[0]);
+    }
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+        float gm = mw;
+        if constexpr (kGrouped) {
+            gm = -INFINITY;
+#pragma unroll
+            for (int j = 0; j < GS; ++j)
+                if (g * GS + j < kvalid)
+#pragma unroll
+                    for (int e = 0; e < E; ++e)
+                        gm = fmaxf(gm, elem<T, VB>(t[0].v[g * GS + j], e));
+#pragma unroll
+            for (int j = 0; j < GS; ++j)
+                fence_vec(t[0].v[g * GS + j]);
+        }
+        float sv = 0.0f, uv = 0.0f;
+#pragma unroll
+        for (int j = 0; j < GS; ++j) {
+            const int k = g * GS + j;
+            if (k < kvalid)
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const float ex = exp_for<T>(elem<T, VB>(t[0].v[k], e) - gm);
+                    if constexpr (is_f32<T>())
+                        set_word<VB>(t[0].v[k], e, __float_as_uint(ex));
+                    sv += ex;
+                    if constexpr (DY)
+                        uv = __builtin_fmaf(ex, elem<T, VB>(t[1].v[k], e), uv);
+                }
+        }
+        gref[g] = gm;
+        sg[g] = sv;
+        ug[g] = uv;
+    }
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+        loc.m[g] = kGrouped ? (g < NG ? gref[g] : -INFINITY) : mw;
+    float st = sg[0], ut = ug[0];
+    if constexpr (kGrouped) {
+        float mt = gref[0];
+#pragma unroll
+        for (int g = 1; g < NG; ++g)
+            mt = fmaxf(mt, gref[g]);
+        mw = wave_max(mt);
+        // a group with no valid vector has s = 0 (a valid one has s >= 1)
+        st = 0.0f;
+#pragma unroll
+        for (int g = 0; g < NG; ++g)
+            if (sg[g] != 0.0f)
+                st += sg[g] * exp_acc(gref[g] - mw);
+    }
+    if constexpr (DY)
+        return Part<3>{{mw, wave_sum(st), wave_sum(ut)}};
+    else
+        return Part<2>{{mw, wave_sum(st)}};
+}
+
+// fp32 output scales of the groups: e^(gm - m) / s, zero for a group with no
+// valid vector.
+__device__ __forceinline__ void group_scales(Coef &c, const Local &loc, float m, float inv_s)
+{
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+        c.f[g] = loc.m[g] != -INFINITY ? exp_acc(loc.m[g] - m) * inv_s : 0.0f;
+}
+
 // ---------------------------------------------------------------------------
-// softmax.  Coef: k0 = output scale (fp32: e^(m_wave - m) / s, because the
-// tile holds e^(x - m_wave); bf16: 1 / s), k1 = row max m.
+// softmax.  Coef: k0 = 1 / s (held fp32 tiles: per vector, the group scale
+// e^(gm - m) / s, because the tile holds e^(x - gm)), k1 = row max m.
 // ---------------------------------------------------------------------------
 template <>
 struct OpTraits<kSoftmax> {
@@ -115,43 +237,10 @@ struct OpTraits<kSoftmax> {
     template <class T> using Out = T;
     using Partial = Part<kQ>;
 
-    // Wave partial over the wave's elements.  For fp32 storage the tile is
-    // overwritten with e_i = exp(x_i - m_wave) so that the output needs no
-    // second exponential.
     template <class T, int VB, int IT>
-    __device__ __forceinline__ static Partial wave_partial(Tile<T, VB, IT> (&tt)[kIn], int kvalid)
+    __device__ __forceinline__ static Partial wave_partial(Tile<T, VB, IT> (&t)[kIn], int kvalid, Local &loc)
     {
-        Tile<T, VB, IT> &t = tt[0];
-        constexpr int E = Tile<T, VB, IT>::kEpv;
-        float mt = -INFINITY;
-#pragma unroll
-        for (int k = 0; k < IT; ++k)
-            if (k < kvalid)
-#pragma unroll
-                for (int e = 0; e < E; ++e)
-                    mt = fmaxf(mt, elem<T, VB>(t.v[k], e));
-        const float mw = wave_max(mt);
-        fence_tile(t);
-        float st = 0.0f;
-        if constexpr (is_f32<T>()) {
-#pragma unroll
-            for (int k = 0; k < IT; ++k)
-                if (k < kvalid)
-#pragma unroll
-                    for (int e = 0; e < E; ++e) {
-                        float ex = exp_acc(elem<T, VB>(t.v[k], e) - mw);
-                        set_word<VB>(t.v[k], e, __float_as_uint(ex));
-                        st += ex;
-                    }
-        } else {
-#pragma unroll
-            for (int k = 0; k < IT; ++k)
-                if (k < kvalid)
-#pragma unroll
-                    for (int e = 0; e < E; ++e)
-                        st += exp_fast(elem<T, VB>(t.v[k], e) - mw);
-        }
-        return Partial{{mw, wave_sum(st)}};
+        return softmax_groups<false, T, VB, IT>(t, kvalid, loc);
     }
 
     // Combine partials p[0..n-1] (n <= N) in index order.
@@ -171,22 +260,21 @@ struct OpTraits<kSoftmax> {
         return Partial{{m, s}};
     }
 
-    // `own` is the partial whose exponentials are stored in this thread's tile.
     template <class T>
-    __device__ __forceinline__ static Coef finalize(const Partial &row, const Partial &own, int64_t, float)
+    __device__ __forceinline__ static Coef finalize(const Partial &row, const Local &loc, int64_t, float)
     {
         const float inv_s = 1.0f / row.v[1];
+        Coef c{{inv_s, row.v[0], 0.0f, 0.0f}};
         if constexpr (is_f32<T>())
-            return Coef{{own.v[1] != 0.0f ? exp_acc(own.v[0] - row.v[0]) * inv_s : 0.0f, row.v[0], 0.0f, 0.0f}};
-        else
-            return Coef{{inv_s, row.v[0], 0.0f, 0.0f}};
+            group_scales(c, loc, row.v[0], inv_s);
+        return c;
     }
 
     template <class T>
     __device__ __forceinline__ static float apply(const float (&in)[kIn], const Coef &c, float, float)
     {
         if constexpr (is_f32<T>())
-            return in[0] * c.k[0];  // in[0] already holds exp(x - m_wave)
+            return in[0] * c.k[0];  // in[0] holds exp(x - gm), k0 the group's scale
         else
             return exp_fast(in[0] - c.k[1]) * c.k[0];
     }
@@ -256,7 +344,7 @@ struct OpTraits<kLayerNorm> {
     using Partial = Part<kQ>;
 
     template <class T, int VB, int IT>
-    __device__ __forceinline__ static Partial wave_partial(Tile<T, VB, IT> (&tt)[kIn], int kvalid)
+    __device__ __forceinline__ static Partial wave_partial(Tile<T, VB, IT> (&tt)[kIn], int kvalid, Local &)
     {
         Tile<T, VB, IT> &t = tt[0];
         constexpr int E = Tile<T, VB, IT>::kEpv;
@@ -306,7 +394,7 @@ struct OpTraits<kLayerNorm> {
     }
 
     template <class T>
-    __device__ __forceinline__ static Coef finalize(const Partial &row, const Partial &, int64_t cols, float eps)
+    __device__ __forceinline__ static Coef finalize(const Partial &row, const Local &, int64_t cols, float eps)
     {
         const float var = row.v[2] / static_cast<float>(cols);
         return Coef{{row.v[1], 1.0f / sqrtf(var + eps), 0.0f, 0.0f}};
@@ -365,7 +453,7 @@ struct OpTraits<kLayerNorm> {
     template <class T>
     __device__ __forceinline__ static Coef finalize_stream(const Partial &row, int64_t cols, float eps)
     {
-        return finalize<T>(row, row, cols, eps);
+        return finalize<T>(row, Local{}, cols, eps);
     }
 
     template <class T>
@@ -389,7 +477,7 @@ struct OpTraits<kRmsNorm> {
     using Partial = Part<kQ>;
 
     template <class T, int VB, int IT>
-    __device__ __forceinline__ static Partial wave_partial(Tile<T, VB, IT> (&tt)[kIn], int kvalid)
+    __device__ __forceinline__ static Partial wave_partial(Tile<T, VB, IT> (&tt)[kIn], int kvalid, Local &)
     {
         Tile<T, VB, IT> &t = tt[0];
         constexpr int E = Tile<T, VB, IT>::kEpv;
@@ -417,7 +505,7 @@ struct OpTraits<kRmsNorm> {
     }
 
     template <class T>
-    __device__ __forceinline__ static Coef finalize(const Partial &row, const Partial &, int64_t cols, float eps)
+    __device__ __forceinline__ static Coef finalize(const Partial &row, const Local &, int64_t cols, float eps)
     {
         return Coef{{1.0f / sqrtf(row.v[0] / static_cast<float>(cols) + eps), 0.0f, 0.0f, 0.0f}};
     }
@@ -453,7 +541,7 @@ struct OpTraits<kRmsNorm> {
     template <class T>
     __device__ __forceinline__ static Coef finalize_stream(const Partial &row, int64_t cols, float eps)
     {
-        return finalize<T>(row, row, cols, eps);
+        return finalize<T>(row, Local{}, cols, eps);
     }
 
     template <class T>
@@ -465,8 +553,8 @@ struct OpTraits<kRmsNorm> {
 
 // ---------------------------------------------------------------------------
 // Softmax-logits backward: inputs x (logits) and dy; dx = p (dy - sum dy p)
-// with p = softmax(x) recomputed from x.  Coef: k0 = probability scale
-// (fp32: e^(m_wave - m) / s, the tile holding e^(x - m_wave); bf16: 1 / s),
+// with p = softmax(x) recomputed from x.  Coef: k0 = 1 / s (held fp32 tiles:
+// e^(m_wave - m) / s, the tile holding e^(x - m_wave)),
 // k1 = u / s (the dot product of dy with p), k2 = row max m.
 // ---------------------------------------------------------------------------
 template <>
@@ -480,31 +568,9 @@ struct OpTraits<kSoftmaxBwd> {
     using Partial = Part<kQ>;
 
     template <class T, int VB, int IT>
-    __device__ __forceinline__ static Partial wave_partial(Tile<T, VB, IT> (&t)[kIn], int kvalid)
+    __device__ __forceinline__ static Partial wave_partial(Tile<T, VB, IT> (&t)[kIn], int kvalid, Local &loc)
     {
-        constexpr int E = Tile<T, VB, IT>::kEpv;
-        float mt = -INFINITY;
-#pragma unroll
-        for (int k = 0; k < IT; ++k)
-            if (k < kvalid)
-#pragma unroll
-                for (int e = 0; e < E; ++e)
-                    mt = fmaxf(mt, elem<T, VB>(t[0].v[k], e));
-        const float mw = wave_max(mt);
-        fence_tile(t[0]);
-        float st = 0.0f, ut = 0.0f;
-#pragma unroll
-        for (int k = 0; k < IT; ++k)
-            if (k < kvalid)
-#pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    const float ex = exp_for<T>(elem<T, VB>(t[0].v[k], e) - mw);
-                    if constexpr (is_f32<T>())
-                        set_word<VB>(t[0].v[k], e, __float_as_uint(ex));
-                    st += ex;
-                    ut = __builtin_fmaf(ex, elem<T, VB>(t[1].v[k], e), ut);
-                }
-        return Partial{{mw, wave_sum(st), wave_sum(ut)}};
+        return softmax_groups<true, T, VB, IT>(t, kvalid, loc);
     }
 
     template <int N>
@@ -527,14 +593,13 @@ struct OpTraits<kSoftmaxBwd> {
     }
 
     template <class T>
-    __device__ __forceinline__ static Coef finalize(const Partial &row, const Partial &own, int64_t, float)
+    __device__ __forceinline__ static Coef finalize(const Partial &row, const Local &loc, int64_t, float)
     {
         const float inv_s = 1.0f / row.v[1];
-        const float dot = row.v[2] / row.v[1];
+        Coef c{{inv_s, row.v[2] / row.v[1], row.v[0], 0.0f}};
         if constexpr (is_f32<T>())
-            return Coef{{own.v[1] != 0.0f ? exp_acc(own.v[0] - row.v[0]) * inv_s : 0.0f, dot, row.v[0], 0.0f}};
-        else
-            return Coef{{inv_s, dot, row.v[0], 0.0f}};
+            group_scales(c, loc, row.v[0], inv_s);
+        return c;
     }
 
     template <class T>
@@ -542,7 +607,7 @@ struct OpTraits<kSoftmaxBwd> {
     {
         float p;
         if constexpr (is_f32<T>())
-            p = in[0] * c.k[0];  // in[0] already holds exp(x - m_wave)
+            p = in[0] * c.k[0];  // in[0] holds exp(x - gm), k0 the group's scale
         else
             p = exp_fast(in[0] - c.k[2]) * c.k[0];
         return p * (in[1] - c.k[1]);
@@ -632,7 +697,7 @@ struct OpTraits<kLayerNormBwd> {
     }
 
     template <class T, int VB, int IT>
-    __device__ __forceinline__ static Partial wave_partial(Tile<T, VB, IT> (&t)[kIn], int kvalid)
+    __device__ __forceinline__ static Partial wave_partial(Tile<T, VB, IT> (&t)[kIn], int kvalid, Local &)
     {
         constexpr int E = Tile<T, VB, IT>::kEpv;
         float sx = 0.0f, sg = 0.0f;
@@ -687,7 +752,7 @@ struct OpTraits<kLayerNormBwd> {
     }
 
     template <class T>
-    __device__ __forceinline__ static Coef finalize(const Partial &row, const Partial &, int64_t cols, float eps)
+    __device__ __forceinline__ static Coef finalize(const Partial &row, const Local &, int64_t cols, float eps)
     {
         const float inv_n = 1.0f / static_cast<float>(cols);
         const float rstd = 1.0f / sqrtf(row.v[2] * inv_n + eps);
@@ -755,7 +820,7 @@ struct OpTraits<kLayerNormBwd> {
     template <class T>
     __device__ __forceinline__ static Coef finalize_stream(const Partial &row, int64_t cols, float eps)
     {
-        return finalize<T>(row, row, cols, eps);
+        return finalize<T>(row, Local{}, cols, eps);
     }
 
     // in[0] = x, in[1] = dy (not yet multiplied by gamma)
@@ -785,7 +850,7 @@ struct OpTraits<kQuantInt8> {
     using Partial = Part<kQ>;
 
     template <class T, int VB, int IT>
-    __device__ __forceinline__ static Partial wave_partial(Tile<T, VB, IT> (&t)[kIn], int kvalid)
+    __device__ __forceinline__ static Partial wave_partial(Tile<T, VB, IT> (&t)[kIn], int kvalid, Local &)
     {
         constexpr int E = Tile<T, VB, IT>::kEpv;
         float a = 0.0f;
@@ -810,7 +875,7 @@ struct OpTraits<kQuantInt8> {
     }
 
     template <class T>
-    __device__ __forceinline__ static Coef finalize(const Partial &row, const Partial &, int64_t, float)
+    __device__ __forceinline__ static Coef finalize(const Partial &row, const Local &, int64_t, float)
     {
         const float a = row.v[0];
         const float inv = a > 0.0f ? fminf(127.0f / a, FLT_MAX) : 0.0f;
@@ -845,7 +910,7 @@ struct OpTraits<kQuantInt8> {
     template <class T>
     __device__ __forceinline__ static Coef finalize_stream(const Partial &row, int64_t cols, float eps)
     {
-        return finalize<T>(row, row, cols, eps);
+        return finalize<T>(row, Local{}, cols, eps);
     }
 
     template <class T>
@@ -854,5 +919,23 @@ struct OpTraits<kQuantInt8> {
         return apply<T>(in, c, g, b);
     }
 };
+
+// The coefficients for vector k of a held tile of IT vectors: for the fp32
+// softmax family, k0 becomes the scale of the vector's group (softmax_groups).
+template <OpKind OP, class T, int IT>
+__device__ __forceinline__ Coef vec_coef(const Coef &c, int k)
+{
+    if constexpr (OP == kSoftmax && is_f32<T>()) {
+        Coef r = c;
+        r.k[0] = c.f[k / (IT / ref_groups<IT>())];
+        return r;
+    } else if constexpr (OP == kSoftmaxBwd && is_f32<T>()) {
+        Coef r = c;
+        r.k[0] = c.f[0];  // one reference (the wave maximum) for the whole tile
+        return r;
+    } else {
+        return c;
+    }
+}
 
 }  // namespace credit
