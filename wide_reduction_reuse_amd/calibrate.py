@@ -23,6 +23,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import math
 import sys
 from collections import defaultdict
 
@@ -30,21 +31,29 @@ from .credit import DTYPES as DTS, OPS
 
 
 def build_table(records):
-    pts = defaultdict(dict)
+    """One row per (op, dtype, cols, plan): the kernel time at every calibrated
+    row count.  A shape timed in several sweeps (runs on different boxes)
+    gets the geometric mean of its medians."""
+    pts = defaultdict(lambda: defaultdict(list))
     for r in records:
         for c in r["candidates"]:
             p = c["plan"]
             key = (OPS[r["op"]], DTS[r["dtype"]], r["cols"], p["path"], p["split_p"], p["block_threads"],
                    p["items"], p["vec_bytes"], p["wgs_per_cu"])
-            pts[key][r["rows"]] = c["median_ms"] * 1000.0
+            pts[key][r["rows"]].append(c["median_ms"] * 1000.0)
     table = []
     for key in sorted(pts):
         rows = sorted(pts[key])
         row = list(key) + [len(rows)]
         for n in rows:
-            row += [n, round(pts[key][n], 4)]
+            ts = pts[key][n]
+            row += [n, round(math.exp(sum(math.log(t) for t in ts) / len(ts)), 4)]
         table.append(row)
     return table
+
+
+def unique_shapes(records) -> int:
+    return len({(r["op"], r["dtype"], r["rows"], r["cols"]) for r in records})
 
 
 def device_info():
@@ -85,7 +94,11 @@ def main(argv=None) -> int:
     stream = max(r["bytes"] / (c["median_ms"] * 1e-3) / 1e9 for r in records if r["bytes"] == biggest
                  for c in r["candidates"])
     dev = device_info()
-    cal = {"version": 2, "source": "median kernel times of every legal plan on %d calibration shapes" % len(records),
+    n_shapes = unique_shapes(records)
+    src = "median kernel times of every legal plan on %d calibration shapes" % n_shapes
+    if len(records) > n_shapes:
+        src += " (%d timed records, repeats averaged)" % len(records)
+    cal = {"version": 2, "source": src,
            "stream_gbs": round(stream, 1), "table": build_table(records)}
     if a.ctrl:
         summ = [json.loads(l) for l in open(a.ctrl) if l.strip() and json.loads(l).get("summary")]
@@ -106,7 +119,8 @@ def main(argv=None) -> int:
         f.write(' "table": [\n')
         f.write(",\n".join("  " + json.dumps(row) for row in cal["table"]))
         f.write("\n ]\n}\n")
-    print("wrote %s: %d candidates over %d shapes" % (a.out, len(cal["table"]), len(records)), file=sys.stderr)
+    print("wrote %s: %d candidates over %d shapes (%d records)" % (a.out, len(cal["table"]), n_shapes, len(records)),
+          file=sys.stderr)
     return 0
 
 
