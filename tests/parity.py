@@ -30,6 +30,8 @@ from __future__ import annotations
 import dataclasses
 from typing import Dict, Optional
 
+import warnings
+
 import numpy as np
 
 import oracle
@@ -67,15 +69,21 @@ def compare(op: str, dtype: str, y_dev: np.ndarray, yhat: np.ndarray, tau_elem: 
         y = np.asarray(y_dev, dtype=np.float32).astype(np.float64)
         tau = tau_elem if tau_elem is not None else (2.0 ** -126 if op == "softmax" else 1.0)
         diff = np.abs(y - yhat)
-        e = diff / np.maximum(np.abs(yhat), tau)
+        # an exact match is no error, also where the scale is zero (a
+        # backward operator's tau where the probability underflows to 0)
+        with np.errstate(divide="ignore", invalid="ignore"):
+            e = np.where(diff == 0, 0.0, diff / np.maximum(np.abs(yhat), tau))
         e = np.where(np.isnan(yhat) & np.isnan(y), 0.0, e)
         e = np.where(np.isnan(e), np.inf, e)
         worst = int(np.argmax(e)) if e.size else -1
         with np.errstate(divide="ignore", invalid="ignore"):
             rel = np.where(yhat != 0, diff / np.abs(yhat), np.where(diff == 0, 0.0, np.inf))
+        with warnings.catch_warnings():  # all-NaN rows only make the reported maxima NaN
+            warnings.simplefilter("ignore", RuntimeWarning)
+            max_abs = float(np.nanmax(diff)) if diff.size else 0.0
+            max_rel = float(np.nanmax(rel)) if rel.size else 0.0
         return Verdict(bool(e.size == 0 or e.max() <= FP32_TOL), float(e.max()) if e.size else 0.0,
-                       float(np.nanmax(diff)) if diff.size else 0.0,
-                       float(np.nanmax(rel)) if rel.size else 0.0, 0, worst)
+                       max_abs, max_rel, 0, worst)
     r_bits = oracle.round_bf16(yhat)
     y_bits = np.asarray(y_dev, dtype=np.uint16)
     r = oracle.bf16_bits_to_f64(r_bits)

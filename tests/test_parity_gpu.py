@@ -321,6 +321,33 @@ def test_rows_fewer_than_cus_and_odd_row_counts():
             _check(inp, _run(inp, path, p), "quantize rows=%d %s" % (rows, path))
 
 
+@pytest.mark.parametrize("op", ["softmax", "softmax_bwd"])
+def test_masked_runs_of_logits(op):
+    # Rows with long runs of very negative logits, as from a mask: whole
+    # groups of a thread's vectors whose own maximum lies ~1e4 below the
+    # row's, so the factor that rescales them to the row maximum underflows
+    # to zero; and rows with a single unmasked element (a one-hot output).
+    w = W.custom(op, "f32", 64, 32768, seed=77, x_dist="scaled_shifted", x_scale=2.0, x_shift=0.0)
+    inp = W.generate(w)
+    rng = np.random.default_rng(77)
+    cols = w.cols
+    for r in range(w.rows):
+        kind = r % 4
+        if kind == 0:
+            inp.x[r, : cols // 2] -= 1e4
+        elif kind == 1:
+            inp.x[r, cols // 2 :] -= 1e4
+        elif kind == 2:
+            for c0 in range(0, cols, 1024):
+                inp.x[r, c0 : c0 + 512] -= 1e4
+        else:
+            keep = int(rng.integers(0, cols))
+            inp.x[r, :] -= 1e4
+            inp.x[r, keep] = 0.0
+    for path, p in [("auto", 0), ("single", 0), ("split", 2), ("split", 4), ("split", 8), ("reread", 0)]:
+        _check(inp, _run(inp, path, p), "masked %s %s P=%d" % (op, path, p))
+
+
 def test_nan_propagates_to_its_row_only():
     C = _lib()
     inp = W.generate(W.custom("softmax", "f32", 4, 4096, seed=9))
