@@ -1,7 +1,9 @@
 """The selector's calibration table on a machine without a GPU: file parsing
 and validation, interpolation in (log rows, log time), the choice among
-measured candidates, forced paths, the analytic fallback for widths the table
-did not measure, and the CREDIT_CALIB environment variable."""
+measured candidates, forced paths, pricing a width the table did not measure
+from the same plans at the nearest measured widths, the analytic fallback
+where the table measured none of the legal plans, and the CREDIT_CALIB
+environment variable."""
 import json
 import math
 import os
@@ -69,12 +71,45 @@ def test_forced_paths_use_the_table_and_fall_back(tmp_path):
     assert p.path == 3
 
 
-def test_unmeasured_width_uses_the_analytic_model(tmp_path):
+def test_width_whose_plans_were_never_measured_uses_the_analytic_model(tmp_path):
+    # at 65536 columns none of the legal plans is one the table measured (at
+    # any width), so the analytic model decides, as with no table at all
     C.credit_load_calibration(_write(tmp_path, [ENTRY_A, ENTRY_B]))
-    a = C.credit_select_path("softmax", "f32", 1000, 8192).as_dict()
+    a = C.credit_select_path("softmax", "f32", 1000, 65536).as_dict()
     C.credit_load_calibration(None)
-    b = C.credit_select_path("softmax", "f32", 1000, 8192).as_dict()
-    assert a["path"] == b["path"] and a["block_threads"] == b["block_threads"] and a["items"] == b["items"]
+    b = C.credit_select_path("softmax", "f32", 1000, 65536).as_dict()
+    # (the predicted times differ: the table's stream rate feeds the model)
+    keys = ("path", "split_p", "block_threads", "items", "vec_bytes", "wgs_per_cu")
+    assert [a[k] for k in keys] == [b[k] for k in keys]
+
+
+# the plan of ENTRY_B measured again at 8192 columns
+ENTRY_B8 = [0, 0, 8192, 2, 2, 256, 8, 16, 0, 2, 100, 9.0, 1000, 150.0]
+
+
+def test_width_between_measured_widths_interpolates_the_plan(tmp_path):
+    # 6144 columns: split P = 2, 256 x 8 is legal and was measured at 4096 and
+    # 8192; each side is read at the rows that move the same bytes, and the two
+    # are interpolated in (log cols, log time); path 1's measured tile (512 x 2)
+    # cannot hold the row, so only the split plan is priced
+    C.credit_load_calibration(_write(tmp_path, [ENTRY_A, ENTRY_B, ENTRY_B8]))
+    rows = 500
+    p = C.credit_select_path("softmax", "f32", rows, 6144)
+    assert (p.path, p.split_p, p.block_threads, p.items) == (2, 2, 256, 8)
+    lo = _loglog(100, 5.0, 1000, 100.0, rows * 6144 / 4096)
+    hi = _loglog(100, 9.0, 1000, 150.0, rows * 6144 / 8192)
+    w = math.log(6144 / 4096) / math.log(2.0)
+    assert p.predicted_us[1] == pytest.approx(math.exp((1 - w) * math.log(lo) + w * math.log(hi)), rel=1e-9)
+    assert p.predicted_us[0] < 0 and p.predicted_us[2] < 0
+
+
+def test_width_beyond_the_measured_widths_scales_at_equal_bytes(tmp_path):
+    # 12288 columns: the plan was measured below only (4096 and 8192); the
+    # nearest width is read at the rows that move the same bytes
+    C.credit_load_calibration(_write(tmp_path, [ENTRY_A, ENTRY_B, ENTRY_B8]))
+    p = C.credit_plan("softmax", "f32", 300, 12288, "split", 2)
+    assert (p.path, p.split_p, p.block_threads, p.items) == (2, 2, 256, 8)
+    assert p.predicted_us[1] == pytest.approx(_loglog(100, 9.0, 1000, 150.0, 300 * 12288 / 8192), rel=1e-9)
 
 
 @pytest.mark.parametrize("bad", [

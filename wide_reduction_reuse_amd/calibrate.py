@@ -6,7 +6,9 @@ With --run it first times every legal plan on the calibration shapes
 (workloads.calibration_points(): the crossover sweep's operators, dtypes and
 widths at 8, 64, 512 and 2048 MiB, sizes the scored sweep does not use; and
 workloads.calibration_points_next(): the three further workloads at row counts
-their width grid does not use) with the sweep driver and writes the records to
+their width grid does not use; workloads.calibration_points_odd(): widths
+2^k + 1, whose rows are not whole 16-byte vectors and run on tiles of their
+own) with the sweep driver and writes the records to
 the (one) --sweep file.  Several --sweep files are merged.  --ctrl FILE (the
 output of ctrlbench.py; with --run it is measured first) adds the analytic
 model's launch and per-row-wave exchange costs, fitted to the work-free

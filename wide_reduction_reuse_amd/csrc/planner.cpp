@@ -386,11 +386,83 @@ bool plan_from_table(const PlanRequest &req, const Calibration &cal, int forced_
     return true;
 }
 
+// Time of candidate `cd` at a width the table did not measure, from the same
+// plan's measurements at the nearest calibrated widths below and above:
+// each is read at the row count that moves the same bytes, and the two are
+// interpolated in (log cols, log time); one side alone is used as it is.
+// Negative when the table never measured the plan.
+double neighbour_time_us(const PlanRequest &req, const Calibration &cal, const Candidate &cd)
+{
+    const CalibEntry *lo = nullptr, *hi = nullptr;
+    for (const CalibEntry &e : cal.table) {
+        if (e.op != req.op || e.dt != req.dt || e.path != cd.path || e.split_p != cd.split_p ||
+            e.block != cd.est.tile.block || e.items != cd.est.tile.items || e.vb != cd.est.tile.vb ||
+            e.wgs_per_cu != cd.wgs_per_cu || e.rows.empty())
+            continue;
+        if (e.cols <= req.cols && (lo == nullptr || e.cols > lo->cols))
+            lo = &e;
+        if (e.cols >= req.cols && (hi == nullptr || e.cols < hi->cols))
+            hi = &e;
+    }
+    const double bytes_rows = static_cast<double>(req.rows) * static_cast<double>(req.cols);
+    auto at = [&](const CalibEntry *e) { return calib_time_us(*e, bytes_rows / static_cast<double>(e->cols)); };
+    if (lo == nullptr && hi == nullptr)
+        return -1.0;
+    if (lo == nullptr || lo == hi)
+        return at(hi);
+    if (hi == nullptr)
+        return at(lo);
+    const double w = std::log(static_cast<double>(req.cols) / lo->cols) / std::log(static_cast<double>(hi->cols) / lo->cols);
+    return std::exp((1.0 - w) * std::log(at(lo)) + w * std::log(at(hi)));
+}
+
+// Plan for a width the table did not measure: every legal candidate the
+// table measured at some width is priced by neighbour_time_us and the
+// fastest wins.  Returns false when no candidate was ever measured (odd
+// widths without odd-width calibration, another device's table).
+bool plan_from_neighbours(const PlanRequest &req, const Calibration &cal, int forced_path, int forced_p, Plan *out)
+{
+    std::vector<Candidate> cands;
+    enumerate_candidates(req, cal, &cands);
+    Plan p;
+    const Candidate *best = nullptr;
+    double best_us = 0.0;
+    for (const Candidate &cd : cands) {
+        if (forced_path != kPathAuto && cd.path != forced_path)
+            continue;
+        if (forced_p != 0 && cd.path == kPathSplit && cd.split_p != forced_p)
+            continue;
+        const double us = neighbour_time_us(req, cal, cd);
+        if (us < 0.0)
+            continue;
+        PathEstimate &pe = p.est[cd.path - 1];
+        if (!pe.legal || us < pe.us) {
+            pe = cd.est;
+            pe.legal = true;
+            pe.us = us;
+        }
+        if (best == nullptr || us < best_us) {
+            best = &cd;
+            best_us = us;
+        }
+    }
+    if (best == nullptr)
+        return false;
+    p.path = best->path;
+    p.split_p = best->split_p;
+    p.wgs_per_cu = best->wgs_per_cu;
+    p.tile = best->est.tile;
+    *out = p;
+    return true;
+}
+
 }  // namespace
 
 bool make_plan(const PlanRequest &req, const Calibration &cal, int forced_path, int forced_p, Plan *out)
 {
     if (!cal.table.empty() && plan_from_table(req, cal, forced_path, forced_p, out))
+        return true;
+    if (!cal.table.empty() && plan_from_neighbours(req, cal, forced_path, forced_p, out))
         return true;
     Plan p;
     TileSpec t;

@@ -137,6 +137,27 @@ def next_points() -> List[Workload]:
     return pts
 
 
+OFFGRID_COLS = (3072, 12288, 24576, 49152, 98304, 196608,  # rows of whole 16-byte vectors
+                1000, 5000, 30001, 50257, 100003)            # and of odd lengths
+OFFGRID_BYTES = 256 << 20
+
+
+def offgrid_points() -> List[Workload]:
+    """Widths off the calibration grid (which has only powers of two), where
+    the selector prices plans with its analytic model: the forward operators,
+    both dtypes, 256 MiB of input."""
+    pts = []
+    idx = 0
+    for op in FWD_OPS:
+        for dt in DTYPES:
+            for cols in OFFGRID_COLS:
+                rows = OFFGRID_BYTES // (cols * ELEM_BYTES[dt])
+                pts.append(Workload("offgrid%02d_%s_%s_%dx%d" % (idx, op, dt, rows, cols), op, dt, rows, cols,
+                                    seed=5000 + idx, eps=DEFAULT_EPS[op]))
+                idx += 1
+    return pts
+
+
 CALIB_BYTES = (8 << 20, 64 << 20, 512 << 20, 2048 << 20)
 CALIB_COLS = tuple(1 << k for k in range(10, 19))  # 1024 ... 262144
 
@@ -155,6 +176,50 @@ def calibration_points() -> List[Workload]:
                     rows = nbytes // (cols * ELEM_BYTES[dt])
                     name = "calib%02d_%s_%s_%dx%d" % (idx, op, dt, rows, cols)
                     pts.append(Workload(name, op, dt, rows, cols, seed=2000 + idx, eps=DEFAULT_EPS[op]))
+                    idx += 1
+    return pts
+
+
+# Widths between the powers of two, near 2^(k + 1/2): whole 16-byte vectors
+# (multiples of 256 elements) and odd lengths.  With them a tile, which is
+# timed only where it is at least half used, has measured widths on both sides
+# of most widths off the grid.
+CALIB_MID_COLS = tuple(round(2 ** (k + 0.5) / 256) * 256 for k in range(10, 18))  # 1536 ... 185344
+CALIB_ODD_COLS = tuple((1 << k) + 1 for k in (10, 12, 14, 16, 17, 18))  # 1025 ... 262145
+CALIB_ODD_MID_COLS = tuple(round(2 ** (k + 0.5)) | 1 for k in (10, 12, 14, 15, 16, 17))  # 1449 ... 185365
+
+
+def calibration_points_mid() -> List[Workload]:
+    """Calibration shapes at the aligned widths between the powers of two
+    (CALIB_MID_COLS), the forward operators, both dtypes, the sizes of
+    calibration_points()."""
+    pts = []
+    idx = 0
+    for op in FWD_OPS:
+        for dt in DTYPES:
+            for cols in CALIB_MID_COLS:
+                for nbytes in CALIB_BYTES:
+                    rows = max(1, nbytes // (cols * ELEM_BYTES[dt]))
+                    pts.append(Workload("calibm%03d_%s_%s_%dx%d" % (idx, op, dt, rows, cols), op, dt, rows, cols,
+                                        seed=7000 + idx, eps=DEFAULT_EPS[op]))
+                    idx += 1
+    return pts
+
+
+def calibration_points_odd() -> List[Workload]:
+    """Calibration shapes for rows that are not whole 16-byte vectors (their
+    kernels use 4- or 2-byte accesses and tiles of their own): the forward
+    operators, both dtypes, widths 2^k + 1 and odd widths near 2^(k + 1/2),
+    at the sizes of calibration_points()."""
+    pts = []
+    idx = 0
+    for op in FWD_OPS:
+        for dt in DTYPES:
+            for cols in CALIB_ODD_COLS + CALIB_ODD_MID_COLS:
+                for nbytes in CALIB_BYTES:
+                    rows = max(1, nbytes // (cols * ELEM_BYTES[dt]))
+                    pts.append(Workload("calibo%03d_%s_%s_%dx%d" % (idx, op, dt, rows, cols), op, dt, rows, cols,
+                                        seed=6000 + idx, eps=DEFAULT_EPS[op]))
                     idx += 1
     return pts
 
