@@ -209,7 +209,8 @@ ODD_CASES = [(op, dt, cols, path, p)
              for op in W.OPS for dt in W.DTYPES if (op, dt) in W.SUPPORTED
              for cols, path, p in [(1, "auto", 0), (3, "auto", 0), (1001, "auto", 0), (1001, "reread", 0),
                                    (16383, "single", 0), (30001, "split", 2), (30001, "reread", 0),
-                                   (60007, "split", 4)]]
+                                   (60007, "split", 4), (50257, "auto", 0), (100003, "auto", 0),
+                                   (100003, "split", 8)]]
 
 
 @pytest.mark.parametrize("op,dt,cols,path,p", ODD_CASES, ids=["%s-%s-c%d-%s%d" % c for c in ODD_CASES])
