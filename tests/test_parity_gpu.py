@@ -169,7 +169,7 @@ def _tile_excluded(op, kind, block, items, vb=16):
     rule restated, so that the library's refusals are checked against it."""
     if kind == "reread" or block < 1024:
         return False
-    held = W.N_INPUTS.get(op, 1) * items * vb
+    held = W.N_INPUTS.get(op, 1) * items * max(vb, 4)  # a 2-byte vector takes a 32-bit register
     if op == "layernorm" and kind == "split" and items == 16 and vb == 16:
         return True
     if op == "softmax_bwd" and held > (128 if kind == "split" else 256):

@@ -50,7 +50,7 @@ constexpr int op_stats(int op)
 
 // Tiles left out for one operator, all at 1024 threads, where a thread has
 // at most 128 VGPRs; each of them spilled registers to scratch memory when
-// compiled.  held = bytes of row data a thread holds (all inputs).
+// compiled.  held = register bytes of row data a thread holds (all inputs).
 //   LayerNorm split 16 x 16 B: the next smaller tiles split such slices finer.
 //   softmax-logits backward (x and dy held): more than 256 B (path 1) or
 //     128 B (split, which also keeps the exchange state).
@@ -61,7 +61,8 @@ constexpr bool tile_enabled(int op, int kind, int block, int items, int vb)
     if (kind == kKindReread || block < 1024)
         return true;
     const bool split = kind == kKindSplit || kind == kKindControl;
-    const int held = op_inputs(op) * items * vb;
+    // a 2-byte vector still takes a whole 32-bit register
+    const int held = op_inputs(op) * items * (vb < 4 ? 4 : vb);
     if (op == 1 && split && items == 16 && vb == 16)
         return false;
     if (op == 3 && held > (split ? 128 : 256))
@@ -72,10 +73,14 @@ constexpr bool tile_enabled(int op, int kind, int block, int items, int vb)
 }
 
 // Ladders for one-element accesses (rows whose byte length is not a multiple
-// of 16 bytes).
+// of 16 bytes).  The 32-vector tiles let such rows up to 32768 elements stay
+// on one workgroup and wider ones split in fewer, larger slices (4- and 2-byte
+// accesses stream at 5.8-6.0 TB/s on MI355X when a thread keeps 32 in flight);
+// 48 vectors spilled registers for LayerNorm, RMSNorm bf16 and softmax
+// backward.
 #define CREDIT_WAVE_TILES_1E(X) X(4) X(16)
-#define CREDIT_WG_TILES_1E(X) X(1024, 4) X(1024, 16)
-#define CREDIT_SPLIT_TILES_1E(X) X(1024, 16)
+#define CREDIT_WG_TILES_1E(X) X(1024, 4) X(1024, 16) X(1024, 32)
+#define CREDIT_SPLIT_TILES_1E(X) X(1024, 16) X(1024, 32)
 #define CREDIT_REREAD_TILES_1E(X) X(256, 8)
 
 }  // namespace credit
