@@ -1,6 +1,6 @@
 """Exhaustive timing of every legal plan on a set of shapes.
 
-    python -m wide_reduction_reuse_amd.sweep --points named|sweep|next|all|calib|calib_next|calib_mid|calib_odd|calib_all|offgrid
+    python -m wide_reduction_reuse_amd.sweep --points named|sweep|next|all|calib|calib_next|calib_next_more|calib_mid|calib_odd|calib_all|offgrid
                                              [--steps 15] [--warmup 3] [--ops ...]
 
 For each shape it enumerates the legal plans (credit_enumerate_plans: every
@@ -96,12 +96,14 @@ def points(which: str, ops=None, min_cols: int = 0):
         pts += W.calibration_points()
     if which in ("calib_next", "calib_all"):
         pts += W.calibration_points_next()
+    if which in ("calib_next_more", "calib_all"):
+        pts += W.calibration_points_next_more()
     if which in ("calib_mid", "calib_all"):
         pts += W.calibration_points_mid()
     if which in ("calib_odd", "calib_all"):
         pts += W.calibration_points_odd()
     if which == "offgrid":
-        pts += W.offgrid_points()
+        pts += W.offgrid_points() + W.offgrid_points_next()
     if ops:
         pts = [p for p in pts if p.op in ops]
     return [p for p in pts if p.cols >= min_cols]
@@ -109,8 +111,8 @@ def points(which: str, ops=None, min_cols: int = 0):
 
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
-    ap.add_argument("--points", default="named", choices=("named", "sweep", "next", "all", "calib", "calib_next", "calib_mid",
-                                                         "calib_odd", "calib_all", "offgrid"))
+    ap.add_argument("--points", default="named", choices=("named", "sweep", "next", "all", "calib", "calib_next", "calib_next_more",
+                                                         "calib_mid", "calib_odd", "calib_all", "offgrid"))
     ap.add_argument("--ops", nargs="*", default=None)
     ap.add_argument("--min-cols", type=int, default=0, help="only shapes at least this wide")
     ap.add_argument("--out", default="-")

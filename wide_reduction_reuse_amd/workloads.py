@@ -251,6 +251,48 @@ def calibration_points_next() -> List[Workload]:
     return pts
 
 
+def calibration_points_next_more() -> List[Workload]:
+    """The further workloads' calibration at the widths between the powers of
+    two and the odd widths (CALIB_MID_COLS, CALIB_ODD_COLS,
+    CALIB_ODD_MID_COLS), at the rows of calibration_points_next()."""
+    pts = []
+    idx = 0
+    for name in NEXT_ORDER:
+        base = NAMED[name]
+        for dt in DTYPES:
+            if (base.op, dt) not in SUPPORTED:
+                continue
+            for cols in CALIB_MID_COLS + CALIB_ODD_COLS + CALIB_ODD_MID_COLS:
+                for rows in CALIB_NEXT_ROWS:
+                    if rows * cols * ELEM_BYTES[dt] > CALIB_NEXT_MAX_BYTES:
+                        continue
+                    pts.append(dataclasses.replace(
+                        base, name="calibx%03d_%s_%s_%dx%d" % (idx, base.op, dt, rows, cols), dtype=dt,
+                        rows=rows, cols=cols, seed=8000 + idx))
+                    idx += 1
+    return pts
+
+
+def offgrid_points_next() -> List[Workload]:
+    """The further workloads at the off-grid widths (OFFGRID_COLS), each
+    supported dtype, at the rows of their width grid (4096; 2048 for
+    LayerNorm backward)."""
+    pts = []
+    idx = 0
+    for name in NEXT_ORDER:
+        base = NAMED[name]
+        for dt in DTYPES:
+            if (base.op, dt) not in SUPPORTED:
+                continue
+            for cols in OFFGRID_COLS:
+                rows = NEXT_ROWS[base.op]
+                pts.append(dataclasses.replace(
+                    base, name="offgridn%02d_%s_%s_%dx%d" % (idx, base.op, dt, rows, cols), dtype=dt,
+                    rows=rows, cols=cols, seed=9000 + idx))
+                idx += 1
+    return pts
+
+
 def sweep_points() -> List[Workload]:
     """The 90-point crossover sweep, in a fixed order (op, dtype, cols, bytes)."""
     pts = []
