@@ -105,6 +105,27 @@ def test_softmax_matches_torch_f64():
     np.testing.assert_allclose(oracle.softmax(x), ref, rtol=1e-12, atol=0)
 
 
+def test_softmax_with_logits_masked_to_the_lowest_float():
+    # logits masked with the lowest finite float32 (as a masked fill does):
+    # those entries are exactly 0 and the rest is the softmax of the unmasked
+    # entries alone (torch float64 on the subset); a fully masked row is
+    # uniform, 1/N exactly
+    low = float(np.finfo(np.float32).min)
+    x = _rand(3, 64, 11, scale=3.0)
+    mask = np.zeros_like(x, dtype=bool)
+    mask[0, ::3] = True
+    mask[1, 1:] = True
+    mask[2, :] = True
+    x[mask] = low
+    y = oracle.softmax(x)
+    assert np.all(y[0][mask[0]] == 0.0) and np.all(y[1][mask[1]] == 0.0)
+    for r in (0, 1):
+        keep = ~mask[r]
+        ref = torch.softmax(torch.from_numpy(x[r][keep]), dim=-1).numpy()
+        np.testing.assert_allclose(y[r][keep], ref, rtol=1e-12, atol=0)
+    assert np.all(y[2] == 1.0 / 64)
+
+
 def test_softmax_nan_propagates_to_row():
     x = _rand(2, 16, 4)
     x[1, 5] = np.nan

@@ -349,6 +349,27 @@ def test_masked_runs_of_logits(op):
         _check(inp, _run(inp, path, p), "masked %s %s P=%d" % (op, path, p))
 
 
+@pytest.mark.parametrize("op,dt", [("softmax", "f32"), ("softmax", "bf16"), ("softmax_bwd", "f32"),
+                                   ("softmax_bwd", "bf16")])
+def test_logits_masked_to_the_lowest_finite_value(op, dt):
+    # A masked fill with the dtype's lowest finite value (float32 -3.4028e38,
+    # bf16 -3.3895e38): x - max lies below -FLT_MAX / log2 e, where the product
+    # x log2 e overflows; such entries must come out 0.  Rows half masked,
+    # all but ~1% masked, and fully masked (a uniform softmax).
+    w = W.custom(op, dt, 48, 8192, seed=78)
+    inp = W.generate(w)
+    rng = np.random.default_rng(78)
+    fill = np.float32(np.finfo(np.float32).min) if dt == "f32" else np.uint16(0xFF7F)
+    for r in range(w.rows):
+        kind = r % 3
+        mask = rng.random(w.cols) < (0.5 if kind == 0 else 0.99)
+        if kind == 2:
+            mask[:] = True
+        inp.x[r, mask] = fill
+    for path, p in [("auto", 0), ("single", 0), ("split", 2), ("split", 4), ("reread", 0)]:
+        _check(inp, _run(inp, path, p), "lowest-fill %s %s %s P=%d" % (op, dt, path, p))
+
+
 def test_nan_propagates_to_its_row_only():
     C = _lib()
     inp = W.generate(W.custom("softmax", "f32", 4, 4096, seed=9))

@@ -245,7 +245,8 @@ __device__ __forceinline__ float wave_max(float v)
 // the product is split as t + c, t = fl(d * L) with L = fl(log2 e), and
 // c = (d * L - t) + d * (log2 e - L) (the first term exact by FMA), so
 // exp(d) = 2^t * 2^c with |c| < 2^-20 and 2^c = 1 + c ln 2 to within 1e-13.
-// 2^t uses the hardware v_exp_f32.
+// 2^t uses the hardware v_exp_f32; where d * L overflows to -inf the result
+// is 0.
 //
 // exp_fast: 2^(d * L) only; used where the output is bf16.
 // ---------------------------------------------------------------------------
@@ -255,7 +256,13 @@ __device__ __forceinline__ float exp_acc(float d)
     const float Llo = 1.925963033500011e-08f;          // log2 e - L
     const float Ln2 = 0.693147180559945309f;
     float t = d * L;
-    float c = __builtin_fmaf(d, L, -t) + d * Llo;
+    // |c| < 2^-20 wherever d * L is finite.  Below d = -FLT_MAX / log2 e (a
+    // logit masked with a value near -FLT_MAX, minus the row maximum; every
+    // caller passes d <= 0) t overflows to -inf and the exact product minus t
+    // makes c = +inf (NaN for d = -inf): the clamp (minnum returns the number)
+    // turns the result into 2^-inf * (1 + ln 2) = 0 there and changes nothing
+    // elsewhere.  A NaN d still gives NaN through 2^t.
+    float c = fminf(__builtin_fmaf(d, L, -t) + d * Llo, 1.0f);
     return __builtin_amdgcn_exp2f(t) * __builtin_fmaf(c, Ln2, 1.0f);
 }
 
