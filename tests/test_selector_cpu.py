@@ -183,3 +183,20 @@ def test_control_fit_recovers_launch_and_per_wave_cost():
     from wide_reduction_reuse_amd.ctrlbench import fit_line
     a, b = fit_line([1, 2, 4, 8, 16], [3.0 + 0.5 * w for w in (1, 2, 4, 8, 16)])
     assert abs(a - 3.0) < 1e-12 and abs(b - 0.5) < 1e-12
+
+
+def test_calibration_merges_repeated_timings_by_geometric_mean():
+    from wide_reduction_reuse_amd import calibrate as K
+    plan = {"path": 1, "split_p": 1, "block_threads": 512, "items": 2, "vec_bytes": 16, "wgs_per_cu": -1}
+
+    def rec(rows, ms):
+        return {"op": "softmax", "dtype": "f32", "rows": rows, "cols": 4096,
+                "candidates": [{"plan": plan, "median_ms": ms}]}
+    records = [rec(100, 0.010), rec(1000, 0.050), rec(100, 0.040)]  # 100 rows timed twice
+    table = K.build_table(records)
+    assert len(table) == 1
+    row = table[0]
+    assert row[:9] == [0, 0, 4096, 1, 1, 512, 2, 16, -1] and row[9] == 2
+    assert row[10] == 100 and row[11] == pytest.approx(math.sqrt(10.0 * 40.0), rel=1e-4)
+    assert row[12] == 1000 and row[13] == pytest.approx(50.0)
+    assert K.unique_shapes(records) == 2

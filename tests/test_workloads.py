@@ -59,3 +59,23 @@ def test_outliers_and_row_offsets():
     means = x.mean(axis=1)
     assert means.min() < -20 and means.max() > 20 and np.abs(means).max() <= 51
     assert abs((x - means[:, None]).std() - 4.0) < 0.1
+
+
+def test_scored_widths_are_never_calibrated():
+    # the selector is scored on shapes the calibration never timed: the sweep
+    # and off-grid widths at their sizes, the further workloads' grid rows
+    calib = W.calibration_points() + W.calibration_points_mid() + W.calibration_points_odd()
+    calib_next = W.calibration_points_next() + W.calibration_points_next_more()
+    timed = {(p.op, p.dtype, p.rows, p.cols) for p in calib + calib_next}
+    for p in W.sweep_points() + W.next_points() + W.offgrid_points() + W.offgrid_points_next():
+        assert (p.op, p.dtype, p.rows, p.cols) not in timed, p.name
+    calib_cols = {p.cols for p in calib + calib_next}
+    assert not calib_cols & set(W.OFFGRID_COLS)
+
+
+def test_offgrid_widths_cover_aligned_and_odd_rows():
+    aligned = [c for c in W.OFFGRID_COLS if (c * 2) % 16 == 0]
+    odd = [c for c in W.OFFGRID_COLS if (c * 4) % 16 != 0]
+    assert len(aligned) >= 6 and len(odd) >= 3
+    assert all(c % 2 == 1 for c in W.CALIB_ODD_COLS + W.CALIB_ODD_MID_COLS)
+    assert all(c % 256 == 0 for c in W.CALIB_MID_COLS)
