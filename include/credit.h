@@ -279,8 +279,11 @@ credit_status_t credit_flush(void *buf, int64_t bytes, void *stream);
  * (op, dtype, cols) with its median kernel time at several row counts.  A shape
  * whose (op, dtype, cols) the table measured is planned from it (each
  * candidate's time interpolated piecewise linearly in log rows / log time,
- * the fastest chosen); other shapes use the analytic model.  NULL clears it
- * (back to the analytic model alone).  Returns CREDIT_ERR_NO_CALIBRATION if the
+ * the fastest chosen).  At another width each legal plan is priced from the
+ * same plan's measurements at the nearest measured widths below and above
+ * (read at the row count that moves the same bytes, interpolated in log
+ * width); only where the table measured none of the legal plans does the
+ * analytic model decide.  NULL clears it (back to the analytic model alone).  Returns CREDIT_ERR_NO_CALIBRATION if the
  * file is missing or malformed, in which case the previous calibration stays
  * in force.  If the environment variable CREDIT_CALIB names a file, it is
  * loaded before the first plan unless a calibration was loaded explicitly.
