@@ -111,6 +111,24 @@ def test_named_workload(name, path, p):
     _check(inp, out, "%s %s P=%d" % (name, path, p), rows)
 
 
+@pytest.mark.parametrize("op,dt,rows,cols", [("softmax", "f32", 9000, 131072),
+                                             ("rmsnorm", "bf16", 17000, 131072)])
+def test_tensors_beyond_4_gib(op, dt, rows, cols):
+    # 4.4 GiB inputs and outputs (the bf16 one holds more than 2^31
+    # elements): row and slice offsets past every 32-bit limit, on the
+    # selected plan; the oracle on rows spread over the whole tensor, the
+    # last one included
+    import torch
+    w = W.custom(op, dt, rows, cols, seed=91)
+    assert w.rows * w.cols * (4 if dt == "f32" else 2) > (4 << 30)
+    inp = W.generate(w)
+    out = _run(inp)
+    sample = np.unique(np.concatenate([np.arange(0, rows, 997), [rows // 2, rows - 2, rows - 1]]))
+    out = {k: (None if v is None else v[sample]) for k, v in out.items()}
+    _check(inp, out, "beyond 4 GiB %s %s %dx%d" % (op, dt, rows, cols), sample)
+    torch.cuda.empty_cache()
+
+
 def test_single_row_too_wide_is_refused():
     C = _lib()
     inp = W.generate(W.NAMED["softmax_f32_256x262144"].with_shape(2, 262144))
