@@ -101,7 +101,11 @@ typedef struct {
     int32_t split_p;       /* workgroups per row: 1 for paths 1 and 3 */
     int32_t block_threads; /* threads per row owner: 64 = one wavefront per row */
     int32_t items;         /* vectors per thread held (paths 1, 2) or streamed per step (path 3) */
-    int32_t vec_bytes;     /* bytes per global access: 16, or one element for rows not 16-B multiples */
+    int32_t vec_bytes;     /* bytes per global access (0 in a plan passed in = the row's own): 16 for
+                              rows of whole 16-byte vectors; for other rows one element, except
+                              that paths 1 and 2 of softmax, LayerNorm, RMSNorm and softmax
+                              backward hold rows whose byte length is a multiple of 4 as 16-byte
+                              vectors, the last one partial (its missing elements masked) */
     int32_t wgs_per_cu;    /* paths 1, 2: 0 = as many workgroups as the device holds at once, each
                               owner looping over rows (and loading the next row while writing the
                               current one); k > 0 = at most k per CU; path 1 only: -1 = one

@@ -181,6 +181,27 @@ def test_selector_legality_on_cpu():
     assert C.lib().credit_select_path(4, 1, 1, 1, ctypes.byref(C.Plan())) == 2  # LayerNorm backward bf16
 
 
+def test_partial_rows_are_held_as_16_byte_vectors():
+    # byte length a multiple of 4 but not of 16: softmax, LayerNorm, RMSNorm
+    # and softmax backward hold the row as 16-byte vectors (the last partial)
+    # and reread it by element; the other operators use one-element tiles
+    L = C.lib()
+    for op, dt, cols in [("softmax", "f32", 1001), ("layernorm", "bf16", 1002), ("rmsnorm", "f32", 3),
+                         ("softmax_bwd", "bf16", 30006)]:
+        p = C.credit_plan(op, dt, 64, cols, "single")
+        assert p.vec_bytes == 16
+        assert C.credit_plan(op, dt, 64, cols, "reread").vec_bytes == 16 // (4 if dt == "f32" else 8)
+        # the one-element held tile of that width is refused for such rows
+        plan = C.Plan.make(C.PATH_SINGLE_WG, 1, p.block_threads, p.items, 4 if dt == "f32" else 2)
+        assert L.credit_run_plan(C.OPS[op], _ops(x=A, dy=G, gamma=G, beta=G, y=B), 4, cols, 1e-5,
+                                 C.DTYPES[dt], ctypes.byref(plan), None) == 4
+    p = C.credit_plan("softmax", "f32", 64, 100006, "split", 8)
+    assert p.vec_bytes == 16
+    assert C.credit_plan("quantize_int8", "f32", 64, 1001, "single").vec_bytes == 4
+    assert C.credit_plan("layernorm_bwd", "f32", 64, 1001, "single").vec_bytes == 4
+    assert C.credit_plan("rmsnorm", "bf16", 64, 1001, "single").vec_bytes == 2  # odd bytes / 4
+
+
 def test_selector_legality_of_the_further_workloads():
     # x and dy held: path 1 holds at most 32768 fp32 columns (two inputs)
     for op in ("softmax_bwd", "layernorm_bwd"):

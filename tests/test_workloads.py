@@ -64,7 +64,8 @@ def test_outliers_and_row_offsets():
 def test_scored_widths_are_never_calibrated():
     # the selector is scored on shapes the calibration never timed: the sweep
     # and off-grid widths at their sizes, the further workloads' grid rows
-    calib = W.calibration_points() + W.calibration_points_mid() + W.calibration_points_odd()
+    calib = (W.calibration_points() + W.calibration_points_mid() + W.calibration_points_odd() +
+             W.calibration_points_part())
     calib_next = W.calibration_points_next() + W.calibration_points_next_more()
     timed = {(p.op, p.dtype, p.rows, p.cols) for p in calib + calib_next}
     for p in W.sweep_points() + W.next_points() + W.offgrid_points() + W.offgrid_points_next():
@@ -78,4 +79,8 @@ def test_offgrid_widths_cover_aligned_and_odd_rows():
     odd = [c for c in W.OFFGRID_COLS if (c * 4) % 16 != 0]
     assert len(aligned) >= 6 and len(odd) >= 3
     assert all(c % 2 == 1 for c in W.CALIB_ODD_COLS + W.CALIB_ODD_MID_COLS)
+    # bf16 rows ending in a partial 16-byte vector: even, not whole vectors
+    assert any((c * 2) % 16 != 0 and c % 2 == 0 for c in W.OFFGRID_COLS)
+    assert all((c * 2) % 16 != 0 and c % 2 == 0 for c in W.CALIB_PART_COLS)
+    assert len(set(W.CALIB_PART_COLS)) == 12
     assert all(c % 256 == 0 for c in W.CALIB_MID_COLS)

@@ -41,10 +41,11 @@ const std::vector<KernelEntry> &registry()
     return table;
 }
 
-const KernelEntry *find_kernel(int kind, int op, int dt, int vb, int block, int items)
+const KernelEntry *find_kernel(int kind, int op, int dt, int vb, int block, int items, bool part = false)
 {
     for (const KernelEntry &e : registry())
-        if (e.kind == kind && e.op == op && e.dt == dt && e.vb == vb && e.block == block && e.items == items)
+        if (e.kind == kind && e.op == op && e.dt == dt && e.vb == vb && e.block == block && e.items == items &&
+            e.part == part)
             return &e;
     return nullptr;
 }
@@ -419,10 +420,15 @@ credit_status_t launch_split(const KernelEntry *k, const RowArgs &a0, int p, int
 credit_status_t resolve_plan(int op, int dt, int64_t cols, const credit_plan_t &plan, const KernelEntry **out,
                              int *kind_out)
 {
-    const int vb = vec_bytes_for(dt, cols);
+    if (plan.path < CREDIT_PATH_SINGLE_WG || plan.path > CREDIT_PATH_REREAD)
+        return CREDIT_ERR_INVALID_ARG;
+    // a partial row (byte length a multiple of 4, not of 16) is held as
+    // 16-byte vectors, the last one partial, and reread by element
+    const bool part = plan.path != CREDIT_PATH_REREAD && row_is_partial(op, dt, cols);
+    const int vb = path_vec_bytes(op, dt, cols, plan.path);
     if (plan.vec_bytes != 0 && plan.vec_bytes != vb)
         return CREDIT_ERR_ILLEGAL_PATH;
-    const int64_t nv = cols * elem_bytes(dt) / vb;
+    const int64_t nv = (cols * elem_bytes(dt) + vb - 1) / vb;
     int kind = 0;
     int64_t need = nv;
     switch (plan.path) {
@@ -444,7 +450,7 @@ credit_status_t resolve_plan(int op, int dt, int64_t cols, const credit_plan_t &
     default:
         return CREDIT_ERR_INVALID_ARG;
     }
-    const KernelEntry *k = find_kernel(kind, op, dt, vb, plan.block_threads, plan.items);
+    const KernelEntry *k = find_kernel(kind, op, dt, vb, plan.block_threads, plan.items, part);
     if (k == nullptr)
         return CREDIT_ERR_UNSUPPORTED;
     if (need > static_cast<int64_t>(plan.block_threads) * plan.items)
@@ -497,9 +503,10 @@ credit_status_t run_plan_checked(int op, const credit_operands_t &t, int64_t row
     a.cols = cols;
     a.eps = eps;
     if (log_enabled())
-        std::fprintf(stderr, "[credit] op=%d dt=%d rows=%lld cols=%lld path=%d p=%d block=%d items=%d vb=%d%s\n",
+        std::fprintf(stderr, "[credit] op=%d dt=%d rows=%lld cols=%lld path=%d p=%d block=%d items=%d vb=%d%s%s\n",
                      op, dt, static_cast<long long>(rows), static_cast<long long>(cols), plan.path, plan.split_p,
-                     plan.block_threads, plan.items, k->vb, control ? " (control)" : "");
+                     plan.block_threads, plan.items, k->vb, k->part ? " (partial last vector)" : "",
+                     control ? " (control)" : "");
     if (kind == kKindSplit)
         return launch_split(k, a, plan.split_p, stats_per_partial(op), plan.wgs_per_cu, s, ev);
     return launch_rowwise(k, a, plan.wgs_per_cu, s, ev);

@@ -1,5 +1,6 @@
 // Instantiates every tile of the ladders in registry.hpp for one operator and
-// storage type, plus the work-free control twin of every split tile.
+// storage type, plus the work-free control twin of every split tile and, for
+// the operators with them, the PART kernels of the 16-byte held tiles.
 #pragma once
 
 #include "kernels.hpp"
@@ -29,6 +30,12 @@ void register_op_dtype(std::vector<KernelEntry> &v)
     CREDIT_K(kKindSplit, VS, b, it, split_kernel<OP, T, VS, b, it, false>); \
     CREDIT_K(kKindControl, VS, b, it, split_kernel<OP, T, VS, b, it, true>);
 #define REREAD1E(b, it) CREDIT_K(kKindReread, VS, b, it, reread_kernel<OP, T, VS, b, it>);
+#define CREDIT_KP(kind, vb, block, items, ...)                                                                  \
+    if constexpr (op_has_part(OP) && tile_enabled(OP, kind, block, items, vb))                                    \
+        v.push_back(KernelEntry{kind, OP, DT, vb, block, items, reinterpret_cast<const void *>(&__VA_ARGS__), true})
+#define WAVEP(it) CREDIT_KP(kKindWave, VB, 64, it, single_wave_kernel<OP, T, VB, it, true>);
+#define WGP(b, it) CREDIT_KP(kKindWg, VB, b, it, single_wg_kernel<OP, T, VB, b, it, true>);
+#define SPLITP(b, it) CREDIT_KP(kKindSplit, VB, b, it, split_kernel<OP, T, VB, b, it, false, true>);
 
     CREDIT_WAVE_TILES(WAVE)
     CREDIT_WG_TILES(WG)
@@ -38,6 +45,9 @@ void register_op_dtype(std::vector<KernelEntry> &v)
     CREDIT_WG_TILES_1E(WG1E)
     CREDIT_SPLIT_TILES_1E(SPLIT1E)
     CREDIT_REREAD_TILES_1E(REREAD1E)
+    CREDIT_WAVE_TILES(WAVEP)
+    CREDIT_WG_TILES(WGP)
+    CREDIT_SPLIT_TILES(SPLITP)
 
 #undef WAVE
 #undef WG
@@ -47,6 +57,10 @@ void register_op_dtype(std::vector<KernelEntry> &v)
 #undef WG1E
 #undef SPLIT1E
 #undef REREAD1E
+#undef WAVEP
+#undef WGP
+#undef SPLITP
+#undef CREDIT_KP
 #undef CREDIT_K
 }
 

@@ -45,6 +45,8 @@
 // the iteration in between, i.e. after every member has read this buffer.
 #pragma once
 
+#include <type_traits>
+
 #include "args.hpp"
 #include "common.hpp"
 #include "ops.hpp"
@@ -295,10 +297,10 @@ struct ParamCache {
 // the operator reduces over them.  (A second, unmasked copy for full waves
 // behind a wave-uniform branch was measured to raise register use by a third
 // with no gain: the masks are register selects.)
-template <OpKind OP, class T, int VB, int IT, int W, int OWNER>
+template <OpKind OP, class T, int VB, int IT, int W, int OWNER, class L>
 __device__ __forceinline__ typename OpTraits<OP>::Partial tile_partial(
     Tile<T, VB, IT> (&t)[OpTraits<OP>::kIn], int kv, const ParamCache<OP, T, VB, IT, W, OWNER> &pc, int pos,
-    Local &loc)
+    L &loc)
 {
     using Op = OpTraits<OP>;
     if constexpr (Op::kParamsInReduce) {
@@ -448,17 +450,53 @@ __device__ __forceinline__ rsrc_t span(const void *base, int64_t first, int64_t 
     return make_rsrc(reinterpret_cast<const void *>(p), static_cast<uint32_t>(nvec * VB));
 }
 
+// Vectors [first, first + nvec) of row `row`.  PEB = 0: rows of nv whole
+// vectors.  PEB = element bytes (a PART kernel): rows of `cols` elements, the
+// last vector partial, and the descriptor ends at the row's last byte.  On
+// MI355X a descriptor's range check acts per dword (a straddling 16-byte load
+// returns its in-row dwords and zeros, a straddling store writes only its
+// in-row dwords) and 16-byte accesses at 4-byte alignment are served, so such
+// rows keep 16-byte vectors when their byte length is a multiple of 4.
+template <int VB, int PEB>
+__device__ __forceinline__ rsrc_t row_span(const void *base, int64_t row, int64_t cols, int64_t nv,
+                                           int64_t first, int64_t nvec)
+{
+    if constexpr (PEB == 0) {
+        return span<VB>(base, row * nv + first, nvec);
+    } else {
+        constexpr int E = VB / PEB;
+        const int64_t e0 = first * E;
+        int64_t ne = cols - e0;
+        ne = ne < nvec * E ? ne : nvec * E;
+        ne = ne > 0 ? ne : 0;
+        const uintptr_t p = reinterpret_cast<uintptr_t>(base) + static_cast<uintptr_t>((row * cols + e0) * PEB);
+        return make_rsrc(reinterpret_cast<const void *>(p), static_cast<uint32_t>(ne * PEB));
+    }
+}
+
 // The row inputs (x, and dy for two-input operators): `nvec` vectors from
-// vector `first` of row `row` (nv vectors per row).
-template <OpKind OP, int VB>
+// vector `first` of row `row` (nv vectors per row; PEB as for row_span).
+template <OpKind OP, int VB, int PEB = 0>
 __device__ __forceinline__ Srcs<OpTraits<OP>::kIn> row_srcs(const RowArgs &a, int64_t row, int64_t nv,
                                                             int64_t first, int64_t nvec)
 {
     Srcs<OpTraits<OP>::kIn> s;
-    s.r[0] = span<VB>(a.x, row * nv + first, nvec);
+    s.r[0] = row_span<VB, PEB>(a.x, row, a.cols, nv, first, nvec);
     if constexpr (OpTraits<OP>::kIn >= 2)
-        s.r[1] = span<VB>(a.dy, row * nv + first, nvec);
+        s.r[1] = row_span<VB, PEB>(a.dy, row, a.cols, nv, first, nvec);
     return s;
+}
+
+// The thread's index (among its vectors k, at slice positions pos + k * G) of
+// the slice's last vector, when that vector is the row's partial last one
+// (`last` = the slice ends the row); -1 otherwise.
+template <int IT, int G>
+__device__ __forceinline__ int partial_index(int64_t ns, int pos, bool last)
+{
+    const int64_t d = ns - 1 - pos;
+    if (!last || d < 0 || d % G != 0 || d / G >= IT)
+        return -1;
+    return static_cast<int>(d / G);
 }
 
 // The per-row output (quantization scale) of `row`, written by one lane.
@@ -479,34 +517,44 @@ __device__ __forceinline__ void store_row_value(const RowArgs &a, int64_t row, c
 // of the grid handles rows w, w + W, w + 2W, ... (W waves in the grid).  No
 // barrier on the row: the wave reduction is the row reduction.
 // ---------------------------------------------------------------------------
-template <OpKind OP, class T, int VB, int IT>
+// PART: rows whose last vector is partial (see row_span).
+template <OpKind OP, class T, int VB, int IT, bool PART = false>
 __global__ __launch_bounds__(kWave *kWaveRowsPerWg) void single_wave_kernel(RowArgs a)
 {
     using Op = OpTraits<OP>;
     using PC = ParamCache<OP, T, VB, IT, kWave, kOwnerWaves>;
+    using Loc = std::conditional_t<PART, LocalPart, Local>;
     constexpr int E = VB / StorageTraits<T>::kBytes;
     constexpr int VBO = out_vb<OP, T, VB>();
+    constexpr int PEB = PART ? StorageTraits<T>::kBytes : 0;
+    static_assert(!PART || VBO == VB, "PART rows need outputs of the input's element size");
     __shared__ RawVec<VB> lds_params[param_lds_vectors<OP, VB, IT, kWave, kOwnerWaves>()];
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t nv = a.cols / E;
+    const int64_t nv = PART ? (a.cols + E - 1) / E : a.cols / E;
     const int64_t waves = static_cast<int64_t>(gridDim.x) * kWaveRowsPerWg;
     int64_t row = uniform(static_cast<int64_t>(blockIdx.x) * kWaveRowsPerWg + threadIdx.x / kWave);
     Tile<T, VB, IT> t[Op::kIn];
-    load_tile<T, VB, IT, kWave>(t, row_srcs<OP, VB>(a, row, nv, 0, row < a.rows ? nv : 0), lane);
+    load_tile<T, VB, IT, kWave>(t, row_srcs<OP, VB, PEB>(a, row, nv, 0, row < a.rows ? nv : 0), lane);
     PC pc;
-    pc.init(span<VB>(a.gamma, 0, nv), span<VB>(a.beta, 0, nv), lane, lds_params, threadIdx.x,
-            kWave * kWaveRowsPerWg);
+    pc.init(row_span<VB, PEB>(a.gamma, 0, a.cols, nv, 0, nv), row_span<VB, PEB>(a.beta, 0, a.cols, nv, 0, nv),
+            lane, lds_params, threadIdx.x, kWave * kWaveRowsPerWg);
     if constexpr (PC::kMode == kParamLds)
         __syncthreads();
     const int kv = count_valid<IT, kWave>(nv, lane);
+    Loc loc0;
+    if constexpr (PART) {
+        loc0.ntail = static_cast<int>(a.cols % E);
+        loc0.kpart = partial_index<IT, kWave>(nv, lane, loc0.ntail != 0);
+    }
     for (; row < a.rows; row += waves) {
         const int64_t next = row + waves;
-        Local loc;
+        Loc loc = loc0;
         const auto wp = tile_partial<OP, T, VB, IT, kWave, kOwnerWaves>(t, kv, pc, lane, loc);
         const Coef c = Op::template finalize<T>(wp, loc, a.cols, a.eps);
         store_row_value<OP>(a, row, c, lane == 0);
-        const auto nsrc = row_srcs<OP, VB>(a, next, nv, 0, next < a.rows ? nv : 0);
-        store_tile<OP, T, VB, IT, kWave, kOwnerWaves>(t, span<VBO>(a.y, row * nv, nv), pc, lane, c, nsrc);
+        const auto nsrc = row_srcs<OP, VB, PEB>(a, next, nv, 0, next < a.rows ? nv : 0);
+        store_tile<OP, T, VB, IT, kWave, kOwnerWaves>(t, row_span<VBO, PEB>(a.y, row, a.cols, nv, 0, nv), pc, lane,
+                                                      c, nsrc);
         load_next<OP, T, VB, IT, kWave, kOwnerWaves>(t, nsrc, lane);
     }
 }
@@ -515,36 +563,45 @@ __global__ __launch_bounds__(kWave *kWaveRowsPerWg) void single_wave_kernel(RowA
 // Path 1b: one workgroup of BLOCK threads per row; workgroup g handles rows
 // g, g + G, g + 2G, ... (G workgroups in the grid).
 // ---------------------------------------------------------------------------
-template <OpKind OP, class T, int VB, int BLOCK, int IT>
+template <OpKind OP, class T, int VB, int BLOCK, int IT, bool PART = false>
 __global__ __launch_bounds__(BLOCK) void single_wg_kernel(RowArgs a)
 {
     using Op = OpTraits<OP>;
     using PC = ParamCache<OP, T, VB, IT, BLOCK, kOwnerRow>;
+    using Loc = std::conditional_t<PART, LocalPart, Local>;
     constexpr int E = VB / StorageTraits<T>::kBytes;
+    constexpr int PEB = PART ? StorageTraits<T>::kBytes : 0;
     constexpr int NW = BLOCK / kWave;
     constexpr int VBO = out_vb<OP, T, VB>();
     __shared__ typename Op::Partial sh[NW];
     __shared__ RawVec<VB> lds_params[param_lds_vectors<OP, VB, IT, BLOCK, kOwnerRow>()];
     const int tid = threadIdx.x;
     const int pos = (tid / kWave) * kWave * IT + (tid & (kWave - 1));  // this wave's run + lane
-    const int64_t nv = a.cols / E;
+    const int64_t nv = PART ? (a.cols + E - 1) / E : a.cols / E;
     int64_t row = blockIdx.x;
     Tile<T, VB, IT> t[Op::kIn];
-    load_tile<T, VB, IT, kWave>(t, row_srcs<OP, VB>(a, row, nv, 0, nv), pos);
+    load_tile<T, VB, IT, kWave>(t, row_srcs<OP, VB, PEB>(a, row, nv, 0, nv), pos);
     PC pc;
-    pc.init(span<VB>(a.gamma, 0, nv), span<VB>(a.beta, 0, nv), pos, lds_params, tid, BLOCK);
+    pc.init(row_span<VB, PEB>(a.gamma, 0, a.cols, nv, 0, nv), row_span<VB, PEB>(a.beta, 0, a.cols, nv, 0, nv), pos,
+            lds_params, tid, BLOCK);
     if constexpr (PC::kMode == kParamLds)
         __syncthreads();
     const int kv = count_valid<IT, kWave>(nv, pos);
+    Loc loc0;
+    if constexpr (PART) {
+        loc0.ntail = static_cast<int>(a.cols % E);
+        loc0.kpart = partial_index<IT, kWave>(nv, pos, loc0.ntail != 0);
+    }
     for (; row < a.rows; row += gridDim.x) {
         const int64_t next = row + gridDim.x;
-        Local loc;
+        Loc loc = loc0;
         const auto wp = tile_partial<OP, T, VB, IT, BLOCK, kOwnerRow>(t, kv, pc, pos, loc);
         const auto rp = block_combine<OP, NW>(wp, sh);
         const Coef c = Op::template finalize<T>(rp, loc, a.cols, a.eps);
         store_row_value<OP>(a, row, c, tid == 0);
-        const auto nsrc = row_srcs<OP, VB>(a, next, nv, 0, next < a.rows ? nv : 0);
-        store_tile<OP, T, VB, IT, BLOCK, kOwnerRow>(t, span<VBO>(a.y, row * nv, nv), pc, pos, c, nsrc);
+        const auto nsrc = row_srcs<OP, VB, PEB>(a, next, nv, 0, next < a.rows ? nv : 0);
+        store_tile<OP, T, VB, IT, BLOCK, kOwnerRow>(t, row_span<VBO, PEB>(a.y, row, a.cols, nv, 0, nv), pc, pos, c,
+                                                     nsrc);
         load_next<OP, T, VB, IT, BLOCK, kOwnerRow>(t, nsrc, pos);
         // the next block_combine rewrites sh: every wave must have read it
         __syncthreads();
@@ -557,13 +614,16 @@ __global__ __launch_bounds__(BLOCK) void single_wg_kernel(RowArgs a)
 // reductions (over zero tiles), but no access to rows, parameters or outputs
 // at all (the control launch passes null pointers for them).
 // ---------------------------------------------------------------------------
-template <OpKind OP, class T, int VB, int BLOCK, int IT, bool CONTROL>
+template <OpKind OP, class T, int VB, int BLOCK, int IT, bool CONTROL, bool PART = false>
 __global__ __launch_bounds__(BLOCK) void split_kernel(SplitArgs a)
 {
     using Op = OpTraits<OP>;
     using Partial = typename Op::Partial;
     using PC = ParamCache<OP, T, VB, IT, BLOCK, kOwnerSlice>;
+    using Loc = std::conditional_t<PART, LocalPart, Local>;
     constexpr int E = VB / StorageTraits<T>::kBytes;
+    constexpr int PEB = PART ? StorageTraits<T>::kBytes : 0;
+    static_assert(!(PART && CONTROL), "the control twin touches no row");
     constexpr int NW = BLOCK / kWave;
     constexpr int Q = Op::kQ;
     constexpr int VBO = out_vb<OP, T, VB>();
@@ -582,7 +642,7 @@ __global__ __launch_bounds__(BLOCK) void split_kernel(SplitArgs a)
     const int64_t k = ticket / static_cast<uint32_t>(P);
     const int c = static_cast<int>(ticket % static_cast<uint32_t>(P));
 
-    const int64_t nv = a.r.cols / E;
+    const int64_t nv = PART ? (a.r.cols + E - 1) / E : a.r.cols / E;
     const int64_t per = (nv + P - 1) / P;
     const int64_t v0 = min(nv, per * c);
     const int64_t ns = min(nv, v0 + per) - v0;  // vectors in this slice
@@ -599,8 +659,9 @@ __global__ __launch_bounds__(BLOCK) void split_kernel(SplitArgs a)
             for (int j = 0; j < IT; ++j)
                 t[i].v[j] = RawVec<VB>{};
     } else {
-        load_tile<T, VB, IT, kWave>(t, row_srcs<OP, VB>(a.r, k, nv, v0, k < a.r.rows ? ns : 0), pos);
-        pc.init(span<VB>(a.r.gamma, v0, ns), span<VB>(a.r.beta, v0, ns), pos, lds_params, tid, BLOCK);
+        load_tile<T, VB, IT, kWave>(t, row_srcs<OP, VB, PEB>(a.r, k, nv, v0, k < a.r.rows ? ns : 0), pos);
+        pc.init(row_span<VB, PEB>(a.r.gamma, 0, a.r.cols, nv, v0, ns), row_span<VB, PEB>(a.r.beta, 0, a.r.cols, nv, v0, ns),
+                pos, lds_params, tid, BLOCK);
         if constexpr (PC::kMode == kParamLds)
             __syncthreads();
     }
@@ -611,10 +672,15 @@ __global__ __launch_bounds__(BLOCK) void split_kernel(SplitArgs a)
     // sequence, which lets the compiler wait for each held vector precisely
     // instead of conservatively (measured: 3% on RMSNorm bf16 split plans; the
     // kernels that do not roll gain nothing from it and are not peeled).
+    Loc loc0;
+    if constexpr (PART) {
+        loc0.ntail = static_cast<int>(a.r.cols % E);
+        loc0.kpart = partial_index<IT, kWave>(ns, pos, loc0.ntail != 0 && v0 + ns == nv);
+    }
     auto step = [&](int64_t row, uint32_t it) __attribute__((always_inline)) {
         const int64_t next = row + a.clusters;
         Partial wp;
-        Local loc;
+        Loc loc = loc0;
         if constexpr (CONTROL)
             wp = Op::template wave_partial<T, VB, IT>(t, kv, loc);
         else
@@ -651,9 +717,9 @@ __global__ __launch_bounds__(BLOCK) void split_kernel(SplitArgs a)
             (void)next;
         } else {
             store_row_value<OP>(a.r, row, cf, c == 0 && tid == 0);
-            const auto nsrc = row_srcs<OP, VB>(a.r, next, nv, v0, next < a.r.rows ? ns : 0);
-            store_tile<OP, T, VB, IT, BLOCK, kOwnerSlice>(t, span<VBO>(a.r.y, row * nv + v0, ns), pc, pos, cf,
-                                                          nsrc);
+            const auto nsrc = row_srcs<OP, VB, PEB>(a.r, next, nv, v0, next < a.r.rows ? ns : 0);
+            store_tile<OP, T, VB, IT, BLOCK, kOwnerSlice>(t, row_span<VBO, PEB>(a.r.y, row, a.r.cols, nv, v0, ns), pc,
+                                                          pos, cf, nsrc);
             load_next<OP, T, VB, IT, BLOCK, kOwnerSlice>(t, nsrc, pos);
         }
         // (no barrier needed before the next row rewrites sh or peer: every

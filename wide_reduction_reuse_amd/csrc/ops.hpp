@@ -66,8 +66,30 @@ struct Coef {
 // softmax family keeps the maximum of each group of the thread's vectors
 // (ref_groups of them), to which the fp32 tile's exponentials are relative.
 struct Local {
+    static constexpr bool kPartial = false;
     float m[4];
 };
+
+// The same, for rows that are not whole vectors (see the kernels' PART mode):
+// the row's last vector holds only ntail valid elements (the rest were loaded
+// as zeros from past the row's end); kpart is its index among this thread's
+// vectors, -1 when the thread does not hold it.
+struct LocalPart : Local {
+    static constexpr bool kPartial = true;
+    int kpart = -1;
+    int ntail = 0;
+};
+
+// Whether element e of the thread's vector k is part of the row (only the
+// partial last vector of a PART row has elements that are not).
+template <class L>
+__device__ __forceinline__ bool elem_in_row(const L &loc, int k, int e)
+{
+    if constexpr (L::kPartial)
+        return k != loc.kpart || e < loc.ntail;
+    else
+        return true;
+}
 
 // Vector groups of a held tile of IT vectors reduced one after another (see
 // softmax_groups).
@@ -137,8 +159,8 @@ __device__ __forceinline__ void fence_vec(RawVec<VB> &v)
 // grouping measured 1-2% slower on MI355X): every exponential is taken
 // against the wave maximum.  Either way loc.m holds the reference maximum of
 // each group's exponentials (the wave maximum for all of them, ungrouped).
-template <bool DY, class T, int VB, int IT, int NI>
-__device__ __forceinline__ Part<DY ? 3 : 2> softmax_groups(Tile<T, VB, IT> (&t)[NI], int kvalid, Local &loc)
+template <bool DY, class T, int VB, int IT, int NI, class L>
+__device__ __forceinline__ Part<DY ? 3 : 2> softmax_groups(Tile<T, VB, IT> (&t)[NI], int kvalid, L &loc)
 {
     constexpr int E = Tile<T, VB, IT>::kEpv;
     constexpr bool kGrouped = !DY && is_f32<T>();
@@ -153,7 +175,7 @@ __device__ __forceinline__ Part<DY ? 3 : 2> softmax_groups(Tile<T, VB, IT> (&t)[
             if (k < kvalid)
 #pragma unroll
                 for (int e = 0; e < E; ++e)
-                    mt = fmaxf(mt, elem<T, VB>(t[0].v[k], e));
+                    mt = fmaxf(mt, elem_in_row(loc, k, e) ? elem<T, VB>(t[0].v[k], e) : -INFINITY);
         mw = wave_max(mt);
         fence_tile(t[0]);
     }
@@ -167,7 +189,8 @@ __device__ __forceinline__ Part<DY ? 3 : 2> softmax_groups(Tile<T, VB, IT> (&t)[
                 if (g * GS + j < kvalid)
 #pragma unroll
                     for (int e = 0; e < E; ++e)
-                        gm = fmaxf(gm, elem<T, VB>(t[0].v[g * GS + j], e));
+                        gm = fmaxf(gm, elem_in_row(loc, g * GS + j, e) ? elem<T, VB>(t[0].v[g * GS + j], e)
+                                                                       : -INFINITY);
 #pragma unroll
             for (int j = 0; j < GS; ++j)
                 fence_vec(t[0].v[g * GS + j]);
@@ -179,7 +202,8 @@ __device__ __forceinline__ Part<DY ? 3 : 2> softmax_groups(Tile<T, VB, IT> (&t)[
             if (k < kvalid)
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
-                    const float ex = exp_for<T>(elem<T, VB>(t[0].v[k], e) - gm);
+                    const float ex =
+                        elem_in_row(loc, k, e) ? exp_for<T>(elem<T, VB>(t[0].v[k], e) - gm) : 0.0f;
                     if constexpr (is_f32<T>())
                         set_word<VB>(t[0].v[k], e, __float_as_uint(ex));
                     sv += ex;
@@ -237,8 +261,8 @@ struct OpTraits<kSoftmax> {
     template <class T> using Out = T;
     using Partial = Part<kQ>;
 
-    template <class T, int VB, int IT>
-    __device__ __forceinline__ static Partial wave_partial(Tile<T, VB, IT> (&t)[kIn], int kvalid, Local &loc)
+    template <class T, int VB, int IT, class L>
+    __device__ __forceinline__ static Partial wave_partial(Tile<T, VB, IT> (&t)[kIn], int kvalid, L &loc)
     {
         return softmax_groups<false, T, VB, IT>(t, kvalid, loc);
     }
@@ -343,8 +367,8 @@ struct OpTraits<kLayerNorm> {
     template <class T> using Out = T;
     using Partial = Part<kQ>;
 
-    template <class T, int VB, int IT>
-    __device__ __forceinline__ static Partial wave_partial(Tile<T, VB, IT> (&tt)[kIn], int kvalid, Local &)
+    template <class T, int VB, int IT, class L>
+    __device__ __forceinline__ static Partial wave_partial(Tile<T, VB, IT> (&tt)[kIn], int kvalid, L &loc)
     {
         Tile<T, VB, IT> &t = tt[0];
         constexpr int E = Tile<T, VB, IT>::kEpv;
@@ -355,7 +379,11 @@ struct OpTraits<kLayerNorm> {
 #pragma unroll
                 for (int e = 0; e < E; ++e)
                     sum += elem<T, VB>(t.v[k], e);
-        const float nw = wave_sum(static_cast<float>(kvalid * E));
+        int nvalid = kvalid * E;
+        if constexpr (L::kPartial)
+            if (loc.kpart >= 0 && loc.kpart < kvalid)
+                nvalid -= E - loc.ntail;  // the partial vector's zeros are no elements
+        const float nw = wave_sum(static_cast<float>(nvalid));
         const float sw = wave_sum(sum);
         const float mean = nw > 0.0f ? sw / nw : 0.0f;
         fence_tile(t);
@@ -365,7 +393,7 @@ struct OpTraits<kLayerNorm> {
             if (k < kvalid)
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
-                    float d = elem<T, VB>(t.v[k], e) - mean;
+                    float d = elem_in_row(loc, k, e) ? elem<T, VB>(t.v[k], e) - mean : 0.0f;
                     m2 = __builtin_fmaf(d, d, m2);
                 }
         return Partial{{nw, mean, wave_sum(m2)}};
@@ -476,8 +504,8 @@ struct OpTraits<kRmsNorm> {
     template <class T> using Out = T;
     using Partial = Part<kQ>;
 
-    template <class T, int VB, int IT>
-    __device__ __forceinline__ static Partial wave_partial(Tile<T, VB, IT> (&tt)[kIn], int kvalid, Local &)
+    template <class T, int VB, int IT, class L>
+    __device__ __forceinline__ static Partial wave_partial(Tile<T, VB, IT> (&tt)[kIn], int kvalid, L &)
     {
         Tile<T, VB, IT> &t = tt[0];
         constexpr int E = Tile<T, VB, IT>::kEpv;
@@ -567,8 +595,8 @@ struct OpTraits<kSoftmaxBwd> {
     template <class T> using Out = T;
     using Partial = Part<kQ>;
 
-    template <class T, int VB, int IT>
-    __device__ __forceinline__ static Partial wave_partial(Tile<T, VB, IT> (&t)[kIn], int kvalid, Local &loc)
+    template <class T, int VB, int IT, class L>
+    __device__ __forceinline__ static Partial wave_partial(Tile<T, VB, IT> (&t)[kIn], int kvalid, L &loc)
     {
         return softmax_groups<true, T, VB, IT>(t, kvalid, loc);
     }
@@ -696,8 +724,8 @@ struct OpTraits<kLayerNormBwd> {
             set_word<VB>(t[1].v[k], e, __float_as_uint(elem<T, VB>(gv, e) * elem<T, VB>(t[1].v[k], e)));
     }
 
-    template <class T, int VB, int IT>
-    __device__ __forceinline__ static Partial wave_partial(Tile<T, VB, IT> (&t)[kIn], int kvalid, Local &)
+    template <class T, int VB, int IT, class L>
+    __device__ __forceinline__ static Partial wave_partial(Tile<T, VB, IT> (&t)[kIn], int kvalid, L &)
     {
         constexpr int E = Tile<T, VB, IT>::kEpv;
         float sx = 0.0f, sg = 0.0f;
@@ -849,8 +877,8 @@ struct OpTraits<kQuantInt8> {
     template <class T> using Out = i8_t;
     using Partial = Part<kQ>;
 
-    template <class T, int VB, int IT>
-    __device__ __forceinline__ static Partial wave_partial(Tile<T, VB, IT> (&t)[kIn], int kvalid, Local &)
+    template <class T, int VB, int IT, class L>
+    __device__ __forceinline__ static Partial wave_partial(Tile<T, VB, IT> (&t)[kIn], int kvalid, L &)
     {
         constexpr int E = Tile<T, VB, IT>::kEpv;
         float a = 0.0f;

@@ -31,6 +31,25 @@ int vec_bytes_for(int dt, int64_t cols)
     return (cols * elem_bytes(dt)) % 16 == 0 ? 16 : elem_bytes(dt);
 }
 
+bool row_is_partial(int op, int dt, int64_t cols)
+{
+    const int64_t bytes = cols * elem_bytes(dt);
+    return op_has_part(op) && bytes % 16 != 0 && bytes % 4 == 0;
+}
+
+int held_vec_bytes(int op, int dt, int64_t cols) { return row_is_partial(op, dt, cols) ? 16 : vec_bytes_for(dt, cols); }
+
+int path_vec_bytes(int op, int dt, int64_t cols, int path)
+{
+    return path == kPathReread ? vec_bytes_for(dt, cols) : held_vec_bytes(op, dt, cols);
+}
+
+int64_t held_vectors(int op, int dt, int64_t cols)
+{
+    const int64_t vb = held_vec_bytes(op, dt, cols);
+    return (cols * elem_bytes(dt) + vb - 1) / vb;
+}
+
 // ---------------------------------------------------------------------------
 // Tile ladders: the same X-macro lists the kernel instantiations expand.
 // ---------------------------------------------------------------------------
@@ -88,8 +107,6 @@ const std::vector<TileSpec> &tiles_for(int kind, int vb_is_16)
     return it->second;
 }
 
-static int64_t vectors_in_row(int dt, int64_t cols, int vb) { return cols * elem_bytes(dt) / vb; }
-
 // Preference among tiles that can hold `nv` vectors: the smallest capacity,
 // and within a capacity the one closest to 2 vectors per thread (then more
 // threads); measured on MI355X, two 16-byte vectors per thread over many
@@ -133,8 +150,8 @@ static std::vector<TileSpec> single_ladder(int op, int vb)
 
 bool single_tile(int op, int dt, int64_t cols, TileSpec *out)
 {
-    const int vb = vec_bytes_for(dt, cols);
-    const int64_t nv = vectors_in_row(dt, cols, vb);
+    const int vb = held_vec_bytes(op, dt, cols);
+    const int64_t nv = held_vectors(op, dt, cols);
     const std::vector<TileSpec> ladder = single_ladder(op, vb);
     TileSpec t;
     if (!pick_holding_tile(ladder, nv, &t))
@@ -148,8 +165,8 @@ bool split_tile(int op, int dt, int64_t cols, int p, TileSpec *out)
 {
     if (p != 2 && p != 4 && p != 8)
         return false;
-    const int vb = vec_bytes_for(dt, cols);
-    const int64_t nv = vectors_in_row(dt, cols, vb);
+    const int vb = held_vec_bytes(op, dt, cols);
+    const int64_t nv = held_vectors(op, dt, cols);
     const int64_t per = (nv + p - 1) / p;
     if (per * (p - 1) >= nv)
         return false;  // the last slice would be empty: too narrow to split p ways
@@ -168,7 +185,7 @@ bool split_tile(int op, int dt, int64_t cols, int p, TileSpec *out)
 TileSpec reread_tile(int dt, int64_t cols)
 {
     const int vb = vec_bytes_for(dt, cols);
-    const int64_t nv = vectors_in_row(dt, cols, vb);
+    const int64_t nv = cols * elem_bytes(dt) / vb;
     const auto &ladder = tiles_for(kKindReread, vb == 16);
     TileSpec t = ladder.front();
     if (vb == 16) {
@@ -350,7 +367,8 @@ namespace {
 // Plan from the calibration table when it measured this (op, dtype, cols)
 // and holds a candidate the forced path / P allow: every such candidate's
 // time at req.rows is interpolated from its measurements, and the fastest
-// wins.  Returns false when the table cannot decide.
+// wins.  Returns false when the table cannot decide, or measured this width
+// with an access width no longer planned (then the neighbours price it).
 bool plan_from_table(const PlanRequest &req, const Calibration &cal, int forced_path, int forced_p, Plan *out)
 {
     Plan p;
@@ -363,6 +381,8 @@ bool plan_from_table(const PlanRequest &req, const Calibration &cal, int forced_
             continue;
         if (forced_p != 0 && e.path == kPathSplit && e.split_p != forced_p)
             continue;
+        if (e.vb != path_vec_bytes(req.op, req.dt, req.cols, e.path))
+            return false;  // measured with an access width no longer planned: price from the neighbours
         const double us = calib_time_us(e, static_cast<double>(req.rows));
         PathEstimate &pe = p.est[e.path - 1];
         if (!pe.legal || us < pe.us) {
@@ -390,20 +410,29 @@ bool plan_from_table(const PlanRequest &req, const Calibration &cal, int forced_
 // plan's measurements at the nearest calibrated widths below and above:
 // each is read at the row count that moves the same bytes, and the two are
 // interpolated in (log cols, log time); one side alone is used as it is.
+// A held plan (paths 1, 2) runs partial-vector kernels on rows that end in a
+// partial 16-byte vector, which stream slower than whole-vector rows: such
+// widths are priced from each other, whole-vector widths likewise, and the
+// other kind serves only where the plan was never measured on the same kind.
 // Negative when the table never measured the plan.
 double neighbour_time_us(const PlanRequest &req, const Calibration &cal, const Candidate &cd)
 {
     const CalibEntry *lo = nullptr, *hi = nullptr;
-    for (const CalibEntry &e : cal.table) {
-        if (e.op != req.op || e.dt != req.dt || e.path != cd.path || e.split_p != cd.split_p ||
-            e.block != cd.est.tile.block || e.items != cd.est.tile.items || e.vb != cd.est.tile.vb ||
-            e.wgs_per_cu != cd.wgs_per_cu || e.rows.empty())
-            continue;
-        if (e.cols <= req.cols && (lo == nullptr || e.cols > lo->cols))
-            lo = &e;
-        if (e.cols >= req.cols && (hi == nullptr || e.cols < hi->cols))
-            hi = &e;
-    }
+    const bool held = cd.path != kPathReread;
+    const bool part = held && row_is_partial(req.op, req.dt, req.cols);
+    for (int same_kind = 1; same_kind >= 0 && lo == nullptr && hi == nullptr; --same_kind)
+        for (const CalibEntry &e : cal.table) {
+            if (e.op != req.op || e.dt != req.dt || e.path != cd.path || e.split_p != cd.split_p ||
+                e.block != cd.est.tile.block || e.items != cd.est.tile.items || e.vb != cd.est.tile.vb ||
+                e.wgs_per_cu != cd.wgs_per_cu || e.rows.empty())
+                continue;
+            if (same_kind && held && row_is_partial(e.op, e.dt, e.cols) != part)
+                continue;
+            if (e.cols <= req.cols && (lo == nullptr || e.cols > lo->cols))
+                lo = &e;
+            if (e.cols >= req.cols && (hi == nullptr || e.cols < hi->cols))
+                hi = &e;
+        }
     const double bytes_rows = static_cast<double>(req.rows) * static_cast<double>(req.cols);
     auto at = [&](const CalibEntry *e) { return calib_time_us(*e, bytes_rows / static_cast<double>(e->cols)); };
     if (lo == nullptr && hi == nullptr)
@@ -521,9 +550,12 @@ static bool worth_holding(const std::vector<TileSpec> &ladder, const TileSpec &t
 void enumerate_candidates(const PlanRequest &req, const Calibration &cal, std::vector<Candidate> *out)
 {
     out->clear();
-    const int vb = vec_bytes_for(req.dt, req.cols);
+    // held tiles (paths 1, 2) and the reread tiles of path 3 can differ in
+    // access width: a partial row is held as 16-byte vectors, reread by element
+    const int vb = held_vec_bytes(req.op, req.dt, req.cols);
     const bool v16 = vb == 16;
-    const int64_t nv = vectors_in_row(req.dt, req.cols, vb);
+    const int64_t nv = held_vectors(req.op, req.dt, req.cols);
+    const int rvb = vec_bytes_for(req.dt, req.cols);
     const std::vector<TileSpec> held = single_ladder(req.op, vb);
     PathEstimate best1;
     for (int kind : {kKindWave, kKindWg})
@@ -538,8 +570,8 @@ void enumerate_candidates(const PlanRequest &req, const Calibration &cal, std::v
                 best1 = e;
         }
     PathEstimate best3;
-    for (TileSpec t : tiles_for(kKindReread, v16)) {
-        t.vb = vb;
+    for (TileSpec t : tiles_for(kKindReread, rvb == 16)) {
+        t.vb = rvb;
         const PathEstimate e = estimate_reread(req, cal, t);
         out->push_back(Candidate{kPathReread, 1, e, 0});
         if (!best3.legal || e.us < best3.us)

@@ -116,6 +116,16 @@ bool op_supported(int op, int dt);  // a compiled (operator, dtype) pair
 // Bytes per global access for a row of `cols` elements: 16 when the row's byte
 // length is a multiple of 16 (rows stay 16-byte aligned), else one element.
 int vec_bytes_for(int dt, int64_t cols);
+// Rows whose byte length is a multiple of 4 but not of 16, of an operator
+// with PART kernels: paths 1 and 2 hold them as 16-byte vectors whose last
+// one is partial (PART kernels mask its missing elements).
+bool row_is_partial(int op, int dt, int64_t cols);
+// Bytes per access of the held tiles (paths 1, 2): 16 for partial rows too.
+int held_vec_bytes(int op, int dt, int64_t cols);
+// Bytes per access that `path` (kPathSingle / kPathSplit / kPathReread) uses.
+int path_vec_bytes(int op, int dt, int64_t cols, int path);
+// Vectors of held_vec_bytes covering a row, the last one possibly partial.
+int64_t held_vectors(int op, int dt, int64_t cols);
 
 // Tile ladders, mirroring the compiled instantiations.
 const std::vector<TileSpec> &tiles_for(int kind, int vb_is_16);

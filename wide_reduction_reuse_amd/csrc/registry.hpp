@@ -18,7 +18,13 @@ struct KernelEntry {
     int block;  // threads per row owner (64 for wave-per-row)
     int items;  // vectors held per thread (paths 1, 2) or streamed per step (path 3)
     const void *fn;
+    bool part = false;  // rows whose last 16-byte vector is partial (PART kernels)
 };
+
+// Operators with PART kernels: their partials mask the partial vector's
+// elements (softmax, LayerNorm, RMSNorm, softmax backward); the others keep
+// one-element tiles for rows that are not whole vectors.
+constexpr bool op_has_part(int op) { return op <= 3; }
 
 void register_softmax_kernels(std::vector<KernelEntry> &out);
 void register_layernorm_kernels(std::vector<KernelEntry> &out);

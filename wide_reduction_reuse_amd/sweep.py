@@ -102,6 +102,8 @@ def points(which: str, ops=None, min_cols: int = 0):
         pts += W.calibration_points_mid()
     if which in ("calib_odd", "calib_all"):
         pts += W.calibration_points_odd()
+    if which in ("calib_part", "calib_all"):
+        pts += W.calibration_points_part()
     if which == "offgrid":
         pts += W.offgrid_points() + W.offgrid_points_next()
     if ops:
@@ -112,7 +114,8 @@ def points(which: str, ops=None, min_cols: int = 0):
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--points", default="named", choices=("named", "sweep", "next", "all", "calib", "calib_next", "calib_next_more",
-                                                         "calib_mid", "calib_odd", "calib_all", "offgrid"))
+                                                         "calib_mid", "calib_odd", "calib_part", "calib_all",
+                                                         "offgrid"))
     ap.add_argument("--ops", nargs="*", default=None)
     ap.add_argument("--min-cols", type=int, default=0, help="only shapes at least this wide")
     ap.add_argument("--out", default="-")

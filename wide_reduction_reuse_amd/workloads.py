@@ -138,7 +138,8 @@ def next_points() -> List[Workload]:
 
 
 OFFGRID_COLS = (3072, 12288, 24576, 49152, 98304, 196608,  # rows of whole 16-byte vectors
-                1000, 5000, 30001, 50257, 100003)            # and of odd lengths
+                1000, 5000, 30001, 50257, 100003,            # and of odd lengths
+                20002)                                       # a partial last vector in both dtypes
 OFFGRID_BYTES = 256 << 20
 
 
@@ -187,6 +188,10 @@ def calibration_points() -> List[Workload]:
 CALIB_MID_COLS = tuple(round(2 ** (k + 0.5) / 256) * 256 for k in range(10, 18))  # 1536 ... 185344
 CALIB_ODD_COLS = tuple((1 << k) + 1 for k in (10, 12, 14, 16, 17, 18))  # 1025 ... 262145
 CALIB_ODD_MID_COLS = tuple(round(2 ** (k + 0.5)) | 1 for k in (10, 12, 14, 15, 16, 17))  # 1449 ... 185365
+# Even bf16 widths that are not multiples of 8 elements: their rows end in a
+# partial 16-byte vector (the fp32 rows of the odd widths above do too).
+CALIB_PART_COLS = (tuple((1 << k) + 2 for k in (10, 12, 14, 16, 17, 18)) +                       # 1026 ... 262146
+                   tuple(round(2 ** (k + 0.5)) // 8 * 8 + 2 for k in (10, 12, 14, 15, 16, 17)))  # 1450 ... 185362
 
 
 def calibration_points_mid() -> List[Workload]:
@@ -221,6 +226,31 @@ def calibration_points_odd() -> List[Workload]:
                     pts.append(Workload("calibo%03d_%s_%s_%dx%d" % (idx, op, dt, rows, cols), op, dt, rows, cols,
                                         seed=6000 + idx, eps=DEFAULT_EPS[op]))
                     idx += 1
+    return pts
+
+
+def calibration_points_part() -> List[Workload]:
+    """Calibration shapes for bf16 rows that end in a partial 16-byte vector
+    (CALIB_PART_COLS): the forward operators at the sizes of
+    calibration_points(), softmax backward at the rows of
+    calibration_points_next()."""
+    pts = []
+    idx = 0
+    for op in FWD_OPS:
+        for cols in CALIB_PART_COLS:
+            for nbytes in CALIB_BYTES:
+                rows = max(1, nbytes // (cols * ELEM_BYTES["bf16"]))
+                pts.append(Workload("calibp%03d_%s_bf16_%dx%d" % (idx, op, rows, cols), op, "bf16", rows, cols,
+                                    seed=9000 + idx, eps=DEFAULT_EPS[op]))
+                idx += 1
+    base = NAMED["softmax_bwd_f32_4096x65536"]
+    for cols in CALIB_PART_COLS:
+        for rows in CALIB_NEXT_ROWS:
+            if rows * cols * ELEM_BYTES["bf16"] <= CALIB_NEXT_MAX_BYTES:
+                pts.append(dataclasses.replace(
+                    base, name="calibp%03d_softmax_bwd_bf16_%dx%d" % (idx, rows, cols), dtype="bf16",
+                    rows=rows, cols=cols, seed=9000 + idx))
+                idx += 1
     return pts
 
 
