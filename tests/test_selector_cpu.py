@@ -200,3 +200,18 @@ def test_calibration_merges_repeated_timings_by_geometric_mean():
     assert row[10] == 100 and row[11] == pytest.approx(math.sqrt(10.0 * 40.0), rel=1e-4)
     assert row[12] == 1000 and row[13] == pytest.approx(50.0)
     assert K.unique_shapes(records) == 2
+
+
+def test_calibration_extension_keeps_base_rows_and_merges_shared_ones():
+    from wide_reduction_reuse_amd import calibrate as K
+    base = [[0, 0, 4096, 1, 1, 512, 2, 16, -1, 2, 100, 10.0, 1000, 50.0],
+            [2, 1, 8192, 1, 1, 64, 16, 16, 0, 1, 64, 5.0]]
+    new = [[0, 0, 4096, 1, 1, 512, 2, 16, -1, 2, 100, 40.0, 4000, 190.0],   # same plan: 100 rows again, 4000 new
+           [0, 1, 1026, 1, 1, 256, 4, 16, -1, 1, 8192, 7.0]]              # a plan the base never measured
+    t = K.merge_tables(base, new)
+    assert [r[:9] for r in t] == sorted([r[:9] for r in base] + [new[1][:9]])
+    shared = next(r for r in t if r[:3] == [0, 0, 4096])
+    assert shared[9] == 3 and shared[10] == 100 and shared[11] == pytest.approx(20.0)
+    assert shared[12:] == [1000, 50.0, 4000, 190.0]
+    assert next(r for r in t if r[:3] == [2, 1, 8192]) == base[1]
+    assert next(r for r in t if r[:3] == [0, 1, 1026]) == new[1]

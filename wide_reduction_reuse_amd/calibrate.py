@@ -1,6 +1,6 @@
 """Selector calibration: measured candidates to a calibration file.
 
-    python -m wide_reduction_reuse_amd.calibrate --out FILE [--sweep SWEEP.jsonl ...] [--run]
+    python -m wide_reduction_reuse_amd.calibrate --out FILE [--sweep SWEEP.jsonl ...] [--run] [--base FILE]
 
 With --run it first times every legal plan on the calibration shapes
 (workloads.calibration_points(): the crossover sweep's operators, dtypes and
@@ -19,7 +19,10 @@ interpolates these in (log rows, log time) for the rows it is asked about
 (the CREDIT paper prices a schedule at the rate measured for it rather than a
 device peak, Sec. III-D, Eq. 7; here every candidate is measured the same way).
 The analytic model's streaming bandwidth is set to the best rate measured on
-the largest calibration shapes.
+the largest calibration shapes.  --base FILE extends an existing calibration
+file instead: its table rows are kept, the sweep records add rows, and a row
+both hold gets, at each row count, the geometric mean of the two times (the
+base's scalars, control-kernel costs and streaming rate are kept).
 """
 from __future__ import annotations
 
@@ -54,6 +57,33 @@ def build_table(records):
     return table
 
 
+def merge_tables(base, new):
+    """Rows of `base` and `new` (build_table's format) keyed by their first nine
+    fields; a key in both gets, per row count, the geometric mean of the two
+    times, and the row counts only one of them measured as they are."""
+    def points(row):
+        n = row[9]
+        return {row[10 + 2 * i]: row[11 + 2 * i] for i in range(n)}
+    merged = {tuple(r[:9]): points(r) for r in base}
+    for r in new:
+        key = tuple(r[:9])
+        pts = points(r)
+        if key in merged:
+            old = merged[key]
+            for n, t in pts.items():
+                old[n] = round(math.sqrt(old[n] * t), 4) if n in old else t
+        else:
+            merged[key] = pts
+    table = []
+    for key in sorted(merged):
+        pts = merged[key]
+        row = list(key) + [len(pts)]
+        for n in sorted(pts):
+            row += [n, pts[n]]
+        table.append(row)
+    return table
+
+
 def unique_shapes(records) -> int:
     return len({(r["op"], r["dtype"], r["rows"], r["cols"]) for r in records})
 
@@ -69,6 +99,21 @@ def device_info():
     return {}
 
 
+def write_calibration(path: str, cal: dict) -> None:
+    """The calibration file: scalars first, then one table row per line."""
+    with open(path, "w") as f:
+        f.write("{\n")
+        f.write(' "version": 2,\n "source": %s,\n "stream_gbs": %s,\n' % (json.dumps(cal["source"]), cal["stream_gbs"]))
+        for k in ("launch_us", "exchange_us"):
+            if k in cal:
+                f.write(' "%s": %s,\n' % (k, cal[k]))
+        if "device" in cal:
+            f.write(' "device": %s,\n' % json.dumps(cal["device"]))
+        f.write(' "table": [\n')
+        f.write(",\n".join("  " + json.dumps(row) for row in cal["table"]))
+        f.write("\n ]\n}\n")
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--out", required=True)
@@ -76,6 +121,7 @@ def main(argv=None) -> int:
     ap.add_argument("--run", action="store_true", help="time the calibration shapes first (needs a GPU)")
     ap.add_argument("--steps", type=int, default=15)
     ap.add_argument("--ctrl", default=None, help="control-kernel fit (ctrlbench.py output)")
+    ap.add_argument("--base", default=None, help="calibration file to extend with the sweep records")
     a = ap.parse_args(argv)
     if a.run:
         from . import sweep
@@ -92,6 +138,17 @@ def main(argv=None) -> int:
     if not a.sweep:
         ap.error("--sweep FILE is required")
     records = [json.loads(l) for path in a.sweep for l in open(path) if l.strip()]
+    if a.base:
+        with open(a.base) as f:
+            base = json.load(f)
+        n_shapes = unique_shapes(records)
+        cal = dict(base)
+        cal["table"] = merge_tables(base["table"], build_table(records))
+        cal["source"] = "%s; extended with %d more calibration shapes" % (base["source"], n_shapes)
+        write_calibration(a.out, cal)
+        print("wrote %s: %d candidates (%d from %s, %d shapes added)" % (a.out, len(cal["table"]), len(base["table"]),
+                                                                        a.base, n_shapes), file=sys.stderr)
+        return 0
     biggest = max(r["bytes"] for r in records)
     stream = max(r["bytes"] / (c["median_ms"] * 1e-3) / 1e9 for r in records if r["bytes"] == biggest
                  for c in r["candidates"])
@@ -110,17 +167,7 @@ def main(argv=None) -> int:
         cal["exchange_us"] = summ[-1]["exchange_us"]
     if dev.get("cus"):
         cal["device"] = {"cus": dev["cus"]}
-    with open(a.out, "w") as f:
-        f.write("{\n")
-        f.write(' "version": 2,\n "source": %s,\n "stream_gbs": %s,\n' % (json.dumps(cal["source"]), cal["stream_gbs"]))
-        for k in ("launch_us", "exchange_us"):
-            if k in cal:
-                f.write(' "%s": %s,\n' % (k, cal[k]))
-        if "device" in cal:
-            f.write(' "device": %s,\n' % json.dumps(cal["device"]))
-        f.write(' "table": [\n')
-        f.write(",\n".join("  " + json.dumps(row) for row in cal["table"]))
-        f.write("\n ]\n}\n")
+    write_calibration(a.out, cal)
     print("wrote %s: %d candidates over %d shapes (%d records)" % (a.out, len(cal["table"]), n_shapes, len(records)),
           file=sys.stderr)
     return 0
