@@ -21,6 +21,10 @@
  *     must be 16-byte aligned, except scale (4-byte).  gamma, beta, dy and a
  *     floating-point output have the same dtype as x.  In-place operation
  *     (output == x, or dx == dy) is allowed; any other overlap is undefined.
+ *     bf16 softmax and softmax backward on rows of odd length read whole
+ *     4-byte words: when rows * cols is odd, the 2 bytes after the last
+ *     element of x (and dy) are read, never written, and never affect the
+ *     result (they lie in the same aligned 4-byte word as that element).
  *   - Calls are asynchronous and stream-ordered on `stream` (a hipStream_t;
  *     NULL means the default stream).  A successful return means the work was
  *     enqueued; device faults surface at the caller's next synchronization.
@@ -105,7 +109,11 @@ typedef struct {
                               rows of whole 16-byte vectors; for other rows one element, except
                               that paths 1 and 2 of softmax, LayerNorm, RMSNorm and softmax
                               backward hold rows whose byte length is a multiple of 4 as 16-byte
-                              vectors, the last one partial (its missing elements masked) */
+                              vectors, the last one partial (its missing elements masked), and
+                              paths 1 and 2 of bf16 softmax and softmax backward hold odd-length
+                              rows as 16-byte vectors from the 4-byte word below the row's start
+                              (the neighbouring rows' elements in it masked; that shared word is
+                              written one 2-byte half at a time) */
     int32_t wgs_per_cu;    /* paths 1, 2: 0 = as many workgroups as the device holds at once, each
                               owner looping over rows (and loading the next row while writing the
                               current one); k > 0 = at most k per CU; path 1 only: -1 = one

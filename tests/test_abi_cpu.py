@@ -202,6 +202,26 @@ def test_partial_rows_are_held_as_16_byte_vectors():
     assert C.credit_plan("rmsnorm", "bf16", 64, 1001, "single").vec_bytes == 2  # odd bytes / 4
 
 
+def test_odd_bf16_rows_of_the_softmax_family_are_held_as_16_byte_vectors():
+    # bf16 rows of odd length: softmax and softmax backward (no parameter
+    # vectors) hold them as 16-byte vectors from the 4-byte word below the
+    # row's start on paths 1 and 2 and reread them by element; operators with
+    # parameters and the quantizer keep one-element tiles
+    L = C.lib()
+    for op, cols in [("softmax", 1), ("softmax", 1001), ("softmax", 50257), ("softmax_bwd", 30001)]:
+        p = C.credit_plan(op, "bf16", 64, cols, "single")
+        assert p.vec_bytes == 16
+        assert p.block_threads * p.items * 8 >= cols + 1  # the held span has one more element
+        assert C.credit_plan(op, "bf16", 64, cols, "reread").vec_bytes == 2
+        plan = C.Plan.make(C.PATH_SINGLE_WG, 1, p.block_threads, p.items, 2)
+        assert L.credit_run_plan(C.OPS[op], _ops(x=A, dy=G, y=B), 4, cols, 0.0, C.DTYPES["bf16"],
+                                 ctypes.byref(plan), None) == 4
+    assert C.credit_plan("softmax", "bf16", 64, 100003, "split", 8).vec_bytes == 16
+    for op in ("layernorm", "rmsnorm", "quantize_int8"):
+        assert C.credit_plan(op, "bf16", 64, 1001, "single").vec_bytes == 2
+    assert C.credit_plan("softmax", "f32", 64, 1001, "single").vec_bytes == 16  # a partial row, not odd
+
+
 def test_selector_legality_of_the_further_workloads():
     # x and dy held: path 1 holds at most 32768 fp32 columns (two inputs)
     for op in ("softmax_bwd", "layernorm_bwd"):

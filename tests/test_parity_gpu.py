@@ -281,6 +281,100 @@ def test_every_tile_partial_last_vector(op, dt, kind, block, items, p, cols):
 
 
 # ---------------------------------------------------------------------------
+# odd-length bf16 rows: the held tiles of softmax and softmax backward hold
+# them as 16-byte vectors from the 4-byte word below the row's start (odd
+# rows start in the middle of a word, even rows end in one); the shared word
+# is written by halves
+# ---------------------------------------------------------------------------
+ODD_ROW_OPS = ("softmax", "softmax_bwd")
+
+
+def _odd_tile_cases():
+    cases = []
+    ladders = {"wave": _ladder("CREDIT_WAVE_TILES"), "wg": _ladder("CREDIT_WG_TILES"),
+               "split": _ladder("CREDIT_SPLIT_TILES")}
+    i = 0
+    for op in ODD_ROW_OPS:
+        for kind, tiles in ladders.items():
+            for block, items in tiles:
+                cap = block * items
+                for fill in ("ragged", "full"):
+                    ntail = (1, 3, 5, 7)[i % 4]  # elements of the last vector of an even row
+                    i += 1
+                    if kind == "split":
+                        for p in (2, 4, 8):
+                            nv = p * cap - 3 * p - 1 if fill == "ragged" else p * cap
+                            cases.append((op, kind, block, items, p, (nv - 1) * 8 + ntail))
+                    else:
+                        nv = cap - 3 if fill == "ragged" else cap
+                        cases.append((op, kind, block, items, 1, (nv - 1) * 8 + ntail))
+    return cases
+
+
+ODD_TILE_CASES = _odd_tile_cases()
+
+
+@pytest.mark.parametrize("op,kind,block,items,p,cols", ODD_TILE_CASES,
+                         ids=["%s-%s%dx%d-p%d-c%d" % c for c in ODD_TILE_CASES])
+def test_every_tile_odd_length_bf16(op, kind, block, items, p, cols):
+    # Rows of both parities (an odd row count), owners looping over rows as in
+    # test_every_tile; the row's first and last elements sit at a different
+    # thread and item in each case.
+    C = _lib()
+    rows = {"wave": 1101, "wg": 301, "split": 301}[kind]
+    if cols * rows > 24_000_000:
+        rows = max(5, 24_000_000 // cols) | 1
+    w = W.custom(op, "bf16", rows, cols, seed=zlib.crc32(("odd%s%s%d%d%d%d" % (op, kind, block, items, p, cols)).encode()) % 10000,
+                 x_dist="scaled_shifted", x_scale=3.0, x_shift=0.5)
+    inp = W.generate(w)
+    path = C.PATH_SPLIT_ROW if kind == "split" else C.PATH_SINGLE_WG
+    plan = C.Plan.make(path, p, block, items, 16, wgs_per_cu=1)
+    if _tile_excluded(op, kind, block, items):
+        with pytest.raises(C.CreditError) as ei:
+            _run(inp, plan=plan)
+        assert ei.value.status == 2
+        return
+    out = _run(inp, plan=plan)
+    _check(inp, out, "odd-length tile %s %dx%d p=%d %s cols=%d" % (kind, block, items, p, op, cols))
+
+
+@pytest.mark.parametrize("cols", [1, 7, 12291])
+@pytest.mark.parametrize("path,p", [("single", 0), ("split", 2), ("split", 8), ("reread", 0)])
+@pytest.mark.parametrize("op,alias", [("softmax", "x"), ("softmax_bwd", "x"), ("softmax_bwd", "dy")])
+def test_odd_length_bf16_in_place_and_boundary_nan(op, alias, path, p, cols):
+    # The output overwrites an input while the neighbouring rows' owners read
+    # the 4-byte words they share with this row; then NaN in the first and
+    # last elements of some rows (x, and dy for the backward operator) must
+    # stay in those rows.
+    C = _lib()
+    if path == "split" and (cols + 7) // 8 < p:
+        pytest.skip("too narrow to split %d ways" % p)
+    w = W.custom(op, "bf16", 37, cols, seed=cols + 3, x_dist="scaled_shifted", x_scale=3.0, x_shift=0.5)
+    inp = W.generate(w)
+    t = _device_operands(inp)
+    t["y"] = t[alias]
+    out = _run(inp, path, p, t=t)
+    _check(inp, out, "odd in-place y=%s %s %s P=%d cols=%d" % (alias, op, path, p, cols))
+    nan = np.uint16(0x7FC0)
+    bad = (5, 6, 20)
+    inp.x[5, 0] = nan
+    inp.x[6, cols - 1] = nan
+    if inp.dy is not None:
+        inp.dy[20, 0] = nan
+        inp.dy[20, cols - 1] = nan
+    else:
+        inp.x[20, cols - 1] = nan
+    y = _run(inp, path, p)["y"]
+    yf = y.astype(np.uint32) << 16
+    isnan = np.isnan(yf.view(np.float32))
+    for r in range(w.rows):
+        if r in bad:
+            assert isnan[r].all(), "row %d should be NaN" % r
+        else:
+            assert not isnan[r].any(), "NaN leaked into row %d" % r
+
+
+# ---------------------------------------------------------------------------
 # rows whose byte length is not a multiple of 16: partial last vectors
 # (above) and one-element accesses (odd bf16 lengths, int8 quantization,
 # LayerNorm backward, the reread path)
@@ -447,7 +541,7 @@ def test_masked_runs_of_logits(op, cols):
         _check(inp, _run(inp, path, p), "masked %s %s P=%d cols=%d" % (op, path, p, cols))
 
 
-@pytest.mark.parametrize("cols", [8192, 8190])
+@pytest.mark.parametrize("cols", [8192, 8190, 8191])
 @pytest.mark.parametrize("op,dt", [("softmax", "f32"), ("softmax", "bf16"), ("softmax_bwd", "f32"),
                                    ("softmax_bwd", "bf16")])
 def test_logits_masked_to_the_lowest_finite_value(op, dt, cols):
@@ -455,7 +549,7 @@ def test_logits_masked_to_the_lowest_finite_value(op, dt, cols):
     # bf16 -3.3895e38): x - max lies below -FLT_MAX / log2 e, where the product
     # x log2 e overflows; such entries must come out 0.  Rows half masked,
     # all but ~1% masked, and fully masked (a uniform softmax).  8190 columns
-    # end in a partial vector.
+    # end in a partial vector; 8191 bf16 columns are an odd-length row.
     w = W.custom(op, dt, 48, cols, seed=78)
     inp = W.generate(w)
     rng = np.random.default_rng(78)

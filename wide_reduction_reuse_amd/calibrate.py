@@ -22,7 +22,10 @@ The analytic model's streaming bandwidth is set to the best rate measured on
 the largest calibration shapes.  --base FILE extends an existing calibration
 file instead: its table rows are kept, the sweep records add rows, and a row
 both hold gets, at each row count, the geometric mean of the two times (the
-base's scalars, control-kernel costs and streaming rate are kept).
+base's scalars, control-kernel costs and streaming rate are kept).  Base rows
+of a plan the library no longer offers for their width (one it does not
+enumerate, e.g. measured with an access width the planner no longer uses
+there) are dropped.
 """
 from __future__ import annotations
 
@@ -84,6 +87,21 @@ def merge_tables(base, new):
     return table
 
 
+def offered(row) -> bool:
+    """Whether the library still enumerates the plan of a table row for its
+    (op, dtype, cols), at the row's smallest calibrated row count."""
+    from . import credit as C
+    op, dt, cols, path, p, block, items, vb, wpc = row[:9]
+    key = (op, dt, cols, row[10])
+    if key not in _OFFERED:
+        _OFFERED[key] = {(q.path, q.split_p, q.block_threads, q.items, q.vec_bytes)
+                         for q in C.credit_enumerate_plans(op, dt, row[10], cols)}
+    return (path, p, block, items, vb) in _OFFERED[key]
+
+
+_OFFERED = {}
+
+
 def unique_shapes(records) -> int:
     return len({(r["op"], r["dtype"], r["rows"], r["cols"]) for r in records})
 
@@ -143,7 +161,11 @@ def main(argv=None) -> int:
             base = json.load(f)
         n_shapes = unique_shapes(records)
         cal = dict(base)
-        cal["table"] = merge_tables(base["table"], build_table(records))
+        kept = [r for r in base["table"] if offered(r)]
+        if len(kept) != len(base["table"]):
+            print("dropped %d base rows of plans no longer offered" % (len(base["table"]) - len(kept)),
+                  file=sys.stderr)
+        cal["table"] = merge_tables(kept, build_table(records))
         cal["source"] = "%s; extended with %d more calibration shapes" % (base["source"], n_shapes)
         write_calibration(a.out, cal)
         print("wrote %s: %d candidates (%d from %s, %d shapes added)" % (a.out, len(cal["table"]), len(base["table"]),

@@ -41,7 +41,7 @@ const std::vector<KernelEntry> &registry()
     return table;
 }
 
-const KernelEntry *find_kernel(int kind, int op, int dt, int vb, int block, int items, bool part = false)
+const KernelEntry *find_kernel(int kind, int op, int dt, int vb, int block, int items, int part = 0)
 {
     for (const KernelEntry &e : registry())
         if (e.kind == kind && e.op == op && e.dt == dt && e.vb == vb && e.block == block && e.items == items &&
@@ -422,9 +422,10 @@ credit_status_t resolve_plan(int op, int dt, int64_t cols, const credit_plan_t &
 {
     if (plan.path < CREDIT_PATH_SINGLE_WG || plan.path > CREDIT_PATH_REREAD)
         return CREDIT_ERR_INVALID_ARG;
-    // a partial row (byte length a multiple of 4, not of 16) is held as
-    // 16-byte vectors, the last one partial, and reread by element
-    const bool part = plan.path != CREDIT_PATH_REREAD && row_is_partial(op, dt, cols);
+    // a partial row (byte length a multiple of 4, not of 16) and an
+    // odd-length bf16 row of the softmax family are held as 16-byte vectors
+    // (held_row_kind) and reread by element
+    const int part = plan.path != CREDIT_PATH_REREAD ? held_row_kind(op, dt, cols) : 0;
     const int vb = path_vec_bytes(op, dt, cols, plan.path);
     if (plan.vec_bytes != 0 && plan.vec_bytes != vb)
         return CREDIT_ERR_ILLEGAL_PATH;
@@ -505,7 +506,8 @@ credit_status_t run_plan_checked(int op, const credit_operands_t &t, int64_t row
     if (log_enabled())
         std::fprintf(stderr, "[credit] op=%d dt=%d rows=%lld cols=%lld path=%d p=%d block=%d items=%d vb=%d%s%s\n",
                      op, dt, static_cast<long long>(rows), static_cast<long long>(cols), plan.path, plan.split_p,
-                     plan.block_threads, plan.items, k->vb, k->part ? " (partial last vector)" : "",
+                     plan.block_threads, plan.items, k->vb,
+                     k->part == 1 ? " (partial last vector)" : (k->part == 2 ? " (odd bf16 row)" : ""),
                      control ? " (control)" : "");
     if (kind == kKindSplit)
         return launch_split(k, a, plan.split_p, stats_per_partial(op), plan.wgs_per_cu, s, ev);

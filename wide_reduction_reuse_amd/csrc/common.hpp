@@ -124,6 +124,21 @@ __device__ __forceinline__ void buf_store(const RawVec<VB> &v, rsrc_t r, uint32_
     }
 }
 
+// Stores of part of a 16-byte vector (odd-length bf16 rows, whose first or
+// last 4-byte word is shared with the neighbouring row): its words 1..3, and
+// one 16-bit half of a word.
+__device__ __forceinline__ void buf_store_words123(const RawVec<16> &v, rsrc_t r, uint32_t voff)
+{
+    typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+    const u32x3 w = {v.w[1], v.w[2], v.w[3]};
+    __builtin_amdgcn_raw_buffer_store_b96(w, r, static_cast<int>(voff), 0, kStreamStore);
+}
+__device__ __forceinline__ void buf_store_half(uint32_t bits16, rsrc_t r, uint32_t voff)
+{
+    __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(bits16), r, static_cast<int>(voff), 0,
+                                          kStreamStore);
+}
+
 // Make a value the compiler treats as per-lane known to be wave-uniform.
 __device__ __forceinline__ int64_t uniform(int64_t v)
 {

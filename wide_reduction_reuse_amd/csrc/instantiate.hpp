@@ -1,6 +1,6 @@
 // Instantiates every tile of the ladders in registry.hpp for one operator and
 // storage type, plus the work-free control twin of every split tile and, for
-// the operators with them, the PART kernels of the 16-byte held tiles.
+// the operators with them, the PART and ODD kernels of the 16-byte held tiles.
 #pragma once
 
 #include "kernels.hpp"
@@ -32,10 +32,16 @@ void register_op_dtype(std::vector<KernelEntry> &v)
 #define REREAD1E(b, it) CREDIT_K(kKindReread, VS, b, it, reread_kernel<OP, T, VS, b, it>);
 #define CREDIT_KP(kind, vb, block, items, ...)                                                                  \
     if constexpr (op_has_part(OP) && tile_enabled(OP, kind, block, items, vb))                                    \
-        v.push_back(KernelEntry{kind, OP, DT, vb, block, items, reinterpret_cast<const void *>(&__VA_ARGS__), true})
+        v.push_back(KernelEntry{kind, OP, DT, vb, block, items, reinterpret_cast<const void *>(&__VA_ARGS__), 1})
 #define WAVEP(it) CREDIT_KP(kKindWave, VB, 64, it, single_wave_kernel<OP, T, VB, it, true>);
 #define WGP(b, it) CREDIT_KP(kKindWg, VB, b, it, single_wg_kernel<OP, T, VB, b, it, true>);
 #define SPLITP(b, it) CREDIT_KP(kKindSplit, VB, b, it, split_kernel<OP, T, VB, b, it, false, true>);
+#define CREDIT_KO(kind, vb, block, items, ...)                                                                  \
+    if constexpr (op_has_odd(OP) && DT == 1 && tile_enabled(OP, kind, block, items, vb))                          \
+        v.push_back(KernelEntry{kind, OP, DT, vb, block, items, reinterpret_cast<const void *>(&__VA_ARGS__), 2})
+#define WAVEO(it) CREDIT_KO(kKindWave, VB, 64, it, single_wave_kernel<OP, T, VB, it, true, true>);
+#define WGO(b, it) CREDIT_KO(kKindWg, VB, b, it, single_wg_kernel<OP, T, VB, b, it, true, true>);
+#define SPLITO(b, it) CREDIT_KO(kKindSplit, VB, b, it, split_kernel<OP, T, VB, b, it, false, true, true>);
 
     CREDIT_WAVE_TILES(WAVE)
     CREDIT_WG_TILES(WG)
@@ -48,6 +54,9 @@ void register_op_dtype(std::vector<KernelEntry> &v)
     CREDIT_WAVE_TILES(WAVEP)
     CREDIT_WG_TILES(WGP)
     CREDIT_SPLIT_TILES(SPLITP)
+    CREDIT_WAVE_TILES(WAVEO)
+    CREDIT_WG_TILES(WGO)
+    CREDIT_SPLIT_TILES(SPLITO)
 
 #undef WAVE
 #undef WG
@@ -60,6 +69,10 @@ void register_op_dtype(std::vector<KernelEntry> &v)
 #undef WAVEP
 #undef WGP
 #undef SPLITP
+#undef WAVEO
+#undef WGO
+#undef SPLITO
+#undef CREDIT_KO
 #undef CREDIT_KP
 #undef CREDIT_K
 }

@@ -332,15 +332,31 @@ constexpr bool rolls()
     return OWNER == kOwnerSlice && NI == 1 && MODE != kParamDirect;
 }
 
+// The output side of an ODD row (an odd-length bf16 row, held from the
+// 4-byte word below its start): either its first or its last word is shared
+// with the neighbouring row, and only this row's half of that word may be
+// written.  The store descriptor excludes a shared last word; `full` also
+// covers it.  head: the thread's vector 0 starts with the shared first word
+// (the row begins at its upper half).  ktail, dtail: the thread's vector and
+// word whose lower half is the row's last element, in a shared last word
+// (ktail = -1: none).
+struct OddOut {
+    rsrc_t full;
+    int ktail;
+    int dtail;
+    bool head;
+};
+
 // Apply h to the held tile and write it out; dst, and the parameter
 // descriptors, cover the same columns (the row or slice).  When rolling,
 // vector k of the next row (`next`, a zero-length descriptor when there is
 // none: its loads return zero without touching memory) is loaded into the
-// register that vector k of this row leaves free.
-template <OpKind OP, class T, int VB, int IT, int W, int OWNER>
+// register that vector k of this row leaves free.  ODD: the shared words of
+// an odd-length bf16 row are written one half at a time (see OddOut).
+template <OpKind OP, class T, int VB, int IT, int W, int OWNER, bool ODD = false>
 __device__ __forceinline__ void store_tile(Tile<T, VB, IT> (&t)[OpTraits<OP>::kIn], rsrc_t dst,
                                            const ParamCache<OP, T, VB, IT, W, OWNER> &pc, int pos, const Coef &c,
-                                           const Srcs<OpTraits<OP>::kIn> &next)
+                                           const Srcs<OpTraits<OP>::kIn> &next, const OddOut *oo = nullptr)
 {
     using Op = OpTraits<OP>;
     constexpr int NI = Op::kIn;
@@ -375,7 +391,23 @@ __device__ __forceinline__ void store_tile(Tile<T, VB, IT> (&t)[OpTraits<OP>::kI
 #pragma unroll
             for (int i = 0; i < NI; ++i)
                 in[i] = t[i].v[k];
-            buf_store<VBO, kStreamStore>(apply_vec<OP, T, VB, false>(in, g, b, vec_coef<OP, T, IT>(c, k)), dst, ooff);
+            const RawVec<VBO> ov = apply_vec<OP, T, VB, false>(in, g, b, vec_coef<OP, T, IT>(c, k));
+            if constexpr (ODD) {
+                static_assert(VBO == 16 && NP == 0, "ODD rows: 16-byte bf16 vectors, no parameters");
+                if (k == 0 && oo->head) {
+                    buf_store_half(ov.w[0] >> 16, dst, off + 2u);
+                    buf_store_words123(ov, dst, off + 4u);
+                } else {
+                    buf_store<VBO, kStreamStore>(ov, dst, ooff);
+                }
+                if (k == oo->ktail) {
+                    const int d = oo->dtail;
+                    const uint32_t wv = d == 0 ? ov.w[0] : (d == 1 ? ov.w[1] : (d == 2 ? ov.w[2] : ov.w[3]));
+                    buf_store_half(wv, oo->full, off + 4u * static_cast<uint32_t>(d));
+                }
+            } else {
+                buf_store<VBO, kStreamStore>(ov, dst, ooff);
+            }
             if constexpr (rolls<MODE, OWNER, NI>())
 #pragma unroll
                 for (int i = 0; i < NI; ++i) {
@@ -474,17 +506,70 @@ __device__ __forceinline__ rsrc_t row_span(const void *base, int64_t row, int64_
     }
 }
 
+// ODD rows: bf16 rows of odd length, held as 16-byte vectors from the
+// 4-byte word below their start.  Row r starts s = (r * cols) mod 2 elements
+// into a word, and held position p is row element p - s.  The held span is
+// 2 * cols + 2 bytes, from the word below the row's start to the end of the
+// word holding its last element; for s = 0 that last word also holds the next
+// row's first element (or, for the last row, the 2 bytes after the tensor,
+// inside the same 4-byte word: read, masked, never written).  With
+// store = true the span leaves out a shared last word (s = 0); a shared first
+// word (s = 1) is in every span and store_tile writes it by halves.
+__device__ __forceinline__ int odd_shift(int64_t row, int64_t cols)
+{
+    return static_cast<int>((row * cols) & 1);
+}
+
+template <int VB>
+__device__ __forceinline__ rsrc_t odd_span(const void *base, int64_t row, int64_t cols, int64_t first, int64_t nvec,
+                                           bool store)
+{
+    const int s = odd_shift(row, cols);
+    const int64_t lo = (row * cols - s) * 2;
+    const int64_t len = (store && s == 0) ? 2 * cols - 2 : 2 * cols + 2;
+    int64_t n = len - first * VB;
+    n = n < nvec * VB ? n : nvec * VB;
+    n = n > 0 ? n : 0;
+    const uintptr_t p = reinterpret_cast<uintptr_t>(base) + static_cast<uintptr_t>(lo + first * VB);
+    return make_rsrc(reinterpret_cast<const void *>(p), static_cast<uint32_t>(n));
+}
+
 // The row inputs (x, and dy for two-input operators): `nvec` vectors from
-// vector `first` of row `row` (nv vectors per row; PEB as for row_span).
-template <OpKind OP, int VB, int PEB = 0>
+// vector `first` of row `row` (nv vectors per row; PEB as for row_span; ODD
+// rows as for odd_span).
+template <OpKind OP, int VB, int PEB = 0, bool ODD = false>
 __device__ __forceinline__ Srcs<OpTraits<OP>::kIn> row_srcs(const RowArgs &a, int64_t row, int64_t nv,
                                                             int64_t first, int64_t nvec)
 {
     Srcs<OpTraits<OP>::kIn> s;
-    s.r[0] = row_span<VB, PEB>(a.x, row, a.cols, nv, first, nvec);
-    if constexpr (OpTraits<OP>::kIn >= 2)
-        s.r[1] = row_span<VB, PEB>(a.dy, row, a.cols, nv, first, nvec);
+    if constexpr (ODD) {
+        s.r[0] = odd_span<VB>(a.x, row, a.cols, first, nvec, false);
+        if constexpr (OpTraits<OP>::kIn >= 2)
+            s.r[1] = odd_span<VB>(a.dy, row, a.cols, first, nvec, false);
+    } else {
+        s.r[0] = row_span<VB, PEB>(a.x, row, a.cols, nv, first, nvec);
+        if constexpr (OpTraits<OP>::kIn >= 2)
+            s.r[1] = row_span<VB, PEB>(a.dy, row, a.cols, nv, first, nvec);
+    }
     return s;
+}
+
+// Per-row state of an ODD row for the thread at slice position `pos` of a
+// slice starting at vector v0 (kpart already set): the last vector's valid
+// elements, the masked first element, and the output halves (OddOut).
+template <int E>
+__device__ __forceinline__ OddOut odd_row(LocalOdd &loc, const void *y, int64_t row, int64_t cols, int64_t nv,
+                                          int64_t v0, int64_t ns, int pos)
+{
+    const int s = odd_shift(row, cols);
+    loc.ntail = static_cast<int>(cols + s - E * (nv - 1));
+    loc.khead = (s != 0 && v0 == 0 && pos == 0) ? 0 : -1;
+    OddOut oo;
+    oo.full = odd_span<16>(y, row, cols, v0, ns, false);
+    oo.ktail = s == 0 ? loc.kpart : -1;
+    oo.dtail = (loc.ntail - 1) / 2;
+    oo.head = loc.khead == 0;
+    return oo;
 }
 
 // The thread's index (among its vectors k, at slice positions pos + k * G) of
@@ -517,24 +602,27 @@ __device__ __forceinline__ void store_row_value(const RowArgs &a, int64_t row, c
 // of the grid handles rows w, w + W, w + 2W, ... (W waves in the grid).  No
 // barrier on the row: the wave reduction is the row reduction.
 // ---------------------------------------------------------------------------
-// PART: rows whose last vector is partial (see row_span).
-template <OpKind OP, class T, int VB, int IT, bool PART = false>
+// PART: rows whose last vector is partial (see row_span).  ODD (with PART):
+// odd-length bf16 rows held from the word below their start (see odd_span).
+template <OpKind OP, class T, int VB, int IT, bool PART = false, bool ODD = false>
 __global__ __launch_bounds__(kWave *kWaveRowsPerWg) void single_wave_kernel(RowArgs a)
 {
     using Op = OpTraits<OP>;
     using PC = ParamCache<OP, T, VB, IT, kWave, kOwnerWaves>;
-    using Loc = std::conditional_t<PART, LocalPart, Local>;
+    using Loc = std::conditional_t<ODD, LocalOdd, std::conditional_t<PART, LocalPart, Local>>;
     constexpr int E = VB / StorageTraits<T>::kBytes;
     constexpr int VBO = out_vb<OP, T, VB>();
     constexpr int PEB = PART ? StorageTraits<T>::kBytes : 0;
     static_assert(!PART || VBO == VB, "PART rows need outputs of the input's element size");
+    static_assert(!ODD || (PART && VB == 16 && StorageTraits<T>::kBytes == 2 && Op::kParams == 0),
+                  "ODD rows: bf16, 16-byte vectors, operators without parameters");
     __shared__ RawVec<VB> lds_params[param_lds_vectors<OP, VB, IT, kWave, kOwnerWaves>()];
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t nv = PART ? (a.cols + E - 1) / E : a.cols / E;
     const int64_t waves = static_cast<int64_t>(gridDim.x) * kWaveRowsPerWg;
     int64_t row = uniform(static_cast<int64_t>(blockIdx.x) * kWaveRowsPerWg + threadIdx.x / kWave);
     Tile<T, VB, IT> t[Op::kIn];
-    load_tile<T, VB, IT, kWave>(t, row_srcs<OP, VB, PEB>(a, row, nv, 0, row < a.rows ? nv : 0), lane);
+    load_tile<T, VB, IT, kWave>(t, row_srcs<OP, VB, PEB, ODD>(a, row, nv, 0, row < a.rows ? nv : 0), lane);
     PC pc;
     pc.init(row_span<VB, PEB>(a.gamma, 0, a.cols, nv, 0, nv), row_span<VB, PEB>(a.beta, 0, a.cols, nv, 0, nv),
             lane, lds_params, threadIdx.x, kWave * kWaveRowsPerWg);
@@ -544,17 +632,21 @@ __global__ __launch_bounds__(kWave *kWaveRowsPerWg) void single_wave_kernel(RowA
     Loc loc0;
     if constexpr (PART) {
         loc0.ntail = static_cast<int>(a.cols % E);
-        loc0.kpart = partial_index<IT, kWave>(nv, lane, loc0.ntail != 0);
+        loc0.kpart = partial_index<IT, kWave>(nv, lane, ODD || loc0.ntail != 0);
     }
     for (; row < a.rows; row += waves) {
         const int64_t next = row + waves;
         Loc loc = loc0;
+        OddOut oo;
+        if constexpr (ODD)
+            oo = odd_row<E>(loc, a.y, row, a.cols, nv, 0, nv, lane);
         const auto wp = tile_partial<OP, T, VB, IT, kWave, kOwnerWaves>(t, kv, pc, lane, loc);
         const Coef c = Op::template finalize<T>(wp, loc, a.cols, a.eps);
         store_row_value<OP>(a, row, c, lane == 0);
-        const auto nsrc = row_srcs<OP, VB, PEB>(a, next, nv, 0, next < a.rows ? nv : 0);
-        store_tile<OP, T, VB, IT, kWave, kOwnerWaves>(t, row_span<VBO, PEB>(a.y, row, a.cols, nv, 0, nv), pc, lane,
-                                                      c, nsrc);
+        const auto nsrc = row_srcs<OP, VB, PEB, ODD>(a, next, nv, 0, next < a.rows ? nv : 0);
+        const rsrc_t dst = ODD ? odd_span<VBO>(a.y, row, a.cols, 0, nv, true)
+                               : row_span<VBO, PEB>(a.y, row, a.cols, nv, 0, nv);
+        store_tile<OP, T, VB, IT, kWave, kOwnerWaves, ODD>(t, dst, pc, lane, c, nsrc, &oo);
         load_next<OP, T, VB, IT, kWave, kOwnerWaves>(t, nsrc, lane);
     }
 }
@@ -563,16 +655,18 @@ __global__ __launch_bounds__(kWave *kWaveRowsPerWg) void single_wave_kernel(RowA
 // Path 1b: one workgroup of BLOCK threads per row; workgroup g handles rows
 // g, g + G, g + 2G, ... (G workgroups in the grid).
 // ---------------------------------------------------------------------------
-template <OpKind OP, class T, int VB, int BLOCK, int IT, bool PART = false>
+template <OpKind OP, class T, int VB, int BLOCK, int IT, bool PART = false, bool ODD = false>
 __global__ __launch_bounds__(BLOCK) void single_wg_kernel(RowArgs a)
 {
     using Op = OpTraits<OP>;
     using PC = ParamCache<OP, T, VB, IT, BLOCK, kOwnerRow>;
-    using Loc = std::conditional_t<PART, LocalPart, Local>;
+    using Loc = std::conditional_t<ODD, LocalOdd, std::conditional_t<PART, LocalPart, Local>>;
     constexpr int E = VB / StorageTraits<T>::kBytes;
     constexpr int PEB = PART ? StorageTraits<T>::kBytes : 0;
     constexpr int NW = BLOCK / kWave;
     constexpr int VBO = out_vb<OP, T, VB>();
+    static_assert(!ODD || (PART && VB == 16 && StorageTraits<T>::kBytes == 2 && Op::kParams == 0),
+                  "ODD rows: bf16, 16-byte vectors, operators without parameters");
     __shared__ typename Op::Partial sh[NW];
     __shared__ RawVec<VB> lds_params[param_lds_vectors<OP, VB, IT, BLOCK, kOwnerRow>()];
     const int tid = threadIdx.x;
@@ -580,7 +674,7 @@ __global__ __launch_bounds__(BLOCK) void single_wg_kernel(RowArgs a)
     const int64_t nv = PART ? (a.cols + E - 1) / E : a.cols / E;
     int64_t row = blockIdx.x;
     Tile<T, VB, IT> t[Op::kIn];
-    load_tile<T, VB, IT, kWave>(t, row_srcs<OP, VB, PEB>(a, row, nv, 0, nv), pos);
+    load_tile<T, VB, IT, kWave>(t, row_srcs<OP, VB, PEB, ODD>(a, row, nv, 0, nv), pos);
     PC pc;
     pc.init(row_span<VB, PEB>(a.gamma, 0, a.cols, nv, 0, nv), row_span<VB, PEB>(a.beta, 0, a.cols, nv, 0, nv), pos,
             lds_params, tid, BLOCK);
@@ -590,18 +684,22 @@ __global__ __launch_bounds__(BLOCK) void single_wg_kernel(RowArgs a)
     Loc loc0;
     if constexpr (PART) {
         loc0.ntail = static_cast<int>(a.cols % E);
-        loc0.kpart = partial_index<IT, kWave>(nv, pos, loc0.ntail != 0);
+        loc0.kpart = partial_index<IT, kWave>(nv, pos, ODD || loc0.ntail != 0);
     }
     for (; row < a.rows; row += gridDim.x) {
         const int64_t next = row + gridDim.x;
         Loc loc = loc0;
+        OddOut oo;
+        if constexpr (ODD)
+            oo = odd_row<E>(loc, a.y, row, a.cols, nv, 0, nv, pos);
         const auto wp = tile_partial<OP, T, VB, IT, BLOCK, kOwnerRow>(t, kv, pc, pos, loc);
         const auto rp = block_combine<OP, NW>(wp, sh);
         const Coef c = Op::template finalize<T>(rp, loc, a.cols, a.eps);
         store_row_value<OP>(a, row, c, tid == 0);
-        const auto nsrc = row_srcs<OP, VB, PEB>(a, next, nv, 0, next < a.rows ? nv : 0);
-        store_tile<OP, T, VB, IT, BLOCK, kOwnerRow>(t, row_span<VBO, PEB>(a.y, row, a.cols, nv, 0, nv), pc, pos, c,
-                                                     nsrc);
+        const auto nsrc = row_srcs<OP, VB, PEB, ODD>(a, next, nv, 0, next < a.rows ? nv : 0);
+        const rsrc_t dst = ODD ? odd_span<VBO>(a.y, row, a.cols, 0, nv, true)
+                               : row_span<VBO, PEB>(a.y, row, a.cols, nv, 0, nv);
+        store_tile<OP, T, VB, IT, BLOCK, kOwnerRow, ODD>(t, dst, pc, pos, c, nsrc, &oo);
         load_next<OP, T, VB, IT, BLOCK, kOwnerRow>(t, nsrc, pos);
         // the next block_combine rewrites sh: every wave must have read it
         __syncthreads();
@@ -614,16 +712,18 @@ __global__ __launch_bounds__(BLOCK) void single_wg_kernel(RowArgs a)
 // reductions (over zero tiles), but no access to rows, parameters or outputs
 // at all (the control launch passes null pointers for them).
 // ---------------------------------------------------------------------------
-template <OpKind OP, class T, int VB, int BLOCK, int IT, bool CONTROL, bool PART = false>
+template <OpKind OP, class T, int VB, int BLOCK, int IT, bool CONTROL, bool PART = false, bool ODD = false>
 __global__ __launch_bounds__(BLOCK) void split_kernel(SplitArgs a)
 {
     using Op = OpTraits<OP>;
     using Partial = typename Op::Partial;
     using PC = ParamCache<OP, T, VB, IT, BLOCK, kOwnerSlice>;
-    using Loc = std::conditional_t<PART, LocalPart, Local>;
+    using Loc = std::conditional_t<ODD, LocalOdd, std::conditional_t<PART, LocalPart, Local>>;
     constexpr int E = VB / StorageTraits<T>::kBytes;
     constexpr int PEB = PART ? StorageTraits<T>::kBytes : 0;
     static_assert(!(PART && CONTROL), "the control twin touches no row");
+    static_assert(!ODD || (PART && VB == 16 && StorageTraits<T>::kBytes == 2 && Op::kParams == 0),
+                  "ODD rows: bf16, 16-byte vectors, operators without parameters");
     constexpr int NW = BLOCK / kWave;
     constexpr int Q = Op::kQ;
     constexpr int VBO = out_vb<OP, T, VB>();
@@ -659,7 +759,7 @@ __global__ __launch_bounds__(BLOCK) void split_kernel(SplitArgs a)
             for (int j = 0; j < IT; ++j)
                 t[i].v[j] = RawVec<VB>{};
     } else {
-        load_tile<T, VB, IT, kWave>(t, row_srcs<OP, VB, PEB>(a.r, k, nv, v0, k < a.r.rows ? ns : 0), pos);
+        load_tile<T, VB, IT, kWave>(t, row_srcs<OP, VB, PEB, ODD>(a.r, k, nv, v0, k < a.r.rows ? ns : 0), pos);
         pc.init(row_span<VB, PEB>(a.r.gamma, 0, a.r.cols, nv, v0, ns), row_span<VB, PEB>(a.r.beta, 0, a.r.cols, nv, v0, ns),
                 pos, lds_params, tid, BLOCK);
         if constexpr (PC::kMode == kParamLds)
@@ -675,12 +775,15 @@ __global__ __launch_bounds__(BLOCK) void split_kernel(SplitArgs a)
     Loc loc0;
     if constexpr (PART) {
         loc0.ntail = static_cast<int>(a.r.cols % E);
-        loc0.kpart = partial_index<IT, kWave>(ns, pos, loc0.ntail != 0 && v0 + ns == nv);
+        loc0.kpart = partial_index<IT, kWave>(ns, pos, (ODD || loc0.ntail != 0) && v0 + ns == nv);
     }
     auto step = [&](int64_t row, uint32_t it) __attribute__((always_inline)) {
         const int64_t next = row + a.clusters;
         Partial wp;
         Loc loc = loc0;
+        OddOut oo;
+        if constexpr (ODD)
+            oo = odd_row<E>(loc, a.r.y, row, a.r.cols, nv, v0, ns, pos);
         if constexpr (CONTROL)
             wp = Op::template wave_partial<T, VB, IT>(t, kv, loc);
         else
@@ -717,9 +820,10 @@ __global__ __launch_bounds__(BLOCK) void split_kernel(SplitArgs a)
             (void)next;
         } else {
             store_row_value<OP>(a.r, row, cf, c == 0 && tid == 0);
-            const auto nsrc = row_srcs<OP, VB, PEB>(a.r, next, nv, v0, next < a.r.rows ? ns : 0);
-            store_tile<OP, T, VB, IT, BLOCK, kOwnerSlice>(t, row_span<VBO, PEB>(a.r.y, row, a.r.cols, nv, v0, ns), pc,
-                                                          pos, cf, nsrc);
+            const auto nsrc = row_srcs<OP, VB, PEB, ODD>(a.r, next, nv, v0, next < a.r.rows ? ns : 0);
+            const rsrc_t dst = ODD ? odd_span<VBO>(a.r.y, row, a.r.cols, v0, ns, true)
+                                   : row_span<VBO, PEB>(a.r.y, row, a.r.cols, nv, v0, ns);
+            store_tile<OP, T, VB, IT, BLOCK, kOwnerSlice, ODD>(t, dst, pc, pos, cf, nsrc, &oo);
             load_next<OP, T, VB, IT, BLOCK, kOwnerSlice>(t, nsrc, pos);
         }
         // (no barrier needed before the next row rewrites sh or peer: every

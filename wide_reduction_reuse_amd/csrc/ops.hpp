@@ -67,6 +67,7 @@ struct Coef {
 // (ref_groups of them), to which the fp32 tile's exponentials are relative.
 struct Local {
     static constexpr bool kPartial = false;
+    static constexpr bool kHead = false;
     float m[4];
 };
 
@@ -80,12 +81,26 @@ struct LocalPart : Local {
     int ntail = 0;
 };
 
+// The same, for odd-length bf16 rows held from the 4-byte word below their
+// start (the kernels' ODD mode): a row that starts in the middle of a word
+// has its first held element (the previous row's last) at element 0 of the
+// thread's vector khead (-1 when the thread does not hold it, or the row
+// starts on a word boundary), and the last vector's ntail valid elements
+// count from the start of the held span.
+struct LocalOdd : LocalPart {
+    static constexpr bool kHead = true;
+    int khead = -1;
+};
+
 // Whether element e of the thread's vector k is part of the row (only the
-// partial last vector of a PART row has elements that are not).
+// partial last vector of a PART or ODD row, and an ODD row's first vector,
+// have elements that are not).
 template <class L>
 __device__ __forceinline__ bool elem_in_row(const L &loc, int k, int e)
 {
-    if constexpr (L::kPartial)
+    if constexpr (L::kHead)
+        return (k != loc.kpart || e < loc.ntail) && (k != loc.khead || e != 0);
+    else if constexpr (L::kPartial)
         return k != loc.kpart || e < loc.ntail;
     else
         return true;
@@ -207,8 +222,14 @@ __device__ __forceinline__ Part<DY ? 3 : 2> softmax_groups(Tile<T, VB, IT> (&t)[
                     if constexpr (is_f32<T>())
                         set_word<VB>(t[0].v[k], e, __float_as_uint(ex));
                     sv += ex;
-                    if constexpr (DY)
-                        uv = __builtin_fmaf(ex, elem<T, VB>(t[1].v[k], e), uv);
+                    if constexpr (DY) {
+                        // an ODD row's masked elements are the neighbouring
+                        // rows' data: keep their dy (even an inf) out of u
+                        if constexpr (L::kHead)
+                            uv = elem_in_row(loc, k, e) ? __builtin_fmaf(ex, elem<T, VB>(t[1].v[k], e), uv) : uv;
+                        else
+                            uv = __builtin_fmaf(ex, elem<T, VB>(t[1].v[k], e), uv);
+                    }
                 }
         }
         gref[g] = gm;

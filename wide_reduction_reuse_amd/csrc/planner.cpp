@@ -37,7 +37,17 @@ bool row_is_partial(int op, int dt, int64_t cols)
     return op_has_part(op) && bytes % 16 != 0 && bytes % 4 == 0;
 }
 
-int held_vec_bytes(int op, int dt, int64_t cols) { return row_is_partial(op, dt, cols) ? 16 : vec_bytes_for(dt, cols); }
+bool row_is_odd(int op, int dt, int64_t cols) { return op_has_odd(op) && dt == 1 && cols % 2 == 1; }
+
+int held_row_kind(int op, int dt, int64_t cols)
+{
+    return row_is_partial(op, dt, cols) ? 1 : (row_is_odd(op, dt, cols) ? 2 : 0);
+}
+
+int held_vec_bytes(int op, int dt, int64_t cols)
+{
+    return held_row_kind(op, dt, cols) != 0 ? 16 : vec_bytes_for(dt, cols);
+}
 
 int path_vec_bytes(int op, int dt, int64_t cols, int path)
 {
@@ -411,22 +421,23 @@ bool plan_from_table(const PlanRequest &req, const Calibration &cal, int forced_
 // each is read at the row count that moves the same bytes, and the two are
 // interpolated in (log cols, log time); one side alone is used as it is.
 // A held plan (paths 1, 2) runs partial-vector kernels on rows that end in a
-// partial 16-byte vector, which stream slower than whole-vector rows: such
-// widths are priced from each other, whole-vector widths likewise, and the
-// other kind serves only where the plan was never measured on the same kind.
+// partial 16-byte vector and ODD kernels on odd-length bf16 rows, which
+// stream slower than whole-vector rows: widths are priced from widths of the
+// same kind (held_row_kind), and another kind serves only where the plan was
+// never measured on the same kind.
 // Negative when the table never measured the plan.
 double neighbour_time_us(const PlanRequest &req, const Calibration &cal, const Candidate &cd)
 {
     const CalibEntry *lo = nullptr, *hi = nullptr;
     const bool held = cd.path != kPathReread;
-    const bool part = held && row_is_partial(req.op, req.dt, req.cols);
+    const int kind = held ? held_row_kind(req.op, req.dt, req.cols) : 0;
     for (int same_kind = 1; same_kind >= 0 && lo == nullptr && hi == nullptr; --same_kind)
         for (const CalibEntry &e : cal.table) {
             if (e.op != req.op || e.dt != req.dt || e.path != cd.path || e.split_p != cd.split_p ||
                 e.block != cd.est.tile.block || e.items != cd.est.tile.items || e.vb != cd.est.tile.vb ||
                 e.wgs_per_cu != cd.wgs_per_cu || e.rows.empty())
                 continue;
-            if (same_kind && held && row_is_partial(e.op, e.dt, e.cols) != part)
+            if (same_kind && held && held_row_kind(e.op, e.dt, e.cols) != kind)
                 continue;
             if (e.cols <= req.cols && (lo == nullptr || e.cols > lo->cols))
                 lo = &e;

@@ -120,7 +120,13 @@ int vec_bytes_for(int dt, int64_t cols);
 // with PART kernels: paths 1 and 2 hold them as 16-byte vectors whose last
 // one is partial (PART kernels mask its missing elements).
 bool row_is_partial(int op, int dt, int64_t cols);
-// Bytes per access of the held tiles (paths 1, 2): 16 for partial rows too.
+// bf16 rows of odd length, of an operator with ODD kernels: paths 1 and 2
+// hold them as 16-byte vectors from the 4-byte word below the row's start.
+bool row_is_odd(int op, int dt, int64_t cols);
+// The kernels' row kind for paths 1 and 2: 0 whole vectors or one-element
+// tiles, 1 partial last vector (row_is_partial), 2 odd-length bf16 (row_is_odd).
+int held_row_kind(int op, int dt, int64_t cols);
+// Bytes per access of the held tiles (paths 1, 2): 16 for partial and ODD rows too.
 int held_vec_bytes(int op, int dt, int64_t cols);
 // Bytes per access that `path` (kPathSingle / kPathSplit / kPathReread) uses.
 int path_vec_bytes(int op, int dt, int64_t cols, int path);

@@ -18,13 +18,22 @@ struct KernelEntry {
     int block;  // threads per row owner (64 for wave-per-row)
     int items;  // vectors held per thread (paths 1, 2) or streamed per step (path 3)
     const void *fn;
-    bool part = false;  // rows whose last 16-byte vector is partial (PART kernels)
+    // row shape the kernel holds: 0 whole 16-byte vectors (or one-element
+    // tiles), 1 a partial last vector (PART kernels), 2 odd-length bf16 rows
+    // held from the 4-byte word below their start (ODD kernels)
+    int part = 0;
 };
 
 // Operators with PART kernels: their partials mask the partial vector's
 // elements (softmax, LayerNorm, RMSNorm, softmax backward); the others keep
 // one-element tiles for rows that are not whole vectors.
 constexpr bool op_has_part(int op) { return op <= 3; }
+
+// Operators with ODD kernels (bf16 rows of odd length held as 16-byte
+// vectors): those without parameter vectors whose output has the input's
+// type, softmax and softmax backward.  (A row that starts in the middle of a
+// 4-byte word would need its parameters shifted by one element.)
+constexpr bool op_has_odd(int op) { return op == 0 || op == 3; }
 
 void register_softmax_kernels(std::vector<KernelEntry> &out);
 void register_layernorm_kernels(std::vector<KernelEntry> &out);

@@ -1,7 +1,8 @@
 """Exhaustive timing of every legal plan on a set of shapes.
 
     python -m wide_reduction_reuse_amd.sweep --points named|sweep|next|all|calib|calib_next|calib_next_more|calib_mid|calib_odd|calib_all|offgrid
-                                             [--steps 15] [--warmup 3] [--ops ...]
+                                             [--steps 15] [--warmup 3] [--ops ...] [--dtypes ...]
+                                             [--min-cols N] [--odd-cols]
 
 For each shape it enumerates the legal plans (credit_enumerate_plans: every
 path 1 tile that holds the row, every path 3 tile, every (P, tile) of path 2),
@@ -84,7 +85,7 @@ def sweep_shape(w: W.Workload, steps: int, warmup: int, flush_buf) -> dict:
     return rec
 
 
-def points(which: str, ops=None, min_cols: int = 0):
+def points(which: str, ops=None, min_cols: int = 0, dtypes=None, odd_cols=False):
     pts = []
     if which in ("named", "all"):
         pts += [W.NAMED[n] for n in W.CONFIG_ORDER + W.NEXT_ORDER]
@@ -108,6 +109,10 @@ def points(which: str, ops=None, min_cols: int = 0):
         pts += W.offgrid_points() + W.offgrid_points_next()
     if ops:
         pts = [p for p in pts if p.op in ops]
+    if dtypes:
+        pts = [p for p in pts if p.dtype in dtypes]
+    if odd_cols:
+        pts = [p for p in pts if p.cols % 2 == 1]
     return [p for p in pts if p.cols >= min_cols]
 
 
@@ -118,6 +123,8 @@ def main(argv=None) -> int:
                                                          "offgrid"))
     ap.add_argument("--ops", nargs="*", default=None)
     ap.add_argument("--min-cols", type=int, default=0, help="only shapes at least this wide")
+    ap.add_argument("--dtypes", nargs="*", default=None, help="only these dtypes (f32, bf16)")
+    ap.add_argument("--odd-cols", action="store_true", help="only shapes of odd width")
     ap.add_argument("--out", default="-")
     ap.add_argument("--steps", type=int, default=15)
     ap.add_argument("--warmup", type=int, default=3)
@@ -131,7 +138,7 @@ def main(argv=None) -> int:
     flush_buf = flush_buffer()
     out = sys.stdout if a.out == "-" else open(a.out, "w")
     t0 = time.time()
-    for w in points(a.points, a.ops, a.min_cols):
+    for w in points(a.points, a.ops, a.min_cols, a.dtypes, a.odd_cols):
         rec = sweep_shape(w, a.steps, a.warmup, flush_buf)
         out.write(json.dumps(rec) + "\n")
         out.flush()
