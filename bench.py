@@ -17,8 +17,9 @@ reports), so the flush, host-side planning and launch latency are outside it.
 
 Prints one JSON line: metric, value (algorithmic GB/s = one read of every row
 input + one write of the output + each parameter vector once, over the mean
-kernel duration), the roofline object for the kernel, and the CPU oracle's rate
-on the same workload.  --workload picks any named workload, including the three
+kernel duration), the roofline object for the kernel, the CPU oracle's rate
+on the same workload, and (in config) the rate of the library's streaming copy
+of the same number of bytes, timed the same way.  --workload picks any named workload, including the three
 further workloads (softmax-logits backward, LayerNorm backward, int8
 quantization).  With --all FILE it also writes one JSON line per (workload,
 path) and the streaming-copy ceiling to FILE.
@@ -201,6 +202,9 @@ def main(argv=None) -> int:
     r = run_workload(w, "auto", 0, a.steps, a.warmup, flush_buf, inputs=inp)
     achieved = r["gbs"]
     traffic = load_traffic(a.workload, plan)
+    # the streaming copy of the same number of bytes (half read, half written),
+    # timed the same way: the ceiling a kernel of this size can reach here
+    copy = copy_ceiling(w.algorithmic_bytes() // 2 // 16 * 16, a.steps, a.warmup, flush_buf)
     result = {
         "metric": METRIC,
         "value": round(achieved, 2),
@@ -220,7 +224,9 @@ def main(argv=None) -> int:
                    "cache_flush_bytes_between_steps": FLUSH_BYTES,
                    "median_ms": round(r["median_ms"], 5), "min_ms": round(r["min_ms"], 5),
                    "wall_s_timed_loop_incl_flush": round(r["wall_s"], 4),
-                   "timing": "hipExtLaunchKernel dispatch timestamps"},
+                   "timing": "hipExtLaunchKernel dispatch timestamps",
+                   "copy_same_bytes_gbs": round(copy["gbs"], 2),
+                   "frac_of_copy_same_bytes": round(achieved / copy["gbs"], 4)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None if traffic is None else traffic["bytes_per_launch"]},
