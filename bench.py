@@ -242,7 +242,7 @@ def main(argv=None) -> int:
                 f.flush()
                 print("[all] copy %d MiB %.1f GB/s (%.4f ms)" % (mib, cc["gbs"], cc["mean_ms"]),
                       file=sys.stderr, flush=True)
-            for name in W.CONFIG_ORDER + W.NEXT_ORDER:
+            for name in W.CONFIG_ORDER + W.NEXT_ORDER + W.EXTRA_ORDER:
                 wk = W.NAMED[name]
                 inpk = W.generate(wk)
                 pl = C.credit_select_path(wk.op, wk.dtype, wk.rows, wk.cols)

@@ -73,7 +73,7 @@ def _same(a, b):
 # twice the bytes): path 1 is refused for these
 NO_SINGLE = {"softmax_f32_256x262144", "softmax_bwd_f32_4096x65536", "layernorm_bwd_f32_2048x65536"}
 NAMED_CASES = []
-for name in W.CONFIG_ORDER + W.NEXT_ORDER:
+for name in W.CONFIG_ORDER + W.NEXT_ORDER + W.EXTRA_ORDER:
     NAMED_CASES.append((name, "auto", 0))
     NAMED_CASES.append((name, "reread", 0))
     for p in (2, 4, 8):

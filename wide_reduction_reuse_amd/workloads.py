@@ -113,11 +113,15 @@ NAMED: Dict[str, Workload] = {
                  x_dist="scaled_shifted", x_scale=3.0, x_shift=0.5, eps=1e-5),
         Workload("quantize_int8_f32_4096x65536", "quantize_int8", "f32", 4096, 65536, seed=7,
                  x_dist="outliers", outlier_prob=0.01, outlier_scale=50.0),
+        # a softmax over a vocabulary-sized odd width in bf16 (256 MiB of
+        # logits): rows of odd length, held from the 4-byte word below them
+        Workload("softmax_bf16_2670x50257", "softmax", "bf16", 2670, 50257, seed=8),
     ]
 }
 CONFIG_ORDER = ["softmax_f32_64x4096", "layernorm_bf16_4096x8192",
                 "rmsnorm_bf16_1024x65536", "softmax_f32_256x262144"]
 NEXT_ORDER = ["softmax_bwd_f32_4096x65536", "layernorm_bwd_f32_2048x65536", "quantize_int8_f32_4096x65536"]
+EXTRA_ORDER = ["softmax_bf16_2670x50257"]
 NEXT_COLS = (4096, 8192, 16384, 32768, 65536)
 NEXT_ROWS = {"softmax_bwd": 4096, "layernorm_bwd": 2048, "quantize_int8": 4096}
 
