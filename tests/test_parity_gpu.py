@@ -374,6 +374,29 @@ def test_odd_length_bf16_in_place_and_boundary_nan(op, alias, path, p, cols):
             assert not isnan[r].any(), "NaN leaked into row %d" % r
 
 
+@pytest.mark.parametrize("op", ODD_ROW_OPS)
+@pytest.mark.parametrize("path,p", [("single", 0), ("split", 4)])
+def test_odd_length_bf16_word_after_the_tensor_is_masked(op, path, p):
+    # rows * cols odd: the last row ends in the middle of a 4-byte word whose
+    # other half lies after the tensor; the kernels read that word and must
+    # mask it.  Here it holds a NaN (x and dy are views of longer buffers).
+    import torch
+    C = _lib()
+    rows, cols = 35, 4099
+    w = W.custom(op, "bf16", rows, cols, seed=17)
+    inp = W.generate(w)
+    t = _device_operands(inp)
+    for k in ("x", "dy"):
+        if t.get(k) is None:
+            continue
+        buf = torch.empty(rows * cols + 8, dtype=torch.bfloat16, device="cuda")
+        buf.view(torch.int16)[rows * cols:] = 0x7FC0  # NaN after the tensor
+        buf[: rows * cols].copy_(t[k].reshape(-1))
+        t[k] = buf[: rows * cols].view(rows, cols)
+    out = _run(inp, path, p, t=t)
+    _check(inp, out, "word after the tensor %s %s P=%d" % (op, path, p))
+
+
 # ---------------------------------------------------------------------------
 # rows whose byte length is not a multiple of 16: partial last vectors
 # (above) and one-element accesses (odd bf16 lengths, int8 quantization,
