@@ -182,12 +182,13 @@ def test_selector_legality_on_cpu():
 
 
 def test_partial_rows_are_held_as_16_byte_vectors():
-    # byte length a multiple of 4 but not of 16: softmax, LayerNorm, RMSNorm
-    # and softmax backward hold the row as 16-byte vectors (the last partial)
-    # and reread it by element; the other operators use one-element tiles
+    # byte length a multiple of 4 but not of 16: softmax, LayerNorm, RMSNorm,
+    # softmax backward and LayerNorm backward hold the row as 16-byte vectors
+    # (the last partial) and reread it by element; the quantizer uses
+    # one-element tiles
     L = C.lib()
     for op, dt, cols in [("softmax", "f32", 1001), ("layernorm", "bf16", 1002), ("rmsnorm", "f32", 3),
-                         ("softmax_bwd", "bf16", 30006)]:
+                         ("softmax_bwd", "bf16", 30006), ("layernorm_bwd", "f32", 1001)]:
         p = C.credit_plan(op, dt, 64, cols, "single")
         assert p.vec_bytes == 16
         assert C.credit_plan(op, dt, 64, cols, "reread").vec_bytes == 16 // (4 if dt == "f32" else 8)
@@ -198,7 +199,7 @@ def test_partial_rows_are_held_as_16_byte_vectors():
     p = C.credit_plan("softmax", "f32", 64, 100006, "split", 8)
     assert p.vec_bytes == 16
     assert C.credit_plan("quantize_int8", "f32", 64, 1001, "single").vec_bytes == 4
-    assert C.credit_plan("layernorm_bwd", "f32", 64, 1001, "single").vec_bytes == 4
+    assert C.credit_plan("layernorm_bwd", "f32", 64, 100003, "split", 8).vec_bytes == 16
     assert C.credit_plan("rmsnorm", "bf16", 64, 1001, "single").vec_bytes == 2  # odd bytes / 4
 
 

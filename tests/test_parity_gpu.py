@@ -222,10 +222,10 @@ def test_every_tile(op, dt, kind, block, items, p, cols):
 
 # ---------------------------------------------------------------------------
 # rows whose last 16-byte vector is partial: the held tiles of softmax,
-# LayerNorm, RMSNorm and softmax backward hold such rows as 16-byte vectors
-# and mask the missing elements of the last one
+# LayerNorm, RMSNorm, softmax backward and LayerNorm backward hold such rows
+# as 16-byte vectors and mask the missing elements of the last one
 # ---------------------------------------------------------------------------
-PART_OPS = ("softmax", "layernorm", "rmsnorm", "softmax_bwd")
+PART_OPS = ("softmax", "layernorm", "rmsnorm", "softmax_bwd", "layernorm_bwd")
 
 
 def _partial_tile_cases():
@@ -235,6 +235,8 @@ def _partial_tile_cases():
     i = 0
     for op in PART_OPS:
         for dt in W.DTYPES:
+            if (op, dt) not in W.SUPPORTED:
+                continue
             epv = 16 // W.ELEM_BYTES[dt]
             tails = (1, 2, 3) if dt == "f32" else (2, 4, 6)  # elements in the partial vector
             for kind, tiles in ladders.items():
@@ -417,13 +419,6 @@ def test_unaligned_row_lengths(op, dt, cols, path, p):
     C = _lib()
     w = W.custom(op, dt, 6, cols, seed=cols + 7, x_dist="scaled_shifted", x_scale=2.0, x_shift=-0.25)
     inp = W.generate(w)
-    if op == "layernorm_bwd" and (path == "split" or (path == "single" and cols > 1024 * 4)):
-        # its one-element split tile and 1024 x 16 tile are left out (they
-        # spilled): such rows are refused before launch (auto takes path 3)
-        with pytest.raises(C.CreditError) as ei:
-            _run(inp, path, p)
-        assert ei.value.status == 4
-        return
     out = _run(inp, path, p)
     _check(inp, out, "odd %s %s cols=%d %s P=%d" % (op, dt, cols, path, p))
 
@@ -467,12 +462,6 @@ def test_in_place(op, alias, path, p, cols):
     inp = W.generate(w)
     t = _device_operands(inp)
     t["y"] = t[alias]
-    if op == "layernorm_bwd" and cols % 4 and path in ("split", "single"):
-        # its one-element split tile and 1024 x 16 tile are left out (they spilled)
-        with pytest.raises(C.CreditError) as ei:
-            _run(inp, path, p, t=t)
-        assert ei.value.status == 4
-        return
     out = _run(inp, path, p, t=t)
     _check(inp, out, "in-place y=%s %s %s P=%d cols=%d" % (alias, op, path, p, cols))
 
@@ -509,15 +498,12 @@ def test_persistent_owners_match_one_row_per_owner_bitwise(op, dt):
 @pytest.mark.parametrize("op,dt", SUPPORTED_CASES)
 def test_paths_agree_closely(op, dt, cols):
     # all legal paths on one shape: each within tolerance of the oracle, and
-    # path 1 bitwise stable run to run (32764 bf16 columns end in a partial
-    # vector, LayerNorm backward then has no split tile)
+    # path 1 bitwise stable run to run (32764 columns end in a partial vector)
     C = _lib()
     w = W.custom(op, dt, 40, cols, seed=31)
     inp = W.generate(w)
     ys = {}
     for path, p in [("single", 0), ("split", 2), ("split", 4), ("split", 8), ("reread", 0)]:
-        if op == "layernorm_bwd" and path == "split" and cols % 4:
-            continue
         ys[(path, p)] = _run(inp, path, p)
         _check(inp, ys[(path, p)], "agree %s %s %s P=%d" % (op, dt, path, p))
     assert _same(ys[("single", 0)], _run(inp, "single", 0))

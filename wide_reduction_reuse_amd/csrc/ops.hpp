@@ -745,8 +745,10 @@ struct OpTraits<kLayerNormBwd> {
             set_word<VB>(t[1].v[k], e, __float_as_uint(elem<T, VB>(gv, e) * elem<T, VB>(t[1].v[k], e)));
     }
 
+    // (A PART row's missing elements load as zeros in x and g: neutral in the
+    // sums and in b, masked out of the count and of M2.)
     template <class T, int VB, int IT, class L>
-    __device__ __forceinline__ static Partial wave_partial(Tile<T, VB, IT> (&t)[kIn], int kvalid, L &)
+    __device__ __forceinline__ static Partial wave_partial(Tile<T, VB, IT> (&t)[kIn], int kvalid, L &loc)
     {
         constexpr int E = Tile<T, VB, IT>::kEpv;
         float sx = 0.0f, sg = 0.0f;
@@ -758,7 +760,11 @@ struct OpTraits<kLayerNormBwd> {
                     sx += elem<T, VB>(t[0].v[k], e);
                     sg += elem<T, VB>(t[1].v[k], e);
                 }
-        const float nw = wave_sum(static_cast<float>(kvalid * E));
+        int nvalid = kvalid * E;
+        if constexpr (L::kPartial)
+            if (loc.kpart >= 0 && loc.kpart < kvalid)
+                nvalid -= E - loc.ntail;
+        const float nw = wave_sum(static_cast<float>(nvalid));
         const float sw = wave_sum(sx);
         const float mean = nw > 0.0f ? sw / nw : 0.0f;
         fence_tile(t[0]);
@@ -769,7 +775,7 @@ struct OpTraits<kLayerNormBwd> {
             if (k < kvalid)
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
-                    const float d = elem<T, VB>(t[0].v[k], e) - mean;
+                    const float d = elem_in_row(loc, k, e) ? elem<T, VB>(t[0].v[k], e) - mean : 0.0f;
                     m2 = __builtin_fmaf(d, d, m2);
                     b = __builtin_fmaf(elem<T, VB>(t[1].v[k], e), d, b);
                 }

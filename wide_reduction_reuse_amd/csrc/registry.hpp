@@ -25,9 +25,11 @@ struct KernelEntry {
 };
 
 // Operators with PART kernels: their partials mask the partial vector's
-// elements (softmax, LayerNorm, RMSNorm, softmax backward); the others keep
-// one-element tiles for rows that are not whole vectors.
-constexpr bool op_has_part(int op) { return op <= 3; }
+// elements (softmax, LayerNorm, RMSNorm, softmax backward, LayerNorm
+// backward); the int8 quantizer, whose output rows of one byte per element
+// end inside a 4-byte word, keeps one-element tiles for rows that are not
+// whole vectors.
+constexpr bool op_has_part(int op) { return op <= 4; }
 
 // Operators with ODD kernels (bf16 rows of odd length held as 16-byte
 // vectors): those without parameter vectors whose output has the input's
