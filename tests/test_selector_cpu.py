@@ -215,3 +215,15 @@ def test_calibration_extension_keeps_base_rows_and_merges_shared_ones():
     assert shared[12:] == [1000, 50.0, 4000, 190.0]
     assert next(r for r in t if r[:3] == [2, 1, 8192]) == base[1]
     assert next(r for r in t if r[:3] == [0, 1, 1026]) == new[1]
+
+
+def test_calibration_extension_drops_plans_the_library_no_longer_offers():
+    # an odd-length bf16 softmax row is held as 16-byte vectors now: a table
+    # row of its one-element held tile is stale, its reread row and the
+    # 16-byte held row are offered
+    from wide_reduction_reuse_amd import calibrate as K
+    stale = [0, 1, 50257, 1, 1, 1024, 32, 2, -1, 1, 2670, 250.0]
+    held = [0, 1, 50257, 1, 1, 512, 16, 16, -1, 1, 2670, 120.0]
+    reread = [0, 1, 50257, 3, 1, 256, 8, 2, 0, 1, 2670, 320.0]
+    assert not K.offered(stale)
+    assert K.offered(held) and K.offered(reread)
