@@ -40,7 +40,7 @@ from wide_reduction_reuse_amd import workloads as W  # noqa: E402
 from wide_reduction_reuse_amd.timing import FLUSH_BYTES, summarize, time_launches  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
-DEFAULT_WORKLOAD = "layernorm_bf16_4096x8192"
+DEFAULT_WORKLOAD = "softmax_f32_256x262144"
 PROFILES = os.path.join(ROOT, "profiles")
 CPU_BASELINE_SECONDS = 10.0
 METRIC = "achieved HBM GB/s (one read + one write) and % of MI355X peak per op/shape"

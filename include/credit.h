@@ -32,8 +32,18 @@
  *     left untouched.  rows == 0 is a successful no-op.
  *   - The library owns only a small exchange scratch per (device, stream) for
  *     the split-row path, allocated on first use of that path on that stream.
- *     That first call must not be made under stream capture.  Two streams never
- *     share a scratch; concurrent calls on one stream are ordered by the stream.
+ *     Two streams never share a scratch; calls on one stream are ordered by
+ *     the stream.  The state of the split-row protocol (ticket counter, tags)
+ *     lives in that scratch and is advanced by the kernels themselves, so a
+ *     split-row launch may be captured into a graph and replayed any number
+ *     of times, provided the stream's scratch already exists when the capture
+ *     starts (a first split-row call on a stream under capture returns
+ *     CREDIT_ERR_UNSUPPORTED before enqueueing anything) and replays do not
+ *     overlap other split-row work that uses the same scratch (e.g. by
+ *     replaying on the capture stream).
+ *   - If a split-row workgroup's wait for its peers' partials gives up (see
+ *     credit_check_errors), that row's output is NaN (for the int8 quantizer:
+ *     its scale is NaN), never a result from stale statistics.
  *
  * Arithmetic: fp32 inputs compute in fp32; bf16 inputs are widened exactly to
  * fp32, computed in fp32 and rounded to nearest-even bf16 on output (the int8
@@ -305,9 +315,36 @@ credit_status_t credit_load_calibration(const char *json_path);
 /*
  * Synchronize `stream` and read (then clear) the device error word of that
  * stream's split-row scratch: CREDIT_ERR_DEVICE_TIMEOUT if a spin-wait gave up
- * since the last check, CREDIT_ERR_HIP if synchronization failed, else CREDIT_OK.
+ * since the last check (the rows concerned were written as NaN),
+ * CREDIT_ERR_HIP if synchronization failed, else CREDIT_OK.
  */
 credit_status_t credit_check_errors(void *stream);
+
+/*
+ * Test hooks for the failure handling of the split-row exchange; normal use
+ * needs neither.
+ *
+ * credit_test_exchange: for split-row launches enqueued after the call (in any
+ * thread), a workgroup polls a peer's exchange word at most `spin_limit`
+ * times before it gives up (spin_limit < 0 restores the default, 2^20; 0
+ * gives up after the first poll).  Host-only; CREDIT_ERR_INVALID_ARG for a
+ * spin_limit above 2^32 - 1.
+ *
+ * credit_test_scratch: after synchronizing `stream`, set two fields of the
+ * control block of its split-row scratch (allocating the scratch if needed):
+ * the count of exchange tags issued (0 <= tags_used < 2^31; a test can make
+ * the next launches cross the point, 2^31, where the kernels clear the
+ * exchange words and restart the tags; tags_used < 0 leaves the count as it
+ * is), and, with unmatched_tags != 0, make every
+ * reader wait for a tag no workgroup writes (while fewer than 2^30 tags have
+ * been issued), so that every wait gives up: every kernel still runs to its
+ * end, the rows come out NaN (a quantizer's scales NaN) and
+ * credit_check_errors reports CREDIT_ERR_DEVICE_TIMEOUT.  unmatched_tags = 0
+ * restores normal exchanges.  CREDIT_ERR_INVALID_ARG for tags_used >= 2^31,
+ * CREDIT_ERR_HIP if a HIP call fails.
+ */
+credit_status_t credit_test_exchange(int64_t spin_limit);
+credit_status_t credit_test_scratch(int64_t tags_used, int32_t unmatched_tags, void *stream);
 
 /* Static, human-readable name of a status code. */
 const char *credit_status_str(credit_status_t status);

@@ -37,7 +37,8 @@ EXPORTED = ["credit_softmax", "credit_layernorm", "credit_rmsnorm", "credit_soft
             "credit_layernorm_backward", "credit_quantize_int8", "credit_select_path", "credit_make_plan",
             "credit_enumerate_plans", "credit_occupancy",
             "credit_run_plan", "credit_run_plan_timed", "credit_control", "credit_copy", "credit_flush",
-            "credit_load_calibration", "credit_check_errors", "credit_status_str", "credit_version"]
+            "credit_load_calibration", "credit_check_errors", "credit_status_str", "credit_version",
+            "credit_test_exchange", "credit_test_scratch"]
 
 
 class CreditError(RuntimeError):
@@ -110,6 +111,8 @@ def lib() -> ctypes.CDLL:
         "credit_check_errors": [vp],
         "credit_status_str": [i32],
         "credit_version": [],
+        "credit_test_exchange": [i64],
+        "credit_test_scratch": [i64, i32, vp],
     }
     for name, args in sig.items():
         fn = getattr(L, name)
@@ -127,6 +130,13 @@ def lib() -> ctypes.CDLL:
 def _check(status: int, where: str) -> None:
     if status != OK:
         raise CreditError(status, where)
+
+
+def _finish(check: bool, stream) -> None:
+    """With check=True: synchronize the stream and raise if a split-row
+    exchange wait gave up (credit_check_errors), whose rows were written as NaN."""
+    if check:
+        credit_check_errors(stream)
 
 
 def _stream(stream) -> Optional[int]:
@@ -178,41 +188,48 @@ def _same(x, t, name):
         raise ValueError("%s must be a contiguous tensor with x's shape and dtype" % name)
 
 
-def credit_softmax(x, y=None, path="auto", split_p: int = 0, stream=None):
+def credit_softmax(x, y=None, path="auto", split_p: int = 0, stream=None, check: bool = False):
     y = _out(x, y)
     rows, cols = _shape2d(x)
     _check(lib().credit_softmax(_ptr(x), _ptr(y), rows, cols, _dtype_code(x), _path(path), split_p,
                                 _stream(stream)), "credit_softmax")
+    _finish(check, stream)
     return y
 
 
-def credit_layernorm(x, gamma, beta, eps: float, y=None, path="auto", split_p: int = 0, stream=None):
+def credit_layernorm(x, gamma, beta, eps: float, y=None, path="auto", split_p: int = 0, stream=None,
+                     check: bool = False):
     y = _out(x, y)
     rows, cols = _shape2d(x)
     _check(lib().credit_layernorm(_ptr(x), _ptr(gamma), _ptr(beta), _ptr(y), rows, cols, float(eps),
                                   _dtype_code(x), _path(path), split_p, _stream(stream)), "credit_layernorm")
+    _finish(check, stream)
     return y
 
 
-def credit_rmsnorm(x, gamma, eps: float, y=None, path="auto", split_p: int = 0, stream=None):
+def credit_rmsnorm(x, gamma, eps: float, y=None, path="auto", split_p: int = 0, stream=None,
+                   check: bool = False):
     y = _out(x, y)
     rows, cols = _shape2d(x)
     _check(lib().credit_rmsnorm(_ptr(x), _ptr(gamma), _ptr(y), rows, cols, float(eps), _dtype_code(x),
                                 _path(path), split_p, _stream(stream)), "credit_rmsnorm")
+    _finish(check, stream)
     return y
 
 
-def credit_softmax_backward(x, dy, dx=None, path="auto", split_p: int = 0, stream=None):
+def credit_softmax_backward(x, dy, dx=None, path="auto", split_p: int = 0, stream=None, check: bool = False):
     """Gradient of row-wise softmax with respect to its logits x, given dy."""
     _same(x, dy, "dy")
     dx = _out(x, dx)
     rows, cols = _shape2d(x)
     _check(lib().credit_softmax_backward(_ptr(x), _ptr(dy), _ptr(dx), rows, cols, _dtype_code(x), _path(path),
                                          split_p, _stream(stream)), "credit_softmax_backward")
+    _finish(check, stream)
     return dx
 
 
-def credit_layernorm_backward(x, dy, gamma, eps: float, dx=None, path="auto", split_p: int = 0, stream=None):
+def credit_layernorm_backward(x, dy, gamma, eps: float, dx=None, path="auto", split_p: int = 0, stream=None,
+                              check: bool = False):
     """Row part of the LayerNorm gradient: dL/dx given dL/dy (fp32)."""
     _same(x, dy, "dy")
     dx = _out(x, dx)
@@ -220,10 +237,11 @@ def credit_layernorm_backward(x, dy, gamma, eps: float, dx=None, path="auto", sp
     _check(lib().credit_layernorm_backward(_ptr(x), _ptr(dy), _ptr(gamma), _ptr(dx), rows, cols, float(eps),
                                            _dtype_code(x), _path(path), split_p, _stream(stream)),
            "credit_layernorm_backward")
+    _finish(check, stream)
     return dx
 
 
-def credit_quantize_int8(x, q=None, scale=None, path="auto", split_p: int = 0, stream=None):
+def credit_quantize_int8(x, q=None, scale=None, path="auto", split_p: int = 0, stream=None, check: bool = False):
     """Row-wise symmetric int8 quantization: returns (q int8 like x, scale float32 [rows])."""
     import torch
     q = _out(x, q, torch.int8)
@@ -234,6 +252,7 @@ def credit_quantize_int8(x, q=None, scale=None, path="auto", split_p: int = 0, s
         raise ValueError("scale must be a contiguous float32 tensor with one entry per row")
     _check(lib().credit_quantize_int8(_ptr(x), _ptr(q), _ptr(scale), rows, cols, _dtype_code(x), _path(path),
                                       split_p, _stream(stream)), "credit_quantize_int8")
+    _finish(check, stream)
     return q, scale
 
 
@@ -285,13 +304,14 @@ def operands(t) -> Operands:
     return o
 
 
-def credit_run_plan(op, plan: Plan, t, eps: float = 0.0, stream=None):
+def credit_run_plan(op, plan: Plan, t, eps: float = 0.0, stream=None, check: bool = False):
     """Run `plan` on the operands in mapping `t` (see operands())."""
     op = OPS[op] if isinstance(op, str) else int(op)
     rows, cols = _shape2d(t["x"])
     o = operands(t)
     _check(lib().credit_run_plan(op, ctypes.byref(o), rows, cols, float(eps), _dtype_code(t["x"]),
                                  ctypes.byref(plan), _stream(stream)), "credit_run_plan")
+    _finish(check, stream)
     return t["y"]
 
 
@@ -336,6 +356,19 @@ def credit_check_errors(stream=None) -> None:
     _check(lib().credit_check_errors(_stream(stream)), "credit_check_errors")
 
 
+def credit_test_exchange(spin_limit: int = -1) -> None:
+    """Test hook: polls before a split-row exchange wait gives up (-1 = default)."""
+    _check(lib().credit_test_exchange(int(spin_limit)), "credit_test_exchange")
+
+
+def credit_test_scratch(tags_used: int, unmatched_tags: bool = False, stream=None) -> None:
+    """Test hook: set the exchange-tag count of the stream's split-row scratch
+    (tags_used < 0 leaves it) and, with unmatched_tags, make every exchange
+    wait give up."""
+    _check(lib().credit_test_scratch(int(tags_used), 1 if unmatched_tags else 0, _stream(stream)),
+           "credit_test_scratch")
+
+
 def credit_status_str(status: int) -> str:
     return lib().credit_status_str(status).decode()
 
@@ -344,22 +377,24 @@ def credit_version() -> int:
     return int(lib().credit_version())
 
 
-def run(op: str, t, eps: float = 0.0, path="auto", split_p: int = 0, stream=None):
+def run(op: str, t, eps: float = 0.0, path="auto", split_p: int = 0, stream=None, check: bool = False):
     """Dispatch by operator name to the matching entry point.  `t` maps operand
     names (x, dy, gamma, beta; outputs y and row_out, allocated when absent)
-    to tensors.  Returns the output row tensor (for quantization, (q, scale))."""
+    to tensors.  Returns the output row tensor (for quantization, (q, scale)).
+    check=True synchronizes and raises CreditError if a split-row exchange
+    wait gave up."""
     x = t["x"]
     y = t.get("y")
     if op == "softmax":
-        return credit_softmax(x, y, path, split_p, stream)
+        return credit_softmax(x, y, path, split_p, stream, check)
     if op == "layernorm":
-        return credit_layernorm(x, t["gamma"], t["beta"], eps, y, path, split_p, stream)
+        return credit_layernorm(x, t["gamma"], t["beta"], eps, y, path, split_p, stream, check)
     if op == "rmsnorm":
-        return credit_rmsnorm(x, t["gamma"], eps, y, path, split_p, stream)
+        return credit_rmsnorm(x, t["gamma"], eps, y, path, split_p, stream, check)
     if op == "softmax_bwd":
-        return credit_softmax_backward(x, t["dy"], y, path, split_p, stream)
+        return credit_softmax_backward(x, t["dy"], y, path, split_p, stream, check)
     if op == "layernorm_bwd":
-        return credit_layernorm_backward(x, t["dy"], t["gamma"], eps, y, path, split_p, stream)
+        return credit_layernorm_backward(x, t["dy"], t["gamma"], eps, y, path, split_p, stream, check)
     if op == "quantize_int8":
-        return credit_quantize_int8(x, y, t.get("row_out"), path, split_p, stream)
+        return credit_quantize_int8(x, y, t.get("row_out"), path, split_p, stream, check)
     raise ValueError(op)

@@ -3,6 +3,7 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
@@ -128,26 +129,35 @@ bool log_enabled()
 // ---------------------------------------------------------------------------
 // split-row scratch, one per (device, stream)
 //
-// The host mirrors the device ticket counter (next_ticket) and hands out the
-// exchange tags (next_tag); both advance only after a launch was enqueued, and
-// launches on one stream run in enqueue order, so each launch's ticket_base is
-// the device counter's value when it starts and its tags were never written
-// before.  Tag 0 is never used (the words start at zero); when the tags would
-// wrap, the words are cleared first.
+// A control block (SplitCtl) and the exchange words.  The protocol's state
+// (ticket counter, tags issued) lives in the control block and is advanced
+// by the kernels themselves (see split_kernel), so the host keeps no
+// counters: a launch enqueued by the host and one replayed from a graph see
+// the same state.  A zero-filled scratch is the initial state.
 // ---------------------------------------------------------------------------
-constexpr int64_t kSlotWords = INT64_C(1) << 17;  // 1 MiB of exchange words
-constexpr uint32_t kSpinLimit = 1u << 20;
+constexpr int64_t kDefaultSpinLimit = INT64_C(1) << 20;
+
+// Polls before a split-row wait gives up (credit_test_exchange).
+std::atomic<int64_t> g_spin_limit{kDefaultSpinLimit};
 
 struct Scratch {
-    SplitCtl *ctl = nullptr;
-    uint64_t *slots = nullptr;
-    uint32_t next_ticket = 0;
-    uint32_t next_tag = 1;
+    SplitCtl *ctl = nullptr;  // kScratchBytes: control block, then the exchange words
 };
 std::map<std::pair<int, hipStream_t>, Scratch> g_scratch;
 
-// Returns the scratch of (current device, s), allocating it on first use.
-// Caller holds g_mu.
+bool stream_capturing(hipStream_t s)
+{
+    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &st) != hipSuccess) {
+        (void)hipGetLastError();
+        return false;
+    }
+    return st != hipStreamCaptureStatusNone;
+}
+
+// Returns the scratch of (current device, s), allocating it on first use;
+// CREDIT_ERR_UNSUPPORTED if that first use is under stream capture (the
+// allocation cannot be captured).  Caller holds g_mu.
 credit_status_t get_scratch_locked(hipStream_t s, Scratch **out)
 {
     int dev = 0;
@@ -159,20 +169,20 @@ credit_status_t get_scratch_locked(hipStream_t s, Scratch **out)
         *out = &it->second;
         return CREDIT_OK;
     }
+    if (stream_capturing(s))
+        return CREDIT_ERR_UNSUPPORTED;
     void *mem = nullptr;
-    const size_t bytes = sizeof(SplitCtl) + kSlotWords * sizeof(uint64_t);
-    if (hipMalloc(&mem, bytes) != hipSuccess) {
+    if (hipMalloc(&mem, kScratchBytes) != hipSuccess) {
         (void)hipGetLastError();
         return CREDIT_ERR_HIP;
     }
-    if (hipMemset(mem, 0, bytes) != hipSuccess) {
+    if (hipMemset(mem, 0, kScratchBytes) != hipSuccess) {
         (void)hipGetLastError();
         (void)hipFree(mem);
         return CREDIT_ERR_HIP;
     }
     Scratch sc;
     sc.ctl = static_cast<SplitCtl *>(mem);
-    sc.slots = reinterpret_cast<uint64_t *>(static_cast<char *>(mem) + sizeof(SplitCtl));
     *out = &(g_scratch[key] = sc);
     return CREDIT_OK;
 }
@@ -267,7 +277,12 @@ credit_status_t launch_raw(const KernelEntry *k, uint32_t grid, uint32_t block, 
                            hipEvent_t ev_start, hipEvent_t ev_stop)
 {
     void *args[] = {arg};
-    const hipError_t e = hipExtLaunchKernel(k->fn, dim3(grid), dim3(block), args, 0, s, ev_start, ev_stop, 0);
+    // timed launches take the dispatch timestamps through hipExtLaunchKernel;
+    // the others use the plain launch, which stream capture records as a
+    // kernel node
+    const hipError_t e = (ev_start != nullptr || ev_stop != nullptr)
+                             ? hipExtLaunchKernel(k->fn, dim3(grid), dim3(block), args, 0, s, ev_start, ev_stop, 0)
+                             : hipLaunchKernel(k->fn, dim3(grid), dim3(block), args, 0, s);
     if (e != hipSuccess) {
         (void)hipGetLastError();
         return CREDIT_ERR_HIP;
@@ -356,6 +371,35 @@ credit_status_t occupancy(const KernelEntry *k, int *out)
     return CREDIT_OK;
 }
 
+// Split-row launches of kernel `k` for the rows of a0 on the scratch `ctl`
+// (kScratchBytes): persistent clusters, as many as `allowed` workgroups hold
+// and the exchange words cover, never more than there are rows; a launch
+// takes at most kMaxSplitIters row iterations per cluster.
+credit_status_t launch_split_on(const KernelEntry *k, const RowArgs &a0, int p, int q, int64_t allowed,
+                                SplitCtl *ctl, hipStream_t s, const LaunchEvents &ev)
+{
+    const int64_t clusters =
+        std::min({std::max<int64_t>(1, allowed / p), kSlotWords / (INT64_C(2) * p * q), a0.rows});
+    const int64_t rows_per_launch = clusters * static_cast<int64_t>(kMaxSplitIters);
+    const uint32_t spin = static_cast<uint32_t>(g_spin_limit.load());
+    for (int64_t r0 = 0; r0 < a0.rows; r0 += rows_per_launch) {
+        const int64_t n = std::min(rows_per_launch, a0.rows - r0);
+        const int64_t c = std::min(clusters, n);
+        SplitArgs sa;
+        sa.r = rows_from(a0, k->op, k->dt, r0, n);
+        sa.ctl = ctl;
+        sa.p = p;
+        sa.clusters = static_cast<int32_t>(c);
+        sa.spin_limit = spin;
+        const uint32_t grid = static_cast<uint32_t>(c * p);
+        const credit_status_t st = launch_raw(k, grid, k->block, &sa, s, r0 == 0 ? ev.start : nullptr,
+                                              r0 + n >= a0.rows ? ev.stop : nullptr);
+        if (st != CREDIT_OK)
+            return st;
+    }
+    return CREDIT_OK;
+}
+
 credit_status_t launch_split(const KernelEntry *k, const RowArgs &a0, int p, int q, int wgs_per_cu,
                              hipStream_t s, const LaunchEvents &ev)
 {
@@ -374,46 +418,7 @@ credit_status_t launch_split(const KernelEntry *k, const RowArgs &a0, int p, int
     st = get_scratch_locked(s, &sc);
     if (st != CREDIT_OK)
         return st;
-    // persistent clusters: as many as the device holds at once and the
-    // exchange words cover, never more than there are rows
-    const int64_t clusters = std::min({std::max<int64_t>(1, allowed / p), kSlotWords / (INT64_C(2) * p * q), a0.rows});
-    const int64_t max_iters = INT64_C(1) << 30;  // row iterations per launch (tag range)
-    const int64_t rows_per_launch = clusters * max_iters;
-    for (int64_t r0 = 0; r0 < a0.rows; r0 += rows_per_launch) {
-        const int64_t n = std::min(rows_per_launch, a0.rows - r0);
-        const int64_t c = std::min(clusters, n);
-        const uint32_t iters = static_cast<uint32_t>((n + c - 1) / c);
-        if (static_cast<uint64_t>(sc->next_tag) + iters > UINT64_C(0xFFFFFFFF)) {
-            const KernelEntry *z = find_misc(-3);
-            uint64_t *slots = sc->slots;
-            int64_t nw = kSlotWords;
-            void *zargs[] = {&slots, &nw};
-            if (hipLaunchKernel(z->fn, dim3(static_cast<uint32_t>(kSlotWords / 256)), dim3(256), zargs, 0, s) !=
-                hipSuccess) {
-                (void)hipGetLastError();
-                return CREDIT_ERR_HIP;
-            }
-            sc->next_tag = 1;
-        }
-        SplitArgs sa;
-        sa.r = rows_from(a0, k->op, k->dt, r0, n);
-        sa.ticket = &sc->ctl->ticket;
-        sa.error = &sc->ctl->error;
-        sa.slots = sc->slots;
-        sa.p = p;
-        sa.clusters = static_cast<int32_t>(c);
-        sa.ticket_base = sc->next_ticket;
-        sa.tag_base = sc->next_tag;
-        sa.spin_limit = kSpinLimit;
-        const uint32_t grid = static_cast<uint32_t>(c * p);
-        st = launch_raw(k, grid, k->block, &sa, s, r0 == 0 ? ev.start : nullptr,
-                        r0 + n >= a0.rows ? ev.stop : nullptr);
-        if (st != CREDIT_OK)
-            return st;
-        sc->next_ticket += grid;
-        sc->next_tag += iters;
-    }
-    return CREDIT_OK;
+    return launch_split_on(k, a0, p, q, allowed, sc->ctl, s, ev);
 }
 
 // Does `plan`'s tile exist and hold the row (or slice)?
@@ -868,6 +873,39 @@ credit_status_t credit_check_errors(void *stream)
         if (hipMemcpy(&sc.ctl->error, &zero, sizeof(zero), hipMemcpyHostToDevice) != hipSuccess)
             return CREDIT_ERR_HIP;
         return CREDIT_ERR_DEVICE_TIMEOUT;
+    }
+    return CREDIT_OK;
+}
+
+credit_status_t credit_test_exchange(int64_t spin_limit)
+{
+    if (spin_limit > INT64_C(0xFFFFFFFF))
+        return CREDIT_ERR_INVALID_ARG;
+    g_spin_limit.store(spin_limit < 0 ? kDefaultSpinLimit : spin_limit);
+    return CREDIT_OK;
+}
+
+credit_status_t credit_test_scratch(int64_t tags_used, int32_t unmatched_tags, void *stream)
+{
+    if (tags_used >= static_cast<int64_t>(kTagResetAt))
+        return CREDIT_ERR_INVALID_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    SplitCtl *ctl = nullptr;
+    {
+        std::lock_guard<std::mutex> lk(g_mu);
+        Scratch *sc = nullptr;
+        const credit_status_t st = get_scratch_locked(s, &sc);
+        if (st != CREDIT_OK)
+            return st;
+        ctl = sc->ctl;
+    }
+    const uint32_t used = static_cast<uint32_t>(tags_used);
+    const uint32_t unmatched = unmatched_tags != 0 ? kTagResetAt : 0u;
+    if (hipStreamSynchronize(s) != hipSuccess ||
+        (tags_used >= 0 && hipMemcpy(&ctl->tags_used, &used, sizeof(used), hipMemcpyHostToDevice) != hipSuccess) ||
+        hipMemcpy(&ctl->unmatched, &unmatched, sizeof(unmatched), hipMemcpyHostToDevice) != hipSuccess) {
+        (void)hipGetLastError();
+        return CREDIT_ERR_HIP;
     }
     return CREDIT_OK;
 }

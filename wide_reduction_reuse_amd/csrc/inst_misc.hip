@@ -1,5 +1,4 @@
-// Measurement and housekeeping kernels: streaming copy, cache flush, and the
-// fill that clears split-row exchange words.
+// Measurement kernels: streaming copy and cache flush.
 #include "kernels.hpp"
 #include "registry.hpp"
 
@@ -34,20 +33,10 @@ __global__ __launch_bounds__(256) void flush_kernel(u32x4 *__restrict__ buf, int
     }
 }
 
-// Zero n 64-bit words (vector stores; used instead of a memset so that the
-// clear is an ordinary kernel node wherever the stream is captured).
-__global__ __launch_bounds__(256) void zero_u64_kernel(uint64_t *__restrict__ p, int64_t n)
-{
-    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
-    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride)
-        p[i] = 0;
-}
-
 void register_misc_kernels(std::vector<KernelEntry> &out)
 {
     out.push_back(KernelEntry{0, -1, -1, 16, 256, 0, reinterpret_cast<const void *>(&copy_kernel)});
     out.push_back(KernelEntry{0, -2, -1, 16, 256, 0, reinterpret_cast<const void *>(&flush_kernel)});
-    out.push_back(KernelEntry{0, -3, -1, 8, 256, 0, reinterpret_cast<const void *>(&zero_u64_kernel)});
 }
 
 }  // namespace credit

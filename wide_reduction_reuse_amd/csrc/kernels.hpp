@@ -33,16 +33,21 @@
 // are running or finished; only the newest group can be incomplete, and its
 // missing members are the next workgroups to start.  As long as the device can
 // hold P workgroups at once, every waiting workgroup's peers are resident or
-// will be dispatched, so no launch-wide co-residency guarantee is needed.  The
-// counter is never reset: the host passes the value it holds at launch start.
+// will be dispatched, so no launch-wide co-residency guarantee is needed.
 //
 // Exchange words are 64-bit {value bits, tag}.  A cluster's words are double
 // buffered by the parity of the row iteration, and iteration i of a launch
-// writes tag tag_base + i; the host advances tag_base past every tag a launch
-// uses, so a reader polls a word until it carries the tag it expects and no
-// fence is needed between the data and its flag.  A peer can only overwrite a
-// buffer two iterations later, after every member has passed the exchange of
-// the iteration in between, i.e. after every member has read this buffer.
+// writes tag tags_used + 1 + i, where tags_used is read from the control block
+// (SplitCtl) at the start; a reader polls a word until it carries the tag it
+// expects, so no fence is needed between the data and its flag.  A peer can
+// only overwrite a buffer two iterations later, after every member has passed
+// the exchange of the iteration in between, i.e. after every member has read
+// this buffer.  The last workgroup of a launch to finish (counted on
+// ctl->done) resets the ticket counter and advances tags_used past every tag
+// the launch used, so the next launch on the scratch starts from a consistent
+// state whether it was enqueued by the host or replayed from a graph; it reads
+// that state only after this launch has ended (launches on one stream run in
+// order).
 #pragma once
 
 #include <type_traits>
@@ -706,6 +711,29 @@ __global__ __launch_bounds__(BLOCK) void single_wg_kernel(RowArgs a)
     }
 }
 
+// The end of every split-row workgroup, in its thread 0: count the
+// workgroup on ctl->done, and in the launch's last workgroup reset the ticket
+// counter and advance the tags past this launch's (clearing every exchange
+// word first when they reach kTagResetAt; one thread, once per 2^31 row
+// iterations).  Every workgroup reaches this only after its last exchange,
+// so when the last one arrives no word is read or written any more.
+__device__ __forceinline__ void finish_split_launch(const SplitArgs &a, uint32_t tag0)
+{
+    if (fetch_add_u32_agent(&a.ctl->done, 1u) != static_cast<uint32_t>(a.clusters * a.p) - 1u)
+        return;
+    const int64_t iters = (a.r.rows + a.clusters - 1) / a.clusters;
+    const uint32_t used = tag0 - 1u + static_cast<uint32_t>(iters);
+    const bool reset = used >= kTagResetAt;
+    if (reset) {
+        uint64_t *slots = scratch_slots(a.ctl);
+        for (int64_t i = 0; i < kSlotWords; ++i)
+            store_u64_agent(slots + i, 0);
+    }
+    store_u32_agent(&a.ctl->ticket, 0u);
+    store_u32_agent(&a.ctl->done, 0u);
+    store_u32_agent(&a.ctl->tags_used, reset ? 0u : used);
+}
+
 // ---------------------------------------------------------------------------
 // Path 2: P workgroups per row (see the header comment).  CONTROL = true is the
 // work-free control kernel: identical launch shape, tickets, exchange and
@@ -729,15 +757,20 @@ __global__ __launch_bounds__(BLOCK) void split_kernel(SplitArgs a)
     constexpr int VBO = out_vb<OP, T, VB>();
     __shared__ Partial sh[NW];
     __shared__ Partial peer[kMaxSplit];
-    __shared__ uint32_t sh_ticket;
+    __shared__ uint32_t sh_ticket, sh_tag0, sh_unmatched;
     __shared__ RawVec<VB> lds_params[param_lds_vectors<OP, VB, IT, BLOCK, kOwnerSlice>()];
     const int tid = threadIdx.x;
-    if (tid == 0)
-        sh_ticket = fetch_add_u32_agent(a.ticket, 1u) - a.ticket_base;
+    if (tid == 0) {
+        sh_ticket = fetch_add_u32_agent(&a.ctl->ticket, 1u);
+        sh_tag0 = load_u32_agent(&a.ctl->tags_used) + 1u;
+        sh_unmatched = load_u32_agent(&a.ctl->unmatched);
+    }
     __syncthreads();
-    // the modulo only guards against a counter the host's bookkeeping does not
-    // match; it keeps every index inside this launch's clusters and slots
+    // the modulo only guards against a control block left inconsistent (it
+    // cannot be by a launch that ran to its end); it keeps every index inside
+    // this launch's clusters and slots
     const uint32_t ticket = sh_ticket % gridDim.x;
+    const uint32_t tag0 = __builtin_amdgcn_readfirstlane(sh_tag0);  // uniform: keep the tags in SGPRs
     const int P = a.p;
     const int64_t k = ticket / static_cast<uint32_t>(P);
     const int c = static_cast<int>(ticket % static_cast<uint32_t>(P));
@@ -748,7 +781,7 @@ __global__ __launch_bounds__(BLOCK) void split_kernel(SplitArgs a)
     const int64_t ns = min(nv, v0 + per) - v0;  // vectors in this slice
     const int pos = (tid / kWave) * kWave * IT + (tid & (kWave - 1));  // this wave's run + lane
     const int kv = count_valid<IT, kWave>(ns, pos);
-    uint64_t *cslots = a.slots + k * 2 * P * Q;
+    uint64_t *cslots = scratch_slots(a.ctl) + k * 2 * P * Q;
 
     Tile<T, VB, IT> t[Op::kIn];
     PC pc;
@@ -790,17 +823,23 @@ __global__ __launch_bounds__(BLOCK) void split_kernel(SplitArgs a)
             wp = tile_partial<OP, T, VB, IT, BLOCK, kOwnerSlice>(t, kv, pc, pos, loc);
         const Partial sp = block_combine<OP, NW>(wp, sh);
 
-        // publish this slice's partial, then gather all P partials of the row
-        const uint32_t tag = a.tag_base + it;
+        // publish this slice's partial, then gather all P partials of the row.
+        // A wait that gives up flags the error word and takes NaN for the
+        // scalar it waited for: every operator's merge carries a NaN into the
+        // row's coefficients, so the slice's output is NaN (a quantizer's
+        // scale NaN) rather than computed from a stale word.
+        const uint32_t tag = tag0 + it;
         uint64_t *slots = cslots + (it & 1u) * P * Q;
         if (tid < Q)
             store_u64_agent(slots + c * Q + tid, (static_cast<uint64_t>(tag) << 32) | __float_as_uint(comp(sp, tid)));
         if (tid < P * Q) {
+            const uint32_t want = tag + sh_unmatched;
             uint64_t w = load_u64_agent(slots + tid);
             uint32_t polls = 0;
-            while (static_cast<uint32_t>(w >> 32) != tag) {
-                if (++polls > a.spin_limit) {
-                    fetch_or_u32_agent(a.error, 1u);
+            while (static_cast<uint32_t>(w >> 32) != want) {
+                if (polls++ >= a.spin_limit) {
+                    fetch_or_u32_agent(&a.ctl->error, 1u);
+                    w = 0x7FC00000u;  // NaN
                     break;
                 }
                 __builtin_amdgcn_s_sleep(1);
@@ -813,7 +852,7 @@ __global__ __launch_bounds__(BLOCK) void split_kernel(SplitArgs a)
 #pragma unroll
         for (int i = 0; i < kMaxSplit; ++i)
             parts[i] = peer[i];
-        const Partial rp = Op::template merge<kMaxSplit>(parts, P);
+        const Partial rp = ExchangeMerge<OP>::template apply<kMaxSplit>(parts, P);
         const Coef cf = Op::template finalize<T>(rp, loc, a.r.cols, a.r.eps);
         if constexpr (CONTROL) {
             (void)cf;
@@ -842,6 +881,10 @@ __global__ __launch_bounds__(BLOCK) void split_kernel(SplitArgs a)
         for (int64_t row = k; row < a.r.rows; row += a.clusters, ++it)
             step(row, it);
     }
+    // every thread of the workgroup is past its last exchange once thread 0
+    // is: each row's exchange ends in a barrier
+    if (tid == 0)
+        finish_split_launch(a, tag0);
 }
 
 // ---------------------------------------------------------------------------

@@ -929,6 +929,19 @@ struct OpTraits<kQuantInt8> {
         return Partial{{a}};
     }
 
+    // The merge of a split row's exchanged partials: as merge, but a NaN
+    // partial (an exchange word a workgroup gave up waiting for) makes the
+    // absmax NaN, which fmaxf alone would drop.
+    template <int N>
+    __device__ __forceinline__ static Partial merge_exchanged(const Partial (&p)[N], int n)
+    {
+        bool nan = false;
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+            nan |= i < n && p[i].v[0] != p[i].v[0];
+        return nan ? Partial{{__builtin_nanf("")}} : merge<N>(p, n);
+    }
+
     template <class T>
     __device__ __forceinline__ static Coef finalize(const Partial &row, const Local &, int64_t, float)
     {
@@ -972,6 +985,24 @@ struct OpTraits<kQuantInt8> {
     __device__ __forceinline__ static float apply_stream(const float (&in)[kIn], const Coef &c, float g, float b)
     {
         return apply<T>(in, c, g, b);
+    }
+};
+
+// The merge of the P partials a split row's workgroups exchanged.  For every
+// operator but the quantizer, merge itself carries a NaN partial (left by an
+// exchange wait that gave up) into the statistics and so into every
+// output: each folds the partials by sums, and softmax's maximum, which
+// fmaxf computes past a NaN, only scales sums that the NaN already reached.
+template <OpKind OP>
+struct ExchangeMerge {
+    template <int N>
+    __device__ __forceinline__ static typename OpTraits<OP>::Partial apply(
+        const typename OpTraits<OP>::Partial (&p)[N], int n)
+    {
+        if constexpr (OP == kQuantInt8)
+            return OpTraits<OP>::template merge_exchanged<N>(p, n);
+        else
+            return OpTraits<OP>::template merge<N>(p, n);
     }
 };
 

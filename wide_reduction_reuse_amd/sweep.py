@@ -29,30 +29,8 @@ from .timing import flush_buffer, summarize, time_launches
 
 
 def device_inputs(w: W.Workload) -> dict:
-    """The operand mapping of w (inputs drawn on the device from w's
-    distributions, seeded; outputs allocated)."""
-    import torch
-    g = torch.Generator(device="cuda")
-    g.manual_seed(w.seed)
-    x = torch.randn((w.rows, w.cols), generator=g, device="cuda", dtype=torch.float32)
-    if w.x_dist == "scaled_shifted":
-        x.mul_(w.x_scale).add_(w.x_shift)
-    elif w.x_dist == "outliers":
-        mask = torch.rand((w.rows, w.cols), generator=g, device="cuda") < w.outlier_prob
-        x = torch.where(mask, x * w.outlier_scale, x)
-    elif w.x_dist == "row_offset":
-        off = (torch.rand((w.rows, 1), generator=g, device="cuda") * 2.0 - 1.0) * w.row_offset
-        x.mul_(w.x_scale).add_(off)
-    gamma = beta = dy = None
-    if W.N_PARAMS[w.op] >= 1:
-        gamma = torch.rand(w.cols, generator=g, device="cuda") + 0.5
-    if W.N_PARAMS[w.op] >= 2:
-        beta = torch.randn(w.cols, generator=g, device="cuda") * 0.1
-    if w.inputs >= 2:
-        dy = torch.randn((w.rows, w.cols), generator=g, device="cuda", dtype=torch.float32)
-    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
-    cast = (lambda t: None if t is None else t.to(dt).contiguous())
-    return W.alloc_outputs(w, {"x": cast(x), "dy": cast(dy), "gamma": cast(gamma), "beta": cast(beta)})
+    """The operand mapping of w, inputs drawn on the device (W.device_inputs)."""
+    return W.device_inputs(w)
 
 
 def plan_key(p) -> str:

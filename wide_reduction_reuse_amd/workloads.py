@@ -32,7 +32,8 @@ width, which the paper's traffic measurement (Fig. 5) also uses:
 The second argument of N(mu, s) is the standard deviation.  Draw order from one
 ``numpy.random.Generator(PCG64(seed))``: x (float32), then the outlier mask or the
 row offsets, then gamma, then beta, then dy.  bf16 values are the float32 draws
-rounded to nearest, ties to even.
+rounded to nearest, ties to even.  ``device_inputs`` draws the same
+distributions on the GPU (torch's generator, same seed) for GiB-sized shapes.
 """
 from __future__ import annotations
 
@@ -431,6 +432,40 @@ def alloc_outputs(w: Workload, t: dict) -> dict:
         t["y"] = torch.empty_like(x)
         t["row_out"] = None
     return t
+
+
+def device_inputs(w: Workload) -> dict:
+    """The operand mapping of w with its inputs drawn on the device, for
+    GiB-sized shapes that need no host-side generation: x (and dy, gamma,
+    beta) from w's distributions with torch's generator seeded with w.seed,
+    drawn in float32 and rounded to the storage dtype (bf16: nearest, ties to
+    even); outputs allocated (alloc_outputs).  The values differ from
+    generate()'s (another generator); a check copies the rows it compares,
+    and the parameters, to the host."""
+    import torch
+    g = torch.Generator(device="cuda")
+    g.manual_seed(w.seed)
+    x = torch.randn((w.rows, w.cols), generator=g, device="cuda", dtype=torch.float32)
+    if w.x_dist == "scaled_shifted":
+        x.mul_(w.x_scale).add_(w.x_shift)
+    elif w.x_dist == "outliers":
+        mask = torch.rand((w.rows, w.cols), generator=g, device="cuda") < w.outlier_prob
+        x = torch.where(mask, x * w.outlier_scale, x)
+    elif w.x_dist == "row_offset":
+        off = (torch.rand((w.rows, 1), generator=g, device="cuda") * 2.0 - 1.0) * w.row_offset
+        x.mul_(w.x_scale).add_(off)
+    elif w.x_dist != "normal":
+        raise ValueError("unknown x_dist %r" % w.x_dist)
+    gamma = beta = dy = None
+    if N_PARAMS[w.op] >= 1:
+        gamma = torch.rand(w.cols, generator=g, device="cuda") + 0.5
+    if N_PARAMS[w.op] >= 2:
+        beta = torch.randn(w.cols, generator=g, device="cuda") * 0.1
+    if w.inputs >= 2:
+        dy = torch.randn((w.rows, w.cols), generator=g, device="cuda", dtype=torch.float32)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    cast = (lambda t: None if t is None else t.to(dt).contiguous())
+    return alloc_outputs(w, {"x": cast(x), "dy": cast(dy), "gamma": cast(gamma), "beta": cast(beta)})
 
 
 def custom(op: str, dtype: str, rows: int, cols: int, seed: int, **kw) -> Workload:
