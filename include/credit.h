@@ -271,6 +271,28 @@ credit_status_t credit_run_plan_timed(credit_op_t op, const credit_operands_t *o
                                       void *stop_event, void *stream);
 
 /*
+ * credit_run_plan for callers that cannot allocate device memory: code under
+ * stream (graph) capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, validation, errors and results as
+ * credit_run_plan; it allocates no device memory.  The split-row exchange
+ * uses the library's static scratch, one array of 1 MiB + 640 bytes per GPU
+ * (a control block and 2^17 exchange words), reserved when the library is
+ * loaded and held until the process ends; its address on a device is looked
+ * up on the first call there.  No shape needs more than that: a launch's
+ * clusters are capped to the words, and further rows loop.  Nothing in it
+ * needs clearing between calls: the kernels keep the control block consistent
+ * from one launch to the next (a first call may be captured, and a captured
+ * call replays correctly).  Paths 1 and 3 use no scratch at all.  Every call
+ * on one GPU shares that scratch, so calls whose split-row launches overlap
+ * on one GPU (from two streams without synchronization between them, or
+ * concurrent with their own graph replays) race and must not be made; calls
+ * on one stream are ordered by it.  credit_check_errors on any stream of the
+ * device also reads (and clears) the static scratch's error word.
+ */
+credit_status_t credit_run_plan_static(credit_op_t op, const credit_operands_t *ops, int64_t rows, int64_t cols,
+                                       float eps, credit_dtype_t dt, const credit_plan_t *plan, void *stream);
+
+/*
  * Work-free control kernel (Sec. III-D, the control that isolates launch,
  * scheduling, occupancy and synchronization costs): the split-row kernel of
  * `plan` with the same grid, tickets and exchange but no row loads or output
@@ -314,9 +336,10 @@ credit_status_t credit_load_calibration(const char *json_path);
 
 /*
  * Synchronize `stream` and read (then clear) the device error word of that
- * stream's split-row scratch: CREDIT_ERR_DEVICE_TIMEOUT if a spin-wait gave up
- * since the last check (the rows concerned were written as NaN),
- * CREDIT_ERR_HIP if synchronization failed, else CREDIT_OK.
+ * stream's split-row scratch, and of the current device's static scratch if
+ * credit_run_plan_static has used it: CREDIT_ERR_DEVICE_TIMEOUT if a
+ * spin-wait gave up since the last check (the rows concerned were written as
+ * NaN), CREDIT_ERR_HIP if synchronization failed, else CREDIT_OK.
  */
 credit_status_t credit_check_errors(void *stream);
 

@@ -31,7 +31,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,
           "-I", INCLUDE, "-I", CSRC]
 
 SOURCES = ["inst_softmax.hip", "inst_layernorm.hip", "inst_rmsnorm.hip", "inst_softmax_bwd.hip",
-           "inst_layernorm_bwd.hip", "inst_quantize.hip", "inst_misc.hip", "api.cpp", "planner.cpp"]
+           "inst_layernorm_bwd.hip", "inst_quantize.hip", "inst_misc.hip", "noalloc.hip", "api.cpp", "planner.cpp"]
 
 
 def _compile(src: str) -> str:

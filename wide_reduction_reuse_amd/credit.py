@@ -36,8 +36,8 @@ OPERANDS = {"softmax": ("x", "y"), "layernorm": ("x", "gamma", "beta", "y"), "rm
 EXPORTED = ["credit_softmax", "credit_layernorm", "credit_rmsnorm", "credit_softmax_backward",
             "credit_layernorm_backward", "credit_quantize_int8", "credit_select_path", "credit_make_plan",
             "credit_enumerate_plans", "credit_occupancy",
-            "credit_run_plan", "credit_run_plan_timed", "credit_control", "credit_copy", "credit_flush",
-            "credit_load_calibration", "credit_check_errors", "credit_status_str", "credit_version",
+            "credit_run_plan", "credit_run_plan_timed", "credit_run_plan_static", "credit_control", "credit_copy",
+            "credit_flush", "credit_load_calibration", "credit_check_errors", "credit_status_str", "credit_version",
             "credit_test_exchange", "credit_test_scratch"]
 
 
@@ -104,6 +104,7 @@ def lib() -> ctypes.CDLL:
         "credit_run_plan": [i32, ctypes.POINTER(Operands), i64, i64, f32, i32, ctypes.POINTER(Plan), vp],
         "credit_run_plan_timed": [i32, ctypes.POINTER(Operands), i64, i64, f32, i32, ctypes.POINTER(Plan), vp, vp,
                                   vp],
+        "credit_run_plan_static": [i32, ctypes.POINTER(Operands), i64, i64, f32, i32, ctypes.POINTER(Plan), vp],
         "credit_control": [i32, i64, i64, i32, ctypes.POINTER(Plan), vp, vp, vp],
         "credit_copy": [vp, vp, i64, vp, vp, vp],
         "credit_flush": [vp, i64, vp],
@@ -311,6 +312,18 @@ def credit_run_plan(op, plan: Plan, t, eps: float = 0.0, stream=None, check: boo
     o = operands(t)
     _check(lib().credit_run_plan(op, ctypes.byref(o), rows, cols, float(eps), _dtype_code(t["x"]),
                                  ctypes.byref(plan), _stream(stream)), "credit_run_plan")
+    _finish(check, stream)
+    return t["y"]
+
+
+def credit_run_plan_static(op, plan: Plan, t, eps: float = 0.0, stream=None, check: bool = False):
+    """credit_run_plan on the library's static split-row scratch: allocates no
+    device memory (for graph capture and serving loops)."""
+    op = OPS[op] if isinstance(op, str) else int(op)
+    rows, cols = _shape2d(t["x"])
+    o = operands(t)
+    _check(lib().credit_run_plan_static(op, ctypes.byref(o), rows, cols, float(eps), _dtype_code(t["x"]),
+                                        ctypes.byref(plan), _stream(stream)), "credit_run_plan_static")
     _finish(check, stream)
     return t["y"]
 

@@ -15,6 +15,7 @@
 #include <utility>
 #include <vector>
 
+#include "api_internal.hpp"
 #include "args.hpp"
 #include "credit.h"
 #include "planner.hpp"
@@ -400,8 +401,9 @@ credit_status_t launch_split_on(const KernelEntry *k, const RowArgs &a0, int p, 
     return CREDIT_OK;
 }
 
+// `fixed`: a scratch to use instead of the stream's own (null: the stream's).
 credit_status_t launch_split(const KernelEntry *k, const RowArgs &a0, int p, int q, int wgs_per_cu,
-                             hipStream_t s, const LaunchEvents &ev)
+                             hipStream_t s, const LaunchEvents &ev, SplitCtl *fixed)
 {
     int occ = 0;
     credit_status_t st = occupancy(k, &occ);
@@ -414,11 +416,15 @@ credit_status_t launch_split(const KernelEntry *k, const RowArgs &a0, int p, int
     const int64_t allowed = wgs_per_cu > 0 ? std::min<int64_t>(resident, int64_t(wgs_per_cu) * d.cus) : resident;
     if (resident < p)
         return CREDIT_ERR_NOT_CORESIDENT;
-    Scratch *sc = nullptr;
-    st = get_scratch_locked(s, &sc);
-    if (st != CREDIT_OK)
-        return st;
-    return launch_split_on(k, a0, p, q, allowed, sc->ctl, s, ev);
+    SplitCtl *ctl = fixed;
+    if (ctl == nullptr) {
+        Scratch *sc = nullptr;
+        st = get_scratch_locked(s, &sc);
+        if (st != CREDIT_OK)
+            return st;
+        ctl = sc->ctl;
+    }
+    return launch_split_on(k, a0, p, q, allowed, ctl, s, ev);
 }
 
 // Does `plan`'s tile exist and hold the row (or slice)?
@@ -484,7 +490,7 @@ void to_c_plan(const Plan &p, credit_plan_t *out)
 
 credit_status_t run_plan_checked(int op, const credit_operands_t &t, int64_t rows, int64_t cols, float eps, int dt,
                                  const credit_plan_t &plan, hipStream_t s, bool control,
-                                 const LaunchEvents &ev = LaunchEvents{})
+                                 const LaunchEvents &ev = LaunchEvents{}, SplitCtl *fixed = nullptr)
 {
     const KernelEntry *k = nullptr;
     int kind = 0;
@@ -515,7 +521,7 @@ credit_status_t run_plan_checked(int op, const credit_operands_t &t, int64_t row
                      k->part == 1 ? " (partial last vector)" : (k->part == 2 ? " (odd bf16 row)" : ""),
                      control ? " (control)" : "");
     if (kind == kKindSplit)
-        return launch_split(k, a, plan.split_p, stats_per_partial(op), plan.wgs_per_cu, s, ev);
+        return launch_split(k, a, plan.split_p, stats_per_partial(op), plan.wgs_per_cu, s, ev, fixed);
     return launch_rowwise(k, a, plan.wgs_per_cu, s, ev);
 }
 
@@ -563,6 +569,25 @@ credit_operands_t operands(const void *x, const void *dy, const void *gamma, con
 }
 
 }  // namespace
+
+credit_status_t validate_operands(credit_op_t op, const credit_operands_t &ops, int64_t rows, int64_t cols,
+                                  float eps, credit_dtype_t dt, bool *noop)
+{
+    return validate(op, ops, rows, cols, eps, dt, noop);
+}
+
+credit_status_t run_plan_on_scratch(credit_op_t op, const credit_operands_t &ops, int64_t rows, int64_t cols,
+                                    float eps, credit_dtype_t dt, const credit_plan_t &plan, void *stream,
+                                    SplitCtl *ctl)
+{
+    bool noop = false;
+    const credit_status_t st = validate(op, ops, rows, cols, eps, dt, &noop);
+    if (st != CREDIT_OK || noop)
+        return st;
+    return run_plan_checked(op, ops, rows, cols, eps, dt, plan, static_cast<hipStream_t>(stream), false,
+                            LaunchEvents{}, ctl);
+}
+
 }  // namespace credit
 
 namespace credit {
@@ -857,24 +882,32 @@ credit_status_t credit_check_errors(void *stream)
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess)
         return CREDIT_ERR_HIP;
-    Scratch sc;
+    SplitCtl *ctls[2] = {nullptr, static_scratch_if_set_up()};
     {
         std::lock_guard<std::mutex> lk(g_mu);
         auto it = g_scratch.find(std::make_pair(dev, s));
-        if (it == g_scratch.end())
-            return CREDIT_OK;
-        sc = it->second;  // the device pointers only
+        if (it != g_scratch.end())
+            ctls[0] = it->second.ctl;
     }
-    uint32_t err = 0;
-    if (hipMemcpy(&err, &sc.ctl->error, sizeof(err), hipMemcpyDeviceToHost) != hipSuccess)
-        return CREDIT_ERR_HIP;
-    if (err != 0) {
-        const uint32_t zero = 0;
-        if (hipMemcpy(&sc.ctl->error, &zero, sizeof(zero), hipMemcpyHostToDevice) != hipSuccess)
+    bool timed_out = false;
+    for (SplitCtl *ctl : ctls) {
+        if (ctl == nullptr)
+            continue;
+        uint32_t err = 0;
+        if (hipMemcpy(&err, &ctl->error, sizeof(err), hipMemcpyDeviceToHost) != hipSuccess) {
+            (void)hipGetLastError();
             return CREDIT_ERR_HIP;
-        return CREDIT_ERR_DEVICE_TIMEOUT;
+        }
+        if (err != 0) {
+            const uint32_t zero = 0;
+            if (hipMemcpy(&ctl->error, &zero, sizeof(zero), hipMemcpyHostToDevice) != hipSuccess) {
+                (void)hipGetLastError();
+                return CREDIT_ERR_HIP;
+            }
+            timed_out = true;
+        }
     }
-    return CREDIT_OK;
+    return timed_out ? CREDIT_ERR_DEVICE_TIMEOUT : CREDIT_OK;
 }
 
 credit_status_t credit_test_exchange(int64_t spin_limit)
