@@ -11,7 +11,8 @@ import os
 from typing import Optional
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libcredit.so")
+# CREDIT_LIB may name another build of the library (the host-ASan variant)
+LIB_PATH = os.environ.get("CREDIT_LIB") or os.path.join(PKG, "libcredit.so")
 # selector calibration measured on MI355X, loaded with the library unless
 # CREDIT_CALIB names another file (the library then loads that one itself)
 CALIB_PATH = os.path.join(PKG, "calib", "mi355x.json")
