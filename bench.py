@@ -2,7 +2,7 @@
 """Benchmark of the reduction-reuse hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--all FILE] [--no-cpu]
+                    [--all FILE] [--no-cpu] [--path P --split-p N] [--no-copy]
 
 A step is one pass of the hot path over one batch of synthetic input that is
 already resident in HBM: the selector picks a plan for the shape
@@ -177,6 +177,10 @@ def main(argv=None) -> int:
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy", type=int, default=0, metavar="MIB",
                     help="only time the streaming-copy kernel on MIB MiB (the reference for counter scaling)")
+    ap.add_argument("--path", default="auto", choices=("auto", "single", "split", "reread"),
+                    help="force a path (for profiling one path; the default line uses the selector's plan)")
+    ap.add_argument("--split-p", type=int, default=0, help="with --path split: workgroups per row (0 = chosen)")
+    ap.add_argument("--no-copy", action="store_true", help="skip timing the streaming copy of the same bytes")
     a = ap.parse_args(argv)
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the row-wise operators shard by rows with no "
@@ -198,13 +202,17 @@ def main(argv=None) -> int:
 
     w = W.NAMED[a.workload]
     inp = W.generate(w)
-    plan = C.credit_select_path(w.op, w.dtype, w.rows, w.cols)
-    r = run_workload(w, "auto", 0, a.steps, a.warmup, flush_buf, inputs=inp)
+    if a.path == "auto":
+        plan = C.credit_select_path(w.op, w.dtype, w.rows, w.cols)
+        r = run_workload(w, "auto", 0, a.steps, a.warmup, flush_buf, inputs=inp)
+    else:
+        plan = C.credit_plan(w.op, w.dtype, w.rows, w.cols, a.path, a.split_p)
+        r = run_workload(w, a.path, a.split_p, a.steps, a.warmup, flush_buf, inputs=inp, plan=plan)
     achieved = r["gbs"]
     traffic = load_traffic(a.workload, plan)
     # the streaming copy of the same number of bytes (half read, half written),
     # timed the same way: the ceiling a kernel of this size can reach here
-    copy = copy_ceiling(w.algorithmic_bytes() // 2 // 16 * 16, a.steps, a.warmup, flush_buf)
+    copy = None if a.no_copy else copy_ceiling(w.algorithmic_bytes() // 2 // 16 * 16, a.steps, a.warmup, flush_buf)
     result = {
         "metric": METRIC,
         "value": round(achieved, 2),
@@ -225,8 +233,9 @@ def main(argv=None) -> int:
                    "median_ms": round(r["median_ms"], 5), "min_ms": round(r["min_ms"], 5),
                    "wall_s_timed_loop_incl_flush": round(r["wall_s"], 4),
                    "timing": "hipExtLaunchKernel dispatch timestamps",
-                   "copy_same_bytes_gbs": round(copy["gbs"], 2),
-                   "frac_of_copy_same_bytes": round(achieved / copy["gbs"], 4)},
+                   "plan_forced": a.path != "auto",
+                   "copy_same_bytes_gbs": None if copy is None else round(copy["gbs"], 2),
+                   "frac_of_copy_same_bytes": None if copy is None else round(achieved / copy["gbs"], 4)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None if traffic is None else traffic["bytes_per_launch"]},

@@ -211,6 +211,44 @@ credit_status_t credit_select_path(credit_op_t op, credit_dtype_t dt, int64_t ro
                                    credit_plan_t *out);
 
 /*
+ * The terms of the selector's analytic cost model (Sec. III-D) for splitting
+ * the rows of a shape over split_p workgroups (2, 4 or 8), priced against the
+ * non-split baseline: path 1 when one owner holds the row, else path 3.
+ * Evaluated with the model constants of the calibration in force (its table
+ * of measured plans is not used).  Times in microseconds.
+ */
+typedef struct {
+    int32_t baseline_path;  /* 1 or 3 */
+    int32_t split_block;    /* the split tile the terms are for: threads, */
+    int32_t split_items;    /* and vectors per thread */
+    int32_t split_resident; /* S: split workgroups the device holds at once */
+    double t_base_us;       /* T_B: the baseline's predicted time */
+    double b_base;          /* bytes per element the baseline moves (Eq. 4) */
+    double b_reread;        /* of which its reread: the row inputs' bytes on path 3, else 0 */
+    double t_save_us;       /* Eq. 7: (b_reread / b_base) * t_base_us */
+    double t_occ_us;        /* the time a baseline that leaves CUs idle gives back:
+                               (t_base_us - t_save_us) * (1 - u_base / u_split), u = the
+                               fraction of the CUs given work */
+    double waves;           /* Eq. 8: W = ceil(rows / floor(S / split_p)), S = split
+                               workgroups the device holds at once */
+    double t_ctrl_us;       /* W exchanges plus the split launch's control cost */
+    double t_dsm_us;        /* s * W * (split_p - 1) * q / B_w: exchange words, not
+                               multiplied by split_p */
+    double delta_us;        /* Eq. 9: t_save + t_occ - t_ctrl - t_dsm (T_replay = T_deposit = 0:
+                               slices are held in registers) */
+    double t_split_us;      /* t_base_us - delta_us */
+} credit_model_terms_t;
+
+/*
+ * Fill *out with the model terms above.  CREDIT_ERR_ILLEGAL_PATH if no split
+ * tile holds a 1/split_p slice of the row, CREDIT_ERR_INVALID_ARG for a null
+ * out, split_p outside {2, 4, 8} or a bad shape, CREDIT_ERR_UNSUPPORTED for an
+ * (op, dtype) without kernels.  Host-only.
+ */
+credit_status_t credit_model_terms(credit_op_t op, credit_dtype_t dt, int64_t rows, int64_t cols, int32_t split_p,
+                                   credit_model_terms_t *out);
+
+/*
  * The plan the operator entry points use for `path` and `split_p` (the same
  * arguments and rules as credit_softmax & co.; CREDIT_PATH_AUTO with
  * split_p = 0 equals credit_select_path).  Returns CREDIT_ERR_ILLEGAL_PATH if

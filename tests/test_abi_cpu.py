@@ -249,14 +249,17 @@ def test_calibration_loader(tmp_path):
     noversion = tmp_path / "nov.json"
     noversion.write_text(json.dumps({"stream_gbs": 5000}))
     assert L.credit_load_calibration(str(noversion).encode()) == 6
+    invalid = tmp_path / "invalid.json"
+    invalid.write_text(json.dumps({"version": 1, "model": {"bw_gbs": 0.0}}))
+    assert L.credit_load_calibration(str(invalid).encode()) == 6
     good = tmp_path / "good.json"
-    good.write_text(json.dumps({"version": 1, "stream_gbs": 1000.0, "launch_us": 2.0,
+    good.write_text(json.dumps({"version": 1, "model": {"bw_gbs": 1000.0, "launch_us": 2.0},
                                 "device": {"cus": 256, "xcds": 8}}))
     assert L.credit_load_calibration(str(good).encode()) == 0
     slow = C.credit_select_path("softmax", "f32", 4096, 4096).predicted_us[0]
     assert L.credit_load_calibration(None) == 0
     fast = C.credit_select_path("softmax", "f32", 4096, 4096).predicted_us[0]
-    assert slow > fast  # 1000 GB/s calibrated streaming is slower than the default model
+    assert slow > fast  # 1000 GB/s model streaming is slower than the default model
 
 
 def test_make_plan_matches_selector_and_honours_forced_paths():

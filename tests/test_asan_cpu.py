@@ -39,6 +39,11 @@ def grid():
                             C.credit_occupancy  # host-only below
                         except C.CreditError as e:
                             assert e.status in (1, 2, 4), (op, dt, rows, cols, path, p, e.status)
+                for p in (2, 4, 8):
+                    try:
+                        C.credit_model_terms(op, dt, max(rows, 1), cols, p)
+                    except C.CreditError as e:
+                        assert e.status in (1, 2, 4), (op, dt, rows, cols, p, e.status)
                 try:
                     C.credit_select_path(op, dt, rows, cols)
                     plans = C.credit_enumerate_plans(op, dt, rows, cols)

@@ -127,6 +127,12 @@ def write_calibration(path: str, cal: dict) -> None:
                 f.write(' "%s": %s,\n' % (k, cal[k]))
         if "device" in cal:
             f.write(' "device": %s,\n' % json.dumps(cal["device"]))
+        if "model" in cal:
+            f.write(' "model": %s,\n' % json.dumps(cal["model"]))
+        if "occupancy" in cal:
+            f.write(' "occupancy": [\n')
+            f.write(",\n".join("  " + json.dumps(row) for row in cal["occupancy"]))
+            f.write("\n ],\n")
         f.write(' "table": [\n')
         f.write(",\n".join("  " + json.dumps(row) for row in cal["table"]))
         f.write("\n ]\n}\n")

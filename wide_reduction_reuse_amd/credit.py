@@ -39,7 +39,7 @@ EXPORTED = ["credit_softmax", "credit_layernorm", "credit_rmsnorm", "credit_soft
             "credit_enumerate_plans", "credit_occupancy",
             "credit_run_plan", "credit_run_plan_timed", "credit_run_plan_static", "credit_control", "credit_copy",
             "credit_flush", "credit_load_calibration", "credit_check_errors", "credit_status_str", "credit_version",
-            "credit_test_exchange", "credit_test_scratch"]
+            "credit_test_exchange", "credit_test_scratch", "credit_model_terms"]
 
 
 class CreditError(RuntimeError):
@@ -65,6 +65,16 @@ class Plan(ctypes.Structure):
         p.path, p.split_p, p.block_threads, p.items, p.vec_bytes = path, split_p, block_threads, items, vec_bytes
         p.wgs_per_cu = wgs_per_cu
         return p
+
+
+class ModelTerms(ctypes.Structure):
+    _fields_ = [("baseline_path", ctypes.c_int32), ("split_block", ctypes.c_int32),
+                ("split_items", ctypes.c_int32), ("split_resident", ctypes.c_int32)] + \
+               [(k, ctypes.c_double) for k in ("t_base_us", "b_base", "b_reread", "t_save_us", "t_occ_us", "waves",
+                                               "t_ctrl_us", "t_dsm_us", "delta_us", "t_split_us")]
+
+    def as_dict(self) -> dict:
+        return {k: getattr(self, k) for k, _ in self._fields_}
 
 
 class Operands(ctypes.Structure):
@@ -115,6 +125,7 @@ def lib() -> ctypes.CDLL:
         "credit_version": [],
         "credit_test_exchange": [i64],
         "credit_test_scratch": [i64, i32, vp],
+        "credit_model_terms": [i32, i32, i64, i64, i32, ctypes.POINTER(ModelTerms)],
     }
     for name, args in sig.items():
         fn = getattr(L, name)
@@ -273,6 +284,15 @@ def credit_plan(op, dtype, rows: int, cols: int, path="auto", split_p: int = 0) 
     dt = DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
     _check(lib().credit_make_plan(op, dt, rows, cols, _path(path), split_p, ctypes.byref(p)), "credit_make_plan")
     return p
+
+
+def credit_model_terms(op, dtype, rows: int, cols: int, split_p: int) -> ModelTerms:
+    """The analytic model's Eq. 7-9 terms for splitting the shape P ways."""
+    t = ModelTerms()
+    op = OPS[op] if isinstance(op, str) else int(op)
+    dt = DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
+    _check(lib().credit_model_terms(op, dt, rows, cols, split_p, ctypes.byref(t)), "credit_model_terms")
+    return t
 
 
 def credit_enumerate_plans(op, dtype, rows: int, cols: int):

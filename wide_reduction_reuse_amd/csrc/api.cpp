@@ -108,13 +108,27 @@ DeviceModel device_model_locked()
     return d;
 }
 
-// The calibration in force with the device description filled in.  Caller
-// holds g_mu.
+credit_status_t occupancy(const KernelEntry *k, int *out);
+
+// Resident workgroups per CU of the compiled kernel `key` names, from the HIP
+// runtime; 0 when there is no such kernel or no device to ask.
+int kernel_occupancy(const OccKey &key)
+{
+    const KernelEntry *k = find_kernel(key.kind, key.op, key.dt, key.vb, key.block, key.items, key.part);
+    int occ = 0;
+    if (k == nullptr || occupancy(k, &occ) != CREDIT_OK)
+        return 0;
+    return occ;
+}
+
+// The calibration in force with the device description and the compiled
+// kernels' occupancy filled in.  Caller holds g_mu.
 Calibration calibration_locked()
 {
     load_env_calibration_locked();
     Calibration cal = g_cal;
     cal.device = device_model_locked();
+    cal.occ_query = kernel_occupancy;
     return cal;
 }
 
@@ -349,27 +363,31 @@ credit_status_t launch_rowwise(const KernelEntry *k, const RowArgs &a0, int wgs_
     return CREDIT_OK;
 }
 
-// Workgroups of kernel `fn` (block threads) one CU holds at once; cached.
+// Workgroups of kernel `k` one CU holds at once; cached, failures too (a
+// process without a usable device asks once).  Its own lock: the planner
+// asks while g_mu is held.
 credit_status_t occupancy(const KernelEntry *k, int *out)
 {
-    static std::map<const void *, int> cache;
+    static std::mutex mu;
+    static std::map<const void *, int> cache;  // 0: the query failed
     {
-        std::lock_guard<std::mutex> lk(g_mu);
+        std::lock_guard<std::mutex> lk(mu);
         auto it = cache.find(k->fn);
         if (it != cache.end()) {
             *out = it->second;
-            return CREDIT_OK;
+            return it->second > 0 ? CREDIT_OK : CREDIT_ERR_HIP;
         }
     }
     int occ = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k->fn, k->block, 0) != hipSuccess) {
+    const int block = k->kind == kKindWave ? 64 * kWaveRowsPerWg : k->block;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k->fn, block, 0) != hipSuccess || occ < 1) {
         (void)hipGetLastError();
-        return CREDIT_ERR_HIP;
+        occ = 0;
     }
-    std::lock_guard<std::mutex> lk(g_mu);
+    std::lock_guard<std::mutex> lk(mu);
     cache[k->fn] = occ;
     *out = occ;
-    return CREDIT_OK;
+    return occ > 0 ? CREDIT_OK : CREDIT_ERR_HIP;
 }
 
 // Split-row launches of kernel `k` for the rows of a0 on the scratch `ctl`
@@ -700,6 +718,48 @@ credit_status_t credit_make_plan(credit_op_t op, credit_dtype_t dt, int64_t rows
     if (!make_plan(req, cal, path, split_p <= 1 ? 0 : split_p, &p))
         return CREDIT_ERR_ILLEGAL_PATH;
     to_c_plan(p, out);
+    return CREDIT_OK;
+}
+
+credit_status_t credit_model_terms(credit_op_t op, credit_dtype_t dt, int64_t rows, int64_t cols, int32_t split_p,
+                                   credit_model_terms_t *out)
+{
+    if (out == nullptr || rows < 1 || cols < 1 || (split_p != 2 && split_p != 4 && split_p != 8))
+        return CREDIT_ERR_INVALID_ARG;
+    const credit_status_t st = check_op_dt(op, dt);
+    if (st != CREDIT_OK)
+        return st;
+    std::lock_guard<std::mutex> lk(g_mu);
+    const Calibration cal = calibration_locked();
+    PlanRequest req;
+    req.op = op;
+    req.dt = dt;
+    req.rows = rows;
+    req.cols = cols;
+    TileSpec t;
+    if (!split_tile(op, dt, cols, split_p, &t))
+        return CREDIT_ERR_ILLEGAL_PATH;
+    int base_path = 0;
+    TileSpec base_tile;
+    double base_us = 0.0;
+    if (!analytic_baseline(req, cal, &base_path, &base_tile, &base_us))
+        return CREDIT_ERR_ILLEGAL_PATH;
+    const SplitTerms r = split_terms(req, cal, split_p, t, base_path, base_tile, base_us);
+    std::memset(out, 0, sizeof(*out));
+    out->baseline_path = base_path;
+    out->split_block = t.block;
+    out->split_items = t.items;
+    out->split_resident = static_cast<int32_t>(r.resident);
+    out->t_base_us = r.t_base_us;
+    out->b_base = r.b_base;
+    out->b_reread = r.b_reread;
+    out->t_save_us = r.t_save_us;
+    out->t_occ_us = r.t_occ_us;
+    out->waves = r.waves;
+    out->t_ctrl_us = r.t_ctrl_us;
+    out->t_dsm_us = r.t_dsm_us;
+    out->delta_us = r.delta_us;
+    out->t_split_us = r.t_split_us;
     return CREDIT_OK;
 }
 

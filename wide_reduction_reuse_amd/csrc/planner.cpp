@@ -118,9 +118,11 @@ const std::vector<TileSpec> &tiles_for(int kind, int vb_is_16)
 }
 
 // Preference among tiles that can hold `nv` vectors: the smallest capacity,
-// and within a capacity the one closest to 2 vectors per thread (then more
-// threads); measured on MI355X, two 16-byte vectors per thread over many
-// threads streamed fastest for most widths, one per thread slower.
+// then the one whose thread count is nearest 512, then fewer vectors per
+// thread.  On the calibration shapes of MI355X (every legal plan timed), this
+// rule picks a tile within 1% of the fastest of its path more often than
+// preferring two vectors per thread, the most resident waves or the most
+// bytes in flight.
 static bool pick_holding_tile(const std::vector<TileSpec> &ladder, int64_t nv, TileSpec *out)
 {
     bool found = false;
@@ -132,8 +134,9 @@ static bool pick_holding_tile(const std::vector<TileSpec> &ladder, int64_t nv, T
             continue;
         bool better = !found || cap < best_cap;
         if (found && cap == best_cap) {
-            const int d_new = std::abs(t.items - 2), d_old = std::abs(best.items - 2);
-            better = d_new < d_old || (d_new == d_old && t.block > best.block);
+            auto from512 = [](int block) { return std::abs(std::log2(static_cast<double>(block)) - 9.0); };
+            const double d_new = from512(t.block), d_old = from512(best.block);
+            better = d_new < d_old || (d_new == d_old && t.items < best.items);
         }
         if (better) {
             best = t;
@@ -213,64 +216,28 @@ double tile_capacity_bytes(const TileSpec &t) { return static_cast<double>(t.blo
 double onchip_budget_bytes(const DeviceModel &d) { return d.vgpr_bytes_per_cu + d.lds_bytes_per_cu; }
 
 // ---------------------------------------------------------------------------
-// Cost model
+// Cost model (CREDIT paper, Sec. III-D), for gfx950.
+//
+// stream_time_us prices one launch of a non-split plan from its shape, its
+// tile and the compiled kernel's occupancy: owners (rows, or row slices)
+// run in rounds of the resident slots; a round streams its bytes at the
+// device rate unless the bytes in flight per CU are too few to cover the
+// memory latency (occupancy enters here), and no owner finishes a row faster
+// than a fixed latency plus a cost per vector each thread holds.  The split
+// path is priced the paper's way, relative to the best non-split baseline
+// (split_terms: Eq. 7's saved reread at the baseline's own rate, Eq. 8's row
+// waves, Eq. 9's difference), with one term added for gfx950: a baseline that
+// leaves CUs idle (fewer owners than CUs) gains from splitting rows across
+// them even when it rereads nothing.  The constants are fitted to exhaustive
+// timings of calibration shapes (model_fit.py) and can be replaced by a
+// calibration file.
 // ---------------------------------------------------------------------------
 namespace {
 
-struct Model {
-    double stream_gbs, per_cu_gbs, launch_us, exchange_us, hit_l2;
-};
-
-Model model_of(const Calibration &c)
-{
-    Model m;
-    m.stream_gbs = c.peak_bandwidth ? c.device.hbm_peak_gbs
-                                    : (c.stream_gbs > 0 ? c.stream_gbs : 0.8 * c.device.hbm_peak_gbs);
-    m.per_cu_gbs = c.per_cu_gbs > 0 ? c.per_cu_gbs : 50.0;
-    m.launch_us = c.launch_us >= 0 ? c.launch_us : 4.0;
-    m.exchange_us = c.exchange_us >= 0 ? c.exchange_us : 3.0;
-    m.hit_l2 = c.reread_hit_l2 >= 0 ? c.reread_hit_l2 : 0.9;
-    return m;
-}
-
-double eff_of(const double (&e)[kNumOps][2], int op, int dt)
-{
-    const double v = e[op][dt];
-    return v > 0 ? v : 1.0;
-}
-
-// Estimated resident workgroups per CU for a tile: VGPRs from the held data
-// plus a fixed overhead, 512 VGPRs per SIMD lane, 4 SIMDs, at most 8 waves/SIMD.
-int wgs_per_cu(const TileSpec &t, int inputs)
-{
-    const int waves = t.block / 64;
-    const int data_vgprs = inputs * ((t.kind == kKindReread) ? t.items * t.vb / 4 * 2 : t.items * t.vb / 4);
-    int vgprs = data_vgprs + 32;
-    vgprs = (vgprs + 7) / 8 * 8;
-    int waves_per_simd = std::min(8, 512 / vgprs);
-    int per_cu = (4 * waves_per_simd) / std::max(1, waves);
-    if (t.kind == kKindWave)
-        per_cu = (4 * waves_per_simd) / 4;  // 4 waves (4 rows) per workgroup
-    return std::max(1, per_cu);
-}
-
-// Time to stream `bytes` with `units` independent workgroups of which at most
-// `resident` run at once on `cus` CUs.
-double stream_us(const Model &m, const DeviceModel &d, double bytes, double units, double per_cu)
-{
-    const double active_cus = std::min<double>(d.cus, units);
-    double bw = std::min(m.stream_gbs, active_cus * m.per_cu_gbs);
-    (void)per_cu;
-    return bytes / (bw * 1e3);  // GB/s = 1e3 bytes/us
-}
-
-}  // namespace
-
-namespace {
+constexpr double kExchangeWordBytes = 8.0;  // one {value, tag} exchange word
 
 // b_in: bytes per element of all row inputs (the bytes a reread reads again);
-// b_out: bytes per element written; bytes_io: one read of every input, one
-// write of the output, each parameter vector once and the per-row outputs.
+// b_out: bytes per element written; row_bytes = N (b_in + b_out).
 struct Shape {
     double M, N, b_in, b_out, row_bytes, bytes_io;
     int inputs;
@@ -284,77 +251,125 @@ Shape shape_of(const PlanRequest &req)
     s.b_in = in_bytes(req.op, req.dt);
     s.b_out = out_bytes(req.op, req.dt);
     s.inputs = op_inputs(req.op);
-    s.row_bytes = s.N * s.b_in;
+    s.row_bytes = s.N * (s.b_in + s.b_out);
     s.bytes_io = s.M * s.N * (s.b_in + s.b_out) + s.N * elem_bytes(req.dt) * n_params(req.op) +
                  s.M * row_out_bytes(req.op);
     return s;
 }
 
-PathEstimate estimate_single(const PlanRequest &req, const Calibration &cal, const TileSpec &t)
+// Estimated resident workgroups per CU for a tile when the compiled
+// kernel's occupancy is not known: VGPRs from the held data plus a fixed
+// overhead, 512 VGPRs per SIMD lane, 4 SIMDs, at most 8 waves per SIMD.
+int estimate_wgs_per_cu(const TileSpec &t, int inputs)
 {
-    const Model m = model_of(cal);
-    const Shape s = shape_of(req);
-    PathEstimate e;
-    e.legal = true;
-    e.tile = t;
-    const double units = t.kind == kKindWave ? std::ceil(s.M / 4.0) : s.M;
-    e.t_stream_us = stream_us(m, cal.device, s.bytes_io, units, wgs_per_cu(t, s.inputs));
-    e.us = m.launch_us + e.t_stream_us * eff_of(cal.single_eff, req.op, req.dt);
-    return e;
+    const int waves = t.kind == kKindWave ? 4 : std::max(1, t.block / 64);
+    const int data_vgprs = inputs * ((t.kind == kKindReread) ? t.items * t.vb / 4 * 2 : t.items * t.vb / 4);
+    const int vgprs = (data_vgprs + 32 + 7) / 8 * 8;
+    const int waves_per_simd = std::min(8, 512 / vgprs);
+    return std::max(1, (4 * waves_per_simd) / waves);
 }
 
-// The reread is served on chip when the rows in flight on one XCD fit its L2,
-// from the Infinity Cache when all rows in flight fit it (counted as half an
-// HBM read), else from HBM.
-PathEstimate estimate_reread(const PlanRequest &req, const Calibration &cal, const TileSpec &t)
+int kind_of(int path, const TileSpec &t)
 {
-    const Model m = model_of(cal);
-    const DeviceModel &d = cal.device;
-    const Shape s = shape_of(req);
-    PathEstimate e;
-    e.legal = true;
-    e.tile = t;
-    const double resident = std::min(s.M, static_cast<double>(d.cus) * wgs_per_cu(t, s.inputs));
-    const double per_xcd = resident / d.xcds;
-    double miss;
-    if (per_xcd * s.row_bytes <= d.l2_bytes_per_xcd)
-        miss = 1.0 - m.hit_l2;
-    else if (resident * s.row_bytes <= d.mall_bytes)
-        miss = 0.5;
-    else
-        miss = 1.0;
-    const double bytes3 = s.bytes_io + s.M * s.N * s.b_in * miss;
-    e.t_stream_us = stream_us(m, d, bytes3, s.M, wgs_per_cu(t, s.inputs));
-    e.us = m.launch_us + e.t_stream_us * eff_of(cal.reread_eff, req.op, req.dt);
-    return e;
-}
-
-// Path 2 at split P against the non-split baseline `base` (path 1 if legal,
-// else path 3): the row streams once over M*P workgroups and pays one exchange
-// round per row wave (Eq. 8); Eq. 7 prices the avoided reread.
-PathEstimate estimate_split(const PlanRequest &req, const Calibration &cal, int P, const TileSpec &t,
-                            const PathEstimate &base, bool base_is_single)
-{
-    const Model m = model_of(cal);
-    const DeviceModel &d = cal.device;
-    const Shape s = shape_of(req);
-    // bytes/element of the baseline schedule
-    const double b_base = base_is_single ? s.b_in + s.b_out : 2.0 * s.b_in + s.b_out;
-    const double b_reread = base_is_single ? 0.0 : s.b_in;
-    PathEstimate e;
-    e.legal = true;
-    e.split_p = P;
-    e.tile = t;
-    const double clusters = std::max(1.0, std::floor(static_cast<double>(d.cus) * wgs_per_cu(t, s.inputs) / P));
-    e.waves = std::ceil(s.M / clusters);
-    e.t_stream_us = stream_us(m, d, s.bytes_io, s.M * P, wgs_per_cu(t, s.inputs));
-    e.t_ctrl_us = e.waves * m.exchange_us;
-    e.t_save_us = (b_reread / b_base) * base.us;  // Eq. 7
-    e.us = m.launch_us + e.t_stream_us * eff_of(cal.split_eff, req.op, req.dt) + e.t_ctrl_us;
-    return e;
+    if (path == kPathSplit)
+        return kKindSplit;
+    if (path == kPathReread)
+        return kKindReread;
+    return t.block == 64 ? kKindWave : kKindWg;
 }
 
 }  // namespace
+
+int occupancy_of(const PlanRequest &req, const Calibration &cal, int path, const TileSpec &t)
+{
+    OccKey k;
+    k.op = req.op;
+    k.dt = req.dt;
+    k.kind = kind_of(path, t);
+    k.block = t.block;
+    k.items = t.items;
+    k.vb = t.vb;
+    k.part = path == kPathReread ? 0 : held_row_kind(req.op, req.dt, req.cols);
+    if (cal.occ_query) {
+        const int o = cal.occ_query(k);
+        if (o > 0)
+            return o;
+    }
+    auto it = cal.occupancy.find(k.tuple());
+    if (it != cal.occupancy.end() && it->second > 0)
+        return it->second;
+    TileSpec u = t;
+    u.kind = k.kind;
+    return estimate_wgs_per_cu(u, op_inputs(req.op));
+}
+
+double stream_time_us(const PlanRequest &req, const Calibration &cal, int path, const TileSpec &t,
+                      int wgs_per_cu_mode)
+{
+    const ModelConsts &m = cal.model;
+    const DeviceModel &d = cal.device;
+    const Shape s = shape_of(req);
+    const double cus = d.cus;
+    const double bw = (cal.peak_bandwidth ? d.hbm_peak_gbs : m.bw_gbs) * 1e3;  // bytes per us
+    const double occ = occupancy_of(req, cal, path, t);
+    const bool wave = path == kPathSingle && t.block == 64;
+    const double own_per_wg = wave ? 4.0 : 1.0;  // a wave-per-row workgroup holds four rows
+    const double slots = occ * cus * own_per_wg;  // rows resident at once
+    const double extra = path == kPathReread ? s.N * s.b_in * m.miss3 : 0.0;
+    const bool persistent = path == kPathSingle && wgs_per_cu_mode == 0;
+    const double n_conc = std::min(s.M, slots);
+    const double cus_active = std::max(1.0, std::min(cus, std::ceil(n_conc / (occ * own_per_wg))));
+    double own_in = s.N * s.b_in;
+    if (path == kPathReread)  // the reread kernel holds one streamed chunk per input
+        own_in = std::min(own_in, static_cast<double>(t.block) * t.items * t.vb * s.inputs);
+    const double inflight_cu = n_conc / cus_active * own_in;
+    const double bw_eff = std::max(1.0, std::min(bw, cus_active * inflight_cu / m.lat_us));
+    const double eta = (path == kPathReread ? m.eta3 : 1.0) * (persistent ? m.persist : 1.0);
+    const double per = (s.row_bytes + extra) * eta;
+    const double t_min = m.l0_us + m.item_us * t.items + (path == kPathReread ? m.own3_us : 0.0) +
+                         (s.row_bytes + extra) / (m.owner_gbs * 1e3);
+    if (persistent) {
+        const double iters = std::ceil(s.M / std::max(1.0, n_conc));
+        return m.launch_us + iters * std::max(n_conc * per / bw_eff, t_min);
+    }
+    const double rounds = std::ceil(s.M / slots);
+    const double last = s.M - (rounds - 1.0) * slots;
+    const double t_full = std::max(slots * per / bw_eff, t_min);
+    const double t_last = std::max(last * per / bw_eff, t_min);
+    return m.launch_us + (rounds - 1.0) * t_full + t_last;
+}
+
+SplitTerms split_terms(const PlanRequest &req, const Calibration &cal, int P, const TileSpec &t, int base_path,
+                       const TileSpec &base_tile, double t_base_us)
+{
+    const ModelConsts &m = cal.model;
+    const DeviceModel &d = cal.device;
+    const Shape s = shape_of(req);
+    SplitTerms r;
+    r.t_base_us = t_base_us;
+    // bytes per element the baseline schedule moves, and its reread (Eq. 4)
+    r.b_reread = base_path == kPathReread ? s.b_in : 0.0;
+    r.b_base = s.b_in + s.b_out + r.b_reread;
+    r.t_save_us = r.b_reread / r.b_base * t_base_us;  // Eq. 7
+    // the fraction of the CUs each schedule gives work (workgroups are spread
+    // over the CUs before any CU takes a second one)
+    auto busy = [&](double wgs) { return std::min(1.0, wgs / d.cus); };
+    const double u_base = busy(base_path == kPathSingle && base_tile.block == 64 ? std::ceil(s.M / 4.0) : s.M);
+    const double u_split = busy(s.M * P);
+    r.t_occ_us = (t_base_us - r.t_save_us) * std::max(0.0, 1.0 - u_base / u_split);
+    // Eq. 8: sequential row waves of the persistent clusters, each one exchange
+    r.resident = static_cast<double>(occupancy_of(req, cal, kPathSplit, t)) * d.cus;
+    const double clusters = std::max(1.0, std::min(std::floor(r.resident / P), s.M));
+    r.waves = std::ceil(s.M / clusters);
+    r.t_ctrl_us = r.waves * m.exch_us + m.split_launch_us;
+    // remote words: each workgroup publishes q words that P - 1 peers read;
+    // the P workgroups do so at once, so the elapsed cost is not P times one
+    // workgroup's (Eq. 8)
+    r.t_dsm_us = kExchangeWordBytes * r.waves * (P - 1) * stats_per_partial(req.op) / (m.word_gbs * 1e3);
+    r.delta_us = r.t_save_us + r.t_occ_us - r.t_ctrl_us - r.t_dsm_us;  // Eq. 9 (T_replay = T_deposit = 0)
+    r.t_split_us = t_base_us - r.delta_us;
+    return r;
+}
 
 double calib_time_us(const CalibEntry &e, double rows)
 {
@@ -504,32 +519,59 @@ bool make_plan(const PlanRequest &req, const Calibration &cal, int forced_path, 
         return true;
     if (!cal.table.empty() && plan_from_neighbours(req, cal, forced_path, forced_p, out))
         return true;
+    // The analytic model.  The non-split baseline is path 1 when a tile holds
+    // the row (a held row is never reread: path 3 moves b_in more bytes per
+    // element at the same rate), else path 3; each split width P is priced
+    // against it by Eq. 7-9 (split_terms) and the fastest prediction wins.
     Plan p;
-    TileSpec t;
-    if (single_tile(req.op, req.dt, req.cols, &t))
-        p.est[0] = estimate_single(req, cal, t);
-    p.est[2] = estimate_reread(req, cal, reread_tile(req.dt, req.cols));
+    TileSpec t1;
+    if (single_tile(req.op, req.dt, req.cols, &t1)) {
+        PathEstimate &e = p.est[0];
+        e.legal = true;
+        e.tile = t1;
+        e.us = stream_time_us(req, cal, kPathSingle, t1, -1);
+    }
+    {
+        PathEstimate &e = p.est[2];
+        for (TileSpec t : tiles_for(kKindReread, vec_bytes_for(req.dt, req.cols) == 16)) {
+            t.kind = kKindReread;
+            t.vb = vec_bytes_for(req.dt, req.cols);
+            const double us = stream_time_us(req, cal, kPathReread, t, 0);
+            if (!e.legal || us < e.us) {
+                e.legal = true;
+                e.tile = t;
+                e.us = us;
+            }
+        }
+    }
     const bool single_legal = p.est[0].legal;
-    const PathEstimate &base = single_legal ? p.est[0] : p.est[2];
+    const int base_path = single_legal ? kPathSingle : kPathReread;
+    const PathEstimate &base = p.est[base_path - 1];
     for (int P : {2, 4, 8}) {
         if (forced_p != 0 && P != forced_p)
             continue;
+        TileSpec t;
         if (!split_tile(req.op, req.dt, req.cols, P, &t))
             continue;
-        const PathEstimate e = estimate_split(req, cal, P, t, base, single_legal);
+        const SplitTerms st = split_terms(req, cal, P, t, base_path, base.tile, base.us);
+        PathEstimate e;
+        e.legal = true;
+        e.split_p = P;
+        e.tile = t;
+        e.us = st.t_split_us;
+        e.t_save_us = st.t_save_us;
+        e.t_occ_us = st.t_occ_us;
+        e.t_ctrl_us = st.t_ctrl_us;
+        e.t_dsm_us = st.t_dsm_us;
+        e.delta_us = st.delta_us;
+        e.waves = st.waves;
         if (!p.est[1].legal || e.us < p.est[1].us)
             p.est[1] = e;
     }
 
     int path = forced_path;
-    if (path == kPathAuto) {
-        double best = -1.0;
-        for (int i = 0; i < 3; ++i)
-            if (p.est[i].legal && (best < 0 || p.est[i].us < best)) {
-                best = p.est[i].us;
-                path = i + 1;
-            }
-    }
+    if (path == kPathAuto)
+        path = p.est[1].legal && p.est[1].delta_us > 0.0 ? kPathSplit : base_path;
     if (path < 1 || path > 3 || !p.est[path - 1].legal)
         return false;
     p.path = path;
@@ -538,6 +580,19 @@ bool make_plan(const PlanRequest &req, const Calibration &cal, int forced_path, 
     p.wgs_per_cu = path == kPathSingle ? -1 : 0;
     p.tile = p.est[path - 1].tile;
     *out = p;
+    return true;
+}
+
+bool analytic_baseline(const PlanRequest &req, const Calibration &cal, int *path, TileSpec *tile, double *us)
+{
+    Calibration c = cal;
+    c.table.clear();
+    Plan p;
+    if (!make_plan(req, c, kPathAuto, 0, &p))
+        return false;
+    *path = p.est[0].legal ? kPathSingle : kPathReread;
+    *tile = p.est[*path - 1].tile;
+    *us = p.est[*path - 1].us;
     return true;
 }
 
@@ -568,30 +623,34 @@ void enumerate_candidates(const PlanRequest &req, const Calibration &cal, std::v
     const int64_t nv = held_vectors(req.op, req.dt, req.cols);
     const int rvb = vec_bytes_for(req.dt, req.cols);
     const std::vector<TileSpec> held = single_ladder(req.op, vb);
-    PathEstimate best1;
     for (int kind : {kKindWave, kKindWg})
         for (TileSpec t : tiles_for(kind, v16)) {
             if (!tile_enabled(req.op, kind, t.block, t.items, vb) || !worth_holding(held, t, nv))
                 continue;
             t.vb = vb;
-            const PathEstimate e = estimate_single(req, cal, t);
-            out->push_back(Candidate{kPathSingle, 1, e, 0});
-            out->push_back(Candidate{kPathSingle, 1, e, -1});
-            if (!best1.legal || e.us < best1.us)
-                best1 = e;
+            for (int mode : {0, -1}) {
+                PathEstimate e;
+                e.legal = true;
+                e.tile = t;
+                e.us = stream_time_us(req, cal, kPathSingle, t, mode);
+                out->push_back(Candidate{kPathSingle, 1, e, mode});
+            }
         }
-    PathEstimate best3;
     for (TileSpec t : tiles_for(kKindReread, rvb == 16)) {
         t.vb = rvb;
-        const PathEstimate e = estimate_reread(req, cal, t);
+        PathEstimate e;
+        e.legal = true;
+        e.tile = t;
+        e.us = stream_time_us(req, cal, kPathReread, t, 0);
         out->push_back(Candidate{kPathReread, 1, e, 0});
-        if (!best3.legal || e.us < best3.us)
-            best3 = e;
     }
-    const PathEstimate &base = best1.legal ? best1 : best3;
+    int base_path = 0;
+    TileSpec base_tile;
+    double base_us = 0.0;
+    const bool have_base = analytic_baseline(req, cal, &base_path, &base_tile, &base_us);
     for (int P : {2, 4, 8}) {
         const int64_t per = (nv + P - 1) / P;
-        if (per * (P - 1) >= nv)
+        if (per * (P - 1) >= nv || !have_base)
             continue;
         std::vector<TileSpec> ladder;
         for (const TileSpec &u : tiles_for(kKindSplit, v16))
@@ -601,7 +660,19 @@ void enumerate_candidates(const PlanRequest &req, const Calibration &cal, std::v
             if (!worth_holding(ladder, t, per))
                 continue;
             t.vb = vb;
-            out->push_back(Candidate{kPathSplit, P, estimate_split(req, cal, P, t, base, best1.legal), 0});
+            const SplitTerms st = split_terms(req, cal, P, t, base_path, base_tile, base_us);
+            PathEstimate e;
+            e.legal = true;
+            e.split_p = P;
+            e.tile = t;
+            e.us = st.t_split_us;
+            e.t_save_us = st.t_save_us;
+            e.t_occ_us = st.t_occ_us;
+            e.t_ctrl_us = st.t_ctrl_us;
+            e.t_dsm_us = st.t_dsm_us;
+            e.delta_us = st.delta_us;
+            e.waves = st.waves;
+            out->push_back(Candidate{kPathSplit, P, e, 0});
         }
     }
 }
@@ -758,21 +829,48 @@ bool parse_calibration(const std::string &text, Calibration *out)
     };
     if (r.nums.find("version") == r.nums.end())
         return false;
-    get("stream_gbs", &c.stream_gbs);
-    get("per_cu_gbs", &c.per_cu_gbs);
-    get("launch_us", &c.launch_us);
-    get("exchange_us", &c.exchange_us);
-    get("reread_hit_l2", &c.reread_hit_l2);
     double peak = 0.0;
     get("model_peak_bandwidth", &peak);
     c.peak_bandwidth = peak != 0.0;
-    const char *effs[3] = {"single_eff", "reread_eff", "split_eff"};
-    double(*dst[3])[kNumOps][2] = {&c.single_eff, &c.reread_eff, &c.split_eff};
-    for (int k = 0; k < 3; ++k)
-        for (int op = 0; op < kNumOps; ++op)
-            for (int dt = 0; dt < 2; ++dt)
-                get((std::string(effs[k]) + "[" + std::to_string(op) + "][" + std::to_string(dt) + "]").c_str(),
-                    &(*dst[k])[op][dt]);
+    // the analytic model's constants (model_fit.py); the control kernel's
+    // measured exchange cost per row wave (ctrlbench.py) is Eq. 8's T_ctrl
+    // per wave when the file has no fitted one
+    get("exchange_us", &c.model.exch_us);
+    ModelConsts &m = c.model;
+    const std::pair<const char *, double *> consts[] = {
+        {"model.bw_gbs", &m.bw_gbs},       {"model.lat_us", &m.lat_us},
+        {"model.miss3", &m.miss3},         {"model.l0_us", &m.l0_us},
+        {"model.item_us", &m.item_us},     {"model.own3_us", &m.own3_us},
+        {"model.launch_us", &m.launch_us}, {"model.exch_us", &m.exch_us},
+        {"model.split_launch_us", &m.split_launch_us}, {"model.eta3", &m.eta3},
+        {"model.persist", &m.persist},     {"model.owner_gbs", &m.owner_gbs},
+        {"model.word_gbs", &m.word_gbs}};
+    for (const auto &kv : consts)
+        get(kv.first, kv.second);
+    if (!(m.bw_gbs > 0) || !(m.lat_us > 0) || !(m.word_gbs > 0) || !(m.owner_gbs > 0) || m.miss3 < 0 || m.eta3 <= 0 || m.persist <= 0)
+        return false;
+    // occupancy[i] = [op, dt, kind, block, items, vec_bytes, row kind, workgroups per CU]
+    for (int i = 0;; ++i) {
+        const std::string pre = "occupancy[" + std::to_string(i) + "]";
+        std::array<int, 7> key;
+        double v = 0.0;
+        auto it = r.nums.find(pre + "[0]");
+        if (it == r.nums.end())
+            break;
+        for (int j = 0; j < 7; ++j) {
+            auto jt = r.nums.find(pre + "[" + std::to_string(j) + "]");
+            if (jt == r.nums.end())
+                return false;
+            key[j] = static_cast<int>(jt->second);
+        }
+        auto vt = r.nums.find(pre + "[7]");
+        if (vt == r.nums.end())
+            return false;
+        v = vt->second;
+        if (v < 1 || v > 64)
+            return false;
+        c.occupancy[key] = static_cast<int>(v);
+    }
     // table[i] = [op, dt, cols, path, split_p, block, items, vec_bytes, wgs_per_cu, n,
     //             rows_1, us_1, ..., rows_n, us_n]
     for (int i = 0;; ++i) {

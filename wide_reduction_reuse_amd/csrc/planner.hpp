@@ -9,11 +9,16 @@
 // prices the avoided reread at the bandwidth the baseline actually achieves,
 // T_save = (b_reread / b_B) * T_B; Eq. 8 counts sequential cluster waves
 // W = ceil(M / floor(S / P)) and the replay and exchange times; Eq. 9 takes
-// dT = T_save - T_ctrl - T_replay - T_deposit - T_DSM.
+// dT = T_save - T_ctrl - T_replay - T_deposit - T_DSM, plus, on gfx950, the
+// time a baseline that leaves CUs idle gives back when its rows are split
+// over them (T_occ).
 #pragma once
 
 #include <stdint.h>
 
+#include <array>
+#include <functional>
+#include <map>
 #include <string>
 #include <vector>
 
@@ -56,23 +61,47 @@ struct CalibEntry {
 // log time) between its measurements and extrapolated along the end segments.
 double calib_time_us(const CalibEntry &e, double rows);
 
-// Measured quantities (from the calibration file); negative = not measured.
+// Constants of the analytic model (fitted to exhaustive timings of
+// calibration shapes by model_fit.py; these defaults are MI355X's).
+struct ModelConsts {
+    double bw_gbs = 4946.9724;     // rate the kernels stream at with enough bytes in flight
+    double lat_us = 0.6641;        // a CU's bytes in flight / lat_us = the rate it can sustain
+    double owner_gbs = 40.6333;    // the most one owner streams: its row's bytes / owner_gbs bound its time
+    double miss3 = 0.2220;         // fraction of path 3's second read served from HBM
+    double l0_us = 2.3188;         // least time of one owner's row: a fixed part
+    double item_us = 0.2012;       // ... and a part per vector each thread holds or streams
+    double own3_us = 1.4955;       // ... and, for a reread owner, its second pass
+    double launch_us = 3.4682;     // one launch
+    double exch_us = 3.7193;       // one split-row exchange per row wave (Eq. 8's control cost)
+    double split_launch_us = 4.0496; // a split launch's control cost beyond its row waves
+    double eta3 = 1.4065;          // bytes multiplier of reread launches (their streaming efficiency)
+    double persist = 1.0106;       // ... of persistent owners on path 1
+    double word_gbs = 10.0;        // exchange-word rate of one workgroup (T_DSM)
+};
+
+// A compiled kernel, for its occupancy: credit_op_t, credit_dtype_t,
+// KernelKind, threads, vectors per thread, bytes per access, row kind
+// (held_row_kind; 0 for the reread path).
+struct OccKey {
+    int op = 0, dt = 0, kind = 0, block = 0, items = 0, vb = 0, part = 0;
+    std::array<int, 7> tuple() const { return {op, dt, kind, block, items, vb, part}; }
+};
+
+// What the planner knows beyond the tile ladders (from a calibration file,
+// else defaults).
 struct Calibration {
     bool loaded = false;
-    double stream_gbs = -1.0;       // achieved read+write streaming bandwidth (copy kernel)
-    double per_cu_gbs = -1.0;       // bandwidth one busy CU sustains
-    double launch_us = -1.0;        // fixed cost of a launch (empty grid time)
-    double exchange_us = -1.0;      // one split-row exchange round (control kernel excess)
-    double reread_hit_l2 = -1.0;    // fraction of a reread served on chip when the working set fits L2
     // ablation of the paper's Table V (first row): price streaming at the
-    // device's peak HBM bandwidth instead of an achieved rate
+    // device's peak HBM bandwidth instead of the achieved rate
     bool peak_bandwidth = false;
-    // per-(op, dtype) multipliers on the streaming time, fitted to path-1 and path-3 timings
-    double single_eff[kNumOps][2] = {{-1, -1}, {-1, -1}, {-1, -1}, {-1, -1}, {-1, -1}, {-1, -1}};
-    double reread_eff[kNumOps][2] = {{-1, -1}, {-1, -1}, {-1, -1}, {-1, -1}, {-1, -1}, {-1, -1}};
-    double split_eff[kNumOps][2] = {{-1, -1}, {-1, -1}, {-1, -1}, {-1, -1}, {-1, -1}, {-1, -1}};
     DeviceModel device;
     bool has_device = false;
+    ModelConsts model;
+    // resident workgroups per CU of the compiled kernels: occ_query (set by
+    // the host library from the HIP runtime) first, then this table (from the
+    // calibration file), else an estimate from the tile's registers
+    std::function<int(const OccKey &)> occ_query;
+    std::map<std::array<int, 7>, int> occupancy;
     // measured candidates; shapes whose (op, dtype, cols) appear here are
     // planned from them, all others by the analytic model
     std::vector<CalibEntry> table;
@@ -90,12 +119,43 @@ struct PathEstimate {
     int split_p = 1;
     TileSpec tile;
     double us = -1.0;
-    // model terms, kept for reporting and tests
-    double t_stream_us = 0.0;
+    // model terms, kept for reporting and tests (path 2: split_terms)
     double t_save_us = 0.0;
+    double t_occ_us = 0.0;
     double t_ctrl_us = 0.0;
+    double t_dsm_us = 0.0;
+    double delta_us = 0.0;
     double waves = 0.0;
 };
+
+// The terms of Eq. 7-9 for splitting a shape's rows over P workgroups with
+// tile t, against the non-split baseline (base_path with base_tile, whose
+// time is t_base_us).
+struct SplitTerms {
+    double t_base_us = 0.0;  // T_B
+    double b_base = 0.0;     // bytes per element the baseline moves
+    double b_reread = 0.0;   // of which its reread (Eq. 4)
+    double t_save_us = 0.0;  // Eq. 7: (b_reread / b_B) T_B
+    double t_occ_us = 0.0;   // gfx950: (T_B - T_save)(1 - u_B / u_split), u = fraction of CUs given work
+    double resident = 0.0;   // S: split workgroups the device holds at once
+    double waves = 0.0;      // Eq. 8: W = ceil(M / floor(S / P))
+    double t_ctrl_us = 0.0;  // W exchanges and the split launch's control cost
+    double t_dsm_us = 0.0;   // s W (P - 1) q / B_w (not multiplied by P)
+    double delta_us = 0.0;   // Eq. 9: T_save + T_occ - T_ctrl - T_DSM (T_replay = T_deposit = 0)
+    double t_split_us = 0.0; // T_B - dT
+};
+
+// Resident workgroups per CU of the kernel `path` runs with tile t.
+int occupancy_of(const PlanRequest &req, const Calibration &cal, int path, const TileSpec &t);
+// Predicted time of one launch of a plan on path 1 or 3 (path 2 is priced by
+// split_terms); wgs_per_cu_mode as credit_plan_t::wgs_per_cu.
+double stream_time_us(const PlanRequest &req, const Calibration &cal, int path, const TileSpec &t,
+                      int wgs_per_cu_mode);
+SplitTerms split_terms(const PlanRequest &req, const Calibration &cal, int P, const TileSpec &t, int base_path,
+                       const TileSpec &base_tile, double t_base_us);
+// The analytic model's non-split baseline for a shape: path 1's tile when one
+// holds the row, else path 3's fastest tile; false only for bad arguments.
+bool analytic_baseline(const PlanRequest &req, const Calibration &cal, int *path, TileSpec *tile, double *us);
 
 struct Plan {
     int path = kPathSingle;

@@ -16,9 +16,10 @@ reports profitability accuracy against measurement (Sec. IV-C, Table V):
     a split is legal).
 
 Models (--model): `calibrated` (the calibration file's measured candidates,
-analytic elsewhere), `analytic` (the cost model alone, streaming priced at the
-calibration's measured copy rate), `peak` (the cost model with streaming
-priced at the device's peak HBM bandwidth: the ablation of the paper's
+analytic elsewhere), `analytic` (the cost model alone: the calibration's
+fitted constants and kernel occupancy table, none of its measured
+candidates), `peak` (the same with streaming priced at the device's peak HBM
+bandwidth: the ablation of the paper's
 Table V, first row; the paper's second ablated term, a shared-memory deposit
 serialized behind the input load, has no counterpart here because held rows
 are loaded straight into registers).
@@ -134,9 +135,10 @@ def main(argv=None) -> int:
         C.credit_load_calibration(a.calib)
     else:
         base = json.load(open(a.calib))
-        model = {"version": 2, "stream_gbs": base.get("stream_gbs", -1)}
-        if "device" in base:
-            model["device"] = base["device"]
+        model = {"version": 2}
+        for k in ("device", "model", "occupancy"):
+            if k in base:
+                model[k] = base[k]
         if a.model == "peak":
             model["model_peak_bandwidth"] = 1
         with tempfile.NamedTemporaryFile("w", suffix=".json", delete=False) as f:
