@@ -128,6 +128,10 @@ typedef struct {
                               owner looping over rows (and loading the next row while writing the
                               current one); k > 0 = at most k per CU; path 1 only: -1 = one
                               workgroup per row (four rows for block_threads 64), no looping */
+    int32_t lds_items;     /* paths 1 and 2, workgroup tiles of rows of whole 16-byte vectors: vectors
+                              per thread held in LDS beside the `items` in registers (the LDS tier; the
+                              row or slice is then at most block_threads * (items + lds_items) vectors);
+                              0 = registers only */
     double predicted_us[3];
 } credit_plan_t;
 

@@ -33,7 +33,8 @@ def _synthetic(consts):
         for p in C.credit_enumerate_plans(op, dt, rows, cols):
             d = p.as_dict()
             us = d["predicted_us"][d["path"] - 1]
-            plan = {k: d[k] for k in ("path", "split_p", "block_threads", "items", "vec_bytes", "wgs_per_cu")}
+            plan = {k: d[k] for k in ("path", "split_p", "block_threads", "items", "vec_bytes", "wgs_per_cu",
+                                      "lds_items")}
             cands.append({"plan": plan, "median_ms": us / 1e3})
         recs.append({"workload": "syn", "op": op, "dtype": dt, "rows": rows, "cols": cols, "candidates": cands})
     return recs
@@ -76,8 +77,8 @@ def test_occupancy_table_and_written_calibration_load(tmp_path):
         {"plan": {"path": 3, "split_p": 1, "block_threads": 512, "items": 4, "vec_bytes": 4, "wgs_per_cu": 0},
          "median_ms": 0.01, "occupancy": 4}]}
     occ = F.occupancy_table(C, [rec])
-    assert occ == [[0, 0, 1, 64, 16, 16, 1, 5], [0, 0, 2, 512, 4, 16, 1, 3], [0, 0, 3, 256, 2, 16, 1, 6],
-                   [0, 0, 4, 512, 4, 4, 0, 4]]
+    assert occ == [[0, 0, 1, 64, 16, 16, 1, 0, 5], [0, 0, 2, 512, 4, 16, 1, 0, 3], [0, 0, 3, 256, 2, 16, 1, 0, 6],
+                   [0, 0, 4, 512, 4, 4, 0, 0, 4]]
     src = tmp_path / "in.jsonl"
     src.write_text(json.dumps(rec) + "\n")
     out = tmp_path / "cal.json"

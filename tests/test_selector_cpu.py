@@ -196,23 +196,26 @@ def test_calibration_merges_repeated_timings_by_geometric_mean():
     table = K.build_table(records)
     assert len(table) == 1
     row = table[0]
-    assert row[:9] == [0, 0, 4096, 1, 1, 512, 2, 16, -1] and row[9] == 2
-    assert row[10] == 100 and row[11] == pytest.approx(math.sqrt(10.0 * 40.0), rel=1e-4)
-    assert row[12] == 1000 and row[13] == pytest.approx(50.0)
+    assert row[:10] == [0, 0, 4096, 1, 1, 512, 2, 0, 16, -1] and row[10] == 2
+    assert row[11] == 100 and row[12] == pytest.approx(math.sqrt(10.0 * 40.0), rel=1e-4)
+    assert row[13] == 1000 and row[14] == pytest.approx(50.0)
     assert K.unique_shapes(records) == 2
 
 
 def test_calibration_extension_keeps_base_rows_and_merges_shared_ones():
     from wide_reduction_reuse_amd import calibrate as K
-    base = [[0, 0, 4096, 1, 1, 512, 2, 16, -1, 2, 100, 10.0, 1000, 50.0],
-            [2, 1, 8192, 1, 1, 64, 16, 16, 0, 1, 64, 5.0]]
-    new = [[0, 0, 4096, 1, 1, 512, 2, 16, -1, 2, 100, 40.0, 4000, 190.0],   # same plan: 100 rows again, 4000 new
-           [0, 1, 1026, 1, 1, 256, 4, 16, -1, 1, 8192, 7.0]]              # a plan the base never measured
+    base = [[0, 0, 4096, 1, 1, 512, 2, 0, 16, -1, 2, 100, 10.0, 1000, 50.0],
+            [2, 1, 8192, 1, 1, 64, 16, 0, 16, 0, 1, 64, 5.0]]
+    new = [[0, 0, 4096, 1, 1, 512, 2, 0, 16, -1, 2, 100, 40.0, 4000, 190.0],   # same plan: 100 rows again, 4000 new
+           [0, 1, 1026, 1, 1, 256, 4, 0, 16, -1, 1, 8192, 7.0],               # a plan the base never measured
+           [0, 0, 4096, 1, 1, 512, 2, 8, 16, -1, 1, 100, 9.0]]                # the same tile with an LDS part
     t = K.merge_tables(base, new)
-    assert [r[:9] for r in t] == sorted([r[:9] for r in base] + [new[1][:9]])
-    shared = next(r for r in t if r[:3] == [0, 0, 4096])
-    assert shared[9] == 3 and shared[10] == 100 and shared[11] == pytest.approx(20.0)
-    assert shared[12:] == [1000, 50.0, 4000, 190.0]
+    assert [r[:10] for r in t] == sorted([r[:10] for r in base] + [new[1][:10], new[2][:10]])
+    shared = next(r for r in t if r[:3] == [0, 0, 4096] and r[7] == 0)
+    assert shared[10] == 3 and shared[11] == 100 and shared[12] == pytest.approx(20.0)
+    assert shared[13:] == [1000, 50.0, 4000, 190.0]
+    # version 2 rows (no LDS column) read as register tiles
+    assert K.upgrade_rows({"version": 2, "table": [base[0][:7] + base[0][8:]]}) == [base[0]]
     assert next(r for r in t if r[:3] == [2, 1, 8192]) == base[1]
     assert next(r for r in t if r[:3] == [0, 1, 1026]) == new[1]
 
@@ -222,8 +225,10 @@ def test_calibration_extension_drops_plans_the_library_no_longer_offers():
     # row of its one-element held tile is stale, its reread row and the
     # 16-byte held row are offered
     from wide_reduction_reuse_amd import calibrate as K
-    stale = [0, 1, 50257, 1, 1, 1024, 32, 2, -1, 1, 2670, 250.0]
-    held = [0, 1, 50257, 1, 1, 512, 16, 16, -1, 1, 2670, 120.0]
-    reread = [0, 1, 50257, 3, 1, 256, 8, 2, 0, 1, 2670, 320.0]
+    stale = [0, 1, 50257, 1, 1, 1024, 32, 0, 2, -1, 1, 2670, 250.0]
+    held = [0, 1, 50257, 1, 1, 512, 16, 0, 16, -1, 1, 2670, 120.0]
+    reread = [0, 1, 50257, 3, 1, 256, 8, 0, 2, 0, 1, 2670, 320.0]
     assert not K.offered(stale)
     assert K.offered(held) and K.offered(reread)
+    # an LDS part is offered only for rows of whole 16-byte vectors
+    assert not K.offered(held[:7] + [8] + held[8:])

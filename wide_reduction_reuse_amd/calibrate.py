@@ -38,6 +38,27 @@ from collections import defaultdict
 from .credit import DTYPES as DTS, OPS
 
 
+# Table rows (version 3): [op, dt, cols, path, split_p, block, items, lds,
+# vec_bytes, wgs_per_cu, n, rows_1, us_1, ...]; version 2 rows had no `lds`
+# (register tiles only).
+NKEY = 10
+
+
+def upgrade_rows(doc: dict) -> list:
+    """The table of a calibration document as version 3 rows."""
+    if doc.get("version", 2) >= 3:
+        return doc.get("table", [])
+    return [r[:7] + [0] + r[7:] for r in doc.get("table", [])]
+
+
+def upgrade_occupancy(doc: dict) -> list:
+    """The occupancy rows of a calibration document in the version 3 layout
+    [op, dt, kind, block, items, vec_bytes, row kind, lds, workgroups per CU]."""
+    if doc.get("version", 2) >= 3:
+        return doc.get("occupancy", [])
+    return [r[:7] + [0] + r[7:] for r in doc.get("occupancy", [])]
+
+
 def build_table(records):
     """One row per (op, dtype, cols, plan): the kernel time at every calibrated
     row count.  A shape timed in several sweeps (runs on different boxes)
@@ -47,7 +68,7 @@ def build_table(records):
         for c in r["candidates"]:
             p = c["plan"]
             key = (OPS[r["op"]], DTS[r["dtype"]], r["cols"], p["path"], p["split_p"], p["block_threads"],
-                   p["items"], p["vec_bytes"], p["wgs_per_cu"])
+                   p["items"], p.get("lds_items", 0), p["vec_bytes"], p["wgs_per_cu"])
             pts[key][r["rows"]].append(c["median_ms"] * 1000.0)
     table = []
     for key in sorted(pts):
@@ -61,15 +82,15 @@ def build_table(records):
 
 
 def merge_tables(base, new):
-    """Rows of `base` and `new` (build_table's format) keyed by their first nine
-    fields; a key in both gets, per row count, the geometric mean of the two
-    times, and the row counts only one of them measured as they are."""
+    """Rows of `base` and `new` (build_table's format) keyed by their first
+    NKEY fields; a key in both gets, per row count, the geometric mean of the
+    two times, and the row counts only one of them measured as they are."""
     def points(row):
-        n = row[9]
-        return {row[10 + 2 * i]: row[11 + 2 * i] for i in range(n)}
-    merged = {tuple(r[:9]): points(r) for r in base}
+        n = row[NKEY]
+        return {row[NKEY + 1 + 2 * i]: row[NKEY + 2 + 2 * i] for i in range(n)}
+    merged = {tuple(r[:NKEY]): points(r) for r in base}
     for r in new:
-        key = tuple(r[:9])
+        key = tuple(r[:NKEY])
         pts = points(r)
         if key in merged:
             old = merged[key]
@@ -91,12 +112,12 @@ def offered(row) -> bool:
     """Whether the library still enumerates the plan of a table row for its
     (op, dtype, cols), at the row's smallest calibrated row count."""
     from . import credit as C
-    op, dt, cols, path, p, block, items, vb, wpc = row[:9]
-    key = (op, dt, cols, row[10])
+    op, dt, cols, path, p, block, items, lds, vb, wpc = row[:NKEY]
+    key = (op, dt, cols, row[NKEY + 1])
     if key not in _OFFERED:
-        _OFFERED[key] = {(q.path, q.split_p, q.block_threads, q.items, q.vec_bytes)
-                         for q in C.credit_enumerate_plans(op, dt, row[10], cols)}
-    return (path, p, block, items, vb) in _OFFERED[key]
+        _OFFERED[key] = {(q.path, q.split_p, q.block_threads, q.items, q.lds_items, q.vec_bytes)
+                         for q in C.credit_enumerate_plans(op, dt, row[NKEY + 1], cols)}
+    return (path, p, block, items, lds, vb) in _OFFERED[key]
 
 
 _OFFERED = {}
@@ -121,7 +142,7 @@ def write_calibration(path: str, cal: dict) -> None:
     """The calibration file: scalars first, then one table row per line."""
     with open(path, "w") as f:
         f.write("{\n")
-        f.write(' "version": 2,\n "source": %s,\n "stream_gbs": %s,\n' % (json.dumps(cal["source"]), cal["stream_gbs"]))
+        f.write(' "version": 3,\n "source": %s,\n "stream_gbs": %s,\n' % (json.dumps(cal["source"]), cal["stream_gbs"]))
         for k in ("launch_us", "exchange_us"):
             if k in cal:
                 f.write(' "%s": %s,\n' % (k, cal[k]))
@@ -167,8 +188,10 @@ def main(argv=None) -> int:
             base = json.load(f)
         n_shapes = unique_shapes(records)
         cal = dict(base)
-        kept = [r for r in base["table"] if offered(r)]
-        if len(kept) != len(base["table"]):
+        base_rows = upgrade_rows(base)
+        cal["occupancy"] = upgrade_occupancy(base)
+        kept = [r for r in base_rows if offered(r)]
+        if len(kept) != len(base_rows):
             print("dropped %d base rows of plans no longer offered" % (len(base["table"]) - len(kept)),
                   file=sys.stderr)
         cal["table"] = merge_tables(kept, build_table(records))
@@ -185,7 +208,7 @@ def main(argv=None) -> int:
     src = "median kernel times of every legal plan on %d calibration shapes" % n_shapes
     if len(records) > n_shapes:
         src += " (%d timed records, repeats averaged)" % len(records)
-    cal = {"version": 2, "source": src,
+    cal = {"version": 3, "source": src,
            "stream_gbs": round(stream, 1), "table": build_table(records)}
     if a.ctrl:
         summ = [json.loads(l) for l in open(a.ctrl) if l.strip() and json.loads(l).get("summary")]

@@ -51,19 +51,19 @@ class CreditError(RuntimeError):
 class Plan(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("split_p", ctypes.c_int32), ("block_threads", ctypes.c_int32),
                 ("items", ctypes.c_int32), ("vec_bytes", ctypes.c_int32), ("wgs_per_cu", ctypes.c_int32),
-                ("predicted_us", ctypes.c_double * 3)]
+                ("lds_items", ctypes.c_int32), ("predicted_us", ctypes.c_double * 3)]
 
     def as_dict(self) -> dict:
         return {"path": self.path, "split_p": self.split_p, "block_threads": self.block_threads,
                 "items": self.items, "vec_bytes": self.vec_bytes, "wgs_per_cu": self.wgs_per_cu,
-                "predicted_us": [self.predicted_us[i] for i in range(3)]}
+                "lds_items": self.lds_items, "predicted_us": [self.predicted_us[i] for i in range(3)]}
 
     @classmethod
     def make(cls, path: int, split_p: int, block_threads: int, items: int, vec_bytes: int = 0,
-             wgs_per_cu: int = 0) -> "Plan":
+             wgs_per_cu: int = 0, lds_items: int = 0) -> "Plan":
         p = cls()
         p.path, p.split_p, p.block_threads, p.items, p.vec_bytes = path, split_p, block_threads, items, vec_bytes
-        p.wgs_per_cu = wgs_per_cu
+        p.wgs_per_cu, p.lds_items = wgs_per_cu, lds_items
         return p
 
 

@@ -43,11 +43,11 @@ const std::vector<KernelEntry> &registry()
     return table;
 }
 
-const KernelEntry *find_kernel(int kind, int op, int dt, int vb, int block, int items, int part = 0)
+const KernelEntry *find_kernel(int kind, int op, int dt, int vb, int block, int items, int part = 0, int lds = 0)
 {
     for (const KernelEntry &e : registry())
         if (e.kind == kind && e.op == op && e.dt == dt && e.vb == vb && e.block == block && e.items == items &&
-            e.part == part)
+            e.part == part && e.lds == lds)
             return &e;
     return nullptr;
 }
@@ -114,7 +114,7 @@ credit_status_t occupancy(const KernelEntry *k, int *out);
 // runtime; 0 when there is no such kernel or no device to ask.
 int kernel_occupancy(const OccKey &key)
 {
-    const KernelEntry *k = find_kernel(key.kind, key.op, key.dt, key.vb, key.block, key.items, key.part);
+    const KernelEntry *k = find_kernel(key.kind, key.op, key.dt, key.vb, key.block, key.items, key.part, key.lds);
     int occ = 0;
     if (k == nullptr || occupancy(k, &occ) != CREDIT_OK)
         return 0;
@@ -480,10 +480,15 @@ credit_status_t resolve_plan(int op, int dt, int64_t cols, const credit_plan_t &
     default:
         return CREDIT_ERR_INVALID_ARG;
     }
-    const KernelEntry *k = find_kernel(kind, op, dt, vb, plan.block_threads, plan.items, part);
+    if (plan.lds_items < 0)
+        return CREDIT_ERR_INVALID_ARG;
+    // the LDS tier: workgroup tiles of paths 1 and 2, rows of whole 16-byte vectors
+    if (plan.lds_items > 0 && (kind == kKindWave || kind == kKindReread || part != 0 || vb != 16))
+        return CREDIT_ERR_ILLEGAL_PATH;
+    const KernelEntry *k = find_kernel(kind, op, dt, vb, plan.block_threads, plan.items, part, plan.lds_items);
     if (k == nullptr)
         return CREDIT_ERR_UNSUPPORTED;
-    if (need > static_cast<int64_t>(plan.block_threads) * plan.items)
+    if (need > static_cast<int64_t>(plan.block_threads) * (plan.items + plan.lds_items))
         return CREDIT_ERR_ILLEGAL_PATH;
     // a row or slice is one buffer descriptor: its byte length must fit 32 bits
     if (kind != kKindReread && need * vb > INT64_C(0xFFFFFFFF))
@@ -502,6 +507,7 @@ void to_c_plan(const Plan &p, credit_plan_t *out)
     out->items = p.tile.items;
     out->vec_bytes = p.tile.vb;
     out->wgs_per_cu = p.wgs_per_cu;
+    out->lds_items = p.tile.lds;
     for (int i = 0; i < 3; ++i)
         out->predicted_us[i] = p.est[i].legal ? p.est[i].us : -1.0;
 }
@@ -518,6 +524,8 @@ credit_status_t run_plan_checked(int op, const credit_operands_t &t, int64_t row
     if (control) {
         if (kind != kKindSplit)
             return CREDIT_ERR_INVALID_ARG;
+        if (k->lds != 0)
+            return CREDIT_ERR_UNSUPPORTED;  // the control twins are register tiles
         k = find_kernel(kKindControl, op, dt, k->vb, k->block, k->items);
         if (k == nullptr)
             return CREDIT_ERR_UNSUPPORTED;
@@ -533,9 +541,9 @@ credit_status_t run_plan_checked(int op, const credit_operands_t &t, int64_t row
     a.cols = cols;
     a.eps = eps;
     if (log_enabled())
-        std::fprintf(stderr, "[credit] op=%d dt=%d rows=%lld cols=%lld path=%d p=%d block=%d items=%d vb=%d%s%s\n",
+        std::fprintf(stderr, "[credit] op=%d dt=%d rows=%lld cols=%lld path=%d p=%d block=%d items=%d lds=%d vb=%d%s%s\n",
                      op, dt, static_cast<long long>(rows), static_cast<long long>(cols), plan.path, plan.split_p,
-                     plan.block_threads, plan.items, k->vb,
+                     plan.block_threads, plan.items, plan.lds_items, k->vb,
                      k->part == 1 ? " (partial last vector)" : (k->part == 2 ? " (odd bf16 row)" : ""),
                      control ? " (control)" : "");
     if (kind == kKindSplit)
@@ -792,6 +800,7 @@ credit_status_t credit_enumerate_plans(credit_op_t op, credit_dtype_t dt, int64_
         c.items = cands[i].est.tile.items;
         c.vec_bytes = cands[i].est.tile.vb;
         c.wgs_per_cu = cands[i].wgs_per_cu;
+        c.lds_items = cands[i].est.tile.lds;
         for (int j = 0; j < 3; ++j)
             c.predicted_us[j] = j == cands[i].path - 1 ? cands[i].est.us : -1.0;
     }

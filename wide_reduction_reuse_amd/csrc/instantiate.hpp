@@ -1,6 +1,7 @@
 // Instantiates every tile of the ladders in registry.hpp for one operator and
 // storage type, plus the work-free control twin of every split tile and, for
-// the operators with them, the PART and ODD kernels of the 16-byte held tiles.
+// the operators with them, the PART and ODD kernels of the 16-byte held tiles,
+// and the LDS-tier tiles.
 #pragma once
 
 #include "kernels.hpp"
@@ -39,6 +40,11 @@ void register_op_dtype(std::vector<KernelEntry> &v)
 #define CREDIT_KO(kind, vb, block, items, ...)                                                                  \
     if constexpr (op_has_odd(OP) && DT == 1 && tile_enabled(OP, kind, block, items, vb))                          \
         v.push_back(KernelEntry{kind, OP, DT, vb, block, items, reinterpret_cast<const void *>(&__VA_ARGS__), 2})
+#define CREDIT_KL(kind, block, items, lt, ...)                                                                \
+    if constexpr (lds_tile_enabled(OP, kind, block, items))                                                        \
+        v.push_back(KernelEntry{kind, OP, DT, VB, block, items, reinterpret_cast<const void *>(&__VA_ARGS__), 0, lt})
+#define WGL(b, it, lt) CREDIT_KL(kKindWg, b, it, lt, single_wg_kernel<OP, T, VB, b, it, false, false, lt>);
+#define SPLITL(b, it, lt) CREDIT_KL(kKindSplit, b, it, lt, split_kernel<OP, T, VB, b, it, false, false, false, lt>);
 #define WAVEO(it) CREDIT_KO(kKindWave, VB, 64, it, single_wave_kernel<OP, T, VB, it, true, true>);
 #define WGO(b, it) CREDIT_KO(kKindWg, VB, b, it, single_wg_kernel<OP, T, VB, b, it, true, true>);
 #define SPLITO(b, it) CREDIT_KO(kKindSplit, VB, b, it, split_kernel<OP, T, VB, b, it, false, true, true>);
@@ -57,6 +63,8 @@ void register_op_dtype(std::vector<KernelEntry> &v)
     CREDIT_WAVE_TILES(WAVEO)
     CREDIT_WG_TILES(WGO)
     CREDIT_SPLIT_TILES(SPLITO)
+    CREDIT_WG_LDS_TILES(WGL)
+    CREDIT_SPLIT_LDS_TILES(SPLITL)
 
 #undef WAVE
 #undef WG
@@ -72,6 +80,9 @@ void register_op_dtype(std::vector<KernelEntry> &v)
 #undef WAVEO
 #undef WGO
 #undef SPLITO
+#undef WGL
+#undef SPLITL
+#undef CREDIT_KL
 #undef CREDIT_KO
 #undef CREDIT_KP
 #undef CREDIT_K

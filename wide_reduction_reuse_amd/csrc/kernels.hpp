@@ -603,6 +603,93 @@ __device__ __forceinline__ void store_row_value(const RowArgs &a, int64_t row, c
 }
 
 // ---------------------------------------------------------------------------
+// The LDS tier of a held tile.  The on-chip budget of a row owner is its
+// registers and its share of the CU's LDS (CREDIT paper, Sec. III-B, Eq. 3);
+// a tile with LT > 0 holds the first BLOCK * IT vectors of its row or slice in
+// registers, as every tile does, and up to BLOCK * LT more in LDS: thread tid
+// holds vectors BLOCK * IT + tid + j * BLOCK (j < LT) in LDS slot [j][tid].
+// Consecutive threads use consecutive 16-byte slots (no bank conflicts), and
+// a thread reads back only the slots it wrote, so the LDS part needs no
+// barrier of its own.  It is reduced with the operator's streaming partial as
+// its vectors arrive (kLdsStep at a time) and merged with the register part's
+// wave partial; its output pass reads it back from LDS and applies the
+// streaming form of the operator (apply_stream, from the same row partial).
+// ---------------------------------------------------------------------------
+constexpr int kLdsStep = 4;  // LDS-part vectors per input loaded and reduced at a time
+
+template <OpKind OP, int VB, int BLOCK, int LT>
+using LdsRow = RawVec<VB>[OpTraits<OP>::kIn][LT][BLOCK];
+
+// Load the LDS part (nl vectors from `src`, parameters `gam` of the same
+// columns) into `buf` and return its wave partial.
+template <OpKind OP, class T, int VB, int BLOCK, int LT>
+__device__ __forceinline__ typename OpTraits<OP>::Partial lds_load_reduce(LdsRow<OP, VB, BLOCK, LT> &buf,
+                                                                          const Srcs<OpTraits<OP>::kIn> &src,
+                                                                          rsrc_t gam, int64_t nl, int tid)
+{
+    using Op = OpTraits<OP>;
+    constexpr int NI = Op::kIn;
+    constexpr int U = kLdsStep;
+    static_assert(LT % U == 0, "LDS vectors per thread: a multiple of the step");
+    typename Op::Partial r = Op::stream_init();
+#pragma unroll
+    for (int j0 = 0; j0 < LT; j0 += U) {
+        RawVec<VB> v[NI][U];
+        RawVec<VB> g[U];
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                v[i][u] = buf_load<VB, kStream>(src.r[i], static_cast<uint32_t>(tid + (j0 + u) * BLOCK) * VB);
+        if constexpr (Op::kParamsInReduce)
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                g[u] = buf_load<VB, kKeep>(gam, static_cast<uint32_t>(tid + (j0 + u) * BLOCK) * VB);
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                buf[i][j0 + u][tid] = v[i][u];
+        Op::template stream_update<T, VB, U>(r, v, g, count_valid<U, BLOCK>(nl, tid + j0 * BLOCK));
+    }
+    return Op::wave_from_thread(r);
+}
+
+// Write the LDS part's output (nl vectors to `dst`; parameters `gam`, `bet`
+// of the same columns) with the streaming coefficients c.
+template <OpKind OP, class T, int VB, int BLOCK, int LT>
+__device__ __forceinline__ void lds_store(const LdsRow<OP, VB, BLOCK, LT> &buf, rsrc_t dst, rsrc_t gam, rsrc_t bet,
+                                          int tid, const Coef &c)
+{
+    using Op = OpTraits<OP>;
+    constexpr int NI = Op::kIn;
+    constexpr int VBO = out_vb<OP, T, VB>();
+#pragma unroll
+    for (int j = 0; j < LT; ++j) {
+        const uint32_t idx = static_cast<uint32_t>(tid + j * BLOCK);
+        RawVec<VB> in[NI];
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+            in[i] = buf[i][j][tid];
+        RawVec<VB> g, b;
+        if constexpr (Op::kParams >= 1)
+            g = buf_load<VB, kKeep>(gam, idx * VB);
+        if constexpr (Op::kParams >= 2)
+            b = buf_load<VB, kKeep>(bet, idx * VB);
+        buf_store<VBO, kStreamStore>(apply_vec<OP, T, VB, true>(in, g, b, c), dst, idx * VBO);
+    }
+}
+
+// The wave partial of a tile's register part merged with its LDS part's.
+template <OpKind OP>
+__device__ __forceinline__ typename OpTraits<OP>::Partial merge_tiers(const typename OpTraits<OP>::Partial &reg,
+                                                                      const typename OpTraits<OP>::Partial &lds)
+{
+    const typename OpTraits<OP>::Partial p[2] = {reg, lds};
+    return OpTraits<OP>::template merge<2>(p, 2);
+}
+
+// ---------------------------------------------------------------------------
 // Path 1a: one wavefront per row, four waves per 256-thread workgroup; wave w
 // of the grid handles rows w, w + W, w + 2W, ... (W waves in the grid).  No
 // barrier on the row: the wave reduction is the row reduction.
@@ -660,7 +747,9 @@ __global__ __launch_bounds__(kWave *kWaveRowsPerWg) void single_wave_kernel(RowA
 // Path 1b: one workgroup of BLOCK threads per row; workgroup g handles rows
 // g, g + G, g + 2G, ... (G workgroups in the grid).
 // ---------------------------------------------------------------------------
-template <OpKind OP, class T, int VB, int BLOCK, int IT, bool PART = false, bool ODD = false>
+// LT > 0: the LDS tier (lds_load_reduce); rows of whole 16-byte vectors,
+// at most BLOCK * (IT + LT) of them (the host checks).
+template <OpKind OP, class T, int VB, int BLOCK, int IT, bool PART = false, bool ODD = false, int LT = 0>
 __global__ __launch_bounds__(BLOCK) void single_wg_kernel(RowArgs a)
 {
     using Op = OpTraits<OP>;
@@ -670,22 +759,28 @@ __global__ __launch_bounds__(BLOCK) void single_wg_kernel(RowArgs a)
     constexpr int PEB = PART ? StorageTraits<T>::kBytes : 0;
     constexpr int NW = BLOCK / kWave;
     constexpr int VBO = out_vb<OP, T, VB>();
+    constexpr bool kLds = LT > 0;
     static_assert(!ODD || (PART && VB == 16 && StorageTraits<T>::kBytes == 2 && Op::kParams == 0),
                   "ODD rows: bf16, 16-byte vectors, operators without parameters");
+    static_assert(!kLds || (!PART && VB == 16), "the LDS tier holds rows of whole 16-byte vectors");
     __shared__ typename Op::Partial sh[NW];
     __shared__ RawVec<VB> lds_params[param_lds_vectors<OP, VB, IT, BLOCK, kOwnerRow>()];
+    __shared__ LdsRow<OP, VB, kLds ? BLOCK : 1, kLds ? LT : kLdsStep> lds_row;
     const int tid = threadIdx.x;
     const int pos = (tid / kWave) * kWave * IT + (tid & (kWave - 1));  // this wave's run + lane
     const int64_t nv = PART ? (a.cols + E - 1) / E : a.cols / E;
+    // vectors held in registers, and in LDS (kLds)
+    const int64_t nreg = kLds ? min(nv, static_cast<int64_t>(BLOCK) * IT) : nv;
+    const int64_t nl = nv - nreg;
     int64_t row = blockIdx.x;
     Tile<T, VB, IT> t[Op::kIn];
-    load_tile<T, VB, IT, kWave>(t, row_srcs<OP, VB, PEB, ODD>(a, row, nv, 0, nv), pos);
+    load_tile<T, VB, IT, kWave>(t, row_srcs<OP, VB, PEB, ODD>(a, row, nv, 0, nreg), pos);
     PC pc;
-    pc.init(row_span<VB, PEB>(a.gamma, 0, a.cols, nv, 0, nv), row_span<VB, PEB>(a.beta, 0, a.cols, nv, 0, nv), pos,
-            lds_params, tid, BLOCK);
+    pc.init(row_span<VB, PEB>(a.gamma, 0, a.cols, nv, 0, nreg), row_span<VB, PEB>(a.beta, 0, a.cols, nv, 0, nreg),
+            pos, lds_params, tid, BLOCK);
     if constexpr (PC::kMode == kParamLds)
         __syncthreads();
-    const int kv = count_valid<IT, kWave>(nv, pos);
+    const int kv = count_valid<IT, kWave>(nreg, pos);
     Loc loc0;
     if constexpr (PART) {
         loc0.ntail = static_cast<int>(a.cols % E);
@@ -697,14 +792,24 @@ __global__ __launch_bounds__(BLOCK) void single_wg_kernel(RowArgs a)
         OddOut oo;
         if constexpr (ODD)
             oo = odd_row<E>(loc, a.y, row, a.cols, nv, 0, nv, pos);
-        const auto wp = tile_partial<OP, T, VB, IT, BLOCK, kOwnerRow>(t, kv, pc, pos, loc);
+        typename Op::Partial lp;
+        if constexpr (kLds)
+            lp = lds_load_reduce<OP, T, VB, BLOCK, LT>(lds_row, row_srcs<OP, VB>(a, row, nv, nreg, nl),
+                                                       span<VB>(a.gamma, nreg, nl), nl, tid);
+        auto wp = tile_partial<OP, T, VB, IT, BLOCK, kOwnerRow>(t, kv, pc, pos, loc);
+        if constexpr (kLds)
+            wp = merge_tiers<OP>(wp, lp);
         const auto rp = block_combine<OP, NW>(wp, sh);
         const Coef c = Op::template finalize<T>(rp, loc, a.cols, a.eps);
         store_row_value<OP>(a, row, c, tid == 0);
-        const auto nsrc = row_srcs<OP, VB, PEB, ODD>(a, next, nv, 0, next < a.rows ? nv : 0);
+        const auto nsrc = row_srcs<OP, VB, PEB, ODD>(a, next, nv, 0, next < a.rows ? nreg : 0);
         const rsrc_t dst = ODD ? odd_span<VBO>(a.y, row, a.cols, 0, nv, true)
-                               : row_span<VBO, PEB>(a.y, row, a.cols, nv, 0, nv);
+                               : row_span<VBO, PEB>(a.y, row, a.cols, nv, 0, nreg);
         store_tile<OP, T, VB, IT, BLOCK, kOwnerRow, ODD>(t, dst, pc, pos, c, nsrc, &oo);
+        if constexpr (kLds)
+            lds_store<OP, T, VB, BLOCK, LT>(lds_row, span<VBO>(a.y, row * nv + nreg, nl), span<VB>(a.gamma, nreg, nl),
+                                            span<VB>(a.beta, nreg, nl), tid,
+                                            Op::template finalize_stream<T>(rp, a.cols, a.eps));
         load_next<OP, T, VB, IT, BLOCK, kOwnerRow>(t, nsrc, pos);
         // the next block_combine rewrites sh: every wave must have read it
         __syncthreads();
@@ -740,7 +845,10 @@ __device__ __forceinline__ void finish_split_launch(const SplitArgs &a, uint32_t
 // reductions (over zero tiles), but no access to rows, parameters or outputs
 // at all (the control launch passes null pointers for them).
 // ---------------------------------------------------------------------------
-template <OpKind OP, class T, int VB, int BLOCK, int IT, bool CONTROL, bool PART = false, bool ODD = false>
+// LT > 0: the LDS tier, as in single_wg_kernel (slices of whole 16-byte
+// vectors, at most BLOCK * (IT + LT) of them).
+template <OpKind OP, class T, int VB, int BLOCK, int IT, bool CONTROL, bool PART = false, bool ODD = false,
+          int LT = 0>
 __global__ __launch_bounds__(BLOCK) void split_kernel(SplitArgs a)
 {
     using Op = OpTraits<OP>;
@@ -752,6 +860,8 @@ __global__ __launch_bounds__(BLOCK) void split_kernel(SplitArgs a)
     static_assert(!(PART && CONTROL), "the control twin touches no row");
     static_assert(!ODD || (PART && VB == 16 && StorageTraits<T>::kBytes == 2 && Op::kParams == 0),
                   "ODD rows: bf16, 16-byte vectors, operators without parameters");
+    constexpr bool kLds = LT > 0;
+    static_assert(!kLds || (!PART && !CONTROL && VB == 16), "the LDS tier holds slices of whole 16-byte vectors");
     constexpr int NW = BLOCK / kWave;
     constexpr int Q = Op::kQ;
     constexpr int VBO = out_vb<OP, T, VB>();
@@ -759,6 +869,7 @@ __global__ __launch_bounds__(BLOCK) void split_kernel(SplitArgs a)
     __shared__ Partial peer[kMaxSplit];
     __shared__ uint32_t sh_ticket, sh_tag0, sh_unmatched;
     __shared__ RawVec<VB> lds_params[param_lds_vectors<OP, VB, IT, BLOCK, kOwnerSlice>()];
+    __shared__ LdsRow<OP, VB, kLds ? BLOCK : 1, kLds ? LT : kLdsStep> lds_row;
     const int tid = threadIdx.x;
     if (tid == 0) {
         sh_ticket = fetch_add_u32_agent(&a.ctl->ticket, 1u);
@@ -779,8 +890,11 @@ __global__ __launch_bounds__(BLOCK) void split_kernel(SplitArgs a)
     const int64_t per = (nv + P - 1) / P;
     const int64_t v0 = min(nv, per * c);
     const int64_t ns = min(nv, v0 + per) - v0;  // vectors in this slice
+    // of which held in registers, and in LDS (kLds)
+    const int64_t nreg = kLds ? min(ns, static_cast<int64_t>(BLOCK) * IT) : ns;
+    const int64_t nl = ns - nreg;
     const int pos = (tid / kWave) * kWave * IT + (tid & (kWave - 1));  // this wave's run + lane
-    const int kv = count_valid<IT, kWave>(ns, pos);
+    const int kv = count_valid<IT, kWave>(nreg, pos);
     uint64_t *cslots = scratch_slots(a.ctl) + k * 2 * P * Q;
 
     Tile<T, VB, IT> t[Op::kIn];
@@ -792,9 +906,9 @@ __global__ __launch_bounds__(BLOCK) void split_kernel(SplitArgs a)
             for (int j = 0; j < IT; ++j)
                 t[i].v[j] = RawVec<VB>{};
     } else {
-        load_tile<T, VB, IT, kWave>(t, row_srcs<OP, VB, PEB, ODD>(a.r, k, nv, v0, k < a.r.rows ? ns : 0), pos);
-        pc.init(row_span<VB, PEB>(a.r.gamma, 0, a.r.cols, nv, v0, ns), row_span<VB, PEB>(a.r.beta, 0, a.r.cols, nv, v0, ns),
-                pos, lds_params, tid, BLOCK);
+        load_tile<T, VB, IT, kWave>(t, row_srcs<OP, VB, PEB, ODD>(a.r, k, nv, v0, k < a.r.rows ? nreg : 0), pos);
+        pc.init(row_span<VB, PEB>(a.r.gamma, 0, a.r.cols, nv, v0, nreg),
+                row_span<VB, PEB>(a.r.beta, 0, a.r.cols, nv, v0, nreg), pos, lds_params, tid, BLOCK);
         if constexpr (PC::kMode == kParamLds)
             __syncthreads();
     }
@@ -817,10 +931,16 @@ __global__ __launch_bounds__(BLOCK) void split_kernel(SplitArgs a)
         OddOut oo;
         if constexpr (ODD)
             oo = odd_row<E>(loc, a.r.y, row, a.r.cols, nv, v0, ns, pos);
+        Partial lp;
+        if constexpr (kLds)
+            lp = lds_load_reduce<OP, T, VB, BLOCK, LT>(lds_row, row_srcs<OP, VB>(a.r, row, nv, v0 + nreg, nl),
+                                                       span<VB>(a.r.gamma, v0 + nreg, nl), nl, tid);
         if constexpr (CONTROL)
             wp = Op::template wave_partial<T, VB, IT>(t, kv, loc);
         else
             wp = tile_partial<OP, T, VB, IT, BLOCK, kOwnerSlice>(t, kv, pc, pos, loc);
+        if constexpr (kLds)
+            wp = merge_tiers<OP>(wp, lp);
         const Partial sp = block_combine<OP, NW>(wp, sh);
 
         // publish this slice's partial, then gather all P partials of the row.
@@ -859,10 +979,14 @@ __global__ __launch_bounds__(BLOCK) void split_kernel(SplitArgs a)
             (void)next;
         } else {
             store_row_value<OP>(a.r, row, cf, c == 0 && tid == 0);
-            const auto nsrc = row_srcs<OP, VB, PEB, ODD>(a.r, next, nv, v0, next < a.r.rows ? ns : 0);
+            const auto nsrc = row_srcs<OP, VB, PEB, ODD>(a.r, next, nv, v0, next < a.r.rows ? nreg : 0);
             const rsrc_t dst = ODD ? odd_span<VBO>(a.r.y, row, a.r.cols, v0, ns, true)
-                                   : row_span<VBO, PEB>(a.r.y, row, a.r.cols, nv, v0, ns);
+                                   : row_span<VBO, PEB>(a.r.y, row, a.r.cols, nv, v0, nreg);
             store_tile<OP, T, VB, IT, BLOCK, kOwnerSlice, ODD>(t, dst, pc, pos, cf, nsrc, &oo);
+            if constexpr (kLds)
+                lds_store<OP, T, VB, BLOCK, LT>(lds_row, span<VBO>(a.r.y, row * nv + v0 + nreg, nl),
+                                                span<VB>(a.r.gamma, v0 + nreg, nl), span<VB>(a.r.beta, v0 + nreg, nl),
+                                                tid, Op::template finalize_stream<T>(rp, a.r.cols, a.r.eps));
             load_next<OP, T, VB, IT, BLOCK, kOwnerSlice>(t, nsrc, pos);
         }
         // (no barrier needed before the next row rewrites sh or peer: every

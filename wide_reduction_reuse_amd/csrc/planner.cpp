@@ -161,13 +161,53 @@ static std::vector<TileSpec> single_ladder(int op, int vb)
     return ladder;
 }
 
+// The held tiles of an LDS ladder that `kind` compiles for `op`.
+static std::vector<TileSpec> lds_tiles(int op, int kind)
+{
+    std::vector<TileSpec> out;
+#define CREDIT_LDS_ADD(b, it, lt)                            \
+    if (lds_tile_enabled(op, kind, b, it))                   \
+        out.push_back(TileSpec{kind, b, it, 16, lt});
+    if (kind == kKindWg) {
+        CREDIT_WG_LDS_TILES(CREDIT_LDS_ADD)
+    } else if (kind == kKindSplit) {
+        CREDIT_SPLIT_LDS_TILES(CREDIT_LDS_ADD)
+    }
+#undef CREDIT_LDS_ADD
+    return out;
+}
+
+std::vector<TileSpec> lds_ladder(int op, int dt, int64_t cols, int kind)
+{
+    if (held_row_kind(op, dt, cols) != 0 || held_vec_bytes(op, dt, cols) != 16)
+        return {};
+    return lds_tiles(op, kind);
+}
+
+// The LDS-tier tile that holds `need` vectors with the fewest LDS vectors
+// per thread (then fewer registers), or false.
+static bool pick_lds_tile(const std::vector<TileSpec> &ladder, int64_t need, TileSpec *out)
+{
+    bool found = false;
+    for (const TileSpec &t : ladder) {
+        const int64_t cap = static_cast<int64_t>(t.block) * (t.items + t.lds);
+        if (cap < need)
+            continue;
+        if (!found || static_cast<int64_t>(t.block) * t.lds < static_cast<int64_t>(out->block) * out->lds) {
+            *out = t;
+            found = true;
+        }
+    }
+    return found;
+}
+
 bool single_tile(int op, int dt, int64_t cols, TileSpec *out)
 {
     const int vb = held_vec_bytes(op, dt, cols);
     const int64_t nv = held_vectors(op, dt, cols);
     const std::vector<TileSpec> ladder = single_ladder(op, vb);
     TileSpec t;
-    if (!pick_holding_tile(ladder, nv, &t))
+    if (!pick_holding_tile(ladder, nv, &t) && !pick_lds_tile(lds_ladder(op, dt, cols, kKindWg), nv, &t))
         return false;
     t.vb = vb;
     *out = t;
@@ -188,7 +228,7 @@ bool split_tile(int op, int dt, int64_t cols, int p, TileSpec *out)
         if (tile_enabled(op, kKindSplit, u.block, u.items, vb))
             ladder.push_back(u);
     TileSpec t;
-    if (!pick_holding_tile(ladder, per, &t))
+    if (!pick_holding_tile(ladder, per, &t) && !pick_lds_tile(lds_ladder(op, dt, cols, kKindSplit), per, &t))
         return false;
     t.vb = vb;
     *out = t;
@@ -211,7 +251,7 @@ TileSpec reread_tile(int dt, int64_t cols)
     return t;
 }
 
-double tile_capacity_bytes(const TileSpec &t) { return static_cast<double>(t.block) * t.items * t.vb; }
+double tile_capacity_bytes(const TileSpec &t) { return static_cast<double>(t.block) * (t.items + t.lds) * t.vb; }
 
 double onchip_budget_bytes(const DeviceModel &d) { return d.vgpr_bytes_per_cu + d.lds_bytes_per_cu; }
 
@@ -260,13 +300,17 @@ Shape shape_of(const PlanRequest &req)
 // Estimated resident workgroups per CU for a tile when the compiled
 // kernel's occupancy is not known: VGPRs from the held data plus a fixed
 // overhead, 512 VGPRs per SIMD lane, 4 SIMDs, at most 8 waves per SIMD.
-int estimate_wgs_per_cu(const TileSpec &t, int inputs)
+int estimate_wgs_per_cu(const TileSpec &t, int inputs, const DeviceModel &d)
 {
     const int waves = t.kind == kKindWave ? 4 : std::max(1, t.block / 64);
     const int data_vgprs = inputs * ((t.kind == kKindReread) ? t.items * t.vb / 4 * 2 : t.items * t.vb / 4);
     const int vgprs = (data_vgprs + 32 + 7) / 8 * 8;
     const int waves_per_simd = std::min(8, 512 / vgprs);
-    return std::max(1, (4 * waves_per_simd) / waves);
+    int wgs = std::max(1, (4 * waves_per_simd) / waves);
+    if (t.lds > 0)  // the LDS part: block * lds vectors per input
+        wgs = std::min(wgs, std::max(1, static_cast<int>(d.lds_bytes_per_cu /
+                                                         (static_cast<double>(t.block) * t.lds * t.vb * inputs))));
+    return wgs;
 }
 
 int kind_of(int path, const TileSpec &t)
@@ -290,6 +334,7 @@ int occupancy_of(const PlanRequest &req, const Calibration &cal, int path, const
     k.items = t.items;
     k.vb = t.vb;
     k.part = path == kPathReread ? 0 : held_row_kind(req.op, req.dt, req.cols);
+    k.lds = t.lds;
     if (cal.occ_query) {
         const int o = cal.occ_query(k);
         if (o > 0)
@@ -300,7 +345,7 @@ int occupancy_of(const PlanRequest &req, const Calibration &cal, int path, const
         return it->second;
     TileSpec u = t;
     u.kind = k.kind;
-    return estimate_wgs_per_cu(u, op_inputs(req.op));
+    return estimate_wgs_per_cu(u, op_inputs(req.op), cal.device);
 }
 
 double stream_time_us(const PlanRequest &req, const Calibration &cal, int path, const TileSpec &t,
@@ -326,7 +371,7 @@ double stream_time_us(const PlanRequest &req, const Calibration &cal, int path, 
     const double bw_eff = std::max(1.0, std::min(bw, cus_active * inflight_cu / m.lat_us));
     const double eta = (path == kPathReread ? m.eta3 : 1.0) * (persistent ? m.persist : 1.0);
     const double per = (s.row_bytes + extra) * eta;
-    const double t_min = m.l0_us + m.item_us * t.items + (path == kPathReread ? m.own3_us : 0.0) +
+    const double t_min = m.l0_us + m.item_us * (t.items + t.lds) + (path == kPathReread ? m.own3_us : 0.0) +
                          (s.row_bytes + extra) / (m.owner_gbs * 1e3);
     if (persistent) {
         const double iters = std::ceil(s.M / std::max(1.0, n_conc));
@@ -414,7 +459,7 @@ bool plan_from_table(const PlanRequest &req, const Calibration &cal, int forced_
             pe.legal = true;
             pe.us = us;
             pe.split_p = e.split_p;
-            pe.tile = TileSpec{0, e.block, e.items, e.vb};
+            pe.tile = TileSpec{0, e.block, e.items, e.vb, e.lds};
         }
         if (best == nullptr || us < best_us) {
             best = &e;
@@ -426,7 +471,7 @@ bool plan_from_table(const PlanRequest &req, const Calibration &cal, int forced_
     p.path = best->path;
     p.split_p = best->split_p;
     p.wgs_per_cu = best->wgs_per_cu;
-    p.tile = TileSpec{0, best->block, best->items, best->vb};
+    p.tile = TileSpec{0, best->block, best->items, best->vb, best->lds};
     *out = p;
     return true;
 }
@@ -450,6 +495,7 @@ double neighbour_time_us(const PlanRequest &req, const Calibration &cal, const C
         for (const CalibEntry &e : cal.table) {
             if (e.op != req.op || e.dt != req.dt || e.path != cd.path || e.split_p != cd.split_p ||
                 e.block != cd.est.tile.block || e.items != cd.est.tile.items || e.vb != cd.est.tile.vb ||
+                e.lds != cd.est.tile.lds ||
                 e.wgs_per_cu != cd.wgs_per_cu || e.rows.empty())
                 continue;
             if (same_kind && held && held_row_kind(e.op, e.dt, e.cols) != kind)
@@ -636,6 +682,20 @@ void enumerate_candidates(const PlanRequest &req, const Calibration &cal, std::v
                 out->push_back(Candidate{kPathSingle, 1, e, mode});
             }
         }
+    // LDS-tier tiles whose register part the row fills (otherwise the same
+    // registers alone hold it)
+    for (TileSpec t : lds_ladder(req.op, req.dt, req.cols, kKindWg)) {
+        const int64_t reg = static_cast<int64_t>(t.block) * t.items;
+        if (nv <= reg || nv > reg + static_cast<int64_t>(t.block) * t.lds)
+            continue;
+        for (int mode : {0, -1}) {
+            PathEstimate e;
+            e.legal = true;
+            e.tile = t;
+            e.us = stream_time_us(req, cal, kPathSingle, t, mode);
+            out->push_back(Candidate{kPathSingle, 1, e, mode});
+        }
+    }
     for (TileSpec t : tiles_for(kKindReread, rvb == 16)) {
         t.vb = rvb;
         PathEstimate e;
@@ -656,10 +716,18 @@ void enumerate_candidates(const PlanRequest &req, const Calibration &cal, std::v
         for (const TileSpec &u : tiles_for(kKindSplit, v16))
             if (tile_enabled(req.op, kKindSplit, u.block, u.items, vb))
                 ladder.push_back(u);
-        for (TileSpec t : ladder) {
-            if (!worth_holding(ladder, t, per))
-                continue;
-            t.vb = vb;
+        std::vector<TileSpec> tiles;
+        for (TileSpec t : ladder)
+            if (worth_holding(ladder, t, per)) {
+                t.vb = vb;
+                tiles.push_back(t);
+            }
+        for (const TileSpec &t : lds_ladder(req.op, req.dt, req.cols, kKindSplit)) {
+            const int64_t reg = static_cast<int64_t>(t.block) * t.items;
+            if (per > reg && per <= reg + static_cast<int64_t>(t.block) * t.lds)
+                tiles.push_back(t);
+        }
+        for (const TileSpec &t : tiles) {
             const SplitTerms st = split_terms(req, cal, P, t, base_path, base_tile, base_us);
             PathEstimate e;
             e.legal = true;
@@ -849,21 +917,25 @@ bool parse_calibration(const std::string &text, Calibration *out)
         get(kv.first, kv.second);
     if (!(m.bw_gbs > 0) || !(m.lat_us > 0) || !(m.word_gbs > 0) || !(m.owner_gbs > 0) || m.miss3 < 0 || m.eta3 <= 0 || m.persist <= 0)
         return false;
-    // occupancy[i] = [op, dt, kind, block, items, vec_bytes, row kind, workgroups per CU]
+    // Version 3 rows carry the LDS-tier vectors per thread (version 2 rows
+    // describe register-only tiles).
+    const bool v3 = r.nums["version"] >= 3.0;
+    const int nkey = v3 ? 8 : 7;
+    // occupancy[i] = [op, dt, kind, block, items, vec_bytes, row kind, (lds,) workgroups per CU]
     for (int i = 0;; ++i) {
         const std::string pre = "occupancy[" + std::to_string(i) + "]";
-        std::array<int, 7> key;
+        std::array<int, 8> key{};
         double v = 0.0;
         auto it = r.nums.find(pre + "[0]");
         if (it == r.nums.end())
             break;
-        for (int j = 0; j < 7; ++j) {
+        for (int j = 0; j < nkey; ++j) {
             auto jt = r.nums.find(pre + "[" + std::to_string(j) + "]");
             if (jt == r.nums.end())
                 return false;
             key[j] = static_cast<int>(jt->second);
         }
-        auto vt = r.nums.find(pre + "[7]");
+        auto vt = r.nums.find(pre + "[" + std::to_string(nkey) + "]");
         if (vt == r.nums.end())
             return false;
         v = vt->second;
@@ -871,7 +943,7 @@ bool parse_calibration(const std::string &text, Calibration *out)
             return false;
         c.occupancy[key] = static_cast<int>(v);
     }
-    // table[i] = [op, dt, cols, path, split_p, block, items, vec_bytes, wgs_per_cu, n,
+    // table[i] = [op, dt, cols, path, split_p, block, items, (lds,) vec_bytes, wgs_per_cu, n,
     //             rows_1, us_1, ..., rows_n, us_n]
     for (int i = 0;; ++i) {
         const std::string pre = "table[" + std::to_string(i) + "]";
@@ -882,12 +954,14 @@ bool parse_calibration(const std::string &text, Calibration *out)
             *v = it->second;
             return true;
         };
-        double f[10];
+        const int nfix = v3 ? 11 : 10;
+        double f[11];
         if (!at(0, &f[0]))
             break;
-        for (int j = 1; j < 10; ++j)
+        for (int j = 1; j < nfix; ++j)
             if (!at(j, &f[j]))
                 return false;
+        const int o = v3 ? 1 : 0;  // columns after `items` shift by one in version 3
         CalibEntry e;
         e.op = static_cast<int>(f[0]);
         e.dt = static_cast<int>(f[1]);
@@ -896,14 +970,16 @@ bool parse_calibration(const std::string &text, Calibration *out)
         e.split_p = static_cast<int>(f[4]);
         e.block = static_cast<int>(f[5]);
         e.items = static_cast<int>(f[6]);
-        e.vb = static_cast<int>(f[7]);
-        e.wgs_per_cu = static_cast<int>(f[8]);
-        const int n = static_cast<int>(f[9]);
-        if (!op_supported(e.op, e.dt) || e.cols < 1 || e.path < 1 || e.path > 3 || n < 1 || n > 64)
+        e.lds = v3 ? static_cast<int>(f[7]) : 0;
+        e.vb = static_cast<int>(f[7 + o]);
+        e.wgs_per_cu = static_cast<int>(f[8 + o]);
+        const int n = static_cast<int>(f[9 + o]);
+        if (!op_supported(e.op, e.dt) || e.cols < 1 || e.path < 1 || e.path > 3 || n < 1 || n > 64 || e.lds < 0 ||
+            e.lds > 64)
             return false;
         for (int j = 0; j < n; ++j) {
             double rr = 0.0, tt = 0.0;
-            if (!at(10 + 2 * j, &rr) || !at(11 + 2 * j, &tt) || !(rr >= 1.0) || !(tt > 0.0))
+            if (!at(nfix + 2 * j, &rr) || !at(nfix + 1 + 2 * j, &tt) || !(rr >= 1.0) || !(tt > 0.0))
                 return false;
             if (!e.rows.empty() && rr <= e.rows.back())
                 return false;

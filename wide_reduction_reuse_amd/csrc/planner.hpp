@@ -33,6 +33,7 @@ struct TileSpec {
     int block = 0;  // threads per row owner (64: one wave per row)
     int items = 0;  // vectors per thread (held) or per step (reread)
     int vb = 16;    // bytes per access
+    int lds = 0;    // vectors per thread held in LDS beside `items` (the LDS tier)
 };
 
 // What the planner knows about the device.  Defaults describe an MI355X.
@@ -53,7 +54,7 @@ struct DeviceModel {
 struct CalibEntry {
     int op = 0, dt = 0;
     int64_t cols = 0;
-    int path = 0, split_p = 1, block = 0, items = 0, vb = 16, wgs_per_cu = 0;
+    int path = 0, split_p = 1, block = 0, items = 0, vb = 16, wgs_per_cu = 0, lds = 0;
     std::vector<double> rows, us;
 };
 
@@ -81,10 +82,10 @@ struct ModelConsts {
 
 // A compiled kernel, for its occupancy: credit_op_t, credit_dtype_t,
 // KernelKind, threads, vectors per thread, bytes per access, row kind
-// (held_row_kind; 0 for the reread path).
+// (held_row_kind; 0 for the reread path), LDS vectors per thread.
 struct OccKey {
-    int op = 0, dt = 0, kind = 0, block = 0, items = 0, vb = 0, part = 0;
-    std::array<int, 7> tuple() const { return {op, dt, kind, block, items, vb, part}; }
+    int op = 0, dt = 0, kind = 0, block = 0, items = 0, vb = 0, part = 0, lds = 0;
+    std::array<int, 8> tuple() const { return {op, dt, kind, block, items, vb, part, lds}; }
 };
 
 // What the planner knows beyond the tile ladders (from a calibration file,
@@ -101,7 +102,7 @@ struct Calibration {
     // the host library from the HIP runtime) first, then this table (from the
     // calibration file), else an estimate from the tile's registers
     std::function<int(const OccKey &)> occ_query;
-    std::map<std::array<int, 7>, int> occupancy;
+    std::map<std::array<int, 8>, int> occupancy;
     // measured candidates; shapes whose (op, dtype, cols) appear here are
     // planned from them, all others by the analytic model
     std::vector<CalibEntry> table;
@@ -196,14 +197,20 @@ int64_t held_vectors(int op, int dt, int64_t cols);
 // Tile ladders, mirroring the compiled instantiations.
 const std::vector<TileSpec> &tiles_for(int kind, int vb_is_16);
 
-// Path 1: the tile that holds a row of `cols`, or false if none can.
+// Path 1: the tile that holds a row of `cols`, or false if none can: a
+// register tile where one holds it, else an LDS-tier tile.
 bool single_tile(int op, int dt, int64_t cols, TileSpec *out);
-// Path 2: the tile that holds a 1/p slice, or false if none can.
+// Path 2: the tile that holds a 1/p slice, or false if none can (registers
+// first, then the LDS tier, as for path 1).
 bool split_tile(int op, int dt, int64_t cols, int p, TileSpec *out);
+// The LDS-tier tiles of `kind` (kKindWg or kKindSplit) that `op` compiles;
+// empty for rows the tier does not hold (not whole 16-byte vectors).
+std::vector<TileSpec> lds_ladder(int op, int dt, int64_t cols, int kind);
 // Path 3: always possible.
 TileSpec reread_tile(int dt, int64_t cols);
 
-// Retained bytes per workgroup for a held tile (Eq. 3's S_CTA) and the budget.
+// Retained bytes per workgroup for a held tile (Eq. 3's S_CTA: registers and
+// LDS) and the budget.
 double tile_capacity_bytes(const TileSpec &t);
 double onchip_budget_bytes(const DeviceModel &d);
 

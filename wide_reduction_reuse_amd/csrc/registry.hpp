@@ -22,6 +22,9 @@ struct KernelEntry {
     // tiles), 1 a partial last vector (PART kernels), 2 odd-length bf16 rows
     // held from the 4-byte word below their start (ODD kernels)
     int part = 0;
+    // vectors per thread held in LDS beside the `items` in registers (the LDS
+    // tier of paths 1 and 2; 0 for every other kernel)
+    int lds = 0;
 };
 
 // Operators with PART kernels: their partials mask the partial vector's
@@ -87,6 +90,20 @@ constexpr bool tile_enabled(int op, int kind, int block, int items, int vb)
     if (op == 4 && held > 64)
         return false;
     return true;
+}
+
+// The LDS tier (paths 1 and 2, rows of whole 16-byte vectors):
+// X(block, items, lds) holds block * items vectors in registers and
+// block * lds more in LDS (128 KiB of the 160 KiB a workgroup may use on
+// gfx950 for one input at 1024 threads or two at 512).  Two-input operators
+// at 1024 threads have no register room beside the LDS part's staging.
+#define CREDIT_WG_LDS_TILES(X) X(512, 16, 8) X(1024, 16, 8)
+#define CREDIT_SPLIT_LDS_TILES(X) X(512, 16, 8) X(1024, 16, 8)
+
+constexpr bool lds_tile_enabled(int op, int kind, int block, int items)
+{
+    // LayerNorm at 1024 threads spilled registers with the LDS part's staging
+    return tile_enabled(op, kind, block, items, 16) && ((op_inputs(op) == 1 && op != 1) || block < 1024);
 }
 
 // Ladders for one-element accesses (rows whose byte length is not a multiple

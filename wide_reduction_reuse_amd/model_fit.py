@@ -48,19 +48,21 @@ KIND_WAVE, KIND_WG, KIND_SPLIT, KIND_REREAD = 1, 2, 3, 4
 
 
 def plan_key(p: dict) -> tuple:
-    return (p["path"], p["split_p"], p["block_threads"], p["items"], p["vec_bytes"], p["wgs_per_cu"])
+    return (p["path"], p["split_p"], p["block_threads"], p["items"], p.get("lds_items", 0), p["vec_bytes"],
+            p["wgs_per_cu"])
 
 
 def records_from_table(doc: dict) -> list:
     """One record per (op, dtype, cols, rows) that a calibration table measured,
     holding every candidate measured there (no occupancy: the table keeps none)."""
+    from wide_reduction_reuse_amd.calibrate import NKEY, upgrade_rows
     shapes = {}
-    for e in doc.get("table", []):
-        op, dt, cols, path, p, block, items, vb, wpc, n = e[:10]
-        plan = {"path": path, "split_p": p, "block_threads": block, "items": items, "vec_bytes": vb,
-                "wgs_per_cu": wpc}
+    for e in upgrade_rows(doc):
+        op, dt, cols, path, p, block, items, lds, vb, wpc, n = e[:NKEY + 1]
+        plan = {"path": path, "split_p": p, "block_threads": block, "items": items, "lds_items": lds,
+                "vec_bytes": vb, "wgs_per_cu": wpc}
         for j in range(n):
-            rows, us = e[10 + 2 * j], e[11 + 2 * j]
+            rows, us = e[NKEY + 1 + 2 * j], e[NKEY + 2 + 2 * j]
             shapes.setdefault((op, dt, cols, int(rows)), []).append({"plan": plan, "median_ms": us / 1e3})
     return [{"workload": "table_%s_%s_%dx%d" % (OPS[op], DTS[dt], rows, cols), "op": OPS[op], "dtype": DTS[dt],
              "rows": rows, "cols": cols, "candidates": c} for (op, dt, cols, rows), c in shapes.items()]
@@ -80,8 +82,8 @@ def row_kind(C, op: str, dt: str, cols: int) -> int:
 
 
 def occupancy_table(C, records) -> list:
-    """[op, dt, kind, block, items, vec_bytes, row kind, workgroups per CU] for
-    every kernel whose occupancy the records hold."""
+    """[op, dt, kind, block, items, vec_bytes, row kind, lds, workgroups per
+    CU] for every kernel whose occupancy the records hold."""
     kinds = {}
     table = {}
     for r in records:
@@ -100,7 +102,7 @@ def occupancy_table(C, records) -> list:
                     kinds[k] = row_kind(C, *k)
                 part = kinds[k]
             key = (OPS.index(r["op"]), DTS.index(r["dtype"]), kind, p["block_threads"], p["items"],
-                   p["vec_bytes"], part)
+                   p["vec_bytes"], part, p.get("lds_items", 0))
             table[key] = int(occ)
     return [list(k) + [v] for k, v in sorted(table.items())]
 
@@ -116,7 +118,7 @@ class Evaluator:
         self.device = device
 
     def load(self, consts: dict, peak: bool = False) -> None:
-        doc = {"version": 2, "model": consts, "occupancy": self.occupancy}
+        doc = {"version": 3, "model": consts, "occupancy": self.occupancy}
         if self.device:
             doc["device"] = self.device
         if peak:
@@ -217,7 +219,9 @@ def main(argv=None) -> int:
     consts = fit(C, records, occupancy, start=base.get("model"), device=base.get("device"))
     print(json.dumps(consts))
     if a.out:
-        from wide_reduction_reuse_amd.calibrate import write_calibration
+        from wide_reduction_reuse_amd.calibrate import upgrade_rows, write_calibration
+        base["table"] = upgrade_rows(base)
+        base["version"] = 3
         base["model"] = consts
         base["occupancy"] = occupancy
         base.setdefault("source", "model constants only")

@@ -41,7 +41,8 @@ DEFAULT_CALIB = os.path.join(PKG, "calib", "mi355x.json")
 
 
 def key_of(p: dict) -> tuple:
-    return (p["path"], p["split_p"], p["block_threads"], p["items"], p["vec_bytes"], p["wgs_per_cu"])
+    return (p["path"], p["split_p"], p["block_threads"], p["items"], p["vec_bytes"], p["wgs_per_cu"],
+            p.get("lds_items", 0))
 
 
 def evaluate(records, C):
@@ -135,8 +136,9 @@ def main(argv=None) -> int:
         C.credit_load_calibration(a.calib)
     else:
         base = json.load(open(a.calib))
-        model = {"version": 2}
-        for k in ("device", "model", "occupancy"):
+        from wide_reduction_reuse_amd.calibrate import upgrade_occupancy
+        model = {"version": 3, "occupancy": upgrade_occupancy(base)}
+        for k in ("device", "model"):
             if k in base:
                 model[k] = base[k]
         if a.model == "peak":

@@ -34,7 +34,8 @@ def device_inputs(w: W.Workload) -> dict:
 
 
 def plan_key(p) -> str:
-    return "p%d-P%d-%dx%d-v%d-w%d" % (p.path, p.split_p, p.block_threads, p.items, p.vec_bytes, p.wgs_per_cu)
+    key = "p%d-P%d-%dx%d-v%d-w%d" % (p.path, p.split_p, p.block_threads, p.items, p.vec_bytes, p.wgs_per_cu)
+    return key + ("-l%d" % p.lds_items if p.lds_items else "")
 
 
 def sweep_shape(w: W.Workload, steps: int, warmup: int, flush_buf) -> dict:
@@ -85,6 +86,8 @@ def points(which: str, ops=None, min_cols: int = 0, dtypes=None, odd_cols=False)
         pts += W.calibration_points_part()
     if which == "offgrid":
         pts += W.offgrid_points() + W.offgrid_points_next()
+    if which == "lds":
+        pts += W.lds_points()
     if ops:
         pts = [p for p in pts if p.op in ops]
     if dtypes:
@@ -98,7 +101,7 @@ def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--points", default="named", choices=("named", "sweep", "next", "all", "calib", "calib_next", "calib_next_more",
                                                          "calib_mid", "calib_odd", "calib_part", "calib_all",
-                                                         "offgrid"))
+                                                         "offgrid", "lds"))
     ap.add_argument("--ops", nargs="*", default=None)
     ap.add_argument("--min-cols", type=int, default=0, help="only shapes at least this wide")
     ap.add_argument("--dtypes", nargs="*", default=None, help="only these dtypes (f32, bf16)")

@@ -164,6 +164,32 @@ def offgrid_points() -> List[Workload]:
     return pts
 
 
+# Widths around the LDS tier's reach (256 MiB of input each): the widest row
+# registers alone hold on path 1, and wider ones up to what registers plus
+# 128 KiB of LDS hold (one input: 65536 -> 98304 fp32, 131072 -> 196608 bf16;
+# two inputs: 32768 -> 49152 fp32 and 65536 -> 98304 bf16).
+LDS_COLS = {("f32", 1): (49152, 65536, 81920, 98304), ("bf16", 1): (98304, 131072, 163840, 196608),
+            ("f32", 2): (32768, 40960, 49152), ("bf16", 2): (65536, 81920, 98304)}
+LDS_BYTES = 256 << 20
+
+
+def lds_points() -> List[Workload]:
+    """Every operator and dtype at the widths where the LDS tier decides
+    whether one owner can hold a row (LDS_COLS)."""
+    pts = []
+    idx = 0
+    for op in OPS:
+        for dt in DTYPES:
+            if (op, dt) not in SUPPORTED:
+                continue
+            for cols in LDS_COLS[(dt, 2 if op in ("softmax_bwd", "layernorm_bwd") else 1)]:
+                rows = LDS_BYTES // (cols * ELEM_BYTES[dt])
+                pts.append(Workload("lds%02d_%s_%s_%dx%d" % (idx, op, dt, rows, cols), op, dt, rows, cols,
+                                    seed=7000 + idx, eps=DEFAULT_EPS[op]))
+                idx += 1
+    return pts
+
+
 CALIB_BYTES = (8 << 20, 64 << 20, 512 << 20, 2048 << 20)
 CALIB_COLS = tuple(1 << k for k in range(10, 19))  # 1024 ... 262144
 
