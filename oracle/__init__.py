@@ -58,6 +58,8 @@ def _load():
         lib.oracle_round_bf16.argtypes = [_D, ctypes.POINTER(ctypes.c_uint16), _I64]
         lib.oracle_softmax_backward.argtypes = [_D, _D, _D, _I64, _I64]
         lib.oracle_layernorm_backward.argtypes = [_D, _D, _D, ctypes.c_double, _D, _I64, _I64]
+        lib.oracle_layernorm_row_stats.argtypes = [_D, ctypes.c_double, _D, _D, _I64, _I64]
+        lib.oracle_layernorm_backward_params.argtypes = [_D, _D, _D, _D, _D, _D, _I64, _I64]
         lib.oracle_quantize_int8.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_int8),
                                              ctypes.POINTER(ctypes.c_float), _I64, _I64]
         lib.oracle_softmax_backward_stats.argtypes = [_D, _D, _I64, _I64, _D, _D, _D]
@@ -251,6 +253,32 @@ def layernorm_backward(x, dy, gamma, eps: float) -> np.ndarray:
         _load().oracle_layernorm_backward(_dptr(a), _dptr(g), _dptr(gam), float(eps), _dptr(out),
                                           a.shape[0], a.shape[1])
     return out
+
+
+def layernorm_row_stats(x, eps: float):
+    """Per-row mean and 1 / sqrt(biased variance + eps) of x [rows][cols]."""
+    a = _as_f64_2d(x)
+    rows, cols = a.shape
+    mu = np.empty(rows)
+    rstd = np.empty(rows)
+    if rows:
+        _load().oracle_layernorm_row_stats(_dptr(a), float(eps), _dptr(mu), _dptr(rstd), rows, cols)
+    return mu, rstd
+
+
+def layernorm_backward_params(x, dy, eps: float):
+    """LayerNorm backward, parameter part: (dgamma, dbeta) [cols], sums over the
+    rows of dy * xhat and of dy."""
+    a = _as_f64_2d(x)
+    g = _as_f64_2d(dy)
+    rows, cols = a.shape
+    mu, rstd = layernorm_row_stats(a, eps)
+    dgam = np.zeros(cols)
+    dbet = np.zeros(cols)
+    if rows and cols:
+        _load().oracle_layernorm_backward_params(_dptr(a), _dptr(g), _dptr(mu), _dptr(rstd), _dptr(dgam),
+                                                 _dptr(dbet), rows, cols)
+    return dgam, dbet
 
 
 def quantize_int8(x):

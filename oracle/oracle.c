@@ -37,9 +37,10 @@
  *   softmax-logits backward : the gradient of softmax with respect to its
  *       logits x given the gradient dy of its output, recomputing the
  *       probabilities from x: dx_i = p_i (dy_i - sum_j dy_j p_j);
- *   LayerNorm backward      : the row part only, the gradient with respect to
- *       x of the LayerNorm above given dy, recomputing mean and variance from
- *       x (the per-column sums for gamma and beta are a separate reduction);
+ *   LayerNorm backward      : the gradient with respect to x of the
+ *       LayerNorm above given dy, recomputing mean and variance from x (the
+ *       row part), and the gradients with respect to gamma and beta, sums
+ *       over the rows (the parameter part, a separate column reduction);
  *   int8 quantization       : symmetric per-row absmax, 127 levels each side,
  *       computed in IEEE single precision because an integer code is decided
  *       by floating-point rounding (see oracle_quantize_int8).
@@ -358,6 +359,50 @@ void oracle_layernorm_backward(const double *x, const double *dy, const double *
             double xhat = (xr[i] - mu) * rstd;
             out[i] = rstd * (gamma[i] * gr[i] - mean_g - xhat * mean_gx);
         }
+    }
+}
+
+/* ---------------------------------------------------------------------------
+ * LayerNorm backward, the parameter part.  For y_ij = xhat_ij gamma_j +
+ * beta_j (row i, column j) and an upstream gradient dy, the gradients with
+ * respect to the parameter vectors are sums over the rows:
+ *   dgamma_j = sum_i dy_ij xhat_ij,    dbeta_j = sum_i dy_ij,
+ * where xhat_ij = (x_ij - mu_i) rstd_i uses row i's own mean and variance
+ * (as in the LayerNorm above: biased variance, eps inside the root).
+ * oracle_layernorm_row_stats gives mu_i and rstd_i; the sums then run over
+ * the rows in order, one column at a time (columns are independent and
+ * spread over threads).
+ * ------------------------------------------------------------------------- */
+void oracle_layernorm_row_stats(const double *x, double eps, double *mu, double *rstd, int64_t rows, int64_t cols)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        const double *xr = x + r * cols;
+        double sum = 0.0;
+        for (int64_t i = 0; i < cols; ++i)
+            sum += xr[i];
+        double m = sum / (double)cols;
+        double ss = 0.0;
+        for (int64_t i = 0; i < cols; ++i)
+            ss += (xr[i] - m) * (xr[i] - m);
+        mu[r] = m;
+        rstd[r] = 1.0 / sqrt(ss / (double)cols + eps);
+    }
+}
+
+void oracle_layernorm_backward_params(const double *x, const double *dy, const double *mu, const double *rstd,
+                                      double *dgamma, double *dbeta, int64_t rows, int64_t cols)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t j = 0; j < cols; ++j) {
+        double sg = 0.0, sb = 0.0;
+        for (int64_t r = 0; r < rows; ++r) {
+            double d = dy[r * cols + j];
+            sg += d * ((x[r * cols + j] - mu[r]) * rstd[r]);
+            sb += d;
+        }
+        dgamma[j] = sg;
+        dbeta[j] = sb;
     }
 }
 
