@@ -52,6 +52,7 @@
 #ifndef CREDIT_H
 #define CREDIT_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -77,7 +78,7 @@ typedef enum {
     CREDIT_OP_LAYERNORM = 1,
     CREDIT_OP_RMSNORM = 2,
     CREDIT_OP_SOFTMAX_BACKWARD = 3,   /* softmax-logits backward */
-    CREDIT_OP_LAYERNORM_BACKWARD = 4, /* LayerNorm backward, row part (fp32 only) */
+    CREDIT_OP_LAYERNORM_BACKWARD = 4, /* LayerNorm backward, row part */
     CREDIT_OP_QUANTIZE_INT8 = 5       /* row-wise symmetric int8 quantization */
 } credit_op_t;
 
@@ -180,13 +181,58 @@ credit_status_t credit_softmax_backward(const void *x, const void *dy, void *dx,
  * given dy, with mean and variance recomputed from x.  With
  * rstd = 1/sqrt(var + eps), xhat = (x - mean) rstd and g = gamma dy:
  *   dx_i = rstd (g_i - mean_j g_j - xhat_i mean_j (g_j xhat_j)).
- * The per-column sums for the gamma and beta gradients are not computed.
- *   x, dy, dx : [rows][cols]; gamma : [cols]; fp32 only (CREDIT_ERR_UNSUPPORTED
- *   for bf16).  eps finite, >= 0.
+ * The gradients of gamma and beta are the parameter part
+ * (credit_layernorm_backward_params).
+ *   x, dy, dx : [rows][cols]; gamma : [cols]; fp32 or bf16 (bf16 rows are held
+ *   as loaded and gamma * dy is formed in fp32 at each use, never rounded to
+ *   bf16).  eps finite, >= 0.
+ * Through credit_run_plan, a non-NULL row_out (8-byte aligned) receives the
+ * rows' statistics as credit_layernorm_backward_stats writes them.
  */
 credit_status_t credit_layernorm_backward(const void *x, const void *dy, const void *gamma, void *dx,
                                           int64_t rows, int64_t cols, float eps, credit_dtype_t dt,
                                           credit_path_t path, int32_t split_p, void *stream);
+
+/*
+ * credit_layernorm_backward that also writes each row's statistics for the
+ * parameter part: row_stats[2 i] = mean of row i, row_stats[2 i + 1] =
+ * 1 / sqrt(var_i + eps), in fp32, as the row kernel computed them (8 bytes
+ * per row: no other traffic).  row_stats : [rows][2] fp32, 8-byte aligned,
+ * caller-owned; NULL (with rows > 0) is CREDIT_ERR_INVALID_ARG.
+ */
+credit_status_t credit_layernorm_backward_stats(const void *x, const void *dy, const void *gamma, void *dx,
+                                                float *row_stats, int64_t rows, int64_t cols, float eps,
+                                                credit_dtype_t dt, credit_path_t path, int32_t split_p,
+                                                void *stream);
+
+/*
+ * LayerNorm backward, parameter part (the rest of the LayerNorm workload of
+ * Sec. IV-A): with xhat_ij = (x_ij - mean_i) rstd_i from row_stats,
+ *   dgamma_j = sum_i dy_ij xhat_ij,   dbeta_j = sum_i dy_ij.
+ * Two kernels on `stream`: workgroups sum groups of rows of a block of
+ * columns into `workspace`, then one thread per column adds the groups in
+ * order (fp32 throughout; the same result on every run).  Reads x and dy
+ * once (the row part has read them already: its registers hold the rows,
+ * with no room for per-column sums).
+ *   x, dy : [rows][cols] of dtype `dt` (fp32 or bf16; 16-byte aligned when a
+ *     row is a whole number of 16-byte vectors, else element-aligned);
+ *   row_stats : [rows][2] fp32 (credit_layernorm_backward_stats);
+ *   dgamma, dbeta : [cols] fp32, caller-owned, 4-byte aligned;
+ *   workspace : at least credit_layernorm_backward_params_workspace bytes of
+ *     device memory, 16-byte aligned, caller-owned.
+ * For rows = 0 the gradients are set to zero and x, dy, row_stats and
+ * workspace may be NULL.
+ * Errors: CREDIT_ERR_INVALID_ARG (NULL pointers, bad shape or dtype, too small
+ * a workspace), CREDIT_ERR_ALIGNMENT, CREDIT_ERR_HIP.
+ */
+credit_status_t credit_layernorm_backward_params(const void *x, const void *dy, const float *row_stats,
+                                                 float *dgamma, float *dbeta, int64_t rows, int64_t cols,
+                                                 credit_dtype_t dt, void *workspace, size_t workspace_bytes,
+                                                 void *stream);
+
+/* Bytes of workspace credit_layernorm_backward_params needs for a shape. */
+credit_status_t credit_layernorm_backward_params_workspace(int64_t rows, int64_t cols, credit_dtype_t dt,
+                                                           size_t *bytes);
 
 /*
  * Row-wise symmetric int8 quantization (the quantization workload of
@@ -209,7 +255,7 @@ credit_status_t credit_quantize_int8(const void *x, int8_t *q, float *scale, int
  * device properties once per device unless a calibration with a device
  * description is loaded.  Returns CREDIT_ERR_INVALID_ARG for a null `out` or
  * bad shape, CREDIT_ERR_UNSUPPORTED for an (op, dtype) pair with no kernels
- * (LayerNorm backward in bf16).
+ * (every operator has both dtypes in this build).
  */
 credit_status_t credit_select_path(credit_op_t op, credit_dtype_t dt, int64_t rows, int64_t cols,
                                    credit_plan_t *out);

@@ -19,9 +19,10 @@ Tolerances (stated by the workload description, read as below):
     the fp32 criterion takes tau_i = that magnitude instead of 1: softmax
     backward tau_i = phat_i (|dy_i| + sum_j |dy_j| phat_j); LayerNorm backward
     tau_i = rstd (|g_i| + mean |g| + |xhat_i| mean |g xhat|).  bf16 outputs of
-    softmax backward, whose values are mostly far below 2e-2 so that the
-    absolute rule alone would check nothing, must in addition be within one
-    bf16 ulp of r, or within 2^-8 |yhat_i| + 1e-5 tau_i of yhat.
+    the backward operators (softmax backward's values are mostly far below
+    2e-2, so that the absolute rule alone would check nothing) must in
+    addition be within one bf16 ulp of r, or within 2^-8 |yhat_i| +
+    1e-5 tau_i of yhat.
   * int8 quantization: codes and per-row scales bit-exact (both sides decide
     them in the same fp32 arithmetic).
 """

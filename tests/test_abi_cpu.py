@@ -81,7 +81,7 @@ def _q(x=A, q=B, s=S4, rows=4, cols=64, dt=0, path=0, p=0):
     (lambda: _rms(g=None), 1), (lambda: _rms(eps=-1e-6), 1), (lambda: _rms(g=MIS), 3),
     (lambda: _smb(dy=None), 1), (lambda: _smb(dx=None), 1), (lambda: _smb(dy=MIS), 3), (lambda: _smb(dt=2), 1),
     (lambda: _lnb(dy=None), 1), (lambda: _lnb(g=None), 1), (lambda: _lnb(eps=-1.0), 1),
-    (lambda: _lnb(dy=MIS), 3), (lambda: _lnb(dt=1), 2),  # LayerNorm backward: fp32 only
+    (lambda: _lnb(dy=MIS), 3), (lambda: _lnb(dt=2), 1),
     (lambda: _q(q=None), 1), (lambda: _q(s=None), 1), (lambda: _q(x=MIS), 3),
     (lambda: _q(s=ctypes.c_void_p(0x7F0000300002)), 3), (lambda: _q(cols=0), 1),
 ])
@@ -162,7 +162,8 @@ def test_misc_entry_points_validate():
     assert L.credit_control(0, 4, 64, 0, None, None, None, None) == 1
     split = C.Plan.make(C.PATH_SPLIT_ROW, 2, 256, 8, 16)
     assert L.credit_control(0, 0, 4096, 0, ctypes.byref(split), None, None, None) == 0  # rows = 0: no-op
-    assert L.credit_control(4, 4, 4096, 1, ctypes.byref(split), None, None, None) == 2  # no bf16 LN backward
+    split_lds = C.Plan.make(C.PATH_SPLIT_ROW, 2, 1024, 16, 16, lds_items=8)
+    assert L.credit_control(0, 4, 4096, 0, ctypes.byref(split_lds), None, None, None) == 2  # control twins: registers only
 
 
 def test_selector_legality_on_cpu():
@@ -178,7 +179,8 @@ def test_selector_legality_on_cpu():
     assert p.vec_bytes == 2
     assert C.lib().credit_select_path(0, 0, 1, 1, None) == 1
     assert C.lib().credit_select_path(6, 0, 1, 1, ctypes.byref(C.Plan())) == 1
-    assert C.lib().credit_select_path(4, 1, 1, 1, ctypes.byref(C.Plan())) == 2  # LayerNorm backward bf16
+    assert C.lib().credit_select_path(4, 2, 1, 1, ctypes.byref(C.Plan())) == 1  # no such dtype
+    assert C.lib().credit_select_path(4, 1, 1, 1, ctypes.byref(C.Plan())) == 0  # LayerNorm backward bf16
 
 
 def test_partial_rows_are_held_as_16_byte_vectors():
@@ -277,3 +279,18 @@ def test_make_plan_matches_selector_and_honours_forced_paths():
     assert ei.value.status == 4
     assert C.lib().credit_make_plan(0, 0, 4, 64, 2, 3, ctypes.byref(C.Plan())) == 1
     assert C.lib().credit_make_plan(0, 0, 4, 64, 0, 0, None) == 1
+
+
+def test_bf16_layernorm_backward_plans():
+    # bf16 LayerNorm backward holds rows of whole 16-byte vectors as such and
+    # rows that end in a partial vector by element (its streaming-form
+    # reduction counts whole vectors)
+    C.credit_load_calibration(None)
+    try:
+        p = C.credit_plan("layernorm_bwd", "bf16", 64, 8192, "single")
+        assert p.vec_bytes == 16 and p.block_threads * p.items * 8 >= 8192
+        assert 2 * p.items * 16 <= 256 or p.block_threads < 512
+        assert C.credit_plan("layernorm_bwd", "bf16", 64, 1002, "single").vec_bytes == 2
+        assert C.credit_plan("layernorm_bwd", "f32", 64, 1001, "single").vec_bytes == 16
+    finally:
+        C.credit_load_calibration(C.CALIB_PATH if os.path.exists(C.CALIB_PATH) else None)

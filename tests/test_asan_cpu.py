@@ -79,7 +79,7 @@ assert L.credit_softmax(vp(16), vp(32), 4, 16, 0, 2, 3, None) == 1
 assert L.credit_layernorm(vp(16), None, vp(16), vp(32), 4, 16, ctypes.c_float(1e-5), 0, 0, 0, None) == 1
 assert L.credit_layernorm(vp(16), vp(16), vp(16), vp(32), 4, 16, ctypes.c_float(-1.0), 0, 0, 0, None) == 1
 assert L.credit_rmsnorm(vp(16), vp(16), vp(32), 4, 16, ctypes.c_float(float("nan")), 0, 0, 0, None) == 1
-assert L.credit_layernorm_backward(vp(16), vp(16), vp(16), vp(32), 4, 16, ctypes.c_float(1e-5), 1, 0, 0, None) == 2
+assert L.credit_layernorm_backward(vp(16), vp(16), vp(16), vp(32), 4, 16, ctypes.c_float(1e-5), 2, 0, 0, None) == 1
 assert L.credit_quantize_int8(vp(16), vp(32), vp(2), 4, 16, 0, 0, 0, None) == 3
 assert L.credit_softmax(vp(16), vp(32), 0, 16, 0, 0, 0, None) == 0  # rows = 0: a no-op
 ops_t = C.Operands()
@@ -94,6 +94,13 @@ assert L.credit_copy(vp(16), vp(32), 15, None, None, None) == 1
 assert L.credit_flush(vp(8), 16, None) == 3
 assert L.credit_select_path(0, 0, 4, 16, None) == 1
 assert L.credit_enumerate_plans(0, 0, 4, 16, None, 3, None) == 1
+n = ctypes.c_size_t()
+assert L.credit_layernorm_backward_params_workspace(2048, 65536, 0, ctypes.byref(n)) == 0 and n.value > 0
+assert L.credit_layernorm_backward_params_workspace(-1, 16, 0, ctypes.byref(n)) == 1
+assert L.credit_layernorm_backward_params(None, None, None, None, None, 4, 16, 0, None, 0, None) == 1
+assert L.credit_layernorm_backward_params(vp(16), vp(16), vp(16), vp(16), vp(16), 4, 16, 0, None, 0, None) == 1
+assert L.credit_layernorm_backward_params(vp(17), vp(16), vp(16), vp(16), vp(16), 4, 16, 0, vp(16), 1 << 20, None) == 3
+assert L.credit_layernorm_backward_stats(vp(16), vp(16), vp(16), vp(32), None, 4, 16, ctypes.c_float(1e-5), 0, 0, 0, None) == 1
 assert L.credit_test_exchange(1 << 33) == 1
 assert L.credit_test_exchange(-1) == 0
 for s in range(-2, 12):

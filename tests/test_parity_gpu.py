@@ -182,9 +182,11 @@ def _tile_cases():
 TILE_CASES = _tile_cases()
 
 
-def _tile_excluded(op, kind, block, items, vb=16):
+def _tile_excluded(op, kind, block, items, vb=16, dt="f32"):
     """The tiles the kernel registry leaves out (they spilled registers): its
     rule restated, so that the library's refusals are checked against it."""
+    if op == "layernorm_bwd" and dt == "bf16" and kind != "reread" and block >= 512 and 2 * items * vb > 256:
+        return True
     if kind == "reread" or block < 1024:
         return False
     held = W.N_INPUTS.get(op, 1) * items * max(vb, 4)  # a 2-byte vector takes a 32-bit register
@@ -211,7 +213,7 @@ def test_every_tile(op, dt, kind, block, items, p, cols):
     path = {"wave": C.PATH_SINGLE_WG, "wg": C.PATH_SINGLE_WG, "split": C.PATH_SPLIT_ROW,
             "reread": C.PATH_REREAD}[kind]
     plan = C.Plan.make(path, p, block, items, 16, wgs_per_cu=1)
-    if _tile_excluded(op, kind, block, items):
+    if _tile_excluded(op, kind, block, items, dt=dt):
         with pytest.raises(C.CreditError) as ei:
             _run(inp, plan=plan)
         assert ei.value.status == 2  # CREDIT_ERR_UNSUPPORTED, refused before launch
@@ -235,7 +237,9 @@ def _partial_tile_cases():
     i = 0
     for op in PART_OPS:
         for dt in W.DTYPES:
-            if (op, dt) not in W.SUPPORTED:
+            # bf16 LayerNorm backward reduces its held rows in the streaming
+            # form and keeps one-element tiles for such rows
+            if (op, dt) not in W.SUPPORTED or (op, dt) == ("layernorm_bwd", "bf16"):
                 continue
             epv = 16 // W.ELEM_BYTES[dt]
             tails = (1, 2, 3) if dt == "f32" else (2, 4, 6)  # elements in the partial vector
@@ -273,7 +277,7 @@ def test_every_tile_partial_last_vector(op, dt, kind, block, items, p, cols):
     inp = W.generate(w)
     path = C.PATH_SPLIT_ROW if kind == "split" else C.PATH_SINGLE_WG
     plan = C.Plan.make(path, p, block, items, 16, wgs_per_cu=1)
-    if _tile_excluded(op, kind, block, items):
+    if _tile_excluded(op, kind, block, items, dt=dt):
         with pytest.raises(C.CreditError) as ei:
             _run(inp, plan=plan)
         assert ei.value.status == 2
@@ -331,7 +335,7 @@ def test_every_tile_odd_length_bf16(op, kind, block, items, p, cols):
     inp = W.generate(w)
     path = C.PATH_SPLIT_ROW if kind == "split" else C.PATH_SINGLE_WG
     plan = C.Plan.make(path, p, block, items, 16, wgs_per_cu=1)
-    if _tile_excluded(op, kind, block, items):
+    if _tile_excluded(op, kind, block, items, dt="bf16"):
         with pytest.raises(C.CreditError) as ei:
             _run(inp, plan=plan)
         assert ei.value.status == 2
@@ -419,6 +423,15 @@ def test_unaligned_row_lengths(op, dt, cols, path, p):
     C = _lib()
     w = W.custom(op, dt, 6, cols, seed=cols + 7, x_dist="scaled_shifted", x_scale=2.0, x_shift=-0.25)
     inp = W.generate(w)
+    if (op, dt) == ("layernorm_bwd", "bf16") and path in ("single", "split") and cols * 2 % 16 != 0 \
+            and cols > 4096:
+        # its one-element tiles end at 1024 x 4 (larger ones spilled
+        # registers): wider such rows are reread, and a forced held path is
+        # refused before launch
+        with pytest.raises(C.CreditError) as ei:
+            _run(inp, path, p)
+        assert ei.value.status == 4
+        return
     out = _run(inp, path, p)
     _check(inp, out, "odd %s %s cols=%d %s P=%d" % (op, dt, cols, path, p))
 
@@ -504,9 +517,17 @@ def test_paths_agree_closely(op, dt, cols):
     inp = W.generate(w)
     ys = {}
     for path, p in [("single", 0), ("split", 2), ("split", 4), ("split", 8), ("reread", 0)]:
+        if (op, dt) == ("layernorm_bwd", "bf16") and cols % 8 != 0 and path != "reread":
+            # rows ending in a partial vector: one-element tiles up to 4096
+            # elements only (see test_unaligned_row_lengths)
+            with pytest.raises(C.CreditError) as ei:
+                _run(inp, path, p)
+            assert ei.value.status == 4
+            continue
         ys[(path, p)] = _run(inp, path, p)
         _check(inp, ys[(path, p)], "agree %s %s %s P=%d" % (op, dt, path, p))
-    assert _same(ys[("single", 0)], _run(inp, "single", 0))
+    if ("single", 0) in ys:
+        assert _same(ys[("single", 0)], _run(inp, "single", 0))
 
 
 def test_rows_fewer_than_cus_and_odd_row_counts():

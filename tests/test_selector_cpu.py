@@ -118,7 +118,7 @@ def test_width_beyond_the_measured_widths_scales_at_equal_bytes(tmp_path):
     [0, 0, 4096, 1, 1, 512, 2, 16, -1, 2, 100, 10.0, 1000],         # a point is missing
     [0, 0, 4096, 1, 1, 512, 2, 16, -1, 2, 100, -1.0, 1000, 50.0],   # non-positive time
     [6, 0, 4096, 1, 1, 512, 2, 16, -1, 2, 100, 10.0, 1000, 50.0],   # no op 6
-    [4, 1, 4096, 1, 1, 512, 2, 16, -1, 2, 100, 10.0, 1000, 50.0],   # LayerNorm backward has no bf16
+    [4, 2, 4096, 1, 1, 512, 2, 16, -1, 2, 100, 10.0, 1000, 50.0],   # no dtype 2
     [0, 0, 4096, 1, 1, 512, 2, 16, -1],                             # header cut short
 ])
 def test_malformed_tables_are_refused_and_the_previous_one_stays(tmp_path, bad):

@@ -33,7 +33,8 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,
           "-I", INCLUDE, "-I", CSRC]
 
 SOURCES = ["inst_softmax.hip", "inst_layernorm.hip", "inst_rmsnorm.hip", "inst_softmax_bwd.hip",
-           "inst_layernorm_bwd.hip", "inst_quantize.hip", "inst_misc.hip", "noalloc.hip", "api.cpp", "planner.cpp"]
+           "inst_layernorm_bwd.hip", "inst_quantize.hip", "inst_misc.hip", "noalloc.hip", "lnbwd_params.hip", "api.cpp",
+           "planner.cpp"]
 
 
 # Host-side AddressSanitizer variant (libcredit_asan.so, for the CPU tests of

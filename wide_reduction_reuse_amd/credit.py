@@ -39,7 +39,9 @@ EXPORTED = ["credit_softmax", "credit_layernorm", "credit_rmsnorm", "credit_soft
             "credit_enumerate_plans", "credit_occupancy",
             "credit_run_plan", "credit_run_plan_timed", "credit_run_plan_static", "credit_control", "credit_copy",
             "credit_flush", "credit_load_calibration", "credit_check_errors", "credit_status_str", "credit_version",
-            "credit_test_exchange", "credit_test_scratch", "credit_model_terms"]
+            "credit_test_exchange", "credit_test_scratch", "credit_model_terms",
+            "credit_layernorm_backward_stats", "credit_layernorm_backward_params",
+            "credit_layernorm_backward_params_workspace"]
 
 
 class CreditError(RuntimeError):
@@ -107,6 +109,9 @@ def lib() -> ctypes.CDLL:
         "credit_rmsnorm": [vp, vp, vp, i64, i64, f32, i32, i32, i32, vp],
         "credit_softmax_backward": [vp, vp, vp, i64, i64, i32, i32, i32, vp],
         "credit_layernorm_backward": [vp, vp, vp, vp, i64, i64, f32, i32, i32, i32, vp],
+        "credit_layernorm_backward_stats": [vp, vp, vp, vp, vp, i64, i64, f32, i32, i32, i32, vp],
+        "credit_layernorm_backward_params": [vp, vp, vp, vp, vp, i64, i64, i32, vp, ctypes.c_size_t, vp],
+        "credit_layernorm_backward_params_workspace": [i64, i64, i32, ctypes.POINTER(ctypes.c_size_t)],
         "credit_quantize_int8": [vp, vp, vp, i64, i64, i32, i32, i32, vp],
         "credit_select_path": [i32, i32, i64, i64, ctypes.POINTER(Plan)],
         "credit_make_plan": [i32, i32, i64, i64, i32, i32, ctypes.POINTER(Plan)],
@@ -252,6 +257,55 @@ def credit_layernorm_backward(x, dy, gamma, eps: float, dx=None, path="auto", sp
            "credit_layernorm_backward")
     _finish(check, stream)
     return dx
+
+
+def credit_layernorm_backward_stats(x, dy, gamma, eps: float, dx=None, stats=None, path="auto", split_p: int = 0,
+                                    stream=None, check: bool = False):
+    """credit_layernorm_backward, also writing each row's (mean, rstd): returns (dx, stats [rows][2] fp32)."""
+    import torch
+    _same(x, dy, "dy")
+    dx = _out(x, dx)
+    rows, cols = _shape2d(x)
+    if stats is None:
+        stats = torch.empty((rows, 2), dtype=torch.float32, device=x.device)
+    if stats.numel() != 2 * rows or stats.dtype != torch.float32 or not stats.is_contiguous():
+        raise ValueError("stats must be a contiguous float32 tensor of two entries per row")
+    _check(lib().credit_layernorm_backward_stats(_ptr(x), _ptr(dy), _ptr(gamma), _ptr(dx), _ptr(stats), rows, cols,
+                                                 float(eps), _dtype_code(x), _path(path), split_p, _stream(stream)),
+           "credit_layernorm_backward_stats")
+    _finish(check, stream)
+    return dx, stats
+
+
+def credit_layernorm_backward_params_workspace(rows: int, cols: int, dtype) -> int:
+    n = ctypes.c_size_t()
+    dt = DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
+    _check(lib().credit_layernorm_backward_params_workspace(rows, cols, dt, ctypes.byref(n)),
+           "credit_layernorm_backward_params_workspace")
+    return n.value
+
+
+def credit_layernorm_backward_params(x, dy, stats, dgamma=None, dbeta=None, workspace=None, stream=None):
+    """Parameter part of the LayerNorm gradient: returns (dgamma, dbeta), fp32 [cols].
+    `stats` as credit_layernorm_backward_stats returns them; the workspace is
+    allocated when not given."""
+    import torch
+    _same(x, dy, "dy")
+    rows, cols = _shape2d(x)
+    if dgamma is None:
+        dgamma = torch.empty(cols, dtype=torch.float32, device=x.device)
+    if dbeta is None:
+        dbeta = torch.empty(cols, dtype=torch.float32, device=x.device)
+    for name, v in (("dgamma", dgamma), ("dbeta", dbeta)):
+        if v.numel() != cols or v.dtype != torch.float32 or not v.is_contiguous():
+            raise ValueError("%s must be a contiguous float32 tensor of cols entries" % name)
+    need = credit_layernorm_backward_params_workspace(rows, cols, _dtype_code(x))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    _check(lib().credit_layernorm_backward_params(_ptr(x), _ptr(dy), _ptr(stats), _ptr(dgamma), _ptr(dbeta), rows,
+                                                  cols, _dtype_code(x), _ptr(workspace), workspace.numel(),
+                                                  _stream(stream)), "credit_layernorm_backward_params")
+    return dgamma, dbeta
 
 
 def credit_quantize_int8(x, q=None, scale=None, path="auto", split_p: int = 0, stream=None, check: bool = False):

@@ -254,7 +254,9 @@ credit_status_t validate(int op, const credit_operands_t &t, int64_t rows, int64
         return CREDIT_ERR_INVALID_ARG;
     if (!aligned16(t.x) || !aligned16(t.y) || (uses_dy(op) && !aligned16(t.dy)) ||
         (uses_gamma(op) && !aligned16(t.gamma)) || (uses_beta(op) && !aligned16(t.beta)) ||
-        (uses_row_out(op) && !aligned4(t.row_out)))
+        (uses_row_out(op) && !aligned4(t.row_out)) ||
+        (op == CREDIT_OP_LAYERNORM_BACKWARD && t.row_out != nullptr &&
+         (reinterpret_cast<uintptr_t>(t.row_out) & 7u) != 0))
         return CREDIT_ERR_ALIGNMENT;
     return CREDIT_OK;
 }
@@ -536,7 +538,8 @@ credit_status_t run_plan_checked(int op, const credit_operands_t &t, int64_t row
     a.gamma = uses_gamma(op) ? t.gamma : nullptr;
     a.beta = uses_beta(op) ? t.beta : nullptr;
     a.y = t.y;
-    a.row_out = uses_row_out(op) ? t.row_out : nullptr;
+    // LayerNorm backward writes each row's mean and rstd when given row_out
+    a.row_out = (uses_row_out(op) || op == CREDIT_OP_LAYERNORM_BACKWARD) ? t.row_out : nullptr;
     a.rows = rows;
     a.cols = cols;
     a.eps = eps;
@@ -672,6 +675,16 @@ credit_status_t credit_layernorm_backward(const void *x, const void *dy, const v
                                           credit_path_t path, int32_t split_p, void *stream)
 {
     return run_op(CREDIT_OP_LAYERNORM_BACKWARD, operands(x, dy, gamma, nullptr, dx, nullptr), rows, cols, eps, dt,
+                  path, split_p, stream);
+}
+
+credit_status_t credit_layernorm_backward_stats(const void *x, const void *dy, const void *gamma, void *dx,
+                                                float *row_stats, int64_t rows, int64_t cols, float eps,
+                                                credit_dtype_t dt, credit_path_t path, int32_t split_p, void *stream)
+{
+    if (row_stats == nullptr && rows > 0)
+        return CREDIT_ERR_INVALID_ARG;
+    return run_op(CREDIT_OP_LAYERNORM_BACKWARD, operands(x, dy, gamma, nullptr, dx, row_stats), rows, cols, eps, dt,
                   path, split_p, stream);
 }
 

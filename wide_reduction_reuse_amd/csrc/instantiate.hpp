@@ -17,7 +17,7 @@ void register_op_dtype(std::vector<KernelEntry> &v)
     constexpr int VB = 16;
     constexpr int VS = StorageTraits<T>::kBytes;  // one-element access
 #define CREDIT_K(kind, vb, block, items, ...)                                                                  \
-    if constexpr (tile_enabled(OP, kind, block, items, vb))                                                       \
+    if constexpr (tile_enabled(OP, DT, kind, block, items, vb))                                                       \
         v.push_back(KernelEntry{kind, OP, DT, vb, block, items, reinterpret_cast<const void *>(&__VA_ARGS__)})
 #define WAVE(it) CREDIT_K(kKindWave, VB, 64, it, single_wave_kernel<OP, T, VB, it>);
 #define WG(b, it) CREDIT_K(kKindWg, VB, b, it, single_wg_kernel<OP, T, VB, b, it>);
@@ -32,16 +32,16 @@ void register_op_dtype(std::vector<KernelEntry> &v)
     CREDIT_K(kKindControl, VS, b, it, split_kernel<OP, T, VS, b, it, true>);
 #define REREAD1E(b, it) CREDIT_K(kKindReread, VS, b, it, reread_kernel<OP, T, VS, b, it>);
 #define CREDIT_KP(kind, vb, block, items, ...)                                                                  \
-    if constexpr (op_has_part(OP) && tile_enabled(OP, kind, block, items, vb))                                    \
+    if constexpr (op_has_part(OP, DT) && tile_enabled(OP, DT, kind, block, items, vb))                                    \
         v.push_back(KernelEntry{kind, OP, DT, vb, block, items, reinterpret_cast<const void *>(&__VA_ARGS__), 1})
 #define WAVEP(it) CREDIT_KP(kKindWave, VB, 64, it, single_wave_kernel<OP, T, VB, it, true>);
 #define WGP(b, it) CREDIT_KP(kKindWg, VB, b, it, single_wg_kernel<OP, T, VB, b, it, true>);
 #define SPLITP(b, it) CREDIT_KP(kKindSplit, VB, b, it, split_kernel<OP, T, VB, b, it, false, true>);
 #define CREDIT_KO(kind, vb, block, items, ...)                                                                  \
-    if constexpr (op_has_odd(OP) && DT == 1 && tile_enabled(OP, kind, block, items, vb))                          \
+    if constexpr (op_has_odd(OP) && DT == 1 && tile_enabled(OP, DT, kind, block, items, vb))                          \
         v.push_back(KernelEntry{kind, OP, DT, vb, block, items, reinterpret_cast<const void *>(&__VA_ARGS__), 2})
 #define CREDIT_KL(kind, block, items, lt, ...)                                                                \
-    if constexpr (lds_tile_enabled(OP, kind, block, items))                                                        \
+    if constexpr (lds_tile_enabled(OP, DT, kind, block, items))                                                        \
         v.push_back(KernelEntry{kind, OP, DT, VB, block, items, reinterpret_cast<const void *>(&__VA_ARGS__), 0, lt})
 #define WGL(b, it, lt) CREDIT_KL(kKindWg, b, it, lt, single_wg_kernel<OP, T, VB, b, it, false, false, lt>);
 #define SPLITL(b, it, lt) CREDIT_KL(kKindSplit, b, it, lt, split_kernel<OP, T, VB, b, it, false, false, false, lt>);

@@ -103,6 +103,24 @@ constexpr int out_params()
     return OpTraits<OP>::kParamsInReduce ? 0 : OpTraits<OP>::kParams;
 }
 
+// Held tiles that keep their inputs as loaded and use the operator's
+// streaming form (stream_update on the held vectors, apply_stream with the
+// parameters fetched at use) instead of folding the parameters into the tile:
+// bf16 LayerNorm backward, whose dy tile cannot hold g = gamma * dy in fp32
+// (rounding g to bf16 would lose what the fp32 path keeps).
+template <OpKind OP, class T>
+constexpr bool holds_raw()
+{
+    return OP == kLayerNormBwd && StorageTraits<T>::kBytes != 4;
+}
+
+// Parameter vectors a held tile's output pass applies.
+template <OpKind OP, class T>
+constexpr int held_out_params()
+{
+    return holds_raw<OP, T>() ? OpTraits<OP>::kParams : out_params<OP>();
+}
+
 // Number of k in [0, IT) with pos + k*G < n (a prefix).
 template <int IT, int G>
 __device__ __forceinline__ int count_valid(int64_t n, int pos)
@@ -308,15 +326,40 @@ __device__ __forceinline__ typename OpTraits<OP>::Partial tile_partial(
     L &loc)
 {
     using Op = OpTraits<OP>;
-    if constexpr (Op::kParamsInReduce) {
+    if constexpr (holds_raw<OP, T>()) {
+        // the streaming form over the held vectors, kLdsStep at a time, with
+        // the parameters fetched per step
+        constexpr int U = IT < 4 ? IT : 4;
+        static_assert(IT % U == 0, "held vectors per thread: a multiple of the step");
+        (void)loc;
+        typename Op::Partial r = Op::stream_init();
 #pragma unroll
-        for (int k = 0; k < IT; ++k) {
-            RawVec<VB> g, b;
-            pc.fetch(k, pos, g, b);
-            Op::template prepare<T, VB, IT>(t, k, g);
+        for (int kb = 0; kb < IT; kb += U) {
+            RawVec<VB> v[Op::kIn][U];
+            RawVec<VB> g[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                RawVec<VB> b;
+                pc.fetch(kb + u, pos, g[u], b);
+#pragma unroll
+                for (int i = 0; i < Op::kIn; ++i)
+                    v[i][u] = t[i].v[kb + u];
+            }
+            const int kvb = kv - kb;
+            Op::template stream_update<T, VB, U>(r, v, g, kvb < 0 ? 0 : (kvb > U ? U : kvb));
         }
+        return Op::wave_from_thread(r);
+    } else {
+        if constexpr (Op::kParamsInReduce) {
+#pragma unroll
+            for (int k = 0; k < IT; ++k) {
+                RawVec<VB> g, b;
+                pc.fetch(k, pos, g, b);
+                Op::template prepare<T, VB, IT>(t, k, g);
+            }
+        }
+        return Op::template wave_partial<T, VB, IT>(t, kv, loc);
     }
-    return Op::template wave_partial<T, VB, IT>(t, kv, loc);
 }
 
 // Whether the output loop loads the next row into the registers it frees
@@ -365,7 +408,8 @@ __device__ __forceinline__ void store_tile(Tile<T, VB, IT> (&t)[OpTraits<OP>::kI
 {
     using Op = OpTraits<OP>;
     constexpr int NI = Op::kIn;
-    constexpr int NP = out_params<OP>();
+    constexpr int NP = held_out_params<OP, T>();
+    constexpr bool RAW = holds_raw<OP, T>();
     constexpr int MODE = ParamCache<OP, T, VB, IT, W, OWNER>::kMode;
     constexpr int VBO = out_vb<OP, T, VB>();
     constexpr int G = kWave;  // vector stride between a thread's vectors
@@ -396,7 +440,7 @@ __device__ __forceinline__ void store_tile(Tile<T, VB, IT> (&t)[OpTraits<OP>::kI
 #pragma unroll
             for (int i = 0; i < NI; ++i)
                 in[i] = t[i].v[k];
-            const RawVec<VBO> ov = apply_vec<OP, T, VB, false>(in, g, b, vec_coef<OP, T, IT>(c, k));
+            const RawVec<VBO> ov = apply_vec<OP, T, VB, RAW>(in, g, b, vec_coef<OP, T, IT>(c, k));
             if constexpr (ODD) {
                 static_assert(VBO == 16 && NP == 0, "ODD rows: 16-byte bf16 vectors, no parameters");
                 if (k == 0 && oo->head) {
@@ -441,7 +485,7 @@ __device__ __forceinline__ void store_tile(Tile<T, VB, IT> (&t)[OpTraits<OP>::kI
 #pragma unroll
                 for (int i = 0; i < NI; ++i)
                     in[i] = t[i].v[kb + j];
-                buf_store<VBO, kStreamStore>(apply_vec<OP, T, VB, false>(in, g[j], b[j], vec_coef<OP, T, IT>(c, kb + j)), dst,
+                buf_store<VBO, kStreamStore>(apply_vec<OP, T, VB, RAW>(in, g[j], b[j], vec_coef<OP, T, IT>(c, kb + j)), dst,
                                              ooff);
             }
         }
@@ -589,15 +633,23 @@ __device__ __forceinline__ int partial_index(int64_t ns, int pos, bool last)
     return static_cast<int>(d / G);
 }
 
-// The per-row output (quantization scale) of `row`, written by one lane.
+// The per-row output of `row` (the quantization scale; LayerNorm backward's
+// mean and rstd when row_out is given), written by one lane.
 template <OpKind OP>
 __device__ __forceinline__ void store_row_value(const RowArgs &a, int64_t row, const Coef &c, bool writer)
 {
-    if constexpr (OpTraits<OP>::kRowOut) {
-        if (writer) {
-            RawVec<4> v;
-            v.w = __float_as_uint(OpTraits<OP>::row_value(c));
-            buf_store<4, kStreamStore>(v, span<4>(a.row_out, row, 1), 0u);
+    using Op = OpTraits<OP>;
+    if constexpr (Op::kRowOut) {
+        if (writer && a.row_out != nullptr) {
+            if constexpr (Op::kRowWords == 1) {
+                RawVec<4> v;
+                v.w = __float_as_uint(Op::row_value(c, 0));
+                buf_store<4, kStreamStore>(v, span<4>(a.row_out, row, 1), 0u);
+            } else {
+                RawVec<8> v;
+                v.w = u32x2{__float_as_uint(Op::row_value(c, 0)), __float_as_uint(Op::row_value(c, 1))};
+                buf_store<8, kStreamStore>(v, span<8>(a.row_out, row, 1), 0u);
+            }
         }
     }
 }

@@ -31,7 +31,9 @@
 //   kParamsInReduce  the parameters enter the statistics (LayerNorm backward)
 //            rather than only the output; `prepare` folds them into the
 //            held tile before the reduction
-//   kRowOut  one fp32 per row is written besides the row (quantization scale)
+//   kRowOut  kRowWords fp32 values per row are written besides the row, by
+//            row_value(c, i): the quantization scale (always), LayerNorm
+//            backward's mean and rstd (when the caller passes row_out)
 //   Out<T>   storage type of the output row
 //   wave_partial, merge, finalize, apply            held rows (paths 1, 2)
 //   stream_init, stream_update, wave_from_thread,
@@ -729,7 +731,8 @@ struct OpTraits<kLayerNormBwd> {
     static constexpr int kIn = 2;
     static constexpr int kParams = 1;
     static constexpr bool kParamsInReduce = true;
-    static constexpr bool kRowOut = false;
+    static constexpr bool kRowOut = true;  // mean and rstd, when row_out is given
+    static constexpr int kRowWords = 2;
     template <class T> using Out = T;
     using Partial = Part<kQ>;
 
@@ -813,6 +816,9 @@ struct OpTraits<kLayerNormBwd> {
         const float rstd = 1.0f / sqrtf(row.v[2] * inv_n + eps);
         return Coef{{row.v[1], rstd, row.v[3] * inv_n, rstd * rstd * (row.v[4] * inv_n)}};
     }
+
+    // the row's mean and rstd, for the parameter part
+    __device__ __forceinline__ static float row_value(const Coef &c, int i) { return i == 0 ? c.k[0] : c.k[1]; }
 
     // in[0] = x, in[1] = g
     template <class T>
@@ -956,7 +962,8 @@ struct OpTraits<kQuantInt8> {
         return fminf(fmaxf(__builtin_rintf(in[0] * c.k[0]), -127.0f), 127.0f);
     }
 
-    __device__ __forceinline__ static float row_value(const Coef &c) { return c.k[1]; }
+    static constexpr int kRowWords = 1;
+    __device__ __forceinline__ static float row_value(const Coef &c, int) { return c.k[1]; }
 
     template <class T, int VB, int U>
     __device__ __forceinline__ static void stream_update(Partial &r, const RawVec<VB> (&v)[kIn][U],

@@ -24,7 +24,7 @@ int stats_per_partial(int op) { return op_stats(op); }
 int in_bytes(int op, int dt) { return op_inputs(op) * elem_bytes(dt); }
 int out_bytes(int op, int dt) { return op == 5 ? 1 : elem_bytes(dt); }
 int row_out_bytes(int op) { return op == 5 ? 4 : 0; }
-bool op_supported(int op, int dt) { return op >= 0 && op < kNumOps && (dt == 0 || (dt == 1 && op != 4)); }
+bool op_supported(int op, int dt) { return op >= 0 && op < kNumOps && (dt == 0 || dt == 1); }
 
 int vec_bytes_for(int dt, int64_t cols)
 {
@@ -34,7 +34,7 @@ int vec_bytes_for(int dt, int64_t cols)
 bool row_is_partial(int op, int dt, int64_t cols)
 {
     const int64_t bytes = cols * elem_bytes(dt);
-    return op_has_part(op) && bytes % 16 != 0 && bytes % 4 == 0;
+    return op_has_part(op, dt) && bytes % 16 != 0 && bytes % 4 == 0;
 }
 
 bool row_is_odd(int op, int dt, int64_t cols) { return op_has_odd(op) && dt == 1 && cols % 2 == 1; }
@@ -151,22 +151,22 @@ static bool pick_holding_tile(const std::vector<TileSpec> &ladder, int64_t nv, T
 
 // The held-tile ladders of path 1 (wave and workgroup tiles) that `op`
 // compiles for rows of `vb`-byte vectors.
-static std::vector<TileSpec> single_ladder(int op, int vb)
+static std::vector<TileSpec> single_ladder(int op, int dt, int vb)
 {
     std::vector<TileSpec> ladder;
     for (int kind : {kKindWave, kKindWg})
         for (const TileSpec &u : tiles_for(kind, vb == 16))
-            if (tile_enabled(op, kind, u.block, u.items, vb))
+            if (tile_enabled(op, dt, kind, u.block, u.items, vb))
                 ladder.push_back(u);
     return ladder;
 }
 
 // The held tiles of an LDS ladder that `kind` compiles for `op`.
-static std::vector<TileSpec> lds_tiles(int op, int kind)
+static std::vector<TileSpec> lds_tiles(int op, int dt, int kind)
 {
     std::vector<TileSpec> out;
 #define CREDIT_LDS_ADD(b, it, lt)                            \
-    if (lds_tile_enabled(op, kind, b, it))                   \
+    if (lds_tile_enabled(op, dt, kind, b, it))               \
         out.push_back(TileSpec{kind, b, it, 16, lt});
     if (kind == kKindWg) {
         CREDIT_WG_LDS_TILES(CREDIT_LDS_ADD)
@@ -181,7 +181,7 @@ std::vector<TileSpec> lds_ladder(int op, int dt, int64_t cols, int kind)
 {
     if (held_row_kind(op, dt, cols) != 0 || held_vec_bytes(op, dt, cols) != 16)
         return {};
-    return lds_tiles(op, kind);
+    return lds_tiles(op, dt, kind);
 }
 
 // The LDS-tier tile that holds `need` vectors with the fewest LDS vectors
@@ -205,7 +205,7 @@ bool single_tile(int op, int dt, int64_t cols, TileSpec *out)
 {
     const int vb = held_vec_bytes(op, dt, cols);
     const int64_t nv = held_vectors(op, dt, cols);
-    const std::vector<TileSpec> ladder = single_ladder(op, vb);
+    const std::vector<TileSpec> ladder = single_ladder(op, dt, vb);
     TileSpec t;
     if (!pick_holding_tile(ladder, nv, &t) && !pick_lds_tile(lds_ladder(op, dt, cols, kKindWg), nv, &t))
         return false;
@@ -225,7 +225,7 @@ bool split_tile(int op, int dt, int64_t cols, int p, TileSpec *out)
         return false;  // the last slice would be empty: too narrow to split p ways
     std::vector<TileSpec> ladder;
     for (const TileSpec &u : tiles_for(kKindSplit, vb == 16))
-        if (tile_enabled(op, kKindSplit, u.block, u.items, vb))
+        if (tile_enabled(op, dt, kKindSplit, u.block, u.items, vb))
             ladder.push_back(u);
     TileSpec t;
     if (!pick_holding_tile(ladder, per, &t) && !pick_lds_tile(lds_ladder(op, dt, cols, kKindSplit), per, &t))
@@ -668,10 +668,10 @@ void enumerate_candidates(const PlanRequest &req, const Calibration &cal, std::v
     const bool v16 = vb == 16;
     const int64_t nv = held_vectors(req.op, req.dt, req.cols);
     const int rvb = vec_bytes_for(req.dt, req.cols);
-    const std::vector<TileSpec> held = single_ladder(req.op, vb);
+    const std::vector<TileSpec> held = single_ladder(req.op, req.dt, vb);
     for (int kind : {kKindWave, kKindWg})
         for (TileSpec t : tiles_for(kind, v16)) {
-            if (!tile_enabled(req.op, kind, t.block, t.items, vb) || !worth_holding(held, t, nv))
+            if (!tile_enabled(req.op, req.dt, kind, t.block, t.items, vb) || !worth_holding(held, t, nv))
                 continue;
             t.vb = vb;
             for (int mode : {0, -1}) {
@@ -714,7 +714,7 @@ void enumerate_candidates(const PlanRequest &req, const Calibration &cal, std::v
             continue;
         std::vector<TileSpec> ladder;
         for (const TileSpec &u : tiles_for(kKindSplit, v16))
-            if (tile_enabled(req.op, kKindSplit, u.block, u.items, vb))
+            if (tile_enabled(req.op, req.dt, kKindSplit, u.block, u.items, vb))
                 ladder.push_back(u);
         std::vector<TileSpec> tiles;
         for (TileSpec t : ladder)

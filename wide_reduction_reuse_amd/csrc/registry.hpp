@@ -28,11 +28,12 @@ struct KernelEntry {
 };
 
 // Operators with PART kernels: their partials mask the partial vector's
-// elements (softmax, LayerNorm, RMSNorm, softmax backward, LayerNorm
+// elements (softmax, LayerNorm, RMSNorm, softmax backward, fp32 LayerNorm
 // backward); the int8 quantizer, whose output rows of one byte per element
-// end inside a 4-byte word, keeps one-element tiles for rows that are not
-// whole vectors.
-constexpr bool op_has_part(int op) { return op <= 4; }
+// end inside a 4-byte word, and bf16 LayerNorm backward, whose held rows are
+// reduced in the streaming form (which counts whole vectors), keep
+// one-element tiles for rows that are not whole vectors.
+constexpr bool op_has_part(int op, int dt) { return op <= 3 || (op == 4 && dt == 0); }
 
 // Operators with ODD kernels (bf16 rows of odd length held as 16-byte
 // vectors): those without parameter vectors whose output has the input's
@@ -68,16 +69,22 @@ constexpr int op_stats(int op)
 #define CREDIT_SPLIT_TILES(X) X(256, 8) X(256, 16) X(512, 4) X(512, 8) X(512, 16) X(1024, 4) X(1024, 8) X(1024, 16)
 #define CREDIT_REREAD_TILES(X) X(256, 4) X(512, 4) X(1024, 4)
 
-// Tiles left out for one operator, all at 1024 threads, where a thread has
-// at most 128 VGPRs; each of them spilled registers to scratch memory when
-// compiled.  held = register bytes of row data a thread holds (all inputs).
+// Tiles left out for one operator (and dtype), each of which spilled
+// registers to scratch memory when compiled.  held = register bytes of row
+// data a thread holds (all inputs).  At 1024 threads, where a thread has at
+// most 128 VGPRs:
 //   LayerNorm split 16 x 16 B: the next smaller tiles split such slices finer.
 //   softmax-logits backward (x and dy held): more than 256 B (path 1) or
 //     128 B (split, which also keeps the exchange state).
 //   LayerNorm backward (x and g held, five statistics): more than 64 B; its
 //     512-thread tiles hold the same rows.
-constexpr bool tile_enabled(int op, int kind, int block, int items, int vb)
+// At 512 threads (256 VGPRs): bf16 LayerNorm backward, which holds x and dy
+// as loaded and converts them for every use, more than 256 B (x and dy of
+// 16 vectors each).
+constexpr bool tile_enabled(int op, int dt, int kind, int block, int items, int vb)
 {
+    if (op == 4 && dt == 1 && kind != kKindReread && block >= 512 && op_inputs(op) * items * vb > 256)
+        return false;
     if (kind == kKindReread || block < 1024)
         return true;
     const bool split = kind == kKindSplit || kind == kKindControl;
@@ -100,10 +107,10 @@ constexpr bool tile_enabled(int op, int kind, int block, int items, int vb)
 #define CREDIT_WG_LDS_TILES(X) X(512, 16, 8) X(1024, 16, 8)
 #define CREDIT_SPLIT_LDS_TILES(X) X(512, 16, 8) X(1024, 16, 8)
 
-constexpr bool lds_tile_enabled(int op, int kind, int block, int items)
+constexpr bool lds_tile_enabled(int op, int dt, int kind, int block, int items)
 {
     // LayerNorm at 1024 threads spilled registers with the LDS part's staging
-    return tile_enabled(op, kind, block, items, 16) && ((op_inputs(op) == 1 && op != 1) || block < 1024);
+    return tile_enabled(op, dt, kind, block, items, 16) && ((op_inputs(op) == 1 && op != 1) || block < 1024);
 }
 
 // Ladders for one-element accesses (rows whose byte length is not a multiple

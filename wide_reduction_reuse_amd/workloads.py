@@ -46,8 +46,8 @@ OPS = ("softmax", "layernorm", "rmsnorm", "softmax_bwd", "layernorm_bwd", "quant
 FWD_OPS = ("softmax", "layernorm", "rmsnorm")          # the crossover sweep's operators
 NEXT_OPS = ("softmax_bwd", "layernorm_bwd", "quantize_int8")
 DTYPES = ("f32", "bf16")
-# (op, dtype) pairs with kernels: LayerNorm backward is fp32 only
-SUPPORTED = {(op, dt) for op in OPS for dt in DTYPES} - {("layernorm_bwd", "bf16")}
+# (op, dtype) pairs with kernels: every operator in both dtypes
+SUPPORTED = {(op, dt) for op in OPS for dt in DTYPES}
 ELEM_BYTES = {"f32": 4, "bf16": 2}
 N_PARAMS = {"softmax": 0, "layernorm": 2, "rmsnorm": 1, "softmax_bwd": 0, "layernorm_bwd": 1, "quantize_int8": 0}
 N_INPUTS = {"softmax_bwd": 2, "layernorm_bwd": 2}      # row inputs per element (x, dy); others 1
