@@ -2,7 +2,7 @@
 """Benchmark of the reduction-reuse hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--all FILE] [--no-cpu] [--path P --split-p N] [--no-copy]
+                    [--all FILE] [--no-cpu] [--path P --split-p N] [--no-copy] [--lnbwd-params]
 
 A step is one pass of the hot path over one batch of synthetic input that is
 already resident in HBM: the selector picks a plan for the shape
@@ -61,7 +61,8 @@ def csrc_hash() -> str:
 
 
 def plan_tag(plan) -> str:
-    return "p%d-P%d-%dx%d" % (plan.path, plan.split_p, plan.block_threads, plan.items)
+    tag = "p%d-P%d-%dx%d" % (plan.path, plan.split_p, plan.block_threads, plan.items)
+    return tag + ("+%d" % plan.lds_items if plan.lds_items else "")
 
 
 def load_traffic(workload: str, plan):
@@ -95,6 +96,30 @@ def run_workload(w: W.Workload, path: str, split_p: int, steps: int, warmup: int
     durs, wall = time_launches(launch, steps, warmup, flush_buf)
     C.credit_check_errors()
     r = summarize(durs, w.algorithmic_bytes())
+    r["wall_s"] = wall
+    return r
+
+
+def lnbwd_params(w: W.Workload, steps: int, warmup: int, flush_buf) -> dict:
+    """Time LayerNorm backward's parameter part (both of its kernels) on the
+    LayerNorm-backward workload w: algorithmic bytes = x and dy read once,
+    the row statistics read, dgamma and dbeta written."""
+    import torch
+    from wide_reduction_reuse_amd import credit as C
+    inp = W.generate(w)
+    t = W.to_device(inp)
+    _, stats = C.credit_layernorm_backward_stats(t["x"], t["dy"], t["gamma"], inp.eps)
+    dg = torch.empty(w.cols, dtype=torch.float32, device="cuda")
+    db = torch.empty_like(dg)
+    ws = torch.empty(max(16, C.credit_layernorm_backward_params_workspace(w.rows, w.cols, w.dtype)),
+                     dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    durs, wall = time_launches(lambda e0, e1: C.credit_layernorm_backward_params(t["x"], t["dy"], stats, dg, db, ws),
+                               steps, warmup, flush_buf, record_on=stream)
+    eb = W.ELEM_BYTES[w.dtype]
+    nbytes = w.rows * w.cols * 2 * eb + w.rows * 8 + 2 * w.cols * 4
+    r = summarize(durs, nbytes)
+    r["bytes"] = nbytes
     r["wall_s"] = wall
     return r
 
@@ -181,6 +206,8 @@ def main(argv=None) -> int:
                     help="force a path (for profiling one path; the default line uses the selector's plan)")
     ap.add_argument("--split-p", type=int, default=0, help="with --path split: workgroups per row (0 = chosen)")
     ap.add_argument("--no-copy", action="store_true", help="skip timing the streaming copy of the same bytes")
+    ap.add_argument("--lnbwd-params", action="store_true",
+                    help="only time LayerNorm backward's parameter part on the workload (a layernorm_bwd one)")
     a = ap.parse_args(argv)
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the row-wise operators shard by rows with no "
@@ -198,6 +225,14 @@ def main(argv=None) -> int:
     if a.copy:
         cc = copy_ceiling(a.copy << 20, a.steps, a.warmup, flush_buf)
         print(json.dumps({"kind": "copy_ceiling", "mib": a.copy, **cc}), flush=True)
+        return 0
+    if a.lnbwd_params:
+        w = W.NAMED[a.workload if W.NAMED[a.workload].op == "layernorm_bwd" else "layernorm_bwd_f32_2048x65536"]
+        r = lnbwd_params(w, a.steps, a.warmup, flush_buf)
+        print(json.dumps({"kind": "layernorm_bwd_params", "workload": w.name, "gbs": round(r["gbs"], 2),
+                          "frac_of_peak": round(r["gbs"] / HBM_PEAK_GBS, 4), "bytes": r["bytes"],
+                          "mean_ms": round(r["mean_ms"], 5), "median_ms": round(r["median_ms"], 5),
+                          "timing": "HIP events recorded around both kernels on their stream"}), flush=True)
         return 0
 
     w = W.NAMED[a.workload]

@@ -10,9 +10,12 @@
 // the parameter part is its own pair of HBM-bound kernels that read x and dy
 // once more:
 //   stage 1: workgroup (b, g) sums rows [g R, (g + 1) R) of column block b
-//     (kParamsBlock 16-byte vectors, one per thread: coalesced along the row)
-//     into partial[g][...]; four rows' loads are issued before their sums;
-//   stage 2: one thread per column adds the G partials in order.
+//     (one 16-byte vector per thread, coalesced along the row; 256 vectors,
+//     or 64 with four row lanes for narrow rows) into partial[g][...], with
+//     eight rows' loads per lane in flight and the next eight issued before
+//     they are summed;
+//   stage 2: four waves per 64 columns add the G partials (each a fixed
+//     subset in order) and then their four sums in order.
 // Both stages sum in a fixed order, so results are reproducible run to run.
 #include <hip/hip_runtime.h>
 
@@ -26,7 +29,7 @@ namespace credit {
 namespace {
 
 constexpr int kParamsBlock = 256;  // threads per workgroup, one column vector each
-constexpr int kRowUnroll = 4;      // rows whose loads are in flight together
+constexpr int kRowUnroll = 8;      // rows per row lane whose loads are in flight together
 constexpr int kTargetWgs = 2048;   // stage-1 workgroups to aim for (8 per CU)
 constexpr int64_t kMinRowsPerGroup = 8;
 
@@ -74,52 +77,106 @@ struct Vec {
     }
 };
 
-template <class T, int VB>
-__global__ __launch_bounds__(kParamsBlock) void lnbwd_params_partial_kernel(ParamsArgs a)
+// Sum rows rl, rl + RL, ... of rows [r0, r1) of one column vector into sg, sb:
+// kRowUnroll rows' loads in flight, the next batch issued before the current
+// one is summed.
+template <class T, int VB, int RL>
+__device__ __forceinline__ void sum_rows(const ParamsArgs &a, int64_t col0, int64_t r0, int64_t n,
+                                         float (&sg)[Vec<T, VB>::kE], float (&sb)[Vec<T, VB>::kE])
 {
     using V = Vec<T, VB>;
     constexpr int E = V::kE;
-    const int64_t col0 = (static_cast<int64_t>(blockIdx.x) * kParamsBlock + threadIdx.x) * E;
-    const int64_t g = blockIdx.y;
-    const int64_t r0 = g * a.rows_per_group;
-    const int64_t r1 = min(a.rows, r0 + a.rows_per_group);
-    if (col0 >= a.cols)
-        return;
-    float sg[E], sb[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e)
-        sg[e] = sb[e] = 0.0f;
-    int64_t r = r0;
-    for (; r + kRowUnroll <= r1; r += kRowUnroll) {
-        V xv[kRowUnroll], dv[kRowUnroll];
-#pragma unroll
-        for (int u = 0; u < kRowUnroll; ++u) {
-            xv[u].load(a.x, (r + u) * a.cols + col0);
-            dv[u].load(a.dy, (r + u) * a.cols + col0);
-        }
-#pragma unroll
-        for (int u = 0; u < kRowUnroll; ++u) {
-            const float mu = a.stats[2 * (r + u)], rstd = a.stats[2 * (r + u) + 1];
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-                const float d = dv[u].at(e);
-                sg[e] = __builtin_fmaf(d, (xv[u].at(e) - mu) * rstd, sg[e]);
-                sb[e] += d;
-            }
-        }
-    }
-    for (; r < r1; ++r) {
-        V xv, dv;
-        xv.load(a.x, r * a.cols + col0);
-        dv.load(a.dy, r * a.cols + col0);
-        const float mu = a.stats[2 * r], rstd = a.stats[2 * r + 1];
+    constexpr int U = kRowUnroll;
+    auto add = [&](const V &xv, const V &dv, int64_t row) __attribute__((always_inline)) {
+        const float mu = a.stats[2 * row], rstd = a.stats[2 * row + 1];
 #pragma unroll
         for (int e = 0; e < E; ++e) {
             const float d = dv.at(e);
             sg[e] = __builtin_fmaf(d, (xv.at(e) - mu) * rstd, sg[e]);
             sb[e] += d;
         }
+    };
+    int64_t k = 0;
+    V xv[U], dv[U];
+    if (U <= n) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            xv[u].load(a.x, (r0 + u * RL) * a.cols + col0);
+            dv[u].load(a.dy, (r0 + u * RL) * a.cols + col0);
+        }
     }
+    for (; k + U <= n; k += U) {
+        V xc[U], dc[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            xc[u] = xv[u];
+            dc[u] = dv[u];
+        }
+        if (k + 2 * U <= n) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                xv[u].load(a.x, (r0 + (k + U + u) * RL) * a.cols + col0);
+                dv[u].load(a.dy, (r0 + (k + U + u) * RL) * a.cols + col0);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            add(xc[u], dc[u], r0 + (k + u) * RL);
+    }
+    for (; k < n; ++k) {
+        V x1, d1;
+        x1.load(a.x, (r0 + k * RL) * a.cols + col0);
+        d1.load(a.dy, (r0 + k * RL) * a.cols + col0);
+        add(x1, d1, r0 + k * RL);
+    }
+}
+
+// Stage 1.  CV column vectors per workgroup: 256 (one row lane), or 64 for
+// narrow rows, where the workgroup's four waves take every fourth row of the
+// group and their sums are added in wave order through LDS (fewer groups, so
+// a smaller workspace and a shorter stage 2).
+template <class T, int VB, int CV>
+__global__ __launch_bounds__(kParamsBlock) void lnbwd_params_partial_kernel(ParamsArgs a)
+{
+    constexpr int E = Vec<T, VB>::kE;
+    constexpr int RL = kParamsBlock / CV;
+    __shared__ float sh[2][RL][CV][E];
+    const int lc = threadIdx.x % CV, rl = threadIdx.x / CV;
+    const int64_t col0 = (static_cast<int64_t>(blockIdx.x) * CV + lc) * E;
+    const int64_t g = blockIdx.y;
+    const int64_t r0 = g * a.rows_per_group;
+    const int64_t r1 = min(a.rows, r0 + a.rows_per_group);
+    const bool active = col0 < a.cols;
+    // rows of this lane: r0 + rl + k RL, k < n
+    const int64_t n = active && r0 + rl < r1 ? (r1 - r0 - rl + RL - 1) / RL : 0;
+    float sg[E], sb[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+        sg[e] = sb[e] = 0.0f;
+    sum_rows<T, VB, RL>(a, col0, r0 + rl, n, sg, sb);
+    if constexpr (RL > 1) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            sh[0][rl][lc][e] = sg[e];
+            sh[1][rl][lc][e] = sb[e];
+        }
+        __syncthreads();
+        if (rl != 0)
+            return;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            float tg = sh[0][0][lc][e], tb = sh[1][0][lc][e];
+#pragma unroll
+            for (int i = 1; i < RL; ++i) {
+                tg += sh[0][i][lc][e];
+                tb += sh[1][i][lc][e];
+            }
+            sg[e] = tg;
+            sb[e] = tb;
+        }
+    }
+    if (!active)
+        return;
     float *pg = a.partial + g * a.cols + col0;
     float *pb = a.partial + (a.groups + g) * a.cols + col0;
 #pragma unroll
@@ -129,33 +186,58 @@ __global__ __launch_bounds__(kParamsBlock) void lnbwd_params_partial_kernel(Para
     }
 }
 
+// Stage 2: 64 columns per workgroup; wave w adds groups w, w + 4, ... and
+// the four sums are added in wave order.
+constexpr int kFinishCols = 64;
 __global__ __launch_bounds__(kParamsBlock) void lnbwd_params_finish_kernel(const float *partial, int64_t groups,
                                                                           int64_t cols, float *dgamma,
                                                                           float *dbeta)
 {
-    const int64_t j = static_cast<int64_t>(blockIdx.x) * kParamsBlock + threadIdx.x;
-    if (j >= cols)
-        return;
+    constexpr int W = kParamsBlock / kFinishCols;
+    __shared__ float sh[2][W][kFinishCols];
+    const int lane = threadIdx.x % kFinishCols, w = threadIdx.x / kFinishCols;
+    const int64_t j = static_cast<int64_t>(blockIdx.x) * kFinishCols + lane;
     float sg = 0.0f, sb = 0.0f;
-    for (int64_t g = 0; g < groups; ++g) {
-        sg += partial[g * cols + j];
-        sb += partial[(groups + g) * cols + j];
+    if (j < cols)
+        for (int64_t g = w; g < groups; g += W) {
+            sg += partial[g * cols + j];
+            sb += partial[(groups + g) * cols + j];
+        }
+    sh[0][w][lane] = sg;
+    sh[1][w][lane] = sb;
+    __syncthreads();
+    if (w != 0 || j >= cols)
+        return;
+    float tg = sh[0][0][lane], tb = sh[1][0][lane];
+#pragma unroll
+    for (int i = 1; i < W; ++i) {
+        tg += sh[0][i][lane];
+        tb += sh[1][i][lane];
     }
-    dgamma[j] = sg;
-    dbeta[j] = sb;
+    dgamma[j] = tg;
+    dbeta[j] = tb;
 }
 
-// Row groups of stage 1 for a shape: enough workgroups to fill the chip,
-// at least kMinRowsPerGroup rows each.
-void params_grid(int64_t rows, int64_t cols, int vb_elems, int64_t *col_blocks, int64_t *groups,
-                 int64_t *rows_per_group)
+// Stage-1 shape: column vectors per workgroup (CV), column blocks and row
+// groups: about kTargetWgs workgroups, at least kMinRowsPerGroup rows per
+// row lane.
+struct ParamsGrid {
+    int cv;
+    int64_t col_blocks, groups, rows_per_group;
+};
+
+ParamsGrid params_grid(int64_t rows, int64_t cols, int vb_elems)
 {
+    ParamsGrid p;
     const int64_t vecs = (cols + vb_elems - 1) / vb_elems;
-    *col_blocks = (vecs + kParamsBlock - 1) / kParamsBlock;
-    int64_t g = (kTargetWgs + *col_blocks - 1) / *col_blocks;
-    g = std::max<int64_t>(1, std::min<int64_t>(g, rows / kMinRowsPerGroup));
-    *rows_per_group = (rows + g - 1) / g;
-    *groups = rows > 0 ? (rows + *rows_per_group - 1) / *rows_per_group : 0;
+    p.cv = vecs >= 32 * kParamsBlock ? kParamsBlock : 64;
+    const int64_t lanes = kParamsBlock / p.cv;
+    p.col_blocks = (vecs + p.cv - 1) / p.cv;
+    int64_t g = (kTargetWgs + p.col_blocks - 1) / p.col_blocks;
+    g = std::max<int64_t>(1, std::min<int64_t>(g, rows / (kMinRowsPerGroup * lanes)));
+    p.rows_per_group = (rows + g - 1) / g;
+    p.groups = rows > 0 ? (rows + p.rows_per_group - 1) / p.rows_per_group : 0;
+    return p;
 }
 
 int elems_per_access(credit_dtype_t dt, int64_t cols)
@@ -174,9 +256,8 @@ extern "C" credit_status_t credit_layernorm_backward_params_workspace(int64_t ro
 {
     if (bytes == nullptr || rows < 0 || cols < 1 || (dt != CREDIT_F32 && dt != CREDIT_BF16))
         return CREDIT_ERR_INVALID_ARG;
-    int64_t cb = 0, g = 0, rpg = 0;
-    params_grid(rows, cols, elems_per_access(dt, cols), &cb, &g, &rpg);
-    *bytes = static_cast<size_t>(2 * g * cols) * sizeof(float);
+    const ParamsGrid pg = params_grid(rows, cols, elems_per_access(dt, cols));
+    *bytes = static_cast<size_t>(2 * pg.groups * cols) * sizeof(float);
     return CREDIT_OK;
 }
 
@@ -194,33 +275,41 @@ extern "C" credit_status_t credit_layernorm_backward_params(const void *x, const
     if ((epa > 1 && (misaligned(x, 16) || misaligned(dy, 16))) || misaligned(x, eb) || misaligned(dy, eb) ||
         misaligned(row_stats, 8) || misaligned(dgamma, 4) || misaligned(dbeta, 4))
         return CREDIT_ERR_ALIGNMENT;
-    int64_t cb = 0, g = 0, rpg = 0;
-    params_grid(rows, cols, epa, &cb, &g, &rpg);
-    const size_t need = static_cast<size_t>(2 * g * cols) * sizeof(float);
+    const ParamsGrid pg = params_grid(rows, cols, epa);
+    const size_t need = static_cast<size_t>(2 * pg.groups * cols) * sizeof(float);
     if (rows > 0 && (workspace == nullptr || workspace_bytes < need || misaligned(workspace, 16)))
         return CREDIT_ERR_INVALID_ARG;
-    if (cb > 0x7FFFFFFF || g > 65535)
+    if (pg.col_blocks > 0x7FFFFFFF || pg.groups > 65535)
         return CREDIT_ERR_UNSUPPORTED;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (rows > 0) {
-        ParamsArgs a{x, dy, row_stats, static_cast<float *>(workspace), rows, cols, rpg, g};
-        const dim3 grid(static_cast<unsigned>(cb), static_cast<unsigned>(g));
+        ParamsArgs a{x, dy, row_stats, static_cast<float *>(workspace), rows, cols, pg.rows_per_group, pg.groups};
+        const dim3 grid(static_cast<unsigned>(pg.col_blocks), static_cast<unsigned>(pg.groups));
+        const dim3 block(kParamsBlock);
+#define CREDIT_PARAMS_LAUNCH(T, VB)                                                          \
+    do {                                                                                     \
+        if (pg.cv == kParamsBlock)                                                           \
+            hipLaunchKernelGGL((lnbwd_params_partial_kernel<T, VB, kParamsBlock>), grid, block, 0, s, a); \
+        else                                                                                 \
+            hipLaunchKernelGGL((lnbwd_params_partial_kernel<T, VB, 64>), grid, block, 0, s, a); \
+    } while (0)
         if (dt == CREDIT_F32) {
             if (epa > 1)
-                hipLaunchKernelGGL((lnbwd_params_partial_kernel<float, 16>), grid, dim3(kParamsBlock), 0, s, a);
+                CREDIT_PARAMS_LAUNCH(float, 16);
             else
-                hipLaunchKernelGGL((lnbwd_params_partial_kernel<float, 4>), grid, dim3(kParamsBlock), 0, s, a);
+                CREDIT_PARAMS_LAUNCH(float, 4);
         } else {
             if (epa > 1)
-                hipLaunchKernelGGL((lnbwd_params_partial_kernel<bf16_t, 16>), grid, dim3(kParamsBlock), 0, s, a);
+                CREDIT_PARAMS_LAUNCH(bf16_t, 16);
             else
-                hipLaunchKernelGGL((lnbwd_params_partial_kernel<bf16_t, 2>), grid, dim3(kParamsBlock), 0, s, a);
+                CREDIT_PARAMS_LAUNCH(bf16_t, 2);
         }
+#undef CREDIT_PARAMS_LAUNCH
     }
-    // zero rows: the sums are zero (g = 0 groups)
-    const unsigned fb = static_cast<unsigned>((cols + kParamsBlock - 1) / kParamsBlock);
+    // zero rows: the sums are zero (no groups)
+    const unsigned fb = static_cast<unsigned>((cols + kFinishCols - 1) / kFinishCols);
     hipLaunchKernelGGL(lnbwd_params_finish_kernel, dim3(fb), dim3(kParamsBlock), 0, s,
-                       static_cast<const float *>(workspace), g, cols, dgamma, dbeta);
+                       static_cast<const float *>(workspace), pg.groups, cols, dgamma, dbeta);
     if (hipGetLastError() != hipSuccess)
         return CREDIT_ERR_HIP;
     return CREDIT_OK;

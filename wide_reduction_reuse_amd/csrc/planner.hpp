@@ -65,18 +65,18 @@ double calib_time_us(const CalibEntry &e, double rows);
 // Constants of the analytic model (fitted to exhaustive timings of
 // calibration shapes by model_fit.py; these defaults are MI355X's).
 struct ModelConsts {
-    double bw_gbs = 4946.9724;     // rate the kernels stream at with enough bytes in flight
-    double lat_us = 0.6641;        // a CU's bytes in flight / lat_us = the rate it can sustain
-    double owner_gbs = 40.6333;    // the most one owner streams: its row's bytes / owner_gbs bound its time
-    double miss3 = 0.2220;         // fraction of path 3's second read served from HBM
-    double l0_us = 2.3188;         // least time of one owner's row: a fixed part
-    double item_us = 0.2012;       // ... and a part per vector each thread holds or streams
-    double own3_us = 1.4955;       // ... and, for a reread owner, its second pass
-    double launch_us = 3.4682;     // one launch
-    double exch_us = 3.7193;       // one split-row exchange per row wave (Eq. 8's control cost)
-    double split_launch_us = 4.0496; // a split launch's control cost beyond its row waves
-    double eta3 = 1.4065;          // bytes multiplier of reread launches (their streaming efficiency)
-    double persist = 1.0106;       // ... of persistent owners on path 1
+    double bw_gbs = 5100.5492;     // rate the kernels stream at with enough bytes in flight
+    double lat_us = 0.6889;        // a CU's bytes in flight / lat_us = the rate it can sustain
+    double owner_gbs = 44.5709;    // the most one owner streams: its row's bytes / owner_gbs bound its time
+    double miss3 = 0.3980;         // fraction of path 3's second read served from HBM
+    double l0_us = 2.2005;         // least time of one owner's row: a fixed part
+    double item_us = 0.2123;       // ... and a part per vector each thread holds or streams
+    double own3_us = 1.6787;       // ... and, for a reread owner, its second pass
+    double launch_us = 3.5074;     // one launch
+    double exch_us = 3.5980;       // one split-row exchange per row wave (Eq. 8's control cost)
+    double split_launch_us = 6.2248; // a split launch's control cost beyond its row waves
+    double eta3 = 1.2562;          // bytes multiplier of reread launches (their streaming efficiency)
+    double persist = 1.0084;       // ... of persistent owners on path 1
     double word_gbs = 10.0;        // exchange-word rate of one workgroup (T_DSM)
 };
 

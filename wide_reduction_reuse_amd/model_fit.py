@@ -39,9 +39,9 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 
 STREAM = ["bw_gbs", "lat_us", "owner_gbs", "miss3", "l0_us", "item_us", "own3_us", "launch_us", "eta3", "persist"]
 SPLIT = ["exch_us", "split_launch_us"]
-DEFAULTS = {"bw_gbs": 4946.9724, "lat_us": 0.6641, "owner_gbs": 40.6333, "miss3": 0.222, "l0_us": 2.3188,
-            "item_us": 0.2012, "own3_us": 1.4955, "launch_us": 3.4682, "exch_us": 3.7193,
-            "split_launch_us": 4.0496, "eta3": 1.4065, "persist": 1.0106, "word_gbs": 10.0}
+DEFAULTS = {"bw_gbs": 5100.5492, "lat_us": 0.6889, "owner_gbs": 44.5709, "miss3": 0.398, "l0_us": 2.2005,
+            "item_us": 0.2123, "own3_us": 1.6787, "launch_us": 3.5074, "exch_us": 3.598,
+            "split_launch_us": 6.2248, "eta3": 1.2562, "persist": 1.0084, "word_gbs": 10.0}
 OPS = ["softmax", "layernorm", "rmsnorm", "softmax_bwd", "layernorm_bwd", "quantize_int8"]
 DTS = ["f32", "bf16"]
 KIND_WAVE, KIND_WG, KIND_SPLIT, KIND_REREAD = 1, 2, 3, 4

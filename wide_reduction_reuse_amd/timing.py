@@ -23,12 +23,18 @@ class HipEvents:
                                                  ctypes.c_void_p]
         self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         self.pairs = []
         for _ in range(n):
             a, b = ctypes.c_void_p(), ctypes.c_void_p()
             if self.hip.hipEventCreate(ctypes.byref(a)) or self.hip.hipEventCreate(ctypes.byref(b)):
                 raise RuntimeError("hipEventCreate failed")
             self.pairs.append((a.value, b.value))
+
+    def record(self, event: int, stream: int) -> None:
+        """Record `event` on `stream` (for launches that take no events)."""
+        if self.hip.hipEventRecord(event, stream):
+            raise RuntimeError("hipEventRecord failed")
 
     def elapsed_ms(self, i: int) -> float:
         a, b = self.pairs[i]
@@ -51,13 +57,23 @@ def flush_buffer():
     return torch.zeros(FLUSH_BYTES // 4, dtype=torch.int32, device="cuda")
 
 
-def time_launches(launch, steps: int, warmup: int, flush_buf):
+def time_launches(launch, steps: int, warmup: int, flush_buf, record_on=None):
     """Call launch(start_event, stop_event) warmup + steps times, each after an
     untimed cache flush; return the per-step kernel durations (ms) of the
-    timed steps and the wall seconds of the timed loop."""
+    timed steps and the wall seconds of the timed loop.  With record_on (a
+    stream handle), the events are recorded on that stream around
+    launch(None, None) instead (work of several kernels, then the interval
+    includes the gaps between them)."""
     import torch
     from . import credit as C
     ev = HipEvents(warmup + steps)
+    if record_on is not None:
+        inner = launch
+
+        def launch(e0, e1):
+            ev.record(e0, record_on)
+            inner(None, None)
+            ev.record(e1, record_on)
     try:
         for i in range(warmup):
             C.credit_flush(flush_buf)
