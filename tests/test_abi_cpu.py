@@ -184,13 +184,12 @@ def test_selector_legality_on_cpu():
 
 
 def test_partial_rows_are_held_as_16_byte_vectors():
-    # byte length a multiple of 4 but not of 16: softmax, LayerNorm, RMSNorm,
-    # softmax backward and LayerNorm backward hold the row as 16-byte vectors
-    # (the last partial) and reread it by element; the quantizer uses
-    # one-element tiles
+    # byte length a multiple of 4 but not of 16, operators with parameter
+    # vectors (LayerNorm, RMSNorm, fp32 LayerNorm backward): paths 1 and 2
+    # hold the row as 16-byte vectors (the last partial) and reread it by
+    # element; odd-length bf16 rows of these operators use one-element tiles
     L = C.lib()
-    for op, dt, cols in [("softmax", "f32", 1001), ("layernorm", "bf16", 1002), ("rmsnorm", "f32", 3),
-                         ("softmax_bwd", "bf16", 30006), ("layernorm_bwd", "f32", 1001)]:
+    for op, dt, cols in [("layernorm", "bf16", 1002), ("rmsnorm", "f32", 3), ("layernorm_bwd", "f32", 1001)]:
         p = C.credit_plan(op, dt, 64, cols, "single")
         assert p.vec_bytes == 16
         assert C.credit_plan(op, dt, 64, cols, "reread").vec_bytes == 16 // (4 if dt == "f32" else 8)
@@ -198,31 +197,51 @@ def test_partial_rows_are_held_as_16_byte_vectors():
         plan = C.Plan.make(C.PATH_SINGLE_WG, 1, p.block_threads, p.items, 4 if dt == "f32" else 2)
         assert L.credit_run_plan(C.OPS[op], _ops(x=A, dy=G, gamma=G, beta=G, y=B), 4, cols, 1e-5,
                                  C.DTYPES[dt], ctypes.byref(plan), None) == 4
-    p = C.credit_plan("softmax", "f32", 64, 100006, "split", 8)
-    assert p.vec_bytes == 16
-    assert C.credit_plan("quantize_int8", "f32", 64, 1001, "single").vec_bytes == 4
     assert C.credit_plan("layernorm_bwd", "f32", 64, 100003, "split", 8).vec_bytes == 16
-    assert C.credit_plan("rmsnorm", "bf16", 64, 1001, "single").vec_bytes == 2  # odd bytes / 4
+    for op in ("layernorm", "rmsnorm"):
+        assert C.credit_plan(op, "bf16", 64, 1001, "single").vec_bytes == 2  # odd bytes / 4
 
 
-def test_odd_bf16_rows_of_the_softmax_family_are_held_as_16_byte_vectors():
-    # bf16 rows of odd length: softmax and softmax backward (no parameter
-    # vectors) hold them as 16-byte vectors from the 4-byte word below the
-    # row's start on paths 1 and 2 and reread them by element; operators with
-    # parameters and the quantizer keep one-element tiles
+def _max_shift_bytes(cols, eb):
+    """The most bytes of the previous row in front of any row of a tensor with
+    16-byte aligned base: brute force over the base's offset in a 64-byte line
+    and enough rows to cycle through every start."""
+    return max((base + r * cols * eb) % 64 for base in (0, 16, 32, 48) for r in range(0, 65))
+
+
+def test_shifted_rows_are_held_from_the_64_byte_line_below():
+    # rows whose byte length is not a multiple of 64, of the operators
+    # without parameter vectors (softmax, softmax backward, the int8
+    # quantizer): paths 1 and 2 hold them as 16-byte vectors from the 64-byte
+    # boundary below each row's start, so a tile must hold the row plus the
+    # largest such offset; the reread path reads them by element (or by
+    # 16-byte vector when the byte length is a multiple of 16)
     L = C.lib()
-    for op, cols in [("softmax", 1), ("softmax", 1001), ("softmax", 50257), ("softmax_bwd", 30001)]:
-        p = C.credit_plan(op, "bf16", 64, cols, "single")
-        assert p.vec_bytes == 16
-        assert p.block_threads * p.items * 8 >= cols + 1  # the held span has one more element
-        assert C.credit_plan(op, "bf16", 64, cols, "reread").vec_bytes == 2
-        plan = C.Plan.make(C.PATH_SINGLE_WG, 1, p.block_threads, p.items, 2)
-        assert L.credit_run_plan(C.OPS[op], _ops(x=A, dy=G, y=B), 4, cols, 0.0, C.DTYPES["bf16"],
-                                 ctypes.byref(plan), None) == 4
+    cases = [("softmax", "f32", 1001), ("softmax", "f32", 1004), ("softmax", "f32", 1016), ("softmax", "bf16", 1),
+             ("softmax", "bf16", 1001), ("softmax", "bf16", 50257), ("softmax", "bf16", 50264),
+             ("softmax_bwd", "bf16", 30001), ("softmax_bwd", "f32", 30006), ("quantize_int8", "f32", 1001),
+             ("quantize_int8", "bf16", 1001), ("quantize_int8", "f32", 4100)]
+    for op, dt, cols in cases:
+        eb = 4 if dt == "f32" else 2
+        p = C.credit_plan(op, dt, 64, cols, "single")
+        assert p.vec_bytes == 16, (op, dt, cols)
+        span = cols * eb + _max_shift_bytes(cols, eb)
+        assert p.block_threads * p.items * 16 >= span, (op, dt, cols)
+        rvb = 16 if (cols * eb) % 16 == 0 else eb
+        assert C.credit_plan(op, dt, 64, cols, "reread").vec_bytes == rvb
+        if rvb != 16:
+            plan = C.Plan.make(C.PATH_SINGLE_WG, 1, p.block_threads, p.items, eb)
+            assert L.credit_run_plan(C.OPS[op], _ops(x=A, dy=G, y=B, row_out=G), 4, cols, 0.0, C.DTYPES[dt],
+                                     ctypes.byref(plan), None) == 4
+    # a tile that holds the row but not the row plus its largest offset is refused
+    small = C.Plan.make(C.PATH_SINGLE_WG, 1, 64, 4, 16)  # 256 vectors = 1024 fp32
+    assert L.credit_run_plan(C.OPS["softmax"], _ops(x=A, y=B), 4, 1020, 0.0, C.DTYPES["f32"],
+                             ctypes.byref(small), None) == 4
     assert C.credit_plan("softmax", "bf16", 64, 100003, "split", 8).vec_bytes == 16
-    for op in ("layernorm", "rmsnorm", "quantize_int8"):
-        assert C.credit_plan(op, "bf16", 64, 1001, "single").vec_bytes == 2
-    assert C.credit_plan("softmax", "f32", 64, 1001, "single").vec_bytes == 16  # a partial row, not odd
+    # rows of whole 64-byte lines are held as they are
+    for op, dt, cols in [("softmax", "f32", 1024), ("quantize_int8", "bf16", 4096), ("softmax_bwd", "f32", 48)]:
+        p = C.credit_plan(op, dt, 64, cols, "single")
+        assert p.vec_bytes == 16 and p.block_threads * p.items * 16 >= cols * (4 if dt == "f32" else 2)
 
 
 def test_selector_legality_of_the_further_workloads():

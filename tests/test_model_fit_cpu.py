@@ -56,13 +56,24 @@ def test_fit_recovers_the_timings_of_known_constants():
     assert got["word_gbs"] == F.DEFAULTS["word_gbs"]  # not fitted
 
 
-def test_row_kind_follows_the_planner():
+def test_row_kind_matches_the_kernel_families():
     C.credit_load_calibration(None)
-    assert F.row_kind(C, "softmax", "f32", 4096) == 0
-    assert F.row_kind(C, "softmax", "f32", 30001) == 1     # fp32 rows end in a partial 16-byte vector
-    assert F.row_kind(C, "softmax", "bf16", 20002) == 1
-    assert F.row_kind(C, "softmax", "bf16", 50257) == 2    # odd bf16 rows held from the word below
-    assert F.row_kind(C, "rmsnorm", "bf16", 50257) == 0    # no odd kernels: 2-byte accesses throughout
+    assert F.row_kind("softmax", "f32", 4096) == 0
+    assert F.row_kind("softmax", "f32", 30001) == 2        # not a multiple of 64 bytes: shifted
+    assert F.row_kind("softmax", "f32", 1004) == 2         # 16-byte multiple, not 64: shifted too
+    assert F.row_kind("softmax", "bf16", 20002) == 2
+    assert F.row_kind("softmax", "bf16", 50257) == 2
+    assert F.row_kind("quantize_int8", "f32", 1001) == 2
+    assert F.row_kind("softmax_bwd", "f32", 48) == 0       # 192 bytes: whole lines
+    assert F.row_kind("rmsnorm", "f32", 30001) == 1        # parameters: a partial last vector
+    assert F.row_kind("layernorm", "bf16", 20002) == 1
+    assert F.row_kind("rmsnorm", "bf16", 50257) == 0       # 2-byte accesses throughout
+    assert F.row_kind("layernorm_bwd", "bf16", 20002) == 0
+    # the library holds kind-2 widths with room for the shift, kind-1 widths without
+    assert C.credit_plan("softmax", "f32", 64, 1020, "single").block_threads * \
+        C.credit_plan("softmax", "f32", 64, 1020, "single").items * 4 >= 1020 + 12
+    assert C.credit_plan("rmsnorm", "f32", 64, 1022, "single").block_threads * \
+        C.credit_plan("rmsnorm", "f32", 64, 1022, "single").items * 4 >= 1022
 
 
 def test_occupancy_table_and_written_calibration_load(tmp_path):
@@ -77,7 +88,7 @@ def test_occupancy_table_and_written_calibration_load(tmp_path):
         {"plan": {"path": 3, "split_p": 1, "block_threads": 512, "items": 4, "vec_bytes": 4, "wgs_per_cu": 0},
          "median_ms": 0.01, "occupancy": 4}]}
     occ = F.occupancy_table(C, [rec])
-    assert occ == [[0, 0, 1, 64, 16, 16, 1, 0, 5], [0, 0, 2, 512, 4, 16, 1, 0, 3], [0, 0, 3, 256, 2, 16, 1, 0, 6],
+    assert occ == [[0, 0, 1, 64, 16, 16, 2, 0, 5], [0, 0, 2, 512, 4, 16, 2, 0, 3], [0, 0, 3, 256, 2, 16, 2, 0, 6],
                    [0, 0, 4, 512, 4, 4, 0, 0, 4]]
     src = tmp_path / "in.jsonl"
     src.write_text(json.dumps(rec) + "\n")

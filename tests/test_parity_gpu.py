@@ -151,6 +151,11 @@ def _ladder(macro):
     return [(64, int(a)) if not b else (int(a), int(b)) for a, b in pairs]
 
 
+# operators without parameter vectors: their held tiles hold rows that are
+# not whole 64-byte lines from the line boundary below each row's start
+SHIFT_OPS = ("softmax", "softmax_bwd", "quantize_int8")
+
+
 def _tile_cases():
     cases = []
     ladders = {
@@ -167,15 +172,20 @@ def _tile_cases():
             for kind, tiles in ladders.items():
                 for block, items in tiles:
                     cap = block * items  # vectors
+                    # the operators without parameters hold rows that are not
+                    # whole 64-byte lines shifted (test_every_tile_shifted):
+                    # here their rows are whole lines (vector counts a
+                    # multiple of 4), held as they are
+                    lines = op in SHIFT_OPS
                     if kind == "split":
                         for p in (2, 4, 8):
                             # slices fill most of the tile, last slice ragged
-                            nv = p * cap - 3 * p - 1
+                            nv = p * cap - 4 * p - 4 if lines else p * cap - 3 * p - 1
                             cases.append((op, dt, kind, block, items, p, nv * epv))
                     elif kind == "reread":
                         cases.append((op, dt, kind, block, items, 1, (3 * cap + 5) * epv))
                     else:
-                        cases.append((op, dt, kind, block, items, 1, (cap - 3) * epv))
+                        cases.append((op, dt, kind, block, items, 1, (cap - (4 if lines else 3)) * epv))
     return cases
 
 
@@ -223,11 +233,11 @@ def test_every_tile(op, dt, kind, block, items, p, cols):
 
 
 # ---------------------------------------------------------------------------
-# rows whose last 16-byte vector is partial: the held tiles of softmax,
-# LayerNorm, RMSNorm, softmax backward and LayerNorm backward hold such rows
-# as 16-byte vectors and mask the missing elements of the last one
+# rows whose last 16-byte vector is partial: the held tiles of LayerNorm,
+# RMSNorm and LayerNorm backward (the operators with parameter vectors) hold
+# such rows as 16-byte vectors and mask the missing elements of the last one
 # ---------------------------------------------------------------------------
-PART_OPS = ("softmax", "layernorm", "rmsnorm", "softmax_bwd", "layernorm_bwd")
+PART_OPS = ("layernorm", "rmsnorm", "layernorm_bwd")
 
 
 def _partial_tile_cases():
@@ -287,81 +297,172 @@ def test_every_tile_partial_last_vector(op, dt, kind, block, items, p, cols):
 
 
 # ---------------------------------------------------------------------------
-# odd-length bf16 rows: the held tiles of softmax and softmax backward hold
-# them as 16-byte vectors from the 4-byte word below the row's start (odd
-# rows start in the middle of a word, even rows end in one); the shared word
-# is written by halves
+# rows that are not whole 64-byte lines, of the operators without parameter
+# vectors: their held tiles hold each row from the 64-byte boundary below its
+# start, with up to 64 - min(g, 16) bytes of the previous row in front (g the
+# lowest set bit of the row's byte length), masked and never written; the
+# vectors at the row's ends are written byte by byte where they are shared
 # ---------------------------------------------------------------------------
-ODD_ROW_OPS = ("softmax", "softmax_bwd")
+def _shift_held_vectors(cols, eb):
+    """The held vectors a shifted row needs (the library's bound, restated)."""
+    nbytes = cols * eb
+    g = 64 if nbytes % 64 == 0 else nbytes & -nbytes
+    return (nbytes + 64 - min(g, 16) + 15) // 16
 
 
-def _odd_tile_cases():
+def _slice_vectors(nv, p):
+    """16-byte vectors per slice (the library's rule, restated): ceil(nv / p)
+    rounded up to whole 64-byte lines."""
+    return ((nv + p - 1) // p + 3) // 4 * 4
+
+
+def _shift_cols(eb, cls, fits):
+    """The widest row of byte-length class `cls` ("odd": odd bf16 length,
+    "part": a multiple of 4 bytes but not of 16, "v16": of 16 but not of 64)
+    whose held vectors satisfy fits(n)."""
+    cols = 1
+    while fits(_shift_held_vectors(cols, eb)):
+        cols *= 2
+    while cols > 0:
+        nbytes = cols * eb
+        ok = {"odd": nbytes % 4 == 2, "part": nbytes % 4 == 0 and nbytes % 16 != 0,
+              "v16": nbytes % 16 == 0 and nbytes % 64 != 0}[cls]
+        if ok and fits(_shift_held_vectors(cols, eb)):
+            return cols
+        cols -= 1
+    return None
+
+
+def _shift_tile_cases():
     cases = []
     ladders = {"wave": _ladder("CREDIT_WAVE_TILES"), "wg": _ladder("CREDIT_WG_TILES"),
                "split": _ladder("CREDIT_SPLIT_TILES")}
     i = 0
-    for op in ODD_ROW_OPS:
-        for kind, tiles in ladders.items():
-            for block, items in tiles:
-                cap = block * items
-                for fill in ("ragged", "full"):
-                    ntail = (1, 3, 5, 7)[i % 4]  # elements of the last vector of an even row
-                    i += 1
-                    if kind == "split":
-                        for p in (2, 4, 8):
-                            nv = p * cap - 3 * p - 1 if fill == "ragged" else p * cap
-                            cases.append((op, kind, block, items, p, (nv - 1) * 8 + ntail))
-                    else:
-                        nv = cap - 3 if fill == "ragged" else cap
-                        cases.append((op, kind, block, items, 1, (nv - 1) * 8 + ntail))
+    for op in SHIFT_OPS:
+        for dt in W.DTYPES:
+            eb = W.ELEM_BYTES[dt]
+            classes = ("odd", "part", "v16") if dt == "bf16" else ("part", "v16")
+            for kind, tiles in ladders.items():
+                for block, items in tiles:
+                    cap = block * items
+                    for fill in ("ragged", "full"):
+                        cls = classes[i % len(classes)]
+                        i += 1
+                        if kind == "split":
+                            for p in (2, 4, 8):
+                                if fill == "full":  # the widest slice fills the tile
+                                    fits = lambda n, p=p: (n + p - 1) // p <= cap
+                                else:
+                                    fits = lambda n, p=p: n <= p * cap - 3 * p - 1
+                                cases.append((op, dt, kind, block, items, p, _shift_cols(eb, cls, fits)))
+                        else:
+                            lim = cap if fill == "full" else cap - 3
+                            cases.append((op, dt, kind, block, items, 1, _shift_cols(eb, cls, lambda n: n <= lim)))
     return cases
 
 
-ODD_TILE_CASES = _odd_tile_cases()
+SHIFT_TILE_CASES = _shift_tile_cases()
 
 
-@pytest.mark.parametrize("op,kind,block,items,p,cols", ODD_TILE_CASES,
-                         ids=["%s-%s%dx%d-p%d-c%d" % c for c in ODD_TILE_CASES])
-def test_every_tile_odd_length_bf16(op, kind, block, items, p, cols):
-    # Rows of both parities (an odd row count), owners looping over rows as in
-    # test_every_tile; the row's first and last elements sit at a different
-    # thread and item in each case.
+@pytest.mark.parametrize("op,dt,kind,block,items,p,cols", SHIFT_TILE_CASES,
+                         ids=["%s-%s-%s%dx%d-p%d-c%d" % c for c in SHIFT_TILE_CASES])
+def test_every_tile_shifted(op, dt, kind, block, items, p, cols):
+    # An odd row count and owners looping over rows as in test_every_tile: the
+    # rows start at every offset their byte length allows inside a 64-byte
+    # line, so the row's first and last elements sit at a different thread,
+    # item and byte in each row; "full" cases need every held vector of the
+    # tile (or slice) for the rows with the largest offset.
     C = _lib()
     rows = {"wave": 1101, "wg": 301, "split": 301}[kind]
     if cols * rows > 24_000_000:
         rows = max(5, 24_000_000 // cols) | 1
-    w = W.custom(op, "bf16", rows, cols, seed=zlib.crc32(("odd%s%s%d%d%d%d" % (op, kind, block, items, p, cols)).encode()) % 10000,
+    w = W.custom(op, dt, rows, cols,
+                 seed=zlib.crc32(("shift%s%s%s%d%d%d%d" % (op, dt, kind, block, items, p, cols)).encode()) % 10000,
                  x_dist="scaled_shifted", x_scale=3.0, x_shift=0.5)
     inp = W.generate(w)
     path = C.PATH_SPLIT_ROW if kind == "split" else C.PATH_SINGLE_WG
     plan = C.Plan.make(path, p, block, items, 16, wgs_per_cu=1)
-    if _tile_excluded(op, kind, block, items, dt="bf16"):
+    if _tile_excluded(op, kind, block, items, dt=dt):
         with pytest.raises(C.CreditError) as ei:
             _run(inp, plan=plan)
         assert ei.value.status == 2
         return
     out = _run(inp, plan=plan)
-    _check(inp, out, "odd-length tile %s %dx%d p=%d %s cols=%d" % (kind, block, items, p, op, cols))
+    _check(inp, out, "shifted tile %s %dx%d p=%d %s %s cols=%d" % (kind, block, items, p, op, dt, cols))
 
 
-@pytest.mark.parametrize("cols", [1, 7, 12291])
+@pytest.mark.parametrize("op,dt", [(op, dt) for op in SHIFT_OPS for dt in W.DTYPES])
+def test_shifted_tile_one_vector_short_is_refused(op, dt):
+    # a tile that holds the row but not the row with its largest offset in
+    # front is refused before launch
+    C = _lib()
+    eb = W.ELEM_BYTES[dt]
+    cols = _shift_cols(eb, "part", lambda n: n <= 256 + 1) if dt == "f32" else _shift_cols(eb, "odd", lambda n: n <= 257)
+    assert _shift_held_vectors(cols, eb) == 257
+    w = W.custom(op, dt, 3, cols, seed=3)
+    inp = W.generate(w)
+    with pytest.raises(C.CreditError) as ei:
+        _run(inp, plan=C.Plan.make(C.PATH_SINGLE_WG, 1, 64, 4, 16))
+    assert ei.value.status == 4
+
+
+@pytest.mark.parametrize("cols", [1, 5, 100, 1001, 1004, 30001])
+@pytest.mark.parametrize("xoff,yoff", [(16, 0), (48, 32), (0, 16)])
+@pytest.mark.parametrize("op,dt", [(op, dt) for op in SHIFT_OPS for dt in W.DTYPES])
+def test_shifted_rows_with_offset_bases(op, dt, xoff, yoff, cols):
+    # x (and dy) and y start 0-48 bytes into a 64-byte line, differently: the
+    # offset of each row is taken from x's address, the first rows (less than
+    # 64 bytes into x) are held from the tensor's start, and y's held spans
+    # are then 16-byte but not line aligned.  Single and split paths.
+    import torch
+    C = _lib()
+    w = W.custom(op, dt, 19, cols, seed=cols + xoff + 3 * yoff, x_dist="scaled_shifted", x_scale=3.0, x_shift=0.5)
+    inp = W.generate(w)
+    for path, p in (("single", 0), ("split", 2)):
+        t = _device_operands(inp)
+
+        def moved(a, off):
+            if a is None:
+                return None
+            nb = a.numel() * a.element_size()
+            buf = torch.empty(nb + 128, dtype=torch.uint8, device="cuda")
+            base = (-buf.data_ptr()) % 64 + off
+            v = buf[base: base + nb].view(a.dtype).view(a.shape)
+            v.copy_(a)
+            return v
+
+        for k in ("x", "dy"):
+            t[k] = moved(t.get(k), xoff)
+        t["y"] = moved(t["y"], yoff)
+        assert t["x"].data_ptr() % 64 == xoff and t["y"].data_ptr() % 64 == yoff
+        nvh = _shift_held_vectors(cols, W.ELEM_BYTES[dt])
+        if path == "split" and nvh <= _slice_vectors(nvh, 2):
+            continue  # too narrow to split
+        out = _run(inp, path, p, t=t)
+        _check(inp, out, "offset bases x+%d y+%d %s %s cols=%d %s" % (xoff, yoff, op, dt, cols, path))
+
+
+@pytest.mark.parametrize("dt,cols", [("bf16", 1), ("bf16", 7), ("bf16", 12291), ("f32", 3), ("f32", 1004),
+                                     ("f32", 12291)])
 @pytest.mark.parametrize("path,p", [("single", 0), ("split", 2), ("split", 8), ("reread", 0)])
 @pytest.mark.parametrize("op,alias", [("softmax", "x"), ("softmax_bwd", "x"), ("softmax_bwd", "dy")])
-def test_odd_length_bf16_in_place_and_boundary_nan(op, alias, path, p, cols):
+def test_shifted_rows_in_place_and_boundary_nan(op, alias, dt, path, p, cols):
     # The output overwrites an input while the neighbouring rows' owners read
-    # the 4-byte words they share with this row; then NaN in the first and
+    # the 64-byte lines they share with this row; then NaN in the first and
     # last elements of some rows (x, and dy for the backward operator) must
     # stay in those rows.
     C = _lib()
-    if path == "split" and (cols + 7) // 8 < p:
+    eb = W.ELEM_BYTES[dt]
+    nvh = _shift_held_vectors(cols, eb)
+    if path == "split" and nvh <= (p - 1) * _slice_vectors(nvh, p):
         pytest.skip("too narrow to split %d ways" % p)
-    w = W.custom(op, "bf16", 37, cols, seed=cols + 3, x_dist="scaled_shifted", x_scale=3.0, x_shift=0.5)
+    w = W.custom(op, dt, 37, cols, seed=cols + 3, x_dist="scaled_shifted", x_scale=3.0, x_shift=0.5)
     inp = W.generate(w)
     t = _device_operands(inp)
     t["y"] = t[alias]
     out = _run(inp, path, p, t=t)
-    _check(inp, out, "odd in-place y=%s %s %s P=%d cols=%d" % (alias, op, path, p, cols))
-    nan = np.uint16(0x7FC0)
+    _check(inp, out, "shifted in-place y=%s %s %s %s P=%d cols=%d" % (alias, op, dt, path, p, cols))
+    nan = np.uint16(0x7FC0) if dt == "bf16" else np.float32("nan")
     bad = (5, 6, 20)
     inp.x[5, 0] = nan
     inp.x[6, cols - 1] = nan
@@ -371,8 +472,7 @@ def test_odd_length_bf16_in_place_and_boundary_nan(op, alias, path, p, cols):
     else:
         inp.x[20, cols - 1] = nan
     y = _run(inp, path, p)["y"]
-    yf = y.astype(np.uint32) << 16
-    isnan = np.isnan(yf.view(np.float32))
+    isnan = np.isnan((y.astype(np.uint32) << 16).view(np.float32)) if dt == "bf16" else np.isnan(y)
     for r in range(w.rows):
         if r in bad:
             assert isnan[r].all(), "row %d should be NaN" % r
@@ -380,7 +480,7 @@ def test_odd_length_bf16_in_place_and_boundary_nan(op, alias, path, p, cols):
             assert not isnan[r].any(), "NaN leaked into row %d" % r
 
 
-@pytest.mark.parametrize("op", ODD_ROW_OPS)
+@pytest.mark.parametrize("op", SHIFT_OPS)
 @pytest.mark.parametrize("path,p", [("single", 0), ("split", 4)])
 def test_odd_length_bf16_word_after_the_tensor_is_masked(op, path, p):
     # rows * cols odd: the last row ends in the middle of a 4-byte word whose

@@ -453,14 +453,19 @@ credit_status_t resolve_plan(int op, int dt, int64_t cols, const credit_plan_t &
 {
     if (plan.path < CREDIT_PATH_SINGLE_WG || plan.path > CREDIT_PATH_REREAD)
         return CREDIT_ERR_INVALID_ARG;
-    // a partial row (byte length a multiple of 4, not of 16) and an
-    // odd-length bf16 row of the softmax family are held as 16-byte vectors
-    // (held_row_kind) and reread by element
-    const int part = plan.path != CREDIT_PATH_REREAD ? held_row_kind(op, dt, cols) : 0;
+    // a partial row (byte length a multiple of 4, not of 16) of an operator
+    // with parameters, and a row of the others that is not a multiple of 64
+    // bytes, are held as 16-byte vectors (held_row_kind) and reread by element
+    // the LDS tier holds rows of whole 16-byte vectors as they are
+    if (plan.lds_items < 0)
+        return CREDIT_ERR_INVALID_ARG;
+    const int part = plan_row_kind(op, dt, cols, plan.path, plan.lds_items);
     const int vb = path_vec_bytes(op, dt, cols, plan.path);
     if (plan.vec_bytes != 0 && plan.vec_bytes != vb)
         return CREDIT_ERR_ILLEGAL_PATH;
-    const int64_t nv = (cols * elem_bytes(dt) + vb - 1) / vb;
+    const int64_t nv = plan.lds_items > 0 ? lds_row_vectors(dt, cols)
+                       : plan.path != CREDIT_PATH_REREAD ? held_vectors(op, dt, cols)
+                                                         : (cols * elem_bytes(dt) + vb - 1) / vb;
     int kind = 0;
     int64_t need = nv;
     switch (plan.path) {
@@ -471,7 +476,7 @@ credit_status_t resolve_plan(int op, int dt, int64_t cols, const credit_plan_t &
         kind = kKindSplit;
         if (plan.split_p != 2 && plan.split_p != 4 && plan.split_p != 8)
             return CREDIT_ERR_ILLEGAL_PATH;
-        need = (nv + plan.split_p - 1) / plan.split_p;
+        need = slice_vectors(nv, plan.split_p, vb);
         if (need * (plan.split_p - 1) >= nv)
             return CREDIT_ERR_ILLEGAL_PATH;
         break;
@@ -482,10 +487,8 @@ credit_status_t resolve_plan(int op, int dt, int64_t cols, const credit_plan_t &
     default:
         return CREDIT_ERR_INVALID_ARG;
     }
-    if (plan.lds_items < 0)
-        return CREDIT_ERR_INVALID_ARG;
     // the LDS tier: workgroup tiles of paths 1 and 2, rows of whole 16-byte vectors
-    if (plan.lds_items > 0 && (kind == kKindWave || kind == kKindReread || part != 0 || vb != 16))
+    if (plan.lds_items > 0 && (kind == kKindWave || kind == kKindReread || nv == 0 || vb != 16))
         return CREDIT_ERR_ILLEGAL_PATH;
     const KernelEntry *k = find_kernel(kind, op, dt, vb, plan.block_threads, plan.items, part, plan.lds_items);
     if (k == nullptr)
@@ -547,7 +550,7 @@ credit_status_t run_plan_checked(int op, const credit_operands_t &t, int64_t row
         std::fprintf(stderr, "[credit] op=%d dt=%d rows=%lld cols=%lld path=%d p=%d block=%d items=%d lds=%d vb=%d%s%s\n",
                      op, dt, static_cast<long long>(rows), static_cast<long long>(cols), plan.path, plan.split_p,
                      plan.block_threads, plan.items, plan.lds_items, k->vb,
-                     k->part == 1 ? " (partial last vector)" : (k->part == 2 ? " (odd bf16 row)" : ""),
+                     k->part == 1 ? " (partial last vector)" : (k->part == 2 ? " (shifted row)" : ""),
                      control ? " (control)" : "");
     if (kind == kKindSplit)
         return launch_split(k, a, plan.split_p, stats_per_partial(op), plan.wgs_per_cu, s, ev, fixed);

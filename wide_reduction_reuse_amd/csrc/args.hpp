@@ -76,6 +76,34 @@ struct SplitArgs {
 // The exchange words of a scratch.
 __host__ __device__ inline uint64_t *scratch_slots(SplitCtl *ctl) { return reinterpret_cast<uint64_t *>(ctl + 1); }
 
+// Rows held from the 64-byte boundary at or below their first byte (the
+// kernels' SHIFT mode) begin with up to shift_max_bytes of the previous row:
+// row r of a tensor whose base is 16-byte aligned starts at
+// (base + r * row_bytes) mod 64 bytes into a 64-byte line, a multiple of
+// g = the lowest set bit of row_bytes (at most 64) plus a multiple of 16 from
+// the base, so at most 64 - min(g, 16).  shift_held_vectors: the 16-byte
+// vectors that any row's held span covers, for eb-byte elements.
+__host__ __device__ constexpr int shift_max_bytes(int64_t row_bytes)
+{
+    const int64_t g = row_bytes % 64 == 0 ? 64 : (row_bytes & -row_bytes);
+    return 64 - static_cast<int>(g < 16 ? g : 16);
+}
+__host__ __device__ constexpr int64_t shift_held_vectors(int64_t cols, int eb)
+{
+    const int64_t e = 16 / eb;
+    return (cols + shift_max_bytes(cols * eb) / eb + e - 1) / e;
+}
+
+// Vectors per slice of a row of nv held vectors of vb bytes split p ways:
+// ceil(nv / p) rounded up to whole 64-byte lines, so that every slice of a
+// line-aligned row starts on a line boundary (the last slice takes the rest).
+__host__ __device__ constexpr int64_t slice_vectors(int64_t nv, int p, int vb)
+{
+    const int64_t q = (nv + p - 1) / p;
+    const int64_t line = vb >= 64 ? 1 : 64 / vb;
+    return (q + line - 1) / line * line;
+}
+
 constexpr int kMaxSplit = 8;
 constexpr int kWaveRowsPerWg = 4;  // path 1, wave-per-row: rows per 256-thread workgroup
 

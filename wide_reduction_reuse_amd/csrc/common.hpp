@@ -124,19 +124,33 @@ __device__ __forceinline__ void buf_store(const RawVec<VB> &v, rsrc_t r, uint32_
     }
 }
 
-// Stores of part of a 16-byte vector (odd-length bf16 rows, whose first or
-// last 4-byte word is shared with the neighbouring row): its words 1..3, and
-// one 16-bit half of a word.
-__device__ __forceinline__ void buf_store_words123(const RawVec<16> &v, rsrc_t r, uint32_t voff)
+// Bytes [from, to) of a vector (0 <= from <= to <= VB, VB a multiple of 4):
+// its 4-byte words that lie wholly inside as word stores, the other bytes
+// one at a time.  Used for the vectors at the ends of rows whose first or
+// last word is shared with the neighbouring row (which writes the rest of
+// that word).
+template <int VB>
+__device__ __forceinline__ void buf_store_bytes(const RawVec<VB> &v, rsrc_t r, uint32_t voff, int from, int to)
 {
-    typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
-    const u32x3 w = {v.w[1], v.w[2], v.w[3]};
-    __builtin_amdgcn_raw_buffer_store_b96(w, r, static_cast<int>(voff), 0, kStreamStore);
-}
-__device__ __forceinline__ void buf_store_half(uint32_t bits16, rsrc_t r, uint32_t voff)
-{
-    __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(bits16), r, static_cast<int>(voff), 0,
-                                          kStreamStore);
+    static_assert(VB % 4 == 0, "vectors of whole words");
+#pragma unroll
+    for (int j = 0; j < VB / 4; ++j) {
+        uint32_t w;
+        if constexpr (VB >= 8)
+            w = v.w[j];
+        else
+            w = v.w;
+        const uint32_t o = voff + 4u * static_cast<uint32_t>(j);
+        if (from <= 4 * j && 4 * j + 4 <= to) {
+            __builtin_amdgcn_raw_buffer_store_b32(w, r, static_cast<int>(o), 0, kStreamStore);
+        } else {
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+                if (from <= 4 * j + b && 4 * j + b < to)
+                    __builtin_amdgcn_raw_buffer_store_b8(static_cast<unsigned char>(w >> (8 * b)), r,
+                                                         static_cast<int>(o + b), 0, kStreamStore);
+        }
+    }
 }
 
 // Make a value the compiler treats as per-lane known to be wave-uniform.

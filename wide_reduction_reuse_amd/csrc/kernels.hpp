@@ -380,31 +380,27 @@ constexpr bool rolls()
     return OWNER == kOwnerSlice && NI == 1 && MODE != kParamDirect;
 }
 
-// The output side of an ODD row (an odd-length bf16 row, held from the
-// 4-byte word below its start): either its first or its last word is shared
-// with the neighbouring row, and only this row's half of that word may be
-// written.  The store descriptor excludes a shared last word; `full` also
-// covers it.  head: the thread's vector 0 starts with the shared first word
-// (the row begins at its upper half).  ktail, dtail: the thread's vector and
-// word whose lower half is the row's last element, in a shared last word
-// (ktail = -1: none).
-struct OddOut {
-    rsrc_t full;
-    int ktail;
-    int dtail;
-    bool head;
+// The output side of a SHIFT row (see shift_geom) for one thread: its
+// vector 0 may begin with hb output bytes of the previous row, and its vector
+// kpart (-1: none) holds the row's last element, the row's part of it being
+// its first tb output bytes.  Those two vectors are written byte-exactly (the
+// bytes outside the row belong to the neighbouring rows' owners).
+struct ShiftOut {
+    int hb;
+    int kpart;
+    int tb;
 };
 
 // Apply h to the held tile and write it out; dst, and the parameter
 // descriptors, cover the same columns (the row or slice).  When rolling,
 // vector k of the next row (`next`, a zero-length descriptor when there is
 // none: its loads return zero without touching memory) is loaded into the
-// register that vector k of this row leaves free.  ODD: the shared words of
-// an odd-length bf16 row are written one half at a time (see OddOut).
-template <OpKind OP, class T, int VB, int IT, int W, int OWNER, bool ODD = false>
+// register that vector k of this row leaves free.  SHIFT: the vectors at the
+// row's ends are written byte-exactly (see ShiftOut).
+template <OpKind OP, class T, int VB, int IT, int W, int OWNER, bool SHIFT = false>
 __device__ __forceinline__ void store_tile(Tile<T, VB, IT> (&t)[OpTraits<OP>::kIn], rsrc_t dst,
                                            const ParamCache<OP, T, VB, IT, W, OWNER> &pc, int pos, const Coef &c,
-                                           const Srcs<OpTraits<OP>::kIn> &next, const OddOut *oo = nullptr)
+                                           const Srcs<OpTraits<OP>::kIn> &next, const ShiftOut *so = nullptr)
 {
     using Op = OpTraits<OP>;
     constexpr int NI = Op::kIn;
@@ -441,19 +437,12 @@ __device__ __forceinline__ void store_tile(Tile<T, VB, IT> (&t)[OpTraits<OP>::kI
             for (int i = 0; i < NI; ++i)
                 in[i] = t[i].v[k];
             const RawVec<VBO> ov = apply_vec<OP, T, VB, RAW>(in, g, b, vec_coef<OP, T, IT>(c, k));
-            if constexpr (ODD) {
-                static_assert(VBO == 16 && NP == 0, "ODD rows: 16-byte bf16 vectors, no parameters");
-                if (k == 0 && oo->head) {
-                    buf_store_half(ov.w[0] >> 16, dst, off + 2u);
-                    buf_store_words123(ov, dst, off + 4u);
-                } else {
+            if constexpr (SHIFT) {
+                static_assert(NP == 0, "SHIFT rows: operators without parameters");
+                if ((k == 0 && so->hb > 0) || k == so->kpart)
+                    buf_store_bytes<VBO>(ov, dst, ooff, k == 0 ? so->hb : 0, k == so->kpart ? so->tb : VBO);
+                else
                     buf_store<VBO, kStreamStore>(ov, dst, ooff);
-                }
-                if (k == oo->ktail) {
-                    const int d = oo->dtail;
-                    const uint32_t wv = d == 0 ? ov.w[0] : (d == 1 ? ov.w[1] : (d == 2 ? ov.w[2] : ov.w[3]));
-                    buf_store_half(wv, oo->full, off + 4u * static_cast<uint32_t>(d));
-                }
             } else {
                 buf_store<VBO, kStreamStore>(ov, dst, ooff);
             }
@@ -555,70 +544,75 @@ __device__ __forceinline__ rsrc_t row_span(const void *base, int64_t row, int64_
     }
 }
 
-// ODD rows: bf16 rows of odd length, held as 16-byte vectors from the
-// 4-byte word below their start.  Row r starts s = (r * cols) mod 2 elements
-// into a word, and held position p is row element p - s.  The held span is
-// 2 * cols + 2 bytes, from the word below the row's start to the end of the
-// word holding its last element; for s = 0 that last word also holds the next
-// row's first element (or, for the last row, the 2 bytes after the tensor,
-// inside the same 4-byte word: read, masked, never written).  With
-// store = true the span leaves out a shared last word (s = 0); a shared first
-// word (s = 1) is in every span and store_tile writes it by halves.
-__device__ __forceinline__ int odd_shift(int64_t row, int64_t cols)
+// SHIFT rows: a row whose start is not 64-byte aligned is held from the
+// 64-byte boundary below its first byte, so that every wave's run of 16-byte
+// vectors covers whole 64-byte lines (on MI355X, rows that start inside a
+// line streamed 15-30% slower, in loads and stores alike).  Row r begins
+// s elements into its held span, the last s elements of row r - 1 (masked in
+// the reduction, never written); s is taken from x's address, and dy and y,
+// whose bases are 16-byte aligned too, use the same s (their held spans then
+// start 16-byte aligned, and line-aligned when their bases are congruent to
+// x's modulo 64).  A row that starts less than 64 bytes into the tensor is
+// held from the tensor's start instead (s = its offset in elements), so no
+// access precedes the tensor.  The held span ends with the 4-byte word that
+// holds the row's last element (its other bytes, when it has any, are the
+// next row's: read, masked, never written; after the tensor's last row they
+// lie inside the same word).
+struct ShiftRow {
+    int s;        // elements of the previous row in front of the row
+    int64_t nv;   // 16-byte vectors of the held span
+    int ntail;    // elements of its last vector up to the row's end (1..E)
+};
+
+template <int EB, int E>
+__device__ __forceinline__ ShiftRow shift_geom(const void *x, int64_t row, int64_t cols)
 {
-    return static_cast<int>((row * cols) & 1);
+    const int64_t first = row * cols;
+    const uintptr_t at = reinterpret_cast<uintptr_t>(x) + static_cast<uintptr_t>(first * EB);
+    int64_t s = static_cast<int64_t>(at & 63u) / EB;
+    s = s < first ? s : first;
+    ShiftRow g;
+    g.s = static_cast<int>(s);
+    const int64_t n = s + cols;
+    g.nv = (n + E - 1) / E;
+    g.ntail = static_cast<int>(n - E * (g.nv - 1));
+    return g;
 }
 
-template <int VB>
-__device__ __forceinline__ rsrc_t odd_span(const void *base, int64_t row, int64_t cols, int64_t first, int64_t nvec,
-                                           bool store)
+// Vectors [first, first + nvec) of row `row`'s held span in a tensor of
+// EBT-byte elements and VBT-byte vectors.
+template <int VBT, int EBT>
+__device__ __forceinline__ rsrc_t shift_span(const void *base, int64_t row, int64_t cols, int s, int64_t first,
+                                             int64_t nvec)
 {
-    const int s = odd_shift(row, cols);
-    const int64_t lo = (row * cols - s) * 2;
-    const int64_t len = (store && s == 0) ? 2 * cols - 2 : 2 * cols + 2;
-    int64_t n = len - first * VB;
-    n = n < nvec * VB ? n : nvec * VB;
+    const int64_t lo = (row * cols - s) * EBT;
+    const int64_t len = ((s + cols) * EBT + 3) & ~INT64_C(3);
+    int64_t n = len - first * VBT;
+    n = n < nvec * VBT ? n : nvec * VBT;
     n = n > 0 ? n : 0;
-    const uintptr_t p = reinterpret_cast<uintptr_t>(base) + static_cast<uintptr_t>(lo + first * VB);
+    const uintptr_t p = reinterpret_cast<uintptr_t>(base) + static_cast<uintptr_t>(lo + first * VBT);
     return make_rsrc(reinterpret_cast<const void *>(p), static_cast<uint32_t>(n));
 }
 
 // The row inputs (x, and dy for two-input operators): `nvec` vectors from
-// vector `first` of row `row` (nv vectors per row; PEB as for row_span; ODD
-// rows as for odd_span).
-template <OpKind OP, int VB, int PEB = 0, bool ODD = false>
+// vector `first` of row `row` (nv vectors per row; PEB as for row_span; SHIFT
+// rows as for shift_span, `sh` elements of the previous row in front).
+template <OpKind OP, int VB, int PEB = 0, bool SHIFT = false>
 __device__ __forceinline__ Srcs<OpTraits<OP>::kIn> row_srcs(const RowArgs &a, int64_t row, int64_t nv,
-                                                            int64_t first, int64_t nvec)
+                                                            int64_t first, int64_t nvec, int sh = 0)
 {
     Srcs<OpTraits<OP>::kIn> s;
-    if constexpr (ODD) {
-        s.r[0] = odd_span<VB>(a.x, row, a.cols, first, nvec, false);
+    if constexpr (SHIFT) {
+        static_assert(PEB > 0, "SHIFT rows are PART rows");
+        s.r[0] = shift_span<VB, PEB>(a.x, row, a.cols, sh, first, nvec);
         if constexpr (OpTraits<OP>::kIn >= 2)
-            s.r[1] = odd_span<VB>(a.dy, row, a.cols, first, nvec, false);
+            s.r[1] = shift_span<VB, PEB>(a.dy, row, a.cols, sh, first, nvec);
     } else {
         s.r[0] = row_span<VB, PEB>(a.x, row, a.cols, nv, first, nvec);
         if constexpr (OpTraits<OP>::kIn >= 2)
             s.r[1] = row_span<VB, PEB>(a.dy, row, a.cols, nv, first, nvec);
     }
     return s;
-}
-
-// Per-row state of an ODD row for the thread at slice position `pos` of a
-// slice starting at vector v0 (kpart already set): the last vector's valid
-// elements, the masked first element, and the output halves (OddOut).
-template <int E>
-__device__ __forceinline__ OddOut odd_row(LocalOdd &loc, const void *y, int64_t row, int64_t cols, int64_t nv,
-                                          int64_t v0, int64_t ns, int pos)
-{
-    const int s = odd_shift(row, cols);
-    loc.ntail = static_cast<int>(cols + s - E * (nv - 1));
-    loc.khead = (s != 0 && v0 == 0 && pos == 0) ? 0 : -1;
-    OddOut oo;
-    oo.full = odd_span<16>(y, row, cols, v0, ns, false);
-    oo.ktail = s == 0 ? loc.kpart : -1;
-    oo.dtail = (loc.ntail - 1) / 2;
-    oo.head = loc.khead == 0;
-    return oo;
 }
 
 // The thread's index (among its vectors k, at slice positions pos + k * G) of
@@ -631,6 +625,24 @@ __device__ __forceinline__ int partial_index(int64_t ns, int pos, bool last)
     if (!last || d < 0 || d % G != 0 || d / G >= IT)
         return -1;
     return static_cast<int>(d / G);
+}
+
+// Per-row state of a SHIFT row for the thread at slice position `pos` of a
+// slice that starts at held vector v0 and holds ns of the row's held
+// vectors: the masks of its first and last vectors (LocalShift) and their
+// output bytes (ShiftOut, OEB output bytes per element).
+template <int IT, int E, int OEB>
+__device__ __forceinline__ ShiftOut shift_row(LocalShift &loc, const ShiftRow &g, int64_t v0, int64_t ns, int pos)
+{
+    loc.ntail = g.ntail;
+    loc.kpart = partial_index<IT, kWave>(ns, pos, v0 + ns == g.nv);
+    const int64_t h = g.s - (v0 + pos) * E;
+    loc.hcount = h <= 0 ? 0 : (h >= E ? E : static_cast<int>(h));
+    ShiftOut so;
+    so.hb = loc.hcount * OEB;
+    so.kpart = loc.kpart;
+    so.tb = loc.ntail * OEB;
+    return so;
 }
 
 // The per-row output of `row` (the quantization scale; LayerNorm backward's
@@ -746,52 +758,65 @@ __device__ __forceinline__ typename OpTraits<OP>::Partial merge_tiers(const type
 // of the grid handles rows w, w + W, w + 2W, ... (W waves in the grid).  No
 // barrier on the row: the wave reduction is the row reduction.
 // ---------------------------------------------------------------------------
-// PART: rows whose last vector is partial (see row_span).  ODD (with PART):
-// odd-length bf16 rows held from the word below their start (see odd_span).
-template <OpKind OP, class T, int VB, int IT, bool PART = false, bool ODD = false>
+// PART: rows whose last vector is partial (see row_span).  SHIFT (with
+// PART): rows held from the 64-byte boundary below their start (see
+// shift_geom), whose held vector count varies from row to row.
+template <OpKind OP, class T, int VB, int IT, bool PART = false, bool SHIFT = false>
 __global__ __launch_bounds__(kWave *kWaveRowsPerWg) void single_wave_kernel(RowArgs a)
 {
     using Op = OpTraits<OP>;
     using PC = ParamCache<OP, T, VB, IT, kWave, kOwnerWaves>;
-    using Loc = std::conditional_t<ODD, LocalOdd, std::conditional_t<PART, LocalPart, Local>>;
-    constexpr int E = VB / StorageTraits<T>::kBytes;
+    using Loc = std::conditional_t<SHIFT, LocalShift, std::conditional_t<PART, LocalPart, Local>>;
+    constexpr int EB = StorageTraits<T>::kBytes;
+    constexpr int E = VB / EB;
     constexpr int VBO = out_vb<OP, T, VB>();
-    constexpr int PEB = PART ? StorageTraits<T>::kBytes : 0;
-    static_assert(!PART || VBO == VB, "PART rows need outputs of the input's element size");
-    static_assert(!ODD || (PART && VB == 16 && StorageTraits<T>::kBytes == 2 && Op::kParams == 0),
-                  "ODD rows: bf16, 16-byte vectors, operators without parameters");
+    constexpr int OEB = StorageTraits<OutT<OP, T>>::kBytes;
+    constexpr int PEB = PART ? EB : 0;
+    static_assert(!PART || SHIFT || VBO == VB, "PART rows need outputs of the input's element size");
+    static_assert(!SHIFT || (PART && VB == 16 && Op::kParams == 0),
+                  "SHIFT rows: 16-byte vectors, operators without parameters");
     __shared__ RawVec<VB> lds_params[param_lds_vectors<OP, VB, IT, kWave, kOwnerWaves>()];
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t nv = PART ? (a.cols + E - 1) / E : a.cols / E;
     const int64_t waves = static_cast<int64_t>(gridDim.x) * kWaveRowsPerWg;
     int64_t row = uniform(static_cast<int64_t>(blockIdx.x) * kWaveRowsPerWg + threadIdx.x / kWave);
+    ShiftRow g{};
+    if constexpr (SHIFT)
+        g = shift_geom<EB, E>(a.x, row, a.cols);
     Tile<T, VB, IT> t[Op::kIn];
-    load_tile<T, VB, IT, kWave>(t, row_srcs<OP, VB, PEB, ODD>(a, row, nv, 0, row < a.rows ? nv : 0), lane);
+    load_tile<T, VB, IT, kWave>(t, row_srcs<OP, VB, PEB, SHIFT>(a, row, nv, 0, row < a.rows ? (SHIFT ? g.nv : nv) : 0,
+                                                                g.s), lane);
     PC pc;
     pc.init(row_span<VB, PEB>(a.gamma, 0, a.cols, nv, 0, nv), row_span<VB, PEB>(a.beta, 0, a.cols, nv, 0, nv),
             lane, lds_params, threadIdx.x, kWave * kWaveRowsPerWg);
     if constexpr (PC::kMode == kParamLds)
         __syncthreads();
-    const int kv = count_valid<IT, kWave>(nv, lane);
+    int kv = count_valid<IT, kWave>(nv, lane);
     Loc loc0;
-    if constexpr (PART) {
+    if constexpr (PART && !SHIFT) {
         loc0.ntail = static_cast<int>(a.cols % E);
-        loc0.kpart = partial_index<IT, kWave>(nv, lane, ODD || loc0.ntail != 0);
+        loc0.kpart = partial_index<IT, kWave>(nv, lane, loc0.ntail != 0);
     }
     for (; row < a.rows; row += waves) {
         const int64_t next = row + waves;
         Loc loc = loc0;
-        OddOut oo;
-        if constexpr (ODD)
-            oo = odd_row<E>(loc, a.y, row, a.cols, nv, 0, nv, lane);
+        ShiftOut so{};
+        ShiftRow gn{};
+        if constexpr (SHIFT) {
+            so = shift_row<IT, E, OEB>(loc, g, 0, g.nv, lane);
+            kv = count_valid<IT, kWave>(g.nv, lane);
+            gn = shift_geom<EB, E>(a.x, next, a.cols);
+        }
         const auto wp = tile_partial<OP, T, VB, IT, kWave, kOwnerWaves>(t, kv, pc, lane, loc);
         const Coef c = Op::template finalize<T>(wp, loc, a.cols, a.eps);
         store_row_value<OP>(a, row, c, lane == 0);
-        const auto nsrc = row_srcs<OP, VB, PEB, ODD>(a, next, nv, 0, next < a.rows ? nv : 0);
-        const rsrc_t dst = ODD ? odd_span<VBO>(a.y, row, a.cols, 0, nv, true)
-                               : row_span<VBO, PEB>(a.y, row, a.cols, nv, 0, nv);
-        store_tile<OP, T, VB, IT, kWave, kOwnerWaves, ODD>(t, dst, pc, lane, c, nsrc, &oo);
+        const auto nsrc =
+            row_srcs<OP, VB, PEB, SHIFT>(a, next, nv, 0, next < a.rows ? (SHIFT ? gn.nv : nv) : 0, gn.s);
+        const rsrc_t dst = SHIFT ? shift_span<VBO, OEB>(a.y, row, a.cols, g.s, 0, g.nv)
+                                 : row_span<VBO, PEB>(a.y, row, a.cols, nv, 0, nv);
+        store_tile<OP, T, VB, IT, kWave, kOwnerWaves, SHIFT>(t, dst, pc, lane, c, nsrc, &so);
         load_next<OP, T, VB, IT, kWave, kOwnerWaves>(t, nsrc, lane);
+        g = gn;
     }
 }
 
@@ -801,19 +826,21 @@ __global__ __launch_bounds__(kWave *kWaveRowsPerWg) void single_wave_kernel(RowA
 // ---------------------------------------------------------------------------
 // LT > 0: the LDS tier (lds_load_reduce); rows of whole 16-byte vectors,
 // at most BLOCK * (IT + LT) of them (the host checks).
-template <OpKind OP, class T, int VB, int BLOCK, int IT, bool PART = false, bool ODD = false, int LT = 0>
+template <OpKind OP, class T, int VB, int BLOCK, int IT, bool PART = false, bool SHIFT = false, int LT = 0>
 __global__ __launch_bounds__(BLOCK) void single_wg_kernel(RowArgs a)
 {
     using Op = OpTraits<OP>;
     using PC = ParamCache<OP, T, VB, IT, BLOCK, kOwnerRow>;
-    using Loc = std::conditional_t<ODD, LocalOdd, std::conditional_t<PART, LocalPart, Local>>;
-    constexpr int E = VB / StorageTraits<T>::kBytes;
-    constexpr int PEB = PART ? StorageTraits<T>::kBytes : 0;
+    using Loc = std::conditional_t<SHIFT, LocalShift, std::conditional_t<PART, LocalPart, Local>>;
+    constexpr int EB = StorageTraits<T>::kBytes;
+    constexpr int E = VB / EB;
+    constexpr int PEB = PART ? EB : 0;
     constexpr int NW = BLOCK / kWave;
     constexpr int VBO = out_vb<OP, T, VB>();
+    constexpr int OEB = StorageTraits<OutT<OP, T>>::kBytes;
     constexpr bool kLds = LT > 0;
-    static_assert(!ODD || (PART && VB == 16 && StorageTraits<T>::kBytes == 2 && Op::kParams == 0),
-                  "ODD rows: bf16, 16-byte vectors, operators without parameters");
+    static_assert(!SHIFT || (PART && VB == 16 && Op::kParams == 0),
+                  "SHIFT rows: 16-byte vectors, operators without parameters");
     static_assert(!kLds || (!PART && VB == 16), "the LDS tier holds rows of whole 16-byte vectors");
     __shared__ typename Op::Partial sh[NW];
     __shared__ RawVec<VB> lds_params[param_lds_vectors<OP, VB, IT, BLOCK, kOwnerRow>()];
@@ -825,25 +852,32 @@ __global__ __launch_bounds__(BLOCK) void single_wg_kernel(RowArgs a)
     const int64_t nreg = kLds ? min(nv, static_cast<int64_t>(BLOCK) * IT) : nv;
     const int64_t nl = nv - nreg;
     int64_t row = blockIdx.x;
+    ShiftRow g{};
+    if constexpr (SHIFT)
+        g = shift_geom<EB, E>(a.x, row, a.cols);
     Tile<T, VB, IT> t[Op::kIn];
-    load_tile<T, VB, IT, kWave>(t, row_srcs<OP, VB, PEB, ODD>(a, row, nv, 0, nreg), pos);
+    load_tile<T, VB, IT, kWave>(t, row_srcs<OP, VB, PEB, SHIFT>(a, row, nv, 0, SHIFT ? g.nv : nreg, g.s), pos);
     PC pc;
     pc.init(row_span<VB, PEB>(a.gamma, 0, a.cols, nv, 0, nreg), row_span<VB, PEB>(a.beta, 0, a.cols, nv, 0, nreg),
             pos, lds_params, tid, BLOCK);
     if constexpr (PC::kMode == kParamLds)
         __syncthreads();
-    const int kv = count_valid<IT, kWave>(nreg, pos);
+    int kv = count_valid<IT, kWave>(nreg, pos);
     Loc loc0;
-    if constexpr (PART) {
+    if constexpr (PART && !SHIFT) {
         loc0.ntail = static_cast<int>(a.cols % E);
-        loc0.kpart = partial_index<IT, kWave>(nv, pos, ODD || loc0.ntail != 0);
+        loc0.kpart = partial_index<IT, kWave>(nv, pos, loc0.ntail != 0);
     }
     for (; row < a.rows; row += gridDim.x) {
         const int64_t next = row + gridDim.x;
         Loc loc = loc0;
-        OddOut oo;
-        if constexpr (ODD)
-            oo = odd_row<E>(loc, a.y, row, a.cols, nv, 0, nv, pos);
+        ShiftOut so{};
+        ShiftRow gn{};
+        if constexpr (SHIFT) {
+            so = shift_row<IT, E, OEB>(loc, g, 0, g.nv, pos);
+            kv = count_valid<IT, kWave>(g.nv, pos);
+            gn = shift_geom<EB, E>(a.x, next, a.cols);
+        }
         typename Op::Partial lp;
         if constexpr (kLds)
             lp = lds_load_reduce<OP, T, VB, BLOCK, LT>(lds_row, row_srcs<OP, VB>(a, row, nv, nreg, nl),
@@ -854,15 +888,17 @@ __global__ __launch_bounds__(BLOCK) void single_wg_kernel(RowArgs a)
         const auto rp = block_combine<OP, NW>(wp, sh);
         const Coef c = Op::template finalize<T>(rp, loc, a.cols, a.eps);
         store_row_value<OP>(a, row, c, tid == 0);
-        const auto nsrc = row_srcs<OP, VB, PEB, ODD>(a, next, nv, 0, next < a.rows ? nreg : 0);
-        const rsrc_t dst = ODD ? odd_span<VBO>(a.y, row, a.cols, 0, nv, true)
-                               : row_span<VBO, PEB>(a.y, row, a.cols, nv, 0, nreg);
-        store_tile<OP, T, VB, IT, BLOCK, kOwnerRow, ODD>(t, dst, pc, pos, c, nsrc, &oo);
+        const auto nsrc =
+            row_srcs<OP, VB, PEB, SHIFT>(a, next, nv, 0, next < a.rows ? (SHIFT ? gn.nv : nreg) : 0, gn.s);
+        const rsrc_t dst = SHIFT ? shift_span<VBO, OEB>(a.y, row, a.cols, g.s, 0, g.nv)
+                                 : row_span<VBO, PEB>(a.y, row, a.cols, nv, 0, nreg);
+        store_tile<OP, T, VB, IT, BLOCK, kOwnerRow, SHIFT>(t, dst, pc, pos, c, nsrc, &so);
         if constexpr (kLds)
             lds_store<OP, T, VB, BLOCK, LT>(lds_row, span<VBO>(a.y, row * nv + nreg, nl), span<VB>(a.gamma, nreg, nl),
                                             span<VB>(a.beta, nreg, nl), tid,
                                             Op::template finalize_stream<T>(rp, a.cols, a.eps));
         load_next<OP, T, VB, IT, BLOCK, kOwnerRow>(t, nsrc, pos);
+        g = gn;
         // the next block_combine rewrites sh: every wave must have read it
         __syncthreads();
     }
@@ -899,19 +935,21 @@ __device__ __forceinline__ void finish_split_launch(const SplitArgs &a, uint32_t
 // ---------------------------------------------------------------------------
 // LT > 0: the LDS tier, as in single_wg_kernel (slices of whole 16-byte
 // vectors, at most BLOCK * (IT + LT) of them).
-template <OpKind OP, class T, int VB, int BLOCK, int IT, bool CONTROL, bool PART = false, bool ODD = false,
+template <OpKind OP, class T, int VB, int BLOCK, int IT, bool CONTROL, bool PART = false, bool SHIFT = false,
           int LT = 0>
 __global__ __launch_bounds__(BLOCK) void split_kernel(SplitArgs a)
 {
     using Op = OpTraits<OP>;
     using Partial = typename Op::Partial;
     using PC = ParamCache<OP, T, VB, IT, BLOCK, kOwnerSlice>;
-    using Loc = std::conditional_t<ODD, LocalOdd, std::conditional_t<PART, LocalPart, Local>>;
-    constexpr int E = VB / StorageTraits<T>::kBytes;
-    constexpr int PEB = PART ? StorageTraits<T>::kBytes : 0;
+    using Loc = std::conditional_t<SHIFT, LocalShift, std::conditional_t<PART, LocalPart, Local>>;
+    constexpr int EB = StorageTraits<T>::kBytes;
+    constexpr int E = VB / EB;
+    constexpr int PEB = PART ? EB : 0;
+    constexpr int OEB = StorageTraits<OutT<OP, T>>::kBytes;
     static_assert(!(PART && CONTROL), "the control twin touches no row");
-    static_assert(!ODD || (PART && VB == 16 && StorageTraits<T>::kBytes == 2 && Op::kParams == 0),
-                  "ODD rows: bf16, 16-byte vectors, operators without parameters");
+    static_assert(!SHIFT || (PART && VB == 16 && Op::kParams == 0),
+                  "SHIFT rows: 16-byte vectors, operators without parameters");
     constexpr bool kLds = LT > 0;
     static_assert(!kLds || (!PART && !CONTROL && VB == 16), "the LDS tier holds slices of whole 16-byte vectors");
     constexpr int NW = BLOCK / kWave;
@@ -938,16 +976,26 @@ __global__ __launch_bounds__(BLOCK) void split_kernel(SplitArgs a)
     const int64_t k = ticket / static_cast<uint32_t>(P);
     const int c = static_cast<int>(ticket % static_cast<uint32_t>(P));
 
-    const int64_t nv = PART ? (a.r.cols + E - 1) / E : a.r.cols / E;
-    const int64_t per = (nv + P - 1) / P;
+    // vectors per row (SHIFT: the most any row's held span covers; each row's
+    // own count, and so its last slices' lengths, come from shift_geom)
+    const int64_t nv = SHIFT ? shift_held_vectors(a.r.cols, EB) : (PART ? (a.r.cols + E - 1) / E : a.r.cols / E);
+    const int64_t per = slice_vectors(nv, P, VB);
     const int64_t v0 = min(nv, per * c);
     const int64_t ns = min(nv, v0 + per) - v0;  // vectors in this slice
     // of which held in registers, and in LDS (kLds)
     const int64_t nreg = kLds ? min(ns, static_cast<int64_t>(BLOCK) * IT) : ns;
     const int64_t nl = ns - nreg;
     const int pos = (tid / kWave) * kWave * IT + (tid & (kWave - 1));  // this wave's run + lane
-    const int kv = count_valid<IT, kWave>(nreg, pos);
+    int kv = count_valid<IT, kWave>(nreg, pos);
     uint64_t *cslots = scratch_slots(a.ctl) + k * 2 * P * Q;
+    // a SHIFT row's vectors in this slice
+    auto shift_ns = [&](const ShiftRow &gr) __attribute__((always_inline)) {
+        const int64_t n = gr.nv - v0;
+        return n < 0 ? INT64_C(0) : (n < per ? n : per);
+    };
+    ShiftRow g{};
+    if constexpr (SHIFT)
+        g = shift_geom<EB, E>(a.r.x, k, a.r.cols);
 
     Tile<T, VB, IT> t[Op::kIn];
     PC pc;
@@ -958,7 +1006,9 @@ __global__ __launch_bounds__(BLOCK) void split_kernel(SplitArgs a)
             for (int j = 0; j < IT; ++j)
                 t[i].v[j] = RawVec<VB>{};
     } else {
-        load_tile<T, VB, IT, kWave>(t, row_srcs<OP, VB, PEB, ODD>(a.r, k, nv, v0, k < a.r.rows ? nreg : 0), pos);
+        load_tile<T, VB, IT, kWave>(
+            t, row_srcs<OP, VB, PEB, SHIFT>(a.r, k, nv, v0, k < a.r.rows ? (SHIFT ? shift_ns(g) : nreg) : 0, g.s),
+            pos);
         pc.init(row_span<VB, PEB>(a.r.gamma, 0, a.r.cols, nv, v0, nreg),
                 row_span<VB, PEB>(a.r.beta, 0, a.r.cols, nv, v0, nreg), pos, lds_params, tid, BLOCK);
         if constexpr (PC::kMode == kParamLds)
@@ -972,17 +1022,22 @@ __global__ __launch_bounds__(BLOCK) void split_kernel(SplitArgs a)
     // instead of conservatively (measured: 3% on RMSNorm bf16 split plans; the
     // kernels that do not roll gain nothing from it and are not peeled).
     Loc loc0;
-    if constexpr (PART) {
+    if constexpr (PART && !SHIFT) {
         loc0.ntail = static_cast<int>(a.r.cols % E);
-        loc0.kpart = partial_index<IT, kWave>(ns, pos, (ODD || loc0.ntail != 0) && v0 + ns == nv);
+        loc0.kpart = partial_index<IT, kWave>(ns, pos, loc0.ntail != 0 && v0 + ns == nv);
     }
     auto step = [&](int64_t row, uint32_t it) __attribute__((always_inline)) {
         const int64_t next = row + a.clusters;
         Partial wp;
         Loc loc = loc0;
-        OddOut oo;
-        if constexpr (ODD)
-            oo = odd_row<E>(loc, a.r.y, row, a.r.cols, nv, v0, ns, pos);
+        ShiftOut so{};
+        ShiftRow gn{};
+        if constexpr (SHIFT) {
+            const int64_t nsr = shift_ns(g);
+            so = shift_row<IT, E, OEB>(loc, g, v0, nsr, pos);
+            kv = count_valid<IT, kWave>(nsr, pos);
+            gn = shift_geom<EB, E>(a.r.x, next, a.r.cols);
+        }
         Partial lp;
         if constexpr (kLds)
             lp = lds_load_reduce<OP, T, VB, BLOCK, LT>(lds_row, row_srcs<OP, VB>(a.r, row, nv, v0 + nreg, nl),
@@ -1031,16 +1086,18 @@ __global__ __launch_bounds__(BLOCK) void split_kernel(SplitArgs a)
             (void)next;
         } else {
             store_row_value<OP>(a.r, row, cf, c == 0 && tid == 0);
-            const auto nsrc = row_srcs<OP, VB, PEB, ODD>(a.r, next, nv, v0, next < a.r.rows ? nreg : 0);
-            const rsrc_t dst = ODD ? odd_span<VBO>(a.r.y, row, a.r.cols, v0, ns, true)
-                                   : row_span<VBO, PEB>(a.r.y, row, a.r.cols, nv, v0, nreg);
-            store_tile<OP, T, VB, IT, BLOCK, kOwnerSlice, ODD>(t, dst, pc, pos, cf, nsrc, &oo);
+            const auto nsrc = row_srcs<OP, VB, PEB, SHIFT>(
+                a.r, next, nv, v0, next < a.r.rows ? (SHIFT ? shift_ns(gn) : nreg) : 0, gn.s);
+            const rsrc_t dst = SHIFT ? shift_span<VBO, OEB>(a.r.y, row, a.r.cols, g.s, v0, shift_ns(g))
+                                     : row_span<VBO, PEB>(a.r.y, row, a.r.cols, nv, v0, nreg);
+            store_tile<OP, T, VB, IT, BLOCK, kOwnerSlice, SHIFT>(t, dst, pc, pos, cf, nsrc, &so);
             if constexpr (kLds)
                 lds_store<OP, T, VB, BLOCK, LT>(lds_row, span<VBO>(a.r.y, row * nv + v0 + nreg, nl),
                                                 span<VB>(a.r.gamma, v0 + nreg, nl), span<VB>(a.r.beta, v0 + nreg, nl),
                                                 tid, Op::template finalize_stream<T>(rp, a.r.cols, a.r.eps));
             load_next<OP, T, VB, IT, BLOCK, kOwnerSlice>(t, nsrc, pos);
         }
+        g = gn;
         // (no barrier needed before the next row rewrites sh or peer: every
         // wave has read sh before the exchange barrier above and reads peer
         // before it reaches the next block_combine barrier)

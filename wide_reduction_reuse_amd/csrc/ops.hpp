@@ -83,29 +83,74 @@ struct LocalPart : Local {
     int ntail = 0;
 };
 
-// The same, for odd-length bf16 rows held from the 4-byte word below their
-// start (the kernels' ODD mode): a row that starts in the middle of a word
-// has its first held element (the previous row's last) at element 0 of the
-// thread's vector khead (-1 when the thread does not hold it, or the row
-// starts on a word boundary), and the last vector's ntail valid elements
-// count from the start of the held span.
-struct LocalOdd : LocalPart {
+// The same, for rows held from the 64-byte boundary at or below their first
+// byte (the kernels' SHIFT mode): the thread's vector 0 begins with `hcount`
+// elements of the previous row (nonzero only in the few threads that hold the
+// row's first vectors), and the last vector's ntail valid elements count from
+// the start of the held span.
+struct LocalShift : LocalPart {
     static constexpr bool kHead = true;
-    int khead = -1;
+    int hcount = 0;
 };
 
 // Whether element e of the thread's vector k is part of the row (only the
-// partial last vector of a PART or ODD row, and an ODD row's first vector,
-// have elements that are not).
+// partial last vector of a PART or SHIFT row, and a SHIFT row's first
+// vectors, have elements that are not).
 template <class L>
 __device__ __forceinline__ bool elem_in_row(const L &loc, int k, int e)
 {
     if constexpr (L::kHead)
-        return (k != loc.kpart || e < loc.ntail) && (k != loc.khead || e != 0);
+        return (k != loc.kpart || e < loc.ntail) && (k != 0 || e >= loc.hcount);
     else if constexpr (L::kPartial)
         return k != loc.kpart || e < loc.ntail;
     else
         return true;
+}
+
+// Whether a reduction must test element e of vector k before using it:
+// PART rows mask their partial last vector element by element; a SHIFT row's
+// elements outside the row are overwritten with the reduction's neutral value
+// instead (fill_outside), so its reductions test nothing.
+template <class L>
+__device__ __forceinline__ bool counts(const L &loc, int k, int e)
+{
+    if constexpr (L::kHead)
+        return true;
+    else
+        return elem_in_row(loc, k, e);
+}
+
+// Element e of a raw vector set to v (bf16: its upper 16 bits, which is exact
+// for the values used here: -inf and 0).
+template <class T, int VB>
+__device__ __forceinline__ void set_elem(RawVec<VB> &r, int e, float v)
+{
+    if constexpr (StorageTraits<T>::kBytes == 4) {
+        set_word<VB>(r, e, __float_as_uint(v));
+    } else {
+        const uint32_t b = __float_as_uint(v) >> 16;
+        const uint32_t w = word<VB>(r, e >> 1);
+        set_word<VB>(r, e >> 1, (e & 1) ? ((w & 0xffffu) | (b << 16)) : ((w & 0xffff0000u) | b));
+    }
+}
+
+// SHIFT rows: vector k's elements outside the row (the thread's vector 0 when
+// it starts before the row, its vector kpart when the row ends inside it)
+// replaced by `fill`.  Called right before the vector's first use, inside a
+// branch that only the lanes holding such a vector take, so the reductions
+// pay one test per vector instead of per element.  Other rows: nothing.
+template <class T, int VB, class L>
+__device__ __forceinline__ void fill_outside(RawVec<VB> &v, const L &loc, int k, float fill)
+{
+    if constexpr (L::kHead) {
+        constexpr int E = VB / StorageTraits<T>::kBytes;
+        if ((k == 0 && loc.hcount > 0) || k == loc.kpart) {
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                if (!elem_in_row(loc, k, e))
+                    set_elem<T, VB>(v, e, fill);
+        }
+    }
 }
 
 // Vector groups of a held tile of IT vectors reduced one after another (see
@@ -189,10 +234,14 @@ __device__ __forceinline__ Part<DY ? 3 : 2> softmax_groups(Tile<T, VB, IT> (&t)[
         float mt = -INFINITY;
 #pragma unroll
         for (int k = 0; k < IT; ++k)
-            if (k < kvalid)
+            if (k < kvalid) {
+                fill_outside<T, VB>(t[0].v[k], loc, k, -INFINITY);
+                if constexpr (DY)
+                    fill_outside<T, VB>(t[1].v[k], loc, k, 0.0f);
 #pragma unroll
                 for (int e = 0; e < E; ++e)
-                    mt = fmaxf(mt, elem_in_row(loc, k, e) ? elem<T, VB>(t[0].v[k], e) : -INFINITY);
+                    mt = fmaxf(mt, counts(loc, k, e) ? elem<T, VB>(t[0].v[k], e) : -INFINITY);
+            }
         mw = wave_max(mt);
         fence_tile(t[0]);
     }
@@ -203,15 +252,21 @@ __device__ __forceinline__ Part<DY ? 3 : 2> softmax_groups(Tile<T, VB, IT> (&t)[
             gm = -INFINITY;
 #pragma unroll
             for (int j = 0; j < GS; ++j)
-                if (g * GS + j < kvalid)
+                if (g * GS + j < kvalid) {
+                    fill_outside<T, VB>(t[0].v[g * GS + j], loc, g * GS + j, -INFINITY);
 #pragma unroll
                     for (int e = 0; e < E; ++e)
-                        gm = fmaxf(gm, elem_in_row(loc, g * GS + j, e) ? elem<T, VB>(t[0].v[g * GS + j], e)
-                                                                       : -INFINITY);
+                        gm = fmaxf(gm, counts(loc, g * GS + j, e) ? elem<T, VB>(t[0].v[g * GS + j], e)
+                                                                  : -INFINITY);
+                }
 #pragma unroll
             for (int j = 0; j < GS; ++j)
                 fence_vec(t[0].v[g * GS + j]);
         }
+        // the reference of the exponentials: a group (or wave) whose valid
+        // elements were all filled with -inf has gm = -inf, whose exp(x - gm)
+        // would be NaN; any finite reference gives its elements exp = 0
+        const float gx = gm == -INFINITY ? 0.0f : gm;
         float sv = 0.0f, uv = 0.0f;
 #pragma unroll
         for (int j = 0; j < GS; ++j) {
@@ -219,19 +274,14 @@ __device__ __forceinline__ Part<DY ? 3 : 2> softmax_groups(Tile<T, VB, IT> (&t)[
             if (k < kvalid)
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
-                    const float ex =
-                        elem_in_row(loc, k, e) ? exp_for<T>(elem<T, VB>(t[0].v[k], e) - gm) : 0.0f;
+                    const float ex = counts(loc, k, e) ? exp_for<T>(elem<T, VB>(t[0].v[k], e) - gx) : 0.0f;
                     if constexpr (is_f32<T>())
                         set_word<VB>(t[0].v[k], e, __float_as_uint(ex));
                     sv += ex;
-                    if constexpr (DY) {
-                        // an ODD row's masked elements are the neighbouring
-                        // rows' data: keep their dy (even an inf) out of u
-                        if constexpr (L::kHead)
-                            uv = elem_in_row(loc, k, e) ? __builtin_fmaf(ex, elem<T, VB>(t[1].v[k], e), uv) : uv;
-                        else
-                            uv = __builtin_fmaf(ex, elem<T, VB>(t[1].v[k], e), uv);
-                    }
+                    // (a SHIFT row's dy outside the row, the neighbouring
+                    // rows' data, was filled with 0 and adds nothing to u)
+                    if constexpr (DY)
+                        uv = __builtin_fmaf(ex, elem<T, VB>(t[1].v[k], e), uv);
                 }
         }
         gref[g] = gm;
@@ -911,16 +961,18 @@ struct OpTraits<kQuantInt8> {
     using Partial = Part<kQ>;
 
     template <class T, int VB, int IT, class L>
-    __device__ __forceinline__ static Partial wave_partial(Tile<T, VB, IT> (&t)[kIn], int kvalid, L &)
+    __device__ __forceinline__ static Partial wave_partial(Tile<T, VB, IT> (&t)[kIn], int kvalid, L &loc)
     {
         constexpr int E = Tile<T, VB, IT>::kEpv;
         float a = 0.0f;
 #pragma unroll
         for (int k = 0; k < IT; ++k)
-            if (k < kvalid)
+            if (k < kvalid) {
+                fill_outside<T, VB>(t[0].v[k], loc, k, 0.0f);
 #pragma unroll
                 for (int e = 0; e < E; ++e)
-                    a = fmaxf(a, fabsf(elem<T, VB>(t[0].v[k], e)));
+                    a = fmaxf(a, counts(loc, k, e) ? fabsf(elem<T, VB>(t[0].v[k], e)) : 0.0f);
+            }
         return Partial{{wave_max(a)}};
     }
 

@@ -7,6 +7,7 @@
 #include <cstdlib>
 #include <map>
 
+#include "args.hpp"
 #include "registry.hpp"
 
 namespace credit {
@@ -37,11 +38,14 @@ bool row_is_partial(int op, int dt, int64_t cols)
     return op_has_part(op, dt) && bytes % 16 != 0 && bytes % 4 == 0;
 }
 
-bool row_is_odd(int op, int dt, int64_t cols) { return op_has_odd(op) && dt == 1 && cols % 2 == 1; }
+bool row_is_shifted(int op, int dt, int64_t cols)
+{
+    return op_has_shift(op) && (cols * elem_bytes(dt)) % 64 != 0;
+}
 
 int held_row_kind(int op, int dt, int64_t cols)
 {
-    return row_is_partial(op, dt, cols) ? 1 : (row_is_odd(op, dt, cols) ? 2 : 0);
+    return row_is_partial(op, dt, cols) ? 1 : (row_is_shifted(op, dt, cols) ? 2 : 0);
 }
 
 int held_vec_bytes(int op, int dt, int64_t cols)
@@ -54,8 +58,21 @@ int path_vec_bytes(int op, int dt, int64_t cols, int path)
     return path == kPathReread ? vec_bytes_for(dt, cols) : held_vec_bytes(op, dt, cols);
 }
 
+int64_t lds_row_vectors(int dt, int64_t cols)
+{
+    const int64_t bytes = cols * elem_bytes(dt);
+    return bytes % 16 == 0 ? bytes / 16 : 0;
+}
+
+int plan_row_kind(int op, int dt, int64_t cols, int path, int lds)
+{
+    return (path == kPathReread || lds > 0) ? 0 : held_row_kind(op, dt, cols);
+}
+
 int64_t held_vectors(int op, int dt, int64_t cols)
 {
+    if (held_row_kind(op, dt, cols) == 2)
+        return shift_held_vectors(cols, elem_bytes(dt));
     const int64_t vb = held_vec_bytes(op, dt, cols);
     return (cols * elem_bytes(dt) + vb - 1) / vb;
 }
@@ -179,7 +196,7 @@ static std::vector<TileSpec> lds_tiles(int op, int dt, int kind)
 
 std::vector<TileSpec> lds_ladder(int op, int dt, int64_t cols, int kind)
 {
-    if (held_row_kind(op, dt, cols) != 0 || held_vec_bytes(op, dt, cols) != 16)
+    if (lds_row_vectors(dt, cols) == 0)
         return {};
     return lds_tiles(op, dt, kind);
 }
@@ -207,7 +224,8 @@ bool single_tile(int op, int dt, int64_t cols, TileSpec *out)
     const int64_t nv = held_vectors(op, dt, cols);
     const std::vector<TileSpec> ladder = single_ladder(op, dt, vb);
     TileSpec t;
-    if (!pick_holding_tile(ladder, nv, &t) && !pick_lds_tile(lds_ladder(op, dt, cols, kKindWg), nv, &t))
+    if (!pick_holding_tile(ladder, nv, &t) &&
+        !pick_lds_tile(lds_ladder(op, dt, cols, kKindWg), lds_row_vectors(dt, cols), &t))
         return false;
     t.vb = vb;
     *out = t;
@@ -220,15 +238,19 @@ bool split_tile(int op, int dt, int64_t cols, int p, TileSpec *out)
         return false;
     const int vb = held_vec_bytes(op, dt, cols);
     const int64_t nv = held_vectors(op, dt, cols);
-    const int64_t per = (nv + p - 1) / p;
+    const int64_t per = slice_vectors(nv, p, vb);
     if (per * (p - 1) >= nv)
         return false;  // the last slice would be empty: too narrow to split p ways
     std::vector<TileSpec> ladder;
     for (const TileSpec &u : tiles_for(kKindSplit, vb == 16))
         if (tile_enabled(op, dt, kKindSplit, u.block, u.items, vb))
             ladder.push_back(u);
+    // the LDS tier holds rows of whole 16-byte vectors as they are (no shift)
+    const int64_t nvl = lds_row_vectors(dt, cols);
+    const int64_t perl = slice_vectors(nvl, p, 16);
     TileSpec t;
-    if (!pick_holding_tile(ladder, per, &t) && !pick_lds_tile(lds_ladder(op, dt, cols, kKindSplit), per, &t))
+    if (!pick_holding_tile(ladder, per, &t) &&
+        !(perl * (p - 1) < nvl && pick_lds_tile(lds_ladder(op, dt, cols, kKindSplit), perl, &t)))
         return false;
     t.vb = vb;
     *out = t;
@@ -333,7 +355,7 @@ int occupancy_of(const PlanRequest &req, const Calibration &cal, int path, const
     k.block = t.block;
     k.items = t.items;
     k.vb = t.vb;
-    k.part = path == kPathReread ? 0 : held_row_kind(req.op, req.dt, req.cols);
+    k.part = plan_row_kind(req.op, req.dt, req.cols, path, t.lds);
     k.lds = t.lds;
     if (cal.occ_query) {
         const int o = cal.occ_query(k);
@@ -490,7 +512,7 @@ double neighbour_time_us(const PlanRequest &req, const Calibration &cal, const C
 {
     const CalibEntry *lo = nullptr, *hi = nullptr;
     const bool held = cd.path != kPathReread;
-    const int kind = held ? held_row_kind(req.op, req.dt, req.cols) : 0;
+    const int kind = plan_row_kind(req.op, req.dt, req.cols, cd.path, cd.est.tile.lds);
     for (int same_kind = 1; same_kind >= 0 && lo == nullptr && hi == nullptr; --same_kind)
         for (const CalibEntry &e : cal.table) {
             if (e.op != req.op || e.dt != req.dt || e.path != cd.path || e.split_p != cd.split_p ||
@@ -498,7 +520,7 @@ double neighbour_time_us(const PlanRequest &req, const Calibration &cal, const C
                 e.lds != cd.est.tile.lds ||
                 e.wgs_per_cu != cd.wgs_per_cu || e.rows.empty())
                 continue;
-            if (same_kind && held && held_row_kind(e.op, e.dt, e.cols) != kind)
+            if (same_kind && held && plan_row_kind(e.op, e.dt, e.cols, e.path, e.lds) != kind)
                 continue;
             if (e.cols <= req.cols && (lo == nullptr || e.cols > lo->cols))
                 lo = &e;
@@ -684,9 +706,10 @@ void enumerate_candidates(const PlanRequest &req, const Calibration &cal, std::v
         }
     // LDS-tier tiles whose register part the row fills (otherwise the same
     // registers alone hold it)
+    const int64_t nvl = lds_row_vectors(req.dt, req.cols);
     for (TileSpec t : lds_ladder(req.op, req.dt, req.cols, kKindWg)) {
         const int64_t reg = static_cast<int64_t>(t.block) * t.items;
-        if (nv <= reg || nv > reg + static_cast<int64_t>(t.block) * t.lds)
+        if (nvl <= reg || nvl > reg + static_cast<int64_t>(t.block) * t.lds)
             continue;
         for (int mode : {0, -1}) {
             PathEstimate e;
@@ -709,8 +732,13 @@ void enumerate_candidates(const PlanRequest &req, const Calibration &cal, std::v
     double base_us = 0.0;
     const bool have_base = analytic_baseline(req, cal, &base_path, &base_tile, &base_us);
     for (int P : {2, 4, 8}) {
-        const int64_t per = (nv + P - 1) / P;
-        if (per * (P - 1) >= nv || !have_base)
+        if (!have_base)
+            continue;
+        const int64_t per = slice_vectors(nv, P, vb);
+        const int64_t perl = slice_vectors(nvl, P, 16);  // the LDS tier's slices (unshifted rows)
+        const bool reg_ok = per * (P - 1) < nv;
+        const bool lds_ok = nvl > 0 && perl * (P - 1) < nvl;
+        if (!reg_ok && !lds_ok)
             continue;
         std::vector<TileSpec> ladder;
         for (const TileSpec &u : tiles_for(kKindSplit, v16))
@@ -718,13 +746,13 @@ void enumerate_candidates(const PlanRequest &req, const Calibration &cal, std::v
                 ladder.push_back(u);
         std::vector<TileSpec> tiles;
         for (TileSpec t : ladder)
-            if (worth_holding(ladder, t, per)) {
+            if (reg_ok && worth_holding(ladder, t, per)) {
                 t.vb = vb;
                 tiles.push_back(t);
             }
         for (const TileSpec &t : lds_ladder(req.op, req.dt, req.cols, kKindSplit)) {
             const int64_t reg = static_cast<int64_t>(t.block) * t.items;
-            if (per > reg && per <= reg + static_cast<int64_t>(t.block) * t.lds)
+            if (lds_ok && perl > reg && perl <= reg + static_cast<int64_t>(t.block) * t.lds)
                 tiles.push_back(t);
         }
         for (const TileSpec &t : tiles) {

@@ -181,17 +181,25 @@ int vec_bytes_for(int dt, int64_t cols);
 // with PART kernels: paths 1 and 2 hold them as 16-byte vectors whose last
 // one is partial (PART kernels mask its missing elements).
 bool row_is_partial(int op, int dt, int64_t cols);
-// bf16 rows of odd length, of an operator with ODD kernels: paths 1 and 2
-// hold them as 16-byte vectors from the 4-byte word below the row's start.
-bool row_is_odd(int op, int dt, int64_t cols);
+// Rows whose byte length is not a multiple of 64, of an operator with SHIFT
+// kernels: paths 1 and 2 hold them as 16-byte vectors from the 64-byte
+// boundary below each row's start.
+bool row_is_shifted(int op, int dt, int64_t cols);
 // The kernels' row kind for paths 1 and 2: 0 whole vectors or one-element
-// tiles, 1 partial last vector (row_is_partial), 2 odd-length bf16 (row_is_odd).
+// tiles, 1 partial last vector (row_is_partial), 2 shifted (row_is_shifted).
 int held_row_kind(int op, int dt, int64_t cols);
-// Bytes per access of the held tiles (paths 1, 2): 16 for partial and ODD rows too.
+// Bytes per access of the held tiles (paths 1, 2): 16 for PART and SHIFT rows too.
 int held_vec_bytes(int op, int dt, int64_t cols);
 // Bytes per access that `path` (kPathSingle / kPathSplit / kPathReread) uses.
 int path_vec_bytes(int op, int dt, int64_t cols, int path);
-// Vectors of held_vec_bytes covering a row, the last one possibly partial.
+// 16-byte vectors of a row that the LDS tier holds: rows of whole 16-byte
+// vectors, held as they are (no shift) by the LDS-tier kernels; else 0.
+int64_t lds_row_vectors(int dt, int64_t cols);
+// The row kind of the kernel a plan runs: held_row_kind for register tiles
+// of paths 1 and 2, 0 for the reread path and the LDS tier.
+int plan_row_kind(int op, int dt, int64_t cols, int path, int lds);
+// Vectors of held_vec_bytes covering a row, the last one possibly partial
+// (SHIFT rows: the most that any row's held span covers, shift_held_vectors).
 int64_t held_vectors(int op, int dt, int64_t cols);
 
 // Tile ladders, mirroring the compiled instantiations.

@@ -19,27 +19,27 @@ struct KernelEntry {
     int items;  // vectors held per thread (paths 1, 2) or streamed per step (path 3)
     const void *fn;
     // row shape the kernel holds: 0 whole 16-byte vectors (or one-element
-    // tiles), 1 a partial last vector (PART kernels), 2 odd-length bf16 rows
-    // held from the 4-byte word below their start (ODD kernels)
+    // tiles), 1 a partial last vector (PART kernels), 2 rows held from the
+    // 64-byte boundary below their start (SHIFT kernels)
     int part = 0;
     // vectors per thread held in LDS beside the `items` in registers (the LDS
     // tier of paths 1 and 2; 0 for every other kernel)
     int lds = 0;
 };
 
-// Operators with PART kernels: their partials mask the partial vector's
-// elements (softmax, LayerNorm, RMSNorm, softmax backward, fp32 LayerNorm
-// backward); the int8 quantizer, whose output rows of one byte per element
-// end inside a 4-byte word, and bf16 LayerNorm backward, whose held rows are
-// reduced in the streaming form (which counts whole vectors), keep
-// one-element tiles for rows that are not whole vectors.
-constexpr bool op_has_part(int op, int dt) { return op <= 3 || (op == 4 && dt == 0); }
+// Operators with PART kernels (rows whose byte length is a multiple of 4 but
+// not of 16, held from their first byte): the operators with parameter
+// vectors, LayerNorm, RMSNorm and fp32 LayerNorm backward.  (bf16 LayerNorm
+// backward, whose held rows are reduced in the streaming form, which counts
+// whole vectors, keeps one-element tiles for such rows.)
+constexpr bool op_has_part(int op, int dt) { return op == 1 || op == 2 || (op == 4 && dt == 0); }
 
-// Operators with ODD kernels (bf16 rows of odd length held as 16-byte
-// vectors): those without parameter vectors whose output has the input's
-// type, softmax and softmax backward.  (A row that starts in the middle of a
-// 4-byte word would need its parameters shifted by one element.)
-constexpr bool op_has_odd(int op) { return op == 0 || op == 3; }
+// Operators with SHIFT kernels (rows whose byte length is not a multiple of
+// 64, held from the 64-byte boundary below their start, any element count):
+// those without parameter vectors, softmax, softmax backward and the int8
+// quantizer.  (Shifting a row would shift its parameter vectors against the
+// 16-byte grid too.)
+constexpr bool op_has_shift(int op) { return op == 0 || op == 3 || op == 5; }
 
 void register_softmax_kernels(std::vector<KernelEntry> &out);
 void register_layernorm_kernels(std::vector<KernelEntry> &out);

@@ -68,23 +68,24 @@ def records_from_table(doc: dict) -> list:
              "rows": rows, "cols": cols, "candidates": c} for (op, dt, cols, rows), c in shapes.items()]
 
 
-def row_kind(C, op: str, dt: str, cols: int) -> int:
-    """The held kernels' row kind for this width, from the planner itself: a
-    held plan that accesses 16-byte vectors where the reread plan accesses
-    elements is a partial-vector row (byte length a multiple of 4) or an odd
-    bf16 row."""
-    plans = [p.as_dict() for p in C.credit_enumerate_plans(op, dt, 1, cols)]
-    held = {p["vec_bytes"] for p in plans if p["path"] in (1, 2)}
-    reread = {p["vec_bytes"] for p in plans if p["path"] == 3}
-    if not held or held == reread:
-        return 0
-    return 1 if cols * (4 if dt == "f32" else 2) % 4 == 0 else 2
+def row_kind(op: str, dt: str, cols: int) -> int:
+    """The held register tiles' row kind for this width (the library's
+    held_row_kind): 2 for rows of the operators without parameter vectors
+    (softmax, softmax backward, the quantizer) whose byte length is not a
+    multiple of 64 (held from the 64-byte boundary below their start), 1 for
+    rows of LayerNorm, RMSNorm and fp32 LayerNorm backward whose byte length
+    is a multiple of 4 but not of 16 (a partial last vector), else 0."""
+    nbytes = cols * (4 if dt == "f32" else 2)
+    if op in ("softmax", "softmax_bwd", "quantize_int8"):
+        return 2 if nbytes % 64 else 0
+    if op in ("layernorm", "rmsnorm") or (op == "layernorm_bwd" and dt == "f32"):
+        return 1 if nbytes % 16 and nbytes % 4 == 0 else 0
+    return 0
 
 
 def occupancy_table(C, records) -> list:
     """[op, dt, kind, block, items, vec_bytes, row kind, lds, workgroups per
     CU] for every kernel whose occupancy the records hold."""
-    kinds = {}
     table = {}
     for r in records:
         for c in r["candidates"]:
@@ -94,13 +95,7 @@ def occupancy_table(C, records) -> list:
             p = c["plan"]
             path = p["path"]
             kind = {2: KIND_SPLIT, 3: KIND_REREAD}.get(path, KIND_WAVE if p["block_threads"] == 64 else KIND_WG)
-            if path == 3:
-                part = 0
-            else:
-                k = (r["op"], r["dtype"], r["cols"])
-                if k not in kinds:
-                    kinds[k] = row_kind(C, *k)
-                part = kinds[k]
+            part = 0 if path == 3 or p.get("lds_items", 0) else row_kind(r["op"], r["dtype"], r["cols"])
             key = (OPS.index(r["op"]), DTS.index(r["dtype"]), kind, p["block_threads"], p["items"],
                    p["vec_bytes"], part, p.get("lds_items", 0))
             table[key] = int(occ)
