@@ -706,10 +706,15 @@ void enumerate_candidates(const PlanRequest &req, const Calibration &cal, std::v
         }
     // LDS-tier tiles whose register part the row fills (otherwise the same
     // registers alone hold it)
+    // (a shifted row whose span no register tile holds, though its whole
+    // 16-byte vectors would fit one, is held unshifted by an LDS-tier tile)
     const int64_t nvl = lds_row_vectors(req.dt, req.cols);
+    bool reg_holds = false;
+    for (const TileSpec &u : held)
+        reg_holds = reg_holds || static_cast<int64_t>(u.block) * u.items >= nv;
     for (TileSpec t : lds_ladder(req.op, req.dt, req.cols, kKindWg)) {
         const int64_t reg = static_cast<int64_t>(t.block) * t.items;
-        if (nvl <= reg || nvl > reg + static_cast<int64_t>(t.block) * t.lds)
+        if ((nvl <= reg && reg_holds) || nvl > reg + static_cast<int64_t>(t.block) * t.lds)
             continue;
         for (int mode : {0, -1}) {
             PathEstimate e;
@@ -750,9 +755,10 @@ void enumerate_candidates(const PlanRequest &req, const Calibration &cal, std::v
                 t.vb = vb;
                 tiles.push_back(t);
             }
+        const bool reg_holds_slice = !tiles.empty();
         for (const TileSpec &t : lds_ladder(req.op, req.dt, req.cols, kKindSplit)) {
             const int64_t reg = static_cast<int64_t>(t.block) * t.items;
-            if (lds_ok && perl > reg && perl <= reg + static_cast<int64_t>(t.block) * t.lds)
+            if (lds_ok && (perl > reg || !reg_holds_slice) && perl <= reg + static_cast<int64_t>(t.block) * t.lds)
                 tiles.push_back(t);
         }
         for (const TileSpec &t : tiles) {
