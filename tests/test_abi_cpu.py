@@ -204,23 +204,23 @@ def test_partial_rows_are_held_as_16_byte_vectors():
 
 def _max_shift_bytes(cols, eb):
     """The most bytes of the previous row in front of any row of a tensor with
-    16-byte aligned base: brute force over the base's offset in a 64-byte line
-    and enough rows to cycle through every start."""
+    16-byte aligned base, held from the 64-byte line below its start: brute
+    force over the base's offset and enough rows to cycle through every start."""
     return max((base + r * cols * eb) % 64 for base in (0, 16, 32, 48) for r in range(0, 65))
 
 
-def test_shifted_rows_are_held_from_the_64_byte_line_below():
+def test_shifted_rows_are_held_from_the_line_below():
     # rows whose byte length is not a multiple of 64, of the operators
     # without parameter vectors (softmax, softmax backward, the int8
     # quantizer): paths 1 and 2 hold them as 16-byte vectors from the 64-byte
-    # boundary below each row's start, so a tile must hold the row plus the
+    # line below each row's start, so a tile must hold the row plus the
     # largest such offset; the reread path reads them by element (or by
     # 16-byte vector when the byte length is a multiple of 16)
     L = C.lib()
-    cases = [("softmax", "f32", 1001), ("softmax", "f32", 1004), ("softmax", "f32", 1016), ("softmax", "bf16", 1),
-             ("softmax", "bf16", 1001), ("softmax", "bf16", 50257), ("softmax", "bf16", 50264),
-             ("softmax_bwd", "bf16", 30001), ("softmax_bwd", "f32", 30006), ("quantize_int8", "f32", 1001),
-             ("quantize_int8", "bf16", 1001), ("quantize_int8", "f32", 4100)]
+    cases = [("softmax", "f32", 1001), ("softmax", "f32", 1004), ("softmax", "f32", 4100), ("softmax", "f32", 5001),
+             ("softmax", "bf16", 1), ("softmax", "bf16", 1001), ("softmax", "bf16", 50257),
+             ("softmax", "bf16", 50264), ("softmax_bwd", "bf16", 30001), ("softmax_bwd", "f32", 30006),
+             ("quantize_int8", "f32", 1001), ("quantize_int8", "bf16", 1001), ("quantize_int8", "f32", 4100)]
     for op, dt, cols in cases:
         eb = 4 if dt == "f32" else 2
         p = C.credit_plan(op, dt, 64, cols, "single")
@@ -233,9 +233,11 @@ def test_shifted_rows_are_held_from_the_64_byte_line_below():
             plan = C.Plan.make(C.PATH_SINGLE_WG, 1, p.block_threads, p.items, eb)
             assert L.credit_run_plan(C.OPS[op], _ops(x=A, dy=G, y=B, row_out=G), 4, cols, 0.0, C.DTYPES[dt],
                                      ctypes.byref(plan), None) == 4
-    # a tile that holds the row but not the row plus its largest offset is refused
-    small = C.Plan.make(C.PATH_SINGLE_WG, 1, 64, 4, 16)  # 256 vectors = 1024 fp32
-    assert L.credit_run_plan(C.OPS["softmax"], _ops(x=A, y=B), 4, 1020, 0.0, C.DTYPES["f32"],
+    # a tile that holds the row but not the row plus its largest offset is
+    # refused: 4100 fp32 elements (1025 vectors) plus up to 48 bytes need
+    # 1028 vectors; 1024 x 1 holds 1024
+    small = C.Plan.make(C.PATH_SINGLE_WG, 1, 1024, 1, 16)
+    assert L.credit_run_plan(C.OPS["softmax"], _ops(x=A, y=B), 4, 4100, 0.0, C.DTYPES["f32"],
                              ctypes.byref(small), None) == 4
     assert C.credit_plan("softmax", "bf16", 64, 100003, "split", 8).vec_bytes == 16
     # rows of whole 64-byte lines are held as they are

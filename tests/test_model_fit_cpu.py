@@ -60,7 +60,8 @@ def test_row_kind_matches_the_kernel_families():
     C.credit_load_calibration(None)
     assert F.row_kind("softmax", "f32", 4096) == 0
     assert F.row_kind("softmax", "f32", 30001) == 2        # not a multiple of 64 bytes: shifted
-    assert F.row_kind("softmax", "f32", 1004) == 2         # 16-byte multiple, not 64: shifted too
+    assert F.row_kind("softmax", "f32", 4100) == 2         # 16-byte multiple, not 64: shifted too
+    assert F.row_kind("softmax", "f32", 1004) == 2
     assert F.row_kind("softmax", "bf16", 20002) == 2
     assert F.row_kind("softmax", "bf16", 50257) == 2
     assert F.row_kind("quantize_int8", "f32", 1001) == 2
@@ -70,8 +71,8 @@ def test_row_kind_matches_the_kernel_families():
     assert F.row_kind("rmsnorm", "bf16", 50257) == 0       # 2-byte accesses throughout
     assert F.row_kind("layernorm_bwd", "bf16", 20002) == 0
     # the library holds kind-2 widths with room for the shift, kind-1 widths without
-    assert C.credit_plan("softmax", "f32", 64, 1020, "single").block_threads * \
-        C.credit_plan("softmax", "f32", 64, 1020, "single").items * 4 >= 1020 + 12
+    assert C.credit_plan("softmax", "f32", 64, 4100, "single").block_threads * \
+        C.credit_plan("softmax", "f32", 64, 4100, "single").items * 4 >= 4100 + 12
     assert C.credit_plan("rmsnorm", "f32", 64, 1022, "single").block_threads * \
         C.credit_plan("rmsnorm", "f32", 64, 1022, "single").items * 4 >= 1022
 

@@ -303,10 +303,15 @@ def test_every_tile_partial_last_vector(op, dt, kind, block, items, p, cols):
 # lowest set bit of the row's byte length), masked and never written; the
 # vectors at the row's ends are written byte by byte where they are shared
 # ---------------------------------------------------------------------------
-def _shift_held_vectors(cols, eb):
-    """The held vectors a shifted row needs (the library's bound, restated)."""
+def _shift_held_vectors(op, cols, eb):
+    """The 16-byte vectors the held span of a row needs (the library's rule,
+    restated): rows that are not whole 64-byte lines are held from the 64-byte
+    line below their start, with up to 64 - min(g, 16) bytes in front (g the
+    lowest set bit of the byte length); rows of whole lines as they are."""
     nbytes = cols * eb
-    g = 64 if nbytes % 64 == 0 else nbytes & -nbytes
+    if nbytes % 64 == 0:
+        return nbytes // 16
+    g = nbytes & -nbytes
     return (nbytes + 64 - min(g, 16) + 15) // 16
 
 
@@ -316,18 +321,18 @@ def _slice_vectors(nv, p):
     return ((nv + p - 1) // p + 3) // 4 * 4
 
 
-def _shift_cols(eb, cls, fits):
+def _shift_cols(op, eb, cls, fits):
     """The widest row of byte-length class `cls` ("odd": odd bf16 length,
     "part": a multiple of 4 bytes but not of 16, "v16": of 16 but not of 64)
     whose held vectors satisfy fits(n)."""
     cols = 1
-    while fits(_shift_held_vectors(cols, eb)):
+    while fits(_shift_held_vectors(op, cols, eb)):
         cols *= 2
     while cols > 0:
         nbytes = cols * eb
         ok = {"odd": nbytes % 4 == 2, "part": nbytes % 4 == 0 and nbytes % 16 != 0,
               "v16": nbytes % 16 == 0 and nbytes % 64 != 0}[cls]
-        if ok and fits(_shift_held_vectors(cols, eb)):
+        if ok and fits(_shift_held_vectors(op, cols, eb)):
             return cols
         cols -= 1
     return None
@@ -354,10 +359,11 @@ def _shift_tile_cases():
                                     fits = lambda n, p=p: (n + p - 1) // p <= cap
                                 else:
                                     fits = lambda n, p=p: n <= p * cap - 3 * p - 1
-                                cases.append((op, dt, kind, block, items, p, _shift_cols(eb, cls, fits)))
+                                cases.append((op, dt, kind, block, items, p, _shift_cols(op, eb, cls, fits)))
                         else:
                             lim = cap if fill == "full" else cap - 3
-                            cases.append((op, dt, kind, block, items, 1, _shift_cols(eb, cls, lambda n: n <= lim)))
+                            cases.append((op, dt, kind, block, items, 1,
+                                          _shift_cols(op, eb, cls, lambda n: n <= lim)))
     return cases
 
 
@@ -397,8 +403,8 @@ def test_shifted_tile_one_vector_short_is_refused(op, dt):
     # front is refused before launch
     C = _lib()
     eb = W.ELEM_BYTES[dt]
-    cols = _shift_cols(eb, "part", lambda n: n <= 256 + 1) if dt == "f32" else _shift_cols(eb, "odd", lambda n: n <= 257)
-    assert _shift_held_vectors(cols, eb) == 257
+    cols = _shift_cols(op, eb, "part" if dt == "f32" else "odd", lambda n: n <= 257)
+    assert _shift_held_vectors(op, cols, eb) == 257
     w = W.custom(op, dt, 3, cols, seed=3)
     inp = W.generate(w)
     with pytest.raises(C.CreditError) as ei:
@@ -435,7 +441,7 @@ def test_shifted_rows_with_offset_bases(op, dt, xoff, yoff, cols):
             t[k] = moved(t.get(k), xoff)
         t["y"] = moved(t["y"], yoff)
         assert t["x"].data_ptr() % 64 == xoff and t["y"].data_ptr() % 64 == yoff
-        nvh = _shift_held_vectors(cols, W.ELEM_BYTES[dt])
+        nvh = _shift_held_vectors(op, cols, W.ELEM_BYTES[dt])
         if path == "split" and nvh <= _slice_vectors(nvh, 2):
             continue  # too narrow to split
         out = _run(inp, path, p, t=t)
@@ -453,7 +459,7 @@ def test_shifted_rows_in_place_and_boundary_nan(op, alias, dt, path, p, cols):
     # stay in those rows.
     C = _lib()
     eb = W.ELEM_BYTES[dt]
-    nvh = _shift_held_vectors(cols, eb)
+    nvh = _shift_held_vectors(op, cols, eb)
     if path == "split" and nvh <= (p - 1) * _slice_vectors(nvh, p):
         pytest.skip("too narrow to split %d ways" % p)
     w = W.custom(op, dt, 37, cols, seed=cols + 3, x_dist="scaled_shifted", x_scale=3.0, x_shift=0.5)
@@ -668,7 +674,7 @@ def test_masked_runs_of_logits(op, cols):
             inp.x[r, :] -= 1e4
             inp.x[r, keep] = 0.0
     for path, p in [("auto", 0), ("single", 0), ("split", 2), ("split", 4), ("split", 8), ("reread", 0)]:
-        if path == "single" and op == "softmax_bwd" and cols * 4 % 64 and _shift_held_vectors(cols, 4) > 8192:
+        if path == "single" and op == "softmax_bwd" and _shift_held_vectors(op, cols, 4) > 8192:
             # a shifted 32766-column row spans 8195 vectors, more than softmax
             # backward's largest path-1 tile (1024 x 8) holds: refused
             with pytest.raises(C.CreditError) as ei:

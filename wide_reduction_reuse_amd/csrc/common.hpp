@@ -124,32 +124,76 @@ __device__ __forceinline__ void buf_store(const RawVec<VB> &v, rsrc_t r, uint32_
     }
 }
 
-// Bytes [from, to) of a vector (0 <= from <= to <= VB, VB a multiple of 4):
-// its 4-byte words that lie wholly inside as word stores, the other bytes
-// one at a time.  Used for the vectors at the ends of rows whose first or
-// last word is shared with the neighbouring row (which writes the rest of
-// that word).
+// Bytes [lo, hi) (0 <= lo <= hi <= 4) of the 4-byte word w at byte offset
+// voff: a 2-byte store for a half-word wholly inside, single bytes
+// otherwise.  For the words at the ends of rows that share them with the
+// neighbouring row, which writes the other bytes.
+__device__ __forceinline__ void buf_store_word_part(uint32_t w, rsrc_t r, uint32_t voff, int lo, int hi)
+{
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int b0 = 2 * h;
+        if (lo <= b0 && b0 + 2 <= hi) {
+            __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(w >> (16 * h)), r,
+                                                  static_cast<int>(voff + b0), 0, kStreamStore);
+        } else {
+#pragma unroll
+            for (int b = b0; b < b0 + 2; ++b)
+                if (lo <= b && b < hi)
+                    __builtin_amdgcn_raw_buffer_store_b8(static_cast<unsigned char>(w >> (8 * b)), r,
+                                                         static_cast<int>(voff + b), 0, kStreamStore);
+        }
+    }
+}
+
+template <int VB>
+__device__ __forceinline__ uint32_t vec_word(const RawVec<VB> &v, int j)
+{
+    if constexpr (VB >= 8)
+        return v.w[j];
+    else
+        return v.w;
+}
+
+// Bytes [from, to) of a vector (0 <= from <= to <= VB, VB a multiple of 4),
+// one at a time: for a row that lies inside one vector (rare; kept small).
 template <int VB>
 __device__ __forceinline__ void buf_store_bytes(const RawVec<VB> &v, rsrc_t r, uint32_t voff, int from, int to)
 {
     static_assert(VB % 4 == 0, "vectors of whole words");
+    for (int b = from; b < to; ++b) {
+        uint32_t w = vec_word<VB>(v, 0);
 #pragma unroll
-    for (int j = 0; j < VB / 4; ++j) {
-        uint32_t w;
-        if constexpr (VB >= 8)
-            w = v.w[j];
-        else
-            w = v.w;
-        const uint32_t o = voff + 4u * static_cast<uint32_t>(j);
-        if (from <= 4 * j && 4 * j + 4 <= to) {
-            __builtin_amdgcn_raw_buffer_store_b32(w, r, static_cast<int>(o), 0, kStreamStore);
-        } else {
-#pragma unroll
-            for (int b = 0; b < 4; ++b)
-                if (from <= 4 * j + b && 4 * j + b < to)
-                    __builtin_amdgcn_raw_buffer_store_b8(static_cast<unsigned char>(w >> (8 * b)), r,
-                                                         static_cast<int>(o + b), 0, kStreamStore);
+        for (int j = 1; j < VB / 4; ++j)
+            w = (b >> 2) == j ? vec_word<VB>(v, j) : w;
+        __builtin_amdgcn_raw_buffer_store_b8(static_cast<unsigned char>(w >> (8 * (b & 3))), r,
+                                             static_cast<int>(voff + static_cast<uint32_t>(b)), 0, kStreamStore);
+    }
+}
+
+// Bytes [from, VB) of a vector (0 < from < VB): the part word, then the
+// whole words after it as one store.
+template <int VB>
+__device__ __forceinline__ void buf_store_from(const RawVec<VB> &v, rsrc_t r, uint32_t voff, int from)
+{
+    static_assert(VB % 4 == 0, "vectors of whole words");
+    const int w0 = (from + 3) >> 2;  // first whole word
+    if (from & 3)
+        buf_store_word_part(vec_word<VB>(v, w0 - 1), r, voff + 4u * static_cast<uint32_t>(w0 - 1), from & 3, 4);
+    if constexpr (VB == 16) {
+        typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+        if (w0 == 1) {
+            const u32x3 w = {v.w[1], v.w[2], v.w[3]};
+            __builtin_amdgcn_raw_buffer_store_b96(w, r, static_cast<int>(voff + 4u), 0, kStreamStore);
+        } else if (w0 == 2) {
+            const u32x2 w = {v.w[2], v.w[3]};
+            __builtin_amdgcn_raw_buffer_store_b64(w, r, static_cast<int>(voff + 8u), 0, kStreamStore);
+        } else if (w0 == 3) {
+            __builtin_amdgcn_raw_buffer_store_b32(v.w[3], r, static_cast<int>(voff + 12u), 0, kStreamStore);
         }
+    } else if constexpr (VB == 8) {
+        if (w0 == 1)
+            __builtin_amdgcn_raw_buffer_store_b32(v.w[1], r, static_cast<int>(voff + 4u), 0, kStreamStore);
     }
 }
 

@@ -384,11 +384,15 @@ constexpr bool rolls()
 // vector 0 may begin with hb output bytes of the previous row, and its vector
 // kpart (-1: none) holds the row's last element, the row's part of it being
 // its first tb output bytes.  Those two vectors are written byte-exactly (the
-// bytes outside the row belong to the neighbouring rows' owners).
+// bytes outside the row belong to the neighbouring rows' owners): the last
+// one through `whole`, the output span without a last word it shares with
+// the next row (so one vector store writes its whole words), and that word's
+// part separately.
 struct ShiftOut {
     int hb;
     int kpart;
     int tb;
+    rsrc_t whole;
 };
 
 // Apply h to the held tile and write it out; dst, and the parameter
@@ -400,7 +404,7 @@ struct ShiftOut {
 template <OpKind OP, class T, int VB, int IT, int W, int OWNER, bool SHIFT = false>
 __device__ __forceinline__ void store_tile(Tile<T, VB, IT> (&t)[OpTraits<OP>::kIn], rsrc_t dst,
                                            const ParamCache<OP, T, VB, IT, W, OWNER> &pc, int pos, const Coef &c,
-                                           const Srcs<OpTraits<OP>::kIn> &next, const ShiftOut *so = nullptr)
+                                           const Srcs<OpTraits<OP>::kIn> &next, const ShiftOut so = ShiftOut{})
 {
     using Op = OpTraits<OP>;
     constexpr int NI = Op::kIn;
@@ -439,10 +443,19 @@ __device__ __forceinline__ void store_tile(Tile<T, VB, IT> (&t)[OpTraits<OP>::kI
             const RawVec<VBO> ov = apply_vec<OP, T, VB, RAW>(in, g, b, vec_coef<OP, T, IT>(c, k));
             if constexpr (SHIFT) {
                 static_assert(NP == 0, "SHIFT rows: operators without parameters");
-                if ((k == 0 && so->hb > 0) || k == so->kpart)
-                    buf_store_bytes<VBO>(ov, dst, ooff, k == 0 ? so->hb : 0, k == so->kpart ? so->tb : VBO);
-                else
+                const bool head = k == 0 && so.hb > 0;
+                if (head && k == so.kpart) {
+                    buf_store_bytes<VBO>(ov, dst, ooff, so.hb, so.tb);  // a row inside one vector
+                } else if (head) {
+                    buf_store_from<VBO>(ov, dst, ooff, so.hb);
+                } else if (k == so.kpart) {
+                    buf_store<VBO, kStreamStore>(ov, so.whole, ooff);
+                    if (so.tb & 3)
+                        buf_store_word_part(vec_word<VBO>(ov, so.tb >> 2), dst,
+                                            ooff + static_cast<uint32_t>(so.tb & ~3), 0, so.tb & 3);
+                } else {
                     buf_store<VBO, kStreamStore>(ov, dst, ooff);
+                }
             } else {
                 buf_store<VBO, kStreamStore>(ov, dst, ooff);
             }
@@ -547,17 +560,18 @@ __device__ __forceinline__ rsrc_t row_span(const void *base, int64_t row, int64_
 // SHIFT rows: a row whose start is not 64-byte aligned is held from the
 // 64-byte boundary below its first byte, so that every wave's run of 16-byte
 // vectors covers whole 64-byte lines (on MI355X, rows that start inside a
-// line streamed 15-30% slower, in loads and stores alike).  Row r begins
-// s elements into its held span, the last s elements of row r - 1 (masked in
-// the reduction, never written); s is taken from x's address, and dy and y,
-// whose bases are 16-byte aligned too, use the same s (their held spans then
-// start 16-byte aligned, and line-aligned when their bases are congruent to
-// x's modulo 64).  A row that starts less than 64 bytes into the tensor is
-// held from the tensor's start instead (s = its offset in elements), so no
-// access precedes the tensor.  The held span ends with the 4-byte word that
-// holds the row's last element (its other bytes, when it has any, are the
-// next row's: read, masked, never written; after the tensor's last row they
-// lie inside the same word).
+// line streamed 10-30% slower, in loads and stores alike, short rows too).
+// Row r begins s elements into its held span, the last s elements of row
+// r - 1 (masked in the reduction, never written); s is taken from x's
+// address, and dy and y, whose bases are 16-byte aligned too, use the same s
+// (their held spans then start 16-byte aligned, and line-aligned when their
+// bases are congruent to x's modulo 64; the int8 codes' spans start 4- or
+// 8-byte aligned, as their vectors need).  A row that starts less than 64
+// bytes into the tensor is held from the tensor's start instead (s = its
+// offset in elements), so no access precedes the tensor.  The held span ends
+// with the 4-byte word that holds the row's last element (its other bytes,
+// when it has any, are the next row's: read, masked, never written; after
+// the tensor's last row they lie inside the same word).
 struct ShiftRow {
     int s;        // elements of the previous row in front of the row
     int64_t nv;   // 16-byte vectors of the held span
@@ -565,10 +579,11 @@ struct ShiftRow {
 };
 
 template <int EB, int E>
-__device__ __forceinline__ ShiftRow shift_geom(const void *x, int64_t row, int64_t cols)
+__device__ __forceinline__ ShiftRow shift_geom(const RowArgs &a, int64_t row)
 {
+    const int64_t cols = a.cols;
     const int64_t first = row * cols;
-    const uintptr_t at = reinterpret_cast<uintptr_t>(x) + static_cast<uintptr_t>(first * EB);
+    const uintptr_t at = reinterpret_cast<uintptr_t>(a.x) + static_cast<uintptr_t>(first * EB);
     int64_t s = static_cast<int64_t>(at & 63u) / EB;
     s = s < first ? s : first;
     ShiftRow g;
@@ -580,13 +595,14 @@ __device__ __forceinline__ ShiftRow shift_geom(const void *x, int64_t row, int64
 }
 
 // Vectors [first, first + nvec) of row `row`'s held span in a tensor of
-// EBT-byte elements and VBT-byte vectors.
+// EBT-byte elements and VBT-byte vectors;
+// whole = true: the span without a last word that the next row shares.
 template <int VBT, int EBT>
 __device__ __forceinline__ rsrc_t shift_span(const void *base, int64_t row, int64_t cols, int s, int64_t first,
-                                             int64_t nvec)
+                                             int64_t nvec, bool whole = false)
 {
     const int64_t lo = (row * cols - s) * EBT;
-    const int64_t len = ((s + cols) * EBT + 3) & ~INT64_C(3);
+    const int64_t len = whole ? ((s + cols) * EBT) & ~INT64_C(3) : ((s + cols) * EBT + 3) & ~INT64_C(3);
     int64_t n = len - first * VBT;
     n = n < nvec * VBT ? n : nvec * VBT;
     n = n > 0 ? n : 0;
@@ -782,7 +798,7 @@ __global__ __launch_bounds__(kWave *kWaveRowsPerWg) void single_wave_kernel(RowA
     int64_t row = uniform(static_cast<int64_t>(blockIdx.x) * kWaveRowsPerWg + threadIdx.x / kWave);
     ShiftRow g{};
     if constexpr (SHIFT)
-        g = shift_geom<EB, E>(a.x, row, a.cols);
+        g = shift_geom<EB, E>(a, row);
     Tile<T, VB, IT> t[Op::kIn];
     load_tile<T, VB, IT, kWave>(t, row_srcs<OP, VB, PEB, SHIFT>(a, row, nv, 0, row < a.rows ? (SHIFT ? g.nv : nv) : 0,
                                                                 g.s), lane);
@@ -805,7 +821,7 @@ __global__ __launch_bounds__(kWave *kWaveRowsPerWg) void single_wave_kernel(RowA
         if constexpr (SHIFT) {
             so = shift_row<IT, E, OEB>(loc, g, 0, g.nv, lane);
             kv = count_valid<IT, kWave>(g.nv, lane);
-            gn = shift_geom<EB, E>(a.x, next, a.cols);
+            gn = shift_geom<EB, E>(a, next);
         }
         const auto wp = tile_partial<OP, T, VB, IT, kWave, kOwnerWaves>(t, kv, pc, lane, loc);
         const Coef c = Op::template finalize<T>(wp, loc, a.cols, a.eps);
@@ -814,7 +830,9 @@ __global__ __launch_bounds__(kWave *kWaveRowsPerWg) void single_wave_kernel(RowA
             row_srcs<OP, VB, PEB, SHIFT>(a, next, nv, 0, next < a.rows ? (SHIFT ? gn.nv : nv) : 0, gn.s);
         const rsrc_t dst = SHIFT ? shift_span<VBO, OEB>(a.y, row, a.cols, g.s, 0, g.nv)
                                  : row_span<VBO, PEB>(a.y, row, a.cols, nv, 0, nv);
-        store_tile<OP, T, VB, IT, kWave, kOwnerWaves, SHIFT>(t, dst, pc, lane, c, nsrc, &so);
+        if constexpr (SHIFT)
+            so.whole = shift_span<VBO, OEB>(a.y, row, a.cols, g.s, 0, g.nv, true);
+        store_tile<OP, T, VB, IT, kWave, kOwnerWaves, SHIFT>(t, dst, pc, lane, c, nsrc, so);
         load_next<OP, T, VB, IT, kWave, kOwnerWaves>(t, nsrc, lane);
         g = gn;
     }
@@ -854,7 +872,7 @@ __global__ __launch_bounds__(BLOCK) void single_wg_kernel(RowArgs a)
     int64_t row = blockIdx.x;
     ShiftRow g{};
     if constexpr (SHIFT)
-        g = shift_geom<EB, E>(a.x, row, a.cols);
+        g = shift_geom<EB, E>(a, row);
     Tile<T, VB, IT> t[Op::kIn];
     load_tile<T, VB, IT, kWave>(t, row_srcs<OP, VB, PEB, SHIFT>(a, row, nv, 0, SHIFT ? g.nv : nreg, g.s), pos);
     PC pc;
@@ -876,7 +894,7 @@ __global__ __launch_bounds__(BLOCK) void single_wg_kernel(RowArgs a)
         if constexpr (SHIFT) {
             so = shift_row<IT, E, OEB>(loc, g, 0, g.nv, pos);
             kv = count_valid<IT, kWave>(g.nv, pos);
-            gn = shift_geom<EB, E>(a.x, next, a.cols);
+            gn = shift_geom<EB, E>(a, next);
         }
         typename Op::Partial lp;
         if constexpr (kLds)
@@ -892,7 +910,9 @@ __global__ __launch_bounds__(BLOCK) void single_wg_kernel(RowArgs a)
             row_srcs<OP, VB, PEB, SHIFT>(a, next, nv, 0, next < a.rows ? (SHIFT ? gn.nv : nreg) : 0, gn.s);
         const rsrc_t dst = SHIFT ? shift_span<VBO, OEB>(a.y, row, a.cols, g.s, 0, g.nv)
                                  : row_span<VBO, PEB>(a.y, row, a.cols, nv, 0, nreg);
-        store_tile<OP, T, VB, IT, BLOCK, kOwnerRow, SHIFT>(t, dst, pc, pos, c, nsrc, &so);
+        if constexpr (SHIFT)
+            so.whole = shift_span<VBO, OEB>(a.y, row, a.cols, g.s, 0, g.nv, true);
+        store_tile<OP, T, VB, IT, BLOCK, kOwnerRow, SHIFT>(t, dst, pc, pos, c, nsrc, so);
         if constexpr (kLds)
             lds_store<OP, T, VB, BLOCK, LT>(lds_row, span<VBO>(a.y, row * nv + nreg, nl), span<VB>(a.gamma, nreg, nl),
                                             span<VB>(a.beta, nreg, nl), tid,
@@ -995,7 +1015,7 @@ __global__ __launch_bounds__(BLOCK) void split_kernel(SplitArgs a)
     };
     ShiftRow g{};
     if constexpr (SHIFT)
-        g = shift_geom<EB, E>(a.r.x, k, a.r.cols);
+        g = shift_geom<EB, E>(a.r, k);
 
     Tile<T, VB, IT> t[Op::kIn];
     PC pc;
@@ -1036,7 +1056,7 @@ __global__ __launch_bounds__(BLOCK) void split_kernel(SplitArgs a)
             const int64_t nsr = shift_ns(g);
             so = shift_row<IT, E, OEB>(loc, g, v0, nsr, pos);
             kv = count_valid<IT, kWave>(nsr, pos);
-            gn = shift_geom<EB, E>(a.r.x, next, a.r.cols);
+            gn = shift_geom<EB, E>(a.r, next);
         }
         Partial lp;
         if constexpr (kLds)
@@ -1090,7 +1110,9 @@ __global__ __launch_bounds__(BLOCK) void split_kernel(SplitArgs a)
                 a.r, next, nv, v0, next < a.r.rows ? (SHIFT ? shift_ns(gn) : nreg) : 0, gn.s);
             const rsrc_t dst = SHIFT ? shift_span<VBO, OEB>(a.r.y, row, a.r.cols, g.s, v0, shift_ns(g))
                                      : row_span<VBO, PEB>(a.r.y, row, a.r.cols, nv, v0, nreg);
-            store_tile<OP, T, VB, IT, BLOCK, kOwnerSlice, SHIFT>(t, dst, pc, pos, cf, nsrc, &so);
+            if constexpr (SHIFT)
+                so.whole = shift_span<VBO, OEB>(a.r.y, row, a.r.cols, g.s, v0, shift_ns(g), true);
+            store_tile<OP, T, VB, IT, BLOCK, kOwnerSlice, SHIFT>(t, dst, pc, pos, cf, nsrc, so);
             if constexpr (kLds)
                 lds_store<OP, T, VB, BLOCK, LT>(lds_row, span<VBO>(a.r.y, row * nv + v0 + nreg, nl),
                                                 span<VB>(a.r.gamma, v0 + nreg, nl), span<VB>(a.r.beta, v0 + nreg, nl),

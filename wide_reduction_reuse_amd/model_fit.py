@@ -72,7 +72,7 @@ def row_kind(op: str, dt: str, cols: int) -> int:
     """The held register tiles' row kind for this width (the library's
     held_row_kind): 2 for rows of the operators without parameter vectors
     (softmax, softmax backward, the quantizer) whose byte length is not a
-    multiple of 64 (held from the 64-byte boundary below their start), 1 for
+    multiple of 64 (held from the boundary below their start), 1 for
     rows of LayerNorm, RMSNorm and fp32 LayerNorm backward whose byte length
     is a multiple of 4 but not of 16 (a partial last vector), else 0."""
     nbytes = cols * (4 if dt == "f32" else 2)
