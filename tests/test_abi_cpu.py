@@ -184,12 +184,12 @@ def test_selector_legality_on_cpu():
 
 
 def test_partial_rows_are_held_as_16_byte_vectors():
-    # byte length a multiple of 4 but not of 16, operators with parameter
-    # vectors (LayerNorm, RMSNorm, fp32 LayerNorm backward): paths 1 and 2
-    # hold the row as 16-byte vectors (the last partial) and reread it by
-    # element; odd-length bf16 rows of these operators use one-element tiles
+    # byte length a multiple of 4 but not of 16, LayerNorm and fp32 LayerNorm
+    # backward: paths 1 and 2 hold the row as 16-byte vectors from its first
+    # byte (the last partial) and reread it by element; odd-length bf16 rows
+    # of LayerNorm backward use one-element tiles
     L = C.lib()
-    for op, dt, cols in [("layernorm", "bf16", 1002), ("rmsnorm", "f32", 3), ("layernorm_bwd", "f32", 1001)]:
+    for op, dt, cols in [("layernorm", "bf16", 1002), ("layernorm", "f32", 3), ("layernorm_bwd", "f32", 1001)]:
         p = C.credit_plan(op, dt, 64, cols, "single")
         assert p.vec_bytes == 16
         assert C.credit_plan(op, dt, 64, cols, "reread").vec_bytes == 16 // (4 if dt == "f32" else 8)
@@ -198,8 +198,7 @@ def test_partial_rows_are_held_as_16_byte_vectors():
         assert L.credit_run_plan(C.OPS[op], _ops(x=A, dy=G, gamma=G, beta=G, y=B), 4, cols, 1e-5,
                                  C.DTYPES[dt], ctypes.byref(plan), None) == 4
     assert C.credit_plan("layernorm_bwd", "f32", 64, 100003, "split", 8).vec_bytes == 16
-    for op in ("layernorm", "rmsnorm"):
-        assert C.credit_plan(op, "bf16", 64, 1001, "single").vec_bytes == 2  # odd bytes / 4
+    assert C.credit_plan("layernorm_bwd", "bf16", 64, 1001, "single").vec_bytes == 2  # odd bytes / 4
 
 
 def _max_shift_bytes(cols, eb):
@@ -210,17 +209,19 @@ def _max_shift_bytes(cols, eb):
 
 
 def test_shifted_rows_are_held_from_the_line_below():
-    # rows whose byte length is not a multiple of 64, of the operators
-    # without parameter vectors (softmax, softmax backward, the int8
-    # quantizer): paths 1 and 2 hold them as 16-byte vectors from the 64-byte
-    # line below each row's start, so a tile must hold the row plus the
-    # largest such offset; the reread path reads them by element (or by
-    # 16-byte vector when the byte length is a multiple of 16)
+    # rows whose byte length is not a multiple of 64, of softmax, softmax
+    # backward, the quantizer, RMSNorm, and LayerNorm's odd-length bf16 rows:
+    # paths 1 and 2 hold them as 16-byte vectors from the 64-byte line below
+    # each row's start, so a tile must hold the row plus the largest such
+    # offset; the reread path reads them by element (or by 16-byte vector
+    # when the byte length is a multiple of 16)
     L = C.lib()
     cases = [("softmax", "f32", 1001), ("softmax", "f32", 1004), ("softmax", "f32", 4100), ("softmax", "f32", 5001),
              ("softmax", "bf16", 1), ("softmax", "bf16", 1001), ("softmax", "bf16", 50257),
              ("softmax", "bf16", 50264), ("softmax_bwd", "bf16", 30001), ("softmax_bwd", "f32", 30006),
-             ("quantize_int8", "f32", 1001), ("quantize_int8", "bf16", 1001), ("quantize_int8", "f32", 4100)]
+             ("quantize_int8", "f32", 1001), ("quantize_int8", "bf16", 1001), ("quantize_int8", "f32", 4100),
+             ("layernorm", "bf16", 1001), ("layernorm", "bf16", 50257), ("rmsnorm", "f32", 3),
+             ("rmsnorm", "bf16", 50257), ("rmsnorm", "f32", 30001)]
     for op, dt, cols in cases:
         eb = 4 if dt == "f32" else 2
         p = C.credit_plan(op, dt, 64, cols, "single")
@@ -231,8 +232,8 @@ def test_shifted_rows_are_held_from_the_line_below():
         assert C.credit_plan(op, dt, 64, cols, "reread").vec_bytes == rvb
         if rvb != 16:
             plan = C.Plan.make(C.PATH_SINGLE_WG, 1, p.block_threads, p.items, eb)
-            assert L.credit_run_plan(C.OPS[op], _ops(x=A, dy=G, y=B, row_out=G), 4, cols, 0.0, C.DTYPES[dt],
-                                     ctypes.byref(plan), None) == 4
+            assert L.credit_run_plan(C.OPS[op], _ops(x=A, dy=G, gamma=G, beta=G, y=B, row_out=G), 4, cols, 1e-5,
+                                     C.DTYPES[dt], ctypes.byref(plan), None) == 4
     # a tile that holds the row but not the row plus its largest offset is
     # refused: 4100 fp32 elements (1025 vectors) plus up to 48 bytes need
     # 1028 vectors; 1024 x 1 holds 1024

@@ -66,15 +66,18 @@ def test_row_kind_matches_the_kernel_families():
     assert F.row_kind("softmax", "bf16", 50257) == 2
     assert F.row_kind("quantize_int8", "f32", 1001) == 2
     assert F.row_kind("softmax_bwd", "f32", 48) == 0       # 192 bytes: whole lines
-    assert F.row_kind("rmsnorm", "f32", 30001) == 1        # parameters: a partial last vector
-    assert F.row_kind("layernorm", "bf16", 20002) == 1
-    assert F.row_kind("rmsnorm", "bf16", 50257) == 0       # 2-byte accesses throughout
-    assert F.row_kind("layernorm_bwd", "bf16", 20002) == 0
+    assert F.row_kind("rmsnorm", "f32", 30001) == 2        # parameters realigned per row
+    assert F.row_kind("layernorm", "bf16", 20002) == 1     # LayerNorm shifts odd bf16 rows only
+    assert F.row_kind("layernorm", "bf16", 20001) == 2
+    assert F.row_kind("layernorm", "f32", 1004) == 0
+    assert F.row_kind("rmsnorm", "bf16", 50257) == 2
+    assert F.row_kind("layernorm_bwd", "f32", 30001) == 1  # parameters in the reduction: a partial last vector
+    assert F.row_kind("layernorm_bwd", "bf16", 20002) == 0  # 2-byte accesses throughout
     # the library holds kind-2 widths with room for the shift, kind-1 widths without
     assert C.credit_plan("softmax", "f32", 64, 4100, "single").block_threads * \
         C.credit_plan("softmax", "f32", 64, 4100, "single").items * 4 >= 4100 + 12
-    assert C.credit_plan("rmsnorm", "f32", 64, 1022, "single").block_threads * \
-        C.credit_plan("rmsnorm", "f32", 64, 1022, "single").items * 4 >= 1022
+    assert C.credit_plan("layernorm_bwd", "f32", 64, 1022, "single").block_threads * \
+        C.credit_plan("layernorm_bwd", "f32", 64, 1022, "single").items * 4 >= 1022
 
 
 def test_occupancy_table_and_written_calibration_load(tmp_path):

@@ -151,9 +151,23 @@ def _ladder(macro):
     return [(64, int(a)) if not b else (int(a), int(b)) for a, b in pairs]
 
 
-# operators without parameter vectors: their held tiles hold rows that are
-# not whole 64-byte lines from the line boundary below each row's start
-SHIFT_OPS = ("softmax", "softmax_bwd", "quantize_int8")
+# operators whose held tiles hold rows that are not whole 64-byte lines from
+# the line boundary below each row's start (RMSNorm's parameter vector, and
+# LayerNorm's two, realigned to each row; LayerNorm shifts its odd-length
+# bf16 rows only, and holds its other rows as they are or with a partial
+# last vector)
+SHIFT_OPS = ("softmax", "softmax_bwd", "quantize_int8", "rmsnorm", "layernorm")
+
+
+def _row_kind(op, dt, cols):
+    """The library's row kind (held_row_kind), restated: 2 shifted, 1 a
+    partial last vector, 0 whole vectors (or one-element tiles)."""
+    nbytes = cols * W.ELEM_BYTES[dt]
+    if op in ("softmax", "softmax_bwd", "quantize_int8", "rmsnorm") or (op == "layernorm" and nbytes % 4):
+        return 2 if nbytes % 64 else 0
+    if op == "layernorm" or (op == "layernorm_bwd" and dt == "f32"):
+        return 1 if nbytes % 16 and nbytes % 4 == 0 else 0
+    return 0
 
 
 def _tile_cases():
@@ -192,9 +206,11 @@ def _tile_cases():
 TILE_CASES = _tile_cases()
 
 
-def _tile_excluded(op, kind, block, items, vb=16, dt="f32"):
+def _tile_excluded(op, kind, block, items, vb=16, dt="f32", shift=False):
     """The tiles the kernel registry leaves out (they spilled registers): its
     rule restated, so that the library's refusals are checked against it."""
+    if shift and op == "layernorm" and kind == "wg" and block == 1024 and items == 16:
+        return True
     if op == "layernorm_bwd" and dt == "bf16" and kind != "reread" and block >= 512 and 2 * items * vb > 256:
         return True
     if kind == "reread" or block < 1024:
@@ -233,11 +249,12 @@ def test_every_tile(op, dt, kind, block, items, p, cols):
 
 
 # ---------------------------------------------------------------------------
-# rows whose last 16-byte vector is partial: the held tiles of LayerNorm,
-# RMSNorm and LayerNorm backward (the operators with parameter vectors) hold
-# such rows as 16-byte vectors and mask the missing elements of the last one
+# rows whose last 16-byte vector is partial: the held tiles of LayerNorm and
+# fp32 LayerNorm backward (whose parameters enter the reduction) hold such
+# rows as 16-byte vectors from their first byte and mask the missing elements
+# of the last one
 # ---------------------------------------------------------------------------
-PART_OPS = ("layernorm", "rmsnorm", "layernorm_bwd")
+PART_OPS = ("layernorm", "layernorm_bwd")
 
 
 def _partial_tile_cases():
@@ -305,12 +322,12 @@ def test_every_tile_partial_last_vector(op, dt, kind, block, items, p, cols):
 # ---------------------------------------------------------------------------
 def _shift_held_vectors(op, cols, eb):
     """The 16-byte vectors the held span of a row needs (the library's rule,
-    restated): rows that are not whole 64-byte lines are held from the 64-byte
-    line below their start, with up to 64 - min(g, 16) bytes in front (g the
-    lowest set bit of the byte length); rows of whole lines as they are."""
+    restated): shifted rows are held from the 64-byte line below their
+    start, with up to 64 - min(g, 16) bytes in front (g the lowest set bit of
+    the byte length); other rows as they are."""
     nbytes = cols * eb
-    if nbytes % 64 == 0:
-        return nbytes // 16
+    if _row_kind(op, "f32" if eb == 4 else "bf16", cols) != 2:
+        return (nbytes + 15) // 16
     g = nbytes & -nbytes
     return (nbytes + 64 - min(g, 16) + 15) // 16
 
@@ -346,7 +363,12 @@ def _shift_tile_cases():
     for op in SHIFT_OPS:
         for dt in W.DTYPES:
             eb = W.ELEM_BYTES[dt]
-            classes = ("odd", "part", "v16") if dt == "bf16" else ("part", "v16")
+            if op == "layernorm":  # shifts its odd-length bf16 rows only
+                classes = ("odd",) if dt == "bf16" else ()
+            else:
+                classes = ("odd", "part", "v16") if dt == "bf16" else ("part", "v16")
+            if not classes:
+                continue
             for kind, tiles in ladders.items():
                 for block, items in tiles:
                     cap = block * items
@@ -388,7 +410,7 @@ def test_every_tile_shifted(op, dt, kind, block, items, p, cols):
     inp = W.generate(w)
     path = C.PATH_SPLIT_ROW if kind == "split" else C.PATH_SINGLE_WG
     plan = C.Plan.make(path, p, block, items, 16, wgs_per_cu=1)
-    if _tile_excluded(op, kind, block, items, dt=dt):
+    if _tile_excluded(op, kind, block, items, dt=dt, shift=_row_kind(op, dt, cols) == 2):
         with pytest.raises(C.CreditError) as ei:
             _run(inp, plan=plan)
         assert ei.value.status == 2

@@ -38,7 +38,7 @@ void register_op_dtype(std::vector<KernelEntry> &v)
 #define WGP(b, it) CREDIT_KP(kKindWg, VB, b, it, single_wg_kernel<OP, T, VB, b, it, true>);
 #define SPLITP(b, it) CREDIT_KP(kKindSplit, VB, b, it, split_kernel<OP, T, VB, b, it, false, true>);
 #define CREDIT_KO(kind, vb, block, items, ...)                                                                  \
-    if constexpr (op_has_shift(OP) && tile_enabled(OP, DT, kind, block, items, vb))                                   \
+    if constexpr (op_has_shift(OP, DT) && tile_enabled(OP, DT, kind, block, items, vb, 2))                            \
         v.push_back(KernelEntry{kind, OP, DT, vb, block, items, reinterpret_cast<const void *>(&__VA_ARGS__), 2})
 #define CREDIT_KL(kind, block, items, lt, ...)                                                                \
     if constexpr (lds_tile_enabled(OP, DT, kind, block, items))                                                        \

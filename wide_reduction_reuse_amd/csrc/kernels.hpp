@@ -253,14 +253,87 @@ constexpr int param_lds_vectors()
 // W: threads that together hold the columns (they share one LDS copy of
 // W * IT vectors per parameter).  A thread's vector k is vector pos + 64 k of
 // the row or slice (pos includes its wave's run offset).
-template <OpKind OP, class T, int VB, int IT, int W, int OWNER>
+//
+// SH: the row is held shifted (SHIFT kernels), so held vector v covers
+// columns v * E - s of a row that begins s elements into its held span, s
+// changing from row to row: the parameters are re-read for every row
+// (kParamDirect) from descriptors over the whole parameter arrays, at byte
+// offset v * VB - s * b, each vector assembled from the two aligned vectors
+// it straddles (shift()).
+template <OpKind OP, class T, int VB, int IT, int W, int OWNER, bool SH = false>
 struct ParamCache {
-    static constexpr int kMode = param_mode<OP, VB, IT, W, OWNER>();
+    static constexpr int kMode = SH && OpTraits<OP>::kParams > 0 ? kParamDirect : param_mode<OP, VB, IT, W, OWNER>();
     static constexpr int kNp = OpTraits<OP>::kParams;
     static constexpr int kRegs = kMode == kParamReg ? IT : 1;
     rsrc_t gam, bet;         // kParamDirect
     RawVec<VB> g[kRegs], b[kRegs];  // kParamReg
     const RawVec<VB> *lds;   // kParamLds: [kNp][W * IT], indexed by vector
+    int32_t adj = 0;         // SH: byte offset of the slice's first held vector in the parameter arrays
+
+    // SH: the row's shift (s elements of the previous row in front, held
+    // vectors from v0 on); adj may be negative (the first vectors of a row
+    // that starts mid-line cover columns before 0, which are never used).
+    __device__ __forceinline__ void shift(int s, int64_t v0)
+    {
+        adj = static_cast<int32_t>(v0 * VB) - s * static_cast<int32_t>(StorageTraits<T>::kBytes);
+    }
+
+    // SH: the parameter vector at byte offset o (o = held offset + adj) of
+    // descriptor r: the aligned vectors A (at o rounded down to 16) and B (the
+    // next), and the 16 bytes from o.  Offsets below 0 wrap past the end of
+    // the descriptor and load zeros.
+    __device__ __forceinline__ static RawVec<VB> load_shifted(rsrc_t r, int32_t o, int rb)
+    {
+        static_assert(VB == 16, "shifted parameter vectors: 16 bytes");
+        const int32_t q = o & ~15;
+        const RawVec<16> A = buf_load<16, kKeep>(r, static_cast<uint32_t>(q));
+        if (rb == 0)
+            return A;
+        const RawVec<16> B = buf_load<16, kKeep>(r, static_cast<uint32_t>(q + 16));
+        const uint32_t c[8] = {A.w[0], A.w[1], A.w[2], A.w[3], B.w[0], B.w[1], B.w[2], B.w[3]};
+        const uint32_t sh = static_cast<uint32_t>(rb & 3) * 8u;
+        RawVec<16> out;
+        switch (rb >> 2) {
+#define CREDIT_FUNNEL(W0)                                                                               \
+    case W0:                                                                                            \
+        out.w = u32x4{static_cast<uint32_t>((((uint64_t)c[W0 + 1] << 32) | c[W0]) >> sh),               \
+                      static_cast<uint32_t>((((uint64_t)c[W0 + 2] << 32) | c[W0 + 1]) >> sh),           \
+                      static_cast<uint32_t>((((uint64_t)c[W0 + 3] << 32) | c[W0 + 2]) >> sh),           \
+                      static_cast<uint32_t>((((uint64_t)c[W0 + 4] << 32) | c[W0 + 3]) >> sh)};          \
+        break;
+            CREDIT_FUNNEL(0)
+            CREDIT_FUNNEL(1)
+            CREDIT_FUNNEL(2)
+        default:
+            out.w = u32x4{static_cast<uint32_t>((((uint64_t)c[4] << 32) | c[3]) >> sh),
+                          static_cast<uint32_t>((((uint64_t)c[5] << 32) | c[4]) >> sh),
+                          static_cast<uint32_t>((((uint64_t)c[6] << 32) | c[5]) >> sh),
+                          static_cast<uint32_t>((((uint64_t)c[7] << 32) | c[6]) >> sh)};
+            break;
+#undef CREDIT_FUNNEL
+        }
+        return out;
+    }
+
+    // kParamDirect: the parameter vectors at held byte offset `off` of the slice.
+    __device__ __forceinline__ void direct(uint32_t off, RawVec<VB> &gk, RawVec<VB> &bk) const
+    {
+        if constexpr (SH) {
+            // off is a multiple of 16, so o's offset in its 16-byte vector is
+            // adj's, the same in every lane
+            const int32_t o = static_cast<int32_t>(off) + adj;
+            const int rb = __builtin_amdgcn_readfirstlane(adj) & 15;
+            if constexpr (kNp >= 1)
+                gk = load_shifted(gam, o, rb);
+            if constexpr (kNp >= 2)
+                bk = load_shifted(bet, o, rb);
+        } else {
+            if constexpr (kNp >= 1)
+                gk = buf_load<VB, kKeep>(gam, off);
+            if constexpr (kNp >= 2)
+                bk = buf_load<VB, kKeep>(bet, off);
+        }
+    }
 
     // Call once per owner, before the row loop.  `nthreads` threads with ids
     // `tid` fill the LDS copy (kParamLds); the caller puts a barrier between
@@ -306,10 +379,7 @@ struct ParamCache {
     __device__ __forceinline__ void fetch(int k, int pos, RawVec<VB> &gk, RawVec<VB> &bk) const
     {
         if constexpr (kMode == kParamDirect) {
-            const uint32_t off = static_cast<uint32_t>(pos + k * kWave) * VB;
-            gk = buf_load<VB, kKeep>(gam, off);
-            if constexpr (kNp >= 2)
-                bk = buf_load<VB, kKeep>(bet, off);
+            direct(static_cast<uint32_t>(pos + k * kWave) * VB, gk, bk);
         } else {
             get(k, pos, gk, bk);
         }
@@ -320,9 +390,9 @@ struct ParamCache {
 // the operator reduces over them.  (A second, unmasked copy for full waves
 // behind a wave-uniform branch was measured to raise register use by a third
 // with no gain: the masks are register selects.)
-template <OpKind OP, class T, int VB, int IT, int W, int OWNER, class L>
+template <OpKind OP, class T, int VB, int IT, int W, int OWNER, class L, bool SH = false>
 __device__ __forceinline__ typename OpTraits<OP>::Partial tile_partial(
-    Tile<T, VB, IT> (&t)[OpTraits<OP>::kIn], int kv, const ParamCache<OP, T, VB, IT, W, OWNER> &pc, int pos,
+    Tile<T, VB, IT> (&t)[OpTraits<OP>::kIn], int kv, const ParamCache<OP, T, VB, IT, W, OWNER, SH> &pc, int pos,
     L &loc)
 {
     using Op = OpTraits<OP>;
@@ -395,6 +465,31 @@ struct ShiftOut {
     rsrc_t whole;
 };
 
+// One output vector, k-th of the thread's: SHIFT rows write the vectors at the
+// row's ends exactly (see ShiftOut), every other vector is one store.
+template <int VBO, bool SHIFT>
+__device__ __forceinline__ void store_out_vec(const RawVec<VBO> &ov, rsrc_t dst, uint32_t ooff, int k,
+                                              const ShiftOut &so)
+{
+    if constexpr (SHIFT) {
+        const bool head = k == 0 && so.hb > 0;
+        if (head && k == so.kpart) {
+            buf_store_bytes<VBO>(ov, dst, ooff, so.hb, so.tb);  // a row inside one vector
+        } else if (head) {
+            buf_store_from<VBO>(ov, dst, ooff, so.hb);
+        } else if (k == so.kpart) {
+            buf_store<VBO, kStreamStore>(ov, so.whole, ooff);
+            if (so.tb & 3)
+                buf_store_word_part(vec_word<VBO>(ov, so.tb >> 2), dst, ooff + static_cast<uint32_t>(so.tb & ~3), 0,
+                                    so.tb & 3);
+        } else {
+            buf_store<VBO, kStreamStore>(ov, dst, ooff);
+        }
+    } else {
+        buf_store<VBO, kStreamStore>(ov, dst, ooff);
+    }
+}
+
 // Apply h to the held tile and write it out; dst, and the parameter
 // descriptors, cover the same columns (the row or slice).  When rolling,
 // vector k of the next row (`next`, a zero-length descriptor when there is
@@ -403,14 +498,14 @@ struct ShiftOut {
 // row's ends are written byte-exactly (see ShiftOut).
 template <OpKind OP, class T, int VB, int IT, int W, int OWNER, bool SHIFT = false>
 __device__ __forceinline__ void store_tile(Tile<T, VB, IT> (&t)[OpTraits<OP>::kIn], rsrc_t dst,
-                                           const ParamCache<OP, T, VB, IT, W, OWNER> &pc, int pos, const Coef &c,
+                                           const ParamCache<OP, T, VB, IT, W, OWNER, SHIFT> &pc, int pos, const Coef &c,
                                            const Srcs<OpTraits<OP>::kIn> &next, const ShiftOut so = ShiftOut{})
 {
     using Op = OpTraits<OP>;
     constexpr int NI = Op::kIn;
     constexpr int NP = held_out_params<OP, T>();
     constexpr bool RAW = holds_raw<OP, T>();
-    constexpr int MODE = ParamCache<OP, T, VB, IT, W, OWNER>::kMode;
+    constexpr int MODE = ParamCache<OP, T, VB, IT, W, OWNER, SHIFT>::kMode;
     constexpr int VBO = out_vb<OP, T, VB>();
     constexpr int G = kWave;  // vector stride between a thread's vectors
 #pragma unroll
@@ -441,24 +536,7 @@ __device__ __forceinline__ void store_tile(Tile<T, VB, IT> (&t)[OpTraits<OP>::kI
             for (int i = 0; i < NI; ++i)
                 in[i] = t[i].v[k];
             const RawVec<VBO> ov = apply_vec<OP, T, VB, RAW>(in, g, b, vec_coef<OP, T, IT>(c, k));
-            if constexpr (SHIFT) {
-                static_assert(NP == 0, "SHIFT rows: operators without parameters");
-                const bool head = k == 0 && so.hb > 0;
-                if (head && k == so.kpart) {
-                    buf_store_bytes<VBO>(ov, dst, ooff, so.hb, so.tb);  // a row inside one vector
-                } else if (head) {
-                    buf_store_from<VBO>(ov, dst, ooff, so.hb);
-                } else if (k == so.kpart) {
-                    buf_store<VBO, kStreamStore>(ov, so.whole, ooff);
-                    if (so.tb & 3)
-                        buf_store_word_part(vec_word<VBO>(ov, so.tb >> 2), dst,
-                                            ooff + static_cast<uint32_t>(so.tb & ~3), 0, so.tb & 3);
-                } else {
-                    buf_store<VBO, kStreamStore>(ov, dst, ooff);
-                }
-            } else {
-                buf_store<VBO, kStreamStore>(ov, dst, ooff);
-            }
+            store_out_vec<VBO, SHIFT>(ov, dst, ooff, k, so);
             if constexpr (rolls<MODE, OWNER, NI>())
 #pragma unroll
                 for (int i = 0; i < NI; ++i) {
@@ -467,18 +545,15 @@ __device__ __forceinline__ void store_tile(Tile<T, VB, IT> (&t)[OpTraits<OP>::kI
                 }
         }
     } else {
-        constexpr int GP = param_group<IT, VB, NP>();
+        // (shifted parameter vectors take two loads each and a funnel shift:
+        // one vector at a time keeps their registers few)
+        constexpr int GP = SHIFT ? 1 : param_group<IT, VB, NP>();
 #pragma unroll
         for (int kb = 0; kb < IT; kb += GP) {
             RawVec<VB> g[GP], b[GP];
 #pragma unroll
-            for (int j = 0; j < GP; ++j) {
-                const uint32_t off = base + static_cast<uint32_t>((kb + j) * G * VB);
-                if constexpr (NP >= 1)
-                    g[j] = buf_load<VB, kKeep>(pc.gam, off);
-                if constexpr (NP >= 2)
-                    b[j] = buf_load<VB, kKeep>(pc.bet, off);
-            }
+            for (int j = 0; j < GP; ++j)
+                pc.direct(base + static_cast<uint32_t>((kb + j) * G * VB), g[j], b[j]);
 #pragma unroll
             for (int j = 0; j < GP; ++j) {
                 const uint32_t off = base + static_cast<uint32_t>((kb + j) * G * VB);
@@ -487,19 +562,19 @@ __device__ __forceinline__ void store_tile(Tile<T, VB, IT> (&t)[OpTraits<OP>::kI
 #pragma unroll
                 for (int i = 0; i < NI; ++i)
                     in[i] = t[i].v[kb + j];
-                buf_store<VBO, kStreamStore>(apply_vec<OP, T, VB, RAW>(in, g[j], b[j], vec_coef<OP, T, IT>(c, kb + j)), dst,
-                                             ooff);
+                store_out_vec<VBO, SHIFT>(apply_vec<OP, T, VB, RAW>(in, g[j], b[j], vec_coef<OP, T, IT>(c, kb + j)),
+                                          dst, ooff, kb + j, so);
             }
         }
     }
 }
 
 // After store_tile: load the next row unless store_tile already did.
-template <OpKind OP, class T, int VB, int IT, int W, int OWNER>
+template <OpKind OP, class T, int VB, int IT, int W, int OWNER, bool SH = false>
 __device__ __forceinline__ void load_next(Tile<T, VB, IT> (&t)[OpTraits<OP>::kIn],
                                           const Srcs<OpTraits<OP>::kIn> &next, int pos)
 {
-    if constexpr (!rolls<ParamCache<OP, T, VB, IT, W, OWNER>::kMode, OWNER, OpTraits<OP>::kIn>())
+    if constexpr (!rolls<ParamCache<OP, T, VB, IT, W, OWNER, SH>::kMode, OWNER, OpTraits<OP>::kIn>())
         load_tile<T, VB, IT, kWave>(t, next, pos);
 }
 
@@ -608,6 +683,18 @@ __device__ __forceinline__ rsrc_t shift_span(const void *base, int64_t row, int6
     n = n > 0 ? n : 0;
     const uintptr_t p = reinterpret_cast<uintptr_t>(base) + static_cast<uintptr_t>(lo + first * VBT);
     return make_rsrc(reinterpret_cast<const void *>(p), static_cast<uint32_t>(n));
+}
+
+// The parameter vectors of held vectors [first, first + nvec) (row_span of
+// row 0); SHIFT rows: the whole parameter array, up to the 4-byte word that
+// holds its last element (ParamCache shifts the offsets row by row).
+template <int VB, int PEB, bool SHIFT>
+__device__ __forceinline__ rsrc_t param_span(const void *base, int64_t cols, int64_t nv, int64_t first, int64_t nvec)
+{
+    if constexpr (SHIFT)
+        return make_rsrc(base, static_cast<uint32_t>((cols * PEB + 3) & ~INT64_C(3)));
+    else
+        return row_span<VB, PEB>(base, 0, cols, nv, first, nvec);
 }
 
 // The row inputs (x, and dy for two-input operators): `nvec` vectors from
@@ -781,7 +868,7 @@ template <OpKind OP, class T, int VB, int IT, bool PART = false, bool SHIFT = fa
 __global__ __launch_bounds__(kWave *kWaveRowsPerWg) void single_wave_kernel(RowArgs a)
 {
     using Op = OpTraits<OP>;
-    using PC = ParamCache<OP, T, VB, IT, kWave, kOwnerWaves>;
+    using PC = ParamCache<OP, T, VB, IT, kWave, kOwnerWaves, SHIFT>;
     using Loc = std::conditional_t<SHIFT, LocalShift, std::conditional_t<PART, LocalPart, Local>>;
     constexpr int EB = StorageTraits<T>::kBytes;
     constexpr int E = VB / EB;
@@ -789,8 +876,8 @@ __global__ __launch_bounds__(kWave *kWaveRowsPerWg) void single_wave_kernel(RowA
     constexpr int OEB = StorageTraits<OutT<OP, T>>::kBytes;
     constexpr int PEB = PART ? EB : 0;
     static_assert(!PART || SHIFT || VBO == VB, "PART rows need outputs of the input's element size");
-    static_assert(!SHIFT || (PART && VB == 16 && Op::kParams == 0),
-                  "SHIFT rows: 16-byte vectors, operators without parameters");
+    static_assert(!SHIFT || (PART && VB == 16 && !Op::kParamsInReduce),
+                  "SHIFT rows: 16-byte vectors, parameters applied at the output");
     __shared__ RawVec<VB> lds_params[param_lds_vectors<OP, VB, IT, kWave, kOwnerWaves>()];
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t nv = PART ? (a.cols + E - 1) / E : a.cols / E;
@@ -803,7 +890,7 @@ __global__ __launch_bounds__(kWave *kWaveRowsPerWg) void single_wave_kernel(RowA
     load_tile<T, VB, IT, kWave>(t, row_srcs<OP, VB, PEB, SHIFT>(a, row, nv, 0, row < a.rows ? (SHIFT ? g.nv : nv) : 0,
                                                                 g.s), lane);
     PC pc;
-    pc.init(row_span<VB, PEB>(a.gamma, 0, a.cols, nv, 0, nv), row_span<VB, PEB>(a.beta, 0, a.cols, nv, 0, nv),
+    pc.init(param_span<VB, PEB, SHIFT>(a.gamma, a.cols, nv, 0, nv), param_span<VB, PEB, SHIFT>(a.beta, a.cols, nv, 0, nv),
             lane, lds_params, threadIdx.x, kWave * kWaveRowsPerWg);
     if constexpr (PC::kMode == kParamLds)
         __syncthreads();
@@ -822,6 +909,7 @@ __global__ __launch_bounds__(kWave *kWaveRowsPerWg) void single_wave_kernel(RowA
             so = shift_row<IT, E, OEB>(loc, g, 0, g.nv, lane);
             kv = count_valid<IT, kWave>(g.nv, lane);
             gn = shift_geom<EB, E>(a, next);
+            pc.shift(g.s, 0);
         }
         const auto wp = tile_partial<OP, T, VB, IT, kWave, kOwnerWaves>(t, kv, pc, lane, loc);
         const Coef c = Op::template finalize<T>(wp, loc, a.cols, a.eps);
@@ -833,7 +921,7 @@ __global__ __launch_bounds__(kWave *kWaveRowsPerWg) void single_wave_kernel(RowA
         if constexpr (SHIFT)
             so.whole = shift_span<VBO, OEB>(a.y, row, a.cols, g.s, 0, g.nv, true);
         store_tile<OP, T, VB, IT, kWave, kOwnerWaves, SHIFT>(t, dst, pc, lane, c, nsrc, so);
-        load_next<OP, T, VB, IT, kWave, kOwnerWaves>(t, nsrc, lane);
+        load_next<OP, T, VB, IT, kWave, kOwnerWaves, SHIFT>(t, nsrc, lane);
         g = gn;
     }
 }
@@ -848,7 +936,7 @@ template <OpKind OP, class T, int VB, int BLOCK, int IT, bool PART = false, bool
 __global__ __launch_bounds__(BLOCK) void single_wg_kernel(RowArgs a)
 {
     using Op = OpTraits<OP>;
-    using PC = ParamCache<OP, T, VB, IT, BLOCK, kOwnerRow>;
+    using PC = ParamCache<OP, T, VB, IT, BLOCK, kOwnerRow, SHIFT>;
     using Loc = std::conditional_t<SHIFT, LocalShift, std::conditional_t<PART, LocalPart, Local>>;
     constexpr int EB = StorageTraits<T>::kBytes;
     constexpr int E = VB / EB;
@@ -857,8 +945,8 @@ __global__ __launch_bounds__(BLOCK) void single_wg_kernel(RowArgs a)
     constexpr int VBO = out_vb<OP, T, VB>();
     constexpr int OEB = StorageTraits<OutT<OP, T>>::kBytes;
     constexpr bool kLds = LT > 0;
-    static_assert(!SHIFT || (PART && VB == 16 && Op::kParams == 0),
-                  "SHIFT rows: 16-byte vectors, operators without parameters");
+    static_assert(!SHIFT || (PART && VB == 16 && !Op::kParamsInReduce),
+                  "SHIFT rows: 16-byte vectors, parameters applied at the output");
     static_assert(!kLds || (!PART && VB == 16), "the LDS tier holds rows of whole 16-byte vectors");
     __shared__ typename Op::Partial sh[NW];
     __shared__ RawVec<VB> lds_params[param_lds_vectors<OP, VB, IT, BLOCK, kOwnerRow>()];
@@ -876,8 +964,8 @@ __global__ __launch_bounds__(BLOCK) void single_wg_kernel(RowArgs a)
     Tile<T, VB, IT> t[Op::kIn];
     load_tile<T, VB, IT, kWave>(t, row_srcs<OP, VB, PEB, SHIFT>(a, row, nv, 0, SHIFT ? g.nv : nreg, g.s), pos);
     PC pc;
-    pc.init(row_span<VB, PEB>(a.gamma, 0, a.cols, nv, 0, nreg), row_span<VB, PEB>(a.beta, 0, a.cols, nv, 0, nreg),
-            pos, lds_params, tid, BLOCK);
+    pc.init(param_span<VB, PEB, SHIFT>(a.gamma, a.cols, nv, 0, nreg),
+            param_span<VB, PEB, SHIFT>(a.beta, a.cols, nv, 0, nreg), pos, lds_params, tid, BLOCK);
     if constexpr (PC::kMode == kParamLds)
         __syncthreads();
     int kv = count_valid<IT, kWave>(nreg, pos);
@@ -895,6 +983,7 @@ __global__ __launch_bounds__(BLOCK) void single_wg_kernel(RowArgs a)
             so = shift_row<IT, E, OEB>(loc, g, 0, g.nv, pos);
             kv = count_valid<IT, kWave>(g.nv, pos);
             gn = shift_geom<EB, E>(a, next);
+            pc.shift(g.s, 0);
         }
         typename Op::Partial lp;
         if constexpr (kLds)
@@ -917,7 +1006,7 @@ __global__ __launch_bounds__(BLOCK) void single_wg_kernel(RowArgs a)
             lds_store<OP, T, VB, BLOCK, LT>(lds_row, span<VBO>(a.y, row * nv + nreg, nl), span<VB>(a.gamma, nreg, nl),
                                             span<VB>(a.beta, nreg, nl), tid,
                                             Op::template finalize_stream<T>(rp, a.cols, a.eps));
-        load_next<OP, T, VB, IT, BLOCK, kOwnerRow>(t, nsrc, pos);
+        load_next<OP, T, VB, IT, BLOCK, kOwnerRow, SHIFT>(t, nsrc, pos);
         g = gn;
         // the next block_combine rewrites sh: every wave must have read it
         __syncthreads();
@@ -961,15 +1050,15 @@ __global__ __launch_bounds__(BLOCK) void split_kernel(SplitArgs a)
 {
     using Op = OpTraits<OP>;
     using Partial = typename Op::Partial;
-    using PC = ParamCache<OP, T, VB, IT, BLOCK, kOwnerSlice>;
+    using PC = ParamCache<OP, T, VB, IT, BLOCK, kOwnerSlice, SHIFT>;
     using Loc = std::conditional_t<SHIFT, LocalShift, std::conditional_t<PART, LocalPart, Local>>;
     constexpr int EB = StorageTraits<T>::kBytes;
     constexpr int E = VB / EB;
     constexpr int PEB = PART ? EB : 0;
     constexpr int OEB = StorageTraits<OutT<OP, T>>::kBytes;
     static_assert(!(PART && CONTROL), "the control twin touches no row");
-    static_assert(!SHIFT || (PART && VB == 16 && Op::kParams == 0),
-                  "SHIFT rows: 16-byte vectors, operators without parameters");
+    static_assert(!SHIFT || (PART && VB == 16 && !Op::kParamsInReduce),
+                  "SHIFT rows: 16-byte vectors, parameters applied at the output");
     constexpr bool kLds = LT > 0;
     static_assert(!kLds || (!PART && !CONTROL && VB == 16), "the LDS tier holds slices of whole 16-byte vectors");
     constexpr int NW = BLOCK / kWave;
@@ -1029,8 +1118,8 @@ __global__ __launch_bounds__(BLOCK) void split_kernel(SplitArgs a)
         load_tile<T, VB, IT, kWave>(
             t, row_srcs<OP, VB, PEB, SHIFT>(a.r, k, nv, v0, k < a.r.rows ? (SHIFT ? shift_ns(g) : nreg) : 0, g.s),
             pos);
-        pc.init(row_span<VB, PEB>(a.r.gamma, 0, a.r.cols, nv, v0, nreg),
-                row_span<VB, PEB>(a.r.beta, 0, a.r.cols, nv, v0, nreg), pos, lds_params, tid, BLOCK);
+        pc.init(param_span<VB, PEB, SHIFT>(a.r.gamma, a.r.cols, nv, v0, nreg),
+                param_span<VB, PEB, SHIFT>(a.r.beta, a.r.cols, nv, v0, nreg), pos, lds_params, tid, BLOCK);
         if constexpr (PC::kMode == kParamLds)
             __syncthreads();
     }
@@ -1057,6 +1146,7 @@ __global__ __launch_bounds__(BLOCK) void split_kernel(SplitArgs a)
             so = shift_row<IT, E, OEB>(loc, g, v0, nsr, pos);
             kv = count_valid<IT, kWave>(nsr, pos);
             gn = shift_geom<EB, E>(a.r, next);
+            pc.shift(g.s, v0);
         }
         Partial lp;
         if constexpr (kLds)
@@ -1117,7 +1207,7 @@ __global__ __launch_bounds__(BLOCK) void split_kernel(SplitArgs a)
                 lds_store<OP, T, VB, BLOCK, LT>(lds_row, span<VBO>(a.r.y, row * nv + v0 + nreg, nl),
                                                 span<VB>(a.r.gamma, v0 + nreg, nl), span<VB>(a.r.beta, v0 + nreg, nl),
                                                 tid, Op::template finalize_stream<T>(rp, a.r.cols, a.r.eps));
-            load_next<OP, T, VB, IT, BLOCK, kOwnerSlice>(t, nsrc, pos);
+            load_next<OP, T, VB, IT, BLOCK, kOwnerSlice, SHIFT>(t, nsrc, pos);
         }
         g = gn;
         // (no barrier needed before the next row rewrites sh or peer: every

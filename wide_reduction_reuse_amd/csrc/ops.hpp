@@ -448,14 +448,19 @@ struct OpTraits<kLayerNorm> {
         float sum = 0.0f;
 #pragma unroll
         for (int k = 0; k < IT; ++k)
-            if (k < kvalid)
+            if (k < kvalid) {
+                fill_outside<T, VB>(t.v[k], loc, k, 0.0f);
 #pragma unroll
                 for (int e = 0; e < E; ++e)
                     sum += elem<T, VB>(t.v[k], e);
+            }
         int nvalid = kvalid * E;
         if constexpr (L::kPartial)
             if (loc.kpart >= 0 && loc.kpart < kvalid)
                 nvalid -= E - loc.ntail;  // the partial vector's zeros are no elements
+        if constexpr (L::kHead)
+            if (kvalid > 0)
+                nvalid -= loc.hcount;  // nor are a shifted row's leading elements
         const float nw = wave_sum(static_cast<float>(nvalid));
         const float sw = wave_sum(sum);
         const float mean = nw > 0.0f ? sw / nw : 0.0f;
@@ -578,19 +583,21 @@ struct OpTraits<kRmsNorm> {
     using Partial = Part<kQ>;
 
     template <class T, int VB, int IT, class L>
-    __device__ __forceinline__ static Partial wave_partial(Tile<T, VB, IT> (&tt)[kIn], int kvalid, L &)
+    __device__ __forceinline__ static Partial wave_partial(Tile<T, VB, IT> (&tt)[kIn], int kvalid, L &loc)
     {
         Tile<T, VB, IT> &t = tt[0];
         constexpr int E = Tile<T, VB, IT>::kEpv;
         float ss = 0.0f;
 #pragma unroll
         for (int k = 0; k < IT; ++k)
-            if (k < kvalid)
+            if (k < kvalid) {
+                fill_outside<T, VB>(t.v[k], loc, k, 0.0f);  // (a PART row's tail loaded as zeros)
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
                     float x = elem<T, VB>(t.v[k], e);
                     ss = __builtin_fmaf(x, x, ss);
                 }
+            }
         return Partial{{wave_sum(ss)}};
     }
 

@@ -40,7 +40,11 @@ bool row_is_partial(int op, int dt, int64_t cols)
 
 bool row_is_shifted(int op, int dt, int64_t cols)
 {
-    return op_has_shift(op) && (cols * elem_bytes(dt)) % 64 != 0;
+    // LayerNorm shifts only the rows it has no 16-byte kernels for otherwise
+    // (odd bf16 lengths): on its other rows the PART and whole-vector kernels
+    // measured as fast or faster
+    const int64_t bytes = cols * elem_bytes(dt);
+    return op_has_shift(op, dt) && bytes % 64 != 0 && (op != 1 || bytes % 4 != 0);
 }
 
 int held_row_kind(int op, int dt, int64_t cols)
@@ -168,12 +172,12 @@ static bool pick_holding_tile(const std::vector<TileSpec> &ladder, int64_t nv, T
 
 // The held-tile ladders of path 1 (wave and workgroup tiles) that `op`
 // compiles for rows of `vb`-byte vectors.
-static std::vector<TileSpec> single_ladder(int op, int dt, int vb)
+static std::vector<TileSpec> single_ladder(int op, int dt, int vb, int part)
 {
     std::vector<TileSpec> ladder;
     for (int kind : {kKindWave, kKindWg})
         for (const TileSpec &u : tiles_for(kind, vb == 16))
-            if (tile_enabled(op, dt, kind, u.block, u.items, vb))
+            if (tile_enabled(op, dt, kind, u.block, u.items, vb, part))
                 ladder.push_back(u);
     return ladder;
 }
@@ -222,7 +226,7 @@ bool single_tile(int op, int dt, int64_t cols, TileSpec *out)
 {
     const int vb = held_vec_bytes(op, dt, cols);
     const int64_t nv = held_vectors(op, dt, cols);
-    const std::vector<TileSpec> ladder = single_ladder(op, dt, vb);
+    const std::vector<TileSpec> ladder = single_ladder(op, dt, vb, held_row_kind(op, dt, cols));
     TileSpec t;
     if (!pick_holding_tile(ladder, nv, &t) &&
         !pick_lds_tile(lds_ladder(op, dt, cols, kKindWg), lds_row_vectors(dt, cols), &t))
@@ -243,7 +247,7 @@ bool split_tile(int op, int dt, int64_t cols, int p, TileSpec *out)
         return false;  // the last slice would be empty: too narrow to split p ways
     std::vector<TileSpec> ladder;
     for (const TileSpec &u : tiles_for(kKindSplit, vb == 16))
-        if (tile_enabled(op, dt, kKindSplit, u.block, u.items, vb))
+        if (tile_enabled(op, dt, kKindSplit, u.block, u.items, vb, held_row_kind(op, dt, cols)))
             ladder.push_back(u);
     // the LDS tier holds rows of whole 16-byte vectors as they are (no shift)
     const int64_t nvl = lds_row_vectors(dt, cols);
@@ -690,10 +694,11 @@ void enumerate_candidates(const PlanRequest &req, const Calibration &cal, std::v
     const bool v16 = vb == 16;
     const int64_t nv = held_vectors(req.op, req.dt, req.cols);
     const int rvb = vec_bytes_for(req.dt, req.cols);
-    const std::vector<TileSpec> held = single_ladder(req.op, req.dt, vb);
+    const int part = held_row_kind(req.op, req.dt, req.cols);
+    const std::vector<TileSpec> held = single_ladder(req.op, req.dt, vb, part);
     for (int kind : {kKindWave, kKindWg})
         for (TileSpec t : tiles_for(kind, v16)) {
-            if (!tile_enabled(req.op, req.dt, kind, t.block, t.items, vb) || !worth_holding(held, t, nv))
+            if (!tile_enabled(req.op, req.dt, kind, t.block, t.items, vb, part) || !worth_holding(held, t, nv))
                 continue;
             t.vb = vb;
             for (int mode : {0, -1}) {
@@ -747,7 +752,7 @@ void enumerate_candidates(const PlanRequest &req, const Calibration &cal, std::v
             continue;
         std::vector<TileSpec> ladder;
         for (const TileSpec &u : tiles_for(kKindSplit, v16))
-            if (tile_enabled(req.op, req.dt, kKindSplit, u.block, u.items, vb))
+            if (tile_enabled(req.op, req.dt, kKindSplit, u.block, u.items, vb, part))
                 ladder.push_back(u);
         std::vector<TileSpec> tiles;
         for (TileSpec t : ladder)

@@ -182,8 +182,8 @@ int vec_bytes_for(int dt, int64_t cols);
 // one is partial (PART kernels mask its missing elements).
 bool row_is_partial(int op, int dt, int64_t cols);
 // Rows whose byte length is not a multiple of 64, of an operator with SHIFT
-// kernels: paths 1 and 2 hold them as 16-byte vectors from the 64-byte
-// boundary below each row's start.
+// kernels (for LayerNorm: odd-length bf16 rows only): paths 1 and 2 hold them
+// as 16-byte vectors from the 64-byte boundary below each row's start.
 bool row_is_shifted(int op, int dt, int64_t cols);
 // The kernels' row kind for paths 1 and 2: 0 whole vectors or one-element
 // tiles, 1 partial last vector (row_is_partial), 2 shifted (row_is_shifted).

@@ -28,18 +28,21 @@ struct KernelEntry {
 };
 
 // Operators with PART kernels (rows whose byte length is a multiple of 4 but
-// not of 16, held from their first byte): the operators with parameter
-// vectors, LayerNorm, RMSNorm and fp32 LayerNorm backward.  (bf16 LayerNorm
-// backward, whose held rows are reduced in the streaming form, which counts
-// whole vectors, keeps one-element tiles for such rows.)
-constexpr bool op_has_part(int op, int dt) { return op == 1 || op == 2 || (op == 4 && dt == 0); }
+// not of 16, held from their first byte): LayerNorm (whose two parameter
+// vectors, realigned to a shifted row, cost it more registers than the
+// shift saves on such rows) and fp32 LayerNorm backward (whose parameters
+// enter the reduction, g = gamma * dy held in the tile, so its rows cannot be
+// shifted against them).  (bf16 LayerNorm backward, whose held rows are
+// reduced in the streaming form, which counts whole vectors, keeps
+// one-element tiles for such rows.)
+constexpr bool op_has_part(int op, int dt) { return op == 1 || (op == 4 && dt == 0); }
 
-// Operators with SHIFT kernels (rows whose byte length is not a multiple of
-// 64, held from the 64-byte boundary below their start, any element count):
-// those without parameter vectors, softmax, softmax backward and the int8
-// quantizer.  (Shifting a row would shift its parameter vectors against the
-// 16-byte grid too.)
-constexpr bool op_has_shift(int op) { return op == 0 || op == 3 || op == 5; }
+// Operators with SHIFT kernels (rows held from the 64-byte boundary below
+// their start): all but LayerNorm backward, and LayerNorm in bf16 only (for
+// its odd-length rows); LayerNorm's and RMSNorm's parameter vectors are
+// realigned to each row's shift at the output.  Which rows are shifted: see
+// the planner's row_is_shifted.
+constexpr bool op_has_shift(int op, int dt) { return op != 4 && (op != 1 || dt == 1); }
 
 void register_softmax_kernels(std::vector<KernelEntry> &out);
 void register_layernorm_kernels(std::vector<KernelEntry> &out);
@@ -81,8 +84,13 @@ constexpr int op_stats(int op)
 // At 512 threads (256 VGPRs): bf16 LayerNorm backward, which holds x and dy
 // as loaded and converts them for every use, more than 256 B (x and dy of
 // 16 vectors each).
-constexpr bool tile_enabled(int op, int dt, int kind, int block, int items, int vb)
+//   LayerNorm's SHIFT workgroup tile 1024 x 16 (its parameter vectors are
+//     realigned at the output, on top of a tile at the 128-VGPR cap).
+// part: the row kind the tile holds (KernelEntry::part).
+constexpr bool tile_enabled(int op, int dt, int kind, int block, int items, int vb, int part = 0)
 {
+    if (part == 2 && op == 1 && kind == kKindWg && block == 1024 && items == 16)
+        return false;
     if (op == 4 && dt == 1 && kind != kKindReread && block >= 512 && op_inputs(op) * items * vb > 256)
         return false;
     if (kind == kKindReread || block < 1024)

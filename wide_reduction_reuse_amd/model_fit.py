@@ -70,15 +70,18 @@ def records_from_table(doc: dict) -> list:
 
 def row_kind(op: str, dt: str, cols: int) -> int:
     """The held register tiles' row kind for this width (the library's
-    held_row_kind): 2 for rows of the operators without parameter vectors
-    (softmax, softmax backward, the quantizer) whose byte length is not a
-    multiple of 64 (held from the boundary below their start), 1 for
-    rows of LayerNorm, RMSNorm and fp32 LayerNorm backward whose byte length
-    is a multiple of 4 but not of 16 (a partial last vector), else 0."""
+    held_row_kind): 2 for rows whose byte length is not a multiple of 64
+    (held from the 64-byte line below their start) of softmax, softmax
+    backward, the quantizer and RMSNorm, and of LayerNorm when the byte length
+    is not a multiple of 4; 1 for the other rows of LayerNorm and fp32
+    LayerNorm backward whose byte length is a multiple of 4 but not of 16 (a
+    partial last vector); else 0."""
     nbytes = cols * (4 if dt == "f32" else 2)
-    if op in ("softmax", "softmax_bwd", "quantize_int8"):
+    if op not in ("layernorm", "layernorm_bwd"):
         return 2 if nbytes % 64 else 0
-    if op in ("layernorm", "rmsnorm") or (op == "layernorm_bwd" and dt == "f32"):
+    if op == "layernorm" and nbytes % 4:
+        return 2
+    if op == "layernorm" or dt == "f32":
         return 1 if nbytes % 16 and nbytes % 4 == 0 else 0
     return 0
 
