@@ -585,6 +585,87 @@ bool plan_from_neighbours(const PlanRequest &req, const Calibration &cal, int fo
 
 }  // namespace
 
+// A held tile is a candidate when it holds `need` vectors and is at least
+// half used (or is the smallest tile that holds them).
+static bool worth_holding(const std::vector<TileSpec> &ladder, const TileSpec &t, int64_t need)
+{
+    const int64_t cap = static_cast<int64_t>(t.block) * t.items;
+    if (cap < need)
+        return false;
+    if (cap < 2 * need)
+        return true;
+    for (const TileSpec &u : ladder) {
+        const int64_t c = static_cast<int64_t>(u.block) * u.items;
+        if (c >= need && c < cap)
+            return false;
+    }
+    return true;
+}
+
+// The path-1 tiles worth pricing for a row: the register tiles that hold it
+// and are at least half used, and the LDS-tier tiles whose register part the
+// row fills (otherwise the same registers alone hold it).  A shifted row
+// whose span no register tile holds, though its whole 16-byte vectors would
+// fit one, is held unshifted by an LDS-tier tile.  vb is set on each.
+static std::vector<TileSpec> held_candidates(int op, int dt, int64_t cols)
+{
+    const int vb = held_vec_bytes(op, dt, cols);
+    const int64_t nv = held_vectors(op, dt, cols);
+    const int part = held_row_kind(op, dt, cols);
+    const std::vector<TileSpec> held = single_ladder(op, dt, vb, part);
+    std::vector<TileSpec> out;
+    bool reg_holds = false;
+    for (TileSpec t : held) {
+        reg_holds = reg_holds || static_cast<int64_t>(t.block) * t.items >= nv;
+        if (!worth_holding(held, t, nv))
+            continue;
+        t.vb = vb;
+        out.push_back(t);
+    }
+    const int64_t nvl = lds_row_vectors(dt, cols);
+    for (const TileSpec &t : lds_ladder(op, dt, cols, kKindWg)) {
+        const int64_t reg = static_cast<int64_t>(t.block) * t.items;
+        if ((nvl <= reg && reg_holds) || nvl > reg + static_cast<int64_t>(t.block) * t.lds)
+            continue;
+        out.push_back(t);
+    }
+    return out;
+}
+
+// The split tiles worth pricing at width p: the register tiles that hold a
+// slice and are at least half used, and the LDS-tier tiles that hold an
+// (unshifted) slice no register tile holds or whose register part it fills.
+static std::vector<TileSpec> split_candidates(int op, int dt, int64_t cols, int p)
+{
+    const int vb = held_vec_bytes(op, dt, cols);
+    const int64_t nv = held_vectors(op, dt, cols);
+    const int part = held_row_kind(op, dt, cols);
+    const int64_t nvl = lds_row_vectors(dt, cols);
+    const int64_t per = slice_vectors(nv, p, vb);
+    const int64_t perl = slice_vectors(nvl, p, 16);
+    const bool reg_ok = per * (p - 1) < nv;
+    const bool lds_ok = nvl > 0 && perl * (p - 1) < nvl;
+    std::vector<TileSpec> tiles;
+    if (!reg_ok && !lds_ok)
+        return tiles;
+    std::vector<TileSpec> ladder;
+    for (const TileSpec &u : tiles_for(kKindSplit, vb == 16))
+        if (tile_enabled(op, dt, kKindSplit, u.block, u.items, vb, part))
+            ladder.push_back(u);
+    for (TileSpec t : ladder)
+        if (reg_ok && worth_holding(ladder, t, per)) {
+            t.vb = vb;
+            tiles.push_back(t);
+        }
+    const bool reg_holds_slice = !tiles.empty();
+    for (const TileSpec &t : lds_ladder(op, dt, cols, kKindSplit)) {
+        const int64_t reg = static_cast<int64_t>(t.block) * t.items;
+        if (lds_ok && (perl > reg || !reg_holds_slice) && perl <= reg + static_cast<int64_t>(t.block) * t.lds)
+            tiles.push_back(t);
+    }
+    return tiles;
+}
+
 bool make_plan(const PlanRequest &req, const Calibration &cal, int forced_path, int forced_p, Plan *out)
 {
     if (!cal.table.empty() && plan_from_table(req, cal, forced_path, forced_p, out))
@@ -595,6 +676,11 @@ bool make_plan(const PlanRequest &req, const Calibration &cal, int forced_path, 
     // the row (a held row is never reread: path 3 moves b_in more bytes per
     // element at the same rate), else path 3; each split width P is priced
     // against it by Eq. 7-9 (split_terms) and the fastest prediction wins.
+    // Within a path the tile is the one pick_holding_tile prefers.  Taking
+    // the candidate tile this model prices fastest instead scored worse on
+    // MI355X (61 against 74 of the 90 width-sweep shapes within 1% of the
+    // fastest plan): the model's terms that depend on the tile, occupancy and
+    // vectors per thread, rank the tiles of one path worse than that rule.
     Plan p;
     TileSpec t1;
     if (single_tile(req.op, req.dt, req.cols, &t1)) {
@@ -668,59 +754,12 @@ bool analytic_baseline(const PlanRequest &req, const Calibration &cal, int *path
     return true;
 }
 
-// A held tile is a candidate when it holds `need` vectors and is at least
-// half used (or is the smallest tile that holds them).
-static bool worth_holding(const std::vector<TileSpec> &ladder, const TileSpec &t, int64_t need)
-{
-    const int64_t cap = static_cast<int64_t>(t.block) * t.items;
-    if (cap < need)
-        return false;
-    if (cap < 2 * need)
-        return true;
-    for (const TileSpec &u : ladder) {
-        const int64_t c = static_cast<int64_t>(u.block) * u.items;
-        if (c >= need && c < cap)
-            return false;
-    }
-    return true;
-}
-
 void enumerate_candidates(const PlanRequest &req, const Calibration &cal, std::vector<Candidate> *out)
 {
     out->clear();
     // held tiles (paths 1, 2) and the reread tiles of path 3 can differ in
     // access width: a partial row is held as 16-byte vectors, reread by element
-    const int vb = held_vec_bytes(req.op, req.dt, req.cols);
-    const bool v16 = vb == 16;
-    const int64_t nv = held_vectors(req.op, req.dt, req.cols);
-    const int rvb = vec_bytes_for(req.dt, req.cols);
-    const int part = held_row_kind(req.op, req.dt, req.cols);
-    const std::vector<TileSpec> held = single_ladder(req.op, req.dt, vb, part);
-    for (int kind : {kKindWave, kKindWg})
-        for (TileSpec t : tiles_for(kind, v16)) {
-            if (!tile_enabled(req.op, req.dt, kind, t.block, t.items, vb, part) || !worth_holding(held, t, nv))
-                continue;
-            t.vb = vb;
-            for (int mode : {0, -1}) {
-                PathEstimate e;
-                e.legal = true;
-                e.tile = t;
-                e.us = stream_time_us(req, cal, kPathSingle, t, mode);
-                out->push_back(Candidate{kPathSingle, 1, e, mode});
-            }
-        }
-    // LDS-tier tiles whose register part the row fills (otherwise the same
-    // registers alone hold it)
-    // (a shifted row whose span no register tile holds, though its whole
-    // 16-byte vectors would fit one, is held unshifted by an LDS-tier tile)
-    const int64_t nvl = lds_row_vectors(req.dt, req.cols);
-    bool reg_holds = false;
-    for (const TileSpec &u : held)
-        reg_holds = reg_holds || static_cast<int64_t>(u.block) * u.items >= nv;
-    for (TileSpec t : lds_ladder(req.op, req.dt, req.cols, kKindWg)) {
-        const int64_t reg = static_cast<int64_t>(t.block) * t.items;
-        if ((nvl <= reg && reg_holds) || nvl > reg + static_cast<int64_t>(t.block) * t.lds)
-            continue;
+    for (const TileSpec &t : held_candidates(req.op, req.dt, req.cols))
         for (int mode : {0, -1}) {
             PathEstimate e;
             e.legal = true;
@@ -728,7 +767,7 @@ void enumerate_candidates(const PlanRequest &req, const Calibration &cal, std::v
             e.us = stream_time_us(req, cal, kPathSingle, t, mode);
             out->push_back(Candidate{kPathSingle, 1, e, mode});
         }
-    }
+    const int rvb = vec_bytes_for(req.dt, req.cols);
     for (TileSpec t : tiles_for(kKindReread, rvb == 16)) {
         t.vb = rvb;
         PathEstimate e;
@@ -740,33 +779,10 @@ void enumerate_candidates(const PlanRequest &req, const Calibration &cal, std::v
     int base_path = 0;
     TileSpec base_tile;
     double base_us = 0.0;
-    const bool have_base = analytic_baseline(req, cal, &base_path, &base_tile, &base_us);
-    for (int P : {2, 4, 8}) {
-        if (!have_base)
-            continue;
-        const int64_t per = slice_vectors(nv, P, vb);
-        const int64_t perl = slice_vectors(nvl, P, 16);  // the LDS tier's slices (unshifted rows)
-        const bool reg_ok = per * (P - 1) < nv;
-        const bool lds_ok = nvl > 0 && perl * (P - 1) < nvl;
-        if (!reg_ok && !lds_ok)
-            continue;
-        std::vector<TileSpec> ladder;
-        for (const TileSpec &u : tiles_for(kKindSplit, v16))
-            if (tile_enabled(req.op, req.dt, kKindSplit, u.block, u.items, vb, part))
-                ladder.push_back(u);
-        std::vector<TileSpec> tiles;
-        for (TileSpec t : ladder)
-            if (reg_ok && worth_holding(ladder, t, per)) {
-                t.vb = vb;
-                tiles.push_back(t);
-            }
-        const bool reg_holds_slice = !tiles.empty();
-        for (const TileSpec &t : lds_ladder(req.op, req.dt, req.cols, kKindSplit)) {
-            const int64_t reg = static_cast<int64_t>(t.block) * t.items;
-            if (lds_ok && (perl > reg || !reg_holds_slice) && perl <= reg + static_cast<int64_t>(t.block) * t.lds)
-                tiles.push_back(t);
-        }
-        for (const TileSpec &t : tiles) {
+    if (!analytic_baseline(req, cal, &base_path, &base_tile, &base_us))
+        return;
+    for (int P : {2, 4, 8})
+        for (const TileSpec &t : split_candidates(req.op, req.dt, req.cols, P)) {
             const SplitTerms st = split_terms(req, cal, P, t, base_path, base_tile, base_us);
             PathEstimate e;
             e.legal = true;
@@ -781,7 +797,6 @@ void enumerate_candidates(const PlanRequest &req, const Calibration &cal, std::v
             e.waves = st.waves;
             out->push_back(Candidate{kPathSplit, P, e, 0});
         }
-    }
 }
 
 // ---------------------------------------------------------------------------
