@@ -184,10 +184,10 @@ def test_selector_legality_on_cpu():
 
 
 def test_partial_rows_are_held_as_16_byte_vectors():
-    # byte length a multiple of 4 but not of 16, LayerNorm and fp32 LayerNorm
-    # backward: paths 1 and 2 hold the row as 16-byte vectors from its first
-    # byte (the last partial) and reread it by element; odd-length bf16 rows
-    # of LayerNorm backward use one-element tiles
+    # byte length a multiple of 4 but not of 16, LayerNorm and fp32
+    # LayerNorm backward: paths 1 and 2 hold the row as 16-byte vectors from
+    # its first byte (the last partial) and reread it by element; odd-length
+    # bf16 rows of LayerNorm backward use one-element tiles
     L = C.lib()
     for op, dt, cols in [("layernorm", "bf16", 1002), ("layernorm", "f32", 3), ("layernorm_bwd", "f32", 1001)]:
         p = C.credit_plan(op, dt, 64, cols, "single")
@@ -210,7 +210,8 @@ def _max_shift_bytes(cols, eb):
 
 def test_shifted_rows_are_held_from_the_line_below():
     # rows whose byte length is not a multiple of 64, of softmax, softmax
-    # backward, the quantizer, RMSNorm, and LayerNorm's odd-length bf16 rows:
+    # backward, the quantizer, RMSNorm, LayerNorm's odd-length bf16 rows, and
+    # fp32 LayerNorm backward's rows of whole 16-byte vectors (single path):
     # paths 1 and 2 hold them as 16-byte vectors from the 64-byte line below
     # each row's start, so a tile must hold the row plus the largest such
     # offset; the reread path reads them by element (or by 16-byte vector
@@ -221,7 +222,8 @@ def test_shifted_rows_are_held_from_the_line_below():
              ("softmax", "bf16", 50264), ("softmax_bwd", "bf16", 30001), ("softmax_bwd", "f32", 30006),
              ("quantize_int8", "f32", 1001), ("quantize_int8", "bf16", 1001), ("quantize_int8", "f32", 4100),
              ("layernorm", "bf16", 1001), ("layernorm", "bf16", 50257), ("rmsnorm", "f32", 3),
-             ("rmsnorm", "bf16", 50257), ("rmsnorm", "f32", 30001)]
+             ("rmsnorm", "bf16", 50257), ("rmsnorm", "f32", 30001), ("layernorm_bwd", "f32", 100),
+             ("layernorm_bwd", "f32", 4100), ("layernorm_bwd", "f32", 12292)]
     for op, dt, cols in cases:
         eb = 4 if dt == "f32" else 2
         p = C.credit_plan(op, dt, 64, cols, "single")

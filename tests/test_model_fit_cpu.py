@@ -71,7 +71,13 @@ def test_row_kind_matches_the_kernel_families():
     assert F.row_kind("layernorm", "bf16", 20001) == 2
     assert F.row_kind("layernorm", "f32", 1004) == 0
     assert F.row_kind("rmsnorm", "bf16", 50257) == 2
-    assert F.row_kind("layernorm_bwd", "f32", 30001) == 1  # parameters in the reduction: a partial last vector
+    assert F.row_kind("layernorm_bwd", "f32", 30001) == 1  # a partial last vector
+    assert F.row_kind("layernorm_bwd", "f32", 4100) == 2   # 16-byte multiple, not a 64-byte one: shifted
+    assert F.row_kind("layernorm_bwd", "f32", 4096) == 0
+    # its split slices keep their parameters and do not shift
+    assert F.row_kind("layernorm_bwd", "f32", 30001, 2) == 1
+    assert F.row_kind("layernorm_bwd", "f32", 4100, 2) == 0
+    assert F.row_kind("softmax", "f32", 4100, 2) == 2
     assert F.row_kind("layernorm_bwd", "bf16", 20002) == 0  # 2-byte accesses throughout
     # the library holds kind-2 widths with room for the shift, kind-1 widths without
     assert C.credit_plan("softmax", "f32", 64, 4100, "single").block_threads * \

@@ -156,16 +156,27 @@ def _ladder(macro):
 # LayerNorm's two, realigned to each row; LayerNorm shifts its odd-length
 # bf16 rows only, and holds its other rows as they are or with a partial
 # last vector)
-SHIFT_OPS = ("softmax", "softmax_bwd", "quantize_int8", "rmsnorm", "layernorm")
+SHIFT_OPS = ("softmax", "softmax_bwd", "quantize_int8", "rmsnorm", "layernorm", "layernorm_bwd")
+# (op, dtype) pairs with shifted rows: bf16 LayerNorm backward holds raw bf16
+# tiles and keeps one-element tiles for rows that are not whole vectors
+SHIFT_CASES = [(op, dt) for op in SHIFT_OPS for dt in W.DTYPES if (op, dt) != ("layernorm_bwd", "bf16")]
 
 
-def _row_kind(op, dt, cols):
-    """The library's row kind (held_row_kind), restated: 2 shifted, 1 a
-    partial last vector, 0 whole vectors (or one-element tiles)."""
+def _row_kind(op, dt, cols, path="single"):
+    """The library's row kind (held_row_kind) on the held path, restated: 2
+    shifted, 1 a partial last vector, 0 whole vectors (or one-element tiles).
+    fp32 LayerNorm backward shifts its rows of whole 16-byte vectors, on the
+    single path only."""
     nbytes = cols * W.ELEM_BYTES[dt]
+    if op == "layernorm_bwd":
+        if dt != "f32":
+            return 0
+        if nbytes % 16:
+            return 1
+        return 2 if path == "single" and nbytes % 64 else 0
     if op in ("softmax", "softmax_bwd", "quantize_int8", "rmsnorm") or (op == "layernorm" and nbytes % 4):
         return 2 if nbytes % 64 else 0
-    if op == "layernorm" or (op == "layernorm_bwd" and dt == "f32"):
+    if op == "layernorm":
         return 1 if nbytes % 16 and nbytes % 4 == 0 else 0
     return 0
 
@@ -314,19 +325,19 @@ def test_every_tile_partial_last_vector(op, dt, kind, block, items, p, cols):
 
 
 # ---------------------------------------------------------------------------
-# rows that are not whole 64-byte lines, of the operators without parameter
-# vectors: their held tiles hold each row from the 64-byte boundary below its
-# start, with up to 64 - min(g, 16) bytes of the previous row in front (g the
-# lowest set bit of the row's byte length), masked and never written; the
-# vectors at the row's ends are written byte by byte where they are shared
+# rows that are not whole 64-byte lines, of the operators with shifted rows:
+# their held tiles hold each row from the 64-byte boundary below its start,
+# with up to 64 - min(g, 16) bytes of the previous row in front (g the lowest
+# set bit of the row's byte length), masked and never written; the vectors at
+# the row's ends are written byte by byte where they are shared
 # ---------------------------------------------------------------------------
-def _shift_held_vectors(op, cols, eb):
-    """The 16-byte vectors the held span of a row needs (the library's rule,
-    restated): shifted rows are held from the 64-byte line below their
-    start, with up to 64 - min(g, 16) bytes in front (g the lowest set bit of
-    the byte length); other rows as they are."""
+def _shift_held_vectors(op, cols, eb, path="single"):
+    """The 16-byte vectors the held span of a row needs on `path` (the
+    library's rule, restated): shifted rows are held from the 64-byte line
+    below their start, with up to 64 - min(g, 16) bytes in front (g the
+    lowest set bit of the byte length); other rows as they are."""
     nbytes = cols * eb
-    if _row_kind(op, "f32" if eb == 4 else "bf16", cols) != 2:
+    if _row_kind(op, "f32" if eb == 4 else "bf16", cols, path) != 2:
         return (nbytes + 15) // 16
     g = nbytes & -nbytes
     return (nbytes + 64 - min(g, 16) + 15) // 16
@@ -360,32 +371,35 @@ def _shift_tile_cases():
     ladders = {"wave": _ladder("CREDIT_WAVE_TILES"), "wg": _ladder("CREDIT_WG_TILES"),
                "split": _ladder("CREDIT_SPLIT_TILES")}
     i = 0
-    for op in SHIFT_OPS:
-        for dt in W.DTYPES:
-            eb = W.ELEM_BYTES[dt]
-            if op == "layernorm":  # shifts its odd-length bf16 rows only
-                classes = ("odd",) if dt == "bf16" else ()
-            else:
-                classes = ("odd", "part", "v16") if dt == "bf16" else ("part", "v16")
-            if not classes:
-                continue
-            for kind, tiles in ladders.items():
-                for block, items in tiles:
-                    cap = block * items
-                    for fill in ("ragged", "full"):
-                        cls = classes[i % len(classes)]
-                        i += 1
-                        if kind == "split":
-                            for p in (2, 4, 8):
-                                if fill == "full":  # the widest slice fills the tile
-                                    fits = lambda n, p=p: (n + p - 1) // p <= cap
-                                else:
-                                    fits = lambda n, p=p: n <= p * cap - 3 * p - 1
-                                cases.append((op, dt, kind, block, items, p, _shift_cols(op, eb, cls, fits)))
-                        else:
-                            lim = cap if fill == "full" else cap - 3
-                            cases.append((op, dt, kind, block, items, 1,
-                                          _shift_cols(op, eb, cls, lambda n: n <= lim)))
+    for op, dt in SHIFT_CASES:
+        eb = W.ELEM_BYTES[dt]
+        if op == "layernorm":  # shifts its odd-length bf16 rows only
+            classes = ("odd",) if dt == "bf16" else ()
+        elif op == "layernorm_bwd":  # fp32 rows of whole 16-byte vectors only
+            classes = ("v16",)
+        else:
+            classes = ("odd", "part", "v16") if dt == "bf16" else ("part", "v16")
+        if not classes:
+            continue
+        for kind, tiles in ladders.items():
+            if kind == "split" and op == "layernorm_bwd":
+                continue  # its split slices are not shifted
+            for block, items in tiles:
+                cap = block * items
+                for fill in ("ragged", "full"):
+                    cls = classes[i % len(classes)]
+                    i += 1
+                    if kind == "split":
+                        for p in (2, 4, 8):
+                            if fill == "full":  # the widest slice fills the tile
+                                fits = lambda n, p=p: (n + p - 1) // p <= cap
+                            else:
+                                fits = lambda n, p=p: n <= p * cap - 3 * p - 1
+                            cases.append((op, dt, kind, block, items, p, _shift_cols(op, eb, cls, fits)))
+                    else:
+                        lim = cap if fill == "full" else cap - 3
+                        cases.append((op, dt, kind, block, items, 1,
+                                      _shift_cols(op, eb, cls, lambda n: n <= lim)))
     return cases
 
 
@@ -419,13 +433,14 @@ def test_every_tile_shifted(op, dt, kind, block, items, p, cols):
     _check(inp, out, "shifted tile %s %dx%d p=%d %s %s cols=%d" % (kind, block, items, p, op, dt, cols))
 
 
-@pytest.mark.parametrize("op,dt", [(op, dt) for op in SHIFT_OPS for dt in W.DTYPES])
+@pytest.mark.parametrize("op,dt", SHIFT_CASES)
 def test_shifted_tile_one_vector_short_is_refused(op, dt):
     # a tile that holds the row but not the row with its largest offset in
     # front is refused before launch
     C = _lib()
     eb = W.ELEM_BYTES[dt]
-    cols = _shift_cols(op, eb, "part" if dt == "f32" else "odd", lambda n: n <= 257)
+    cols = _shift_cols(op, eb, ("v16" if op == "layernorm_bwd" else "part") if dt == "f32" else "odd",
+                       lambda n: n <= 257)
     assert _shift_held_vectors(op, cols, eb) == 257
     w = W.custom(op, dt, 3, cols, seed=3)
     inp = W.generate(w)
@@ -436,7 +451,7 @@ def test_shifted_tile_one_vector_short_is_refused(op, dt):
 
 @pytest.mark.parametrize("cols", [1, 5, 100, 1001, 1004, 30001])
 @pytest.mark.parametrize("xoff,yoff", [(16, 0), (48, 32), (0, 16)])
-@pytest.mark.parametrize("op,dt", [(op, dt) for op in SHIFT_OPS for dt in W.DTYPES])
+@pytest.mark.parametrize("op,dt", SHIFT_CASES)
 def test_shifted_rows_with_offset_bases(op, dt, xoff, yoff, cols):
     # x (and dy) and y start 0-48 bytes into a 64-byte line, differently: the
     # offset of each row is taken from x's address, the first rows (less than
@@ -463,7 +478,7 @@ def test_shifted_rows_with_offset_bases(op, dt, xoff, yoff, cols):
             t[k] = moved(t.get(k), xoff)
         t["y"] = moved(t["y"], yoff)
         assert t["x"].data_ptr() % 64 == xoff and t["y"].data_ptr() % 64 == yoff
-        nvh = _shift_held_vectors(op, cols, W.ELEM_BYTES[dt])
+        nvh = _shift_held_vectors(op, cols, W.ELEM_BYTES[dt], path)
         if path == "split" and nvh <= _slice_vectors(nvh, 2):
             continue  # too narrow to split
         out = _run(inp, path, p, t=t)
@@ -473,15 +488,18 @@ def test_shifted_rows_with_offset_bases(op, dt, xoff, yoff, cols):
 @pytest.mark.parametrize("dt,cols", [("bf16", 1), ("bf16", 7), ("bf16", 12291), ("f32", 3), ("f32", 1004),
                                      ("f32", 12291)])
 @pytest.mark.parametrize("path,p", [("single", 0), ("split", 2), ("split", 8), ("reread", 0)])
-@pytest.mark.parametrize("op,alias", [("softmax", "x"), ("softmax_bwd", "x"), ("softmax_bwd", "dy")])
+@pytest.mark.parametrize("op,alias", [("softmax", "x"), ("softmax_bwd", "x"), ("softmax_bwd", "dy"),
+                                      ("layernorm_bwd", "x"), ("layernorm_bwd", "dy")])
 def test_shifted_rows_in_place_and_boundary_nan(op, alias, dt, path, p, cols):
     # The output overwrites an input while the neighbouring rows' owners read
     # the 64-byte lines they share with this row; then NaN in the first and
     # last elements of some rows (x, and dy for the backward operator) must
     # stay in those rows.
+    if (op, dt) not in SHIFT_CASES:
+        pytest.skip("%s %s rows are not shifted" % (op, dt))
     C = _lib()
     eb = W.ELEM_BYTES[dt]
-    nvh = _shift_held_vectors(op, cols, eb)
+    nvh = _shift_held_vectors(op, cols, eb, path)
     if path == "split" and nvh <= (p - 1) * _slice_vectors(nvh, p):
         pytest.skip("too narrow to split %d ways" % p)
     w = W.custom(op, dt, 37, cols, seed=cols + 3, x_dist="scaled_shifted", x_scale=3.0, x_shift=0.5)
@@ -508,7 +526,7 @@ def test_shifted_rows_in_place_and_boundary_nan(op, alias, dt, path, p, cols):
             assert not isnan[r].any(), "NaN leaked into row %d" % r
 
 
-@pytest.mark.parametrize("op", SHIFT_OPS)
+@pytest.mark.parametrize("op", [op for op, dt in SHIFT_CASES if dt == "bf16"])
 @pytest.mark.parametrize("path,p", [("single", 0), ("split", 4)])
 def test_odd_length_bf16_word_after_the_tensor_is_masked(op, path, p):
     # rows * cols odd: the last row ends in the middle of a 4-byte word whose

@@ -464,7 +464,7 @@ credit_status_t resolve_plan(int op, int dt, int64_t cols, const credit_plan_t &
     if (plan.vec_bytes != 0 && plan.vec_bytes != vb)
         return CREDIT_ERR_ILLEGAL_PATH;
     const int64_t nv = plan.lds_items > 0 ? lds_row_vectors(dt, cols)
-                       : plan.path != CREDIT_PATH_REREAD ? held_vectors(op, dt, cols)
+                       : plan.path != CREDIT_PATH_REREAD ? held_vectors(op, dt, cols, plan.path)
                                                          : (cols * elem_bytes(dt) + vb - 1) / vb;
     int kind = 0;
     int64_t need = nv;

@@ -47,7 +47,9 @@ void register_op_dtype(std::vector<KernelEntry> &v)
 #define SPLITL(b, it, lt) CREDIT_KL(kKindSplit, b, it, lt, split_kernel<OP, T, VB, b, it, false, false, false, lt>);
 #define WAVEO(it) CREDIT_KO(kKindWave, VB, 64, it, single_wave_kernel<OP, T, VB, it, true, true>);
 #define WGO(b, it) CREDIT_KO(kKindWg, VB, b, it, single_wg_kernel<OP, T, VB, b, it, true, true>);
-#define SPLITO(b, it) CREDIT_KO(kKindSplit, VB, b, it, split_kernel<OP, T, VB, b, it, false, true, true>);
+#define SPLITO(b, it)                                                                         \
+    if constexpr (op_shifts_split(OP, DT))                                                    \
+        CREDIT_KO(kKindSplit, VB, b, it, split_kernel<OP, T, VB, b, it, false, true, true>);
 
     CREDIT_WAVE_TILES(WAVE)
     CREDIT_WG_TILES(WG)

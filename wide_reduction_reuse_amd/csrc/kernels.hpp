@@ -876,8 +876,8 @@ __global__ __launch_bounds__(kWave *kWaveRowsPerWg) void single_wave_kernel(RowA
     constexpr int OEB = StorageTraits<OutT<OP, T>>::kBytes;
     constexpr int PEB = PART ? EB : 0;
     static_assert(!PART || SHIFT || VBO == VB, "PART rows need outputs of the input's element size");
-    static_assert(!SHIFT || (PART && VB == 16 && !Op::kParamsInReduce),
-                  "SHIFT rows: 16-byte vectors, parameters applied at the output");
+    static_assert(!SHIFT || (PART && VB == 16 && !holds_raw<OP, T>()),
+                  "SHIFT rows: 16-byte vectors in a tile the reductions can mask");
     __shared__ RawVec<VB> lds_params[param_lds_vectors<OP, VB, IT, kWave, kOwnerWaves>()];
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t nv = PART ? (a.cols + E - 1) / E : a.cols / E;
@@ -945,8 +945,8 @@ __global__ __launch_bounds__(BLOCK) void single_wg_kernel(RowArgs a)
     constexpr int VBO = out_vb<OP, T, VB>();
     constexpr int OEB = StorageTraits<OutT<OP, T>>::kBytes;
     constexpr bool kLds = LT > 0;
-    static_assert(!SHIFT || (PART && VB == 16 && !Op::kParamsInReduce),
-                  "SHIFT rows: 16-byte vectors, parameters applied at the output");
+    static_assert(!SHIFT || (PART && VB == 16 && !holds_raw<OP, T>()),
+                  "SHIFT rows: 16-byte vectors in a tile the reductions can mask");
     static_assert(!kLds || (!PART && VB == 16), "the LDS tier holds rows of whole 16-byte vectors");
     __shared__ typename Op::Partial sh[NW];
     __shared__ RawVec<VB> lds_params[param_lds_vectors<OP, VB, IT, BLOCK, kOwnerRow>()];
@@ -1057,8 +1057,8 @@ __global__ __launch_bounds__(BLOCK) void split_kernel(SplitArgs a)
     constexpr int PEB = PART ? EB : 0;
     constexpr int OEB = StorageTraits<OutT<OP, T>>::kBytes;
     static_assert(!(PART && CONTROL), "the control twin touches no row");
-    static_assert(!SHIFT || (PART && VB == 16 && !Op::kParamsInReduce),
-                  "SHIFT rows: 16-byte vectors, parameters applied at the output");
+    static_assert(!SHIFT || (PART && VB == 16 && !holds_raw<OP, T>()),
+                  "SHIFT rows: 16-byte vectors in a tile the reductions can mask");
     constexpr bool kLds = LT > 0;
     static_assert(!kLds || (!PART && !CONTROL && VB == 16), "the LDS tier holds slices of whole 16-byte vectors");
     constexpr int NW = BLOCK / kWave;

@@ -805,8 +805,9 @@ struct OpTraits<kLayerNormBwd> {
             set_word<VB>(t[1].v[k], e, __float_as_uint(elem<T, VB>(gv, e) * elem<T, VB>(t[1].v[k], e)));
     }
 
-    // (A PART row's missing elements load as zeros in x and g: neutral in the
-    // sums and in b, masked out of the count and of M2.)
+    // (A PART row's missing elements load as zeros in x and g, and a SHIFT
+    // row's elements outside the row are overwritten with zeros: neutral in
+    // the sums and in b, masked out of the count and of M2.)
     template <class T, int VB, int IT, class L>
     __device__ __forceinline__ static Partial wave_partial(Tile<T, VB, IT> (&t)[kIn], int kvalid, L &loc)
     {
@@ -814,16 +815,22 @@ struct OpTraits<kLayerNormBwd> {
         float sx = 0.0f, sg = 0.0f;
 #pragma unroll
         for (int k = 0; k < IT; ++k)
-            if (k < kvalid)
+            if (k < kvalid) {
+                fill_outside<T, VB>(t[0].v[k], loc, k, 0.0f);
+                fill_outside<T, VB>(t[1].v[k], loc, k, 0.0f);
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
                     sx += elem<T, VB>(t[0].v[k], e);
                     sg += elem<T, VB>(t[1].v[k], e);
                 }
+            }
         int nvalid = kvalid * E;
         if constexpr (L::kPartial)
             if (loc.kpart >= 0 && loc.kpart < kvalid)
                 nvalid -= E - loc.ntail;
+        if constexpr (L::kHead)
+            if (kvalid > 0)
+                nvalid -= loc.hcount;  // a shifted row's leading elements
         const float nw = wave_sum(static_cast<float>(nvalid));
         const float sw = wave_sum(sx);
         const float mean = nw > 0.0f ? sw / nw : 0.0f;

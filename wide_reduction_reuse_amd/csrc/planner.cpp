@@ -32,34 +32,39 @@ int vec_bytes_for(int dt, int64_t cols)
     return (cols * elem_bytes(dt)) % 16 == 0 ? 16 : elem_bytes(dt);
 }
 
-bool row_is_partial(int op, int dt, int64_t cols)
-{
-    const int64_t bytes = cols * elem_bytes(dt);
-    return op_has_part(op, dt) && bytes % 16 != 0 && bytes % 4 == 0;
-}
-
-bool row_is_shifted(int op, int dt, int64_t cols)
+bool row_is_shifted(int op, int dt, int64_t cols, int path)
 {
     // LayerNorm shifts only the rows it has no 16-byte kernels for otherwise
     // (odd bf16 lengths): on its other rows the PART and whole-vector kernels
-    // measured as fast or faster
+    // measured as fast or faster.  fp32 LayerNorm backward shifts, on path 1,
+    // the rows of whole 16-byte vectors (2-10% faster than held as they are
+    // on MI355X); its rows with a partial last vector were no faster shifted
+    // (-4% to +5% across widths) than held by the PART kernels, which fetch
+    // the parameters unshifted.
     const int64_t bytes = cols * elem_bytes(dt);
-    return op_has_shift(op, dt) && bytes % 64 != 0 && (op != 1 || bytes % 4 != 0);
+    const bool shifts = path == kPathSplit ? op_shifts_split(op, dt) : op_has_shift(op, dt);
+    return shifts && bytes % 64 != 0 && (op != 1 || bytes % 4 != 0) && (op != 4 || bytes % 16 == 0);
 }
 
-int held_row_kind(int op, int dt, int64_t cols)
+bool row_is_partial(int op, int dt, int64_t cols, int path)
 {
-    return row_is_partial(op, dt, cols) ? 1 : (row_is_shifted(op, dt, cols) ? 2 : 0);
+    const int64_t bytes = cols * elem_bytes(dt);
+    return op_has_part(op, dt) && bytes % 16 != 0 && bytes % 4 == 0 && !row_is_shifted(op, dt, cols, path);
 }
 
-int held_vec_bytes(int op, int dt, int64_t cols)
+int held_row_kind(int op, int dt, int64_t cols, int path)
 {
-    return held_row_kind(op, dt, cols) != 0 ? 16 : vec_bytes_for(dt, cols);
+    return row_is_partial(op, dt, cols, path) ? 1 : (row_is_shifted(op, dt, cols, path) ? 2 : 0);
+}
+
+int held_vec_bytes(int op, int dt, int64_t cols, int path)
+{
+    return held_row_kind(op, dt, cols, path) != 0 ? 16 : vec_bytes_for(dt, cols);
 }
 
 int path_vec_bytes(int op, int dt, int64_t cols, int path)
 {
-    return path == kPathReread ? vec_bytes_for(dt, cols) : held_vec_bytes(op, dt, cols);
+    return path == kPathReread ? vec_bytes_for(dt, cols) : held_vec_bytes(op, dt, cols, path);
 }
 
 int64_t lds_row_vectors(int dt, int64_t cols)
@@ -70,14 +75,14 @@ int64_t lds_row_vectors(int dt, int64_t cols)
 
 int plan_row_kind(int op, int dt, int64_t cols, int path, int lds)
 {
-    return (path == kPathReread || lds > 0) ? 0 : held_row_kind(op, dt, cols);
+    return (path == kPathReread || lds > 0) ? 0 : held_row_kind(op, dt, cols, path);
 }
 
-int64_t held_vectors(int op, int dt, int64_t cols)
+int64_t held_vectors(int op, int dt, int64_t cols, int path)
 {
-    if (held_row_kind(op, dt, cols) == 2)
+    if (held_row_kind(op, dt, cols, path) == 2)
         return shift_held_vectors(cols, elem_bytes(dt));
-    const int64_t vb = held_vec_bytes(op, dt, cols);
+    const int64_t vb = held_vec_bytes(op, dt, cols, path);
     return (cols * elem_bytes(dt) + vb - 1) / vb;
 }
 
@@ -224,9 +229,9 @@ static bool pick_lds_tile(const std::vector<TileSpec> &ladder, int64_t need, Til
 
 bool single_tile(int op, int dt, int64_t cols, TileSpec *out)
 {
-    const int vb = held_vec_bytes(op, dt, cols);
-    const int64_t nv = held_vectors(op, dt, cols);
-    const std::vector<TileSpec> ladder = single_ladder(op, dt, vb, held_row_kind(op, dt, cols));
+    const int vb = held_vec_bytes(op, dt, cols, kPathSingle);
+    const int64_t nv = held_vectors(op, dt, cols, kPathSingle);
+    const std::vector<TileSpec> ladder = single_ladder(op, dt, vb, held_row_kind(op, dt, cols, kPathSingle));
     TileSpec t;
     if (!pick_holding_tile(ladder, nv, &t) &&
         !pick_lds_tile(lds_ladder(op, dt, cols, kKindWg), lds_row_vectors(dt, cols), &t))
@@ -240,14 +245,14 @@ bool split_tile(int op, int dt, int64_t cols, int p, TileSpec *out)
 {
     if (p != 2 && p != 4 && p != 8)
         return false;
-    const int vb = held_vec_bytes(op, dt, cols);
-    const int64_t nv = held_vectors(op, dt, cols);
+    const int vb = held_vec_bytes(op, dt, cols, kPathSplit);
+    const int64_t nv = held_vectors(op, dt, cols, kPathSplit);
     const int64_t per = slice_vectors(nv, p, vb);
     if (per * (p - 1) >= nv)
         return false;  // the last slice would be empty: too narrow to split p ways
     std::vector<TileSpec> ladder;
     for (const TileSpec &u : tiles_for(kKindSplit, vb == 16))
-        if (tile_enabled(op, dt, kKindSplit, u.block, u.items, vb, held_row_kind(op, dt, cols)))
+        if (tile_enabled(op, dt, kKindSplit, u.block, u.items, vb, held_row_kind(op, dt, cols, kPathSplit)))
             ladder.push_back(u);
     // the LDS tier holds rows of whole 16-byte vectors as they are (no shift)
     const int64_t nvl = lds_row_vectors(dt, cols);
@@ -460,11 +465,37 @@ double calib_time_us(const CalibEntry &e, double rows)
 
 namespace {
 
+// Whether a table entry's tile is compiled for this width's row kind and
+// holds the row (or its widest slice) as that kind: a table measured on
+// another kernel set (before a width's rows were shifted, say) can hold
+// plans the library would now refuse.
+bool entry_holds(const PlanRequest &req, const CalibEntry &e)
+{
+    if (e.path == kPathReread)
+        return true;
+    const int kind = e.path == kPathSplit ? kKindSplit : (e.block == 64 ? kKindWave : kKindWg);
+    const int vb = held_vec_bytes(req.op, req.dt, req.cols, e.path);
+    if (e.lds > 0 ? !lds_tile_enabled(req.op, req.dt, kind, e.block, e.items)
+                  : !tile_enabled(req.op, req.dt, kind, e.block, e.items, vb,
+                                  plan_row_kind(req.op, req.dt, req.cols, e.path, 0)))
+        return false;
+    const int64_t nv = e.lds > 0 ? lds_row_vectors(req.dt, req.cols) : held_vectors(req.op, req.dt, req.cols, e.path);
+    int64_t need = nv;
+    if (e.path == kPathSplit) {
+        need = slice_vectors(nv, e.split_p, e.lds > 0 ? 16 : vb);
+        if (need * (e.split_p - 1) >= nv)
+            return false;
+    }
+    return nv > 0 && need <= static_cast<int64_t>(e.block) * (e.items + e.lds);
+}
+
 // Plan from the calibration table when it measured this (op, dtype, cols)
 // and holds a candidate the forced path / P allow: every such candidate's
 // time at req.rows is interpolated from its measurements, and the fastest
 // wins.  Returns false when the table cannot decide, or measured this width
 // with an access width no longer planned (then the neighbours price it).
+// Entries whose tile no longer holds the row as the library holds it now are
+// passed over.
 bool plan_from_table(const PlanRequest &req, const Calibration &cal, int forced_path, int forced_p, Plan *out)
 {
     Plan p;
@@ -479,6 +510,8 @@ bool plan_from_table(const PlanRequest &req, const Calibration &cal, int forced_
             continue;
         if (e.vb != path_vec_bytes(req.op, req.dt, req.cols, e.path))
             return false;  // measured with an access width no longer planned: price from the neighbours
+        if (!entry_holds(req, e))
+            continue;
         const double us = calib_time_us(e, static_cast<double>(req.rows));
         PathEstimate &pe = p.est[e.path - 1];
         if (!pe.legal || us < pe.us) {
@@ -609,9 +642,9 @@ static bool worth_holding(const std::vector<TileSpec> &ladder, const TileSpec &t
 // fit one, is held unshifted by an LDS-tier tile.  vb is set on each.
 static std::vector<TileSpec> held_candidates(int op, int dt, int64_t cols)
 {
-    const int vb = held_vec_bytes(op, dt, cols);
-    const int64_t nv = held_vectors(op, dt, cols);
-    const int part = held_row_kind(op, dt, cols);
+    const int vb = held_vec_bytes(op, dt, cols, kPathSingle);
+    const int64_t nv = held_vectors(op, dt, cols, kPathSingle);
+    const int part = held_row_kind(op, dt, cols, kPathSingle);
     const std::vector<TileSpec> held = single_ladder(op, dt, vb, part);
     std::vector<TileSpec> out;
     bool reg_holds = false;
@@ -637,9 +670,9 @@ static std::vector<TileSpec> held_candidates(int op, int dt, int64_t cols)
 // (unshifted) slice no register tile holds or whose register part it fills.
 static std::vector<TileSpec> split_candidates(int op, int dt, int64_t cols, int p)
 {
-    const int vb = held_vec_bytes(op, dt, cols);
-    const int64_t nv = held_vectors(op, dt, cols);
-    const int part = held_row_kind(op, dt, cols);
+    const int vb = held_vec_bytes(op, dt, cols, kPathSplit);
+    const int64_t nv = held_vectors(op, dt, cols, kPathSplit);
+    const int part = held_row_kind(op, dt, cols, kPathSplit);
     const int64_t nvl = lds_row_vectors(dt, cols);
     const int64_t per = slice_vectors(nv, p, vb);
     const int64_t perl = slice_vectors(nvl, p, 16);

@@ -178,18 +178,21 @@ bool op_supported(int op, int dt);  // a compiled (operator, dtype) pair
 // length is a multiple of 16 (rows stay 16-byte aligned), else one element.
 int vec_bytes_for(int dt, int64_t cols);
 // Rows whose byte length is a multiple of 4 but not of 16, of an operator
-// with PART kernels: paths 1 and 2 hold them as 16-byte vectors whose last
-// one is partial (PART kernels mask its missing elements).
-bool row_is_partial(int op, int dt, int64_t cols);
+// with PART kernels, that `path` (kPathSingle / kPathSplit) does not shift:
+// held as 16-byte vectors whose last one is partial (PART kernels mask its
+// missing elements).
+bool row_is_partial(int op, int dt, int64_t cols, int path);
 // Rows whose byte length is not a multiple of 64, of an operator with SHIFT
-// kernels (for LayerNorm: odd-length bf16 rows only): paths 1 and 2 hold them
-// as 16-byte vectors from the 64-byte boundary below each row's start.
-bool row_is_shifted(int op, int dt, int64_t cols);
-// The kernels' row kind for paths 1 and 2: 0 whole vectors or one-element
-// tiles, 1 partial last vector (row_is_partial), 2 shifted (row_is_shifted).
-int held_row_kind(int op, int dt, int64_t cols);
+// kernels on `path` (for LayerNorm: odd-length bf16 rows only; fp32 LayerNorm
+// backward: rows of whole 16-byte vectors on path 1 only): held as 16-byte
+// vectors from the 64-byte boundary below each row's start.
+bool row_is_shifted(int op, int dt, int64_t cols, int path);
+// The kernels' row kind for the held tiles of `path` (1 or 2): 0 whole
+// vectors or one-element tiles, 1 partial last vector (row_is_partial),
+// 2 shifted (row_is_shifted).
+int held_row_kind(int op, int dt, int64_t cols, int path);
 // Bytes per access of the held tiles (paths 1, 2): 16 for PART and SHIFT rows too.
-int held_vec_bytes(int op, int dt, int64_t cols);
+int held_vec_bytes(int op, int dt, int64_t cols, int path);
 // Bytes per access that `path` (kPathSingle / kPathSplit / kPathReread) uses.
 int path_vec_bytes(int op, int dt, int64_t cols, int path);
 // 16-byte vectors of a row that the LDS tier holds: rows of whole 16-byte
@@ -198,9 +201,10 @@ int64_t lds_row_vectors(int dt, int64_t cols);
 // The row kind of the kernel a plan runs: held_row_kind for register tiles
 // of paths 1 and 2, 0 for the reread path and the LDS tier.
 int plan_row_kind(int op, int dt, int64_t cols, int path, int lds);
-// Vectors of held_vec_bytes covering a row, the last one possibly partial
-// (SHIFT rows: the most that any row's held span covers, shift_held_vectors).
-int64_t held_vectors(int op, int dt, int64_t cols);
+// Vectors of held_vec_bytes covering a row on `path` (1 or 2), the last one
+// possibly partial (SHIFT rows: the most that any row's held span covers,
+// shift_held_vectors).
+int64_t held_vectors(int op, int dt, int64_t cols, int path);
 
 // Tile ladders, mirroring the compiled instantiations.
 const std::vector<TileSpec> &tiles_for(int kind, int vb_is_16);

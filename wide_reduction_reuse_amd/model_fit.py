@@ -68,22 +68,27 @@ def records_from_table(doc: dict) -> list:
              "rows": rows, "cols": cols, "candidates": c} for (op, dt, cols, rows), c in shapes.items()]
 
 
-def row_kind(op: str, dt: str, cols: int) -> int:
-    """The held register tiles' row kind for this width (the library's
-    held_row_kind): 2 for rows whose byte length is not a multiple of 64
-    (held from the 64-byte line below their start) of softmax, softmax
-    backward, the quantizer and RMSNorm, and of LayerNorm when the byte length
-    is not a multiple of 4; 1 for the other rows of LayerNorm and fp32
-    LayerNorm backward whose byte length is a multiple of 4 but not of 16 (a
-    partial last vector); else 0."""
+def row_kind(op: str, dt: str, cols: int, path: int = 1) -> int:
+    """The held register tiles' row kind for this width on `path` (1 or 2;
+    the library's held_row_kind): 2 for rows whose byte length is not a
+    multiple of 64 (held from the 64-byte line below their start) of softmax,
+    softmax backward, the quantizer and RMSNorm, of fp32 LayerNorm backward on
+    path 1 when the byte length is a multiple of 16, and of LayerNorm when the
+    byte length is not a multiple of 4; 1 for the other rows of LayerNorm and
+    fp32 LayerNorm backward whose byte length is a multiple of 4 but not of 16
+    (a partial last vector); else 0 (bf16 LayerNorm backward: always 0)."""
     nbytes = cols * (4 if dt == "f32" else 2)
-    if op not in ("layernorm", "layernorm_bwd"):
-        return 2 if nbytes % 64 else 0
-    if op == "layernorm" and nbytes % 4:
-        return 2
-    if op == "layernorm" or dt == "f32":
-        return 1 if nbytes % 16 and nbytes % 4 == 0 else 0
-    return 0
+    if op == "layernorm_bwd":
+        if dt != "f32":
+            return 0
+        if nbytes % 16:
+            return 1
+        return 2 if path == 1 and nbytes % 64 else 0
+    if op == "layernorm":
+        if nbytes % 4:
+            return 2
+        return 1 if nbytes % 16 else 0
+    return 2 if nbytes % 64 else 0
 
 
 def occupancy_table(C, records) -> list:
@@ -98,7 +103,7 @@ def occupancy_table(C, records) -> list:
             p = c["plan"]
             path = p["path"]
             kind = {2: KIND_SPLIT, 3: KIND_REREAD}.get(path, KIND_WAVE if p["block_threads"] == 64 else KIND_WG)
-            part = 0 if path == 3 or p.get("lds_items", 0) else row_kind(r["op"], r["dtype"], r["cols"])
+            part = 0 if path == 3 or p.get("lds_items", 0) else row_kind(r["op"], r["dtype"], r["cols"], path)
             key = (OPS.index(r["op"]), DTS.index(r["dtype"]), kind, p["block_threads"], p["items"],
                    p["vec_bytes"], part, p.get("lds_items", 0))
             table[key] = int(occ)
