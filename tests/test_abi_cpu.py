@@ -186,8 +186,7 @@ def test_selector_legality_on_cpu():
 def test_partial_rows_are_held_as_16_byte_vectors():
     # byte length a multiple of 4 but not of 16, LayerNorm and fp32
     # LayerNorm backward: paths 1 and 2 hold the row as 16-byte vectors from
-    # its first byte (the last partial) and reread it by element; odd-length
-    # bf16 rows of LayerNorm backward use one-element tiles
+    # its first byte (the last partial) and reread it by element
     L = C.lib()
     for op, dt, cols in [("layernorm", "bf16", 1002), ("layernorm", "f32", 3), ("layernorm_bwd", "f32", 1001)]:
         p = C.credit_plan(op, dt, 64, cols, "single")
@@ -198,7 +197,10 @@ def test_partial_rows_are_held_as_16_byte_vectors():
         assert L.credit_run_plan(C.OPS[op], _ops(x=A, dy=G, gamma=G, beta=G, y=B), 4, cols, 1e-5,
                                  C.DTYPES[dt], ctypes.byref(plan), None) == 4
     assert C.credit_plan("layernorm_bwd", "f32", 64, 100003, "split", 8).vec_bytes == 16
-    assert C.credit_plan("layernorm_bwd", "bf16", 64, 1001, "single").vec_bytes == 2  # odd bytes / 4
+    # odd-length bf16 rows of LayerNorm backward: shifted on the single path,
+    # read by element on the reread path
+    assert C.credit_plan("layernorm_bwd", "bf16", 64, 1001, "single").vec_bytes == 16
+    assert C.credit_plan("layernorm_bwd", "bf16", 64, 100001, "reread").vec_bytes == 2
 
 
 def _max_shift_bytes(cols, eb):
@@ -223,7 +225,8 @@ def test_shifted_rows_are_held_from_the_line_below():
              ("quantize_int8", "f32", 1001), ("quantize_int8", "bf16", 1001), ("quantize_int8", "f32", 4100),
              ("layernorm", "bf16", 1001), ("layernorm", "bf16", 50257), ("rmsnorm", "f32", 3),
              ("rmsnorm", "bf16", 50257), ("rmsnorm", "f32", 30001), ("layernorm_bwd", "f32", 100),
-             ("layernorm_bwd", "f32", 4100), ("layernorm_bwd", "f32", 12292)]
+             ("layernorm_bwd", "f32", 4100), ("layernorm_bwd", "f32", 12292), ("layernorm_bwd", "bf16", 1001),
+             ("layernorm_bwd", "bf16", 20002), ("layernorm_bwd", "bf16", 4100)]
     for op, dt, cols in cases:
         eb = 4 if dt == "f32" else 2
         p = C.credit_plan(op, dt, 64, cols, "single")
@@ -306,15 +309,17 @@ def test_make_plan_matches_selector_and_honours_forced_paths():
 
 
 def test_bf16_layernorm_backward_plans():
-    # bf16 LayerNorm backward holds rows of whole 16-byte vectors as such and
-    # rows that end in a partial vector by element (its streaming-form
-    # reduction counts whole vectors)
+    # bf16 LayerNorm backward holds rows of whole 64-byte lines as such and,
+    # on the single path, its other rows from the line below their start;
+    # its split slices of rows that end in a partial vector are held by
+    # element (one-element split tiles)
     C.credit_load_calibration(None)
     try:
         p = C.credit_plan("layernorm_bwd", "bf16", 64, 8192, "single")
         assert p.vec_bytes == 16 and p.block_threads * p.items * 8 >= 8192
         assert 2 * p.items * 16 <= 256 or p.block_threads < 512
-        assert C.credit_plan("layernorm_bwd", "bf16", 64, 1002, "single").vec_bytes == 2
+        assert C.credit_plan("layernorm_bwd", "bf16", 64, 1002, "single").vec_bytes == 16
+        assert C.credit_plan("layernorm_bwd", "bf16", 64, 1002, "reread").vec_bytes == 2
         assert C.credit_plan("layernorm_bwd", "f32", 64, 1001, "single").vec_bytes == 16
     finally:
         C.credit_load_calibration(C.CALIB_PATH if os.path.exists(C.CALIB_PATH) else None)

@@ -78,7 +78,9 @@ def test_row_kind_matches_the_kernel_families():
     assert F.row_kind("layernorm_bwd", "f32", 30001, 2) == 1
     assert F.row_kind("layernorm_bwd", "f32", 4100, 2) == 0
     assert F.row_kind("softmax", "f32", 4100, 2) == 2
-    assert F.row_kind("layernorm_bwd", "bf16", 20002) == 0  # 2-byte accesses throughout
+    assert F.row_kind("layernorm_bwd", "bf16", 20002) == 2  # shifted raw bf16 tiles on path 1
+    assert F.row_kind("layernorm_bwd", "bf16", 1000) == 0   # whole 16-byte vectors: held as they are
+    assert F.row_kind("layernorm_bwd", "bf16", 20001, 2) == 0  # 2-byte accesses on path 2
     # the library holds kind-2 widths with room for the shift, kind-1 widths without
     assert C.credit_plan("softmax", "f32", 64, 4100, "single").block_threads * \
         C.credit_plan("softmax", "f32", 64, 4100, "single").items * 4 >= 4100 + 12

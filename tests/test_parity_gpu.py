@@ -157,23 +157,28 @@ def _ladder(macro):
 # bf16 rows only, and holds its other rows as they are or with a partial
 # last vector)
 SHIFT_OPS = ("softmax", "softmax_bwd", "quantize_int8", "rmsnorm", "layernorm", "layernorm_bwd")
-# (op, dtype) pairs with shifted rows: bf16 LayerNorm backward holds raw bf16
-# tiles and keeps one-element tiles for rows that are not whole vectors
-SHIFT_CASES = [(op, dt) for op in SHIFT_OPS for dt in W.DTYPES if (op, dt) != ("layernorm_bwd", "bf16")]
+# (LayerNorm's fp32 rows are not shifted, nor are LayerNorm backward's on the
+# split path: the tests below hold them as the library does)
+SHIFT_CASES = [(op, dt) for op in SHIFT_OPS for dt in W.DTYPES]
+
+
+def _split_may_not_hold(op, dt):
+    """bf16 LayerNorm backward's split slices of rows that are not whole
+    16-byte vectors use one-element tiles, of which few are compiled."""
+    return op == "layernorm_bwd" and dt == "bf16"
 
 
 def _row_kind(op, dt, cols, path="single"):
     """The library's row kind (held_row_kind) on the held path, restated: 2
     shifted, 1 a partial last vector, 0 whole vectors (or one-element tiles).
-    fp32 LayerNorm backward shifts its rows of whole 16-byte vectors, on the
-    single path only."""
+    LayerNorm backward shifts on the single path only: fp32 rows of whole
+    16-byte vectors, bf16 rows that are not."""
     nbytes = cols * W.ELEM_BYTES[dt]
     if op == "layernorm_bwd":
-        if dt != "f32":
-            return 0
-        if nbytes % 16:
+        if dt == "f32" and nbytes % 16:
             return 1
-        return 2 if path == "single" and nbytes % 64 else 0
+        v16 = nbytes % 16 == 0
+        return 2 if path == "single" and nbytes % 64 and v16 == (dt == "f32") else 0
     if op in ("softmax", "softmax_bwd", "quantize_int8", "rmsnorm") or (op == "layernorm" and nbytes % 4):
         return 2 if nbytes % 64 else 0
     if op == "layernorm":
@@ -375,8 +380,8 @@ def _shift_tile_cases():
         eb = W.ELEM_BYTES[dt]
         if op == "layernorm":  # shifts its odd-length bf16 rows only
             classes = ("odd",) if dt == "bf16" else ()
-        elif op == "layernorm_bwd":  # fp32 rows of whole 16-byte vectors only
-            classes = ("v16",)
+        elif op == "layernorm_bwd":  # fp32: rows of whole 16-byte vectors; bf16: the others
+            classes = ("odd", "part") if dt == "bf16" else ("v16",)
         else:
             classes = ("odd", "part", "v16") if dt == "bf16" else ("part", "v16")
         if not classes:
@@ -462,6 +467,8 @@ def test_shifted_rows_with_offset_bases(op, dt, xoff, yoff, cols):
     w = W.custom(op, dt, 19, cols, seed=cols + xoff + 3 * yoff, x_dist="scaled_shifted", x_scale=3.0, x_shift=0.5)
     inp = W.generate(w)
     for path, p in (("single", 0), ("split", 2)):
+        if path == "split" and _split_may_not_hold(op, dt):
+            continue
         t = _device_operands(inp)
 
         def moved(a, off):
@@ -495,8 +502,8 @@ def test_shifted_rows_in_place_and_boundary_nan(op, alias, dt, path, p, cols):
     # the 64-byte lines they share with this row; then NaN in the first and
     # last elements of some rows (x, and dy for the backward operator) must
     # stay in those rows.
-    if (op, dt) not in SHIFT_CASES:
-        pytest.skip("%s %s rows are not shifted" % (op, dt))
+    if path == "split" and _split_may_not_hold(op, dt):
+        pytest.skip("%s %s split slices are not shifted" % (op, dt))
     C = _lib()
     eb = W.ELEM_BYTES[dt]
     nvh = _shift_held_vectors(op, cols, eb, path)
@@ -526,7 +533,7 @@ def test_shifted_rows_in_place_and_boundary_nan(op, alias, dt, path, p, cols):
             assert not isnan[r].any(), "NaN leaked into row %d" % r
 
 
-@pytest.mark.parametrize("op", [op for op, dt in SHIFT_CASES if dt == "bf16"])
+@pytest.mark.parametrize("op", [op for op in SHIFT_OPS if op != "layernorm_bwd"])
 @pytest.mark.parametrize("path,p", [("single", 0), ("split", 4)])
 def test_odd_length_bf16_word_after_the_tensor_is_masked(op, path, p):
     # rows * cols odd: the last row ends in the middle of a 4-byte word whose
@@ -569,10 +576,10 @@ def test_unaligned_row_lengths(op, dt, cols, path, p):
     C = _lib()
     w = W.custom(op, dt, 6, cols, seed=cols + 7, x_dist="scaled_shifted", x_scale=2.0, x_shift=-0.25)
     inp = W.generate(w)
-    if (op, dt) == ("layernorm_bwd", "bf16") and path in ("single", "split") and cols * 2 % 16 != 0 \
-            and cols > 4096:
-        # its one-element tiles end at 1024 x 4 (larger ones spilled
-        # registers): wider such rows are reread, and a forced held path is
+    if (op, dt) == ("layernorm_bwd", "bf16") and path == "split" and cols * 2 % 16 != 0:
+        # its split slices of such rows would be held by element, and its
+        # one-element tiles end at 1024 x 4 (larger ones spilled registers;
+        # on the single path such rows are shifted): a forced split is
         # refused before launch
         with pytest.raises(C.CreditError) as ei:
             _run(inp, path, p)

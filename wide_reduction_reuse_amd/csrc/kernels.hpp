@@ -398,10 +398,10 @@ __device__ __forceinline__ typename OpTraits<OP>::Partial tile_partial(
     using Op = OpTraits<OP>;
     if constexpr (holds_raw<OP, T>()) {
         // the streaming form over the held vectors, kLdsStep at a time, with
-        // the parameters fetched per step
+        // the parameters fetched per step (SHIFT rows: masked to the row)
         constexpr int U = IT < 4 ? IT : 4;
         static_assert(IT % U == 0, "held vectors per thread: a multiple of the step");
-        (void)loc;
+        static_assert(!L::kPartial || L::kHead, "raw tiles hold whole or shifted rows");
         typename Op::Partial r = Op::stream_init();
 #pragma unroll
         for (int kb = 0; kb < IT; kb += U) {
@@ -416,7 +416,10 @@ __device__ __forceinline__ typename OpTraits<OP>::Partial tile_partial(
                     v[i][u] = t[i].v[kb + u];
             }
             const int kvb = kv - kb;
-            Op::template stream_update<T, VB, U>(r, v, g, kvb < 0 ? 0 : (kvb > U ? U : kvb));
+            if constexpr (L::kHead)
+                Op::template stream_update_masked<T, VB, U>(r, v, g, kvb < 0 ? 0 : (kvb > U ? U : kvb), loc, kb);
+            else
+                Op::template stream_update<T, VB, U>(r, v, g, kvb < 0 ? 0 : (kvb > U ? U : kvb));
         }
         return Op::wave_from_thread(r);
     } else {
@@ -876,8 +879,7 @@ __global__ __launch_bounds__(kWave *kWaveRowsPerWg) void single_wave_kernel(RowA
     constexpr int OEB = StorageTraits<OutT<OP, T>>::kBytes;
     constexpr int PEB = PART ? EB : 0;
     static_assert(!PART || SHIFT || VBO == VB, "PART rows need outputs of the input's element size");
-    static_assert(!SHIFT || (PART && VB == 16 && !holds_raw<OP, T>()),
-                  "SHIFT rows: 16-byte vectors in a tile the reductions can mask");
+    static_assert(!SHIFT || (PART && VB == 16), "SHIFT rows: 16-byte vectors");
     __shared__ RawVec<VB> lds_params[param_lds_vectors<OP, VB, IT, kWave, kOwnerWaves>()];
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t nv = PART ? (a.cols + E - 1) / E : a.cols / E;
@@ -945,8 +947,7 @@ __global__ __launch_bounds__(BLOCK) void single_wg_kernel(RowArgs a)
     constexpr int VBO = out_vb<OP, T, VB>();
     constexpr int OEB = StorageTraits<OutT<OP, T>>::kBytes;
     constexpr bool kLds = LT > 0;
-    static_assert(!SHIFT || (PART && VB == 16 && !holds_raw<OP, T>()),
-                  "SHIFT rows: 16-byte vectors in a tile the reductions can mask");
+    static_assert(!SHIFT || (PART && VB == 16), "SHIFT rows: 16-byte vectors");
     static_assert(!kLds || (!PART && VB == 16), "the LDS tier holds rows of whole 16-byte vectors");
     __shared__ typename Op::Partial sh[NW];
     __shared__ RawVec<VB> lds_params[param_lds_vectors<OP, VB, IT, BLOCK, kOwnerRow>()];
@@ -1057,8 +1058,7 @@ __global__ __launch_bounds__(BLOCK) void split_kernel(SplitArgs a)
     constexpr int PEB = PART ? EB : 0;
     constexpr int OEB = StorageTraits<OutT<OP, T>>::kBytes;
     static_assert(!(PART && CONTROL), "the control twin touches no row");
-    static_assert(!SHIFT || (PART && VB == 16 && !holds_raw<OP, T>()),
-                  "SHIFT rows: 16-byte vectors in a tile the reductions can mask");
+    static_assert(!SHIFT || (PART && VB == 16), "SHIFT rows: 16-byte vectors");
     constexpr bool kLds = LT > 0;
     static_assert(!kLds || (!PART && !CONTROL && VB == 16), "the LDS tier holds slices of whole 16-byte vectors");
     constexpr int NW = BLOCK / kWave;

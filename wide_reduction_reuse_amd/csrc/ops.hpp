@@ -931,6 +931,64 @@ struct OpTraits<kLayerNormBwd> {
         r.v[0] = n2;
     }
 
+    // The same over held vectors kb .. kb + U - 1 of a SHIFT row (a raw bf16
+    // tile): the elements outside the row (the previous row's in front, the
+    // next row's in the last word) are zeroed in x and dy first, left out of
+    // the count and of the centred squares; a chunk with no element of the
+    // row adds nothing.
+    template <class T, int VB, int U, class L>
+    __device__ __forceinline__ static void stream_update_masked(Partial &r, RawVec<VB> (&v)[kIn][U],
+                                                                const RawVec<VB> (&gam)[U], int kvalid, const L &loc,
+                                                                int kb)
+    {
+        constexpr int E = VB / StorageTraits<T>::kBytes;
+        if (kvalid <= 0)
+            return;
+        int nout = 0;
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (u < kvalid) {
+                fill_outside<T, VB>(v[0][u], loc, kb + u, 0.0f);
+                fill_outside<T, VB>(v[1][u], loc, kb + u, 0.0f);
+                if (kb + u == 0)
+                    nout += loc.hcount;
+                if (kb + u == loc.kpart)
+                    nout += E - loc.ntail;
+            }
+        const int nin = kvalid * E - nout;
+        if (nin <= 0)
+            return;
+        float sx = 0.0f, sg = 0.0f;
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (u < kvalid)
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    sx += elem<T, VB>(v[0][u], e);
+                    sg = __builtin_fmaf(elem<T, VB>(gam[u], e), elem<T, VB>(v[1][u], e), sg);
+                }
+        const float nc = static_cast<float>(nin);
+        const float mc = sx / nc;
+        float m2c = 0.0f, bc = 0.0f;
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (u < kvalid)
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const float d = elem_in_row(loc, kb + u, e) ? elem<T, VB>(v[0][u], e) - mc : 0.0f;
+                    m2c = __builtin_fmaf(d, d, m2c);
+                    bc = __builtin_fmaf(elem<T, VB>(gam[u], e) * elem<T, VB>(v[1][u], e), d, bc);
+                }
+        const float n2 = r.v[0] + nc;
+        const float d = mc - r.v[1];
+        const float mean2 = __builtin_fmaf(d, nc / n2, r.v[1]);
+        r.v[2] += m2c + d * d * (r.v[0] * nc / n2);
+        r.v[4] = __builtin_fmaf(r.v[3], r.v[1] - mean2, r.v[4]) + __builtin_fmaf(sg, mc - mean2, bc);
+        r.v[3] += sg;
+        r.v[1] = mean2;
+        r.v[0] = n2;
+    }
+
     __device__ __forceinline__ static Partial stream_init() { return Partial{{0.0f, 0.0f, 0.0f, 0.0f, 0.0f}}; }
 
     __device__ __forceinline__ static Partial wave_from_thread(const Partial &r)

@@ -36,14 +36,20 @@ bool row_is_shifted(int op, int dt, int64_t cols, int path)
 {
     // LayerNorm shifts only the rows it has no 16-byte kernels for otherwise
     // (odd bf16 lengths): on its other rows the PART and whole-vector kernels
-    // measured as fast or faster.  fp32 LayerNorm backward shifts, on path 1,
-    // the rows of whole 16-byte vectors (2-10% faster than held as they are
-    // on MI355X); its rows with a partial last vector were no faster shifted
-    // (-4% to +5% across widths) than held by the PART kernels, which fetch
-    // the parameters unshifted.
+    // measured as fast or faster.  LayerNorm backward shifts on path 1 only
+    // (measured on MI355X, every legal plan of each width timed): fp32 rows
+    // of whole 16-byte vectors (2-10% faster than held as they are; its rows
+    // with a partial last vector were no faster shifted, -4% to +5%, than
+    // held by the PART kernels, which fetch the parameters unshifted), and
+    // bf16 rows that are not whole 16-byte vectors (1.25-1.76x faster than
+    // the one-element tiles and the reread path; its rows of whole 16-byte
+    // vectors ran 20% slower shifted, the raw bf16 tile fetching the
+    // realigned parameters in both passes).
     const int64_t bytes = cols * elem_bytes(dt);
     const bool shifts = path == kPathSplit ? op_shifts_split(op, dt) : op_has_shift(op, dt);
-    return shifts && bytes % 64 != 0 && (op != 1 || bytes % 4 != 0) && (op != 4 || bytes % 16 == 0);
+    if (op == 4)
+        return shifts && bytes % 64 != 0 && (dt == 0) == (bytes % 16 == 0);
+    return shifts && bytes % 64 != 0 && (op != 1 || bytes % 4 != 0);
 }
 
 bool row_is_partial(int op, int dt, int64_t cols, int path)

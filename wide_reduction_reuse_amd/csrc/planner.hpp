@@ -183,9 +183,10 @@ int vec_bytes_for(int dt, int64_t cols);
 // missing elements).
 bool row_is_partial(int op, int dt, int64_t cols, int path);
 // Rows whose byte length is not a multiple of 64, of an operator with SHIFT
-// kernels on `path` (for LayerNorm: odd-length bf16 rows only; fp32 LayerNorm
-// backward: rows of whole 16-byte vectors on path 1 only): held as 16-byte
-// vectors from the 64-byte boundary below each row's start.
+// kernels on `path` (for LayerNorm: odd-length bf16 rows only; LayerNorm
+// backward: path 1 only, fp32 rows of whole 16-byte vectors and bf16 rows
+// that are not): held as 16-byte vectors from the 64-byte boundary below each
+// row's start.
 bool row_is_shifted(int op, int dt, int64_t cols, int path);
 // The kernels' row kind for the held tiles of `path` (1 or 2): 0 whole
 // vectors or one-element tiles, 1 partial last vector (row_is_partial),

@@ -38,12 +38,11 @@ struct KernelEntry {
 constexpr bool op_has_part(int op, int dt) { return op == 1 || (op == 4 && dt == 0); }
 
 // Operators with SHIFT kernels (rows held from the 64-byte boundary below
-// their start): all but bf16 LayerNorm backward (whose held tile keeps raw
-// bf16 vectors), and LayerNorm in bf16 only (for its odd-length rows); the
+// their start): all, LayerNorm in bf16 only (for its odd-length rows); the
 // parameter vectors of LayerNorm, RMSNorm and LayerNorm backward are
 // realigned to each row's shift where they are applied.  Which rows are
 // shifted: see the planner's row_is_shifted.
-constexpr bool op_has_shift(int op, int dt) { return (op != 4 || dt == 0) && (op != 1 || dt == 1); }
+constexpr bool op_has_shift(int op, int dt) { return op != 1 || dt == 1; }
 
 // Whether the split path shifts rows too: fp32 LayerNorm backward shifts on
 // path 1 only.  Its split slices keep their parameter vectors for every row of

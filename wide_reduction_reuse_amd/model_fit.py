@@ -76,11 +76,12 @@ def row_kind(op: str, dt: str, cols: int, path: int = 1) -> int:
     path 1 when the byte length is a multiple of 16, and of LayerNorm when the
     byte length is not a multiple of 4; 1 for the other rows of LayerNorm and
     fp32 LayerNorm backward whose byte length is a multiple of 4 but not of 16
-    (a partial last vector); else 0 (bf16 LayerNorm backward: always 0)."""
+    (a partial last vector); else 0.  bf16 LayerNorm backward: 2 on path 1
+    for rows that are not whole 16-byte vectors, else 0."""
     nbytes = cols * (4 if dt == "f32" else 2)
     if op == "layernorm_bwd":
         if dt != "f32":
-            return 0
+            return 2 if path == 1 and nbytes % 16 else 0
         if nbytes % 16:
             return 1
         return 2 if path == 1 and nbytes % 64 else 0
