@@ -262,13 +262,18 @@ constexpr int param_lds_vectors()
 // it straddles (shift()).
 template <OpKind OP, class T, int VB, int IT, int W, int OWNER, bool SH = false>
 struct ParamCache {
-    static constexpr int kMode = SH && OpTraits<OP>::kParams > 0 ? kParamDirect : param_mode<OP, VB, IT, W, OWNER>();
+    // SH with a raw tile (which applies the parameters in both of its passes)
+    // and room for them: realigned once per row into registers
+    static constexpr bool kShiftReg = SH && holds_raw<OP, T>() && OpTraits<OP>::kParams == 1 && IT <= 8;
+    static constexpr int kMode = SH && OpTraits<OP>::kParams > 0 ? (kShiftReg ? kParamReg : kParamDirect)
+                                                                 : param_mode<OP, VB, IT, W, OWNER>();
     static constexpr int kNp = OpTraits<OP>::kParams;
     static constexpr int kRegs = kMode == kParamReg ? IT : 1;
     rsrc_t gam, bet;         // kParamDirect
     RawVec<VB> g[kRegs], b[kRegs];  // kParamReg
     const RawVec<VB> *lds;   // kParamLds: [kNp][W * IT], indexed by vector
     int32_t adj = 0;         // SH: byte offset of the slice's first held vector in the parameter arrays
+    int pos0 = 0;            // kShiftReg: the thread's first held vector
 
     // SH: the row's shift (s elements of the previous row in front, held
     // vectors from v0 on); adj may be negative (the first vectors of a row
@@ -276,6 +281,12 @@ struct ParamCache {
     __device__ __forceinline__ void shift(int s, int64_t v0)
     {
         adj = static_cast<int32_t>(v0 * VB) - s * static_cast<int32_t>(StorageTraits<T>::kBytes);
+        if constexpr (kShiftReg) {
+            const int rb = __builtin_amdgcn_readfirstlane(adj) & 15;
+#pragma unroll
+            for (int k = 0; k < IT; ++k)
+                g[k] = load_shifted(gam, static_cast<int32_t>((pos0 + k * kWave) * VB) + adj, rb);
+        }
     }
 
     // SH: the parameter vector at byte offset o (o = held offset + adj) of
@@ -344,7 +355,8 @@ struct ParamCache {
         gam = gam_;
         bet = bet_;
         lds = lds_buf;
-        if constexpr (kMode == kParamReg) {
+        pos0 = pos;
+        if constexpr (kMode == kParamReg && !kShiftReg) {
 #pragma unroll
             for (int k = 0; k < IT; ++k) {
                 const uint32_t off = static_cast<uint32_t>(pos + k * kWave) * VB;

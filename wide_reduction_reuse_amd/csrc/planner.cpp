@@ -41,10 +41,9 @@ bool row_is_shifted(int op, int dt, int64_t cols, int path)
     // of whole 16-byte vectors (2-10% faster than held as they are; its rows
     // with a partial last vector were no faster shifted, -4% to +5%, than
     // held by the PART kernels, which fetch the parameters unshifted), and
-    // bf16 rows that are not whole 16-byte vectors (1.25-1.76x faster than
+    // bf16 rows that are not whole 16-byte vectors (1.39-1.99x faster than
     // the one-element tiles and the reread path; its rows of whole 16-byte
-    // vectors ran 20% slower shifted, the raw bf16 tile fetching the
-    // realigned parameters in both passes).
+    // vectors ran 20% slower shifted than held as they are).
     const int64_t bytes = cols * elem_bytes(dt);
     const bool shifts = path == kPathSplit ? op_shifts_split(op, dt) : op_has_shift(op, dt);
     if (op == 4)
