@@ -500,7 +500,8 @@ bool entry_holds(const PlanRequest &req, const CalibEntry &e)
 // wins.  Returns false when the table cannot decide, or measured this width
 // with an access width no longer planned (then the neighbours price it).
 // Entries whose tile no longer holds the row as the library holds it now are
-// passed over.
+// passed over, and a width where a held path the library now offers has no
+// entry is left to the neighbours.
 bool plan_from_table(const PlanRequest &req, const Calibration &cal, int forced_path, int forced_p, Plan *out)
 {
     Plan p;
@@ -532,6 +533,17 @@ bool plan_from_table(const PlanRequest &req, const Calibration &cal, int forced_
     }
     if (best == nullptr)
         return false;
+    if (forced_path == kPathAuto) {
+        // a held path the library offers at this width now but the table never
+        // timed here (it was timed on another kernel set): the table cannot
+        // weigh it, the neighbours price it
+        TileSpec t;
+        bool split_now = false;
+        for (int P : {2, 4, 8})
+            split_now = split_now || ((forced_p == 0 || P == forced_p) && split_tile(req.op, req.dt, req.cols, P, &t));
+        if ((!p.est[0].legal && single_tile(req.op, req.dt, req.cols, &t)) || (!p.est[1].legal && split_now))
+            return false;
+    }
     p.path = best->path;
     p.split_p = best->split_p;
     p.wgs_per_cu = best->wgs_per_cu;
