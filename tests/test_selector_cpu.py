@@ -232,3 +232,29 @@ def test_calibration_extension_drops_plans_the_library_no_longer_offers():
     assert K.offered(held) and K.offered(reread)
     # an LDS part is offered only for rows of whole 16-byte vectors
     assert not K.offered(held[:7] + [8] + held[8:])
+
+
+def test_width_missing_a_legal_held_path_is_priced_from_the_neighbours(tmp_path):
+    # the table timed only the reread path at 4096 columns (as a table timed
+    # on a kernel set without held tiles for such rows would): it cannot weigh
+    # paths 1 and 2 there, so the neighbours (here none) and the analytic
+    # model decide, not the one timed plan however fast it was
+    reread_only = [0, 0, 4096, 3, 1, 256, 8, 16, 0, 2, 100, 0.1, 1000, 0.5]
+    C.credit_load_calibration(_write(tmp_path, [reread_only]))
+    p = C.credit_select_path("softmax", "f32", 1000, 4096)
+    assert p.path != 3
+    # forced to the reread path, the table's plan is used
+    assert C.credit_plan("softmax", "f32", 1000, 4096, "reread").path == 3
+
+
+def test_table_plans_that_no_longer_hold_the_row_are_passed_over(tmp_path):
+    # 4100 fp32 columns are held shifted (up to 48 bytes in front): 1028
+    # vectors, which a 1024 x 1 tile (1024 vectors) does not hold, though a
+    # table timed before rows were shifted could list it; it is passed over
+    # for the table's other plan
+    stale = [0, 0, 4100, 1, 1, 1024, 1, 16, -1, 2, 100, 1.0, 1000, 5.0]
+    other = [0, 0, 4100, 1, 1, 512, 4, 16, -1, 2, 100, 50.0, 1000, 500.0]
+    split = [0, 0, 4100, 2, 2, 256, 4, 16, 0, 2, 100, 60.0, 1000, 600.0]
+    C.credit_load_calibration(_write(tmp_path, [stale, other, split]))
+    p = C.credit_select_path("softmax", "f32", 1000, 4100)
+    assert (p.path, p.block_threads, p.items) == (1, 512, 4)
