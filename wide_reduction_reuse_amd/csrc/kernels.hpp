@@ -256,10 +256,12 @@ constexpr int param_lds_vectors()
 //
 // SH: the row is held shifted (SHIFT kernels), so held vector v covers
 // columns v * E - s of a row that begins s elements into its held span, s
-// changing from row to row: the parameters are re-read for every row
-// (kParamDirect) from descriptors over the whole parameter arrays, at byte
-// offset v * VB - s * b, each vector assembled from the two aligned vectors
-// it straddles (shift()).
+// changing from row to row: the parameters are re-read for every row from
+// descriptors over the whole parameter arrays, at byte offset v * VB - s * b,
+// each vector assembled from the two aligned vectors it straddles
+// (load_shifted): where they are used (kParamDirect), or, for a raw tile that
+// uses them in both of its passes, once per row into registers (kShiftReg,
+// in shift()).
 template <OpKind OP, class T, int VB, int IT, int W, int OWNER, bool SH = false>
 struct ParamCache {
     // SH with a raw tile (which applies the parameters in both of its passes)
