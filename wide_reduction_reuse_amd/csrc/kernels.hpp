@@ -562,15 +562,33 @@ __device__ __forceinline__ void store_tile(Tile<T, VB, IT> (&t)[OpTraits<OP>::kI
                 }
         }
     } else {
-        // (shifted parameter vectors take two loads each and a funnel shift:
-        // one vector at a time keeps their registers few)
+        // Unshifted rows: the next group's parameter loads are issued before
+        // this group's stores (vector-memory operations complete in issue
+        // order, so a load issued after a store could only be used once that
+        // store had completed; measured 1-5% faster on wide LayerNorm and
+        // RMSNorm rows on MI355X).  Shifted parameter vectors take two loads
+        // each and a funnel shift: one vector at a time, not prefetched,
+        // keeps their registers few.
         constexpr int GP = SHIFT ? 1 : param_group<IT, VB, NP>();
-#pragma unroll
-        for (int kb = 0; kb < IT; kb += GP) {
-            RawVec<VB> g[GP], b[GP];
+        constexpr bool kAhead = !SHIFT;
+        RawVec<VB> g[GP], b[GP];
+        if constexpr (kAhead)
 #pragma unroll
             for (int j = 0; j < GP; ++j)
-                pc.direct(base + static_cast<uint32_t>((kb + j) * G * VB), g[j], b[j]);
+                pc.direct(base + static_cast<uint32_t>(j * G * VB), g[j], b[j]);
+#pragma unroll
+        for (int kb = 0; kb < IT; kb += GP) {
+            RawVec<VB> gn[GP], bn[GP];
+            if constexpr (kAhead) {
+                if (kb + GP < IT)
+#pragma unroll
+                    for (int j = 0; j < GP; ++j)
+                        pc.direct(base + static_cast<uint32_t>((kb + GP + j) * G * VB), gn[j], bn[j]);
+            } else {
+#pragma unroll
+                for (int j = 0; j < GP; ++j)
+                    pc.direct(base + static_cast<uint32_t>((kb + j) * G * VB), g[j], b[j]);
+            }
 #pragma unroll
             for (int j = 0; j < GP; ++j) {
                 const uint32_t off = base + static_cast<uint32_t>((kb + j) * G * VB);
@@ -582,6 +600,13 @@ __device__ __forceinline__ void store_tile(Tile<T, VB, IT> (&t)[OpTraits<OP>::kI
                 store_out_vec<VBO, SHIFT>(apply_vec<OP, T, VB, RAW>(in, g[j], b[j], vec_coef<OP, T, IT>(c, kb + j)),
                                           dst, ooff, kb + j, so);
             }
+            if constexpr (kAhead)
+                if (kb + GP < IT)
+#pragma unroll
+                    for (int j = 0; j < GP; ++j) {
+                        g[j] = gn[j];
+                        b[j] = bn[j];
+                    }
         }
     }
 }
