@@ -117,14 +117,16 @@ typedef struct {
     int32_t block_threads; /* threads per row owner: 64 = one wavefront per row */
     int32_t items;         /* vectors per thread held (paths 1, 2) or streamed per step (path 3) */
     int32_t vec_bytes;     /* bytes per global access (0 in a plan passed in = the row's own): 16 for
-                              rows of whole 16-byte vectors; for other rows one element, except
-                              that paths 1 and 2 of softmax, LayerNorm, RMSNorm and softmax
-                              backward hold rows whose byte length is a multiple of 4 as 16-byte
-                              vectors, the last one partial (its missing elements masked), and
-                              paths 1 and 2 of bf16 softmax and softmax backward hold odd-length
-                              rows as 16-byte vectors from the 4-byte word below the row's start
-                              (the neighbouring rows' elements in it masked; that shared word is
-                              written one 2-byte half at a time) */
+                              rows of whole 16-byte vectors; for other rows one element on path 3,
+                              and on paths 1 and 2 16 where the operator holds such rows as
+                              16-byte vectors: from the 64-byte line at or below each row's start
+                              (softmax, softmax backward, the quantizer, RMSNorm, odd-length bf16
+                              LayerNorm rows, and on path 1 LayerNorm backward's fp32 rows of whole
+                              16-byte vectors and bf16 rows that are not; the neighbouring rows'
+                              elements masked, the words shared with them written byte-exactly),
+                              or from the row's first byte with a partial last vector (LayerNorm's
+                              and fp32 LayerNorm backward's other rows whose byte length is a
+                              multiple of 4); one element otherwise */
     int32_t wgs_per_cu;    /* paths 1, 2: 0 = as many workgroups as the device holds at once, each
                               owner looping over rows (and loading the next row while writing the
                               current one); k > 0 = at most k per CU; path 1 only: -1 = one
