@@ -21,10 +21,10 @@
  *     must be 16-byte aligned, except scale (4-byte).  gamma, beta, dy and a
  *     floating-point output have the same dtype as x.  In-place operation
  *     (output == x, or dx == dy) is allowed; any other overlap is undefined.
- *     bf16 softmax and softmax backward on rows of odd length read whole
- *     4-byte words: when rows * cols is odd, the 2 bytes after the last
- *     element of x (and dy) are read, never written, and never affect the
- *     result (they lie in the same aligned 4-byte word as that element).
+ *     Shifted bf16 rows of odd length (see credit_plan_t.vec_bytes) are read
+ *     in whole 4-byte words: when rows * cols is odd, the 2 bytes after the
+ *     last element of x (and dy) are read, never written, and never affect
+ *     the result (they lie in the same aligned 4-byte word as that element).
  *   - Calls are asynchronous and stream-ordered on `stream` (a hipStream_t;
  *     NULL means the default stream).  A successful return means the work was
  *     enqueued; device faults surface at the caller's next synchronization.
